@@ -1,0 +1,226 @@
+"""fp64 CPU oracle for reshaped-softmax causal attention -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the HIP product
+path and never imports it.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision, OpenMP); this
+module only builds/loads that library and marshals numpy arrays.  Functions:
+
+* ``tempered_fwd``  -- causal softmax attention with logits tau*<q,k>/sqrt(d)
+  (Focal Attention sec. 2.1 eq. focal-const with tau = 1/t; YaRN "Attention
+  Temperature Scaling", score multiplier sqrt(t)).
+* ``dilution_fwd``  -- dilution attention (DilutionAttention v0.1.0, "The
+  operator": bids, exclusive column cumsum, shares, renormalised A, A@v).
+* ``dilution_decode_step`` -- its cached-decode step (same page: K/V cache
+  plus one running demand total per key and head).
+* ``yarn_t`` / ``yarn_tau`` -- t = 0.1 ln s + 1 and sqrt(t) (YaRN page).
+
+Inputs may be numpy float64/float32 arrays or ``Bf16`` wrappers around raw
+bf16 bit patterns (uint16); the C code widens them exactly to double.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_F64, _F32, _BF16 = 0, 1, 2
+
+
+@dataclass
+class Bf16:
+    """Raw bf16 bit patterns (numpy uint16) standing for exact fp64 values."""
+
+    bits: np.ndarray
+
+    @property
+    def shape(self):
+        return self.bits.shape
+
+    def to_f64(self) -> np.ndarray:
+        return (self.bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile oracle.c into liboracle.so (gcc, OpenMP, IEEE arithmetic)."""
+    cmd = ["gcc", "-O3", "-mavx2", "-mfma", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           "-Wall", "-Wno-unknown-pragmas", src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+_lib = None
+
+
+def load_library(path: str):
+    """Open a compiled oracle library (the default one, or a test build)."""
+    lib = ctypes.CDLL(path)
+    _declare(lib)
+    return lib
+
+
+def use_library(lib) -> None:
+    """Route the module functions through ``lib`` (None: back to the default)."""
+    global _lib
+    _lib = lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        _lib = load_library(_LIB)
+    return _lib
+
+
+def _declare(lib):
+    """Give ctypes the C signatures of the oracle's entry points."""
+    for _ in (0,):
+        dp = ctypes.POINTER(ctypes.c_double)
+        ip = ctypes.POINTER(ctypes.c_int)
+        vp = ctypes.c_void_p
+        i = ctypes.c_int
+        d = ctypes.c_double
+        lib.oracle_yarn_t.restype = d
+        lib.oracle_yarn_t.argtypes = [d]
+        lib.oracle_yarn_tau.restype = d
+        lib.oracle_yarn_tau.argtypes = [d]
+        lib.oracle_num_threads.restype = i
+        lib.oracle_tempered_fwd.restype = i
+        lib.oracle_tempered_fwd.argtypes = [vp, vp, vp, i, dp, dp, i, i, i, i, d, ip, i]
+        lib.oracle_dilution_fwd.restype = i
+        lib.oracle_dilution_fwd.argtypes = [vp, vp, vp, i, dp, dp, dp, i, i, i, i, d, d,
+                                            ip, i, ip, i]
+        lib.oracle_dilution_decode_step.restype = i
+        lib.oracle_dilution_decode_step.argtypes = [vp, vp, vp, i, dp, dp, i, i, i, i, ip,
+                                                    d, d, ip, i]
+
+
+def _as_input(x):
+    """Return (contiguous array, dtype code) without changing any value."""
+    if isinstance(x, Bf16):
+        a = np.ascontiguousarray(x.bits, dtype=np.uint16)
+        return a, _BF16
+    a = np.asarray(x)
+    if a.dtype == np.float32:
+        return np.ascontiguousarray(a), _F32
+    if a.dtype == np.float64:
+        return np.ascontiguousarray(a), _F64
+    raise TypeError(f"oracle input must be float64, float32 or Bf16, got {a.dtype}")
+
+
+def _same_code(*codes):
+    if len(set(codes)) != 1:
+        raise TypeError("q, k and v must share one storage type")
+    return codes[0]
+
+
+def _ptr(a, ctype=ctypes.c_double):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _int_array(xs):
+    if xs is None:
+        return None, 0
+    a = np.ascontiguousarray(np.asarray(xs, dtype=np.int32))
+    return a, int(a.size)
+
+
+def yarn_t(s: float) -> float:
+    return _load().oracle_yarn_t(float(s))
+
+
+def yarn_tau(s: float) -> float:
+    return _load().oracle_yarn_tau(float(s))
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def tempered_fwd(q, k, v, tau: float, rows=None):
+    """Tempered causal attention. q,k,v: [B,H,T,d]. Returns (out, lse) in fp64.
+
+    With ``rows`` only those query rows are computed; the others are NaN.
+    """
+    lib = _load()
+    qa, c1 = _as_input(q)
+    ka, c2 = _as_input(k)
+    va, c3 = _as_input(v)
+    code = _same_code(c1, c2, c3)
+    B, H, T, d = qa.shape
+    out = np.full((B, H, T, d), np.nan)
+    lse = np.full((B, H, T), np.nan)
+    ra, nr = _int_array(rows)
+    rc = lib.oracle_tempered_fwd(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, code,
+                                 _ptr(out), _ptr(lse), B, H, T, d, float(tau),
+                                 _ptr(ra, ctypes.c_int) if ra is not None else None, nr)
+    if rc != 0:
+        raise RuntimeError(f"oracle_tempered_fwd failed ({rc})")
+    return out, lse
+
+
+def dilution_fwd(q, k, v, tau: float = 1.0, eps: float = 1e-6, rows=None, heads=None):
+    """Dilution attention. q,k,v: [B,H,T,d]. Returns (out, lse, demand) in fp64.
+
+    ``demand[b,h,j]`` is the final column total sum_i p_ij.  ``rows`` limits
+    which outputs are formed (all rows still add their bids to the demand);
+    ``heads`` (flattened b*H+h) limits which heads are processed.  Entries not
+    computed are NaN.
+    """
+    lib = _load()
+    qa, c1 = _as_input(q)
+    ka, c2 = _as_input(k)
+    va, c3 = _as_input(v)
+    code = _same_code(c1, c2, c3)
+    B, H, T, d = qa.shape
+    out = np.full((B, H, T, d), np.nan)
+    lse = np.full((B, H, T), np.nan)
+    dem = np.full((B, H, T), np.nan)
+    ra, nr = _int_array(rows)
+    ha, nh = _int_array(heads)
+    rc = lib.oracle_dilution_fwd(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, code,
+                                 _ptr(out), _ptr(lse), _ptr(dem), B, H, T, d, float(tau),
+                                 float(eps),
+                                 _ptr(ra, ctypes.c_int) if ra is not None else None, nr,
+                                 _ptr(ha, ctypes.c_int) if ha is not None else None, nh)
+    if rc != 0:
+        raise RuntimeError(f"oracle_dilution_fwd failed ({rc})")
+    return out, lse, dem
+
+
+def dilution_decode_step(q, kcache, vcache, demand: np.ndarray, tau: float = 1.0,
+                         eps: float = 1e-6, kv_len=None, pairs=None):
+    """One cached-decode step. q: [S,H,d]; caches: [S,H,Lcap,d]; demand: [S,H,Lcap]
+    float64, updated IN PLACE (D += p).  Returns out [S,H,d] fp64 (NaN for
+    pairs not selected)."""
+    lib = _load()
+    qa, c1 = _as_input(q)
+    ka, c2 = _as_input(kcache)
+    va, c3 = _as_input(vcache)
+    code = _same_code(c1, c2, c3)
+    S, H, Lcap, d = ka.shape
+    if demand.dtype != np.float64 or not demand.flags.c_contiguous:
+        raise TypeError("demand must be a C-contiguous float64 array (updated in place)")
+    if demand.shape != (S, H, Lcap):
+        raise ValueError("demand shape mismatch")
+    out = np.full((S, H, d), np.nan)
+    la, _ = _int_array(kv_len)
+    pa, npairs = _int_array(pairs)
+    rc = lib.oracle_dilution_decode_step(
+        qa.ctypes.data, ka.ctypes.data, va.ctypes.data, code, _ptr(demand), _ptr(out),
+        S, H, Lcap, d, _ptr(la, ctypes.c_int) if la is not None else None,
+        float(tau), float(eps), _ptr(pa, ctypes.c_int) if pa is not None else None, npairs)
+    if rc != 0:
+        raise RuntimeError(f"oracle_dilution_decode_step failed ({rc})")
+    return out

@@ -1,0 +1,369 @@
+/*
+ * oracle.c -- plain fp64 CPU oracle for reshaped-softmax causal attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  The HIP product path
+ * shares no code, header, table or helper with it.
+ *
+ * Every quantity is computed straight from its definition, one query row at a
+ * time, in double precision.  Inputs arrive as fp64, fp32 or raw bf16 bits and
+ * are widened exactly to double before any arithmetic.
+ *
+ * Sources (cited by page title and section):
+ *   [FOCAL]  "Learning to Focus: Focal Attention for Selective and Scalable
+ *            Transformers" (arXiv 2511.06818), sec. 2 (softmax, eqs. 1-2) and
+ *            sec. 2.1 (scaled dot-product attention, eq. focal-const).
+ *   [YARN]   "YaRN > Attention Temperature Scaling" (Brenndoerfer), the
+ *            temperature formula t = 0.1 ln s + 1 and the sqrt(t) score
+ *            multiplier (code cells In[14] and In[16]).
+ *   [DIL]    "DilutionAttention v0.1.0 - results", section "The operator":
+ *            the four-line definition (bids, committed, share, A/out) and the
+ *            sentence on cached decoding.
+ *
+ * Readings where the pages leave a step open (each is also listed in the
+ * design notes):
+ *   - tau multiplies the already scaled logits: s = tau * <q,k> / sqrt(d)
+ *     ([YARN] In[16] multiplies the scores by sqrt(t) after the 1/sqrt(d)).
+ *   - causal means key j visible to query i iff j <= i.
+ *   - committed(i,j) sums the bids p(i',j) of all earlier queries i' < i
+ *     down key column j ("demand from earlier queries", [DIL]).
+ *   - eps appears only in the share denominator; a zero bid gets a zero
+ *     share (so eps = 0 never yields 0/0).
+ *   - the decode step uses the demand as it stood before the step, then
+ *     adds this query's bids to it (the bid, not the share).
+ *
+ * Parity of every function here is pinned by the CPU tests against closed
+ * forms, brute force on tiny inputs, a library attention routine and the
+ * pages' invariants; none of them is "parity unpinned".
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_F64 = 0, OR_F32 = 1, OR_BF16 = 2 };
+
+/* Exact widening of one stored element to double. */
+static double widen(const void *base, int dtype, size_t idx) {
+  if (dtype == OR_F64) return ((const double *)base)[idx];
+  if (dtype == OR_F32) return (double)((const float *)base)[idx];
+  /* bf16: the upper 16 bits of an IEEE binary32 */
+  uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* Copy n consecutive stored elements starting at idx into a double buffer. */
+static void widen_block(double *dst, const void *base, int dtype, size_t idx, size_t n) {
+  for (size_t e = 0; e < n; ++e) dst[e] = widen(base, dtype, idx + e);
+}
+
+static double dot(const double *a, const double *b, int d) {
+  double acc = 0.0;
+  for (int e = 0; e < d; ++e) acc += a[e] * b[e];
+  return acc;
+}
+
+/* [YARN]: t = 0.1 ln(s) + 1 and the score multiplier sqrt(t). */
+double oracle_yarn_t(double s) { return 0.1 * log(s) + 1.0; }
+double oracle_yarn_tau(double s) { return sqrt(oracle_yarn_t(s)); }
+
+static int nthreads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+#define MAX_PARTS 256
+/* rows shorter than this are summed by one thread (fork/join costs more) */
+#define PAR_MIN_ROW 256
+
+/*
+ * Causal softmax bids of one query row ([FOCAL] eq. 1 applied to the logits
+ * of eq. focal-const, restricted to the visible keys j <= i):
+ *   s_j = c <q_i, k_j>,  c = tau / sqrt(d)
+ *   lse = log sum_j exp(s_j)   (computed around the row maximum)
+ *   p_j = exp(s_j - lse)
+ * Writes p[0..i] and returns lse.
+ */
+static double causal_bids(const double *qi, const double *K, int i, int d, double c,
+                          double *p, int inner_parallel) {
+  /* Work is split into fixed contiguous ranges of j, and the per-range maxima
+     and sums are combined in range order, so the result does not depend on
+     thread timing. */
+  int parts = (inner_parallel && i + 1 >= PAR_MIN_ROW) ? nthreads() : 1;
+  if (parts > MAX_PARTS) parts = MAX_PARTS;
+  double pm[MAX_PARTS], pz[MAX_PARTS];
+  double lse = 0.0;
+#pragma omp parallel num_threads(parts) if (parts > 1)
+  {
+    int t = 0, n = 1;
+#ifdef _OPENMP
+    t = omp_get_thread_num();
+    n = omp_get_num_threads();
+#endif
+    const long lo = (long)(i + 1) * t / n, hi = (long)(i + 1) * (t + 1) / n;
+    double m = -INFINITY;
+    for (long j = lo; j < hi; ++j) {
+      p[j] = c * dot(qi, K + (size_t)j * d, d);
+      if (p[j] > m) m = p[j];
+    }
+    pm[t] = m;
+#pragma omp barrier
+    double M = -INFINITY;
+    for (int u = 0; u < n; ++u)
+      if (pm[u] > M) M = pm[u];
+    double z = 0.0;
+    for (long j = lo; j < hi; ++j) z += exp(p[j] - M);
+    pz[t] = z;
+#pragma omp barrier
+    double Z = 0.0;
+    for (int u = 0; u < n; ++u) Z += pz[u];
+    const double l = M + log(Z);
+    for (long j = lo; j < hi; ++j) p[j] = exp(p[j] - l);
+    if (t == 0) lse = l;
+  }
+  return lse;
+}
+
+/*
+ * Tempered causal attention ([FOCAL] eq. focal-const with tau = 1/t, and the
+ * [YARN] multiplier tau = sqrt(t)):  o_i = sum_{j<=i} p_ij v_j.
+ *
+ * q,k,v: [B,H,T,d] in dtype; out: [B,H,T,d] fp64; lse (optional): [B,H,T].
+ * rows/nrows (optional): only these query rows are computed (others of out
+ * and lse are left untouched); rows == NULL computes all rows.
+ */
+int oracle_tempered_fwd(const void *q, const void *k, const void *v, int dtype, double *out,
+                        double *lse, int B, int H, int T, int d, double tau, const int *rows,
+                        int nrows) {
+  if (B <= 0 || H <= 0 || T <= 0 || d <= 0) return -1;
+  const double c = tau / sqrt((double)d);
+  const int nr = rows ? nrows : T;
+  double *Kh = malloc(sizeof(double) * (size_t)T * d);
+  double *Vh = malloc(sizeof(double) * (size_t)T * d);
+  if (!Kh || !Vh) { free(Kh); free(Vh); return -2; }
+  for (int bh = 0; bh < B * H; ++bh) {
+    const size_t base = (size_t)bh * T * d;
+    widen_block(Kh, k, dtype, base, (size_t)T * d);
+    widen_block(Vh, v, dtype, base, (size_t)T * d);
+    int failed = 0;
+#pragma omp parallel
+    {
+      double *p = malloc(sizeof(double) * (size_t)T);
+      double *qi = malloc(sizeof(double) * (size_t)d);
+      double *acc = malloc(sizeof(double) * (size_t)d);
+      if (!p || !qi || !acc) {
+#pragma omp atomic write
+        failed = 1;
+      } else {
+#pragma omp for schedule(dynamic, 8)
+        for (int r = 0; r < nr; ++r) {
+          const int i = rows ? rows[r] : r;
+          if (i < 0 || i >= T) continue;
+          widen_block(qi, q, dtype, base + (size_t)i * d, d);
+          const double l = causal_bids(qi, Kh, i, d, c, p, 0);
+          for (int e = 0; e < d; ++e) acc[e] = 0.0;
+          for (int j = 0; j <= i; ++j)
+            for (int e = 0; e < d; ++e) acc[e] += p[j] * Vh[(size_t)j * d + e];
+          for (int e = 0; e < d; ++e) out[base + (size_t)i * d + e] = acc[e];
+          if (lse) lse[(size_t)bh * T + i] = l;
+        }
+      }
+      free(p); free(qi); free(acc);
+    }
+    if (failed) { free(Kh); free(Vh); return -2; }
+  }
+  free(Kh); free(Vh);
+  return 0;
+}
+
+/*
+ * One dilution head, rows in increasing order ([DIL] "The operator"):
+ *   p        = causal softmax bids of row i
+ *   committed_ij = D_j = sum_{i'<i} p_i'j   (running column total, i.e. the
+ *                                           exclusive cumulative sum down key
+ *                                           column j)
+ *   share_ij = p_ij / (committed_ij + p_ij + eps)   (0 where p_ij = 0)
+ *   A_ij     = share_ij / sum_j share_ij ;  o_i = sum_j A_ij v_j
+ * then D_j += p_ij before the next row.
+ * want[i] != 0 selects the rows whose output is formed (all rows still add
+ * their bids to D).  D (length T) enters as the demand already committed
+ * before row 0 -- zero for a plain prefill -- and leaves as the final column
+ * totals.
+ */
+static void dilution_head(const double *Qh, const double *Kh, const double *Vh, int T, int d,
+                          double c, double eps, const unsigned char *want, double *Oh,
+                          double *lse_h, double *D, double *p, int inner_parallel) {
+  for (int i = 0; i < T; ++i) {
+    const int par = inner_parallel && i + 1 >= PAR_MIN_ROW;
+    const double l = causal_bids(Qh + (size_t)i * d, Kh, i, d, c, p, inner_parallel);
+    if (lse_h) lse_h[i] = l;
+    if (!want || want[i]) {
+      double r = 0.0;
+      double acc[512];
+      for (int e = 0; e < d; ++e) acc[e] = 0.0;
+      if (par) {
+        /* same sums, split across threads; partial accumulators are added in
+           a fixed order afterwards */
+        int nt = nthreads();
+        double *part = calloc((size_t)nt * (d + 1), sizeof(double));
+#pragma omp parallel
+        {
+          int t = 0;
+#ifdef _OPENMP
+          t = omp_get_thread_num();
+#endif
+          double *pa = part + (size_t)t * (d + 1);
+#pragma omp for schedule(static)
+          for (int j = 0; j <= i; ++j) {
+            if (p[j] > 0.0) {
+              const double share = p[j] / (D[j] + p[j] + eps);
+              pa[d] += share;
+              for (int e = 0; e < d; ++e) pa[e] += share * Vh[(size_t)j * d + e];
+            }
+          }
+        }
+        for (int t = 0; t < nt; ++t) {
+          for (int e = 0; e < d; ++e) acc[e] += part[(size_t)t * (d + 1) + e];
+          r += part[(size_t)t * (d + 1) + d];
+        }
+        free(part);
+      } else {
+        for (int j = 0; j <= i; ++j) {
+          if (p[j] > 0.0) {
+            const double share = p[j] / (D[j] + p[j] + eps);
+            r += share;
+            for (int e = 0; e < d; ++e) acc[e] += share * Vh[(size_t)j * d + e];
+          }
+        }
+      }
+      for (int e = 0; e < d; ++e) Oh[(size_t)i * d + e] = acc[e] / r;
+    }
+#pragma omp parallel for if (par) schedule(static)
+    for (int j = 0; j <= i; ++j) D[j] += p[j];
+  }
+}
+
+/*
+ * Dilution attention forward ([DIL] "The operator").
+ * q,k,v: [B,H,T,d] in dtype.  out: [B,H,T,d] fp64 (rows not selected are left
+ * untouched).  lse (optional): [B,H,T].  demand (optional): [B,H,T] fp64,
+ * receives the final column totals sum_i p_ij.  rows/nrows: optional subset of
+ * query rows whose output is formed; heads/nheads: optional subset of the
+ * flattened (b*H+h) heads to process (others untouched).
+ */
+int oracle_dilution_fwd(const void *q, const void *k, const void *v, int dtype, double *out,
+                        double *lse, double *demand, int B, int H, int T, int d, double tau,
+                        double eps, const int *rows, int nrows, const int *heads, int nheads) {
+  if (B <= 0 || H <= 0 || T <= 0 || d <= 0 || d > 512) return -1;
+  const double c = tau / sqrt((double)d);
+  unsigned char *want = NULL;
+  if (rows) {
+    want = calloc((size_t)T, 1);
+    if (!want) return -2;
+    for (int r = 0; r < nrows; ++r)
+      if (rows[r] >= 0 && rows[r] < T) want[rows[r]] = 1;
+  }
+  const int nh = heads ? nheads : B * H;
+  const int outer = nh >= nthreads();
+  int failed = 0;
+#pragma omp parallel for if (outer) schedule(dynamic, 1)
+  for (int hi = 0; hi < nh; ++hi) {
+    const int bh = heads ? heads[hi] : hi;
+    if (bh < 0 || bh >= B * H) continue;
+    const size_t base = (size_t)bh * T * d;
+    double *Qh = malloc(sizeof(double) * (size_t)T * d);
+    double *Kh = malloc(sizeof(double) * (size_t)T * d);
+    double *Vh = malloc(sizeof(double) * (size_t)T * d);
+    double *D = calloc((size_t)T, sizeof(double));
+    double *p = malloc(sizeof(double) * (size_t)T);
+    if (!Qh || !Kh || !Vh || !D || !p) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+      widen_block(Qh, q, dtype, base, (size_t)T * d);
+      widen_block(Kh, k, dtype, base, (size_t)T * d);
+      widen_block(Vh, v, dtype, base, (size_t)T * d);
+      dilution_head(Qh, Kh, Vh, T, d, c, eps, want, out + base, lse ? lse + (size_t)bh * T : NULL,
+                    D, p, !outer);
+      if (demand) memcpy(demand + (size_t)bh * T, D, sizeof(double) * (size_t)T);
+    }
+    free(Qh); free(Kh); free(Vh); free(D); free(p);
+  }
+  free(want);
+  return failed ? -2 : 0;
+}
+
+/*
+ * One cached-decode step of dilution attention ([DIL], the sentence on cached
+ * decoding: the ordinary key/value cache plus one running demand total per
+ * key and head).  For each selected (sequence, head) with L visible keys:
+ *   s_j = c <q, k_j>, p = softmax(s) over j < L,
+ *   share_j = p_j / (D_j + p_j + eps) (0 where p_j = 0),
+ *   o = sum_j share_j v_j / sum_j share_j,
+ *   then D_j += p_j in place.
+ * q: [S,H,d]; kc,vc: [S,H,Lcap,d] (all in dtype); D: [S,H,Lcap] fp64 in/out;
+ * out: [S,H,d] fp64; kv_len: [S] or NULL (all Lcap); pairs/npairs: optional
+ * subset of flattened (s*H+h) indices to process.
+ */
+int oracle_dilution_decode_step(const void *q, const void *kc, const void *vc, int dtype,
+                                double *D, double *out, int S, int H, int Lcap, int d,
+                                const int *kv_len, double tau, double eps, const int *pairs,
+                                int npairs) {
+  if (S <= 0 || H <= 0 || Lcap <= 0 || d <= 0) return -1;
+  const double c = tau / sqrt((double)d);
+  const int np = pairs ? npairs : S * H;
+  const int outer = np >= nthreads();
+  int failed = 0;
+#pragma omp parallel for if (outer) schedule(dynamic, 1)
+  for (int pi = 0; pi < np; ++pi) {
+    const int sh = pairs ? pairs[pi] : pi;
+    if (sh < 0 || sh >= S * H) continue;
+    const int s = sh / H;
+    const int L = kv_len ? kv_len[s] : Lcap;
+    if (L <= 0 || L > Lcap) {
+#pragma omp atomic write
+      failed = 1;
+      continue;
+    }
+    double *Kh = malloc(sizeof(double) * (size_t)L * d);
+    double *Vh = malloc(sizeof(double) * (size_t)L * d);
+    double *p = malloc(sizeof(double) * (size_t)L);
+    double qv[512];
+    if (!Kh || !Vh || !p || d > 512) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+      widen_block(qv, q, dtype, (size_t)sh * d, d);
+      widen_block(Kh, kc, dtype, (size_t)sh * Lcap * d, (size_t)L * d);
+      widen_block(Vh, vc, dtype, (size_t)sh * Lcap * d, (size_t)L * d);
+      /* the new query sees every cached key: its bids are the causal bids of
+         a row whose last visible key is L-1 */
+      causal_bids(qv, Kh, L - 1, d, c, p, !outer);
+      double *Dh = D + (size_t)sh * Lcap;
+      double r = 0.0, acc[512];
+      for (int e = 0; e < d; ++e) acc[e] = 0.0;
+      for (int j = 0; j < L; ++j) {
+        if (p[j] > 0.0) {
+          const double share = p[j] / (Dh[j] + p[j] + eps);
+          r += share;
+          for (int e = 0; e < d; ++e) acc[e] += share * Vh[(size_t)j * d + e];
+        }
+      }
+      for (int e = 0; e < d; ++e) out[(size_t)sh * d + e] = acc[e] / r;
+      for (int j = 0; j < L; ++j) Dh[j] += p[j];
+    }
+    free(Kh); free(Vh); free(p);
+  }
+  return failed ? -2 : 0;
+}
+
+int oracle_num_threads(void) { return nthreads(); }

@@ -1,0 +1,327 @@
+"""Pins for the fp64 oracle: facts fixed by the pages or by mathematics.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+something that is NOT the oracle itself:
+
+* values printed on the pages (YaRN temperature table, tests/golden/),
+* a library routine the special case reduces to (torch's CPU fp64
+  scaled_dot_product_attention, softmax and logsumexp),
+* closed forms derived here from the definitions (tau = 0 prefix mean; the
+  uniform-bid harmonic-number form of dilution; the two-row case; decode with
+  zero demand),
+* brute force on tiny inputs (whole T x T matrices, written as matrix
+  algebra rather than the oracle's row-by-row running sums),
+* invariants the dilution page states (each query adds one unit of demand,
+  every share is at most one, shares renormalise to one).
+
+They are plain functions so that ``test_oracle_mutants.py`` can run the same
+battery against oracle builds with planted mistakes.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _sdpa(q, k, v, scale):
+    """torch CPU fp64 causal attention (library routine)."""
+    import torch
+
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x)) for x in (q, k, v))
+    return torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, is_causal=True, scale=scale).numpy()
+
+
+def _torch_causal_softmax(q, k, scale):
+    import torch
+
+    tq, tk = torch.from_numpy(q), torch.from_numpy(k)
+    logits = scale * (tq @ tk.transpose(-1, -2))
+    T = q.shape[-2]
+    mask = torch.ones(T, T, dtype=torch.bool).tril()
+    logits = logits.masked_fill(~mask, float("-inf"))
+    return torch.softmax(logits, dim=-1).numpy(), torch.logsumexp(logits, dim=-1).numpy()
+
+
+# --------------------------------------------------------------------------- YaRN
+
+def pin_yarn_table():
+    """t = 0.1 ln s + 1 and sqrt(t) match the page's printed table (4 decimals)."""
+    rows = []
+    with open(os.path.join(GOLDEN, "yarn_temperature_table.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                s, t, st = line.split()
+                rows.append((float(s), float(t), float(st)))
+    assert len(rows) == 7
+    for s, t, st in rows:
+        assert round(oracle.yarn_t(s), 4) == t, (s, oracle.yarn_t(s), t)
+        assert round(oracle.yarn_tau(s), 4) == st, (s, oracle.yarn_tau(s), st)
+    assert oracle.yarn_t(1.0) == 1.0  # no extension, no correction
+
+
+# ----------------------------------------------------------------------- tempered
+
+def pin_tempered_vs_library():
+    """Tempered attention equals torch's causal SDPA with scale tau/sqrt(d)."""
+    rng = _rng(1)
+    for T, d in ((1, 16), (7, 16), (40, 64)):
+        q = rng.standard_normal((2, 3, T, d))
+        k = rng.standard_normal((2, 3, T, d))
+        v = rng.standard_normal((2, 3, T, d))
+        for tau in (0.5, 1.0, oracle.yarn_tau(4.0), 2.5):
+            out, lse = oracle.tempered_fwd(q, k, v, tau)
+            ref = _sdpa(q, k, v, tau / math.sqrt(d))
+            assert np.max(np.abs(out - ref)) < 1e-12, (T, d, tau)
+            _, ref_lse = _torch_causal_softmax(q, k, tau / math.sqrt(d))
+            assert np.max(np.abs(lse - ref_lse)) < 1e-12
+
+
+def pin_tempered_tau0_prefix_mean():
+    """tau = 0 makes every visible bid equal: o_i is the mean of v_0..v_i."""
+    rng = _rng(2)
+    q = rng.standard_normal((1, 2, 33, 8))
+    k = rng.standard_normal((1, 2, 33, 8))
+    v = rng.standard_normal((1, 2, 33, 8))
+    out, lse = oracle.tempered_fwd(q, k, v, 0.0)
+    ref = np.cumsum(v, axis=2) / np.arange(1, 34)[None, None, :, None]
+    assert np.max(np.abs(out - ref)) < 1e-13
+    assert np.max(np.abs(lse - np.log(np.arange(1, 34)))) < 1e-13
+
+
+def pin_tempered_entropy_monotone():
+    """A larger multiplier sharpens every row: row entropy is non-increasing in tau
+    (t < 1 sharpens on the focal page; sqrt(t) > 1 sharpens on the YaRN page)."""
+    rng = _rng(3)
+    T, d = 48, 64
+    q = rng.standard_normal((1, 1, T, d))
+    k = rng.standard_normal((1, 1, T, d))
+    eye = np.zeros((1, 1, T, d))
+    eye[0, 0, np.arange(T), np.arange(T)] = 1.0  # V = I: the output rows are p itself
+    prev = None
+    for tau in (0.0, 0.5, 1.0, oracle.yarn_tau(4.0), 2.5, 6.0):
+        p, _ = oracle.tempered_fwd(q, k, eye, tau)
+        p = p[0, 0, :, :T]
+        assert np.allclose(p.sum(axis=1), 1.0, atol=1e-13)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            ent = -np.sum(np.where(p > 0, p * np.log(p), 0.0), axis=1)
+        if prev is not None:
+            assert np.all(ent <= prev + 1e-12), tau
+        prev = ent
+    # tau = 0 gives the uniform row: entropy log(i+1)
+    p0, _ = oracle.tempered_fwd(q, k, eye, 0.0)
+    assert np.allclose(p0[0, 0, 5, :6], 1.0 / 6.0, atol=1e-15)
+
+
+# ----------------------------------------------------------------------- dilution
+
+def brute_dilution(q, k, v, tau, eps):
+    """The dilution operator written with whole T x T matrices (tiny T only)."""
+    T, d = q.shape
+    logits = tau * (q @ k.T) / math.sqrt(d)
+    visible = np.tril(np.ones((T, T), dtype=bool))
+    logits = np.where(visible, logits, -np.inf)
+    e = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p = e / e.sum(axis=1, keepdims=True)                      # causal softmax bids
+    committed = np.vstack([np.zeros((1, T)), np.cumsum(p, axis=0)[:-1]])  # earlier rows only
+    with np.errstate(divide="ignore", invalid="ignore"):
+        share = np.where(p > 0, p / (committed + p + eps), 0.0)
+    A = share / share.sum(axis=1, keepdims=True)
+    lse = np.log(e.sum(axis=1)) + logits.max(axis=1)
+    return A @ v, A, p, share, lse
+
+
+def pin_dilution_brute_force():
+    """Oracle == whole-matrix brute force for T <= 8, many seeds, eps, tau."""
+    for seed in range(12):
+        rng = _rng(100 + seed)
+        T = 1 + seed % 8
+        d = 8
+        q = rng.standard_normal((1, 1, T, d)) * 1.5
+        k = rng.standard_normal((1, 1, T, d)) * 1.5
+        v = rng.standard_normal((1, 1, T, d))
+        for eps in (0.0, 1e-6, 0.5):
+            for tau in (1.0, oracle.yarn_tau(4.0), 2.5):
+                out, lse, dem = oracle.dilution_fwd(q, k, v, tau, eps)
+                ref, A, p, share, rlse = brute_dilution(q[0, 0], k[0, 0], v[0, 0], tau, eps)
+                assert np.max(np.abs(out[0, 0] - ref)) < 1e-12, (seed, eps, tau)
+                assert np.max(np.abs(lse[0, 0] - rlse)) < 1e-12
+                assert np.max(np.abs(dem[0, 0] - p.sum(axis=0))) < 1e-12
+
+
+def _harmonic(n):
+    return np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, n + 1))])
+
+
+def pin_dilution_uniform_closed_form():
+    """q = 0 makes every visible bid 1/(i+1).  Then committed_ij = H_i - H_j,
+    share_ij = 1 / ((i+1)(H_{i+1} - H_j + eps)), and the final demand of key j
+    is H_T - H_j (H_n the n-th harmonic number)."""
+    rng = _rng(4)
+    for T, eps in ((64, 1e-6), (300, 0.0), (97, 0.25)):
+        d = 16
+        q = np.zeros((1, 1, T, d))
+        k = rng.standard_normal((1, 1, T, d))
+        v = rng.standard_normal((1, 1, T, d))
+        out, lse, dem = oracle.dilution_fwd(q, k, v, 1.0, eps)
+        Hn = _harmonic(T + 1)
+        ref = np.empty((T, d))
+        for i in range(T):
+            j = np.arange(i + 1)
+            share = 1.0 / ((i + 1) * (Hn[i + 1] - Hn[j] + eps))
+            ref[i] = share @ v[0, 0, : i + 1] / share.sum()
+        assert np.max(np.abs(out[0, 0] - ref)) < 1e-11, (T, eps)
+        assert np.max(np.abs(dem[0, 0] - (Hn[T] - Hn[:T]))) < 1e-11
+        assert np.max(np.abs(lse[0, 0] - np.log(np.arange(1, T + 1)))) < 1e-12
+
+
+def pin_dilution_two_rows():
+    """Hand-derived T = 2 case: row 0 returns v_0; row 1 has committed (1, 0)."""
+    rng = _rng(5)
+    d = 4
+    for eps in (0.0, 1e-6, 0.3):
+        q = rng.standard_normal((1, 1, 2, d))
+        k = rng.standard_normal((1, 1, 2, d))
+        v = rng.standard_normal((1, 1, 2, d))
+        out, _, dem = oracle.dilution_fwd(q, k, v, 1.0, eps)
+        s0 = q[0, 0, 1] @ k[0, 0, 0] / 2.0
+        s1 = q[0, 0, 1] @ k[0, 0, 1] / 2.0
+        a = 1.0 / (1.0 + math.exp(s1 - s0))            # bid of query 1 on key 0
+        sh0 = a / (1.0 + a + eps)                      # key 0 already holds 1 unit
+        sh1 = (1.0 - a) / ((1.0 - a) + eps)            # key 1 is fresh
+        o1 = (sh0 * v[0, 0, 0] + sh1 * v[0, 0, 1]) / (sh0 + sh1)
+        assert np.max(np.abs(out[0, 0, 0] - v[0, 0, 0])) < 1e-15
+        assert np.max(np.abs(out[0, 0, 1] - o1)) < 1e-14
+        assert abs(dem[0, 0, 0] - (1.0 + a)) < 1e-14 and abs(dem[0, 0, 1] - (1.0 - a)) < 1e-14
+
+
+def pin_dilution_invariants():
+    """The page's invariants at a size beyond brute force (T = 60, heavy keys):
+    every query adds exactly one unit of demand (sum_j D_j = T); shares
+    renormalise (rows of A sum to one, A causal and non-negative); with eps = 0
+    every diagonal share is exactly one and no share exceeds one, so the
+    diagonal is the largest entry of each row of A; the output is a convex
+    combination of the visible values."""
+    rng = _rng(6)
+    T, d = 60, 64
+    q = rng.standard_normal((1, 2, T, d))
+    k = rng.standard_normal((1, 2, T, d))
+    k[:, :, rng.choice(T, 6, replace=False), :] *= 3.0
+    eye = np.zeros((1, 2, T, d))
+    eye[:, :, np.arange(T), np.arange(T)] = 1.0
+    for eps in (0.0, 1e-6):
+        A, _, dem = oracle.dilution_fwd(q, k, eye, 1.0, eps)
+        A = A[..., :T]
+        assert np.allclose(dem.sum(axis=-1), T, rtol=0, atol=1e-10)
+        assert np.allclose(A.sum(axis=-1), 1.0, atol=1e-13)
+        assert np.all(A >= 0.0)
+        assert np.all(np.triu(A[0, 0], 1) == 0.0) and np.all(np.triu(A[0, 1], 1) == 0.0)
+        if eps == 0.0:
+            diag = np.diagonal(A, axis1=-2, axis2=-1)
+            assert np.all(diag >= A.max(axis=-1) - 1e-15)
+    v = rng.standard_normal((1, 2, T, d))
+    out, _, _ = oracle.dilution_fwd(q, k, v, 1.0, 1e-6)
+    lo = np.minimum.accumulate(v, axis=2)
+    hi = np.maximum.accumulate(v, axis=2)
+    assert np.all(out >= lo - 1e-12) and np.all(out <= hi + 1e-12)
+    assert np.max(np.abs(out[:, :, 0] - v[:, :, 0])) < 1e-15
+
+
+def pin_dilution_subsets():
+    """Computing only some rows/heads gives exactly the full run's values."""
+    rng = _rng(7)
+    q, k, v = (rng.standard_normal((2, 2, 50, 16)) for _ in range(3))
+    full, lse, dem = oracle.dilution_fwd(q, k, v, 1.3, 1e-6)
+    part, plse, pdem = oracle.dilution_fwd(q, k, v, 1.3, 1e-6, rows=[0, 17, 49], heads=[1, 2])
+    for bh in (1, 2):
+        b, h = divmod(bh, 2)
+        assert np.array_equal(part[b, h, [0, 17, 49]], full[b, h, [0, 17, 49]])
+        assert np.array_equal(pdem[b, h], dem[b, h])
+    assert np.all(np.isnan(part[0, 0]))
+
+
+# ------------------------------------------------------------------------- decode
+
+def pin_decode_append_equals_prefill():
+    """Decoding one token at a time -- appending its key/value with zero demand --
+    reproduces the prefill rows, and the carried demand equals the prefill's
+    column totals (the page: cached decoding needs the K/V cache plus one running
+    demand total per key and head)."""
+    rng = _rng(8)
+    S, H, T, d = 1, 2, 24, 16
+    q, k, v = (rng.standard_normal((S, H, T, d)) for _ in range(3))
+    ref, _, dem = oracle.dilution_fwd(q, k, v, 1.1, 1e-6)
+    D = np.zeros((S, H, T))
+    for i in range(T):
+        o = oracle.dilution_decode_step(np.ascontiguousarray(q[:, :, i]), k, v, D, 1.1, 1e-6,
+                                        kv_len=[i + 1])
+        assert np.max(np.abs(o - ref[:, :, i])) < 1e-12, i
+    assert np.max(np.abs(D - dem)) < 1e-12
+
+
+def pin_decode_zero_demand():
+    """With no committed demand and eps = 0 every share is exactly one, so the
+    output is the plain mean of the visible values."""
+    rng = _rng(9)
+    S, H, L, d = 2, 3, 40, 8
+    q = rng.standard_normal((S, H, d))
+    kc, vc = rng.standard_normal((S, H, L, d)), rng.standard_normal((S, H, L, d))
+    D = np.zeros((S, H, L))
+    out = oracle.dilution_decode_step(q, kc, vc, D, 1.0, 0.0)
+    assert np.max(np.abs(out - vc.mean(axis=2))) < 1e-13
+    assert np.allclose(D.sum(axis=-1), 1.0, atol=1e-14)
+
+
+def pin_decode_large_demand():
+    """With a huge, equal demand M on every key, share_j ~ p_j / M, so the
+    renormalised output tends to softmax attention (library routine)."""
+    rng = _rng(10)
+    S, H, L, d = 1, 2, 30, 16
+    q = rng.standard_normal((S, H, d))
+    kc, vc = rng.standard_normal((S, H, L, d)), rng.standard_normal((S, H, L, d))
+    D = np.full((S, H, L), 1e9)
+    out = oracle.dilution_decode_step(q, kc, vc, D, 1.0, 1e-6)
+    qq = np.concatenate([np.zeros((S, H, L - 1, d)), q[:, :, None, :]], axis=2)
+    ref = _sdpa(qq, kc, vc, 1.0 / math.sqrt(d))[:, :, -1]
+    assert np.max(np.abs(out - ref)) < 1e-7
+
+
+def pin_decode_totals():
+    """Every step adds exactly one unit of demand per (sequence, head)."""
+    rng = _rng(11)
+    S, H, L, d = 2, 2, 64, 16
+    kc, vc = rng.standard_normal((S, H, L, d)), rng.standard_normal((S, H, L, d))
+    D = rng.random((S, H, L)) * 4.0
+    total0 = D.sum(axis=-1)
+    for step in range(1, 6):
+        q = rng.standard_normal((S, H, d))
+        oracle.dilution_decode_step(q, kc, vc, D, 1.0, 1e-6)
+        assert np.allclose(D.sum(axis=-1), total0 + step, rtol=0, atol=1e-11)
+
+
+def pin_bf16_widening():
+    """bf16 bit patterns are widened exactly (same results as explicit fp64)."""
+    from transformer_attention_causal_amd.workloads import bf16_round_bits, bf16_bits_to_f32
+
+    rng = _rng(12)
+    x = [bf16_round_bits(rng.standard_normal((1, 1, 20, 64))) for _ in range(3)]
+    as64 = [bf16_bits_to_f32(b).astype(np.float64) for b in x]
+    o1, l1, d1 = oracle.dilution_fwd(*(oracle.Bf16(b) for b in x), 1.0, 1e-6)
+    o2, l2, d2 = oracle.dilution_fwd(*as64, 1.0, 1e-6)
+    assert np.array_equal(o1, o2) and np.array_equal(d1, d2)
+    t1, _ = oracle.tempered_fwd(*(bf16_bits_to_f32(b) for b in x), 1.0)
+    t2, _ = oracle.tempered_fwd(*as64, 1.0)
+    assert np.array_equal(t1, t2)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

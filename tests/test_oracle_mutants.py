@@ -1,0 +1,85 @@
+"""The pins have teeth: plant one plausible mistake at a time in a copy of the
+oracle's C source (on the CPU, in a temporary directory), build it, run the
+whole pin battery against that build in a child process, and require that at
+least one pin fails (or the build crashes).  The real oracle is never touched.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+# (name, text in oracle.c, replacement)
+MUTANTS = [
+    ("share_without_current_bid", "(D[j] + p[j] + eps)", "(D[j] + eps)"),
+    ("committed_inclusive", "(D[j] + p[j] + eps)", "(D[j] + 2.0 * p[j] + eps)"),
+    ("eps_dropped", "(D[j] + p[j] + eps)", "(D[j] + p[j])"),
+    ("tau_ignored", "const double c = tau / sqrt((double)d);",
+     "const double c = 1.0 / sqrt((double)d);"),
+    ("no_sqrt_d", "const double c = tau / sqrt((double)d);", "const double c = tau;"),
+    ("diagonal_key_hidden", "const long lo = (long)(i + 1) * t / n, hi = (long)(i + 1) * (t + 1) / n;",
+     "const long lo = (long)(i) * t / n, hi = (long)(i) * (t + 1) / n;"),
+    ("bids_not_normalised", "p[j] = exp(p[j] - l);", "p[j] = exp(p[j] - M);"),
+    ("lse_wrong_sign", "const double l = M + log(Z);", "const double l = M - log(Z);"),
+    ("diagonal_bid_not_committed", "for (int j = 0; j <= i; ++j) D[j] += p[j];",
+     "for (int j = 0; j < i; ++j) D[j] += p[j];"),
+    ("shares_not_renormalised", "Oh[(size_t)i * d + e] = acc[e] / r;",
+     "Oh[(size_t)i * d + e] = acc[e];"),
+    ("value_rows_reversed", "pa[e] += share * Vh[(size_t)j * d + e];",
+     "pa[e] += share * Vh[(size_t)(i - j) * d + e];"),
+    ("value_rows_reversed_serial",
+     "            for (int e = 0; e < d; ++e) acc[e] += share * Vh[(size_t)j * d + e];",
+     "            for (int e = 0; e < d; ++e) acc[e] += share * Vh[(size_t)(i - j) * d + e];"),
+    ("tempered_value_row_off_by_one", "acc[e] += p[j] * Vh[(size_t)j * d + e];",
+     "acc[e] += p[j] * Vh[(size_t)(j > 0 ? j - 1 : 0) * d + e];"),
+    ("decode_committed_inclusive", "(Dh[j] + p[j] + eps)", "(Dh[j] + 2.0 * p[j] + eps)"),
+    ("decode_first_key_not_updated", "for (int j = 0; j < L; ++j) Dh[j] += p[j];",
+     "for (int j = 1; j < L; ++j) Dh[j] += p[j];"),
+    ("decode_updates_with_share", "for (int j = 0; j < L; ++j) Dh[j] += p[j];",
+     "for (int j = 0; j < L; ++j) Dh[j] += p[j] / (Dh[j] + p[j] + eps);"),
+    ("bf16_widening_shift", "<< 16;", "<< 15;"),
+    ("yarn_coefficient", "return 0.1 * log(s) + 1.0;", "return 0.1 * log2(s) + 1.0;"),
+]
+
+RUNNER = r"""
+import sys, traceback
+sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
+import oracle
+oracle.use_library(oracle.load_library({lib!r}))
+import pins
+failed = []
+for pin in pins.ALL_PINS:
+    try:
+        pin()
+    except Exception:
+        failed.append(pin.__name__)
+print("FAILED_PINS", len(failed), " ".join(failed))
+"""
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(name, old, new):
+    import oracle
+
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mutated = src.replace(old, new)
+    with tempfile.TemporaryDirectory() as tmp:
+        msrc = os.path.join(tmp, "oracle_mutant.c")
+        mlib = os.path.join(tmp, "liboracle_mutant.so")
+        with open(msrc, "w") as f:
+            f.write(mutated)
+        oracle.build(msrc, mlib)
+        r = subprocess.run([sys.executable, "-c", RUNNER.format(
+            root=ROOT, tests=os.path.join(ROOT, "tests"), lib=mlib)],
+            capture_output=True, text=True, timeout=300,
+            env={**os.environ, "OMP_NUM_THREADS": "4"})
+    if r.returncode != 0:
+        return  # the planted mistake crashed the battery: caught
+    line = [ln for ln in r.stdout.splitlines() if ln.startswith("FAILED_PINS")]
+    assert line, r.stdout + r.stderr
+    assert int(line[0].split()[1]) >= 1, f"no pin caught mutant {name}"
