@@ -1,0 +1,135 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) reshaped-softmax causal attention
+ * library (libattn.so).
+ *
+ * Two reshapings of causal softmax attention are provided:
+ *
+ *  ATTN_TEMPERED  o_i = sum_{j<=i} softmax_j(tau * <q_i,k_j> / sqrt(d)) v_j.
+ *                 The multiplier tau sharpens (tau > 1) or flattens the bids:
+ *                 Focal Attention ("Learning to Focus", sec. 2.1, eq.
+ *                 focal-const) divides the logits by t < 1, i.e. tau = 1/t;
+ *                 YaRN ("YaRN > Attention Temperature Scaling") multiplies the
+ *                 scores by sqrt(t) with t = 0.1 ln s + 1 (see attn_yarn_tau).
+ *
+ *  ATTN_DILUTION  DilutionAttention v0.1.0, section "The operator":
+ *                   p         = causal_softmax(tau * q k^T / sqrt(d))   (bids)
+ *                   committed = exclusive cumulative sum of p down each key
+ *                               column (demand from earlier queries)
+ *                   share     = p / (committed + p + eps)
+ *                   A         = share / rowsum(share);  out = A @ v
+ *                 The page writes the plain 1/sqrt(d) scale, i.e. tau = 1.
+ *
+ * attn_decode is the cached-decode form of dilution (same page: the ordinary
+ * key/value cache plus one running demand total per key and head).
+ *
+ * Conventions for every entry point
+ *  - Device pointers are plain HIP device addresses owned by the caller; the
+ *    library never allocates, frees or retains them.  Calls are asynchronous:
+ *    all work is enqueued on `hip_stream` (a hipStream_t; NULL = the default
+ *    stream) and the call returns once it is enqueued.  Errors raised while
+ *    kernels run surface at the caller's next synchronisation on that stream.
+ *  - Tensors are dense and row-major: [B,H,T,d] for the forward pass,
+ *    [S,H,Lcap,d] for the decode caches, with d innermost.  All device
+ *    pointers must be 16-byte aligned.
+ *  - Arithmetic: products on bf16 matrix cores with fp32 accumulation for
+ *    ATTN_BF16 storage; exponentials, scans, reciprocals and row sums in fp32.
+ *    ATTN_F32 storage runs an fp32-only path (no bf16 rounding anywhere).
+ *  - Results are deterministic: no floating-point atomics, fixed reduction
+ *    orders, bit-identical output for identical inputs.
+ *  - Return value: ATTN_OK or a negative attn_status.  Nothing is enqueued
+ *    when a call returns an error (except ATTN_EHIP, which reports a failed
+ *    launch).  The library never aborts or throws across this boundary.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_EINVAL = -1,     /* bad argument: null/misaligned pointer, size <= 0, tau/eps out of range */
+  ATTN_ENOTSUP = -2,    /* valid but unsupported: d != 64, fp32 decode, device not gfx950 */
+  ATTN_EWORKSPACE = -3, /* workspace missing or smaller than *_workspace_bytes() */
+  ATTN_EHIP = -4        /* a HIP runtime call or kernel launch failed */
+} attn_status;
+
+typedef enum { ATTN_TEMPERED = 0, ATTN_DILUTION = 1 } attn_mode;
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* Bytes of device workspace attn_fwd needs for this shape (0 for
+ * ATTN_TEMPERED).  Dilution keeps the fp32 log-sum-exp of every query row
+ * (B*H*T floats) and the demand committed before every 32-row query block on
+ * each earlier key (B*H*16*n*(n-1) floats, n = ceil(T/32)).  Returns 0 for an
+ * invalid shape. */
+size_t attn_fwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype);
+
+/* Causal attention forward pass (both modes; see top of file).
+ *   q, k, v    [B,H,T,d] device arrays of `dtype` (inputs, not modified)
+ *   out        [B,H,T,d] device array of `dtype` (output; may not alias q/k/v)
+ *   B, H, T    batch, heads, sequence length (each >= 1)
+ *   d          head dimension; only 64 is supported (else ATTN_ENOTSUP)
+ *   tau        logit multiplier, finite and >= 0 (tau = 0 gives uniform bids)
+ *   mode       ATTN_TEMPERED or ATTN_DILUTION
+ *   eps        share-denominator constant (dilution), finite and >= 0
+ *   dtype      ATTN_F32 or ATTN_BF16
+ *   workspace  device scratch of >= attn_fwd_workspace_bytes(...) bytes (may
+ *              be NULL when that is 0); contents on entry are ignored
+ *   hip_stream hipStream_t to enqueue on (NULL: default stream) */
+int attn_fwd(const void *q, const void *k, const void *v, void *out, int B, int H, int T, int d,
+             float tau, int mode, float eps, int dtype, void *workspace, size_t workspace_bytes,
+             void *hip_stream);
+
+/* attn_fwd with two optional fp32 outputs (NULL to skip either):
+ *   lse_out    [B,H,T]  natural-log log-sum-exp of each query row's tempered
+ *              logits, log sum_{j<=i} exp(tau <q_i,k_j>/sqrt(d))
+ *   demand_out [B,H,T]  dilution only: each key's final column total
+ *              sum_i p_ij -- the running demand a cached decode continues
+ *              from (DilutionAttention v0.1.0, cached decoding).  Must be
+ *              NULL in ATTN_TEMPERED mode (else ATTN_EINVAL). */
+int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, int B, int H, int T,
+                int d, float tau, int mode, float eps, int dtype, void *workspace,
+                size_t workspace_bytes, float *lse_out, float *demand_out, void *hip_stream);
+
+/* Bytes of device workspace attn_decode needs (per-(sequence,head,split)
+ * partial maxima, sums and weighted values plus one fp32 score per cached
+ * key). */
+size_t attn_decode_workspace_bytes(int S, int H, int Lcap, int d);
+
+/* One cached-decode step of dilution attention for S sequences at once.
+ *   q        [S,H,d] bf16: this step's query per (sequence, head)
+ *   kcache   [S,H,Lcap,d] bf16, vcache [S,H,Lcap,d] bf16: cached keys/values
+ *   demand   [S,H,Lcap] fp32, READ-MODIFY-WRITE: on entry the demand each key
+ *            has received from earlier queries; on return demand_j += p_j,
+ *            where p is this step's softmax bid.  The output uses the demand
+ *            as it stood on entry: share_j = p_j / (demand_j + p_j + eps).
+ *   out      [S,H,d] bf16: sum_j share_j v_j / sum_j share_j
+ *   kv_len   device int32 [S], visible keys per sequence (1..Lcap), or NULL
+ *            for Lcap everywhere.  To decode with the new token's own key, the
+ *            caller writes its k/v at index kv_len-1 and zeroes its demand.
+ *            A kv_len outside [1, Lcap] is clamped to that range on device.
+ *   tau, eps as for attn_fwd; dtype must be ATTN_BF16 (else ATTN_ENOTSUP).
+ * Consecutive steps must be ordered on one stream (each reads the demand the
+ * previous one wrote). */
+int attn_decode(const void *q, const void *kcache, const void *vcache, float *demand, void *out,
+                int S, int H, int Lcap, const int32_t *kv_len, int d, float tau, float eps,
+                int dtype, void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* YaRN attention temperature ("YaRN > Attention Temperature Scaling"):
+ * returns sqrt(t) with t = 0.1 ln(s) + 1, the multiplier for extension
+ * factor s >= 1; NaN for s < 1 or NaN. */
+double attn_yarn_tau(double s);
+
+/* Static description of a status code (never NULL). For ATTN_EHIP it names
+ * the last HIP error the library saw. */
+const char *attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

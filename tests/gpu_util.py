@@ -1,0 +1,64 @@
+"""Helpers for the GPU parity tests: move seeded host inputs to the device,
+hand the same values to the oracle, and measure the error."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from transformer_attention_causal_amd.workloads import HostInputs
+
+BF16_MAX_ABS = 2e-2   # bf16 I/O with fp32 accumulation
+BF16_REL_RMS = 1e-2
+F32_MAX_ABS = 1e-5    # fp32 path
+DEMAND_TOTAL_REL = 1e-4
+
+
+def to_device(x: np.ndarray, dtype: str):
+    import torch
+
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def oracle_view(x: np.ndarray, dtype: str):
+    return oracle.Bf16(x) if dtype == "bf16" else x
+
+
+def device_qkv(inp: HostInputs):
+    return tuple(to_device(a, inp.dtype) for a in (inp.q, inp.k, inp.v))
+
+
+def oracle_qkv(inp: HostInputs):
+    return tuple(oracle_view(a, inp.dtype) for a in (inp.q, inp.k, inp.v))
+
+
+def errors(got: np.ndarray, ref: np.ndarray):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got)), "non-finite output"
+    diff = got - ref
+    max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
+    denom = float(np.sqrt(np.sum(ref * ref)))
+    rel_rms = float(np.sqrt(np.sum(diff * diff)) / denom) if denom > 0 else 0.0
+    return max_abs, rel_rms
+
+
+def assert_close(got, ref, dtype: str, what: str = ""):
+    max_abs, rel_rms = errors(got, ref)
+    if dtype == "bf16":
+        assert max_abs <= BF16_MAX_ABS and rel_rms <= BF16_REL_RMS, \
+            f"{what}: max-abs {max_abs:.3e} rel-RMS {rel_rms:.3e}"
+    else:
+        assert max_abs <= F32_MAX_ABS, f"{what}: max-abs {max_abs:.3e}"
+    return max_abs, rel_rms
+
+
+def sample_rows(T: int, n: int, seed: int = 0):
+    """Rows spread over [0, T): both ends, tile edges and random interior rows."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, T // 2, T - 2, T - 1]
+    rows = set(r for r in fixed if 0 <= r < T)
+    rows.update(int(r) for r in rng.integers(0, T, size=max(0, n - len(rows))))
+    return np.array(sorted(rows), dtype=np.int32)

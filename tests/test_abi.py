@@ -1,0 +1,128 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments before it touches the device."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+from transformer_attention_causal_amd import binding as ab
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declarations_are_exported():
+    lib = ab.load()
+    names = declared_functions()
+    assert set(names) == set(ab.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", ab.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (attn_[a-z_]+)\b", out))
+    assert set(names) <= exported
+
+
+def test_yarn_tau_against_page_table():
+    rows = []
+    with open(os.path.join(ROOT, "tests", "golden", "yarn_temperature_table.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                s, _, st = line.split()
+                rows.append((float(s), float(st)))
+    for s, st in rows:
+        assert round(ab.attn_yarn_tau(s), 4) == st
+    assert ab.attn_yarn_tau(1.0) == 1.0
+    assert math.isnan(ab.attn_yarn_tau(0.5)) and math.isnan(ab.attn_yarn_tau(float("nan")))
+
+
+def test_strerror_is_static_text():
+    for st in (0, -1, -2, -3, -4, 7):
+        assert isinstance(ab.attn_strerror(st), str) and ab.attn_strerror(st)
+
+
+def fwd(**kw):
+    args = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, out=FAKE + 0x3000000, B=1, H=1,
+                T=16, d=64, tau=1.0, mode=0, eps=1e-6, dtype=1, workspace=None,
+                workspace_bytes=0, lse_out=None, demand_out=None, hip_stream=None)
+    args.update(kw)
+    return ab.attn_fwd_ex(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ab.ATTN_EINVAL),
+    (dict(out=None), ab.ATTN_EINVAL),
+    (dict(q=FAKE + 2), ab.ATTN_EINVAL),              # misaligned
+    (dict(B=0), ab.ATTN_EINVAL),
+    (dict(T=-3), ab.ATTN_EINVAL),
+    (dict(mode=2), ab.ATTN_EINVAL),
+    (dict(dtype=5), ab.ATTN_EINVAL),
+    (dict(tau=-1.0), ab.ATTN_EINVAL),
+    (dict(tau=float("nan")), ab.ATTN_EINVAL),
+    (dict(tau=float("inf")), ab.ATTN_EINVAL),
+    (dict(eps=-1e-6), ab.ATTN_EINVAL),
+    (dict(eps=float("nan")), ab.ATTN_EINVAL),
+    (dict(out=FAKE), ab.ATTN_EINVAL),                # out aliases q
+    (dict(demand_out=FAKE + 0x4000000), ab.ATTN_EINVAL),  # demand_out in tempered mode
+    (dict(d=128), ab.ATTN_ENOTSUP),
+    (dict(mode=1), ab.ATTN_EWORKSPACE),              # dilution without workspace
+    (dict(mode=1, workspace=FAKE + 0x5000000, workspace_bytes=16), ab.ATTN_EWORKSPACE),
+])
+def test_fwd_rejects_bad_arguments(kw, status):
+    assert fwd(**kw) == status
+
+
+def test_workspace_sizes():
+    # tempered needs none; dilution keeps lse (B*H*T) + committed demand
+    assert ab.attn_fwd_workspace_bytes(1, 16, 16384, 64, 0, 1) == 0
+    n = 16384 // 32
+    want = 16 * 16384 * 4 + 16 * 16 * n * (n - 1) * 4
+    got = ab.attn_fwd_workspace_bytes(1, 16, 16384, 64, 1, 1)
+    assert want <= got <= want + 512
+    assert ab.attn_fwd_workspace_bytes(1, 1, 16, 128, 1, 1) == 0
+    assert ab.attn_fwd_workspace_bytes(0, 1, 16, 64, 1, 1) == 0
+    assert ab.attn_decode_workspace_bytes(64, 16, 32768, 64) >= 64 * 16 * 32768 * 4
+    assert ab.attn_decode_workspace_bytes(64, 16, 32768, 32) == 0
+
+
+def dec(**kw):
+    args = dict(q=FAKE, kcache=FAKE + 0x1000000, vcache=FAKE + 0x20000000,
+                demand=FAKE + 0x40000000, out=FAKE + 0x60000000, S=2, H=2, Lcap=100,
+                kv_len=None, d=64, tau=1.0, eps=1e-6, dtype=1, workspace=None,
+                workspace_bytes=0, hip_stream=None)
+    args.update(kw)
+    return ab.attn_decode(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(demand=None), ab.ATTN_EINVAL),
+    (dict(kcache=FAKE + 8), ab.ATTN_EINVAL),
+    (dict(S=0), ab.ATTN_EINVAL),
+    (dict(Lcap=0), ab.ATTN_EINVAL),
+    (dict(tau=-0.5), ab.ATTN_EINVAL),
+    (dict(eps=float("inf")), ab.ATTN_EINVAL),
+    (dict(dtype=0), ab.ATTN_ENOTSUP),                # fp32 decode
+    (dict(d=128), ab.ATTN_ENOTSUP),
+    (dict(out=FAKE + 0x1000000), ab.ATTN_EINVAL),     # out inside the K cache
+    (dict(), ab.ATTN_EWORKSPACE),
+])
+def test_decode_rejects_bad_arguments(kw, status):
+    assert dec(**kw) == status
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(ab, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(ab, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        ab.load()

@@ -1,0 +1,189 @@
+"""GPU parity of the forward pass (tempered and dilution) against the fp64
+oracle, through the C ABI.  Every input is seeded and synthetic; the oracle
+receives the exact values the device receives."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import (DEMAND_TOTAL_REL, assert_close, device_qkv, errors, oracle_qkv,
+                      sample_rows)
+from transformer_attention_causal_amd import binding as ab
+from transformer_attention_causal_amd.workloads import PREFILL, draw_qkv, prefill_inputs
+
+pytestmark = pytest.mark.gpu
+
+TAU4 = math.sqrt(0.1 * math.log(4.0) + 1.0)   # YaRN multiplier for 4x extension
+TAU8 = math.sqrt(0.1 * math.log(8.0) + 1.0)   # and for 8x
+
+
+def run_fwd(inp, tau, mode, eps=1e-6, want_lse=False, want_demand=False):
+    import torch
+
+    q, k, v = device_qkv(inp)
+    B, H, T, _ = q.shape
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda") if want_lse else None
+    dem = torch.empty((B, H, T), dtype=torch.float32, device="cuda") if want_demand else None
+    out = ab.fwd(q, k, v, tau=tau, mode=mode, eps=eps, lse_out=lse, demand_out=dem)
+    torch.cuda.synchronize()
+    res = [out.float().cpu().numpy()]
+    if want_lse:
+        res.append(lse.cpu().numpy())
+    if want_demand:
+        res.append(dem.cpu().numpy())
+    return res if len(res) > 1 else res[0]
+
+
+# ------------------------------------------------------------------ fp32 path
+
+@pytest.mark.parametrize("tau", [1.0, TAU4, 2.5, 0.0])
+def test_fp32_tempered_matches_oracle(tau):
+    w = PREFILL["fp32_t256"]
+    inp = prefill_inputs(w)
+    out, lse = run_fwd(inp, tau, ab.ATTN_TEMPERED, want_lse=True)
+    ref, rlse = oracle.tempered_fwd(*oracle_qkv(inp), tau)
+    assert_close(out, ref, "f32", f"tempered tau={tau}")
+    assert np.max(np.abs(lse - rlse)) <= 1e-5
+
+
+@pytest.mark.parametrize("tau,eps", [(1.0, 1e-6), (TAU4, 1e-6), (1.0, 0.0), (1.0, 0.5)])
+def test_fp32_dilution_matches_oracle(tau, eps):
+    w = PREFILL["fp32_t256"]
+    inp = prefill_inputs(w)
+    out, lse, dem = run_fwd(inp, tau, ab.ATTN_DILUTION, eps, want_lse=True, want_demand=True)
+    ref, rlse, rdem = oracle.dilution_fwd(*oracle_qkv(inp), tau, eps)
+    assert_close(out, ref, "f32", f"dilution tau={tau} eps={eps}")
+    assert np.max(np.abs(lse - rlse)) <= 1e-5
+    assert np.max(np.abs(dem - rdem) / np.maximum(1.0, np.abs(rdem))) <= 1e-5
+
+
+@pytest.mark.parametrize("T", [1, 7, 31, 33, 100, 257])
+def test_fp32_ragged_lengths(T):
+    inp = draw_qkv(2, 2, T, 64, "f32", seed=900 + T)
+    for mode in (ab.ATTN_TEMPERED, ab.ATTN_DILUTION):
+        out = run_fwd(inp, 1.3, mode)
+        if mode == ab.ATTN_TEMPERED:
+            ref, _ = oracle.tempered_fwd(*oracle_qkv(inp), 1.3)
+        else:
+            ref, _, _ = oracle.dilution_fwd(*oracle_qkv(inp), 1.3, 1e-6)
+        assert_close(out, ref, "f32", f"T={T} mode={mode}")
+
+
+# ------------------------------------------------------------------ bf16 path
+
+@pytest.mark.parametrize("T", [1, 7, 32, 33, 64, 127, 129, 257, 300, 1000])
+def test_bf16_ragged_lengths_tempered(T):
+    inp = draw_qkv(2, 3, T, 64, "bf16", seed=1000 + T, heavy_frac=0.05)
+    out, lse = run_fwd(inp, TAU4, ab.ATTN_TEMPERED, want_lse=True)
+    ref, rlse = oracle.tempered_fwd(*oracle_qkv(inp), TAU4)
+    assert_close(out, ref, "bf16", f"tempered T={T}")
+    assert np.max(np.abs(lse - rlse)) <= 2e-3
+
+
+@pytest.mark.parametrize("T", [1, 7, 32, 33, 64, 127, 129, 257, 300, 1000])
+def test_bf16_ragged_lengths_dilution(T):
+    inp = draw_qkv(2, 3, T, 64, "bf16", seed=2000 + T, heavy_frac=0.05)
+    out, lse, dem = run_fwd(inp, 1.0, ab.ATTN_DILUTION, 1e-6, want_lse=True, want_demand=True)
+    ref, rlse, rdem = oracle.dilution_fwd(*oracle_qkv(inp), 1.0, 1e-6)
+    assert_close(out, ref, "bf16", f"dilution T={T}")
+    assert np.max(np.abs(lse - rlse)) <= 2e-3
+    # every query adds one unit of demand: totals are T per head
+    assert np.max(np.abs(dem.sum(axis=-1) / T - 1.0)) <= DEMAND_TOTAL_REL
+    assert np.max(np.abs(dem - rdem)) <= 2e-2 * max(1.0, float(np.max(rdem)))
+
+
+@pytest.mark.parametrize("tau,eps", [(0.0, 1e-6), (2.5, 1e-6), (TAU4, 0.0), (1.0, 0.3)])
+def test_bf16_dilution_tau_eps(tau, eps):
+    inp = draw_qkv(1, 2, 300, 64, "bf16", seed=3000, heavy_frac=0.05)
+    out = run_fwd(inp, tau, ab.ATTN_DILUTION, eps)
+    ref, _, _ = oracle.dilution_fwd(*oracle_qkv(inp), tau, eps)
+    assert_close(out, ref, "bf16", f"dilution tau={tau} eps={eps}")
+
+
+def test_bf16_tempered_tau_zero_is_prefix_mean():
+    inp = draw_qkv(1, 2, 200, 64, "bf16", seed=3100)
+    out = run_fwd(inp, 0.0, ab.ATTN_TEMPERED)
+    ref, _ = oracle.tempered_fwd(*oracle_qkv(inp), 0.0)
+    assert_close(out, ref, "bf16", "tempered tau=0")
+
+
+def test_softmax_t2048_workload():
+    """Tempered, bf16 I/O: B=4, H=16, T=2048, Q,K,V ~ N(0,1)/sqrt(2), tau = YaRN(s=4)."""
+    w = PREFILL["softmax_t2048"]
+    inp = prefill_inputs(w)
+    out = run_fwd(inp, TAU4, ab.ATTN_TEMPERED)
+    ref, _ = oracle.tempered_fwd(*oracle_qkv(inp), TAU4)
+    print("softmax_t2048 max-abs %.3e rel-RMS %.3e" % errors(out, ref))
+    assert_close(out, ref, "bf16", "softmax_t2048")
+
+
+def test_dilution_t16k_workload():
+    """Dilution (eps=1e-6, tau=1) and tempered (tau=YaRN(4)) at T=16384, H=16,
+    5% heavy keys; sampled rows of every head against the oracle, plus the
+    per-head demand totals."""
+    w = PREFILL["dilution_t16k"]
+    inp = prefill_inputs(w)
+    rows = sample_rows(w.T, 48, seed=16)
+    out, dem = run_fwd(inp, 1.0, ab.ATTN_DILUTION, w.eps, want_demand=True)
+    ref, _, rdem = oracle.dilution_fwd(*oracle_qkv(inp), 1.0, w.eps, rows=rows)
+    ma, rr = assert_close(out[:, :, rows], ref[:, :, rows], "bf16", "dilution_t16k")
+    print(f"dilution_t16k max-abs {ma:.3e} rel-RMS {rr:.3e}")
+    assert np.max(np.abs(dem.sum(axis=-1) / w.T - 1.0)) <= DEMAND_TOTAL_REL
+    assert np.max(np.abs(dem - rdem) / np.maximum(1.0, rdem)) <= 2e-2
+    out_t = run_fwd(inp, TAU4, ab.ATTN_TEMPERED)
+    ref_t, _ = oracle.tempered_fwd(*oracle_qkv(inp), TAU4, rows=rows)
+    assert_close(out_t[:, :, rows], ref_t[:, :, rows], "bf16", "tempered_t16k")
+
+
+@pytest.mark.timeout(900)
+def test_long_t128k_workload_head0():
+    """T=131072, H=16 (8x the training context): all heads run on the device,
+    head 0 is checked against the oracle on sampled rows (dilution, tau=1) and
+    the tempered run (tau = YaRN(8)); every head's demand totals are checked."""
+    import torch
+
+    w = PREFILL["long_t128k"]
+    inp = prefill_inputs(w)
+    rows = sample_rows(w.T, 24, seed=128)
+    out, dem = run_fwd(inp, 1.0, ab.ATTN_DILUTION, w.eps, want_demand=True)
+    torch.cuda.empty_cache()
+    assert np.max(np.abs(dem.sum(axis=-1) / w.T - 1.0)) <= DEMAND_TOTAL_REL
+    head0 = [oracle.Bf16(np.ascontiguousarray(x[:, :1])) for x in (inp.q, inp.k, inp.v)]
+    ref, _, _ = oracle.dilution_fwd(*head0, 1.0, w.eps, rows=rows)
+    ma, rr = assert_close(out[:, :1, rows], ref[:, :, rows], "bf16", "dilution_t128k head 0")
+    print(f"dilution_t128k head0 max-abs {ma:.3e} rel-RMS {rr:.3e}")
+    out_t = run_fwd(inp, TAU8, ab.ATTN_TEMPERED)
+    ref_t, _ = oracle.tempered_fwd(*head0, TAU8, rows=rows)
+    assert_close(out_t[:, :1, rows], ref_t[:, :, rows], "bf16", "tempered_t128k head 0")
+
+
+def test_deterministic():
+    import torch
+
+    inp = draw_qkv(1, 4, 777, 64, "bf16", seed=4000, heavy_frac=0.05)
+    q, k, v = device_qkv(inp)
+    for mode in (ab.ATTN_TEMPERED, ab.ATTN_DILUTION):
+        a = ab.fwd(q, k, v, tau=1.0, mode=mode)
+        b = ab.fwd(q, k, v, tau=1.0, mode=mode)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+
+
+def test_dilution_rows_sum_to_one_via_identity_values():
+    """With V = I (T <= 64) the output rows are the attention rows A: they sum
+    to one and vanish above the diagonal (bf16 rounding of A aside)."""
+    import torch
+
+    T = 64
+    inp = draw_qkv(1, 1, T, 64, "bf16", seed=4100, heavy_frac=0.05)
+    eye = np.zeros((1, 1, T, 64), dtype=np.float32)
+    eye[0, 0, np.arange(T), np.arange(T)] = 1.0
+    from transformer_attention_causal_amd.workloads import bf16_round_bits
+
+    inp.v = bf16_round_bits(eye)
+    A = run_fwd(inp, 1.0, ab.ATTN_DILUTION)[0, 0]
+    assert np.all(np.abs(A.sum(axis=1) - 1.0) <= 1e-2)
+    assert np.all(np.triu(A, 1) == 0.0)
+    assert np.all(A >= 0.0)
+    torch.cuda.synchronize()

@@ -1,0 +1,194 @@
+"""Thin Python binding of libattn.so (argument marshalling only).
+
+The functions named like the C ABI (``attn_fwd``, ``attn_fwd_ex``,
+``attn_decode``, ``attn_fwd_workspace_bytes``, ``attn_decode_workspace_bytes``,
+``attn_yarn_tau``, ``attn_strerror``) take exactly the C arguments, with device
+pointers as Python ints.  ``fwd`` and ``decode`` accept torch tensors, check
+their shapes/dtypes, allocate the output and workspace with torch, pass the
+current torch stream, and raise ``AttnError`` on a non-zero status.  Every step
+of the computation runs in the library's HIP kernels; nothing here computes.
+
+The library must have been built (``transformer_attention_causal_amd.build``);
+there is no fallback: a missing library raises at first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libattn.so")
+
+ATTN_OK, ATTN_EINVAL, ATTN_ENOTSUP, ATTN_EWORKSPACE, ATTN_EHIP = 0, -1, -2, -3, -4
+ATTN_TEMPERED, ATTN_DILUTION = 0, 1
+ATTN_F32, ATTN_BF16 = 0, 1
+
+EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_bytes", "attn_decode",
+            "attn_decode_workspace_bytes", "attn_yarn_tau", "attn_strerror")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {attn_strerror(status)} (status {status})")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Open libattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m transformer_attention_causal_amd.build` (no fallback path exists)")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.attn_fwd.restype = i
+        lib.attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, f, i, vp, sz, vp]
+        lib.attn_fwd_ex.restype = i
+        lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, f, i, vp, sz, vp, vp, vp]
+        lib.attn_fwd_workspace_bytes.restype = sz
+        lib.attn_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        lib.attn_decode.restype = i
+        lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, vp, i, f, f, i, vp, sz, vp]
+        lib.attn_decode_workspace_bytes.restype = sz
+        lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
+        lib.attn_yarn_tau.restype = ctypes.c_double
+        lib.attn_yarn_tau.argtypes = [ctypes.c_double]
+        lib.attn_strerror.restype = ctypes.c_char_p
+        lib.attn_strerror.argtypes = [i]
+        _lib = lib
+    return _lib
+
+
+# ------------------------------------------------------------- raw C ABI names
+
+def attn_fwd(q, k, v, out, B, H, T, d, tau, mode, eps, dtype, workspace, workspace_bytes,
+             hip_stream) -> int:
+    return load().attn_fwd(q, k, v, out, B, H, T, d, tau, mode, eps, dtype, workspace,
+                           workspace_bytes, hip_stream)
+
+
+def attn_fwd_ex(q, k, v, out, B, H, T, d, tau, mode, eps, dtype, workspace, workspace_bytes,
+                lse_out, demand_out, hip_stream) -> int:
+    return load().attn_fwd_ex(q, k, v, out, B, H, T, d, tau, mode, eps, dtype, workspace,
+                              workspace_bytes, lse_out, demand_out, hip_stream)
+
+
+def attn_fwd_workspace_bytes(B, H, T, d, mode, dtype) -> int:
+    return int(load().attn_fwd_workspace_bytes(B, H, T, d, mode, dtype))
+
+
+def attn_decode(q, kcache, vcache, demand, out, S, H, Lcap, kv_len, d, tau, eps, dtype,
+                workspace, workspace_bytes, hip_stream) -> int:
+    return load().attn_decode(q, kcache, vcache, demand, out, S, H, Lcap, kv_len, d, tau, eps,
+                              dtype, workspace, workspace_bytes, hip_stream)
+
+
+def attn_decode_workspace_bytes(S, H, Lcap, d) -> int:
+    return int(load().attn_decode_workspace_bytes(S, H, Lcap, d))
+
+
+def attn_yarn_tau(s: float) -> float:
+    return float(load().attn_yarn_tau(float(s)))
+
+
+def attn_strerror(status: int) -> str:
+    return load().attn_strerror(int(status)).decode()
+
+
+# ------------------------------------------------------------ torch marshalling
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream_handle(device):
+    import torch
+
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def fwd_workspace(B, H, T, mode, dtype_code, device):
+    import torch
+
+    n = attn_fwd_workspace_bytes(B, H, T, 64, mode, dtype_code)
+    if n == 0:
+        return None, 0
+    return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
+def fwd(q, k, v, tau: float = 1.0, mode: int = ATTN_TEMPERED, eps: float = 1e-6,
+        out=None, workspace=None, lse_out=None, demand_out=None):
+    """Run attn_fwd_ex on [B,H,T,64] tensors; returns ``out``."""
+    import torch
+
+    if not (q.shape == k.shape == v.shape) or q.dim() != 4:
+        raise ValueError("q, k, v must share one [B,H,T,d] shape")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, T, d = q.shape
+    code = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    ws_bytes = 0
+    if workspace is None:
+        workspace, ws_bytes = fwd_workspace(B, H, T, mode, code, q.device)
+    else:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, T, d,
+                     float(tau), int(mode), float(eps), code,
+                     workspace.data_ptr() if workspace is not None else None, ws_bytes,
+                     lse_out.data_ptr() if lse_out is not None else None,
+                     demand_out.data_ptr() if demand_out is not None else None,
+                     _stream_handle(q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_ex")
+    return out
+
+
+def decode_workspace(S, H, Lcap, device):
+    import torch
+
+    n = attn_decode_workspace_bytes(S, H, Lcap, 64)
+    return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
+def decode(q, kcache, vcache, demand, tau: float = 1.0, eps: float = 1e-6, kv_len=None,
+           out=None, workspace=None):
+    """Run one attn_decode step; ``demand`` is updated in place.  Returns ``out``."""
+    import torch
+
+    S, H, Lcap, d = kcache.shape
+    if vcache.shape != kcache.shape or q.shape != (S, H, d) or demand.shape != (S, H, Lcap):
+        raise ValueError("decode shapes must be q [S,H,d], caches [S,H,L,d], demand [S,H,L]")
+    if demand.dtype != torch.float32:
+        raise TypeError("demand must be float32")
+    for t in (q, kcache, vcache, demand):
+        if not t.is_contiguous():
+            raise ValueError("decode tensors must be contiguous")
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace, ws_bytes = decode_workspace(S, H, Lcap, q.device)
+    else:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    if kv_len is not None and (kv_len.dtype != torch.int32 or kv_len.numel() != S):
+        raise ValueError("kv_len must be an int32 device tensor of length S")
+    st = attn_decode(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), demand.data_ptr(),
+                     out.data_ptr(), S, H, Lcap,
+                     kv_len.data_ptr() if kv_len is not None else None, d, float(tau),
+                     float(eps), _dtype_code(q), workspace.data_ptr(), ws_bytes,
+                     _stream_handle(q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode")
+    return out

@@ -1,0 +1,262 @@
+// api.cpp -- the extern "C" boundary of libattn.so (declared in include/attn.h).
+//
+// Validates arguments on the host, sizes and carves the caller's workspace,
+// and enqueues the kernels on the caller's stream.  Nothing here allocates
+// device memory, synchronises, throws or aborts.
+#include "../../include/attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_hip_error[160] = "no HIP error recorded";
+
+int fail_hip(hipError_t e) {
+  std::snprintf(g_hip_error, sizeof g_hip_error, "HIP error: %s", hipGetErrorString(e));
+  return ATTN_EHIP;
+}
+
+// gfx950 check, once per device.
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+int g_dev_ok[kMaxDevices];
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e);
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_ENOTSUP;
+  std::call_once(g_dev_once[dev], [dev] {
+    hipDeviceProp_t prop;
+    g_dev_ok[dev] = (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+                     std::strncmp(prop.gcnArchName, "gfx950", 6) == 0)
+                        ? 1
+                        : 0;
+  });
+  return g_dev_ok[dev] ? ATTN_OK : ATTN_ENOTSUP;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Do [a, a+na) and [b, b+nb) share a byte?
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace layout of a dilution forward: [lse2: BH*T][committed demand].
+struct FwdWorkspace {
+  size_t lse_bytes, cin_bytes, total;
+};
+
+bool fwd_workspace(int B, int H, int T, FwdWorkspace *ws) {
+  const size_t BH = (size_t)B * H;
+  if (BH > (size_t)INT32_MAX) return false;
+  ws->lse_bytes = round_up(BH * (size_t)T * sizeof(float));
+  ws->cin_bytes = round_up(BH * attn::cin_floats_per_head(T) * sizeof(float));
+  ws->total = ws->lse_bytes + ws->cin_bytes;
+  return true;
+}
+
+// Decode: chunk of keys per workgroup.
+constexpr int kDecChunk = 2048;
+
+struct DecWorkspace {
+  int splits;
+  size_t scores_bytes, ml_bytes, o_bytes, total;
+};
+
+bool dec_workspace(int S, int H, int Lcap, DecWorkspace *ws) {
+  const size_t SH = (size_t)S * H;
+  if (SH > (size_t)INT32_MAX) return false;
+  ws->splits = (Lcap + kDecChunk - 1) / kDecChunk;
+  if (SH * (size_t)ws->splits > (size_t)INT32_MAX) return false;
+  ws->scores_bytes = round_up(SH * (size_t)Lcap * sizeof(float));
+  ws->ml_bytes = round_up(SH * ws->splits * 2 * sizeof(float));
+  ws->o_bytes = round_up(SH * ws->splits * (attn::kHeadDim + 1) * sizeof(float));
+  ws->total = ws->scores_bytes + ws->ml_bytes + ws->o_bytes;
+  return true;
+}
+
+bool shape_ok(int B, int H, int T) {
+  if (B <= 0 || H <= 0 || T <= 0) return false;
+  // element counts must fit the kernels' 64-bit offsets and 32-bit grids
+  const size_t BH = (size_t)B * H;
+  if (BH > (size_t)INT32_MAX / 1024) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_fwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype) {
+  if (!shape_ok(B, H, T) || d != attn::kHeadDim) return 0;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
+  if (mode != ATTN_DILUTION) return 0;
+  FwdWorkspace ws;
+  if (!fwd_workspace(B, H, T, &ws)) return 0;
+  return ws.total;
+}
+
+int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, int B, int H, int T,
+                int d, float tau, int mode, float eps, int dtype, void *workspace,
+                size_t workspace_bytes, float *lse_out, float *demand_out, void *hip_stream) {
+  if (!q || !k || !v || !out) return ATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_EINVAL;
+  if (!shape_ok(B, H, T)) return ATTN_EINVAL;
+  if (mode != ATTN_TEMPERED && mode != ATTN_DILUTION) return ATTN_EINVAL;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EINVAL;
+  if (!std::isfinite(tau) || tau < 0.0f) return ATTN_EINVAL;
+  if (!std::isfinite(eps) || eps < 0.0f) return ATTN_EINVAL;
+  if (mode == ATTN_TEMPERED && demand_out) return ATTN_EINVAL;
+  if (d != attn::kHeadDim) return ATTN_ENOTSUP;
+  const size_t esz = dtype == ATTN_BF16 ? 2 : 4;
+  const size_t nbytes = (size_t)B * H * (size_t)T * d * esz;
+  if (overlaps(out, nbytes, q, nbytes) || overlaps(out, nbytes, k, nbytes) ||
+      overlaps(out, nbytes, v, nbytes))
+    return ATTN_EINVAL;
+  // the optional [B,H,T] fp32 outputs may not alias any tensor argument or each other
+  const size_t rbytes = (size_t)B * H * (size_t)T * sizeof(float);
+  for (const void *r : {static_cast<const void *>(lse_out), static_cast<const void *>(demand_out)}) {
+    if (!r) continue;
+    if (!aligned16(r)) return ATTN_EINVAL;
+    if (overlaps(r, rbytes, q, nbytes) || overlaps(r, rbytes, k, nbytes) ||
+        overlaps(r, rbytes, v, nbytes) || overlaps(r, rbytes, out, nbytes))
+      return ATTN_EINVAL;
+  }
+  if (lse_out && demand_out && overlaps(lse_out, rbytes, demand_out, rbytes)) return ATTN_EINVAL;
+
+  FwdWorkspace ws{0, 0, 0};
+  if (mode == ATTN_DILUTION) {
+    if (!fwd_workspace(B, H, T, &ws)) return ATTN_EINVAL;
+    if (!workspace || workspace_bytes < ws.total || !aligned16(workspace)) return ATTN_EWORKSPACE;
+  }
+  const int dev_status = check_device();
+  if (dev_status != ATTN_OK) return dev_status;
+
+  attn::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse_nat = lse_out;
+  a.demand_out = demand_out;
+  a.BH = B * H;
+  a.T = T;
+  a.c2 = (float)((double)tau / std::sqrt((double)d) * 1.4426950408889634);
+  a.eps = eps;
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  hipError_t e;
+  const bool bf16 = dtype == ATTN_BF16;
+  if (mode == ATTN_TEMPERED) {
+    a.lse2 = nullptr;
+    e = bf16 ? attn::launch_rows_bf16(attn::kRowTempered, a, s)
+             : attn::launch_rows_f32(attn::kRowTempered, a, s);
+    return e == hipSuccess ? ATTN_OK : fail_hip(e);
+  }
+  char *wsp = static_cast<char *>(workspace);
+  a.lse2 = reinterpret_cast<float *>(wsp);
+  a.cin = reinterpret_cast<float *>(wsp + ws.lse_bytes);
+  // pass 1: row log-sum-exp (also the optional natural-log output)
+  e = bf16 ? attn::launch_rows_bf16(attn::kRowLse, a, s) : attn::launch_rows_f32(attn::kRowLse, a, s);
+  if (e != hipSuccess) return fail_hip(e);
+  a.lse_nat = nullptr;
+  // pass 2a: demand committed before each 32-row query block
+  e = bf16 ? attn::launch_colsum_bf16(a, s) : attn::launch_colsum_f32(a, s);
+  if (e != hipSuccess) return fail_hip(e);
+  a.demand_out = nullptr;
+  // pass 2b: shares, share@V, renormalisation
+  e = bf16 ? attn::launch_rows_bf16(attn::kRowShare, a, s) : attn::launch_rows_f32(attn::kRowShare, a, s);
+  return e == hipSuccess ? ATTN_OK : fail_hip(e);
+}
+
+int attn_fwd(const void *q, const void *k, const void *v, void *out, int B, int H, int T, int d,
+             float tau, int mode, float eps, int dtype, void *workspace, size_t workspace_bytes,
+             void *hip_stream) {
+  return attn_fwd_ex(q, k, v, out, B, H, T, d, tau, mode, eps, dtype, workspace, workspace_bytes,
+                     nullptr, nullptr, hip_stream);
+}
+
+size_t attn_decode_workspace_bytes(int S, int H, int Lcap, int d) {
+  if (S <= 0 || H <= 0 || Lcap <= 0 || d != attn::kHeadDim) return 0;
+  DecWorkspace ws;
+  if (!dec_workspace(S, H, Lcap, &ws)) return 0;
+  return ws.total;
+}
+
+int attn_decode(const void *q, const void *kcache, const void *vcache, float *demand, void *out,
+                int S, int H, int Lcap, const int32_t *kv_len, int d, float tau, float eps,
+                int dtype, void *workspace, size_t workspace_bytes, void *hip_stream) {
+  if (!q || !kcache || !vcache || !demand || !out) return ATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(demand) ||
+      !aligned16(out))
+    return ATTN_EINVAL;
+  if (S <= 0 || H <= 0 || Lcap <= 0) return ATTN_EINVAL;
+  if (!std::isfinite(tau) || tau < 0.0f) return ATTN_EINVAL;
+  if (!std::isfinite(eps) || eps < 0.0f) return ATTN_EINVAL;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EINVAL;
+  if (d != attn::kHeadDim || dtype != ATTN_BF16) return ATTN_ENOTSUP;
+  DecWorkspace ws;
+  if (!dec_workspace(S, H, Lcap, &ws)) return ATTN_EINVAL;
+  const size_t cache_bytes = (size_t)S * H * (size_t)Lcap * d * 2;
+  const size_t out_bytes = (size_t)S * H * d * 2;
+  const size_t dem_bytes = (size_t)S * H * (size_t)Lcap * 4;
+  if (overlaps(out, out_bytes, kcache, cache_bytes) || overlaps(out, out_bytes, vcache, cache_bytes) ||
+      overlaps(out, out_bytes, demand, dem_bytes) || overlaps(out, out_bytes, q, out_bytes) ||
+      overlaps(demand, dem_bytes, kcache, cache_bytes) ||
+      overlaps(demand, dem_bytes, vcache, cache_bytes) || overlaps(demand, dem_bytes, q, out_bytes))
+    return ATTN_EINVAL;
+  if (!workspace || workspace_bytes < ws.total || !aligned16(workspace)) return ATTN_EWORKSPACE;
+  const int dev_status = check_device();
+  if (dev_status != ATTN_OK) return dev_status;
+
+  attn::DecodeArgs a{};
+  a.q = q;
+  a.kc = kcache;
+  a.vc = vcache;
+  a.demand = demand;
+  a.out = out;
+  a.kv_len = kv_len;
+  a.S = S;
+  a.H = H;
+  a.Lcap = Lcap;
+  a.splits = ws.splits;
+  a.chunk = kDecChunk;
+  a.c2 = (float)((double)tau / std::sqrt((double)d) * 1.4426950408889634);
+  a.eps = eps;
+  char *wsp = static_cast<char *>(workspace);
+  a.scores = reinterpret_cast<float *>(wsp);
+  a.part_ml = reinterpret_cast<float *>(wsp + ws.scores_bytes);
+  a.part_o = reinterpret_cast<float *>(wsp + ws.scores_bytes + ws.ml_bytes);
+  hipError_t e = attn::launch_decode(a, reinterpret_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? ATTN_OK : fail_hip(e);
+}
+
+double attn_yarn_tau(double s) {
+  if (!(s >= 1.0)) return std::nan("");
+  return std::sqrt(0.1 * std::log(s) + 1.0);
+}
+
+const char *attn_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_EINVAL: return "invalid argument";
+    case ATTN_ENOTSUP: return "unsupported (head dim must be 64, decode needs bf16, device must be gfx950)";
+    case ATTN_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case ATTN_EHIP: return g_hip_error;
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// attn_common.hpp -- device helpers shared by the gfx950 attention kernels.
+//
+// Matrix-core layout facts used throughout (v_mfma_f32_32x32x16_bf16, one
+// wave64; h = lane / 32):
+//   A operand (32 x 16): lane holds A[lane % 32][8h + e], e = 0..7
+//   B operand (16 x 32): lane holds B[8h + e][lane % 32]
+//   C/D       (32 x 32): lane holds D[8 (r / 4) + 4h + (r % 4)][lane % 32], r = 0..15
+// Only the pairing of A's and B's reduction index matters for a product, so a
+// kernel may assign any physical index to the logical slot (h, e) as long as
+// both operands use the same assignment.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.hpp"
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kSub = 32;  // rows of one query sub-block = side of one MFMA output tile
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+  return z;
+}
+
+// Round-to-nearest-even fp32 -> bf16 of two values, packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Eight fp32 values -> one bf16x8 operand (element e from v[e]).
+__device__ __forceinline__ bf16x8 to_bf16x8(float v0, float v1, float v2, float v3, float v4,
+                                            float v5, float v6, float v7) {
+  u32x4 u;
+  u[0] = pack_bf16x2(v0, v1);
+  u[1] = pack_bf16x2(v2, v3);
+  u[2] = pack_bf16x2(v4, v5);
+  u[3] = pack_bf16x2(v6, v7);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Exchange a value with the lane 32 positions away (the other half of the wave).
+__device__ __forceinline__ float swap_halves(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+}  // namespace attn

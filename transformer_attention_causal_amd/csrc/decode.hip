@@ -1,0 +1,222 @@
+// decode.hip -- cached-decode step of dilution attention for gfx950.
+//
+// "DilutionAttention v0.1.0 - results", "The operator": cached decoding needs
+// the ordinary key/value cache plus one running demand total per key and
+// head.  For one new query per (sequence, head) over L cached keys:
+//   s_j = tau <q,k_j> / sqrt(d),  p = softmax(s),
+//   share_j = p_j / (D_j + p_j + eps),  out = sum_j share_j v_j / sum_j share_j,
+//   then D_j += p_j in place (the bid, not the share).
+//
+// The step streams K once and V once, so it is bound by HBM bandwidth.  Keys
+// of a (sequence, head) are split into chunks, one workgroup each:
+//   dec_scores   : s_j (kept in fp32 scratch) and a partial (max, sum exp)
+//   dec_share_v  : global log-sum-exp from the partials, p_j, share_j, the
+//                  in-place demand update, and partial (sum share v, sum share)
+//   dec_combine  : out = sum of partial numerators / sum of partial row sums
+// Loads are 16 bytes per lane; eight lanes cover one 128-byte key row, so one
+// wave instruction reads eight consecutive rows (1 KB, fully coalesced).
+#include "attn_common.hpp"
+#include "launch.hpp"
+
+#include <float.h>
+
+namespace attn {
+
+constexpr int kDecThreads = 256;
+constexpr int kDecUnroll = 8;  // 16-byte loads in flight per lane
+
+__device__ __forceinline__ int visible_keys(const int32_t *kv_len, int s, int Lcap) {
+  if (!kv_len) return Lcap;
+  const int L = kv_len[s];
+  return L < 1 ? 1 : (L > Lcap ? Lcap : L);
+}
+
+__device__ __forceinline__ float dot8_bf16(const u32x4 &kw, const float *qv) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = __builtin_fmaf(bf16_lo(kw[i]), qv[2 * i], acc);
+    acc = __builtin_fmaf(bf16_hi(kw[i]), qv[2 * i + 1], acc);
+  }
+  return acc;
+}
+
+__global__ void __launch_bounds__(kDecThreads) dec_scores(DecodeArgs a) {
+  __shared__ float sm[kDecThreads / 64], sl[kDecThreads / 64];
+  const int split = blockIdx.x % a.splits;
+  const int sh = blockIdx.x / a.splits;
+  const int seq = sh / a.H;
+  const int L = visible_keys(a.kv_len, seq, a.Lcap);
+  const int c0 = split * a.chunk, c1 = min(c0 + a.chunk, L);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int slot = lane >> 3, dc = lane & 7;
+
+  float qv[8];
+  {
+    const u32x4 qw = *reinterpret_cast<const u32x4 *>(
+        reinterpret_cast<const __bf16 *>(a.q) + (size_t)sh * kHeadDim + 8 * dc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qv[2 * i] = bf16_lo(qw[i]) * a.c2;
+      qv[2 * i + 1] = bf16_hi(qw[i]) * a.c2;
+    }
+  }
+  const __bf16 *K = reinterpret_cast<const __bf16 *>(a.kc) + (size_t)sh * a.Lcap * kHeadDim;
+  float *S = a.scores + (size_t)sh * a.Lcap;
+  float m = -INFINITY, l = 0.0f;
+
+  // each wave-iteration covers 8 * kDecUnroll consecutive keys
+  constexpr int kWaveKeys = 8 * kDecUnroll;
+  for (int base = c0 + w * kWaveKeys; base < c1; base += (kDecThreads / 64) * kWaveKeys) {
+    u32x4 kw[kDecUnroll];
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const int j = base + 8 * u + slot;
+      kw[u] = (j < c1) ? *reinterpret_cast<const u32x4 *>(K + (size_t)j * kHeadDim + 8 * dc)
+                       : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const int j = base + 8 * u + slot;
+      float s = dot8_bf16(kw[u], qv);
+      s += __shfl_xor(s, 1, 8);
+      s += __shfl_xor(s, 2, 8);
+      s += __shfl_xor(s, 4, 8);
+      if (j < c1 && dc == 0) {
+        S[j] = s;
+        const float m_new = fmaxf(m, s);
+        l = l * fast_exp2(m - m_new) + fast_exp2(s - m_new);
+        m = m_new;
+      }
+    }
+  }
+  // combine (m, l) over the wave, then over the waves
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float mo = __shfl_xor(m, off, 64), lo = __shfl_xor(l, off, 64);
+    const float mn = fmaxf(m, mo);
+    l = (mn == -INFINITY) ? 0.0f : l * fast_exp2(m - mn) + lo * fast_exp2(mo - mn);
+    m = mn;
+  }
+  if (lane == 0) { sm[w] = m; sl[w] = l; }
+  __syncthreads();
+  if (tid == 0) {
+    float M = -INFINITY, Ls = 0.0f;
+    for (int i = 0; i < kDecThreads / 64; ++i) {
+      const float mn = fmaxf(M, sm[i]);
+      Ls = (mn == -INFINITY) ? 0.0f : Ls * fast_exp2(M - mn) + sl[i] * fast_exp2(sm[i] - mn);
+      M = mn;
+    }
+    a.part_ml[2 * ((size_t)sh * a.splits + split)] = M;
+    a.part_ml[2 * ((size_t)sh * a.splits + split) + 1] = Ls;
+  }
+}
+
+__global__ void __launch_bounds__(kDecThreads) dec_share_v(DecodeArgs a) {
+  __shared__ float sShare[kDecThreads / 64][64];
+  __shared__ float sO[kDecThreads / 64][kHeadDim + 1];
+  const int split = blockIdx.x % a.splits;
+  const int sh = blockIdx.x / a.splits;
+  const int seq = sh / a.H;
+  const int L = visible_keys(a.kv_len, seq, a.Lcap);
+  const int c0 = split * a.chunk, c1 = min(c0 + a.chunk, L);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int slot = lane >> 3, dc = lane & 7;
+
+  // log-sum-exp of this query's scores over all chunks (fixed order)
+  float M = -INFINITY, Ls = 0.0f;
+  for (int i = 0; i < a.splits; ++i) {
+    const float mi = a.part_ml[2 * ((size_t)sh * a.splits + i)];
+    const float li = a.part_ml[2 * ((size_t)sh * a.splits + i) + 1];
+    const float mn = fmaxf(M, mi);
+    Ls = (mn == -INFINITY) ? 0.0f : Ls * fast_exp2(M - mn) + li * fast_exp2(mi - mn);
+    M = mn;
+  }
+  const float lse2 = M + __builtin_log2f(Ls);
+  const float eps_floor = fmaxf(a.eps, FLT_MIN);
+
+  const __bf16 *Vc = reinterpret_cast<const __bf16 *>(a.vc) + (size_t)sh * a.Lcap * kHeadDim;
+  const float *S = a.scores + (size_t)sh * a.Lcap;
+  float *D = a.demand + (size_t)sh * a.Lcap;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float rsum = 0.0f;
+
+  for (int base = c0 + 64 * w; base < c1; base += 64 * (kDecThreads / 64)) {
+    // one key per lane: bid, share and the demand update
+    const int j = base + lane;
+    float share = 0.0f;
+    if (j < c1) {
+      const float p = fast_exp2(S[j] - lse2);
+      const float dj = D[j];
+      share = p / fmaxf(dj + p + a.eps, eps_floor);
+      D[j] = dj + p;
+    }
+    rsum += share;
+    sShare[w][lane] = share;
+    // eight lanes per key row for the values
+    u32x4 vw[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int jj = base + 8 * u + slot;
+      vw[u] = (jj < c1) ? *reinterpret_cast<const u32x4 *>(Vc + (size_t)jj * kHeadDim + 8 * dc)
+                        : u32x4{0u, 0u, 0u, 0u};
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float sj = sShare[w][8 * u + slot];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = __builtin_fmaf(sj, bf16_lo(vw[u][i]), acc[2 * i]);
+        acc[2 * i + 1] = __builtin_fmaf(sj, bf16_hi(vw[u][i]), acc[2 * i + 1]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  // reduce over the 8 key slots of the wave (lanes with equal dc), then waves
+#pragma unroll
+  for (int off = 8; off < 64; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) rsum += __shfl_xor(rsum, off, 64);
+  if (lane < 8) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sO[w][8 * dc + e] = acc[e];
+  }
+  if (lane == 0) sO[w][kHeadDim] = rsum;
+  __syncthreads();
+  if (tid <= kHeadDim) {
+    float v = 0.0f;
+    for (int i = 0; i < kDecThreads / 64; ++i) v += sO[i][tid];
+    a.part_o[((size_t)sh * a.splits + split) * (kHeadDim + 1) + tid] = v;
+  }
+}
+
+__global__ void __launch_bounds__(128) dec_combine(DecodeArgs a) {
+  const int sh = blockIdx.x * 2 + (threadIdx.x >> 6);
+  const int d = threadIdx.x & 63;
+  if (sh >= a.S * a.H) return;
+  float num = 0.0f, den = 0.0f;
+  for (int i = 0; i < a.splits; ++i) {
+    const float *po = a.part_o + ((size_t)sh * a.splits + i) * (kHeadDim + 1);
+    num += po[d];
+    den += po[kHeadDim];
+  }
+  reinterpret_cast<__bf16 *>(a.out)[(size_t)sh * kHeadDim + d] = (__bf16)(num / den);
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
+  const unsigned nwg = (unsigned)(a.S * a.H * a.splits);
+  hipLaunchKernelGGL(dec_scores, dim3(nwg), dim3(kDecThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dec_share_v, dim3(nwg), dim3(kDecThreads), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dec_combine, dim3((unsigned)((a.S * a.H + 1) / 2)), dim3(128), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -1,0 +1,169 @@
+// fwd_f32.hip -- fp32 forward kernels (vector ALU only; no bf16 anywhere).
+//
+// Same operations and the same three-pass structure as the bf16 kernels
+// (tempered causal softmax attention -- "Learning to Focus: Focal Attention"
+// sec. 2.1 eq. focal-const, "YaRN > Attention Temperature Scaling"; dilution
+// attention -- "DilutionAttention v0.1.0 - results", "The operator"), for
+// fp32 storage where full single precision is required.  One lane owns one
+// query row (row kernels) or one key column (pass 2a); K/V or Q rows stream
+// through LDS in 64-row tiles and are read as broadcasts.  The column prefix
+// inside a 32-row query block is a shuffle scan across the 32 lanes that own
+// those rows.
+#include "attn_common.hpp"
+#include "launch.hpp"
+
+#include <float.h>
+
+namespace attn {
+
+constexpr int kFR = 64;  // rows per workgroup / tile
+
+template <int MODE>
+__global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
+  __shared__ __attribute__((aligned(16))) float sK[kFR * kHeadDim];
+  __shared__ __attribute__((aligned(16))) float sV[MODE == kRowLse ? 4 : kFR * kHeadDim];
+  const int t = threadIdx.x;
+  const int bh = blockIdx.x % a.BH;
+  const int qb = nqb - 1 - blockIdx.x / a.BH;
+  const int T = a.T;
+  const int q0 = qb * kFR;
+  const int i = q0 + t;  // this lane's query row
+  const size_t head = (size_t)bh * T * kHeadDim;
+  const float *Q = reinterpret_cast<const float *>(a.q) + head;
+  const float *K = reinterpret_cast<const float *>(a.k) + head;
+  const float *V = reinterpret_cast<const float *>(a.v) + head;
+
+  float q[kHeadDim], acc[kHeadDim];
+#pragma unroll
+  for (int e = 0; e < kHeadDim; ++e) {
+    q[e] = (i < T) ? Q[(size_t)i * kHeadDim + e] : 0.0f;
+    acc[e] = 0.0f;
+  }
+  float m = -INFINITY, l = 0.0f, lse2 = 0.0f;
+  const int qs = i >> 5;
+  const float *cin_blk = nullptr;
+  if constexpr (MODE == kRowShare) {
+    lse2 = (i < T) ? a.lse2[(size_t)bh * T + i] : 0.0f;
+    cin_blk = a.cin + (size_t)bh * cin_floats_per_head(T) + (size_t)16 * qs * (qs - 1);
+  }
+  const float eps_floor = fmaxf(a.eps, FLT_MIN);
+  const int kend = min(q0 + kFR, T);
+
+  for (int j0 = 0; j0 < kend; j0 += kFR) {
+    __syncthreads();
+    for (int u = t; u < kFR * kHeadDim; u += 64) {
+      const int row = j0 + u / kHeadDim;
+      sK[u] = row < T ? K[(size_t)j0 * kHeadDim + u] : 0.0f;
+      if constexpr (MODE != kRowLse) sV[u] = row < T ? V[(size_t)j0 * kHeadDim + u] : 0.0f;
+    }
+    __syncthreads();
+    const int jn = min(kFR, kend - j0);
+    for (int jj = 0; jj < jn; ++jj) {
+      const int j = j0 + jj;
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < kHeadDim; ++e) s = __builtin_fmaf(q[e], sK[jj * kHeadDim + e], s);
+      const bool vis = (j <= i) && (i < T);
+      if constexpr (MODE == kRowTempered || MODE == kRowLse) {
+        if (vis) {
+          const float x = s * a.c2;
+          const float m_new = fmaxf(m, x);
+          const float alpha = exp2f(m - m_new);
+          const float p = exp2f(x - m_new);
+          l = l * alpha + p;
+          if constexpr (MODE == kRowTempered) {
+#pragma unroll
+            for (int e = 0; e < kHeadDim; ++e) acc[e] = __builtin_fmaf(p, sV[jj * kHeadDim + e], acc[e] * alpha);
+          }
+          m = m_new;
+        }
+      } else {
+        const float p = vis ? exp2f(__builtin_fmaf(s, a.c2, -lse2)) : 0.0f;
+        // inclusive prefix of the bids over the 32 rows of this lane's block
+        float incl = p;
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) {
+          const float o = __shfl_up(incl, off, 32);
+          if ((t & 31) >= off) incl += o;
+        }
+        float base = (j < 32 * qs) ? cin_blk[j] : 0.0f;
+        base = fmaxf(base + a.eps, eps_floor);
+        const float share = p / (base + incl);
+        l += share;
+#pragma unroll
+        for (int e = 0; e < kHeadDim; ++e) acc[e] = __builtin_fmaf(share, sV[jj * kHeadDim + e], acc[e]);
+      }
+    }
+  }
+  if (i >= T) return;
+  if constexpr (MODE == kRowTempered || MODE == kRowLse) {
+    const float l2 = m + log2f(l);
+    if (a.lse2) a.lse2[(size_t)bh * T + i] = l2;
+    if (a.lse_nat) a.lse_nat[(size_t)bh * T + i] = l2 * kLn2;
+  }
+  if constexpr (MODE != kRowLse) {
+    float *O = reinterpret_cast<float *>(a.out) + head + (size_t)i * kHeadDim;
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int e = 0; e < kHeadDim; ++e) O[e] = acc[e] * inv;
+  }
+}
+
+__global__ void __launch_bounds__(64) colsum_f32_kernel(FwdArgs a, int nkb) {
+  __shared__ __attribute__((aligned(16))) float sQ[kFR * kHeadDim];
+  __shared__ float sL[kFR];
+  const int t = threadIdx.x;
+  const int bh = blockIdx.x % a.BH;
+  const int kb = blockIdx.x / a.BH;
+  const int T = a.T;
+  const int k0 = kb * kFR;
+  const int j = k0 + t;  // this lane's key column
+  const size_t head = (size_t)bh * T * kHeadDim;
+  const float *Q = reinterpret_cast<const float *>(a.q) + head;
+  const float *K = reinterpret_cast<const float *>(a.k) + head;
+  float *cin = a.cin + (size_t)bh * cin_floats_per_head(T);
+
+  float kv[kHeadDim];
+#pragma unroll
+  for (int e = 0; e < kHeadDim; ++e) kv[e] = (j < T) ? K[(size_t)j * kHeadDim + e] : 0.0f;
+  float run = 0.0f;
+  for (int i0 = k0; i0 < T; i0 += kFR) {
+    __syncthreads();
+    for (int u = t; u < kFR * kHeadDim; u += 64) {
+      const int row = i0 + u / kHeadDim;
+      sQ[u] = row < T ? Q[(size_t)i0 * kHeadDim + u] : 0.0f;
+    }
+    sL[t] = (i0 + t < T) ? a.lse2[(size_t)bh * T + i0 + t] : 0.0f;
+    __syncthreads();
+    const int in = min(kFR, T - i0);
+    for (int ii = 0; ii < in; ++ii) {
+      const int i = i0 + ii;
+      if ((i & 31) == 0 && (i >> 5) > (j >> 5) && j < T)
+        cin[(size_t)16 * (i >> 5) * ((i >> 5) - 1) + j] = run;  // demand before block i/32
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < kHeadDim; ++e) s = __builtin_fmaf(sQ[ii * kHeadDim + e], kv[e], s);
+      if (j <= i) run += exp2f(__builtin_fmaf(s, a.c2, -sL[ii]));
+    }
+  }
+  if (a.demand_out && j < T) a.demand_out[(size_t)bh * T + j] = run;
+}
+
+hipError_t launch_rows_f32(int mode, const FwdArgs &a, hipStream_t s) {
+  const int nqb = (a.T + kFR - 1) / kFR;
+  dim3 grid((unsigned)(nqb * a.BH)), block(64);
+  switch (mode) {
+    case kRowTempered: hipLaunchKernelGGL(rows_f32_kernel<kRowTempered>, grid, block, 0, s, a, nqb); break;
+    case kRowLse: hipLaunchKernelGGL(rows_f32_kernel<kRowLse>, grid, block, 0, s, a, nqb); break;
+    default: hipLaunchKernelGGL(rows_f32_kernel<kRowShare>, grid, block, 0, s, a, nqb); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum_f32(const FwdArgs &a, hipStream_t s) {
+  const int nkb = (a.T + kFR - 1) / kFR;
+  hipLaunchKernelGGL(colsum_f32_kernel, dim3((unsigned)(nkb * a.BH)), dim3(64), 0, s, a, nkb);
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -1,0 +1,54 @@
+// launch.hpp -- host-side launchers of the attention kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+constexpr int kHeadDim = 64;  // the head dimension every kernel is built for
+
+// Row-major passes over the causal score matrix (one workgroup per query
+// block).  lse2 is the log2-domain log-sum-exp of each row.
+enum RowMode { kRowTempered = 0, kRowLse = 1, kRowShare = 2 };
+
+struct FwdArgs {
+  const void *q, *k, *v;
+  void *out;
+  float *lse2;          // [BH*T] workspace (dilution) or NULL
+  float *lse_nat;       // [BH*T] optional natural-log output
+  float *cin;           // committed demand per 32-row query block (dilution)
+  float *demand_out;    // [BH*T] optional final column totals (dilution)
+  int BH, T;
+  float c2;             // tau / sqrt(d) * log2(e)
+  float eps;
+};
+
+// Committed-demand storage: query sub-block qs (32 rows) keeps one float per
+// key j < 32*qs, at offset 16*qs*(qs-1) inside its head's region.
+__host__ __device__ inline size_t cin_floats_per_head(int T) {
+  const size_t n = ((size_t)T + 31) / 32;
+  return 16 * n * (n - 1);
+}
+
+hipError_t launch_rows_bf16(int mode, const FwdArgs &a, hipStream_t s);
+hipError_t launch_colsum_bf16(const FwdArgs &a, hipStream_t s);
+hipError_t launch_rows_f32(int mode, const FwdArgs &a, hipStream_t s);
+hipError_t launch_colsum_f32(const FwdArgs &a, hipStream_t s);
+
+struct DecodeArgs {
+  const void *q, *kc, *vc;
+  float *demand;
+  void *out;
+  const int32_t *kv_len;
+  int S, H, Lcap, splits, chunk;
+  float c2, eps;
+  float *scores;   // [S*H*Lcap]
+  float *part_ml;  // [S*H*splits*2]  (max, sum) in log2 domain
+  float *part_o;   // [S*H*splits*(64+1)]
+};
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+
+}  // namespace attn
