@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of the reshaped-softmax causal attention hot path on one MI355X.
+
+One step runs the whole path once over resident synthetic inputs:
+  * dilution attention forward (three stages) at B=1, H=16, T=16384, d=64,
+    bf16, eps=1e-6, 5 % heavy keys -- the per-layer shape of the 24-layer,
+    ~209M-parameter decoder at its 16K training context;
+  * tempered causal attention forward on the same inputs, tau = YaRN(s=4);
+  * one cached dilution decode step: 64 sequences x 32768-key bf16 cache,
+    H=16, d=64, fp32 demand updated in place (the 128 queries of the decode
+    workload are used in turn).
+
+Printed: one JSON line.  ``value`` is the dilution forward's algorithmic
+TFLOP/s (4*d flops per causal (query, key) pair: q.k and the weighted v, once)
+over the measured time of its three launches; the tempered forward TFLOP/s and
+the decode step's HBM GB/s (K + V + demand read + demand write) are reported
+under ``components``.  Kernel durations come from HIP events recorded on the
+stream the library launches on, inside the timed region.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd TFLOP/s (dilution & tempered) at T=16K; decode HBM GB/s at 32K cache"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E peak
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def causal_pairs(B, H, T):
+    return B * H * T * (T + 1) // 2
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=4,
+                    help="heads of the T=16384 dilution workload the oracle runs for the CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the hot path has no multi-GPU form here "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from transformer_attention_causal_amd import binding as ab
+    from transformer_attention_causal_amd.workloads import (DECODE, PREFILL, decode_cache_device,
+                                                            decode_initial_demand,
+                                                            decode_queries, prefill_inputs)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ab.load()
+
+    # ---------------------------------------------------------------- inputs
+    w = PREFILL["dilution_t16k"]
+    log(f"bench: drawing {w.name} inputs B={w.B} H={w.H} T={w.T}")
+    inp = prefill_inputs(w)
+
+    def dev_bf16(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v)
+    tau_t = ab.attn_yarn_tau(w.yarn_s)
+    out_d = torch.empty_like(q)
+    out_t = torch.empty_like(q)
+    ws, ws_bytes = ab.fwd_workspace(w.B, w.H, w.T, ab.ATTN_DILUTION, ab.ATTN_BF16, dev)
+    stages, _ = ab.dilution_stages(q, k, v, tau=1.0, eps=w.eps, out=out_d, workspace=ws)
+
+    dw = DECODE["decode_32k"]
+    log(f"bench: drawing {dw.name} cache S={dw.S} H={dw.H} L={dw.L}")
+    kc, vc = decode_cache_device(dw.S, dw.H, dw.L, dw.d, dw.seed, device=dev)
+    demand = torch.from_numpy(decode_initial_demand(dw.S, dw.H, dw.L, dw.seed, dw.demand_max)).to(dev)
+    qs = dev_bf16(decode_queries(dw.steps, dw.S, dw.H, dw.d, dw.seed))
+    dec_out = torch.empty((dw.S, dw.H, dw.d), dtype=torch.bfloat16, device=dev)
+    dws, _ = ab.decode_workspace(dw.S, dw.H, dw.L, dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    names = ["dil_lse", "dil_committed", "dil_shares", "tempered", "decode"]
+
+    def step(i, events=None):
+        def mark(j):
+            if events is not None:
+                events[j].record(stream)
+        mark(0)
+        for j, st in enumerate(stages):
+            st()
+            mark(j + 1)
+        ab.fwd(q, k, v, tau=tau_t, mode=ab.ATTN_TEMPERED, out=out_t)
+        mark(4)
+        ab.decode(qs[i % dw.steps], kc, vc, demand, tau=dw.tau, eps=dw.eps, out=dec_out,
+                  workspace=dws)
+        mark(5)
+
+    log(f"bench: warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    log(f"bench: timing {args.steps} steps")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    seg = {n: [] for n in names}
+    for e in evs:
+        for j, n in enumerate(names):
+            seg[n].append(e[j].elapsed_time(e[j + 1]))
+    ms = {n: float(np.mean(seg[n])) for n in names}
+    ms_min = {n: float(np.min(seg[n])) for n in names}
+    log("bench: per-launch ms " + json.dumps({n: round(ms[n], 4) for n in names}))
+
+    # ------------------------------------------------------------ throughputs
+    d = w.d
+    flops = 4.0 * d * causal_pairs(w.B, w.H, w.T)            # algorithmic, per forward
+    dil_ms = ms["dil_lse"] + ms["dil_committed"] + ms["dil_shares"]
+    dil_tflops = flops / (dil_ms * 1e-3) / 1e12
+    tmp_tflops = flops / (ms["tempered"] * 1e-3) / 1e12
+    dec_bytes = (2.0 * dw.S * dw.H * dw.L * dw.d * 2        # K and V caches, bf16
+                 + 2.0 * dw.S * dw.H * dw.L * 4             # demand read + write, fp32
+                 + 2.0 * dw.S * dw.H * dw.d * 2)            # query in, output out
+    dec_gbps = dec_bytes / (ms["decode"] * 1e-3) / 1e9
+    shares_tflops = flops / (ms["dil_shares"] * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(dil_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "dilution_t16k (value) + tempered_t16k + decode_32k step",
+            "B": w.B, "H": w.H, "T": w.T, "d": d, "eps": w.eps, "heavy_key_frac": w.heavy_frac,
+            "tempered_tau": tau_t,
+            "decode": {"S": dw.S, "H": dw.H, "L": dw.L, "d": dw.d, "steps_in_workload": dw.steps},
+        },
+        "components": {
+            "dilution_fwd": {"ms": round(dil_ms, 4), "tflops": round(dil_tflops, 3),
+                             "stage_ms": {n: round(ms[n], 4) for n in names[:3]},
+                             "frac_of_bf16_peak": round(dil_tflops / PEAK_BF16_TFLOPS, 4)},
+            "tempered_fwd": {"ms": round(ms["tempered"], 4), "tflops": round(tmp_tflops, 3),
+                             "frac_of_bf16_peak": round(tmp_tflops / PEAK_BF16_TFLOPS, 4)},
+            "decode_step": {"ms": round(ms["decode"], 4), "gbps": round(dec_gbps, 2),
+                            "bytes": dec_bytes,
+                            "frac_of_hbm_peak": round(dec_gbps / PEAK_HBM_GBPS, 4)},
+            "min_ms": {n: round(ms_min[n], 4) for n in names},
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "rows_bf16_kernel<kRowShare> (dilution stage 3: shares and share@V)",
+            "achieved": round(shares_tflops, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(shares_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "units": f"{causal_pairs(w.B, w.H, w.T)} causal pairs x {4 * d} flops",
+        },
+        "roofline_decode": {
+            "bound": "hbm",
+            "kernel": "attn_decode step (dec_scores + dec_share_v + dec_combine)",
+            "achieved": round(dec_gbps, 2),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": None,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_heads)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(inp, w, nheads):
+    """The fp64 oracle (untuned) on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+
+    heads = list(range(min(nheads, w.H)))
+    log(f"bench: cpu baseline (oracle) on {len(heads)} head(s) of T={w.T} dilution")
+    sub = [oracle.Bf16(np.ascontiguousarray(x[:, heads])) for x in (inp.q, inp.k, inp.v)]
+    t0 = time.perf_counter()
+    oracle.dilution_fwd(*sub, 1.0, w.eps)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.d * causal_pairs(1, len(heads), w.T)
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"dilution forward, {len(heads)} of {w.H} heads at T={w.T} (all rows), "
+                  f"{dt:.2f} s, fp64",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -95,6 +95,36 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, int B, i
                 int d, float tau, int mode, float eps, int dtype, void *workspace,
                 size_t workspace_bytes, float *lse_out, float *demand_out, void *hip_stream);
 
+/* The dilution forward pass, one stage per call (attn_fwd with ATTN_DILUTION
+ * runs exactly these three in order on one stream).  All three take the same
+ * shape, tau, dtype and workspace (>= attn_fwd_workspace_bytes(...,
+ * ATTN_DILUTION, dtype)); a stage reads what the previous stage left in the
+ * workspace, so they must be enqueued in order on one stream.
+ *
+ * attn_dilution_lse        stage 1: log-sum-exp of each query row's logits,
+ *                          the normaliser of the causal softmax bids ("The
+ *                          operator").  lse_out: optional [B,H,T] fp32
+ *                          natural-log copy.
+ * attn_dilution_committed  stage 2: for every 32-row query block and every
+ *                          earlier key, the demand committed by all earlier
+ *                          rows -- the exclusive cumulative sum of the bids
+ *                          down each key column ("The operator", committed),
+ *                          taken block by block.  demand_out: optional
+ *                          [B,H,T] fp32 final column totals.
+ * attn_dilution_shares     stage 3: shares p / (committed + p + eps) with the
+ *                          prefix finished inside each block, then out = A @ v
+ *                          with A the row-renormalised shares ("The operator",
+ *                          share and A). */
+int attn_dilution_lse(const void *q, const void *k, int B, int H, int T, int d, float tau,
+                      int dtype, void *workspace, size_t workspace_bytes, float *lse_out,
+                      void *hip_stream);
+int attn_dilution_committed(const void *q, const void *k, int B, int H, int T, int d, float tau,
+                            int dtype, void *workspace, size_t workspace_bytes,
+                            float *demand_out, void *hip_stream);
+int attn_dilution_shares(const void *q, const void *k, const void *v, void *out, int B, int H,
+                         int T, int d, float tau, float eps, int dtype, void *workspace,
+                         size_t workspace_bytes, void *hip_stream);
+
 /* Bytes of device workspace attn_decode needs (per-(sequence,head,split)
  * partial maxima, sums and weighted values plus one fp32 score per cached
  * key). */

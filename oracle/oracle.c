@@ -252,6 +252,32 @@ static void dilution_head(const double *Qh, const double *Kh, const double *Vh, 
   }
 }
 
+/* Widen one head's inputs and run dilution_head on it (0 on success). */
+static int dilution_one_head(const void *q, const void *k, const void *v, int dtype, double *out,
+                             double *lse, double *demand, int B, int H, int T, int d, double c,
+                             double eps, const unsigned char *want, int bh, int inner_parallel) {
+  if (bh < 0 || bh >= B * H) return 0;
+  const size_t base = (size_t)bh * T * d;
+  double *Qh = malloc(sizeof(double) * (size_t)T * d);
+  double *Kh = malloc(sizeof(double) * (size_t)T * d);
+  double *Vh = malloc(sizeof(double) * (size_t)T * d);
+  double *D = calloc((size_t)T, sizeof(double));
+  double *p = malloc(sizeof(double) * (size_t)T);
+  int rc = 0;
+  if (!Qh || !Kh || !Vh || !D || !p) {
+    rc = -2;
+  } else {
+    widen_block(Qh, q, dtype, base, (size_t)T * d);
+    widen_block(Kh, k, dtype, base, (size_t)T * d);
+    widen_block(Vh, v, dtype, base, (size_t)T * d);
+    dilution_head(Qh, Kh, Vh, T, d, c, eps, want, out + base, lse ? lse + (size_t)bh * T : NULL,
+                  D, p, inner_parallel);
+    if (demand) memcpy(demand + (size_t)bh * T, D, sizeof(double) * (size_t)T);
+  }
+  free(Qh); free(Kh); free(Vh); free(D); free(p);
+  return rc;
+}
+
 /*
  * Dilution attention forward ([DIL] "The operator").
  * q,k,v: [B,H,T,d] in dtype.  out: [B,H,T,d] fp64 (rows not selected are left
@@ -273,33 +299,65 @@ int oracle_dilution_fwd(const void *q, const void *k, const void *v, int dtype, 
       if (rows[r] >= 0 && rows[r] < T) want[rows[r]] = 1;
   }
   const int nh = heads ? nheads : B * H;
+  /* Heads are independent: with enough of them each thread takes whole heads;
+     otherwise heads run one after another and each row's sums are split
+     across the threads. */
   const int outer = nh >= nthreads();
   int failed = 0;
-#pragma omp parallel for if (outer) schedule(dynamic, 1)
-  for (int hi = 0; hi < nh; ++hi) {
-    const int bh = heads ? heads[hi] : hi;
-    if (bh < 0 || bh >= B * H) continue;
-    const size_t base = (size_t)bh * T * d;
-    double *Qh = malloc(sizeof(double) * (size_t)T * d);
-    double *Kh = malloc(sizeof(double) * (size_t)T * d);
-    double *Vh = malloc(sizeof(double) * (size_t)T * d);
-    double *D = calloc((size_t)T, sizeof(double));
-    double *p = malloc(sizeof(double) * (size_t)T);
-    if (!Qh || !Kh || !Vh || !D || !p) {
+  if (outer) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int hi = 0; hi < nh; ++hi)
+      if (dilution_one_head(q, k, v, dtype, out, lse, demand, B, H, T, d, c, eps, want,
+                            heads ? heads[hi] : hi, 0) != 0) {
 #pragma omp atomic write
-      failed = 1;
-    } else {
-      widen_block(Qh, q, dtype, base, (size_t)T * d);
-      widen_block(Kh, k, dtype, base, (size_t)T * d);
-      widen_block(Vh, v, dtype, base, (size_t)T * d);
-      dilution_head(Qh, Kh, Vh, T, d, c, eps, want, out + base, lse ? lse + (size_t)bh * T : NULL,
-                    D, p, !outer);
-      if (demand) memcpy(demand + (size_t)bh * T, D, sizeof(double) * (size_t)T);
-    }
-    free(Qh); free(Kh); free(Vh); free(D); free(p);
+        failed = 1;
+      }
+  } else {
+    for (int hi = 0; hi < nh; ++hi)
+      if (dilution_one_head(q, k, v, dtype, out, lse, demand, B, H, T, d, c, eps, want,
+                            heads ? heads[hi] : hi, 1) != 0)
+        failed = 1;
   }
   free(want);
   return failed ? -2 : 0;
+}
+
+/* One (sequence, head) of a decode step; 0 on success. */
+static int decode_one_pair(const void *q, const void *kc, const void *vc, int dtype, double *D,
+                           double *out, int H, int Lcap, int d, const int *kv_len, double c,
+                           double eps, int sh, int inner_parallel) {
+  const int s = sh / H;
+  const int L = kv_len ? kv_len[s] : Lcap;
+  if (L <= 0 || L > Lcap || d > 512) return -1;
+  double *Kh = malloc(sizeof(double) * (size_t)L * d);
+  double *Vh = malloc(sizeof(double) * (size_t)L * d);
+  double *p = malloc(sizeof(double) * (size_t)L);
+  double qv[512];
+  int rc = 0;
+  if (!Kh || !Vh || !p) {
+    rc = -2;
+  } else {
+    widen_block(qv, q, dtype, (size_t)sh * d, d);
+    widen_block(Kh, kc, dtype, (size_t)sh * Lcap * d, (size_t)L * d);
+    widen_block(Vh, vc, dtype, (size_t)sh * Lcap * d, (size_t)L * d);
+    /* the new query sees every cached key: its bids are the causal bids of a
+       row whose last visible key is L-1 */
+    causal_bids(qv, Kh, L - 1, d, c, p, inner_parallel);
+    double *Dh = D + (size_t)sh * Lcap;
+    double r = 0.0, acc[512];
+    for (int e = 0; e < d; ++e) acc[e] = 0.0;
+    for (int j = 0; j < L; ++j) {
+      if (p[j] > 0.0) {
+        const double share = p[j] / (Dh[j] + p[j] + eps);
+        r += share;
+        for (int e = 0; e < d; ++e) acc[e] += share * Vh[(size_t)j * d + e];
+      }
+    }
+    for (int e = 0; e < d; ++e) out[(size_t)sh * d + e] = acc[e] / r;
+    for (int j = 0; j < L; ++j) Dh[j] += p[j];
+  }
+  free(Kh); free(Vh); free(p);
+  return rc;
 }
 
 /*
@@ -323,45 +381,23 @@ int oracle_dilution_decode_step(const void *q, const void *kc, const void *vc, i
   const int np = pairs ? npairs : S * H;
   const int outer = np >= nthreads();
   int failed = 0;
-#pragma omp parallel for if (outer) schedule(dynamic, 1)
-  for (int pi = 0; pi < np; ++pi) {
-    const int sh = pairs ? pairs[pi] : pi;
-    if (sh < 0 || sh >= S * H) continue;
-    const int s = sh / H;
-    const int L = kv_len ? kv_len[s] : Lcap;
-    if (L <= 0 || L > Lcap) {
+  if (outer) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int pi = 0; pi < np; ++pi) {
+      const int sh = pairs ? pairs[pi] : pi;
+      if (sh < 0 || sh >= S * H) continue;
+      if (decode_one_pair(q, kc, vc, dtype, D, out, H, Lcap, d, kv_len, c, eps, sh, 0) != 0) {
 #pragma omp atomic write
-      failed = 1;
-      continue;
-    }
-    double *Kh = malloc(sizeof(double) * (size_t)L * d);
-    double *Vh = malloc(sizeof(double) * (size_t)L * d);
-    double *p = malloc(sizeof(double) * (size_t)L);
-    double qv[512];
-    if (!Kh || !Vh || !p || d > 512) {
-#pragma omp atomic write
-      failed = 1;
-    } else {
-      widen_block(qv, q, dtype, (size_t)sh * d, d);
-      widen_block(Kh, kc, dtype, (size_t)sh * Lcap * d, (size_t)L * d);
-      widen_block(Vh, vc, dtype, (size_t)sh * Lcap * d, (size_t)L * d);
-      /* the new query sees every cached key: its bids are the causal bids of
-         a row whose last visible key is L-1 */
-      causal_bids(qv, Kh, L - 1, d, c, p, !outer);
-      double *Dh = D + (size_t)sh * Lcap;
-      double r = 0.0, acc[512];
-      for (int e = 0; e < d; ++e) acc[e] = 0.0;
-      for (int j = 0; j < L; ++j) {
-        if (p[j] > 0.0) {
-          const double share = p[j] / (Dh[j] + p[j] + eps);
-          r += share;
-          for (int e = 0; e < d; ++e) acc[e] += share * Vh[(size_t)j * d + e];
-        }
+        failed = 1;
       }
-      for (int e = 0; e < d; ++e) out[(size_t)sh * d + e] = acc[e] / r;
-      for (int j = 0; j < L; ++j) Dh[j] += p[j];
     }
-    free(Kh); free(Vh); free(p);
+  } else {
+    for (int pi = 0; pi < np; ++pi) {
+      const int sh = pairs ? pairs[pi] : pi;
+      if (sh < 0 || sh >= S * H) continue;
+      if (decode_one_pair(q, kc, vc, dtype, D, out, H, Lcap, d, kv_len, c, eps, sh, 1) != 0)
+        failed = 1;
+    }
   }
   return failed ? -2 : 0;
 }

@@ -23,7 +23,8 @@ ATTN_OK, ATTN_EINVAL, ATTN_ENOTSUP, ATTN_EWORKSPACE, ATTN_EHIP = 0, -1, -2, -3, 
 ATTN_TEMPERED, ATTN_DILUTION = 0, 1
 ATTN_F32, ATTN_BF16 = 0, 1
 
-EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_bytes", "attn_decode",
+EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_bytes", "attn_dilution_lse",
+            "attn_dilution_committed", "attn_dilution_shares", "attn_decode",
             "attn_decode_workspace_bytes", "attn_yarn_tau", "attn_strerror")
 
 
@@ -50,6 +51,12 @@ def load() -> ctypes.CDLL:
         lib.attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, f, i, vp, sz, vp]
         lib.attn_fwd_ex.restype = i
         lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, f, i, vp, sz, vp, vp, vp]
+        lib.attn_dilution_lse.restype = i
+        lib.attn_dilution_lse.argtypes = [vp, vp, i, i, i, i, f, i, vp, sz, vp, vp]
+        lib.attn_dilution_committed.restype = i
+        lib.attn_dilution_committed.argtypes = [vp, vp, i, i, i, i, f, i, vp, sz, vp, vp]
+        lib.attn_dilution_shares.restype = i
+        lib.attn_dilution_shares.argtypes = [vp, vp, vp, vp, i, i, i, i, f, f, i, vp, sz, vp]
         lib.attn_fwd_workspace_bytes.restype = sz
         lib.attn_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
         lib.attn_decode.restype = i
@@ -76,6 +83,24 @@ def attn_fwd_ex(q, k, v, out, B, H, T, d, tau, mode, eps, dtype, workspace, work
                 lse_out, demand_out, hip_stream) -> int:
     return load().attn_fwd_ex(q, k, v, out, B, H, T, d, tau, mode, eps, dtype, workspace,
                               workspace_bytes, lse_out, demand_out, hip_stream)
+
+
+def attn_dilution_lse(q, k, B, H, T, d, tau, dtype, workspace, workspace_bytes, lse_out,
+                      hip_stream) -> int:
+    return load().attn_dilution_lse(q, k, B, H, T, d, tau, dtype, workspace, workspace_bytes,
+                                    lse_out, hip_stream)
+
+
+def attn_dilution_committed(q, k, B, H, T, d, tau, dtype, workspace, workspace_bytes,
+                            demand_out, hip_stream) -> int:
+    return load().attn_dilution_committed(q, k, B, H, T, d, tau, dtype, workspace,
+                                          workspace_bytes, demand_out, hip_stream)
+
+
+def attn_dilution_shares(q, k, v, out, B, H, T, d, tau, eps, dtype, workspace, workspace_bytes,
+                         hip_stream) -> int:
+    return load().attn_dilution_shares(q, k, v, out, B, H, T, d, tau, eps, dtype, workspace,
+                                       workspace_bytes, hip_stream)
 
 
 def attn_fwd_workspace_bytes(B, H, T, d, mode, dtype) -> int:
@@ -154,6 +179,46 @@ def fwd(q, k, v, tau: float = 1.0, mode: int = ATTN_TEMPERED, eps: float = 1e-6,
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_ex")
     return out
+
+
+def dilution_stages(q, k, v, tau: float = 1.0, eps: float = 1e-6, out=None, workspace=None,
+                    lse_out=None, demand_out=None):
+    """Run the three dilution stages as separate calls; returns a list of
+    three zero-argument callables (lse, committed, shares) that enqueue one
+    stage each on the current stream, and the output tensor they fill."""
+    import torch
+
+    B, H, T, d = q.shape
+    code = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace, ws_bytes = fwd_workspace(B, H, T, ATTN_DILUTION, code, q.device)
+    else:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    wp = workspace.data_ptr()
+    lp = lse_out.data_ptr() if lse_out is not None else None
+    dp = demand_out.data_ptr() if demand_out is not None else None
+
+    def check(st, where):
+        if st != ATTN_OK:
+            raise AttnError(st, where)
+
+    def lse():
+        check(attn_dilution_lse(q.data_ptr(), k.data_ptr(), B, H, T, d, float(tau), code, wp,
+                                ws_bytes, lp, _stream_handle(q.device)), "attn_dilution_lse")
+
+    def committed():
+        check(attn_dilution_committed(q.data_ptr(), k.data_ptr(), B, H, T, d, float(tau), code,
+                                      wp, ws_bytes, dp, _stream_handle(q.device)),
+              "attn_dilution_committed")
+
+    def shares():
+        check(attn_dilution_shares(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B,
+                                   H, T, d, float(tau), float(eps), code, wp, ws_bytes,
+                                   _stream_handle(q.device)), "attn_dilution_shares")
+
+    return [lse, committed, shares], out
 
 
 def decode_workspace(S, H, Lcap, device):

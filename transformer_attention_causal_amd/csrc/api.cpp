@@ -109,22 +109,27 @@ size_t attn_fwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype)
   return ws.total;
 }
 
-int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, int B, int H, int T,
-                int d, float tau, int mode, float eps, int dtype, void *workspace,
-                size_t workspace_bytes, float *lse_out, float *demand_out, void *hip_stream) {
-  if (!q || !k || !v || !out) return ATTN_EINVAL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_EINVAL;
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the forward entry points.  `v`/`out` may be NULL
+// for the stages that do not read or write them.
+int check_fwd(const void *q, const void *k, const void *v, const void *out, int B, int H, int T,
+              int d, float tau, float eps, int dtype, const float *lse_out,
+              const float *demand_out) {
+  if (!q || !k) return ATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || (v && !aligned16(v)) || (out && !aligned16(out)))
+    return ATTN_EINVAL;
   if (!shape_ok(B, H, T)) return ATTN_EINVAL;
-  if (mode != ATTN_TEMPERED && mode != ATTN_DILUTION) return ATTN_EINVAL;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EINVAL;
   if (!std::isfinite(tau) || tau < 0.0f) return ATTN_EINVAL;
   if (!std::isfinite(eps) || eps < 0.0f) return ATTN_EINVAL;
-  if (mode == ATTN_TEMPERED && demand_out) return ATTN_EINVAL;
   if (d != attn::kHeadDim) return ATTN_ENOTSUP;
   const size_t esz = dtype == ATTN_BF16 ? 2 : 4;
   const size_t nbytes = (size_t)B * H * (size_t)T * d * esz;
-  if (overlaps(out, nbytes, q, nbytes) || overlaps(out, nbytes, k, nbytes) ||
-      overlaps(out, nbytes, v, nbytes))
+  if (out && (overlaps(out, nbytes, q, nbytes) || overlaps(out, nbytes, k, nbytes) ||
+              (v && overlaps(out, nbytes, v, nbytes))))
     return ATTN_EINVAL;
   // the optional [B,H,T] fp32 outputs may not alias any tensor argument or each other
   const size_t rbytes = (size_t)B * H * (size_t)T * sizeof(float);
@@ -132,53 +137,129 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, int B, i
     if (!r) continue;
     if (!aligned16(r)) return ATTN_EINVAL;
     if (overlaps(r, rbytes, q, nbytes) || overlaps(r, rbytes, k, nbytes) ||
-        overlaps(r, rbytes, v, nbytes) || overlaps(r, rbytes, out, nbytes))
+        (v && overlaps(r, rbytes, v, nbytes)) || (out && overlaps(r, rbytes, out, nbytes)))
       return ATTN_EINVAL;
   }
   if (lse_out && demand_out && overlaps(lse_out, rbytes, demand_out, rbytes)) return ATTN_EINVAL;
+  return ATTN_OK;
+}
 
-  FwdWorkspace ws{0, 0, 0};
-  if (mode == ATTN_DILUTION) {
-    if (!fwd_workspace(B, H, T, &ws)) return ATTN_EINVAL;
-    if (!workspace || workspace_bytes < ws.total || !aligned16(workspace)) return ATTN_EWORKSPACE;
-  }
-  const int dev_status = check_device();
-  if (dev_status != ATTN_OK) return dev_status;
+int check_workspace(int B, int H, int T, void *workspace, size_t workspace_bytes,
+                    FwdWorkspace *ws) {
+  if (!fwd_workspace(B, H, T, ws)) return ATTN_EINVAL;
+  if (!workspace || workspace_bytes < ws->total || !aligned16(workspace)) return ATTN_EWORKSPACE;
+  return ATTN_OK;
+}
 
+attn::FwdArgs make_args(const void *q, const void *k, const void *v, void *out, int B, int H,
+                        int T, int d, float tau, float eps, void *workspace,
+                        const FwdWorkspace &ws) {
   attn::FwdArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
   a.out = out;
-  a.lse_nat = lse_out;
-  a.demand_out = demand_out;
   a.BH = B * H;
   a.T = T;
+  // logits are tau <q,k> / sqrt(d); the kernels work in base 2
   a.c2 = (float)((double)tau / std::sqrt((double)d) * 1.4426950408889634);
   a.eps = eps;
+  if (workspace) {
+    char *wsp = static_cast<char *>(workspace);
+    a.lse2 = reinterpret_cast<float *>(wsp);
+    a.cin = reinterpret_cast<float *>(wsp + ws.lse_bytes);
+  }
+  return a;
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? ATTN_OK : fail_hip(e); }
+
+}  // namespace
+
+extern "C" {
+
+int attn_dilution_lse(const void *q, const void *k, int B, int H, int T, int d, float tau,
+                      int dtype, void *workspace, size_t workspace_bytes, float *lse_out,
+                      void *hip_stream) {
+  int st = check_fwd(q, k, nullptr, nullptr, B, H, T, d, tau, 0.0f, dtype, lse_out, nullptr);
+  FwdWorkspace ws{};
+  if (st == ATTN_OK) st = check_workspace(B, H, T, workspace, workspace_bytes, &ws);
+  if (st == ATTN_OK) st = check_device();
+  if (st != ATTN_OK) return st;
+  attn::FwdArgs a = make_args(q, k, nullptr, nullptr, B, H, T, d, tau, 0.0f, workspace, ws);
+  a.lse_nat = lse_out;
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  hipError_t e;
+  return finish(dtype == ATTN_BF16 ? attn::launch_rows_bf16(attn::kRowLse, a, s)
+                                   : attn::launch_rows_f32(attn::kRowLse, a, s));
+}
+
+int attn_dilution_committed(const void *q, const void *k, int B, int H, int T, int d, float tau,
+                            int dtype, void *workspace, size_t workspace_bytes,
+                            float *demand_out, void *hip_stream) {
+  int st = check_fwd(q, k, nullptr, nullptr, B, H, T, d, tau, 0.0f, dtype, nullptr, demand_out);
+  FwdWorkspace ws{};
+  if (st == ATTN_OK) st = check_workspace(B, H, T, workspace, workspace_bytes, &ws);
+  if (st == ATTN_OK) st = check_device();
+  if (st != ATTN_OK) return st;
+  attn::FwdArgs a = make_args(q, k, nullptr, nullptr, B, H, T, d, tau, 0.0f, workspace, ws);
+  a.demand_out = demand_out;
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  return finish(dtype == ATTN_BF16 ? attn::launch_colsum_bf16(a, s) : attn::launch_colsum_f32(a, s));
+}
+
+int attn_dilution_shares(const void *q, const void *k, const void *v, void *out, int B, int H,
+                         int T, int d, float tau, float eps, int dtype, void *workspace,
+                         size_t workspace_bytes, void *hip_stream) {
+  if (!v || !out) return ATTN_EINVAL;
+  int st = check_fwd(q, k, v, out, B, H, T, d, tau, eps, dtype, nullptr, nullptr);
+  FwdWorkspace ws{};
+  if (st == ATTN_OK) st = check_workspace(B, H, T, workspace, workspace_bytes, &ws);
+  if (st == ATTN_OK) st = check_device();
+  if (st != ATTN_OK) return st;
+  attn::FwdArgs a = make_args(q, k, v, out, B, H, T, d, tau, eps, workspace, ws);
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  return finish(dtype == ATTN_BF16 ? attn::launch_rows_bf16(attn::kRowShare, a, s)
+                                   : attn::launch_rows_f32(attn::kRowShare, a, s));
+}
+
+int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, int B, int H, int T,
+                int d, float tau, int mode, float eps, int dtype, void *workspace,
+                size_t workspace_bytes, float *lse_out, float *demand_out, void *hip_stream) {
+  if (!v || !out) return ATTN_EINVAL;
+  if (mode != ATTN_TEMPERED && mode != ATTN_DILUTION) return ATTN_EINVAL;
+  if (mode == ATTN_TEMPERED && demand_out) return ATTN_EINVAL;
+  int st = check_fwd(q, k, v, out, B, H, T, d, tau, eps, dtype, lse_out, demand_out);
+  if (st != ATTN_OK) return st;
+  FwdWorkspace ws{};
+  if (mode == ATTN_DILUTION) {
+    st = check_workspace(B, H, T, workspace, workspace_bytes, &ws);
+    if (st != ATTN_OK) return st;
+  }
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
   const bool bf16 = dtype == ATTN_BF16;
   if (mode == ATTN_TEMPERED) {
-    a.lse2 = nullptr;
-    e = bf16 ? attn::launch_rows_bf16(attn::kRowTempered, a, s)
-             : attn::launch_rows_f32(attn::kRowTempered, a, s);
-    return e == hipSuccess ? ATTN_OK : fail_hip(e);
+    attn::FwdArgs a = make_args(q, k, v, out, B, H, T, d, tau, eps, nullptr, ws);
+    a.lse_nat = lse_out;
+    return finish(bf16 ? attn::launch_rows_bf16(attn::kRowTempered, a, s)
+                       : attn::launch_rows_f32(attn::kRowTempered, a, s));
   }
-  char *wsp = static_cast<char *>(workspace);
-  a.lse2 = reinterpret_cast<float *>(wsp);
-  a.cin = reinterpret_cast<float *>(wsp + ws.lse_bytes);
-  // pass 1: row log-sum-exp (also the optional natural-log output)
-  e = bf16 ? attn::launch_rows_bf16(attn::kRowLse, a, s) : attn::launch_rows_f32(attn::kRowLse, a, s);
+  attn::FwdArgs a = make_args(q, k, v, out, B, H, T, d, tau, eps, workspace, ws);
+  // stage 1: row log-sum-exp (and the optional natural-log copy)
+  a.lse_nat = lse_out;
+  hipError_t e = bf16 ? attn::launch_rows_bf16(attn::kRowLse, a, s)
+                      : attn::launch_rows_f32(attn::kRowLse, a, s);
   if (e != hipSuccess) return fail_hip(e);
   a.lse_nat = nullptr;
-  // pass 2a: demand committed before each 32-row query block
+  // stage 2: demand committed before each 32-row query block
+  a.demand_out = demand_out;
   e = bf16 ? attn::launch_colsum_bf16(a, s) : attn::launch_colsum_f32(a, s);
   if (e != hipSuccess) return fail_hip(e);
   a.demand_out = nullptr;
-  // pass 2b: shares, share@V, renormalisation
-  e = bf16 ? attn::launch_rows_bf16(attn::kRowShare, a, s) : attn::launch_rows_f32(attn::kRowShare, a, s);
-  return e == hipSuccess ? ATTN_OK : fail_hip(e);
+  // stage 3: shares, share@V, renormalisation
+  return finish(bf16 ? attn::launch_rows_bf16(attn::kRowShare, a, s)
+                     : attn::launch_rows_f32(attn::kRowShare, a, s));
 }
 
 int attn_fwd(const void *q, const void *k, const void *v, void *out, int B, int H, int T, int d,

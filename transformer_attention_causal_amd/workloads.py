@@ -33,8 +33,12 @@ import numpy as np
 def bf16_round_bits(x) -> np.ndarray:
     """Round to bf16 (round-to-nearest-even on the fp32 value); return uint16 bits."""
     f = np.ascontiguousarray(x, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = f.view(np.uint32)
+    # finite inputs only: the carry cannot leave 32 bits
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
     return r.astype(np.uint16)
 
 
