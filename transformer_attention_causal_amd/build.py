@@ -17,6 +17,7 @@ SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-variable",
 ]
 

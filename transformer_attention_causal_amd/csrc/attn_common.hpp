@@ -37,11 +37,14 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-// Round-to-nearest-even fp32 -> bf16 of two values, packed low/high.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even fp32 -> bf16 of two values, packed low/high (one
+// v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
 // Eight fp32 values -> one bf16x8 operand (element e from v[e]).
@@ -64,6 +67,29 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 // Exchange a value with the lane 32 positions away (the other half of the wave).
 __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);
+}
+
+// The values a lane pair (l, l^32) holds, in half order, on both lanes:
+// .h0 from the lane in the lower half, .h1 from the lane in the upper half.
+// One v_permlane32_swap: it exchanges the upper half of its first operand with
+// the lower half of its second; fed the same value twice, the first result
+// holds the lower-half values in both halves and the second the upper-half
+// values.
+struct HalfPair {
+  float h0, h1;
+};
+__device__ __forceinline__ HalfPair halves(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float both_halves_max(float x) {
+  const HalfPair p = halves(x);
+  return fmaxf(p.h0, p.h1);
+}
+__device__ __forceinline__ float both_halves_sum(float x) {
+  const HalfPair p = halves(x);
+  return p.h0 + p.h1;
 }
 
 constexpr float kLog2e = 1.4426950408889634f;

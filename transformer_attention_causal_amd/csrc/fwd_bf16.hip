@@ -20,7 +20,9 @@
 //  * row kernels: a workgroup owns 128 query rows, wave w the 32 rows
 //    [q0+32w, q0+32w+32); K and V stream through LDS in 64-key tiles (double
 //    buffered, one barrier per tile).  Scores of a 32x32 (key, query) block
-//    come from four 32x32x16 bf16 MFMAs over d = 64.
+//    come from four 32x32x16 bf16 MFMAs over d = 64; a 64-key tile is two such
+//    blocks, handled together.  Only the one tile holding a wave's diagonal
+//    applies the causal mask.
 //  * tempered / pass 1 keep scores as S^T (lane = query, 16 keys in
 //    registers), so row maxima and sums are in-lane plus one exchange between
 //    the two wave halves, and the bf16 bids feed the P@V MFMA directly as its
@@ -32,6 +34,8 @@
 //  * pass 2a: a workgroup owns 128 keys (wave w 32 of them, held in
 //    registers) and walks the 32-row query blocks below them in order,
 //    carrying each key's running demand in a register.
+//  * Rows past the end of the sequence get a log-sum-exp of +1e30, which makes
+//    their bids exactly zero in passes 2a/2b without a per-element mask.
 #include "attn_common.hpp"
 #include "launch.hpp"
 
@@ -46,6 +50,7 @@ constexpr int kVRow = 68;       // LDS row stride of V^T tiles, bf16 (64 keys + 
 constexpr int kKTile = kBN * kKRow;        // bf16 elements per K buffer
 constexpr int kVTile = kHeadDim * kVRow;   // bf16 elements per V^T buffer
 constexpr float kRescaleSlack = 8.0f;      // log2 units the running max may lag
+constexpr float kNoRow = 1e30f;            // log-sum-exp given to rows past the end
 
 // Query index (within a wave's 32 rows) of accumulator element r in lane half h.
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
@@ -70,6 +75,143 @@ __device__ __forceinline__ bf16x8 lds_vfrag(const __bf16 *vrow, int c, int h) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
+__device__ __forceinline__ bf16x8 pack8(const float *v) {
+  return to_bf16x8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
+}
+
+// O^T[d][query] += V^T[d][keys of sub-tile t] * P^T[keys][query] for both
+// 32-row halves of d.  pf0/pf1 hold keys 0..15 / 16..31 of the sub-tile in
+// the accumulator-layout order.
+__device__ __forceinline__ void pv_update(f32x16 &o0, f32x16 &o1, const __bf16 *vt_lds, int t,
+                                          int l32, int h, const bf16x8 &pf0, const bf16x8 &pf1) {
+  const __bf16 *v0 = vt_lds + l32 * kVRow + 32 * t;
+  const __bf16 *v1 = vt_lds + (32 + l32) * kVRow + 32 * t;
+  o0 = mfma32(lds_vfrag(v0, 0, h), pf0, o0);
+  o1 = mfma32(lds_vfrag(v1, 0, h), pf0, o1);
+  o0 = mfma32(lds_vfrag(v0, 1, h), pf1, o0);
+  o1 = mfma32(lds_vfrag(v1, 1, h), pf1, o1);
+}
+
+// Per-wave state of the row kernels.
+struct RowState {
+  f32x16 o0, o1;   // O^T[d][query]: d in [0,32) and [32,64)
+  float m_run;     // running max of the scaled logits (log2 units)
+  float l_run;     // running sum of exp2(x - m_run) over this half's keys
+  float rsum;      // share row sum over this half's keys (pass 2b)
+};
+
+// Tempered softmax / pass-1 update for one 64-key tile (S^T orientation).
+template <int MODE, bool DIAG>
+__device__ __forceinline__ void st_tile(RowState &st, const bf16x8 *qf, const __bf16 *kt_lds,
+                                        const __bf16 *vt_lds, int kb, int qw0, int l32, int h,
+                                        float c2) {
+  f32x16 s[2] = {zero16(), zero16()};
+  const __bf16 *krow0 = kt_lds + l32 * kKRow;
+  const __bf16 *krow1 = kt_lds + (32 + l32) * kKRow;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    s[0] = mfma32(lds_frag(krow0, c, h), qf[c], s[0]);
+    s[1] = mfma32(lds_frag(krow1, c, h), qf[c], s[1]);
+  }
+  // lane: query qw0 + l32; element (t, r): key kb + 32t + acc_row(r, h)
+  const int qrel = qw0 + l32 - kb;   // keys with 32t + acc_row <= qrel are visible
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float v = (!DIAG || 32 * t + acc_row(r, h) <= qrel) ? s[t][r] : -INFINITY;
+      tmax = fmaxf(tmax, v);
+    }
+  }
+  tmax = both_halves_max(tmax);
+  const float tmax2 = tmax * c2;   // finite: every row sees at least its first key
+  if (__ballot(tmax2 > st.m_run + kRescaleSlack) != 0ull) {
+    const float m_new = fmaxf(st.m_run, tmax2);
+    const float alpha = fast_exp2(st.m_run - m_new);
+    st.l_run *= alpha;
+    if constexpr (MODE == kRowTempered) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        st.o0[r] *= alpha;
+        st.o1[r] *= alpha;
+      }
+    }
+    st.m_run = m_new;
+  }
+  const float mneg = -st.m_run;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float e = fast_exp2(__builtin_fmaf(s[t][r], c2, mneg));
+      if (DIAG && 32 * t + acc_row(r, h) > qrel) e = 0.0f;
+      p[r] = e;
+      st.l_run += e;
+    }
+    if constexpr (MODE == kRowTempered) pv_update(st.o0, st.o1, vt_lds, t, l32, h, pack8(p), pack8(p + 8));
+  }
+}
+
+// Pass-2b update for one 64-key tile (S orientation).
+template <bool DIAG>
+__device__ __forceinline__ void share_tile(RowState &st, const bf16x8 *qf, const float *lseq,
+                                           const bf16x8 *ident, const float *base,
+                                           const __bf16 *kt_lds, const __bf16 *vt_lds, int kb,
+                                           int qw0, int l32, int h, float c2) {
+  f32x16 s[2] = {zero16(), zero16()};
+  const __bf16 *krow0 = kt_lds + l32 * kKRow;
+  const __bf16 *krow1 = kt_lds + (32 + l32) * kKRow;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    s[0] = mfma32(qf[c], lds_frag(krow0, c, h), s[0]);
+    s[1] = mfma32(qf[c], lds_frag(krow1, c, h), s[1]);
+  }
+  const float hsel = h ? 1.0f : 0.0f;
+  // lane: key kb + 32t + l32; element r: query qw0 + acc_row(r, h)
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int krel = kb + 32 * t + l32 - qw0;   // visible to rows with acc_row >= krel
+    float p[16], run[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float e = fast_exp2(__builtin_fmaf(s[t][r], c2, -lseq[r]));
+      if (DIAG && acc_row(r, h) < krel) e = 0.0f;
+      p[r] = e;
+      run[r] = e;
+    }
+    // inclusive prefix of the bids down the 32 rows of this block: in-lane
+    // over each run of 4 consecutive rows, then across the two halves
+    float acc_off = base[t];
+    float share[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      run[4 * g + 1] += run[4 * g];
+      run[4 * g + 2] += run[4 * g + 1];
+      run[4 * g + 3] += run[4 * g + 2];
+      const HalfPair tot = halves(run[4 * g + 3]);   // rows 8g..8g+3 | 8g+4..8g+7
+      const float off = __builtin_fmaf(tot.h0, hsel, acc_off);
+      acc_off += tot.h0 + tot.h1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        share[r] = p[r] * fast_rcp(run[r] + off);
+      }
+    }
+    // transpose the shares to S^T (lane = query) with an identity MFMA
+    f32x16 sT = mfma32(pack8(share), ident[0], zero16());
+    sT = mfma32(pack8(share + 8), ident[1], sT);
+    float stv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      stv[r] = sT[r];
+      st.rsum += stv[r];
+    }
+    pv_update(st.o0, st.o1, vt_lds, t, l32, h, pack8(stv), pack8(stv + 8));
+  }
+}
+
 template <int MODE>
 __global__ void __launch_bounds__(256) rows_bf16_kernel(FwdArgs a, int nqb) {
   constexpr bool kNeedV = (MODE != kRowLse);
@@ -85,6 +227,7 @@ __global__ void __launch_bounds__(256) rows_bf16_kernel(FwdArgs a, int nqb) {
   const int q0 = qb * kBM;
   const int qw0 = q0 + 32 * w;              // first row of this wave
   const bool wave_live = qw0 < T;
+  const int kd = qw0 / kBN;                 // the tile holding this wave's diagonal
   const size_t head = (size_t)bh * T * kHeadDim;
   const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + head;
   const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + head;
@@ -96,14 +239,9 @@ __global__ void __launch_bounds__(256) rows_bf16_kernel(FwdArgs a, int nqb) {
   // Q fragments: lane holds Q[qw0 + l32][16c + 8h .. +8) -- usable as the B
   // operand of S^T = K Q^T and as the A operand of S = Q K^T.
   bf16x8 qf[4];
-  {
-    const int row = qw0 + l32;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      u32x4 u = load_row_chunk(Q, row, T, 2 * c + h);
-      qf[c] = __builtin_bit_cast(bf16x8, u);
-    }
-  }
+  for (int c = 0; c < 4; ++c)
+    qf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(Q, qw0 + l32, T, 2 * c + h));
 
   // tile loaders: K as [key][d] rows; V transposed to [d][key] on the way in.
   u32x4 kreg[2], vreg[2];
@@ -133,162 +271,80 @@ __global__ void __launch_bounds__(256) rows_bf16_kernel(FwdArgs a, int nqb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t a0 = vreg[0][i], a1 = vreg[1][i];
-        const uint32_t even = (a0 & 0xffffu) | (a1 << 16);           // d = 8dc + 2i
-        const uint32_t odd = (a0 >> 16) | (a1 & 0xffff0000u);        // d = 8dc + 2i + 1
+        const uint32_t even = __builtin_amdgcn_perm(a1, a0, 0x05040100u);  // d = 8dc + 2i
+        const uint32_t odd = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // d = 8dc + 2i + 1
         *reinterpret_cast<uint32_t *>(vt + (8 * dc + 2 * i) * kVRow + 2 * kp) = even;
         *reinterpret_cast<uint32_t *>(vt + (8 * dc + 2 * i + 1) * kVRow + 2 * kp) = odd;
       }
     }
   };
 
-  // ---- per-mode state
-  f32x16 o0 = zero16(), o1 = zero16();   // O^T[d][query]: d in [0,32) and [32,64)
-  float m_run = -INFINITY, l_run = 0.0f; // tempered / lse: running max (scaled) and sum
-  float rsum = 0.0f;                     // share: running share row sum (this half's keys)
-  float lseq[16];                        // share: lse2 of this lane's 16 query rows
-  bf16x8 ident[2];                       // share: identity operand for the transpose
+  RowState st;
+  st.o0 = zero16();
+  st.o1 = zero16();
+  st.m_run = -INFINITY;
+  st.l_run = 0.0f;
+  st.rsum = 0.0f;
+
+  float lseq[16];      // pass 2b: lse2 of this lane's 16 query rows (kNoRow past the end)
+  bf16x8 ident[2];     // pass 2b: identity operand of the transpose
   const float *cin_blk = nullptr;
-  const int qs = qw0 >> 5;
+  float cin_next[2] = {0.0f, 0.0f};
+  const float eps_floor = fmaxf(a.eps, FLT_MIN);
   if constexpr (MODE == kRowShare) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = qw0 + acc_row(r, h);
-      lseq[r] = row < T ? a.lse2[(size_t)bh * T + row] : 0.0f;
+      lseq[r] = row < T ? a.lse2[(size_t)bh * T + row] : kNoRow;
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       float e[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) e[j] = (acc_row(8 * c + j, h) == l32) ? 1.0f : 0.0f;
-      ident[c] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+      ident[c] = pack8(e);
     }
+    const int qs = qw0 >> 5;
     cin_blk = a.cin + (size_t)bh * cin_floats_per_head(T) + (size_t)16 * qs * (qs - 1);
   }
-  const float eps_floor = fmaxf(a.eps, FLT_MIN);
+  // committed demand of this wave's block on keys kt*64 + 32t + l32 (0 on and
+  // past the diagonal, where no earlier row of the sequence sees the key)
+  auto load_cin = [&](int kt) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int key = kt * kBN + 32 * t + l32;
+      cin_next[t] = (wave_live && key < qw0) ? cin_blk[key] : 0.0f;
+    }
+  };
 
   load_tile(0);
   store_tile(0);
+  if constexpr (MODE == kRowShare) load_cin(0);
   __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nkt) load_tile(kt + 1);
+    float base[2];
+    if constexpr (MODE == kRowShare) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) base[t] = fmaxf(cin_next[t] + a.eps, eps_floor);
+    }
+    if (kt + 1 < nkt) {
+      load_tile(kt + 1);
+      if constexpr (MODE == kRowShare) load_cin(kt + 1);
+    }
     const __bf16 *kt_lds = sK + buf * kKTile;
     const __bf16 *vt_lds = sV + (kNeedV ? buf * kVTile : 0);
-
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int kb = kt * kBN + 32 * s;       // first key of this 32-key sub-tile
-      if (!wave_live || kb > qw0) continue;   // wave-uniform: the sub-tile is in every row's future
-      const bool diag = (kb == qw0);
-      const __bf16 *krow = kt_lds + (32 * s + l32) * kKRow;
-
-      if constexpr (MODE == kRowTempered || MODE == kRowLse) {
-        // S^T[key][query] = K Q^T ; lane: query l32, keys kb + acc_row(r,h)
-        f32x16 sc = zero16();
-#pragma unroll
-        for (int c = 0; c < 4; ++c) sc = mfma32(lds_frag(krow, c, h), qf[c], sc);
-        float x[16];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = sc[r];
-          if (diag && acc_row(r, h) > l32) v = -INFINITY;
-          x[r] = v;
-          tmax = fmaxf(tmax, v);
-        }
-        tmax = fmaxf(tmax, swap_halves(tmax));
-        const float tmax2 = (tmax == -INFINITY) ? -INFINITY : tmax * a.c2;
-        if (__ballot(tmax2 > m_run + kRescaleSlack) != 0ull) {
-          const float m_new = fmaxf(m_run, tmax2);
-          const float alpha = fast_exp2(m_run - m_new);
-          l_run *= alpha;
-          if constexpr (MODE == kRowTempered) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) { o0[r] *= alpha; o1[r] *= alpha; }
-          }
-          m_run = m_new;
-        }
-        float p[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float y = (x[r] == -INFINITY) ? -INFINITY : __builtin_fmaf(x[r], a.c2, -m_run);
-          p[r] = fast_exp2(y);
-          l_run += p[r];
-        }
-        if constexpr (MODE == kRowTempered) {
-          const bf16x8 pf0 = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-          const bf16x8 pf1 = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
-          const __bf16 *v0 = vt_lds + l32 * kVRow + 32 * s;
-          const __bf16 *v1 = vt_lds + (32 + l32) * kVRow + 32 * s;
-          o0 = mfma32(lds_vfrag(v0, 0, h), pf0, o0);
-          o0 = mfma32(lds_vfrag(v0, 1, h), pf1, o0);
-          o1 = mfma32(lds_vfrag(v1, 0, h), pf0, o1);
-          o1 = mfma32(lds_vfrag(v1, 1, h), pf1, o1);
-        }
+    const int kb = kt * kBN;
+    if (wave_live && kt <= kd) {
+      if constexpr (MODE == kRowShare) {
+        if (kt < kd) share_tile<false>(st, qf, lseq, ident, base, kt_lds, vt_lds, kb, qw0, l32, h, a.c2);
+        else share_tile<true>(st, qf, lseq, ident, base, kt_lds, vt_lds, kb, qw0, l32, h, a.c2);
       } else {
-        // ---- pass 2b: S[query][key] = Q K^T ; lane: key kb + l32, queries acc_row(r,h)
-        f32x16 sc = zero16();
-#pragma unroll
-        for (int c = 0; c < 4; ++c) sc = mfma32(qf[c], lds_frag(krow, c, h), sc);
-        const int key = kb + l32;
-        // demand committed on this key by all rows before this 32-row block
-        float base = (kb < qw0) ? cin_blk[key] : 0.0f;
-        base = fmaxf(base + a.eps, eps_floor);
-        const bool tail = (qw0 + 32 > T);
-        float p[16], run[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = fast_exp2(__builtin_fmaf(sc[r], a.c2, -lseq[r]));
-          if (diag && l32 > acc_row(r, h)) v = 0.0f;
-          if (tail && qw0 + acc_row(r, h) >= T) v = 0.0f;
-          p[r] = v;
-          run[r] = v;
-        }
-        // inclusive prefix of the bids down the 32 query rows of this block:
-        // in-lane over runs of 4 consecutive rows, then across the two halves
-        float mine[4], other[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          run[4 * g + 1] += run[4 * g];
-          run[4 * g + 2] += run[4 * g + 1];
-          run[4 * g + 3] += run[4 * g + 2];
-          mine[g] = run[4 * g + 3];
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) other[g] = swap_halves(mine[g]);
-        float acc_off = base;
-        float share[16];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float off = acc_off + (h ? other[g] : 0.0f);
-          acc_off += mine[g] + other[g];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * g + i;
-            share[r] = p[r] * fast_rcp(run[r] + off);
-          }
-        }
-        // transpose the shares to S^T (lane = query) with an identity MFMA
-        const bf16x8 sb0 = to_bf16x8(share[0], share[1], share[2], share[3], share[4],
-                                     share[5], share[6], share[7]);
-        const bf16x8 sb1 = to_bf16x8(share[8], share[9], share[10], share[11], share[12],
-                                     share[13], share[14], share[15]);
-        f32x16 st = mfma32(sb0, ident[0], zero16());
-        st = mfma32(sb1, ident[1], st);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) rsum += st[r];
-        const bf16x8 pf0 = to_bf16x8(st[0], st[1], st[2], st[3], st[4], st[5], st[6], st[7]);
-        const bf16x8 pf1 = to_bf16x8(st[8], st[9], st[10], st[11], st[12], st[13], st[14], st[15]);
-        const __bf16 *v0 = vt_lds + l32 * kVRow + 32 * s;
-        const __bf16 *v1 = vt_lds + (32 + l32) * kVRow + 32 * s;
-        o0 = mfma32(lds_vfrag(v0, 0, h), pf0, o0);
-        o0 = mfma32(lds_vfrag(v0, 1, h), pf1, o0);
-        o1 = mfma32(lds_vfrag(v1, 0, h), pf0, o1);
-        o1 = mfma32(lds_vfrag(v1, 1, h), pf1, o1);
+        if (kt < kd) st_tile<MODE, false>(st, qf, kt_lds, vt_lds, kb, qw0, l32, h, a.c2);
+        else st_tile<MODE, true>(st, qf, kt_lds, vt_lds, kb, qw0, l32, h, a.c2);
       }
     }
-
     if (kt + 1 < nkt) store_tile(buf ^ 1);
     __syncthreads();
   }
@@ -297,11 +353,11 @@ __global__ void __launch_bounds__(256) rows_bf16_kernel(FwdArgs a, int nqb) {
   const int row = qw0 + l32;
   float denom;
   if constexpr (MODE == kRowShare) {
-    denom = rsum + swap_halves(rsum);
+    denom = both_halves_sum(st.rsum);
   } else {
-    denom = l_run + swap_halves(l_run);
+    denom = both_halves_sum(st.l_run);
     if (h == 0 && row < T) {
-      const float lse2 = m_run + __builtin_log2f(denom);
+      const float lse2 = st.m_run + __builtin_log2f(denom);
       if (a.lse2) a.lse2[(size_t)bh * T + row] = lse2;
       if (a.lse_nat) a.lse_nat[(size_t)bh * T + row] = lse2 * kLn2;
     }
@@ -314,10 +370,10 @@ __global__ void __launch_bounds__(256) rows_bf16_kernel(FwdArgs a, int nqb) {
       for (int g = 0; g < 4; ++g) {
         const int d0 = 8 * g + 4 * h;
         u32x2 lo, hi;
-        lo[0] = pack_bf16x2(o0[4 * g] * inv, o0[4 * g + 1] * inv);
-        lo[1] = pack_bf16x2(o0[4 * g + 2] * inv, o0[4 * g + 3] * inv);
-        hi[0] = pack_bf16x2(o1[4 * g] * inv, o1[4 * g + 1] * inv);
-        hi[1] = pack_bf16x2(o1[4 * g + 2] * inv, o1[4 * g + 3] * inv);
+        lo[0] = pack_bf16x2(st.o0[4 * g] * inv, st.o0[4 * g + 1] * inv);
+        lo[1] = pack_bf16x2(st.o0[4 * g + 2] * inv, st.o0[4 * g + 3] * inv);
+        hi[0] = pack_bf16x2(st.o1[4 * g] * inv, st.o1[4 * g + 1] * inv);
+        hi[1] = pack_bf16x2(st.o1[4 * g + 2] * inv, st.o1[4 * g + 3] * inv);
         *reinterpret_cast<u32x2 *>(O + d0) = lo;
         *reinterpret_cast<u32x2 *>(O + 32 + d0) = hi;
       }
@@ -328,10 +384,11 @@ __global__ void __launch_bounds__(256) rows_bf16_kernel(FwdArgs a, int nqb) {
 // ---------------------------------------------------------------- pass 2a
 
 constexpr int kCB = 128;  // keys per workgroup (4 waves x 32)
+constexpr int kCQ = 64;   // query rows per LDS tile (two 32-row blocks)
 
 __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, int nqs) {
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[2][32 * kKRow];
-  __shared__ __attribute__((aligned(16))) float sL[2][32];
+  __shared__ __attribute__((aligned(16))) __bf16 sQ[2][kCQ * kKRow];
+  __shared__ __attribute__((aligned(16))) float sL[2][kCQ];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
@@ -351,58 +408,69 @@ __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, in
 #pragma unroll
   for (int c = 0; c < 4; ++c) kf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(K, key, T, 2 * c + h));
 
-  const int qs0 = (kb * kCB) >> 5;
-  u32x4 qreg;
+  const int qt0 = (kb * kCB) / kCQ;          // first 64-row query tile
+  const int nqt = (T + kCQ - 1) / kCQ;
+  u32x4 qreg[2];
   float lreg = 0.0f;
-  auto load_q = [&](int qs) {
-    const int row = 32 * qs + (tid >> 3);
-    qreg = load_row_chunk(Q, row, T, tid & 7);
-    if (tid < 32) lreg = (32 * qs + tid < T) ? L2[32 * qs + tid] : 0.0f;
+  auto load_q = [&](int qt) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = tid + 256 * i;
+      qreg[i] = load_row_chunk(Q, qt * kCQ + (u >> 3), T, u & 7);
+    }
+    if (tid < kCQ) lreg = (qt * kCQ + tid < T) ? L2[qt * kCQ + tid] : kNoRow;
   };
   auto store_q = [&](int buf) {
-    *reinterpret_cast<u32x4 *>(&sQ[buf][(tid >> 3) * kKRow + (tid & 7) * 8]) = qreg;
-    if (tid < 32) sL[buf][tid] = lreg;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = tid + 256 * i;
+      *reinterpret_cast<u32x4 *>(&sQ[buf][(u >> 3) * kKRow + (u & 7) * 8]) = qreg[i];
+    }
+    if (tid < kCQ) sL[buf][tid] = lreg;
   };
 
   float run = 0.0f;  // demand this half-lane's rows have put on `key` so far
-  load_q(qs0);
+  load_q(qt0);
   store_q(0);
   __syncthreads();
-  for (int qs = qs0; qs < nqs; ++qs) {
-    const int buf = (qs - qs0) & 1;
-    if (qs + 1 < nqs) load_q(qs + 1);
-    if (wave_live && 32 * qs + 31 >= kw0) {
-      const bool diag = (32 * qs == kw0);
-      const bool tail = (32 * qs + 32 > T);
-      f32x16 sc = zero16();
-      const __bf16 *qrow = &sQ[buf][l32 * kKRow];
+  for (int qt = qt0; qt < nqt; ++qt) {
+    const int buf = (qt - qt0) & 1;
+    if (qt + 1 < nqt) load_q(qt + 1);
+    if (wave_live) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) sc = mfma32(lds_frag(qrow, c, h), kf[c], sc);
-      if (32 * qs > kw0) {
-        // demand committed before block qs: rows < 32 qs, both halves
-        const float total = run + swap_halves(run);
-        if (h == 0 && key < T) cin[(size_t)16 * qs * (qs - 1) + key] = total;
-      }
-      float part = 0.0f;
+      for (int sb = 0; sb < 2; ++sb) {
+        const int qs = 2 * qt + sb;              // 32-row block
+        if (qs >= nqs || 32 * qs + 31 < kw0) continue;   // block entirely before the keys
+        f32x16 sc = zero16();
+        const __bf16 *qrow = &sQ[buf][(32 * sb + l32) * kKRow];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 lq = *reinterpret_cast<const f32x4 *>(&sL[buf][8 * g + 4 * h]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * g + i;
-          float v = fast_exp2(__builtin_fmaf(sc[r], a.c2, -lq[i]));
-          if (diag && l32 > acc_row(r, h)) v = 0.0f;
-          if (tail && 32 * qs + acc_row(r, h) >= T) v = 0.0f;
-          part += v;
+        for (int c = 0; c < 4; ++c) sc = mfma32(lds_frag(qrow, c, h), kf[c], sc);
+        if (32 * qs > kw0) {
+          // demand committed before block qs: rows < 32 qs, both halves
+          const float total = both_halves_sum(run);
+          if (h == 0 && key < T) cin[(size_t)16 * qs * (qs - 1) + key] = total;
         }
+        const bool diag = (32 * qs == kw0);
+        float part = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 lq = *reinterpret_cast<const f32x4 *>(&sL[buf][32 * sb + 8 * g + 4 * h]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i;
+            float v = fast_exp2(__builtin_fmaf(sc[r], a.c2, -lq[i]));
+            if (diag && l32 > acc_row(r, h)) v = 0.0f;
+            part += v;
+          }
+        }
+        run += part;
       }
-      run += part;
     }
-    if (qs + 1 < nqs) store_q(buf ^ 1);
+    if (qt + 1 < nqt) store_q(buf ^ 1);
     __syncthreads();
   }
   if (a.demand_out && wave_live) {
-    const float total = run + swap_halves(run);
+    const float total = both_halves_sum(run);
     if (h == 0 && key < T) a.demand_out[(size_t)bh * T + key] = total;
   }
 }
