@@ -154,29 +154,26 @@ __device__ __forceinline__ void st_tile(RowState &st, const bf16x8 *qf, const __
   }
 }
 
-// Pass-2b update for one 64-key tile (S orientation).
+// Pass-2b update for one 64-key tile (S orientation), one 32-key sub-tile at
+// a time.
 template <bool DIAG>
 __device__ __forceinline__ void share_tile(RowState &st, const bf16x8 *qf, const float *lseq,
                                            const bf16x8 *ident, const float *base,
                                            const __bf16 *kt_lds, const __bf16 *vt_lds, int kb,
                                            int qw0, int l32, int h, float c2) {
-  f32x16 s[2] = {zero16(), zero16()};
-  const __bf16 *krow0 = kt_lds + l32 * kKRow;
-  const __bf16 *krow1 = kt_lds + (32 + l32) * kKRow;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    s[0] = mfma32(qf[c], lds_frag(krow0, c, h), s[0]);
-    s[1] = mfma32(qf[c], lds_frag(krow1, c, h), s[1]);
-  }
   const float hsel = h ? 1.0f : 0.0f;
-  // lane: key kb + 32t + l32; element r: query qw0 + acc_row(r, h)
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
+    // lane: key kb + 32t + l32; element r: query qw0 + acc_row(r, h)
+    const __bf16 *krow = kt_lds + (32 * t + l32) * kKRow;
+    f32x16 s = zero16();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s = mfma32(qf[c], lds_frag(krow, c, h), s);
     const int krel = kb + 32 * t + l32 - qw0;   // visible to rows with acc_row >= krel
     float p[16], run[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float e = fast_exp2(__builtin_fmaf(s[t][r], c2, -lseq[r]));
+      float e = fast_exp2(__builtin_fmaf(s[r], c2, -lseq[r]));
       if (DIAG && acc_row(r, h) < krel) e = 0.0f;
       p[r] = e;
       run[r] = e;
@@ -184,7 +181,6 @@ __device__ __forceinline__ void share_tile(RowState &st, const bf16x8 *qf, const
     // inclusive prefix of the bids down the 32 rows of this block: in-lane
     // over each run of 4 consecutive rows, then across the two halves
     float acc_off = base[t];
-    float share[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       run[4 * g + 1] += run[4 * g];
@@ -196,31 +192,38 @@ __device__ __forceinline__ void share_tile(RowState &st, const bf16x8 *qf, const
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * g + i;
-        share[r] = p[r] * fast_rcp(run[r] + off);
+        run[r] = p[r] * fast_rcp(run[r] + off);   // the share
       }
     }
     // transpose the shares to S^T (lane = query) with an identity MFMA
-    f32x16 sT = mfma32(pack8(share), ident[0], zero16());
-    sT = mfma32(pack8(share + 8), ident[1], sT);
-    float stv[16];
+    f32x16 sT = mfma32(pack8(run), ident[0], zero16());
+    sT = mfma32(pack8(run + 8), ident[1], sT);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      stv[r] = sT[r];
-      st.rsum += stv[r];
+      p[r] = sT[r];
+      st.rsum += p[r];
     }
-    pv_update(st.o0, st.o1, vt_lds, t, l32, h, pack8(stv), pack8(stv + 8));
+    pv_update(st.o0, st.o1, vt_lds, t, l32, h, pack8(p), pack8(p + 8));
   }
 }
 
+// Waves per SIMD each mode is compiled for (register budget 512/n per lane).
 template <int MODE>
-__global__ void __launch_bounds__(256) rows_bf16_kernel(FwdArgs a, int nqb) {
+struct RowOccupancy {
+  static constexpr int value = MODE == kRowLse ? 4 : 3;
+};
+
+template <int MODE>
+__global__ void __launch_bounds__(256, RowOccupancy<MODE>::value) rows_bf16_kernel(FwdArgs a, int nqb) {
   constexpr bool kNeedV = (MODE != kRowLse);
   __shared__ __attribute__((aligned(16))) __bf16 sK[2 * kKTile];
   __shared__ __attribute__((aligned(16))) __bf16 sV[kNeedV ? 2 * kVTile : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
-  // heaviest query blocks first; consecutive workgroups take different heads
+  // heaviest query blocks first; consecutive workgroups take different heads.
+  // Workgroups go to the 8 XCDs round-robin, so with B*H a multiple of 8 each
+  // XCD serves the same B*H/8 heads throughout and keeps their K/V in its L2.
   const int bh = blockIdx.x % a.BH;
   const int qb = nqb - 1 - blockIdx.x / a.BH;
   const int T = a.T;
