@@ -62,6 +62,16 @@ __device__ __forceinline__ u32x4 load_row_chunk(const __bf16 *base, int row, int
   return z;
 }
 
+// Load one 16-byte chunk of row min(row, T-1): rows past the end repeat the
+// last row.  Used for tiles streamed inside loops: every such row is either
+// causally masked or weighted by an exact zero, and the load being
+// unconditional keeps the compiler from waiting on in-flight loads before it
+// zero-fills a register.
+__device__ __forceinline__ u32x4 load_row_clamped(const __bf16 *base, int row, int T, int chunk) {
+  const int r = row < T ? row : T - 1;
+  return *reinterpret_cast<const u32x4 *>(base + (size_t)r * kHeadDim + chunk * 8);
+}
+
 // A/B operand fragment for d-chunk c of a 64-wide bf16 row held in LDS.
 __device__ __forceinline__ bf16x8 lds_frag(const __bf16 *row, int c, int h) {
   return *reinterpret_cast<const bf16x8 *>(row + 16 * c + 8 * h);
@@ -253,12 +263,12 @@ __global__ void __launch_bounds__(256, RowOccupancy<MODE>::value) rows_bf16_kern
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int u = tid + 256 * i;
-      kreg[i] = load_row_chunk(K, key0 + (u >> 3), T, u & 7);
+      kreg[i] = load_row_clamped(K, key0 + (u >> 3), T, u & 7);
     }
     if constexpr (kNeedV) {
       const int kp = tid & 31, dc = tid >> 5;
-      vreg[0] = load_row_chunk(V, key0 + 2 * kp, T, dc);
-      vreg[1] = load_row_chunk(V, key0 + 2 * kp + 1, T, dc);
+      vreg[0] = load_row_clamped(V, key0 + 2 * kp, T, dc);
+      vreg[1] = load_row_clamped(V, key0 + 2 * kp + 1, T, dc);
     }
   };
   auto store_tile = [&](int buf) {
@@ -319,6 +329,12 @@ __global__ void __launch_bounds__(256, RowOccupancy<MODE>::value) rows_bf16_kern
       cin_next[t] = (wave_live && key < qw0) ? cin_blk[key] : 0.0f;
     }
   };
+
+  // Wait here for the one-time loads (Q fragments, row LSEs).  Without this
+  // the compiler cannot prove them complete on every path into the loop and
+  // waits for all outstanding loads -- the tile prefetch included -- at their
+  // first use in every iteration.
+  __builtin_amdgcn_s_waitcnt(0);
 
   load_tile(0);
   store_tile(0);
@@ -411,17 +427,24 @@ __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, in
 #pragma unroll
   for (int c = 0; c < 4; ++c) kf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(K, key, T, 2 * c + h));
 
+  __builtin_amdgcn_s_waitcnt(0);             // K fragments: see the row kernels
+
   const int qt0 = (kb * kCB) / kCQ;          // first 64-row query tile
   const int nqt = (T + kCQ - 1) / kCQ;
   u32x4 qreg[2];
   float lreg = 0.0f;
+  bool lvalid = false;
   auto load_q = [&](int qt) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int u = tid + 256 * i;
-      qreg[i] = load_row_chunk(Q, qt * kCQ + (u >> 3), T, u & 7);
+      qreg[i] = load_row_clamped(Q, qt * kCQ + (u >> 3), T, u & 7);
     }
-    if (tid < kCQ) lreg = (qt * kCQ + tid < T) ? L2[qt * kCQ + tid] : kNoRow;
+    if (tid < kCQ) {
+      const int row = qt * kCQ + tid;
+      lvalid = row < T;
+      lreg = L2[lvalid ? row : T - 1];
+    }
   };
   auto store_q = [&](int buf) {
 #pragma unroll
@@ -429,7 +452,7 @@ __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, in
       const int u = tid + 256 * i;
       *reinterpret_cast<u32x4 *>(&sQ[buf][(u >> 3) * kKRow + (u & 7) * 8]) = qreg[i];
     }
-    if (tid < kCQ) sL[buf][tid] = lreg;
+    if (tid < kCQ) sL[buf][tid] = lvalid ? lreg : kNoRow;   // rows past the end bid nothing
   };
 
   float run = 0.0f;  // demand this half-lane's rows have put on `key` so far
