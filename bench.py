@@ -17,11 +17,20 @@ the decode step's HBM GB/s (K + V + demand read + demand write) are reported
 under ``components``.  Kernel durations come from HIP events recorded on the
 stream the library launches on, inside the timed region.
 
+``roofline.traffic`` is the measured HBM bytes per launch of the roofline
+kernel, read from the committed counter summary under ``profiles/`` when that
+summary was taken from the same kernel sources and build flags (a SHA-256 over
+them is stored with it), else null.  ``--copy-calibration-mib N`` appends a
+plain streaming fp32 copy kernel of N MiB read and N MiB written after the
+timed steps: the known-size reference that scales the HBM byte counters.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--copy-calibration-mib N]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -34,6 +43,10 @@ sys.path.insert(0, ROOT)
 METRIC = "fwd TFLOP/s (dilution & tempered) at T=16K; decode HBM GB/s at 32K cache"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E peak
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_dilution_t16k_decode_32k.md")
+CSRC = os.path.join(ROOT, "transformer_attention_causal_amd", "csrc")
+FWD_SOURCES = ("attn_common.hpp", "launch.hpp", "fwd_bf16.hip")
+DEC_SOURCES = ("attn_common.hpp", "launch.hpp", "decode.hip")
 
 
 def log(msg):
@@ -44,12 +57,40 @@ def causal_pairs(B, H, T):
     return B * H * T * (T + 1) // 2
 
 
+def source_digest(files):
+    """SHA-256 over the kernel sources and the hipcc flags they are built with."""
+    from transformer_attention_causal_amd.build import FLAGS
+    h = hashlib.sha256(" ".join(FLAGS).encode())
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(key, files):
+    """HBM bytes per launch of kernel ``key`` from the committed counter summary,
+    or None when it is absent or was taken from other sources."""
+    try:
+        with open(TRAFFIC_SUMMARY) as fh:
+            for line in fh:
+                if line.startswith("traffic-record: "):
+                    rec = json.loads(line[len("traffic-record: "):])
+                    ent = rec.get(key)
+                    if ent and ent.get("sources_sha256") == source_digest(files):
+                        return ent["bytes_per_launch"]
+    except OSError:
+        pass
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run a streaming fp32 copy of this many MiB three times")
     ap.add_argument("--cpu-heads", type=int, default=4,
                     help="heads of the T=16384 dilution workload the oracle runs for the CPU baseline")
     args = ap.parse_args()
@@ -135,6 +176,16 @@ def main():
     ms = {n: float(np.mean(seg[n])) for n in names}
     ms_min = {n: float(np.min(seg[n])) for n in names}
     log("bench: per-launch ms " + json.dumps({n: round(ms[n], 4) for n in names}))
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        log(f"bench: calibration copy {args.copy_calibration_mib} MiB read + written, 3 launches")
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ------------------------------------------------------------ throughputs
     d = w.d
@@ -185,7 +236,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(shares_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("rows_bf16_kernel<kRowShare>", FWD_SOURCES),
             "units": f"{causal_pairs(w.B, w.H, w.T)} causal pairs x {4 * d} flops",
         },
         "roofline_decode": {
@@ -195,7 +246,7 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("attn_decode", DEC_SOURCES),
         },
     }
 
