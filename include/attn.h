@@ -71,7 +71,8 @@ size_t attn_fwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype)
 /* Causal attention forward pass (both modes; see top of file).
  *   q, k, v    [B,H,T,d] device arrays of `dtype` (inputs, not modified)
  *   out        [B,H,T,d] device array of `dtype` (output; may not alias q/k/v)
- *   B, H, T    batch, heads, sequence length (each >= 1)
+ *   B, H, T    batch, heads, sequence length (each >= 1; T <= 16777216, the
+ *              kernels address one head's rows with 32-bit byte offsets)
  *   d          head dimension; only 64 is supported (else ATTN_ENOTSUP)
  *   tau        logit multiplier, finite and >= 0 (tau = 0 gives uniform bids)
  *   mode       ATTN_TEMPERED or ATTN_DILUTION

@@ -47,6 +47,7 @@ def errors(got: np.ndarray, ref: np.ndarray):
 
 def assert_close(got, ref, dtype: str, what: str = ""):
     max_abs, rel_rms = errors(got, ref)
+    print(f"{what}: max-abs {max_abs:.3e} rel-RMS {rel_rms:.3e}")
     if dtype == "bf16":
         assert max_abs <= BF16_MAX_ABS and rel_rms <= BF16_REL_RMS, \
             f"{what}: max-abs {max_abs:.3e} rel-RMS {rel_rms:.3e}"

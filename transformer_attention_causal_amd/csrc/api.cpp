@@ -90,6 +90,8 @@ bool dec_workspace(int S, int H, int Lcap, DecWorkspace *ws) {
 
 bool shape_ok(int B, int H, int T) {
   if (B <= 0 || H <= 0 || T <= 0) return false;
+  // one head's rows are addressed with 32-bit byte offsets (buffer loads)
+  if (T > (1 << 24)) return false;
   // element counts must fit the kernels' 64-bit offsets and 32-bit grids
   const size_t BH = (size_t)B * H;
   if (BH > (size_t)INT32_MAX / 1024) return false;

@@ -30,6 +30,30 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x32_bf16: A lane holds A[lane % 16][8 (lane / 16) + e],
+// B lane holds B[8 (lane / 16) + e][lane % 16], D lane holds
+// D[4 (lane / 16) + r][lane % 16], r = 0..3.
+__device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row sums on the matrix cores.  A bf16x8 operand laid out for the 32x32x16
+// product with lane = query (lane % 32) and 8 keys per lane, read as the B
+// operand of the 16x16x32 product, puts query 16 (g & 1) + n in column n of
+// lane group g = lane / 16.  Against this selector as A (1 where bit 2 of the
+// row matches bit 0 of the lane group), row m of column n sums the 16 keys of
+// query 16 ((m >> 2) & 1) + n, so every element a lane receives in D is the
+// key sum of its own query lane % 32.
+__device__ __forceinline__ bf16x8 rowsum_selector(int lane) {
+  const __bf16 v = (__bf16)((((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? 1.0f : 0.0f);
+  bf16x8 a;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = v;
+  return a;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
@@ -61,6 +85,14 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float v0, float v1, float v2, float 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// x as a bf16 pair: low half the rounded value, high half the rounding
+// residual, also rounded.  Their fp32 sum restores x to about 2^-17 relative.
+__device__ __forceinline__ uint32_t split2_bf16(float x) {
+  const uint32_t hi = pack_bf16x2(x, 0.0f);
+  const uint32_t lo = pack_bf16x2(x - __uint_as_float(hi << 16), 0.0f);
+  return hi | (lo << 16);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
@@ -90,6 +122,20 @@ __device__ __forceinline__ float both_halves_max(float x) {
 __device__ __forceinline__ float both_halves_sum(float x) {
   const HalfPair p = halves(x);
   return p.h0 + p.h1;
+}
+
+// Buffer resource over `bytes` bytes starting at `base` (raw buffer, 32-bit
+// data format).  The hardware range check makes every load at a byte offset
+// at or past `bytes` return zeros, so a tile running off the end of a
+// sequence needs no mask, clamp or branch; the offsets stay 32-bit.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0);
+}
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voffset, 0, 0));
 }
 
 constexpr float kLog2e = 1.4426950408889634f;

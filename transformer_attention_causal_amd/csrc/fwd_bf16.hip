@@ -62,16 +62,6 @@ __device__ __forceinline__ u32x4 load_row_chunk(const __bf16 *base, int row, int
   return z;
 }
 
-// Load one 16-byte chunk of row min(row, T-1): rows past the end repeat the
-// last row.  Used for tiles streamed inside loops: every such row is either
-// causally masked or weighted by an exact zero, and the load being
-// unconditional keeps the compiler from waiting on in-flight loads before it
-// zero-fills a register.
-__device__ __forceinline__ u32x4 load_row_clamped(const __bf16 *base, int row, int T, int chunk) {
-  const int r = row < T ? row : T - 1;
-  return *reinterpret_cast<const u32x4 *>(base + (size_t)r * kHeadDim + chunk * 8);
-}
-
 // A/B operand fragment for d-chunk c of a 64-wide bf16 row held in LDS.
 __device__ __forceinline__ bf16x8 lds_frag(const __bf16 *row, int c, int h) {
   return *reinterpret_cast<const bf16x8 *>(row + 16 * c + 8 * h);
@@ -106,15 +96,17 @@ __device__ __forceinline__ void pv_update(f32x16 &o0, f32x16 &o1, const __bf16 *
 struct RowState {
   f32x16 o0, o1;   // O^T[d][query]: d in [0,32) and [32,64)
   float m_run;     // running max of the scaled logits (log2 units)
-  float l_run;     // running sum of exp2(x - m_run) over this half's keys
-  float rsum;      // share row sum over this half's keys (pass 2b)
+  float l_run;     // fp32 row sum of exp2(x - m_run) over this half's keys (kernels
+                   // that output the log-sum-exp)
+  f32x4 lsum;      // row sum, on the matrix cores, of the bf16 weights fed to P@V
+                   // (tempered: exp2(x - m_run), pass 2b: the shares), all elements equal
 };
 
 // Tempered softmax / pass-1 update for one 64-key tile (S^T orientation).
-template <int MODE, bool DIAG>
-__device__ __forceinline__ void st_tile(RowState &st, const bf16x8 *qf, const __bf16 *kt_lds,
-                                        const __bf16 *vt_lds, int kb, int qw0, int l32, int h,
-                                        float c2) {
+template <int MODE, bool FP32SUM, bool DIAG>
+__device__ __forceinline__ void st_tile(RowState &st, const bf16x8 *qf, const bf16x8 &sel,
+                                        const __bf16 *kt_lds, const __bf16 *vt_lds, int kb,
+                                        int qw0, int l32, int h, float c2) {
   f32x16 s[2] = {zero16(), zero16()};
   const __bf16 *krow0 = kt_lds + l32 * kKRow;
   const __bf16 *krow1 = kt_lds + (32 + l32) * kKRow;
@@ -139,7 +131,8 @@ __device__ __forceinline__ void st_tile(RowState &st, const bf16x8 *qf, const __
   if (__ballot(tmax2 > st.m_run + kRescaleSlack) != 0ull) {
     const float m_new = fmaxf(st.m_run, tmax2);
     const float alpha = fast_exp2(st.m_run - m_new);
-    st.l_run *= alpha;
+    if constexpr (FP32SUM) st.l_run *= alpha;
+    else st.lsum *= alpha;
     if constexpr (MODE == kRowTempered) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -158,72 +151,147 @@ __device__ __forceinline__ void st_tile(RowState &st, const bf16x8 *qf, const __
       float e = fast_exp2(__builtin_fmaf(s[t][r], c2, mneg));
       if (DIAG && 32 * t + acc_row(r, h) > qrel) e = 0.0f;
       p[r] = e;
-      st.l_run += e;
+      if constexpr (FP32SUM) st.l_run += e;
     }
-    if constexpr (MODE == kRowTempered) pv_update(st.o0, st.o1, vt_lds, t, l32, h, pack8(p), pack8(p + 8));
+    if constexpr (MODE == kRowTempered) {
+      const bf16x8 pf0 = pack8(p), pf1 = pack8(p + 8);
+      if constexpr (!FP32SUM) {
+        st.lsum = mfma16(sel, pf0, st.lsum);
+        st.lsum = mfma16(sel, pf1, st.lsum);
+      }
+      pv_update(st.o0, st.o1, vt_lds, t, l32, h, pf0, pf1);
+    }
   }
 }
 
-// Pass-2b update for one 64-key tile (S orientation), one 32-key sub-tile at
-// a time.
+// Pass-2b constant B operands, built once per wave.  Slot (h, e) of operand
+// j carries query acc_row(8j + e, h) of the wave's block (the order in which
+// a lane of the S layout holds its 16 queries); column n is query n.
+struct ShareConsts {
+  bf16x8 upre[2];   // inclusive prefix: 1 where the slot's query <= query n
+  bf16x8 ident[2];  // transpose: 1 where the slot's query == query n
+  bf16x8 bone;      // committed-demand slots: 1 in slots (0, 0..1), else 0
+};
+
+__device__ __forceinline__ ShareConsts share_consts(int l32, int h) {
+  ShareConsts c;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    float u[8], id[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int qs = acc_row(8 * j + e, h);
+      u[e] = qs <= l32 ? 1.0f : 0.0f;
+      id[e] = qs == l32 ? 1.0f : 0.0f;
+    }
+    c.upre[j] = pack8(u);
+    c.ident[j] = pack8(id);
+  }
+  const float one = h == 0 ? 1.0f : 0.0f;
+  c.bone = to_bf16x8(one, one, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f);
+  return c;
+}
+
+// Pass-2b update for one 64-key tile, one 32-key sub-tile at a time.
+//  1. S = Q K^T with lane = key and the 16 queries in registers; bids
+//     p = exp2(c2 s - lse2(query)) (zero above the diagonal), packed to bf16.
+//  2. The bids, as the A operand (row = key, slot = query), are multiplied by
+//     three constant B operands, transposing them to lane = query:
+//       D = committed + eps + sum of the bids of the block's rows up to and
+//           including the column's query (the inclusive column prefix;
+//           committed + eps enters as its stored bf16 (hi, lo) pair);
+//       P = the bids themselves.
+//  3. share = P / D, the row sums, and share @ V on the matrix cores.
+template <bool DIAG>
+__device__ __forceinline__ void share_bids(const f32x16 &s, const float *lseq, int krel, int h,
+                                           float c2, bf16x8 &pa0, bf16x8 &pa1) {
+  float p[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float e = fast_exp2(__builtin_fmaf(s[r], c2, -lseq[r]));
+    if (DIAG && acc_row(r, h) < krel) e = 0.0f;
+    p[r] = e;
+  }
+  pa0 = pack8(p);
+  pa1 = pack8(p + 8);
+}
+
+// D (inclusive prefix + committed + eps) and P, both transposed to lane = query.
+__device__ __forceinline__ void share_prefix(const bf16x8 &pa0, const bf16x8 &pa1, uint32_t base,
+                                             const ShareConsts &sc, f32x16 &d, f32x16 &pt) {
+  const u32x4 bw = {base, 0u, 0u, 0u};
+  d = mfma32(pa0, sc.upre[0], zero16());
+  pt = mfma32(pa0, sc.ident[0], zero16());
+  d = mfma32(pa1, sc.upre[1], d);
+  pt = mfma32(pa1, sc.ident[1], pt);
+  d = mfma32(__builtin_bit_cast(bf16x8, bw), sc.bone, d);
+}
+
+__device__ __forceinline__ void share_values(const f32x16 &d, const f32x16 &pt, bf16x8 &sf0,
+                                             bf16x8 &sf1) {
+  float sh[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sh[r] = pt[r] * fast_rcp(d[r]);
+  sf0 = pack8(sh);
+  sf1 = pack8(sh + 8);
+}
+
 template <bool DIAG>
 __device__ __forceinline__ void share_tile(RowState &st, const bf16x8 *qf, const float *lseq,
-                                           const bf16x8 *ident, const float *base,
+                                           const ShareConsts &sc, const bf16x8 &sel,
+                                           const uint32_t *base,
                                            const __bf16 *kt_lds, const __bf16 *vt_lds, int kb,
                                            int qw0, int l32, int h, float c2) {
-  const float hsel = h ? 1.0f : 0.0f;
+  // The two 32-key sub-tiles are independent until share@V; their stages are
+  // written staggered so that each sub-tile's matrix-core work overlaps the
+  // other's vector work:
+  //   scores 0,1 | bids 0 | prefix 0, bids 1 | prefix 1, shares 0 |
+  //   P@V 0, shares 1 | P@V 1
+  // sub-tile t, lane: key kb + 32t + l32; element r: query qw0 + acc_row(r, h)
+  const __bf16 *krow0 = kt_lds + l32 * kKRow;
+  const __bf16 *krow1 = kt_lds + (32 + l32) * kKRow;
+  f32x16 s0 = zero16(), s1 = zero16();
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    // lane: key kb + 32t + l32; element r: query qw0 + acc_row(r, h)
-    const __bf16 *krow = kt_lds + (32 * t + l32) * kKRow;
-    f32x16 s = zero16();
-#pragma unroll
-    for (int c = 0; c < 4; ++c) s = mfma32(qf[c], lds_frag(krow, c, h), s);
-    const int krel = kb + 32 * t + l32 - qw0;   // visible to rows with acc_row >= krel
-    float p[16], run[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float e = fast_exp2(__builtin_fmaf(s[r], c2, -lseq[r]));
-      if (DIAG && acc_row(r, h) < krel) e = 0.0f;
-      p[r] = e;
-      run[r] = e;
-    }
-    // inclusive prefix of the bids down the 32 rows of this block: in-lane
-    // over each run of 4 consecutive rows, then across the two halves
-    float acc_off = base[t];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      run[4 * g + 1] += run[4 * g];
-      run[4 * g + 2] += run[4 * g + 1];
-      run[4 * g + 3] += run[4 * g + 2];
-      const HalfPair tot = halves(run[4 * g + 3]);   // rows 8g..8g+3 | 8g+4..8g+7
-      const float off = __builtin_fmaf(tot.h0, hsel, acc_off);
-      acc_off += tot.h0 + tot.h1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g + i;
-        run[r] = p[r] * fast_rcp(run[r] + off);   // the share
-      }
-    }
-    // transpose the shares to S^T (lane = query) with an identity MFMA
-    f32x16 sT = mfma32(pack8(run), ident[0], zero16());
-    sT = mfma32(pack8(run + 8), ident[1], sT);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p[r] = sT[r];
-      st.rsum += p[r];
-    }
-    pv_update(st.o0, st.o1, vt_lds, t, l32, h, pack8(p), pack8(p + 8));
+  for (int c = 0; c < 4; ++c) {
+    s0 = mfma32(qf[c], lds_frag(krow0, c, h), s0);
+    s1 = mfma32(qf[c], lds_frag(krow1, c, h), s1);
   }
+  const int krel0 = kb + l32 - qw0;   // key visible to rows with acc_row >= krel
+  bf16x8 pa00, pa01, pa10, pa11;
+  share_bids<DIAG>(s0, lseq, krel0, h, c2, pa00, pa01);
+  // sub-tile t transposed, lane: query qw0 + l32; element r: key kb + 32t + acc_row(r, h)
+  f32x16 d0, pt0, d1, pt1;
+  share_prefix(pa00, pa01, base[0], sc, d0, pt0);
+  share_bids<DIAG>(s1, lseq, krel0 + 32, h, c2, pa10, pa11);
+  share_prefix(pa10, pa11, base[1], sc, d1, pt1);
+  bf16x8 sf00, sf01, sf10, sf11;
+  share_values(d0, pt0, sf00, sf01);
+  st.lsum = mfma16(sel, sf00, st.lsum);
+  st.lsum = mfma16(sel, sf01, st.lsum);
+  pv_update(st.o0, st.o1, vt_lds, 0, l32, h, sf00, sf01);
+  share_values(d1, pt1, sf10, sf11);
+  st.lsum = mfma16(sel, sf10, st.lsum);
+  st.lsum = mfma16(sel, sf11, st.lsum);
+  pv_update(st.o0, st.o1, vt_lds, 1, l32, h, sf10, sf11);
+#ifdef ATTN_SHARE_SCHED
+  // issue pattern for the tile: one matrix-core op, then vector ops
+#pragma unroll
+  for (int i = 0; i < 30; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, ATTN_SHARE_SCHED, 0);
+  }
+#endif
 }
 
 // Waves per SIMD each mode is compiled for (register budget 512/n per lane).
 template <int MODE>
 struct RowOccupancy {
-  static constexpr int value = MODE == kRowLse ? 4 : 3;
+  static constexpr int value = MODE == kRowLse ? 4 : (MODE == kRowShare ? 2 : 3);
 };
 
-template <int MODE>
+// FP32SUM: row sums in fp32 on the vector ALUs (exact log-sum-exp output);
+// otherwise on the matrix cores over the bf16 weights.
+template <int MODE, bool FP32SUM>
 __global__ void __launch_bounds__(256, RowOccupancy<MODE>::value) rows_bf16_kernel(FwdArgs a, int nqb) {
   constexpr bool kNeedV = (MODE != kRowLse);
   __shared__ __attribute__((aligned(16))) __bf16 sK[2 * kKTile];
@@ -257,18 +325,21 @@ __global__ void __launch_bounds__(256, RowOccupancy<MODE>::value) rows_bf16_kern
     qf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(Q, qw0 + l32, T, 2 * c + h));
 
   // tile loaders: K as [key][d] rows; V transposed to [d][key] on the way in.
+  // Buffer loads with per-lane byte offsets fixed for the whole loop; keys
+  // past the end of the sequence read as zeros.
   u32x4 kreg[2], vreg[2];
+  const uint32_t koff0 = 16u * tid, koff1 = 16u * (tid + 256);
+  const uint32_t voff0 = 256u * (tid & 31) + 16u * (tid >> 5), voff1 = voff0 + 128u;
   auto load_tile = [&](int kt) {
-    const int key0 = kt * kBN;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int u = tid + 256 * i;
-      kreg[i] = load_row_clamped(K, key0 + (u >> 3), T, u & 7);
-    }
+    const int key0 = kt * kBN;                          // < T for every tile loaded
+    const int bytes = (T - key0) * (kHeadDim * 2);
+    const auto rk = make_rsrc(K + (size_t)key0 * kHeadDim, bytes);
+    kreg[0] = buf_load16(rk, koff0);
+    kreg[1] = buf_load16(rk, koff1);
     if constexpr (kNeedV) {
-      const int kp = tid & 31, dc = tid >> 5;
-      vreg[0] = load_row_clamped(V, key0 + 2 * kp, T, dc);
-      vreg[1] = load_row_clamped(V, key0 + 2 * kp + 1, T, dc);
+      const auto rv = make_rsrc(V + (size_t)key0 * kHeadDim, bytes);
+      vreg[0] = buf_load16(rv, voff0);
+      vreg[1] = buf_load16(rv, voff1);
     }
   };
   auto store_tile = [&](int buf) {
@@ -297,36 +368,33 @@ __global__ void __launch_bounds__(256, RowOccupancy<MODE>::value) rows_bf16_kern
   st.o1 = zero16();
   st.m_run = -INFINITY;
   st.l_run = 0.0f;
-  st.rsum = 0.0f;
+  st.lsum = zero4();
+  const bf16x8 sel = rowsum_selector(lane);
 
   float lseq[16];      // pass 2b: lse2 of this lane's 16 query rows (kNoRow past the end)
-  bf16x8 ident[2];     // pass 2b: identity operand of the transpose
-  const float *cin_blk = nullptr;
-  float cin_next[2] = {0.0f, 0.0f};
-  const float eps_floor = fmaxf(a.eps, FLT_MIN);
+  ShareConsts sc;      // pass 2b: constant operands of the prefix and transpose
+  const uint32_t *cin_blk = nullptr;
+  uint32_t cin_next[2] = {0u, 0u};
+  // committed + eps of a key no earlier row sees (on and past the diagonal)
+  const uint32_t eps_word = split2_bf16(fmaxf(a.eps, FLT_MIN));
   if constexpr (MODE == kRowShare) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = qw0 + acc_row(r, h);
       lseq[r] = row < T ? a.lse2[(size_t)bh * T + row] : kNoRow;
     }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float e[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) e[j] = (acc_row(8 * c + j, h) == l32) ? 1.0f : 0.0f;
-      ident[c] = pack8(e);
-    }
+    sc = share_consts(l32, h);
     const int qs = qw0 >> 5;
-    cin_blk = a.cin + (size_t)bh * cin_floats_per_head(T) + (size_t)16 * qs * (qs - 1);
+    cin_blk = reinterpret_cast<const uint32_t *>(a.cin) + (size_t)bh * cin_floats_per_head(T) +
+              (size_t)16 * qs * (qs - 1);
   }
-  // committed demand of this wave's block on keys kt*64 + 32t + l32 (0 on and
-  // past the diagonal, where no earlier row of the sequence sees the key)
+  // committed demand (+ eps, as a bf16 pair) of this wave's block on keys
+  // kt*64 + 32t + l32; on and past the diagonal no earlier row sees the key
   auto load_cin = [&](int kt) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int key = kt * kBN + 32 * t + l32;
-      cin_next[t] = (wave_live && key < qw0) ? cin_blk[key] : 0.0f;
+      cin_next[t] = (wave_live && key < qw0) ? cin_blk[key] : eps_word;
     }
   };
 
@@ -343,10 +411,10 @@ __global__ void __launch_bounds__(256, RowOccupancy<MODE>::value) rows_bf16_kern
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
-    float base[2];
+    uint32_t base[2];
     if constexpr (MODE == kRowShare) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) base[t] = fmaxf(cin_next[t] + a.eps, eps_floor);
+      for (int t = 0; t < 2; ++t) base[t] = cin_next[t];
     }
     if (kt + 1 < nkt) {
       load_tile(kt + 1);
@@ -357,11 +425,11 @@ __global__ void __launch_bounds__(256, RowOccupancy<MODE>::value) rows_bf16_kern
     const int kb = kt * kBN;
     if (wave_live && kt <= kd) {
       if constexpr (MODE == kRowShare) {
-        if (kt < kd) share_tile<false>(st, qf, lseq, ident, base, kt_lds, vt_lds, kb, qw0, l32, h, a.c2);
-        else share_tile<true>(st, qf, lseq, ident, base, kt_lds, vt_lds, kb, qw0, l32, h, a.c2);
+        if (kt < kd) share_tile<false>(st, qf, lseq, sc, sel, base, kt_lds, vt_lds, kb, qw0, l32, h, a.c2);
+        else share_tile<true>(st, qf, lseq, sc, sel, base, kt_lds, vt_lds, kb, qw0, l32, h, a.c2);
       } else {
-        if (kt < kd) st_tile<MODE, false>(st, qf, kt_lds, vt_lds, kb, qw0, l32, h, a.c2);
-        else st_tile<MODE, true>(st, qf, kt_lds, vt_lds, kb, qw0, l32, h, a.c2);
+        if (kt < kd) st_tile<MODE, FP32SUM, false>(st, qf, sel, kt_lds, vt_lds, kb, qw0, l32, h, a.c2);
+        else st_tile<MODE, FP32SUM, true>(st, qf, sel, kt_lds, vt_lds, kb, qw0, l32, h, a.c2);
       }
     }
     if (kt + 1 < nkt) store_tile(buf ^ 1);
@@ -370,11 +438,8 @@ __global__ void __launch_bounds__(256, RowOccupancy<MODE>::value) rows_bf16_kern
 
   if (!wave_live) return;
   const int row = qw0 + l32;
-  float denom;
-  if constexpr (MODE == kRowShare) {
-    denom = both_halves_sum(st.rsum);
-  } else {
-    denom = both_halves_sum(st.l_run);
+  const float denom = FP32SUM ? both_halves_sum(st.l_run) : st.lsum[0];
+  if constexpr (MODE != kRowShare) {
     if (h == 0 && row < T) {
       const float lse2 = st.m_run + __builtin_log2f(denom);
       if (a.lse2) a.lse2[(size_t)bh * T + row] = lse2;
@@ -405,6 +470,21 @@ __global__ void __launch_bounds__(256, RowOccupancy<MODE>::value) rows_bf16_kern
 constexpr int kCB = 128;  // keys per workgroup (4 waves x 32)
 constexpr int kCQ = 64;   // query rows per LDS tile (two 32-row blocks)
 
+// Sum of the bids exp2(sc) down this lane's 16 query rows of a 32x32 block
+// (S layout: lane = key); on the diagonal block rows before the key see
+// nothing of it.
+template <bool DIAG>
+__device__ __forceinline__ float colsum_bids(const f32x16 &sc, int l32, int h) {
+  float part = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float v = fast_exp2(sc[r]);
+    if (DIAG && l32 > acc_row(r, h)) v = 0.0f;
+    part += v;
+  }
+  return part;
+}
+
 __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, int nqs) {
   __shared__ __attribute__((aligned(16))) __bf16 sQ[2][kCQ * kKRow];
   __shared__ __attribute__((aligned(16))) float sL[2][kCQ];
@@ -421,7 +501,10 @@ __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, in
   const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + head;
   const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + head;
   const float *L2 = a.lse2 + (size_t)bh * T;
-  float *cin = a.cin + (size_t)bh * cin_floats_per_head(T);
+  // committed demand + eps of each (32-row block, key), stored as a bf16 pair
+  uint32_t *cin = reinterpret_cast<uint32_t *>(a.cin) + (size_t)bh * cin_floats_per_head(T);
+  const float eps_floor = fmaxf(a.eps, FLT_MIN);
+  auto committed_word = [&](float total) { return split2_bf16(fmaxf(total + a.eps, eps_floor)); };
 
   bf16x8 kf[4];
 #pragma unroll
@@ -435,11 +518,10 @@ __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, in
   float lreg = 0.0f;
   bool lvalid = false;
   auto load_q = [&](int qt) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int u = tid + 256 * i;
-      qreg[i] = load_row_clamped(Q, qt * kCQ + (u >> 3), T, u & 7);
-    }
+    const int row0 = qt * kCQ;                         // < T for every tile loaded
+    const auto rq = make_rsrc(Q + (size_t)row0 * kHeadDim, (T - row0) * (kHeadDim * 2));
+    qreg[0] = buf_load16(rq, 16u * tid);
+    qreg[1] = buf_load16(rq, 16u * (tid + 256));
     if (tid < kCQ) {
       const int row = qt * kCQ + tid;
       lvalid = row < T;
@@ -452,7 +534,32 @@ __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, in
       const int u = tid + 256 * i;
       *reinterpret_cast<u32x4 *>(&sQ[buf][(u >> 3) * kKRow + (u & 7) * 8]) = qreg[i];
     }
-    if (tid < kCQ) sL[buf][tid] = lvalid ? lreg : kNoRow;   // rows past the end bid nothing
+    if (tid < kCQ) sL[buf][tid] = lvalid ? -lreg : -kNoRow;   // rows past the end bid nothing
+  };
+
+  // Scores of the 32x32 block (rows 32 sb.. of Q buffer `buf`, this wave's
+  // keys) in the S layout, as log2 of the bid: c2 s - lse2 of the query
+  // (element r: query acc_row(r, h)).
+  auto block_scores = [&](int buf, int sb) {
+    f32x16 sc = zero16();
+    const __bf16 *qrow = &sQ[buf][(32 * sb + l32) * kKRow];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf16x8 qa = lds_frag(qrow, c, h);
+      sc = mfma32(qa, kf[c], sc);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 nl = *reinterpret_cast<const f32x4 *>(&sL[buf][32 * sb + 8 * g + 4 * h]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[4 * g + i] = __builtin_fmaf(sc[4 * g + i], a.c2, nl[i]);
+    }
+    return sc;
+  };
+  // demand committed before block qs (rows < 32 qs, both halves)
+  auto commit = [&](int qs, float r) {
+    const float total = both_halves_sum(r);
+    if (h == 0 && key < T) cin[(size_t)16 * qs * (qs - 1) + key] = committed_word(total);
   };
 
   float run = 0.0f;  // demand this half-lane's rows have put on `key` so far
@@ -463,33 +570,28 @@ __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, in
     const int buf = (qt - qt0) & 1;
     if (qt + 1 < nqt) load_q(qt + 1);
     if (wave_live) {
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const int qs = 2 * qt + sb;              // 32-row block
-        if (qs >= nqs || 32 * qs + 31 < kw0) continue;   // block entirely before the keys
-        f32x16 sc = zero16();
-        const __bf16 *qrow = &sQ[buf][(32 * sb + l32) * kKRow];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) sc = mfma32(lds_frag(qrow, c, h), kf[c], sc);
-        if (32 * qs > kw0) {
-          // demand committed before block qs: rows < 32 qs, both halves
-          const float total = both_halves_sum(run);
-          if (h == 0 && key < T) cin[(size_t)16 * qs * (qs - 1) + key] = total;
+      const int qs0 = 2 * qt;
+      if (32 * qs0 > kw0 && qs0 + 1 < nqs) {
+        // both blocks below the diagonal block and inside the sequence: the
+        // two independent MFMA chains interleave
+        const f32x16 s0 = block_scores(buf, 0), s1 = block_scores(buf, 1);
+        const float r0 = run;
+        const float r1 = r0 + colsum_bids<false>(s0, l32, h);
+        run = r1 + colsum_bids<false>(s1, l32, h);
+        const float t0 = both_halves_sum(r0), t1 = both_halves_sum(r1);
+        if (h == 0 && key < T) {
+          cin[(size_t)16 * qs0 * (qs0 - 1) + key] = committed_word(t0);
+          cin[(size_t)16 * (qs0 + 1) * qs0 + key] = committed_word(t1);
         }
-        const bool diag = (32 * qs == kw0);
-        float part = 0.0f;
+      } else {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 lq = *reinterpret_cast<const f32x4 *>(&sL[buf][32 * sb + 8 * g + 4 * h]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * g + i;
-            float v = fast_exp2(__builtin_fmaf(sc[r], a.c2, -lq[i]));
-            if (diag && l32 > acc_row(r, h)) v = 0.0f;
-            part += v;
-          }
+        for (int sb = 0; sb < 2; ++sb) {
+          const int qs = qs0 + sb;                  // 32-row block
+          if (qs >= nqs || 32 * qs + 31 < kw0) continue;   // past the end, or before the keys
+          const f32x16 sc = block_scores(buf, sb);
+          if (32 * qs > kw0) commit(qs, run);
+          run += (32 * qs == kw0) ? colsum_bids<true>(sc, l32, h) : colsum_bids<false>(sc, l32, h);
         }
-        run += part;
       }
     }
     if (qt + 1 < nqt) store_q(buf ^ 1);
@@ -505,9 +607,15 @@ hipError_t launch_rows_bf16(int mode, const FwdArgs &a, hipStream_t s) {
   const int nqb = (a.T + kBM - 1) / kBM;
   dim3 grid((unsigned)(nqb * a.BH)), block(256);
   switch (mode) {
-    case kRowTempered: hipLaunchKernelGGL(rows_bf16_kernel<kRowTempered>, grid, block, 0, s, a, nqb); break;
-    case kRowLse: hipLaunchKernelGGL(rows_bf16_kernel<kRowLse>, grid, block, 0, s, a, nqb); break;
-    default: hipLaunchKernelGGL(rows_bf16_kernel<kRowShare>, grid, block, 0, s, a, nqb); break;
+    case kRowTempered:
+      // an exact log-sum-exp output needs fp32 row sums
+      if (a.lse2 || a.lse_nat)
+        hipLaunchKernelGGL((rows_bf16_kernel<kRowTempered, true>), grid, block, 0, s, a, nqb);
+      else
+        hipLaunchKernelGGL((rows_bf16_kernel<kRowTempered, false>), grid, block, 0, s, a, nqb);
+      break;
+    case kRowLse: hipLaunchKernelGGL((rows_bf16_kernel<kRowLse, true>), grid, block, 0, s, a, nqb); break;
+    default: hipLaunchKernelGGL((rows_bf16_kernel<kRowShare, false>), grid, block, 0, s, a, nqb); break;
   }
   return hipGetLastError();
 }

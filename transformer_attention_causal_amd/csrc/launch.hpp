@@ -18,7 +18,9 @@ struct FwdArgs {
   void *out;
   float *lse2;          // [BH*T] workspace (dilution) or NULL
   float *lse_nat;       // [BH*T] optional natural-log output
-  float *cin;           // committed demand per 32-row query block (dilution)
+  float *cin;           // committed demand per 32-row query block (dilution); the
+                        // bf16 path stores each entry as a bf16 (hi, lo) pair of
+                        // committed + eps in the same 32 bits
   float *demand_out;    // [BH*T] optional final column totals (dilution)
   int BH, T;
   float c2;             // tau / sqrt(d) * log2(e)
