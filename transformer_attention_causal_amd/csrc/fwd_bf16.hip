@@ -50,6 +50,7 @@ constexpr int kVRow = 68;       // LDS row stride of V^T tiles, bf16 (64 keys + 
 constexpr int kKTile = kBN * kKRow;        // bf16 elements per K buffer
 constexpr int kVTile = kHeadDim * kVRow;   // bf16 elements per V^T buffer
 constexpr float kRescaleSlack = 8.0f;      // log2 units the running max may lag
+constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64: largest tile sum kept
 constexpr float kNoRow = 1e30f;            // log-sum-exp given to rows past the end
 
 // Query index (within a wave's 32 rows) of accumulator element r in lane half h.
@@ -102,7 +103,57 @@ struct RowState {
                    // (tempered: exp2(x - m_run), pass 2b: the shares), all elements equal
 };
 
+// Bring the running max up to the tile's (masked) maximum and rescale what
+// has been accumulated against the old one.
+template <int MODE, bool FP32SUM, bool DIAG>
+__device__ __forceinline__ void st_rescale(RowState &st, const f32x16 *s, int qrel, int h,
+                                           float c2) {
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float v = (!DIAG || 32 * t + acc_row(r, h) <= qrel) ? s[t][r] : -INFINITY;
+      tmax = fmaxf(tmax, v);
+    }
+  }
+  tmax = both_halves_max(tmax);
+  const float m_new = fmaxf(st.m_run, tmax * c2);   // finite: every row sees its first key
+  const float alpha = fast_exp2(st.m_run - m_new);  // 0 while m_run is still -inf
+  if constexpr (FP32SUM) st.l_run *= alpha;
+  else st.lsum *= alpha;
+  if constexpr (MODE == kRowTempered) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      st.o0[r] *= alpha;
+      st.o1[r] *= alpha;
+    }
+  }
+  st.m_run = m_new;
+}
+
+template <bool DIAG>
+__device__ __forceinline__ void st_weights(const f32x16 *s, float m_run, int qrel, int h, float c2,
+                                           float *p) {
+  const float mneg = -m_run;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float e = fast_exp2(__builtin_fmaf(s[t][r], c2, mneg));
+      if (DIAG && 32 * t + acc_row(r, h) > qrel) e = 0.0f;
+      p[16 * t + r] = e;
+    }
+  }
+}
+
 // Tempered softmax / pass-1 update for one 64-key tile (S^T orientation).
+// The running max m_run is lazy.  With fp32 row sums the tile is weighted
+// against the current m_run directly and the max is only taken when a lane's
+// tile sum leaves [0, 2^64] (weights that large are still exact in fp32 and
+// bf16; an overflow or the first tile, where m_run = -inf, shows up there as
+// inf).  Otherwise the tile max is taken first and m_run moves when it is
+// exceeded by more than kRescaleSlack.
 template <int MODE, bool FP32SUM, bool DIAG>
 __device__ __forceinline__ void st_tile(RowState &st, const bf16x8 *qf, const bf16x8 &sel,
                                         const __bf16 *kt_lds, const __bf16 *vt_lds, int kb,
@@ -117,49 +168,52 @@ __device__ __forceinline__ void st_tile(RowState &st, const bf16x8 *qf, const bf
   }
   // lane: query qw0 + l32; element (t, r): key kb + 32t + acc_row(r, h)
   const int qrel = qw0 + l32 - kb;   // keys with 32t + acc_row <= qrel are visible
-  float tmax = -INFINITY;
+  if constexpr (FP32SUM) {
+    float p[32];
+    st_weights<DIAG>(s, st.m_run, qrel, h, c2, p);
+    float ts = 0.0f;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+    for (int i = 0; i < 32; ++i) ts += p[i];
+    if (__ballot(!(ts <= kSumLimit)) != 0ull) {
+      st_rescale<MODE, FP32SUM, DIAG>(st, s, qrel, h, c2);
+      st_weights<DIAG>(s, st.m_run, qrel, h, c2, p);
+      ts = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float v = (!DIAG || 32 * t + acc_row(r, h) <= qrel) ? s[t][r] : -INFINITY;
-      tmax = fmaxf(tmax, v);
+      for (int i = 0; i < 32; ++i) ts += p[i];
     }
-  }
-  tmax = both_halves_max(tmax);
-  const float tmax2 = tmax * c2;   // finite: every row sees at least its first key
-  if (__ballot(tmax2 > st.m_run + kRescaleSlack) != 0ull) {
-    const float m_new = fmaxf(st.m_run, tmax2);
-    const float alpha = fast_exp2(st.m_run - m_new);
-    if constexpr (FP32SUM) st.l_run *= alpha;
-    else st.lsum *= alpha;
+    st.l_run += ts;
     if constexpr (MODE == kRowTempered) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        pv_update(st.o0, st.o1, vt_lds, t, l32, h, pack8(p + 16 * t), pack8(p + 16 * t + 8));
+    }
+  } else {
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        st.o0[r] *= alpha;
-        st.o1[r] *= alpha;
+        const float v = (!DIAG || 32 * t + acc_row(r, h) <= qrel) ? s[t][r] : -INFINITY;
+        tmax = fmaxf(tmax, v);
       }
     }
-    st.m_run = m_new;
-  }
-  const float mneg = -st.m_run;
+    tmax = both_halves_max(tmax);
+    if (__ballot(tmax * c2 > st.m_run + kRescaleSlack) != 0ull)
+      st_rescale<MODE, FP32SUM, DIAG>(st, s, qrel, h, c2);
+    const float mneg = -st.m_run;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    float p[16];
+    for (int t = 0; t < 2; ++t) {
+      float p[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float e = fast_exp2(__builtin_fmaf(s[t][r], c2, mneg));
-      if (DIAG && 32 * t + acc_row(r, h) > qrel) e = 0.0f;
-      p[r] = e;
-      if constexpr (FP32SUM) st.l_run += e;
-    }
-    if constexpr (MODE == kRowTempered) {
+      for (int r = 0; r < 16; ++r) {
+        float e = fast_exp2(__builtin_fmaf(s[t][r], c2, mneg));
+        if (DIAG && 32 * t + acc_row(r, h) > qrel) e = 0.0f;
+        p[r] = e;
+      }
       const bf16x8 pf0 = pack8(p), pf1 = pack8(p + 8);
-      if constexpr (!FP32SUM) {
-        st.lsum = mfma16(sel, pf0, st.lsum);
-        st.lsum = mfma16(sel, pf1, st.lsum);
-      }
-      pv_update(st.o0, st.o1, vt_lds, t, l32, h, pf0, pf1);
+      st.lsum = mfma16(sel, pf0, st.lsum);
+      st.lsum = mfma16(sel, pf1, st.lsum);
+      if constexpr (MODE == kRowTempered) pv_update(st.o0, st.o1, vt_lds, t, l32, h, pf0, pf1);
     }
   }
 }
