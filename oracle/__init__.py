@@ -14,6 +14,9 @@ module only builds/loads that library and marshals numpy arrays.  Functions:
   operator": bids, exclusive column cumsum, shares, renormalised A, A@v).
 * ``dilution_decode_step`` -- its cached-decode step (same page: K/V cache
   plus one running demand total per key and head).
+* ``attn_bwd`` -- exact gradients (dq, dk, dv) of either operator by the
+  chain rule through its definition (the dilution page ships training kernels
+  with exact gradients), plus the dilution row sums of the shares.
 * ``yarn_t`` / ``yarn_tau`` -- t = 0.1 ln s + 1 and sqrt(t) (YaRN page).
 
 Inputs may be numpy float64/float32 arrays or ``Bf16`` wrappers around raw
@@ -104,6 +107,8 @@ def _declare(lib):
         lib.oracle_dilution_decode_step.restype = i
         lib.oracle_dilution_decode_step.argtypes = [vp, vp, vp, i, dp, dp, i, i, i, i, ip,
                                                     d, d, ip, i]
+        lib.oracle_attn_bwd.restype = i
+        lib.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, i, dp, dp, dp, dp, i, i, i, i, d, d, i]
 
 
 def _as_input(x):
@@ -224,3 +229,27 @@ def dilution_decode_step(q, kcache, vcache, demand: np.ndarray, tau: float = 1.0
     if rc != 0:
         raise RuntimeError(f"oracle_dilution_decode_step failed ({rc})")
     return out
+
+
+def attn_bwd(q, k, v, dout, tau: float = 1.0, eps: float = 1e-6, mode: int = 1):
+    """Exact gradients of the scalar sum(out * dout).  q,k,v,dout: [B,H,T,d] in
+    one storage type; mode 0 tempered, 1 dilution.  Returns (dq, dk, dv, rsum)
+    in fp64; rsum [B,H,T] holds the dilution row sums of the shares (NaN for
+    tempered)."""
+    lib = _load()
+    qa, c1 = _as_input(q)
+    ka, c2 = _as_input(k)
+    va, c3 = _as_input(v)
+    ga, c4 = _as_input(dout)
+    code = _same_code(c1, c2, c3, c4)
+    B, H, T, d = qa.shape
+    dq = np.zeros((B, H, T, d))
+    dk = np.zeros((B, H, T, d))
+    dv = np.zeros((B, H, T, d))
+    rs = np.full((B, H, T), np.nan)
+    rc = lib.oracle_attn_bwd(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, ga.ctypes.data,
+                             code, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(rs), B, H, T, d,
+                             float(tau), float(eps), int(mode))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attn_bwd failed ({rc})")
+    return dq, dk, dv, rs

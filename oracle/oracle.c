@@ -18,7 +18,8 @@
  *            multiplier (code cells In[14] and In[16]).
  *   [DIL]    "DilutionAttention v0.1.0 - results", section "The operator":
  *            the four-line definition (bids, committed, share, A/out) and the
- *            sentence on cached decoding.
+ *            sentence on cached decoding; section "Everything behind these
+ *            charts" (the release's kernels carry exact gradients).
  *
  * Readings where the pages leave a step open (each is also listed in the
  * design notes):
@@ -399,6 +400,136 @@ int oracle_dilution_decode_step(const void *q, const void *kc, const void *vc, i
         failed = 1;
     }
   }
+  return failed ? -2 : 0;
+}
+
+/*
+ * Exact gradients of both operators ([DIL] "Everything behind these charts":
+ * the kernels train with exact gradients), by the chain rule through the
+ * forward definitions above, one head at a time with every (i, j) matrix
+ * materialised.  For dilution, with p the bids, C the committed demand,
+ * D = C + p + eps, sigma = p / D, r_i = sum_j sigma_ij, a = sigma / r and
+ * o_i = sum_j a_ij v_j, given dO:
+ *   dV_j      = sum_i a_ij dO_i
+ *   dA_ij     = <dO_i, v_j>,            delta_i = sum_j a_ij dA_ij
+ *   dsigma_ij = (dA_ij - delta_i) / r_i
+ *   sigma depends on p_ij directly and through D_ij, and C_i''j of every
+ *   later row i'' > i contains p_ij, so with g_ij = dsigma_ij p_ij / D_ij^2
+ *   dp_ij     = dsigma_ij / D_ij - sum_{i'' >= i} g_i''j
+ *   (entries with p_ij = 0 -- masked or underflowed -- carry no gradient)
+ *   dS_ij     = p_ij (dp_ij - sum_j' p_ij' dp_ij')     (softmax)
+ *   dQ_i = c sum_j dS_ij k_j,  dK_j = c sum_i dS_ij q_i,  c = tau / sqrt(d).
+ * Tempered is the same with a = p, so dp_ij = dA_ij.
+ *
+ * q,k,v,dout: [B,H,T,d] in dtype; dq,dk,dv: [B,H,T,d] fp64.  rsum (optional,
+ * dilution): [B,H,T] fp64, the row sums r_i.  mode: 0 tempered, 1 dilution.
+ */
+static int bwd_one_head(const void *q, const void *k, const void *v, const void *dout, int dtype,
+                        double *dq, double *dk, double *dv, double *rsum, int T, int d, double c,
+                        double eps, int mode, int bh) {
+  const size_t base = (size_t)bh * T * d, TT = (size_t)T * T;
+  double *Q = malloc(sizeof(double) * (size_t)T * d), *K = malloc(sizeof(double) * (size_t)T * d);
+  double *V = malloc(sizeof(double) * (size_t)T * d), *dO = malloc(sizeof(double) * (size_t)T * d);
+  double *P = calloc(TT, sizeof(double)), *Dn = calloc(TT, sizeof(double));
+  double *A = calloc(TT, sizeof(double)), *dP = calloc(TT, sizeof(double));
+  double *r = calloc((size_t)T, sizeof(double)), *col = calloc((size_t)T, sizeof(double));
+  int rc = 0;
+  if (!Q || !K || !V || !dO || !P || !Dn || !A || !dP || !r || !col) {
+    rc = -2;
+    goto done;
+  }
+  widen_block(Q, q, dtype, base, (size_t)T * d);
+  widen_block(K, k, dtype, base, (size_t)T * d);
+  widen_block(V, v, dtype, base, (size_t)T * d);
+  widen_block(dO, dout, dtype, base, (size_t)T * d);
+  /* forward: bids, committed demand, shares, weights A */
+  for (int i = 0; i < T; ++i) causal_bids(Q + (size_t)i * d, K, i, d, c, P + (size_t)i * T, 0);
+  for (int i = 0; i < T; ++i) {
+    double *Pi = P + (size_t)i * T, *Ai = A + (size_t)i * T, *Di = Dn + (size_t)i * T;
+    if (mode == 0) {
+      for (int j = 0; j <= i; ++j) Ai[j] = Pi[j];
+      continue;
+    }
+    for (int j = 0; j <= i; ++j) {
+      Di[j] = col[j] + Pi[j] + eps;          /* col[j] = committed C_ij */
+      Ai[j] = Pi[j] > 0.0 ? Pi[j] / Di[j] : 0.0;
+      r[i] += Ai[j];
+    }
+    for (int j = 0; j <= i; ++j) Ai[j] /= r[i];
+    for (int j = 0; j <= i; ++j) col[j] += Pi[j];
+  }
+  if (rsum && mode == 1) memcpy(rsum + (size_t)bh * T, r, sizeof(double) * (size_t)T);
+  /* dA and the gradient with respect to the bids */
+  for (int i = 0; i < T; ++i) {
+    const double *Ai = A + (size_t)i * T;
+    double *dPi = dP + (size_t)i * T;
+    double delta = 0.0;
+    for (int j = 0; j <= i; ++j) {
+      dPi[j] = dot(dO + (size_t)i * d, V + (size_t)j * d, d);   /* dA_ij for now */
+      delta += Ai[j] * dPi[j];
+    }
+    if (mode == 1)
+      for (int j = 0; j <= i; ++j) dPi[j] = (dPi[j] - delta) / r[i];   /* dsigma_ij */
+  }
+  if (mode == 1) {
+    /* dp_ij = dsigma_ij / D_ij - (inclusive suffix sum of g down column j) */
+    for (int j = 0; j < T; ++j) col[j] = 0.0;
+    for (int i = T - 1; i >= 0; --i) {
+      const double *Pi = P + (size_t)i * T, *Di = Dn + (size_t)i * T;
+      double *dPi = dP + (size_t)i * T;
+      for (int j = 0; j <= i; ++j) {
+        if (Pi[j] > 0.0) {
+          col[j] += dPi[j] * Pi[j] / (Di[j] * Di[j]);
+          dPi[j] = dPi[j] / Di[j] - col[j];
+        } else {
+          dPi[j] = 0.0;
+        }
+      }
+    }
+  }
+  /* softmax: dS = p (dp - sum_j p dp), kept in dP */
+  for (int i = 0; i < T; ++i) {
+    const double *Pi = P + (size_t)i * T;
+    double *dPi = dP + (size_t)i * T;
+    double rho = 0.0;
+    for (int j = 0; j <= i; ++j) rho += Pi[j] * dPi[j];
+    for (int j = 0; j <= i; ++j) dPi[j] = Pi[j] * (dPi[j] - rho);
+  }
+  for (int i = 0; i < T; ++i) {
+    const double *Si = dP + (size_t)i * T;
+    double *dqi = dq + base + (size_t)i * d;
+    for (int e = 0; e < d; ++e) dqi[e] = 0.0;
+    for (int j = 0; j <= i; ++j)
+      for (int e = 0; e < d; ++e) dqi[e] += c * Si[j] * K[(size_t)j * d + e];
+  }
+  for (int j = 0; j < T; ++j) {
+    double *dkj = dk + base + (size_t)j * d, *dvj = dv + base + (size_t)j * d;
+    for (int e = 0; e < d; ++e) dkj[e] = dvj[e] = 0.0;
+    for (int i = j; i < T; ++i) {
+      const double s = dP[(size_t)i * T + j], a = A[(size_t)i * T + j];
+      for (int e = 0; e < d; ++e) {
+        dkj[e] += c * s * Q[(size_t)i * d + e];
+        dvj[e] += a * dO[(size_t)i * d + e];
+      }
+    }
+  }
+done:
+  free(Q); free(K); free(V); free(dO); free(P); free(Dn); free(A); free(dP); free(r); free(col);
+  return rc;
+}
+
+int oracle_attn_bwd(const void *q, const void *k, const void *v, const void *dout, int dtype,
+                    double *dq, double *dk, double *dv, double *rsum, int B, int H, int T, int d,
+                    double tau, double eps, int mode) {
+  if (B <= 0 || H <= 0 || T <= 0 || d <= 0 || (mode != 0 && mode != 1)) return -1;
+  const double c = tau / sqrt((double)d);
+  int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int bh = 0; bh < B * H; ++bh)
+    if (bwd_one_head(q, k, v, dout, dtype, dq, dk, dv, rsum, T, d, c, eps, mode, bh) != 0) {
+#pragma omp atomic write
+      failed = 1;
+    }
   return failed ? -2 : 0;
 }
 

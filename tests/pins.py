@@ -324,4 +324,90 @@ def pin_bf16_widening():
     assert np.array_equal(t1, t2)
 
 
+# ------------------------------------------------------------------ gradients
+
+def _fd_grads(fwd, q, k, v, dout, h=1e-6):
+    """Central finite differences of sum(fwd(q, k, v) * dout)."""
+    grads = []
+    for name in ("q", "k", "v"):
+        X = {"q": q, "k": k, "v": v}[name]
+        g = np.zeros_like(X)
+        for idx in np.ndindex(X.shape):
+            args = {"q": q, "k": k, "v": v}
+            Xp, Xm = X.copy(), X.copy()
+            Xp[idx] += h
+            Xm[idx] -= h
+            args[name] = Xp
+            lp = float(np.sum(fwd(**args) * dout))
+            args[name] = Xm
+            lm = float(np.sum(fwd(**args) * dout))
+            g[idx] = (lp - lm) / (2 * h)
+        grads.append(g)
+    return grads
+
+
+def pin_bwd_finite_differences():
+    """Both gradients agree with central differences of the pinned forwards."""
+    rng = _rng(21)
+    for T, tau, eps in [(1, 1.0, 1e-6), (5, 1.0, 1e-6), (9, 1.3, 0.0), (7, 0.7, 0.3)]:
+        q, k, v, do = (rng.standard_normal((1, 2, T, 4)) for _ in range(4))
+        for mode in (0, 1):
+            if mode == 0:
+                fwd = lambda q, k, v: oracle.tempered_fwd(q, k, v, tau)[0]
+            else:
+                fwd = lambda q, k, v: oracle.dilution_fwd(q, k, v, tau, eps)[0]
+            got = oracle.attn_bwd(q, k, v, do, tau, eps, mode)[:3]
+            for g, n in zip(got, _fd_grads(fwd, q, k, v, do)):
+                scale = max(1.0, float(np.max(np.abs(n))))
+                assert np.max(np.abs(g - n)) <= 2e-7 * scale, (T, tau, eps, mode)
+
+
+def pin_bwd_tempered_vs_library():
+    """Tempered gradients equal torch autograd through CPU fp64 SDPA."""
+    import torch
+
+    rng = _rng(22)
+    q, k, v, do = (rng.standard_normal((2, 2, 48, 16)) for _ in range(4))
+    tau = 1.2
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, is_causal=True, scale=tau / math.sqrt(16))
+    out.backward(torch.from_numpy(do))
+    got = oracle.attn_bwd(q, k, v, do, tau, 0.0, 0)[:3]
+    for g, t in zip(got, (tq.grad, tk.grad, tv.grad)):
+        assert np.max(np.abs(g - t.numpy())) <= 1e-12
+
+
+def pin_bwd_dilution_softmax_limit():
+    """With eps far above all demand, shares are p / eps and the renormalised
+    weights are the softmax: the dilution gradients tend to the tempered ones."""
+    rng = _rng(23)
+    q, k, v, do = (rng.standard_normal((1, 2, 32, 8)) for _ in range(4))
+    dil = oracle.attn_bwd(q, k, v, do, 1.0, 1e9, 1)[:3]
+    tmp = oracle.attn_bwd(q, k, v, do, 1.0, 0.0, 0)[:3]
+    for a, b in zip(dil, tmp):
+        assert np.max(np.abs(a - b)) <= 1e-6 * max(1.0, float(np.max(np.abs(b))))
+
+
+def pin_bwd_tau0_and_value_totals():
+    """tau = 0 makes the bids independent of q and k (zero dq, dk); in either
+    mode the rows of A sum to one, so the dv rows sum to the dO rows' sum."""
+    rng = _rng(24)
+    q, k, v, do = (rng.standard_normal((1, 1, 12, 8)) for _ in range(4))
+    for mode in (0, 1):
+        dq, dk, dv, _ = oracle.attn_bwd(q, k, v, do, 0.0, 1e-6, mode)
+        assert np.all(dq == 0.0) and np.all(dk == 0.0)
+        dq, dk, dv, _ = oracle.attn_bwd(q, k, v, do, 1.1, 1e-6, mode)
+        assert np.allclose(dv.sum(axis=2), do.sum(axis=2), rtol=0, atol=1e-12)
+
+
+def pin_bwd_rowsums_brute_force():
+    """The returned dilution row sums equal the brute-force shares' row sums."""
+    rng = _rng(25)
+    q, k, v, do = (rng.standard_normal((1, 1, 8, 4)) for _ in range(4))
+    _, _, _, rs = oracle.attn_bwd(q, k, v, do, 1.0, 1e-6, 1)
+    share = brute_dilution(q[0, 0], k[0, 0], v[0, 0], 1.0, 1e-6)[3]
+    assert np.allclose(rs[0, 0], share.sum(axis=1), rtol=1e-13, atol=0)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

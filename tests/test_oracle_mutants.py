@@ -43,6 +43,17 @@ MUTANTS = [
      "for (int j = 0; j < L; ++j) Dh[j] += p[j] / (Dh[j] + p[j] + eps);"),
     ("bf16_widening_shift", "<< 16;", "<< 15;"),
     ("yarn_coefficient", "return 0.1 * log(s) + 1.0;", "return 0.1 * log2(s) + 1.0;"),
+    ("bwd_suffix_exclusive",
+     "          col[j] += dPi[j] * Pi[j] / (Di[j] * Di[j]);\n          dPi[j] = dPi[j] / Di[j] - col[j];",
+     "          dPi[j] = dPi[j] / Di[j] - col[j];\n          col[j] += dPi[j] * Pi[j] / (Di[j] * Di[j]);"),
+    ("bwd_later_rows_ignored", "dPi[j] = dPi[j] / Di[j] - col[j];",
+     "dPi[j] = dPi[j] / Di[j] - dPi[j] * Pi[j] / (Di[j] * Di[j]);"),
+    ("bwd_delta_dropped", "dPi[j] = (dPi[j] - delta) / r[i];", "dPi[j] = dPi[j] / r[i];"),
+    ("bwd_softmax_rho_dropped", "dPi[j] = Pi[j] * (dPi[j] - rho);", "dPi[j] = Pi[j] * dPi[j];"),
+    ("bwd_dk_from_k", "dkj[e] += c * s * Q[(size_t)i * d + e];",
+     "dkj[e] += c * s * K[(size_t)i * d + e];"),
+    ("bwd_dv_from_bids", "dvj[e] += a * dO[(size_t)i * d + e];",
+     "dvj[e] += P[(size_t)i * T + j] * dO[(size_t)i * d + e];"),
 ]
 
 RUNNER = r"""
