@@ -10,6 +10,11 @@ One step runs the whole path once over resident synthetic inputs:
     H=16, d=64, fp32 demand updated in place (the 128 queries of the decode
     workload are used in turn).
 
+After the timed steps, the exact backward of both operators (attn_bwd, from
+the forward's saved out / lse / row sums and a synthetic dO) is timed the same
+way and reported under ``components`` at 10*d flops per causal pair (the
+usual 2.5x of the forward's 4*d).
+
 Printed: one JSON line.  ``value`` is the dilution forward's algorithmic
 TFLOP/s (4*d flops per causal (query, key) pair: q.k and the weighted v, once)
 over the measured time of its three launches; the tempered forward TFLOP/s and
@@ -176,6 +181,43 @@ def main():
     ms = {n: float(np.mean(seg[n])) for n in names}
     ms_min = {n: float(np.min(seg[n])) for n in names}
     log("bench: per-launch ms " + json.dumps({n: round(ms[n], 4) for n in names}))
+
+    # ------------------------------------------------------------- backward
+    from transformer_attention_causal_amd.workloads import draw_grad
+
+    dout = dev_bf16(draw_grad(w.B, w.H, w.T, w.d, w.seed))
+    lse_d = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=dev)
+    rs_d = torch.empty_like(lse_d)
+    lse_t = torch.empty_like(lse_d)
+    ab.fwd(q, k, v, tau=1.0, mode=ab.ATTN_DILUTION, eps=w.eps, out=out_d, workspace=ws,
+           lse_out=lse_d, rowsum_out=rs_d)
+    ab.fwd(q, k, v, tau=tau_t, mode=ab.ATTN_TEMPERED, out=out_t, lse_out=lse_t)
+    bws, _ = ab.bwd_workspace(w.B, w.H, w.T, ab.ATTN_DILUTION, ab.ATTN_BF16, dev)
+    grads = [torch.empty_like(q) for _ in range(3)]
+
+    def bwd_step(events=None):
+        if events is not None:
+            events[0].record(stream)
+        ab.bwd(q, k, v, out_d, dout, lse_d, rs_d, tau=1.0, mode=ab.ATTN_DILUTION, eps=w.eps,
+               dq=grads[0], dk=grads[1], dv=grads[2], workspace=bws)
+        if events is not None:
+            events[1].record(stream)
+        ab.bwd(q, k, v, out_t, dout, lse_t, None, tau=tau_t, mode=ab.ATTN_TEMPERED,
+               dq=grads[0], dk=grads[1], dv=grads[2], workspace=bws)
+        if events is not None:
+            events[2].record(stream)
+
+    for _ in range(args.warmup):
+        bwd_step()
+    bevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        bwd_step(bevs[i])
+    torch.cuda.synchronize()
+    bwd_ms = {"dilution_bwd": float(np.mean([e[0].elapsed_time(e[1]) for e in bevs])),
+              "tempered_bwd": float(np.mean([e[1].elapsed_time(e[2]) for e in bevs]))}
+    log("bench: backward ms " + json.dumps({n: round(x, 4) for n, x in bwd_ms.items()}))
+    del bws, grads
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -228,6 +270,10 @@ def main():
                             "bytes": dec_bytes,
                             "frac_of_hbm_peak": round(dec_gbps / PEAK_HBM_GBPS, 4)},
             "min_ms": {n: round(ms_min[n], 4) for n in names},
+            "dilution_bwd": {"ms": round(bwd_ms["dilution_bwd"], 4),
+                             "tflops": round(2.5 * flops / (bwd_ms["dilution_bwd"] * 1e-3) / 1e12, 3)},
+            "tempered_bwd": {"ms": round(bwd_ms["tempered_bwd"], 4),
+                             "tflops": round(2.5 * flops / (bwd_ms["tempered_bwd"] * 1e-3) / 1e12, 3)},
         },
         "roofline": {
             "bound": "mfma",

@@ -85,16 +85,46 @@ int attn_fwd(const void *q, const void *k, const void *v, void *out, int B, int 
              float tau, int mode, float eps, int dtype, void *workspace, size_t workspace_bytes,
              void *hip_stream);
 
-/* attn_fwd with two optional fp32 outputs (NULL to skip either):
+/* attn_fwd with three optional fp32 outputs (NULL to skip any):
  *   lse_out    [B,H,T]  natural-log log-sum-exp of each query row's tempered
  *              logits, log sum_{j<=i} exp(tau <q_i,k_j>/sqrt(d))
  *   demand_out [B,H,T]  dilution only: each key's final column total
  *              sum_i p_ij -- the running demand a cached decode continues
- *              from (DilutionAttention v0.1.0, cached decoding).  Must be
- *              NULL in ATTN_TEMPERED mode (else ATTN_EINVAL). */
+ *              from (DilutionAttention v0.1.0, cached decoding).
+ *   rowsum_out [B,H,T]  dilution only: each row's sum of shares, the
+ *              renormaliser of A ("The operator"); attn_bwd needs it.
+ * demand_out and rowsum_out must be NULL in ATTN_TEMPERED mode (else
+ * ATTN_EINVAL).  The outputs may not alias each other or any tensor. */
 int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, int B, int H, int T,
                 int d, float tau, int mode, float eps, int dtype, void *workspace,
-                size_t workspace_bytes, float *lse_out, float *demand_out, void *hip_stream);
+                size_t workspace_bytes, float *lse_out, float *demand_out, float *rowsum_out,
+                void *hip_stream);
+
+/* Bytes of device workspace attn_bwd needs: four fp32 values per query row,
+ * and for dilution the committed demand and the later rows' gradient sums
+ * per (32-row query block, key): B*H*16*n*(n-1) and B*H*16*n*(n+1) floats,
+ * n = ceil(T/32).  0 for an unsupported shape, mode or dtype (bf16 only). */
+size_t attn_bwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype);
+
+/* Exact gradients of either operator (DilutionAttention v0.1.0: the release's
+ * kernels train with exact gradients; "The operator" defines what is
+ * differentiated).  For the loss L with dL/dout = dout:
+ *   q, k, v, out, dout  [B,H,T,d] bf16 device arrays: the forward's inputs,
+ *                       its output, and the incoming gradient
+ *   lse                 [B,H,T] fp32: the forward's lse_out (natural log)
+ *   rowsum              [B,H,T] fp32: the forward's rowsum_out (dilution;
+ *                       ignored and may be NULL for ATTN_TEMPERED)
+ *   dq, dk, dv          [B,H,T,d] bf16 outputs, overwritten; may not alias
+ *                       each other or any input
+ *   B, H, T, d, tau, mode, eps  as passed to the forward
+ *   dtype               ATTN_BF16 (ATTN_F32 returns ATTN_ENOTSUP)
+ *   workspace           device scratch of >= attn_bwd_workspace_bytes(...)
+ *                       bytes; contents on entry are ignored
+ * Deterministic: fixed reduction orders, no atomics. */
+int attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout,
+             const float *lse, const float *rowsum, void *dq, void *dk, void *dv, int B, int H,
+             int T, int d, float tau, int mode, float eps, int dtype, void *workspace,
+             size_t workspace_bytes, void *hip_stream);
 
 /* The dilution forward pass, one stage per call (attn_fwd with ATTN_DILUTION
  * runs exactly these three in order on one stream).  All three take the same

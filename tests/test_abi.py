@@ -55,7 +55,8 @@ def test_strerror_is_static_text():
 def fwd(**kw):
     args = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, out=FAKE + 0x3000000, B=1, H=1,
                 T=16, d=64, tau=1.0, mode=0, eps=1e-6, dtype=1, workspace=None,
-                workspace_bytes=0, lse_out=None, demand_out=None, hip_stream=None)
+                workspace_bytes=0, lse_out=None, demand_out=None, rowsum_out=None,
+                hip_stream=None)
     args.update(kw)
     return ab.attn_fwd_ex(**args)
 
@@ -75,6 +76,9 @@ def fwd(**kw):
     (dict(eps=float("nan")), ab.ATTN_EINVAL),
     (dict(out=FAKE), ab.ATTN_EINVAL),                # out aliases q
     (dict(demand_out=FAKE + 0x4000000), ab.ATTN_EINVAL),  # demand_out in tempered mode
+    (dict(rowsum_out=FAKE + 0x4000000), ab.ATTN_EINVAL),  # rowsum_out in tempered mode
+    (dict(mode=1, lse_out=FAKE + 0x4000000, rowsum_out=FAKE + 0x4000010,
+          workspace=FAKE + 0x5000000, workspace_bytes=1 << 30), ab.ATTN_EINVAL),  # outputs overlap
     (dict(d=128), ab.ATTN_ENOTSUP),
     (dict(mode=1), ab.ATTN_EWORKSPACE),              # dilution without workspace
     (dict(mode=1, workspace=FAKE + 0x5000000, workspace_bytes=16), ab.ATTN_EWORKSPACE),
@@ -94,6 +98,48 @@ def test_workspace_sizes():
     assert ab.attn_fwd_workspace_bytes(0, 1, 16, 64, 1, 1) == 0
     assert ab.attn_decode_workspace_bytes(64, 16, 32768, 64) >= 64 * 16 * 32768 * 4
     assert ab.attn_decode_workspace_bytes(64, 16, 32768, 32) == 0
+
+
+def test_bwd_workspace_sizes():
+    n = 16384 // 32
+    rows = 16 * 16384 * 4
+    want = 4 * rows + 16 * 16 * n * (n - 1) * 4 + 16 * 16 * n * (n + 1) * 4
+    got = ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 1)
+    assert want <= got <= want + 6 * 256
+    assert 4 * rows <= ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 0, 1) <= 4 * rows + 4 * 256
+    assert ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 0) == 0   # fp32: not supported
+    assert ab.attn_bwd_workspace_bytes(1, 16, 16384, 128, 1, 1) == 0
+
+
+def bwd(**kw):
+    base = FAKE
+    args = dict(q=base, k=base + 0x1000000, v=base + 0x2000000, out=base + 0x3000000,
+                dout=base + 0x4000000, lse=base + 0x5000000, rowsum=base + 0x6000000,
+                dq=base + 0x7000000, dk=base + 0x8000000, dv=base + 0x9000000, B=1, H=1, T=16,
+                d=64, tau=1.0, mode=1, eps=1e-6, dtype=1, workspace=None, workspace_bytes=0,
+                hip_stream=None)
+    args.update(kw)
+    return ab.attn_bwd(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dout=None), ab.ATTN_EINVAL),
+    (dict(lse=None), ab.ATTN_EINVAL),
+    (dict(rowsum=None), ab.ATTN_EINVAL),              # dilution needs the row sums
+    (dict(dq=FAKE + 4), ab.ATTN_EINVAL),              # misaligned
+    (dict(mode=3), ab.ATTN_EINVAL),
+    (dict(T=0), ab.ATTN_EINVAL),
+    (dict(tau=-1.0), ab.ATTN_EINVAL),
+    (dict(eps=float("nan")), ab.ATTN_EINVAL),
+    (dict(dtype=0), ab.ATTN_ENOTSUP),                 # fp32 backward
+    (dict(d=128), ab.ATTN_ENOTSUP),
+    (dict(dk=FAKE + 0x7000000), ab.ATTN_EINVAL),      # dk aliases dq
+    (dict(dv=FAKE), ab.ATTN_EINVAL),                  # dv aliases q
+    (dict(), ab.ATTN_EWORKSPACE),
+    (dict(mode=0, rowsum=None), ab.ATTN_EWORKSPACE),  # tempered: row sums not needed
+])
+def test_bwd_rejects_bad_arguments(kw, status):
+    assert bwd(**kw) == status
 
 
 def dec(**kw):

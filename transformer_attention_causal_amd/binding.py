@@ -1,9 +1,9 @@
 """Thin Python binding of libattn.so (argument marshalling only).
 
-The functions named like the C ABI (``attn_fwd``, ``attn_fwd_ex``,
-``attn_decode``, ``attn_fwd_workspace_bytes``, ``attn_decode_workspace_bytes``,
-``attn_yarn_tau``, ``attn_strerror``) take exactly the C arguments, with device
-pointers as Python ints.  ``fwd`` and ``decode`` accept torch tensors, check
+The functions named like the C ABI (``attn_fwd``, ``attn_fwd_ex``, ``attn_bwd``,
+``attn_decode``, the ``*_workspace_bytes`` queries, ``attn_yarn_tau``,
+``attn_strerror``) take exactly the C arguments, with device pointers as Python
+ints.  ``fwd``, ``bwd`` and ``decode`` accept torch tensors, check
 their shapes/dtypes, allocate the output and workspace with torch, pass the
 current torch stream, and raise ``AttnError`` on a non-zero status.  Every step
 of the computation runs in the library's HIP kernels; nothing here computes.
@@ -24,8 +24,9 @@ ATTN_TEMPERED, ATTN_DILUTION = 0, 1
 ATTN_F32, ATTN_BF16 = 0, 1
 
 EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_bytes", "attn_dilution_lse",
-            "attn_dilution_committed", "attn_dilution_shares", "attn_decode",
-            "attn_decode_workspace_bytes", "attn_yarn_tau", "attn_strerror")
+            "attn_dilution_committed", "attn_dilution_shares", "attn_bwd",
+            "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_workspace_bytes",
+            "attn_yarn_tau", "attn_strerror")
 
 
 class AttnError(RuntimeError):
@@ -50,7 +51,13 @@ def load() -> ctypes.CDLL:
         lib.attn_fwd.restype = i
         lib.attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, f, i, vp, sz, vp]
         lib.attn_fwd_ex.restype = i
-        lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, f, i, vp, sz, vp, vp, vp]
+        lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, f, i, vp, sz, vp, vp, vp,
+                                    vp]
+        lib.attn_bwd.restype = i
+        lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, f, i,
+                                 vp, sz, vp]
+        lib.attn_bwd_workspace_bytes.restype = sz
+        lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
         lib.attn_dilution_lse.restype = i
         lib.attn_dilution_lse.argtypes = [vp, vp, i, i, i, i, f, i, vp, sz, vp, vp]
         lib.attn_dilution_committed.restype = i
@@ -80,9 +87,19 @@ def attn_fwd(q, k, v, out, B, H, T, d, tau, mode, eps, dtype, workspace, workspa
 
 
 def attn_fwd_ex(q, k, v, out, B, H, T, d, tau, mode, eps, dtype, workspace, workspace_bytes,
-                lse_out, demand_out, hip_stream) -> int:
+                lse_out, demand_out, rowsum_out, hip_stream) -> int:
     return load().attn_fwd_ex(q, k, v, out, B, H, T, d, tau, mode, eps, dtype, workspace,
-                              workspace_bytes, lse_out, demand_out, hip_stream)
+                              workspace_bytes, lse_out, demand_out, rowsum_out, hip_stream)
+
+
+def attn_bwd(q, k, v, out, dout, lse, rowsum, dq, dk, dv, B, H, T, d, tau, mode, eps, dtype,
+             workspace, workspace_bytes, hip_stream) -> int:
+    return load().attn_bwd(q, k, v, out, dout, lse, rowsum, dq, dk, dv, B, H, T, d, tau, mode,
+                           eps, dtype, workspace, workspace_bytes, hip_stream)
+
+
+def attn_bwd_workspace_bytes(B, H, T, d, mode, dtype) -> int:
+    return int(load().attn_bwd_workspace_bytes(B, H, T, d, mode, dtype))
 
 
 def attn_dilution_lse(q, k, B, H, T, d, tau, dtype, workspace, workspace_bytes, lse_out,
@@ -153,7 +170,7 @@ def fwd_workspace(B, H, T, mode, dtype_code, device):
 
 
 def fwd(q, k, v, tau: float = 1.0, mode: int = ATTN_TEMPERED, eps: float = 1e-6,
-        out=None, workspace=None, lse_out=None, demand_out=None):
+        out=None, workspace=None, lse_out=None, demand_out=None, rowsum_out=None):
     """Run attn_fwd_ex on [B,H,T,64] tensors; returns ``out``."""
     import torch
 
@@ -175,10 +192,47 @@ def fwd(q, k, v, tau: float = 1.0, mode: int = ATTN_TEMPERED, eps: float = 1e-6,
                      workspace.data_ptr() if workspace is not None else None, ws_bytes,
                      lse_out.data_ptr() if lse_out is not None else None,
                      demand_out.data_ptr() if demand_out is not None else None,
+                     rowsum_out.data_ptr() if rowsum_out is not None else None,
                      _stream_handle(q.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_ex")
     return out
+
+
+def bwd_workspace(B, H, T, mode, dtype_code, device):
+    import torch
+
+    n = attn_bwd_workspace_bytes(B, H, T, 64, mode, dtype_code)
+    if n == 0:
+        raise AttnError(ATTN_ENOTSUP, "attn_bwd_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
+def bwd(q, k, v, out, dout, lse, rowsum=None, tau: float = 1.0, mode: int = ATTN_TEMPERED,
+        eps: float = 1e-6, dq=None, dk=None, dv=None, workspace=None):
+    """Run attn_bwd on [B,H,T,64] tensors (``lse``/``rowsum`` from ``fwd``'s
+    ``lse_out``/``rowsum_out``); returns (dq, dk, dv)."""
+    import torch
+
+    for t in (q, k, v, out, dout):
+        if t.shape != q.shape or not t.is_contiguous():
+            raise ValueError("q, k, v, out, dout must be contiguous and share one shape")
+    B, H, T, d = q.shape
+    code = _dtype_code(q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    if workspace is None:
+        workspace, ws_bytes = bwd_workspace(B, H, T, mode, code, q.device)
+    else:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                  lse.data_ptr(), rowsum.data_ptr() if rowsum is not None else None,
+                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, T, d, float(tau), int(mode),
+                  float(eps), code, workspace.data_ptr(), ws_bytes, _stream_handle(q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv
 
 
 def dilution_stages(q, k, v, tau: float = 1.0, eps: float = 1e-6, out=None, workspace=None,

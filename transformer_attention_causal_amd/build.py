@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
 
-SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip"]
+SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "bwd_bf16.hip"]
 
 # Packed fp32 VALU forms are disabled: every fp32 operation is a plain
 # single-lane instruction.

@@ -119,7 +119,7 @@ namespace {
 // for the stages that do not read or write them.
 int check_fwd(const void *q, const void *k, const void *v, const void *out, int B, int H, int T,
               int d, float tau, float eps, int dtype, const float *lse_out,
-              const float *demand_out) {
+              const float *demand_out, const float *rowsum_out = nullptr) {
   if (!q || !k) return ATTN_EINVAL;
   if (!aligned16(q) || !aligned16(k) || (v && !aligned16(v)) || (out && !aligned16(out)))
     return ATTN_EINVAL;
@@ -135,14 +135,17 @@ int check_fwd(const void *q, const void *k, const void *v, const void *out, int 
     return ATTN_EINVAL;
   // the optional [B,H,T] fp32 outputs may not alias any tensor argument or each other
   const size_t rbytes = (size_t)B * H * (size_t)T * sizeof(float);
-  for (const void *r : {static_cast<const void *>(lse_out), static_cast<const void *>(demand_out)}) {
+  const void *rs[3] = {lse_out, demand_out, rowsum_out};
+  for (int i = 0; i < 3; ++i) {
+    const void *r = rs[i];
     if (!r) continue;
     if (!aligned16(r)) return ATTN_EINVAL;
     if (overlaps(r, rbytes, q, nbytes) || overlaps(r, rbytes, k, nbytes) ||
         (v && overlaps(r, rbytes, v, nbytes)) || (out && overlaps(r, rbytes, out, nbytes)))
       return ATTN_EINVAL;
+    for (int j = 0; j < i; ++j)
+      if (rs[j] && overlaps(r, rbytes, rs[j], rbytes)) return ATTN_EINVAL;
   }
-  if (lse_out && demand_out && overlaps(lse_out, rbytes, demand_out, rbytes)) return ATTN_EINVAL;
   return ATTN_OK;
 }
 
@@ -226,11 +229,12 @@ int attn_dilution_shares(const void *q, const void *k, const void *v, void *out,
 
 int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, int B, int H, int T,
                 int d, float tau, int mode, float eps, int dtype, void *workspace,
-                size_t workspace_bytes, float *lse_out, float *demand_out, void *hip_stream) {
+                size_t workspace_bytes, float *lse_out, float *demand_out, float *rowsum_out,
+                void *hip_stream) {
   if (!v || !out) return ATTN_EINVAL;
   if (mode != ATTN_TEMPERED && mode != ATTN_DILUTION) return ATTN_EINVAL;
-  if (mode == ATTN_TEMPERED && demand_out) return ATTN_EINVAL;
-  int st = check_fwd(q, k, v, out, B, H, T, d, tau, eps, dtype, lse_out, demand_out);
+  if (mode == ATTN_TEMPERED && (demand_out || rowsum_out)) return ATTN_EINVAL;
+  int st = check_fwd(q, k, v, out, B, H, T, d, tau, eps, dtype, lse_out, demand_out, rowsum_out);
   if (st != ATTN_OK) return st;
   FwdWorkspace ws{};
   if (mode == ATTN_DILUTION) {
@@ -260,6 +264,7 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, int B, i
   if (e != hipSuccess) return fail_hip(e);
   a.demand_out = nullptr;
   // stage 3: shares, share@V, renormalisation
+  a.rowsum_out = rowsum_out;
   return finish(bf16 ? attn::launch_rows_bf16(attn::kRowShare, a, s)
                      : attn::launch_rows_f32(attn::kRowShare, a, s));
 }
@@ -268,7 +273,104 @@ int attn_fwd(const void *q, const void *k, const void *v, void *out, int B, int 
              float tau, int mode, float eps, int dtype, void *workspace, size_t workspace_bytes,
              void *hip_stream) {
   return attn_fwd_ex(q, k, v, out, B, H, T, d, tau, mode, eps, dtype, workspace, workspace_bytes,
-                     nullptr, nullptr, hip_stream);
+                     nullptr, nullptr, nullptr, hip_stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace layout of a backward pass: four per-row fp32 arrays (lse2, 1/r,
+// delta/r, rho), then for dilution the committed demand and the later blocks'
+// gradient sums, per (32-row block, key).
+struct BwdWorkspace {
+  size_t row_bytes, cin_bytes, gin_bytes, total;
+};
+
+bool bwd_workspace(int B, int H, int T, int mode, BwdWorkspace *ws) {
+  const size_t BH = (size_t)B * H;
+  if (BH > (size_t)INT32_MAX) return false;
+  ws->row_bytes = round_up(BH * (size_t)T * sizeof(float));
+  ws->cin_bytes = mode == ATTN_DILUTION ? round_up(BH * attn::cin_floats_per_head(T) * 4) : 0;
+  ws->gin_bytes = mode == ATTN_DILUTION ? round_up(BH * attn::gin_floats_per_head(T) * 4) : 0;
+  ws->total = 4 * ws->row_bytes + ws->cin_bytes + ws->gin_bytes;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_bwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype) {
+  if (!shape_ok(B, H, T) || d != attn::kHeadDim || dtype != ATTN_BF16) return 0;
+  if (mode != ATTN_TEMPERED && mode != ATTN_DILUTION) return 0;
+  BwdWorkspace ws;
+  if (!bwd_workspace(B, H, T, mode, &ws)) return 0;
+  return ws.total;
+}
+
+int attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout,
+             const float *lse, const float *rowsum, void *dq, void *dk, void *dv, int B, int H,
+             int T, int d, float tau, int mode, float eps, int dtype, void *workspace,
+             size_t workspace_bytes, void *hip_stream) {
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv) return ATTN_EINVAL;
+  if (mode != ATTN_TEMPERED && mode != ATTN_DILUTION) return ATTN_EINVAL;
+  if (mode == ATTN_DILUTION && !rowsum) return ATTN_EINVAL;
+  const void *ptrs[9] = {q, k, v, out, dout, lse, dq, dk, dv};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return ATTN_EINVAL;
+  if (rowsum && !aligned16(rowsum)) return ATTN_EINVAL;
+  if (!shape_ok(B, H, T)) return ATTN_EINVAL;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EINVAL;
+  if (!std::isfinite(tau) || tau < 0.0f) return ATTN_EINVAL;
+  if (!std::isfinite(eps) || eps < 0.0f) return ATTN_EINVAL;
+  if (d != attn::kHeadDim || dtype != ATTN_BF16) return ATTN_ENOTSUP;
+  // the three gradients may not alias each other or any input
+  const size_t nbytes = (size_t)B * H * (size_t)T * d * 2;
+  const size_t rbytes = (size_t)B * H * (size_t)T * sizeof(float);
+  const void *grads[3] = {dq, dk, dv};
+  for (int i = 0; i < 3; ++i) {
+    for (const void *in : {q, k, v, out, dout})
+      if (overlaps(grads[i], nbytes, in, nbytes)) return ATTN_EINVAL;
+    if (overlaps(grads[i], nbytes, lse, rbytes) || (rowsum && overlaps(grads[i], nbytes, rowsum, rbytes)))
+      return ATTN_EINVAL;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(grads[i], nbytes, grads[j], nbytes)) return ATTN_EINVAL;
+  }
+  BwdWorkspace ws;
+  if (!bwd_workspace(B, H, T, mode, &ws)) return ATTN_EINVAL;
+  if (!workspace || workspace_bytes < ws.total || !aligned16(workspace)) return ATTN_EWORKSPACE;
+  const int dev_status = check_device();
+  if (dev_status != ATTN_OK) return dev_status;
+
+  attn::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.rowsum = rowsum;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  char *wsp = static_cast<char *>(workspace);
+  a.lse2 = reinterpret_cast<float *>(wsp);
+  a.invr = reinterpret_cast<float *>(wsp + ws.row_bytes);
+  a.dri = reinterpret_cast<float *>(wsp + 2 * ws.row_bytes);
+  a.rho = reinterpret_cast<float *>(wsp + 3 * ws.row_bytes);
+  if (mode == ATTN_DILUTION) {
+    a.cin = reinterpret_cast<float *>(wsp + 4 * ws.row_bytes);
+    a.gin = reinterpret_cast<float *>(wsp + 4 * ws.row_bytes + ws.cin_bytes);
+  }
+  a.BH = B * H;
+  a.T = T;
+  const double c = (double)tau / std::sqrt((double)d);
+  a.c = (float)c;
+  a.c2 = (float)(c * 1.4426950408889634);
+  a.eps = eps;
+  hipError_t e = attn::launch_bwd_bf16(mode, a, reinterpret_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? ATTN_OK : fail_hip(e);
 }
 
 size_t attn_decode_workspace_bytes(int S, int H, int Lcap, int d) {

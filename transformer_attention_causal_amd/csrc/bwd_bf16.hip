@@ -1,0 +1,752 @@
+// bwd_bf16.hip -- bf16 backward kernels for gfx950 (exact gradients).
+//
+// "DilutionAttention v0.1.0 - results": the operator ("The operator") and
+// the release's training kernels with exact gradients ("Everything behind
+// these charts").  With p the bids, C the committed demand, D = C + p + eps,
+// sigma = p / D, r_i = sum_j sigma_ij, a = sigma / r, o = a v and the
+// incoming gradient dO, the chain rule gives (per head)
+//   dV_j      = sum_i a_ij dO_i
+//   dA_ij     = <dO_i, v_j>,  delta_i = <dO_i, o_i>
+//   dsigma_ij = (dA_ij - delta_i) / r_i
+//   g_ij      = dsigma_ij p_ij / D_ij^2
+//   dp_ij     = dsigma_ij / D_ij - G_ij,   G_ij = sum_{i'' >= i} g_i''j
+//               (every later row's committed demand contains p_ij)
+//   dS_ij     = p_ij (dp_ij - rho_i),      rho_i = sum_j p_ij dp_ij
+//   dQ_i = c sum_j dS_ij k_j,   dK_j = c sum_i dS_ij q_i,   c = tau / sqrt(d).
+// Tempered attention is the same with a = p: dS_ij = p_ij (dA_ij - delta_i).
+//
+// Passes (dilution; tempered skips 2 and 3):
+//   1 bwd_prep_kernel   per row: log2-domain lse, 1/r, delta/r
+//   2 colsum_bf16_kernel (the forward's) committed demand per 32-row block
+//   3 bwd_gsum_kernel   per key, walking 32-row blocks from the last one up:
+//                       the sum of g over every later block (G's block part)
+//   4 bwd_dq_kernel     per 32 query rows: dQ, rho
+//   5 bwd_dkdv_kernel   per 32 keys: dK, dV
+// Both in-block scans (the column prefix inside D and the column suffix
+// inside G) are matrix-core products against constant triangular operands,
+// as in the forward shares pass.
+#include "attn_common.hpp"
+#include "launch.hpp"
+#include "tiles.hpp"
+
+#include <float.h>
+
+namespace attn {
+
+constexpr int kColKeys = 128;   // keys per workgroup in the column kernels (4 waves x 32)
+constexpr int kTRow = 36;       // LDS row stride of the transposed 32-row blocks (32 + 4 pad)
+constexpr float kInvDMax = 18446744073709551616.0f;   // 2^64: clamp on 1/D (eps = 0 only)
+
+__device__ __forceinline__ bf16x8 word_operand(uint32_t w) {
+  const u32x4 u = {w, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// ------------------------------------------------------------------ prep
+
+// Eight lanes per row: delta = <dO_i, o_i> from 16-byte loads, then the
+// per-row scalars the other passes read.
+__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a, int dilution) {
+  const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t row = gid >> 3;
+  const int dc = (int)(gid & 7);
+  const bool live = row < (size_t)a.BH * a.T;
+  float acc = 0.0f;
+  if (live) {
+    const u32x4 ov = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const __bf16 *>(a.o) +
+                                                      row * kHeadDim + 8 * dc);
+    const u32x4 gv = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const __bf16 *>(a.dout) +
+                                                      row * kHeadDim + 8 * dc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t x = ov[i], y = gv[i];
+      acc = __builtin_fmaf(bf16_lo(x), bf16_lo(y), acc);
+      acc = __builtin_fmaf(bf16_hi(x), bf16_hi(y), acc);
+    }
+  }
+  acc += __shfl_xor(acc, 1, 8);
+  acc += __shfl_xor(acc, 2, 8);
+  acc += __shfl_xor(acc, 4, 8);
+  if (live && dc == 0) {
+    a.lse2[row] = a.lse[row] * kLog2e;
+    if (dilution) {
+      const float ir = 1.0f / a.rowsum[row];
+      a.invr[row] = ir;
+      a.dri[row] = acc * ir;
+    } else {
+      a.invr[row] = 1.0f;
+      a.dri[row] = acc;
+    }
+  }
+}
+
+// ------------------------------------------------------- column kernels
+//
+// A workgroup owns 128 keys (wave w the 32 keys [kw0, kw0 + 32), K and V rows
+// held in registers as B operands) and walks the 32-row query blocks that
+// see them.  Scores of a block are in the S layout (lane = key, element r =
+// query acc_row(r, h)).  The column scans take the packed bids / gradient
+// terms as the B operand against constant A operands (lane = output row m):
+
+struct ScanConsts {
+  bf16x8 le[2];    // inclusive prefix: 1 where the slot's query <= m
+  bf16x8 ge[2];    // inclusive suffix: 1 where the slot's query >= m
+  bf16x8 ones;     // slots (0, 0) and (0, 1): adds a per-key bf16 (hi, lo) pair
+};
+
+__device__ __forceinline__ ScanConsts scan_consts(int l32, int h) {
+  ScanConsts c;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    float le[8], ge[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int qs = acc_row(8 * j + e, h);
+      le[e] = qs <= l32 ? 1.0f : 0.0f;
+      ge[e] = qs >= l32 ? 1.0f : 0.0f;
+    }
+    c.le[j] = pack8(le);
+    c.ge[j] = pack8(ge);
+  }
+  const float one = h == 0 ? 1.0f : 0.0f;
+  c.ones = to_bf16x8(one, one, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f);
+  return c;
+}
+
+// Per-block LDS staging shared by the column kernels: Q and dO rows of one
+// 32-row block (row-major, the A operands of S = Q K^T and dA = dO V^T), and
+// the per-row scalars.
+struct ColBlock {
+  __bf16 q[32 * kKRow];
+  __bf16 g[32 * kKRow];
+  float lse2[32], invr[32], dri[32], rho[32];
+};
+
+// Bids of a block in the S layout; on the diagonal block rows before the key
+// see nothing of it.
+template <bool DIAG>
+__device__ __forceinline__ void col_bids(const f32x16 &s, const float *lq, float c2, int l32,
+                                         int h, float *p) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float e = fast_exp2(__builtin_fmaf(s[r], c2, -lq[r]));
+    if (DIAG && acc_row(r, h) < l32) e = 0.0f;
+    p[r] = e;
+  }
+}
+
+// Per-row scalars of the block in the S-layout register order.
+__device__ __forceinline__ void col_rowvals(const float *src, int h, float *dst) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(src + 8 * g + 4 * h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[4 * g + i] = v[i];
+  }
+}
+
+// The block's S = Q K^T and dA = dO V^T for this wave's keys.
+__device__ __forceinline__ void col_scores(const ColBlock &b, const bf16x8 *kf, const bf16x8 *vf,
+                                           int l32, int h, f32x16 &s, f32x16 &da) {
+  const __bf16 *qrow = b.q + l32 * kKRow;
+  const __bf16 *grow = b.g + l32 * kKRow;
+  s = zero16();
+  da = zero16();
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    s = mfma32(lds_frag(qrow, c, h), kf[c], s);
+    da = mfma32(lds_frag(grow, c, h), vf[c], da);
+  }
+}
+
+// dilution quantities of one block (S layout): p, 1/D (clamped), sigma,
+// dsigma and g = dsigma sigma / D.
+struct ColTerms {
+  float p[16], invd[16], sg[16], dsg[16], g[16];
+};
+
+template <bool DIAG>
+__device__ __forceinline__ void col_terms(const f32x16 &s, const f32x16 &da, const ColBlock &b,
+                                          const ScanConsts &sc, uint32_t cin_word, float c2,
+                                          int l32, int h, ColTerms &t) {
+  float lq[16], iq[16], rq[16];
+  col_rowvals(b.lse2, h, lq);
+  col_rowvals(b.invr, h, iq);
+  col_rowvals(b.dri, h, rq);
+  col_bids<DIAG>(s, lq, c2, l32, h, t.p);
+  const bf16x8 pa0 = pack8(t.p), pa1 = pack8(t.p + 8);
+  // D = committed + eps + inclusive column prefix of the bids (S layout)
+  f32x16 d = mfma32(sc.le[0], pa0, zero16());
+  d = mfma32(sc.le[1], pa1, d);
+  d = mfma32(sc.ones, word_operand(cin_word), d);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float invd = fminf(fast_rcp(d[r]), kInvDMax);
+    t.invd[r] = invd;
+    t.sg[r] = t.p[r] * invd;
+    t.dsg[r] = __builtin_fmaf(da[r], iq[r], -rq[r]);
+    t.g[r] = t.dsg[r] * t.sg[r] * invd;
+  }
+}
+
+// Pass 3: sums of g over the blocks below each block, walking up.
+__global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdArgs a, int nqs) {
+  __shared__ __attribute__((aligned(16))) ColBlock sb[2];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int bh = blockIdx.x % a.BH;
+  const int kb = blockIdx.x / a.BH;
+  const int T = a.T;
+  const int kw0 = kb * kColKeys + 32 * w;
+  const bool wave_live = kw0 < T;
+  const int key = kw0 + l32;
+  const size_t head = (size_t)bh * T * kHeadDim;
+  const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + head;
+  const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + head;
+  const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + head;
+  const __bf16 *G = reinterpret_cast<const __bf16 *>(a.dout) + head;
+  const float *L2 = a.lse2 + (size_t)bh * T;
+  const float *IR = a.invr + (size_t)bh * T;
+  const float *DR = a.dri + (size_t)bh * T;
+  const uint32_t *cin = reinterpret_cast<const uint32_t *>(a.cin) + (size_t)bh * cin_floats_per_head(T);
+  uint32_t *gin = reinterpret_cast<uint32_t *>(a.gin) + (size_t)bh * gin_floats_per_head(T);
+  const uint32_t eps_word = split2_bf16(fmaxf(a.eps, FLT_MIN));
+
+  bf16x8 kf[4], vf[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    kf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(K, key, T, 2 * c + h));
+    vf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(V, key, T, 2 * c + h));
+  }
+  const ScanConsts sc = scan_consts(l32, h);
+  __builtin_amdgcn_s_waitcnt(0);
+
+  const int qs_lo = (kb * kColKeys) / 32;   // first block that sees a key of this workgroup
+  u32x4 qreg, greg;
+  float lreg = 0.0f, ireg = 0.0f, rreg = 0.0f;
+  auto load_block = [&](int qs) {           // 32 qs < T for every block loaded
+    const int row0 = 32 * qs;
+    const int bytes = (T - row0) * (kHeadDim * 2);
+    qreg = buf_load16(make_rsrc(Q + (size_t)row0 * kHeadDim, bytes), 16u * tid);
+    greg = buf_load16(make_rsrc(G + (size_t)row0 * kHeadDim, bytes), 16u * tid);
+    if (tid < 32) {
+      const int row = row0 + tid;
+      const bool ok = row < T;
+      const int rr = ok ? row : T - 1;
+      lreg = ok ? L2[rr] : kNoRow;   // rows past the end bid nothing
+      ireg = ok ? IR[rr] : 0.0f;
+      rreg = ok ? DR[rr] : 0.0f;
+    }
+  };
+  auto store_block = [&](int buf) {
+    *reinterpret_cast<u32x4 *>(&sb[buf].q[(tid >> 3) * kKRow + (tid & 7) * 8]) = qreg;
+    *reinterpret_cast<u32x4 *>(&sb[buf].g[(tid >> 3) * kKRow + (tid & 7) * 8]) = greg;
+    if (tid < 32) {
+      sb[buf].lse2[tid] = lreg;
+      sb[buf].invr[tid] = ireg;
+      sb[buf].dri[tid] = rreg;
+    }
+  };
+
+  float running = 0.0f;   // sum of g over this half-lane's rows in blocks below
+  load_block(nqs - 1);
+  store_block(0);
+  __syncthreads();
+  for (int qs = nqs - 1; qs >= qs_lo; --qs) {
+    const int buf = (nqs - 1 - qs) & 1;
+    if (qs - 1 >= qs_lo) load_block(qs - 1);
+    if (wave_live && 32 * qs + 31 >= kw0) {
+      f32x16 s, da;
+      col_scores(sb[buf], kf, vf, l32, h, s, da);
+      const uint32_t cw = key < 32 * qs ? cin[(size_t)16 * qs * (qs - 1) + key] : eps_word;
+      ColTerms t;
+      if (32 * qs == kw0) col_terms<true>(s, da, sb[buf], sc, cw, a.c2, l32, h, t);
+      else col_terms<false>(s, da, sb[buf], sc, cw, a.c2, l32, h, t);
+      float part = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part += t.g[r];
+      const float below = both_halves_sum(running);
+      if (h == 0 && key < T) gin[(size_t)16 * qs * (qs + 1) + key] = split2_bf16(below);
+      running += part;
+    }
+    if (qs - 1 >= qs_lo) store_block(buf ^ 1);
+    __syncthreads();
+  }
+}
+
+// Pass 5: dK and dV for this wave's keys.  The transposed Q and dO blocks
+// (dim-major) are the A operands of dK^T += Q^T dS and dV^T += dO^T a; the
+// packed dS and a (S layout) are their B operands.
+struct ColBlockT {
+  __bf16 qt[kHeadDim * kTRow];
+  __bf16 gt[kHeadDim * kTRow];
+};
+
+template <bool DIL, bool DIAG>
+__device__ __forceinline__ void dkdv_block(const ColBlock &b, const ColBlockT &bt,
+                                           const bf16x8 *kf, const bf16x8 *vf,
+                                           const ScanConsts &sc, uint32_t cin_word,
+                                           uint32_t gin_word, float c2, int l32, int h,
+                                           f32x16 *dkt, f32x16 *dvt) {
+  f32x16 s, da;
+  col_scores(b, kf, vf, l32, h, s, da);
+  float ds[16], aw[16];
+  if constexpr (DIL) {
+    ColTerms t;
+    col_terms<DIAG>(s, da, b, sc, cin_word, c2, l32, h, t);
+    // G = gradient terms of the later blocks + inclusive suffix in this one
+    const bf16x8 ga0 = pack8(t.g), ga1 = pack8(t.g + 8);
+    f32x16 G = mfma32(sc.ge[0], ga0, zero16());
+    G = mfma32(sc.ge[1], ga1, G);
+    G = mfma32(sc.ones, word_operand(gin_word), G);
+    float iq[16], pq[16];
+    col_rowvals(b.invr, h, iq);
+    col_rowvals(b.rho, h, pq);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float dp = __builtin_fmaf(t.dsg[r], t.invd[r], -G[r]);
+      ds[r] = t.p[r] * (dp - pq[r]);
+      aw[r] = t.sg[r] * iq[r];
+    }
+  } else {
+    float lq[16], rq[16];
+    col_rowvals(b.lse2, h, lq);
+    col_rowvals(b.dri, h, rq);
+    col_bids<DIAG>(s, lq, c2, l32, h, aw);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ds[r] = aw[r] * (da[r] - rq[r]);
+  }
+  const bf16x8 sf[2] = {pack8(ds), pack8(ds + 8)};
+  const bf16x8 af[2] = {pack8(aw), pack8(aw + 8)};
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const __bf16 *qtr = bt.qt + (32 * u + l32) * kTRow;
+    const __bf16 *gtr = bt.gt + (32 * u + l32) * kTRow;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      dkt[u] = mfma32(lds_vfrag(qtr, j, h), sf[j], dkt[u]);
+      dvt[u] = mfma32(lds_vfrag(gtr, j, h), af[j], dvt[u]);
+    }
+  }
+}
+
+template <bool DIL>
+__global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nqs) {
+  __shared__ __attribute__((aligned(16))) ColBlock sb[2];
+  __shared__ __attribute__((aligned(16))) ColBlockT st[2];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int bh = blockIdx.x % a.BH;
+  const int kb = blockIdx.x / a.BH;
+  const int T = a.T;
+  const int kw0 = kb * kColKeys + 32 * w;
+  const bool wave_live = kw0 < T;
+  const int key = kw0 + l32;
+  const size_t head = (size_t)bh * T * kHeadDim;
+  const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + head;
+  const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + head;
+  const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + head;
+  const __bf16 *G = reinterpret_cast<const __bf16 *>(a.dout) + head;
+  const float *L2 = a.lse2 + (size_t)bh * T;
+  const float *IR = a.invr + (size_t)bh * T;
+  const float *DR = a.dri + (size_t)bh * T;
+  const float *RH = a.rho + (size_t)bh * T;
+  const uint32_t *cin = nullptr, *gin = nullptr;
+  if constexpr (DIL) {
+    cin = reinterpret_cast<const uint32_t *>(a.cin) + (size_t)bh * cin_floats_per_head(T);
+    gin = reinterpret_cast<const uint32_t *>(a.gin) + (size_t)bh * gin_floats_per_head(T);
+  }
+  const uint32_t eps_word = split2_bf16(fmaxf(a.eps, FLT_MIN));
+
+  bf16x8 kf[4], vf[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    kf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(K, key, T, 2 * c + h));
+    vf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(V, key, T, 2 * c + h));
+  }
+  const ScanConsts sc = scan_consts(l32, h);
+  f32x16 dkt[2] = {zero16(), zero16()}, dvt[2] = {zero16(), zero16()};
+  __builtin_amdgcn_s_waitcnt(0);
+
+  const int qs_lo = (kb * kColKeys) / 32;
+  // loaders: thread tid holds row tid >> 3, chunk tid & 7 of the Q and dO
+  // blocks; for the transposed copies, rows 2 kp, 2 kp + 1 (kp = tid & 15)
+  // and chunk (tid >> 4) & 7 of the two tensors (Q for tid < 128, dO above).
+  u32x4 qreg, greg, tr0, tr1;
+  float lreg = 0.0f, ireg = 0.0f, rreg = 0.0f, hreg = 0.0f;
+  const int kp = tid & 15, tdc = (tid >> 4) & 7;
+  const bool tq = tid < 128;
+  auto load_block = [&](int qs) {
+    const int row0 = 32 * qs;
+    const int bytes = (T - row0) * (kHeadDim * 2);
+    const auto rq = make_rsrc(Q + (size_t)row0 * kHeadDim, bytes);
+    const auto rg = make_rsrc(G + (size_t)row0 * kHeadDim, bytes);
+    qreg = buf_load16(rq, 16u * tid);
+    greg = buf_load16(rg, 16u * tid);
+    const auto rt = tq ? rq : rg;
+    tr0 = buf_load16(rt, 256u * kp + 16u * tdc);
+    tr1 = buf_load16(rt, 256u * kp + 128u + 16u * tdc);
+    if (tid < 32) {
+      const int row = row0 + tid;
+      const bool ok = row < T;
+      const int rr = ok ? row : T - 1;
+      lreg = ok ? L2[rr] : kNoRow;
+      ireg = ok ? IR[rr] : 0.0f;
+      rreg = ok ? DR[rr] : 0.0f;
+      hreg = (DIL && ok) ? RH[rr] : 0.0f;
+    }
+  };
+  auto store_block = [&](int buf) {
+    *reinterpret_cast<u32x4 *>(&sb[buf].q[(tid >> 3) * kKRow + (tid & 7) * 8]) = qreg;
+    *reinterpret_cast<u32x4 *>(&sb[buf].g[(tid >> 3) * kKRow + (tid & 7) * 8]) = greg;
+    store_rows_transposed(tq ? st[buf].qt : st[buf].gt, kTRow, kp, tdc, tr0, tr1);
+    if (tid < 32) {
+      sb[buf].lse2[tid] = lreg;
+      sb[buf].invr[tid] = ireg;
+      sb[buf].dri[tid] = rreg;
+      sb[buf].rho[tid] = hreg;
+    }
+  };
+
+  load_block(qs_lo);
+  store_block(0);
+  __syncthreads();
+  for (int qs = qs_lo; qs < nqs; ++qs) {
+    const int buf = (qs - qs_lo) & 1;
+    if (qs + 1 < nqs) load_block(qs + 1);
+    if (wave_live && 32 * qs + 31 >= kw0) {
+      uint32_t cw = 0u, gw = 0u;
+      if constexpr (DIL) {
+        cw = key < 32 * qs ? cin[(size_t)16 * qs * (qs - 1) + key] : eps_word;
+        gw = (key < 32 * (qs + 1) && key < T) ? gin[(size_t)16 * qs * (qs + 1) + key] : 0u;
+      }
+      if (32 * qs == kw0)
+        dkdv_block<DIL, true>(sb[buf], st[buf], kf, vf, sc, cw, gw, a.c2, l32, h, dkt, dvt);
+      else
+        dkdv_block<DIL, false>(sb[buf], st[buf], kf, vf, sc, cw, gw, a.c2, l32, h, dkt, dvt);
+    }
+    if (qs + 1 < nqs) store_block(buf ^ 1);
+    __syncthreads();
+  }
+  if (!wave_live || key >= T) return;
+  // lane: key; element (u, r): dim 32u + acc_row(r, h)
+  __bf16 *dK = reinterpret_cast<__bf16 *>(a.dk) + head + (size_t)key * kHeadDim;
+  __bf16 *dV = reinterpret_cast<__bf16 *>(a.dv) + head + (size_t)key * kHeadDim;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * u + 8 * g + 4 * h;
+      u32x2 kk, vv;
+      kk[0] = pack_bf16x2(dkt[u][4 * g] * a.c, dkt[u][4 * g + 1] * a.c);
+      kk[1] = pack_bf16x2(dkt[u][4 * g + 2] * a.c, dkt[u][4 * g + 3] * a.c);
+      vv[0] = pack_bf16x2(dvt[u][4 * g], dvt[u][4 * g + 1]);
+      vv[1] = pack_bf16x2(dvt[u][4 * g + 2], dvt[u][4 * g + 3]);
+      *reinterpret_cast<u32x2 *>(dK + d0) = kk;
+      *reinterpret_cast<u32x2 *>(dV + d0) = vv;
+    }
+  }
+}
+
+// --------------------------------------------------------------- dQ rows
+//
+// A workgroup owns 128 query rows (wave w the 32 rows [qw0, qw0 + 32)) and
+// streams 64-key tiles of K (row-major, and transposed: the A operand of
+// dQ^T += K^T dS^T) and V (row-major) through LDS.  Scores are taken as S^T
+// (lane = query, element r = key acc_row(r, h)), so the per-row scalars are
+// per lane; the column scans need the bids and g with queries in the
+// operand slots, so those are moved to the S layout by identity products.
+
+struct DqConsts {
+  bf16x8 upre[2];   // B operands, slot (h, e) of operand j = query acc_row(8j+e, h):
+  bf16x8 usuf[2];   //   inclusive prefix (<= n), inclusive suffix (>= n)
+  bf16x8 ident[2];  //   and identity (== n); keys in place of queries for the
+  bf16x8 bone;      //   S^T -> S transpose.  bone: slots (0, 0..1) on h = 0.
+};
+
+__device__ __forceinline__ DqConsts dq_consts(int l32, int h) {
+  DqConsts c;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    float u[8], v[8], id[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int qs = acc_row(8 * j + e, h);
+      u[e] = qs <= l32 ? 1.0f : 0.0f;
+      v[e] = qs >= l32 ? 1.0f : 0.0f;
+      id[e] = qs == l32 ? 1.0f : 0.0f;
+    }
+    c.upre[j] = pack8(u);
+    c.usuf[j] = pack8(v);
+    c.ident[j] = pack8(id);
+  }
+  const float one = h == 0 ? 1.0f : 0.0f;
+  c.bone = to_bf16x8(one, one, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f);
+  return c;
+}
+
+struct DqState {
+  f32x16 x0, x1;   // X^T[d][query] = sum_j p_ij dp_ij k_j (tempered: sum_j dS_ij k_j)
+  f32x16 y0, y1;   // Y^T[d][query] = sum_j p_ij k_j (dilution)
+  f32x4 rho;       // sum_j p_ij dp_ij, every element equal (dilution)
+};
+
+template <bool DIL, bool DIAG>
+__device__ __forceinline__ void dq_subtile(DqState &st, const bf16x8 *qf, const bf16x8 *gf,
+                                           const DqConsts &dc, const bf16x8 &sel,
+                                           const __bf16 *kt_lds, const __bf16 *vt_lds,
+                                           const __bf16 *ktt_lds, int t, uint32_t cin_word,
+                                           uint32_t gin_word, float lse2, float invr, float dri,
+                                           int qrel, int l32, int h, float c2) {
+  // S^T and dA^T for keys 32t.. of the tile (lane = query)
+  const __bf16 *krow = kt_lds + (32 * t + l32) * kKRow;
+  const __bf16 *vrow = vt_lds + (32 * t + l32) * kKRow;
+  f32x16 s = zero16(), da = zero16();
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    s = mfma32(lds_frag(krow, c, h), qf[c], s);
+    da = mfma32(lds_frag(vrow, c, h), gf[c], da);
+  }
+  float p[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float e = fast_exp2(__builtin_fmaf(s[r], c2, -lse2));
+    if (DIAG && 32 * t + acc_row(r, h) > qrel) e = 0.0f;
+    p[r] = e;
+  }
+  const bf16x8 pt0 = pack8(p), pt1 = pack8(p + 8);
+  if constexpr (DIL) {
+    // the bids with queries in the slots (S layout), then D^T
+    f32x16 ps = mfma32(pt0, dc.ident[0], zero16());
+    ps = mfma32(pt1, dc.ident[1], ps);
+    float pv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pv[r] = ps[r];
+    const bf16x8 pa0 = pack8(pv), pa1 = pack8(pv + 8);
+    f32x16 d = mfma32(pa0, dc.upre[0], zero16());
+    d = mfma32(pa1, dc.upre[1], d);
+    d = mfma32(word_operand(cin_word), dc.bone, d);
+    float invd[16], dsg[16], g[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      invd[r] = fminf(fast_rcp(d[r]), kInvDMax);
+      const float sg = p[r] * invd[r];
+      dsg[r] = __builtin_fmaf(da[r], invr, -dri);
+      g[r] = dsg[r] * sg * invd[r];
+    }
+    // G^T: g to the S layout, then the inclusive suffix plus later blocks
+    f32x16 gs = mfma32(pack8(g), dc.ident[0], zero16());
+    gs = mfma32(pack8(g + 8), dc.ident[1], gs);
+    float gv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) gv[r] = gs[r];
+    f32x16 G = mfma32(pack8(gv), dc.usuf[0], zero16());
+    G = mfma32(pack8(gv + 8), dc.usuf[1], G);
+    G = mfma32(word_operand(gin_word), dc.bone, G);
+    float e[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) e[r] = p[r] * __builtin_fmaf(dsg[r], invd[r], -G[r]);
+    const bf16x8 ef0 = pack8(e), ef1 = pack8(e + 8);
+    pv_update(st.x0, st.x1, ktt_lds, t, l32, h, ef0, ef1);
+    pv_update(st.y0, st.y1, ktt_lds, t, l32, h, pt0, pt1);
+    st.rho = mfma16(sel, ef0, st.rho);
+    st.rho = mfma16(sel, ef1, st.rho);
+  } else {
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ds[r] = p[r] * (da[r] - dri);
+    pv_update(st.x0, st.x1, ktt_lds, t, l32, h, pack8(ds), pack8(ds + 8));
+  }
+}
+
+template <bool DIL>
+__global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2 * kKTile];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[2 * kKTile];
+  __shared__ __attribute__((aligned(16))) __bf16 sKt[2 * kVTile];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int bh = blockIdx.x % a.BH;
+  const int qb = nqb - 1 - blockIdx.x / a.BH;   // heaviest query blocks first
+  const int T = a.T;
+  const int q0 = qb * 128;
+  const int qw0 = q0 + 32 * w;
+  const bool wave_live = qw0 < T;
+  const int kd = qw0 / kBN;
+  const size_t head = (size_t)bh * T * kHeadDim;
+  const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + head;
+  const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + head;
+  const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + head;
+  const __bf16 *G = reinterpret_cast<const __bf16 *>(a.dout) + head;
+  const int kend = min(q0 + 128, T);
+  const int nkt = (kend + kBN - 1) / kBN;
+  const int row = qw0 + l32;
+  const bool row_ok = row < T;
+
+  bf16x8 qf[4], gf[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    qf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(Q, row, T, 2 * c + h));
+    gf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(G, row, T, 2 * c + h));
+  }
+  const size_t ridx = (size_t)bh * T + (row_ok ? row : T - 1);
+  const float lse2 = row_ok ? a.lse2[ridx] : kNoRow;
+  const float invr = row_ok ? a.invr[ridx] : 0.0f;
+  const float dri = row_ok ? a.dri[ridx] : 0.0f;
+  const DqConsts dc = dq_consts(l32, h);
+  const bf16x8 sel = rowsum_selector(lane);
+  const uint32_t eps_word = split2_bf16(fmaxf(a.eps, FLT_MIN));
+  const uint32_t *cin_blk = nullptr, *gin_blk = nullptr;
+  const int qsb = qw0 >> 5;   // this wave's 32-row block
+  if constexpr (DIL) {
+    cin_blk = reinterpret_cast<const uint32_t *>(a.cin) + (size_t)bh * cin_floats_per_head(T) +
+              (size_t)16 * qsb * (qsb - 1);
+    gin_blk = reinterpret_cast<const uint32_t *>(a.gin) + (size_t)bh * gin_floats_per_head(T) +
+              (size_t)16 * qsb * (qsb + 1);
+  }
+
+  u32x4 kreg[2], vreg[2], treg[2];
+  const uint32_t koff0 = 16u * tid, koff1 = 16u * (tid + 256);
+  const uint32_t toff0 = 256u * (tid & 31) + 16u * (tid >> 5), toff1 = toff0 + 128u;
+  auto load_tile = [&](int kt) {   // kt < nkt, so its first key is < T
+    const int key0 = kt * kBN;
+    const int bytes = (T - key0) * (kHeadDim * 2);
+    const auto rk = make_rsrc(K + (size_t)key0 * kHeadDim, bytes);
+    const auto rv = make_rsrc(V + (size_t)key0 * kHeadDim, bytes);
+    kreg[0] = buf_load16(rk, koff0);
+    kreg[1] = buf_load16(rk, koff1);
+    vreg[0] = buf_load16(rv, koff0);
+    vreg[1] = buf_load16(rv, koff1);
+    treg[0] = buf_load16(rk, toff0);
+    treg[1] = buf_load16(rk, toff1);
+  };
+  auto store_tile = [&](int buf) {
+    __bf16 *k = sK + buf * kKTile;
+    __bf16 *v = sV + buf * kKTile;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = tid + 256 * i;
+      *reinterpret_cast<u32x4 *>(k + (u >> 3) * kKRow + (u & 7) * 8) = kreg[i];
+      *reinterpret_cast<u32x4 *>(v + (u >> 3) * kKRow + (u & 7) * 8) = vreg[i];
+    }
+    store_rows_transposed(sKt + buf * kVTile, kVRow, tid & 31, tid >> 5, treg[0], treg[1]);
+  };
+  // committed demand (+eps) and later blocks' g sums of this wave's block on
+  // keys kt*64 + 32t + l32
+  uint32_t cw_next[2] = {0u, 0u}, gw_next[2] = {0u, 0u};
+  auto load_words = [&](int kt) {
+    if constexpr (DIL) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int key = kt * kBN + 32 * t + l32;
+        cw_next[t] = (wave_live && key < qw0) ? cin_blk[key] : eps_word;
+        // keys past the end are masked, but their sums enter the scans: zero
+        gw_next[t] = (wave_live && key < qw0 + 32 && key < T) ? gin_blk[key] : 0u;
+      }
+    }
+  };
+
+  DqState st;
+  st.x0 = zero16();
+  st.x1 = zero16();
+  st.y0 = zero16();
+  st.y1 = zero16();
+  st.rho = zero4();
+  __builtin_amdgcn_s_waitcnt(0);
+
+  load_tile(0);
+  store_tile(0);
+  load_words(0);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int buf = kt & 1;
+    const uint32_t cw[2] = {cw_next[0], cw_next[1]}, gw[2] = {gw_next[0], gw_next[1]};
+    if (kt + 1 < nkt) {
+      load_tile(kt + 1);
+      load_words(kt + 1);
+    }
+    if (wave_live && kt <= kd) {
+      const __bf16 *kl = sK + buf * kKTile, *vl = sV + buf * kKTile, *tl = sKt + buf * kVTile;
+      const int qrel = qw0 + l32 - kt * kBN;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        if (kt < kd)
+          dq_subtile<DIL, false>(st, qf, gf, dc, sel, kl, vl, tl, t, cw[t], gw[t], lse2, invr, dri,
+                                 qrel, l32, h, a.c2);
+        else
+          dq_subtile<DIL, true>(st, qf, gf, dc, sel, kl, vl, tl, t, cw[t], gw[t], lse2, invr, dri,
+                                qrel, l32, h, a.c2);
+      }
+    }
+    if (kt + 1 < nkt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+  if (!wave_live || !row_ok) return;
+  float rho = 0.0f;
+  if constexpr (DIL) {
+    rho = st.rho[0];
+    if (h == 0) a.rho[ridx] = rho;
+  }
+  __bf16 *dQ = reinterpret_cast<__bf16 *>(a.dq) + head + (size_t)row * kHeadDim;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int d0 = 8 * g + 4 * h;
+    float lo[4], hi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo[i] = a.c * __builtin_fmaf(-rho, st.y0[4 * g + i], st.x0[4 * g + i]);
+      hi[i] = a.c * __builtin_fmaf(-rho, st.y1[4 * g + i], st.x1[4 * g + i]);
+    }
+    u32x2 l2, h2;
+    l2[0] = pack_bf16x2(lo[0], lo[1]);
+    l2[1] = pack_bf16x2(lo[2], lo[3]);
+    h2[0] = pack_bf16x2(hi[0], hi[1]);
+    h2[1] = pack_bf16x2(hi[2], hi[3]);
+    *reinterpret_cast<u32x2 *>(dQ + d0) = l2;
+    *reinterpret_cast<u32x2 *>(dQ + 32 + d0) = h2;
+  }
+}
+
+hipError_t launch_bwd_bf16(int mode, const BwdArgs &a, hipStream_t s) {
+  const bool dil = mode == 1;
+  const size_t rows = (size_t)a.BH * a.T;
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, s,
+                     a, dil ? 1 : 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nqs = (a.T + 31) / 32;
+  const int nkb = (a.T + kColKeys - 1) / kColKeys;
+  const int nqb = (a.T + 127) / 128;
+  if (dil) {
+    FwdArgs f{};
+    f.q = a.q;
+    f.k = a.k;
+    f.lse2 = a.lse2;
+    f.cin = a.cin;
+    f.BH = a.BH;
+    f.T = a.T;
+    f.c2 = a.c2;
+    f.eps = a.eps;
+    e = launch_colsum_bf16(f, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_gsum_kernel, dim3((unsigned)(nkb * a.BH)), dim3(256), 0, s, a, nqs);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3((unsigned)(nqb * a.BH)), dim3(256), 0, s, a, nqb);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3((unsigned)(nkb * a.BH)), dim3(256), 0, s, a,
+                       nqs);
+  } else {
+    hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3((unsigned)(nqb * a.BH)), dim3(256), 0, s, a,
+                       nqb);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3((unsigned)(nkb * a.BH)), dim3(256), 0, s, a,
+                       nqs);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace attn

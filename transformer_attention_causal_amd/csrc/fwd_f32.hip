@@ -101,6 +101,9 @@ __global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
     if (a.lse2) a.lse2[(size_t)bh * T + i] = l2;
     if (a.lse_nat) a.lse_nat[(size_t)bh * T + i] = l2 * kLn2;
   }
+  if constexpr (MODE == kRowShare) {
+    if (a.rowsum_out) a.rowsum_out[(size_t)bh * T + i] = l;
+  }
   if constexpr (MODE != kRowLse) {
     float *O = reinterpret_cast<float *>(a.out) + head + (size_t)i * kHeadDim;
     const float inv = 1.0f / l;

@@ -22,6 +22,7 @@ struct FwdArgs {
                         // bf16 path stores each entry as a bf16 (hi, lo) pair of
                         // committed + eps in the same 32 bits
   float *demand_out;    // [BH*T] optional final column totals (dilution)
+  float *rowsum_out;    // [BH*T] optional row sums of the shares (dilution)
   int BH, T;
   float c2;             // tau / sqrt(d) * log2(e)
   float eps;
@@ -38,6 +39,32 @@ hipError_t launch_rows_bf16(int mode, const FwdArgs &a, hipStream_t s);
 hipError_t launch_colsum_bf16(const FwdArgs &a, hipStream_t s);
 hipError_t launch_rows_f32(int mode, const FwdArgs &a, hipStream_t s);
 hipError_t launch_colsum_f32(const FwdArgs &a, hipStream_t s);
+
+// Suffix sums of the committed-demand gradient terms: query sub-block qs keeps
+// one entry per key j < 32*(qs+1), at offset 16*qs*(qs+1) in its head's region.
+__host__ __device__ inline size_t gin_floats_per_head(int T) {
+  const size_t n = ((size_t)T + 31) / 32;
+  return 16 * n * (n + 1);
+}
+
+struct BwdArgs {
+  const void *q, *k, *v, *o, *dout;
+  const float *lse;       // [BH*T] natural-log log-sum-exp of each row (forward)
+  const float *rowsum;    // [BH*T] dilution: row sums of the shares (forward)
+  void *dq, *dk, *dv;
+  float *lse2;            // [BH*T] workspace: log2-domain log-sum-exp
+  float *invr;            // [BH*T] workspace: 1 / rowsum (dilution)
+  float *dri;             // [BH*T] workspace: <dO_i, o_i> / rowsum (tempered: <dO_i, o_i>)
+  float *rho;             // [BH*T] workspace: sum_j p_ij dp_ij (dilution)
+  float *cin;             // committed demand + eps per (32-row block, key), bf16 pairs
+  float *gin;             // later blocks' share-gradient sums per (block, key), bf16 pairs
+  int BH, T;
+  float c2;               // tau / sqrt(d) * log2(e)
+  float c;                // tau / sqrt(d)
+  float eps;
+};
+
+hipError_t launch_bwd_bf16(int mode, const BwdArgs &a, hipStream_t s);
 
 struct DecodeArgs {
   const void *q, *kc, *vc;

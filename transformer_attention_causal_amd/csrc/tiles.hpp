@@ -1,0 +1,72 @@
+// tiles.hpp -- LDS tile geometry and operand-fragment helpers shared by the
+// bf16 forward and backward kernels (layout facts in attn_common.hpp).
+#pragma once
+
+#include "attn_common.hpp"
+
+namespace attn {
+
+constexpr int kBN = 64;         // keys per LDS tile (row kernels)
+constexpr int kKRow = 72;       // LDS row stride of K tiles, bf16 (64 + 8 pad)
+constexpr int kVRow = 68;       // LDS row stride of V^T tiles, bf16 (64 keys + 4 pad)
+constexpr int kKTile = kBN * kKRow;        // bf16 elements per K buffer
+constexpr int kVTile = kHeadDim * kVRow;   // bf16 elements per V^T buffer
+constexpr float kNoRow = 1e30f;            // log-sum-exp given to rows past the end
+
+// Query index (within a wave's 32 rows) of accumulator element r in lane half h.
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Load one 16-byte chunk of a [BH][T][64] bf16 tensor, zeros past the end.
+__device__ __forceinline__ u32x4 load_row_chunk(const __bf16 *base, int row, int T, int chunk) {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  if (row < T) z = *reinterpret_cast<const u32x4 *>(base + (size_t)row * kHeadDim + chunk * 8);
+  return z;
+}
+
+// A/B operand fragment for d-chunk c of a 64-wide bf16 row held in LDS.
+__device__ __forceinline__ bf16x8 lds_frag(const __bf16 *row, int c, int h) {
+  return *reinterpret_cast<const bf16x8 *>(row + 16 * c + 8 * h);
+}
+
+// V^T operand for keys [16c+4h, +4) and [16c+8+4h, +4) of a 32-key sub-tile.
+__device__ __forceinline__ bf16x8 lds_vfrag(const __bf16 *vrow, int c, int h) {
+  u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + 16 * c + 4 * h);
+  u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 16 * c + 8 + 4 * h);
+  u32x4 u = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float *v) {
+  return to_bf16x8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
+}
+
+// O^T[d][query] += V^T[d][keys of sub-tile t] * P^T[keys][query] for both
+// 32-row halves of d.  pf0/pf1 hold keys 0..15 / 16..31 of the sub-tile in
+// the accumulator-layout order.
+__device__ __forceinline__ void pv_update(f32x16 &o0, f32x16 &o1, const __bf16 *vt_lds, int t,
+                                          int l32, int h, const bf16x8 &pf0, const bf16x8 &pf1) {
+  const __bf16 *v0 = vt_lds + l32 * kVRow + 32 * t;
+  const __bf16 *v1 = vt_lds + (32 + l32) * kVRow + 32 * t;
+  o0 = mfma32(lds_vfrag(v0, 0, h), pf0, o0);
+  o1 = mfma32(lds_vfrag(v1, 0, h), pf0, o1);
+  o0 = mfma32(lds_vfrag(v0, 1, h), pf1, o0);
+  o1 = mfma32(lds_vfrag(v1, 1, h), pf1, o1);
+}
+
+// Rows 2kp and 2kp+1 (d-chunk dc, 8 elements each) of a [rows][64] bf16 tile,
+// written transposed into a dim-major LDS tile of row stride `stride`:
+// element (row, dim) lands at dst[dim * stride + row].  Pairs of rows are
+// merged with byte permutes so every LDS store is 32 bits wide.
+__device__ __forceinline__ void store_rows_transposed(__bf16 *dst, int stride, int kp, int dc,
+                                                      const u32x4 &r0, const u32x4 &r1) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a0 = r0[i], a1 = r1[i];
+    const uint32_t even = __builtin_amdgcn_perm(a1, a0, 0x05040100u);  // dim 8dc + 2i
+    const uint32_t odd = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // dim 8dc + 2i + 1
+    *reinterpret_cast<uint32_t *>(dst + (8 * dc + 2 * i) * stride + 2 * kp) = even;
+    *reinterpret_cast<uint32_t *>(dst + (8 * dc + 2 * i + 1) * stride + 2 * kp) = odd;
+  }
+}
+
+}  // namespace attn

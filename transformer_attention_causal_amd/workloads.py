@@ -145,6 +145,12 @@ def draw_qkv(B: int, H: int, T: int, d: int, dtype: str, seed: int, scale: float
     return HostInputs(q, k, v, dtype, heavy)
 
 
+def draw_grad(B: int, H: int, T: int, d: int, seed: int) -> np.ndarray:
+    """An incoming output gradient dO ~ N(0,1), bf16 bit patterns (stream seed+29)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 29))
+    return bf16_round_bits(rng.standard_normal((B, H, T, d)).astype(np.float32))
+
+
 def prefill_inputs(w: Prefill, T: int | None = None, H: int | None = None,
                    B: int | None = None) -> HostInputs:
     """Inputs of a named forward workload (optionally at a reduced shape)."""
