@@ -103,7 +103,8 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, int B, i
 /* Bytes of device workspace attn_bwd needs: four fp32 values per query row,
  * and for dilution the committed demand and the later rows' gradient sums
  * per (32-row query block, key): B*H*16*n*(n-1) and B*H*16*n*(n+1) floats,
- * n = ceil(T/32).  0 for an unsupported shape, mode or dtype (bf16 only). */
+ * n = ceil(T/32), plus a bf16 [B,H,T,d] array.  0 for an unsupported shape,
+ * mode or dtype (bf16 only). */
 size_t attn_bwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype);
 
 /* Exact gradients of either operator (DilutionAttention v0.1.0: the release's

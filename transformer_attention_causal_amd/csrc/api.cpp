@@ -282,9 +282,10 @@ namespace {
 
 // Workspace layout of a backward pass: four per-row fp32 arrays (lse2, 1/r,
 // delta/r, rho), then for dilution the committed demand and the later blocks'
-// gradient sums, per (32-row block, key).
+// gradient sums, per (32-row block, key), and the bf16 [B,H,T,d] array of
+// softmax-weighted keys.
 struct BwdWorkspace {
-  size_t row_bytes, cin_bytes, gin_bytes, total;
+  size_t row_bytes, cin_bytes, gin_bytes, pk_bytes, total;
 };
 
 bool bwd_workspace(int B, int H, int T, int mode, BwdWorkspace *ws) {
@@ -293,7 +294,8 @@ bool bwd_workspace(int B, int H, int T, int mode, BwdWorkspace *ws) {
   ws->row_bytes = round_up(BH * (size_t)T * sizeof(float));
   ws->cin_bytes = mode == ATTN_DILUTION ? round_up(BH * attn::cin_floats_per_head(T) * 4) : 0;
   ws->gin_bytes = mode == ATTN_DILUTION ? round_up(BH * attn::gin_floats_per_head(T) * 4) : 0;
-  ws->total = 4 * ws->row_bytes + ws->cin_bytes + ws->gin_bytes;
+  ws->pk_bytes = mode == ATTN_DILUTION ? round_up(BH * (size_t)T * attn::kHeadDim * 2) : 0;
+  ws->total = 4 * ws->row_bytes + ws->cin_bytes + ws->gin_bytes + ws->pk_bytes;
   return true;
 }
 
@@ -362,6 +364,7 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *out, const
   if (mode == ATTN_DILUTION) {
     a.cin = reinterpret_cast<float *>(wsp + 4 * ws.row_bytes);
     a.gin = reinterpret_cast<float *>(wsp + 4 * ws.row_bytes + ws.cin_bytes);
+    a.pk = wsp + 4 * ws.row_bytes + ws.cin_bytes + ws.gin_bytes;
   }
   a.BH = B * H;
   a.T = T;

@@ -15,13 +15,15 @@
 //   dQ_i = c sum_j dS_ij k_j,   dK_j = c sum_i dS_ij q_i,   c = tau / sqrt(d).
 // Tempered attention is the same with a = p: dS_ij = p_ij (dA_ij - delta_i).
 //
-// Passes (dilution; tempered skips 2 and 3):
+// Passes (dilution; tempered skips 2, 3 and 4):
 //   1 bwd_prep_kernel   per row: log2-domain lse, 1/r, delta/r
 //   2 colsum_bf16_kernel (the forward's) committed demand per 32-row block
 //   3 bwd_gsum_kernel   per key, walking 32-row blocks from the last one up:
 //                       the sum of g over every later block (G's block part)
-//   4 bwd_dq_kernel     per 32 query rows: dQ, rho
-//   5 bwd_dkdv_kernel   per 32 keys: dK, dV
+//   4 rows_bf16_kernel  (the tempered forward with V := K) PK_i = sum_j p_ij k_j
+//   5 bwd_dq_kernel     per 32 query rows: X_i = sum_j p_ij dp_ij k_j and rho,
+//                       then dQ_i = c (X_i - rho_i PK_i)
+//   6 bwd_dkdv_kernel   per 32 keys: dK, dV
 // Both in-block scans (the column prefix inside D and the column suffix
 // inside G) are matrix-core products against constant triangular operands,
 // as in the forward shares pass.
@@ -292,21 +294,43 @@ __device__ __forceinline__ void dkdv_block(const ColBlock &b, const ColBlockT &b
   col_scores(b, kf, vf, l32, h, s, da);
   float ds[16], aw[16];
   if constexpr (DIL) {
-    ColTerms t;
-    col_terms<DIAG>(s, da, b, sc, cin_word, c2, l32, h, t);
-    // G = gradient terms of the later blocks + inclusive suffix in this one
-    const bf16x8 ga0 = pack8(t.g), ga1 = pack8(t.g + 8);
-    f32x16 G = mfma32(sc.ge[0], ga0, zero16());
-    G = mfma32(sc.ge[1], ga1, G);
-    G = mfma32(sc.ones, word_operand(gin_word), G);
-    float iq[16], pq[16];
+    // written out stage by stage so each per-row array and temporary dies
+    // as soon as it is used
+    float lq[16];
+    col_rowvals(b.lse2, h, lq);
+    float p[16];
+    col_bids<DIAG>(s, lq, c2, l32, h, p);
+    f32x16 d = mfma32(sc.le[0], pack8(p), zero16());
+    d = mfma32(sc.le[1], pack8(p + 8), d);
+    d = mfma32(sc.ones, word_operand(cin_word), d);
+    float invd[16], sg[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      invd[r] = fminf(fast_rcp(d[r]), kInvDMax);
+      sg[r] = p[r] * invd[r];
+    }
+    float iq[16];
     col_rowvals(b.invr, h, iq);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) aw[r] = sg[r] * iq[r];
+    float rq[16];
+    col_rowvals(b.dri, h, rq);
+    float dsg[16], g[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dsg[r] = __builtin_fmaf(da[r], iq[r], -rq[r]);
+      g[r] = dsg[r] * sg[r] * invd[r];
+    }
+    // G = gradient terms of the later blocks + inclusive suffix in this one
+    f32x16 G = mfma32(sc.ge[0], pack8(g), zero16());
+    G = mfma32(sc.ge[1], pack8(g + 8), G);
+    G = mfma32(sc.ones, word_operand(gin_word), G);
+    float pq[16];
     col_rowvals(b.rho, h, pq);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float dp = __builtin_fmaf(t.dsg[r], t.invd[r], -G[r]);
-      ds[r] = t.p[r] * (dp - pq[r]);
-      aw[r] = t.sg[r] * iq[r];
+      const float dp = __builtin_fmaf(dsg[r], invd[r], -G[r]);
+      ds[r] = p[r] * (dp - pq[r]);
     }
   } else {
     float lq[16], rq[16];
@@ -487,7 +511,6 @@ __device__ __forceinline__ DqConsts dq_consts(int l32, int h) {
 
 struct DqState {
   f32x16 x0, x1;   // X^T[d][query] = sum_j p_ij dp_ij k_j (tempered: sum_j dS_ij k_j)
-  f32x16 y0, y1;   // Y^T[d][query] = sum_j p_ij k_j (dilution)
   f32x4 rho;       // sum_j p_ij dp_ij, every element equal (dilution)
 };
 
@@ -548,7 +571,6 @@ __device__ __forceinline__ void dq_subtile(DqState &st, const bf16x8 *qf, const 
     for (int r = 0; r < 16; ++r) e[r] = p[r] * __builtin_fmaf(dsg[r], invd[r], -G[r]);
     const bf16x8 ef0 = pack8(e), ef1 = pack8(e + 8);
     pv_update(st.x0, st.x1, ktt_lds, t, l32, h, ef0, ef1);
-    pv_update(st.y0, st.y1, ktt_lds, t, l32, h, pt0, pt1);
     st.rho = mfma16(sel, ef0, st.rho);
     st.rho = mfma16(sel, ef1, st.rho);
   } else {
@@ -650,8 +672,6 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
   DqState st;
   st.x0 = zero16();
   st.x1 = zero16();
-  st.y0 = zero16();
-  st.y1 = zero16();
   st.rho = zero4();
   __builtin_amdgcn_s_waitcnt(0);
 
@@ -669,7 +689,9 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
     if (wave_live && kt <= kd) {
       const __bf16 *kl = sK + buf * kKTile, *vl = sV + buf * kKTile, *tl = sKt + buf * kVTile;
       const int qrel = qw0 + l32 - kt * kBN;
-#pragma unroll
+      // one sub-tile at a time: the per-sub-tile temporaries would not fit
+      // twice beside the accumulators
+#pragma unroll 1
       for (int t = 0; t < 2; ++t) {
         if (kt < kd)
           dq_subtile<DIL, false>(st, qf, gf, dc, sel, kl, vl, tl, t, cw[t], gw[t], lse2, invr, dri,
@@ -683,20 +705,31 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
     __syncthreads();
   }
   if (!wave_live || !row_ok) return;
+  __bf16 *dQ = reinterpret_cast<__bf16 *>(a.dq) + head + (size_t)row * kHeadDim;
   float rho = 0.0f;
+  const __bf16 *PK = nullptr;
   if constexpr (DIL) {
     rho = st.rho[0];
     if (h == 0) a.rho[ridx] = rho;
+    PK = reinterpret_cast<const __bf16 *>(a.pk) + head + (size_t)row * kHeadDim;
   }
-  __bf16 *dQ = reinterpret_cast<__bf16 *>(a.dq) + head + (size_t)row * kHeadDim;
+  // lane: query; element (half u, r): dim 32u + acc_row(r, h)
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int d0 = 8 * g + 4 * h;
+    float pk[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (DIL) {
+      const u32x2 lo = *reinterpret_cast<const u32x2 *>(PK + d0);
+      const u32x2 hi = *reinterpret_cast<const u32x2 *>(PK + 32 + d0);
+      const uint32_t w0 = lo[0], w1 = lo[1], w2 = hi[0], w3 = hi[1];
+      pk[0] = bf16_lo(w0); pk[1] = bf16_hi(w0); pk[2] = bf16_lo(w1); pk[3] = bf16_hi(w1);
+      pk[4] = bf16_lo(w2); pk[5] = bf16_hi(w2); pk[6] = bf16_lo(w3); pk[7] = bf16_hi(w3);
+    }
     float lo[4], hi[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      lo[i] = a.c * __builtin_fmaf(-rho, st.y0[4 * g + i], st.x0[4 * g + i]);
-      hi[i] = a.c * __builtin_fmaf(-rho, st.y1[4 * g + i], st.x1[4 * g + i]);
+      lo[i] = a.c * __builtin_fmaf(-rho, pk[i], st.x0[4 * g + i]);
+      hi[i] = a.c * __builtin_fmaf(-rho, pk[4 + i], st.x1[4 * g + i]);
     }
     u32x2 l2, h2;
     l2[0] = pack_bf16x2(lo[0], lo[1]);
@@ -732,6 +765,17 @@ hipError_t launch_bwd_bf16(int mode, const BwdArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_gsum_kernel, dim3((unsigned)(nkb * a.BH)), dim3(256), 0, s, a, nqs);
     e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // PK = softmax-weighted keys: the tempered forward with the keys as values
+    FwdArgs t{};
+    t.q = a.q;
+    t.k = a.k;
+    t.v = a.k;
+    t.out = a.pk;
+    t.BH = a.BH;
+    t.T = a.T;
+    t.c2 = a.c2;
+    e = launch_rows_bf16(kRowTempered, t, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3((unsigned)(nqb * a.BH)), dim3(256), 0, s, a, nqb);
     e = hipGetLastError();

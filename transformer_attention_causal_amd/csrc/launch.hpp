@@ -58,6 +58,7 @@ struct BwdArgs {
   float *rho;             // [BH*T] workspace: sum_j p_ij dp_ij (dilution)
   float *cin;             // committed demand + eps per (32-row block, key), bf16 pairs
   float *gin;             // later blocks' share-gradient sums per (block, key), bf16 pairs
+  void *pk;               // [BH*T*64] bf16 workspace: sum_j p_ij k_j (dilution)
   int BH, T;
   float c2;               // tau / sqrt(d) * log2(e)
   float c;                // tau / sqrt(d)
