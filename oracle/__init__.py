@@ -14,6 +14,10 @@ module only builds/loads that library and marshals numpy arrays.  Functions:
   operator": bids, exclusive column cumsum, shares, renormalised A, A@v).
 * ``dilution_decode_step`` -- its cached-decode step (same page: K/V cache
   plus one running demand total per key and head).
+* ``prefill`` -- a later chunk of a prefill (queries at the last Tq
+  positions over cached keys), either operator; dilution continues from the
+  demand the earlier rows committed (the cached-decoding sentence's running
+  demand per key and head).
 * ``attn_bwd`` -- exact gradients (dq, dk, dv) of either operator by the
   chain rule through its definition (the dilution page ships training kernels
   with exact gradients), plus the dilution row sums of the shares.
@@ -107,6 +111,8 @@ def _declare(lib):
         lib.oracle_dilution_decode_step.restype = i
         lib.oracle_dilution_decode_step.argtypes = [vp, vp, vp, i, dp, dp, i, i, i, i, ip,
                                                     d, d, ip, i]
+        lib.oracle_prefill.restype = i
+        lib.oracle_prefill.argtypes = [vp, vp, vp, i, dp, dp, dp, i, i, i, i, i, i, d, d, i]
         lib.oracle_attn_bwd.restype = i
         lib.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, i, dp, dp, dp, dp, i, i, i, i, d, d, i]
 
@@ -229,6 +235,39 @@ def dilution_decode_step(q, kcache, vcache, demand: np.ndarray, tau: float = 1.0
     if rc != 0:
         raise RuntimeError(f"oracle_dilution_decode_step failed ({rc})")
     return out
+
+
+def prefill(q, kcache, vcache, Tk: int, tau: float = 1.0, eps: float = 1e-6, mode: int = 1,
+            demand=None):
+    """A chunk of a prefill: q [B,H,Tq,d] holds the rows at positions Tk-Tq..Tk-1;
+    the caches [B,H,Lcap,d] hold keys 0..Tk-1.  mode 0 tempered, 1 dilution.
+    ``demand`` ([B,H,Lcap] float64, dilution) is the demand committed before the
+    chunk and is updated IN PLACE to include the chunk's bids (None: zero start,
+    nothing returned).  Returns (out [B,H,Tq,d], lse [B,H,Tq]) in fp64."""
+    lib = _load()
+    qa, c1 = _as_input(q)
+    ka, c2 = _as_input(kcache)
+    va, c3 = _as_input(vcache)
+    code = _same_code(c1, c2, c3)
+    B, H, Tq, d = qa.shape
+    Lcap = ka.shape[2]
+    if ka.shape != (B, H, Lcap, d) or va.shape != ka.shape:
+        raise ValueError("cache shape mismatch")
+    dp_ = None
+    if demand is not None:
+        if demand.dtype != np.float64 or not demand.flags.c_contiguous:
+            raise TypeError("demand must be a C-contiguous float64 array (updated in place)")
+        if demand.shape != (B, H, Lcap):
+            raise ValueError("demand shape mismatch")
+        dp_ = _ptr(demand)
+    out = np.full((B, H, Tq, d), np.nan)
+    lse = np.full((B, H, Tq), np.nan)
+    rc = lib.oracle_prefill(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, code, _ptr(out),
+                            _ptr(lse), dp_, B, H, Tq, int(Tk), Lcap, d, float(tau), float(eps),
+                            int(mode))
+    if rc != 0:
+        raise RuntimeError(f"oracle_prefill failed ({rc})")
+    return out, lse
 
 
 def attn_bwd(q, k, v, dout, tau: float = 1.0, eps: float = 1e-6, mode: int = 1):

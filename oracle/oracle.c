@@ -195,19 +195,23 @@ int oracle_tempered_fwd(const void *q, const void *k, const void *v, int dtype, 
  *   share_ij = p_ij / (committed_ij + p_ij + eps)   (0 where p_ij = 0)
  *   A_ij     = share_ij / sum_j share_ij ;  o_i = sum_j A_ij v_j
  * then D_j += p_ij before the next row.
- * want[i] != 0 selects the rows whose output is formed (all rows still add
- * their bids to D).  D (length T) enters as the demand already committed
- * before row 0 -- zero for a plain prefill -- and leaves as the final column
- * totals.
+ * The query rows are the positions P..T-1 (P = 0 for a whole prefill; a
+ * later chunk of a prefill starts at P > 0 over the same keys 0..T-1).  Qh,
+ * Oh, lse_h and want are indexed by i - P.  want[i - P] != 0 selects the rows
+ * whose output is formed (all rows still add their bids to D).  D (length T)
+ * enters as the demand already committed before row P -- zero for a plain
+ * prefill, the earlier chunks' column totals otherwise -- and leaves as the
+ * final column totals.
  */
-static void dilution_head(const double *Qh, const double *Kh, const double *Vh, int T, int d,
-                          double c, double eps, const unsigned char *want, double *Oh,
+static void dilution_head(const double *Qh, const double *Kh, const double *Vh, int P, int T,
+                          int d, double c, double eps, const unsigned char *want, double *Oh,
                           double *lse_h, double *D, double *p, int inner_parallel) {
-  for (int i = 0; i < T; ++i) {
+  for (int i = P; i < T; ++i) {
     const int par = inner_parallel && i + 1 >= PAR_MIN_ROW;
-    const double l = causal_bids(Qh + (size_t)i * d, Kh, i, d, c, p, inner_parallel);
-    if (lse_h) lse_h[i] = l;
-    if (!want || want[i]) {
+    const int li = i - P;
+    const double l = causal_bids(Qh + (size_t)li * d, Kh, i, d, c, p, inner_parallel);
+    if (lse_h) lse_h[li] = l;
+    if (!want || want[li]) {
       double r = 0.0;
       double acc[512];
       for (int e = 0; e < d; ++e) acc[e] = 0.0;
@@ -246,7 +250,7 @@ static void dilution_head(const double *Qh, const double *Kh, const double *Vh, 
           }
         }
       }
-      for (int e = 0; e < d; ++e) Oh[(size_t)i * d + e] = acc[e] / r;
+      for (int e = 0; e < d; ++e) Oh[(size_t)li * d + e] = acc[e] / r;
     }
 #pragma omp parallel for if (par) schedule(static)
     for (int j = 0; j <= i; ++j) D[j] += p[j];
@@ -271,8 +275,8 @@ static int dilution_one_head(const void *q, const void *k, const void *v, int dt
     widen_block(Qh, q, dtype, base, (size_t)T * d);
     widen_block(Kh, k, dtype, base, (size_t)T * d);
     widen_block(Vh, v, dtype, base, (size_t)T * d);
-    dilution_head(Qh, Kh, Vh, T, d, c, eps, want, out + base, lse ? lse + (size_t)bh * T : NULL,
-                  D, p, inner_parallel);
+    dilution_head(Qh, Kh, Vh, 0, T, d, c, eps, want, out + base,
+                  lse ? lse + (size_t)bh * T : NULL, D, p, inner_parallel);
     if (demand) memcpy(demand + (size_t)bh * T, D, sizeof(double) * (size_t)T);
   }
   free(Qh); free(Kh); free(Vh); free(D); free(p);
@@ -320,6 +324,63 @@ int oracle_dilution_fwd(const void *q, const void *k, const void *v, int dtype, 
         failed = 1;
   }
   free(want);
+  return failed ? -2 : 0;
+}
+
+/*
+ * A later chunk of a prefill, either operator.  The keys 0..Tk-1 of each
+ * (b, h) sit in caches with room for Lcap rows per head; the chunk's Tq query
+ * rows are the positions P = Tk-Tq .. Tk-1, and row i sees keys j <= i.
+ *   tempered: o_i = sum_{j<=i} p_ij v_j                 ([FOCAL] eq. focal-const)
+ *   dilution: committed_ij = Din_j + sum_{P<=i'<i} p_i'j  ([DIL] "The operator",
+ *             with the demand the cached-decoding sentence keeps per key and
+ *             head standing in for the rows before P), then the shares and
+ *             the renormalised weights as for a whole prefill.
+ * q: [B,H,Tq,d]; kc, vc: [B,H,Lcap,d]; out: [B,H,Tq,d] fp64; lse (optional):
+ * [B,H,Tq]; demand (dilution, optional): [B,H,Lcap] fp64, in: Din (zero where
+ * NULL), out: Din + the chunk's column totals on keys < Tk (others untouched).
+ * mode: 0 tempered, 1 dilution.
+ */
+int oracle_prefill(const void *q, const void *kc, const void *vc, int dtype, double *out,
+                   double *lse, double *demand, int B, int H, int Tq, int Tk, int Lcap, int d,
+                   double tau, double eps, int mode) {
+  if (B <= 0 || H <= 0 || Tq <= 0 || Tk < Tq || Lcap < Tk || d <= 0 || d > 512) return -1;
+  const double c = tau / sqrt((double)d);
+  const int P = Tk - Tq;
+  int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int bh = 0; bh < B * H; ++bh) {
+    const size_t qbase = (size_t)bh * Tq * d, kbase = (size_t)bh * Lcap * d;
+    double *Qh = malloc(sizeof(double) * (size_t)Tq * d);
+    double *Kh = malloc(sizeof(double) * (size_t)Tk * d);
+    double *Vh = malloc(sizeof(double) * (size_t)Tk * d);
+    double *D = calloc((size_t)Tk, sizeof(double));
+    double *p = malloc(sizeof(double) * (size_t)Tk);
+    if (!Qh || !Kh || !Vh || !D || !p) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+      widen_block(Qh, q, dtype, qbase, (size_t)Tq * d);
+      widen_block(Kh, kc, dtype, kbase, (size_t)Tk * d);
+      widen_block(Vh, vc, dtype, kbase, (size_t)Tk * d);
+      double *lse_h = lse ? lse + (size_t)bh * Tq : NULL;
+      if (mode == 1) {
+        if (demand) memcpy(D, demand + (size_t)bh * Lcap, sizeof(double) * (size_t)Tk);
+        dilution_head(Qh, Kh, Vh, P, Tk, d, c, eps, NULL, out + qbase, lse_h, D, p, 0);
+        if (demand) memcpy(demand + (size_t)bh * Lcap, D, sizeof(double) * (size_t)Tk);
+      } else {
+        for (int i = P; i < Tk; ++i) {
+          const double l = causal_bids(Qh + (size_t)(i - P) * d, Kh, i, d, c, p, 0);
+          double *o = out + qbase + (size_t)(i - P) * d;
+          for (int e = 0; e < d; ++e) o[e] = 0.0;
+          for (int j = 0; j <= i; ++j)
+            for (int e = 0; e < d; ++e) o[e] += p[j] * Vh[(size_t)j * d + e];
+          if (lse_h) lse_h[i - P] = l;
+        }
+      }
+    }
+    free(Qh); free(Kh); free(Vh); free(D); free(p);
+  }
   return failed ? -2 : 0;
 }
 

@@ -250,6 +250,92 @@ def pin_dilution_subsets():
     assert np.all(np.isnan(part[0, 0]))
 
 
+# ------------------------------------------------------------------ chunked prefill
+
+def _chunked(q, k, v, bounds, Lcap, tau, eps, mode, fill=7.0):
+    """Run the prefill oracle chunk by chunk (rows [bounds[i], bounds[i+1]))
+    over caches of Lcap rows whose unused tail holds NaN; returns the rows'
+    outputs, LSEs and the carried demand (unused entries start at ``fill``)."""
+    B, H, T, d = q.shape
+    kc = np.full((B, H, Lcap, d), np.nan)
+    vc = np.full((B, H, Lcap, d), np.nan)
+    D = np.full((B, H, Lcap), fill)
+    D[:, :, :T] = 0.0
+    outs, lses = [], []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        kc[:, :, a:b] = k[:, :, a:b]                 # append the chunk's keys/values
+        vc[:, :, a:b] = v[:, :, a:b]
+        o, l = oracle.prefill(np.ascontiguousarray(q[:, :, a:b]), kc, vc, b, tau, eps, mode,
+                              D if mode == 1 else None)
+        outs.append(o)
+        lses.append(l)
+    return np.concatenate(outs, axis=2), np.concatenate(lses, axis=2), D
+
+
+def pin_prefill_chunks_compose():
+    """A prefill run in chunks -- each over the keys so far, dilution carrying
+    the demand committed by the earlier chunks -- gives the whole prefill's
+    rows, LSEs and final column totals; cache rows past the keys are never
+    read and their demand entries are left as they were."""
+    rng = _rng(30)
+    B, H, T, d = 1, 2, 37, 16
+    q, k, v = (rng.standard_normal((B, H, T, d)) for _ in range(3))
+    for bounds in ((0, 37), (0, 11, 37), (0, 1, 2, 30, 37), tuple(range(38))):
+        out, lse, D = _chunked(q, k, v, bounds, 45, 1.2, 1e-6, 1)
+        ref, rlse, dem = oracle.dilution_fwd(q, k, v, 1.2, 1e-6)
+        assert np.max(np.abs(out - ref)) < 1e-12, bounds
+        assert np.max(np.abs(lse - rlse)) < 1e-12, bounds
+        assert np.max(np.abs(D[:, :, :T] - dem)) < 1e-12, bounds
+        assert np.all(D[:, :, T:] == 7.0)
+        out, lse, _ = _chunked(q, k, v, bounds, 45, 1.2, 1e-6, 0)
+        ref, rlse = oracle.tempered_fwd(q, k, v, 1.2)
+        assert np.max(np.abs(out - ref)) < 1e-12, bounds
+        assert np.max(np.abs(lse - rlse)) < 1e-12, bounds
+
+
+def pin_prefill_uniform_closed_form():
+    """q = 0 gives the bid 1/(i+1) to every visible key.  A chunk at positions
+    P.. starting from demand Din then has committed_ij = Din_j + H_i -
+    H_max(P, j) (H_n the n-th harmonic number), so share_ij =
+    (1/(i+1)) / (Din_j + H_i - H_max(P,j) + 1/(i+1) + eps); the carried
+    demand leaves as Din_j + H_T - H_max(P, j)."""
+    rng = _rng(31)
+    d = 8
+    for T, P, eps in ((40, 13, 1e-6), (64, 0, 0.0), (33, 32, 0.2)):
+        Tq = T - P
+        q = np.zeros((1, 1, Tq, d))
+        kc = rng.standard_normal((1, 1, T, d))
+        vc = rng.standard_normal((1, 1, T, d))
+        Din = rng.random(T) * 3.0
+        D = Din[None, None].copy()
+        out, _ = oracle.prefill(q, kc, vc, T, 1.0, eps, 1, D)
+        Hn = _harmonic(T + 1)
+        ref = np.empty((Tq, d))
+        for i in range(P, T):
+            j = np.arange(i + 1)
+            share = (1.0 / (i + 1)) / (Din[j] + Hn[i] - Hn[np.maximum(P, j)] + 1.0 / (i + 1) + eps)
+            ref[i - P] = share @ vc[0, 0, : i + 1] / share.sum()
+        assert np.max(np.abs(out[0, 0] - ref)) < 1e-11, (T, P, eps)
+        assert np.max(np.abs(D[0, 0] - (Din + Hn[T] - Hn[np.maximum(P, np.arange(T))]))) < 1e-11
+
+
+def pin_prefill_single_row_is_decode_step():
+    """A one-row chunk is one cached-decode step over the keys so far: the same
+    output and the same demand update (the decode step is separate code)."""
+    rng = _rng(32)
+    S, H, L, d = 2, 2, 50, 16
+    kc, vc = rng.standard_normal((S, H, L, d)), rng.standard_normal((S, H, L, d))
+    for Tk in (1, 29, 50):
+        q = rng.standard_normal((S, H, d))
+        D0 = rng.random((S, H, L)) * 4.0
+        D1 = D0.copy()
+        D2 = D0.copy()
+        ref = oracle.dilution_decode_step(q, kc, vc, D1, 0.9, 1e-6, kv_len=[Tk] * S)
+        out, _ = oracle.prefill(q[:, :, None, :].copy(), kc, vc, Tk, 0.9, 1e-6, 1, D2)
+        assert np.max(np.abs(out[:, :, 0] - ref)) < 1e-12, Tk
+        assert np.max(np.abs(D2 - D1)) < 1e-12, Tk
+
+
 # ------------------------------------------------------------------------- decode
 
 def pin_decode_append_equals_prefill():

@@ -27,8 +27,8 @@ MUTANTS = [
     ("lse_wrong_sign", "const double l = M + log(Z);", "const double l = M - log(Z);"),
     ("diagonal_bid_not_committed", "for (int j = 0; j <= i; ++j) D[j] += p[j];",
      "for (int j = 0; j < i; ++j) D[j] += p[j];"),
-    ("shares_not_renormalised", "Oh[(size_t)i * d + e] = acc[e] / r;",
-     "Oh[(size_t)i * d + e] = acc[e];"),
+    ("shares_not_renormalised", "Oh[(size_t)li * d + e] = acc[e] / r;",
+     "Oh[(size_t)li * d + e] = acc[e];"),
     ("value_rows_reversed", "pa[e] += share * Vh[(size_t)j * d + e];",
      "pa[e] += share * Vh[(size_t)(i - j) * d + e];"),
     ("value_rows_reversed_serial",
@@ -43,6 +43,15 @@ MUTANTS = [
      "for (int j = 0; j < L; ++j) Dh[j] += p[j] / (Dh[j] + p[j] + eps);"),
     ("bf16_widening_shift", "<< 16;", "<< 15;"),
     ("yarn_coefficient", "return 0.1 * log(s) + 1.0;", "return 0.1 * log2(s) + 1.0;"),
+    ("prefill_demand_in_ignored",
+     "if (demand) memcpy(D, demand + (size_t)bh * Lcap, sizeof(double) * (size_t)Tk);", ""),
+    ("prefill_keys_from_chunk_start",
+     "causal_bids(Qh + (size_t)li * d, Kh, i, d, c, p, inner_parallel)",
+     "causal_bids(Qh + (size_t)li * d, Kh, li, d, c, p, inner_parallel)"),
+    ("prefill_cache_stride", "kbase = (size_t)bh * Lcap * d", "kbase = (size_t)bh * Tk * d"),
+    ("prefill_tempered_keys_from_chunk_start",
+     "causal_bids(Qh + (size_t)(i - P) * d, Kh, i, d, c, p, 0)",
+     "causal_bids(Qh + (size_t)(i - P) * d, Kh, i - P, d, c, p, 0)"),
     ("bwd_suffix_exclusive",
      "          col[j] += dPi[j] * Pi[j] / (Di[j] * Di[j]);\n          dPi[j] = dPi[j] / Di[j] - col[j];",
      "          dPi[j] = dPi[j] / Di[j] - col[j];\n          col[j] += dPi[j] * Pi[j] / (Di[j] * Di[j]);"),
