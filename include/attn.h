@@ -64,15 +64,15 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
 /* Bytes of device workspace attn_fwd needs for this shape (0 for
  * ATTN_TEMPERED).  Dilution keeps the fp32 log-sum-exp of every query row
  * (B*H*T floats) and the demand committed before every 32-row query block on
- * each earlier key (B*H*16*n*(n-1) floats, n = ceil(T/32)).  Returns 0 for an
- * invalid shape. */
+ * each key up to the block's end (B*H*16*n*(n+1) floats, n = ceil(T/32)).
+ * Returns 0 for an invalid shape. */
 size_t attn_fwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype);
 
 /* Causal attention forward pass (both modes; see top of file).
  *   q, k, v    [B,H,T,d] device arrays of `dtype` (inputs, not modified)
  *   out        [B,H,T,d] device array of `dtype` (output; may not alias q/k/v)
- *   B, H, T    batch, heads, sequence length (each >= 1; T <= 16777216, the
- *              kernels address one head's rows with 32-bit byte offsets)
+ *   B, H, T    batch, heads, sequence length (each >= 1; T < 16777216, the
+ *              kernels address one head's rows with byte offsets below 2^31)
  *   d          head dimension; only 64 is supported (else ATTN_ENOTSUP)
  *   tau        logit multiplier, finite and >= 0 (tau = 0 gives uniform bids)
  *   mode       ATTN_TEMPERED or ATTN_DILUTION
@@ -102,7 +102,7 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, int B, i
 
 /* Bytes of device workspace attn_bwd needs: four fp32 values per query row,
  * and for dilution the committed demand and the later rows' gradient sums
- * per (32-row query block, key): B*H*16*n*(n-1) and B*H*16*n*(n+1) floats,
+ * per (32-row query block, key): B*H*16*n*(n+1) floats each,
  * n = ceil(T/32), plus a bf16 [B,H,T,d] array.  0 for an unsupported shape,
  * mode or dtype (bf16 only). */
 size_t attn_bwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype);
@@ -156,6 +156,43 @@ int attn_dilution_committed(const void *q, const void *k, int B, int H, int T, i
 int attn_dilution_shares(const void *q, const void *k, const void *v, void *out, int B, int H,
                          int T, int d, float tau, float eps, int dtype, void *workspace,
                          size_t workspace_bytes, void *hip_stream);
+
+/* Bytes of device workspace attn_prefill needs for Tq query rows over Tk keys
+ * (0 for ATTN_TEMPERED, or for an invalid shape): the fp32 log-sum-exp of
+ * each query row and the committed demand of each 32-row query block from
+ * position P = Tk - Tq rounded down to 128 onwards. */
+size_t attn_prefill_workspace_bytes(int B, int H, int Tq, int Tk, int d, int mode, int dtype);
+
+/* One chunk of a prefill over cached keys, either operator: the Tq new query
+ * rows are the positions P = Tk-Tq .. Tk-1, and the row at position i sees
+ * keys 0..i.  Dilution continues from the demand the rows before P committed
+ * (DilutionAttention v0.1.0: cached decoding keeps one running demand total
+ * per key and head; "The operator" then runs unchanged with committed_ij =
+ * demand_in_j + the bids of this chunk's rows above i).  A whole prefill is
+ * Tq = Tk with no demand; a one-row chunk is one decode step with the new
+ * key visible.
+ *   q          [B,H,Tq,d] of `dtype`: the chunk's queries
+ *   kcache, vcache  [B,H,Lcap,d] of `dtype`: keys/values 0..Tk-1 (the caller
+ *              has written the chunk's own keys/values at P..Tk-1); rows
+ *              Tk..Lcap-1 are not read
+ *   out        [B,H,Tq,d] of `dtype` (may not alias q or the caches)
+ *   B, H       >= 1;  1 <= Tq <= Tk <= Lcap < 16777216
+ *   d, tau, mode, eps, dtype  as for attn_fwd
+ *   demand_in  [B,H,Lcap] fp32 (dilution): each key's demand from the rows
+ *              before P (the new keys' entries are normally 0), or NULL for
+ *              none; entries >= Tk are not read
+ *   demand_out [B,H,Lcap] fp32 (dilution), optional: demand_in + the column
+ *              totals of this chunk's bids on keys < Tk (entries >= Tk are
+ *              not written).  May be demand_in itself (updated in place);
+ *              otherwise no overlap with it.
+ *   lse_out    [B,H,Tq] fp32, optional: natural-log log-sum-exp per row
+ *   workspace  >= attn_prefill_workspace_bytes(B,H,Tq,Tk,d,mode,dtype) bytes
+ * demand_in and demand_out must be NULL for ATTN_TEMPERED (else ATTN_EINVAL).
+ * Outputs may not alias each other or any tensor argument. */
+int attn_prefill(const void *q, const void *kcache, const void *vcache, void *out, int B, int H,
+                 int Tq, int Tk, int Lcap, int d, float tau, int mode, float eps, int dtype,
+                 const float *demand_in, float *demand_out, float *lse_out, void *workspace,
+                 size_t workspace_bytes, void *hip_stream);
 
 /* Bytes of device workspace attn_decode needs (per-(sequence,head,split)
  * partial maxima, sums and weighted values plus one fp32 score per cached

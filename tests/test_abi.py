@@ -80,6 +80,9 @@ def fwd(**kw):
     (dict(mode=1, lse_out=FAKE + 0x4000000, rowsum_out=FAKE + 0x4000010,
           workspace=FAKE + 0x5000000, workspace_bytes=1 << 30), ab.ATTN_EINVAL),  # outputs overlap
     (dict(d=128), ab.ATTN_ENOTSUP),
+    (dict(T=1 << 24), ab.ATTN_EINVAL),               # one head's rows need offsets >= 2^31
+    (dict(mode=1, T=(1 << 24) - 1, k=FAKE + (1 << 32), v=FAKE + (2 << 32),
+          out=FAKE + (3 << 32)), ab.ATTN_EWORKSPACE),   # largest T passes the shape check
     (dict(mode=1), ab.ATTN_EWORKSPACE),              # dilution without workspace
     (dict(mode=1, workspace=FAKE + 0x5000000, workspace_bytes=16), ab.ATTN_EWORKSPACE),
 ])
@@ -91,7 +94,7 @@ def test_workspace_sizes():
     # tempered needs none; dilution keeps lse (B*H*T) + committed demand
     assert ab.attn_fwd_workspace_bytes(1, 16, 16384, 64, 0, 1) == 0
     n = 16384 // 32
-    want = 16 * 16384 * 4 + 16 * 16 * n * (n - 1) * 4
+    want = 16 * 16384 * 4 + 16 * 16 * n * (n + 1) * 4
     got = ab.attn_fwd_workspace_bytes(1, 16, 16384, 64, 1, 1)
     assert want <= got <= want + 512
     assert ab.attn_fwd_workspace_bytes(1, 1, 16, 128, 1, 1) == 0
@@ -103,12 +106,65 @@ def test_workspace_sizes():
 def test_bwd_workspace_sizes():
     n = 16384 // 32
     rows = 16 * 16384 * 4
-    want = 4 * rows + 16 * 16 * n * (n - 1) * 4 + 16 * 16 * n * (n + 1) * 4 + 16 * 16384 * 64 * 2
+    want = 4 * rows + 2 * 16 * 16 * n * (n + 1) * 4 + 16 * 16384 * 64 * 2
     got = ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 1)
     assert want <= got <= want + 7 * 256
     assert 4 * rows <= ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 0, 1) <= 4 * rows + 4 * 256
     assert ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 0) == 0   # fp32: not supported
     assert ab.attn_bwd_workspace_bytes(1, 16, 16384, 128, 1, 1) == 0
+
+
+def test_prefill_workspace_sizes():
+    # a whole prefill needs what attn_fwd needs
+    for T in (1, 100, 16384):
+        assert (ab.attn_prefill_workspace_bytes(2, 3, T, T, 64, 1, 1)
+                == ab.attn_fwd_workspace_bytes(2, 3, T, 64, 1, 1))
+    # a 2048-row chunk after 30000 cached keys: blocks from position 29952
+    Tq, Tk = 2048, 32048
+    n, b0 = (Tk + 31) // 32, 29952 // 32
+    want = 16 * Tq * 4 + 16 * 16 * (n * (n + 1) - b0 * (b0 + 1)) * 4
+    got = ab.attn_prefill_workspace_bytes(1, 16, Tq, Tk, 64, 1, 1)
+    assert want <= got <= want + 512
+    assert ab.attn_prefill_workspace_bytes(1, 16, Tq, Tk, 64, 0, 1) == 0   # tempered
+    assert ab.attn_prefill_workspace_bytes(1, 16, 10, 9, 64, 1, 1) == 0    # Tq > Tk
+    assert ab.attn_prefill_workspace_bytes(1, 16, 0, 9, 64, 1, 1) == 0
+    assert ab.attn_prefill_workspace_bytes(1, 16, 8, 9, 128, 1, 1) == 0
+
+
+def pre(**kw):
+    args = dict(q=FAKE, kcache=FAKE + 0x1000000, vcache=FAKE + 0x2000000, out=FAKE + 0x3000000,
+                B=1, H=2, Tq=16, Tk=40, Lcap=64, d=64, tau=1.0, mode=1, eps=1e-6, dtype=1,
+                demand_in=FAKE + 0x4000000, demand_out=FAKE + 0x4000000, lse_out=None,
+                workspace=None, workspace_bytes=0, hip_stream=None)
+    args.update(kw)
+    return ab.attn_prefill(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ab.ATTN_EINVAL),
+    (dict(vcache=None), ab.ATTN_EINVAL),
+    (dict(out=FAKE + 0x3000004), ab.ATTN_EINVAL),       # misaligned
+    (dict(demand_in=FAKE + 0x4000008), ab.ATTN_EINVAL),
+    (dict(Tq=0), ab.ATTN_EINVAL),
+    (dict(Tq=41), ab.ATTN_EINVAL),                      # more rows than keys
+    (dict(Lcap=39), ab.ATTN_EINVAL),                    # keys beyond the cache
+    (dict(Lcap=1 << 24), ab.ATTN_EINVAL),
+    (dict(mode=0), ab.ATTN_EINVAL),                     # demand arrays in tempered mode
+    (dict(mode=2), ab.ATTN_EINVAL),
+    (dict(tau=float("nan")), ab.ATTN_EINVAL),
+    (dict(eps=-1.0), ab.ATTN_EINVAL),
+    (dict(out=FAKE + 0x1000000 + 64 * 64 * 2), ab.ATTN_EINVAL),    # out inside the K cache
+    (dict(demand_out=FAKE + 0x4000010), ab.ATTN_EINVAL),   # partial overlap with demand_in
+    (dict(lse_out=FAKE + 0x4000000 + 256), ab.ATTN_EINVAL),  # lse inside the demand
+    (dict(lse_out=FAKE), ab.ATTN_EINVAL),               # lse aliases q
+    (dict(demand_out=FAKE + 0x2000000), ab.ATTN_EINVAL),   # demand inside the V cache
+    (dict(d=128), ab.ATTN_ENOTSUP),
+    (dict(), ab.ATTN_EWORKSPACE),                       # in-place demand is accepted
+    (dict(demand_in=None, demand_out=None), ab.ATTN_EWORKSPACE),
+    (dict(workspace=FAKE + 0x5000000, workspace_bytes=64), ab.ATTN_EWORKSPACE),
+])
+def test_prefill_rejects_bad_arguments(kw, status):
+    assert pre(**kw) == status
 
 
 def bwd(**kw):

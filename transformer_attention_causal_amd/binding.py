@@ -1,9 +1,9 @@
 """Thin Python binding of libattn.so (argument marshalling only).
 
 The functions named like the C ABI (``attn_fwd``, ``attn_fwd_ex``, ``attn_bwd``,
-``attn_decode``, the ``*_workspace_bytes`` queries, ``attn_yarn_tau``,
+``attn_prefill``, ``attn_decode``, the ``*_workspace_bytes`` queries, ``attn_yarn_tau``,
 ``attn_strerror``) take exactly the C arguments, with device pointers as Python
-ints.  ``fwd``, ``bwd`` and ``decode`` accept torch tensors, check
+ints.  ``fwd``, ``bwd``, ``prefill`` and ``decode`` accept torch tensors, check
 their shapes/dtypes, allocate the output and workspace with torch, pass the
 current torch stream, and raise ``AttnError`` on a non-zero status.  Every step
 of the computation runs in the library's HIP kernels; nothing here computes.
@@ -25,7 +25,8 @@ ATTN_F32, ATTN_BF16 = 0, 1
 
 EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_bytes", "attn_dilution_lse",
             "attn_dilution_committed", "attn_dilution_shares", "attn_bwd",
-            "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_workspace_bytes",
+            "attn_bwd_workspace_bytes", "attn_prefill", "attn_prefill_workspace_bytes",
+            "attn_decode", "attn_decode_workspace_bytes",
             "attn_yarn_tau", "attn_strerror")
 
 
@@ -58,6 +59,11 @@ def load() -> ctypes.CDLL:
                                  vp, sz, vp]
         lib.attn_bwd_workspace_bytes.restype = sz
         lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        lib.attn_prefill.restype = i
+        lib.attn_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, f, i, vp, vp, vp,
+                                     vp, sz, vp]
+        lib.attn_prefill_workspace_bytes.restype = sz
+        lib.attn_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
         lib.attn_dilution_lse.restype = i
         lib.attn_dilution_lse.argtypes = [vp, vp, i, i, i, i, f, i, vp, sz, vp, vp]
         lib.attn_dilution_committed.restype = i
@@ -100,6 +106,17 @@ def attn_bwd(q, k, v, out, dout, lse, rowsum, dq, dk, dv, B, H, T, d, tau, mode,
 
 def attn_bwd_workspace_bytes(B, H, T, d, mode, dtype) -> int:
     return int(load().attn_bwd_workspace_bytes(B, H, T, d, mode, dtype))
+
+
+def attn_prefill(q, kcache, vcache, out, B, H, Tq, Tk, Lcap, d, tau, mode, eps, dtype,
+                 demand_in, demand_out, lse_out, workspace, workspace_bytes, hip_stream) -> int:
+    return load().attn_prefill(q, kcache, vcache, out, B, H, Tq, Tk, Lcap, d, tau, mode, eps,
+                               dtype, demand_in, demand_out, lse_out, workspace, workspace_bytes,
+                               hip_stream)
+
+
+def attn_prefill_workspace_bytes(B, H, Tq, Tk, d, mode, dtype) -> int:
+    return int(load().attn_prefill_workspace_bytes(B, H, Tq, Tk, d, mode, dtype))
 
 
 def attn_dilution_lse(q, k, B, H, T, d, tau, dtype, workspace, workspace_bytes, lse_out,
@@ -233,6 +250,49 @@ def bwd(q, k, v, out, dout, lse, rowsum=None, tau: float = 1.0, mode: int = ATTN
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd")
     return dq, dk, dv
+
+
+def prefill(q, kcache, vcache, Tk: int, tau: float = 1.0, mode: int = ATTN_DILUTION,
+            eps: float = 1e-6, demand_in=None, demand_out=None, lse_out=None, out=None,
+            workspace=None):
+    """Run attn_prefill: q [B,H,Tq,64] holds the rows at positions Tk-Tq..Tk-1,
+    the caches [B,H,Lcap,64] keys/values 0..Tk-1; ``demand_in``/``demand_out``
+    are [B,H,Lcap] fp32 (may be one tensor: updated in place).  Returns ``out``."""
+    import torch
+
+    if q.dim() != 4 or kcache.dim() != 4 or vcache.shape != kcache.shape:
+        raise ValueError("q must be [B,H,Tq,d] and the caches one [B,H,Lcap,d] shape")
+    B, H, Tq, d = q.shape
+    Lcap = kcache.shape[2]
+    if kcache.shape[:2] != (B, H) or kcache.shape[3] != d:
+        raise ValueError("q and the caches disagree on B, H or d")
+    for t in (q, kcache, vcache):
+        if not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("q and the caches must be contiguous and share one dtype")
+    for t in (demand_in, demand_out):
+        if t is not None and (t.shape != (B, H, Lcap) or t.dtype != torch.float32
+                              or not t.is_contiguous()):
+            raise ValueError("demand arrays must be contiguous float32 [B,H,Lcap]")
+    code = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    ws_bytes = 0
+    if workspace is None:
+        n = attn_prefill_workspace_bytes(B, H, Tq, int(Tk), d, mode, code)
+        if n:
+            workspace, ws_bytes = torch.empty(n, dtype=torch.uint8, device=q.device), n
+    else:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = attn_prefill(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), out.data_ptr(), B, H,
+                      Tq, int(Tk), Lcap, d, float(tau), int(mode), float(eps), code,
+                      demand_in.data_ptr() if demand_in is not None else None,
+                      demand_out.data_ptr() if demand_out is not None else None,
+                      lse_out.data_ptr() if lse_out is not None else None,
+                      workspace.data_ptr() if workspace is not None else None, ws_bytes,
+                      _stream_handle(q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_prefill")
+    return out
 
 
 def dilution_stages(q, k, v, tau: float = 1.0, eps: float = 1e-6, out=None, workspace=None,

@@ -54,19 +54,23 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 
 size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace layout of a dilution forward: [lse2: BH*T][committed demand].
+// Workspace layout of a dilution forward over keys 0..Tk-1 with Tq query rows
+// (Tq = Tk for a whole prefill): [lse2: BH*Tq][committed demand].
 struct FwdWorkspace {
   size_t lse_bytes, cin_bytes, total;
 };
 
-bool fwd_workspace(int B, int H, int T, FwdWorkspace *ws) {
+bool prefill_workspace(int B, int H, int Tq, int Tk, FwdWorkspace *ws) {
   const size_t BH = (size_t)B * H;
   if (BH > (size_t)INT32_MAX) return false;
-  ws->lse_bytes = round_up(BH * (size_t)T * sizeof(float));
-  ws->cin_bytes = round_up(BH * attn::cin_floats_per_head(T) * sizeof(float));
+  const int vrow0 = attn::first_block_row(Tk, Tq);
+  ws->lse_bytes = round_up(BH * (size_t)Tq * sizeof(float));
+  ws->cin_bytes = round_up(BH * attn::cin_floats_per_head(Tk, vrow0) * sizeof(float));
   ws->total = ws->lse_bytes + ws->cin_bytes;
   return true;
 }
+
+bool fwd_workspace(int B, int H, int T, FwdWorkspace *ws) { return prefill_workspace(B, H, T, T, ws); }
 
 // Decode: chunk of keys per workgroup.
 constexpr int kDecChunk = 2048;
@@ -90,8 +94,8 @@ bool dec_workspace(int S, int H, int Lcap, DecWorkspace *ws) {
 
 bool shape_ok(int B, int H, int T) {
   if (B <= 0 || H <= 0 || T <= 0) return false;
-  // one head's rows are addressed with 32-bit byte offsets (buffer loads)
-  if (T > (1 << 24)) return false;
+  // one head's rows are addressed with byte offsets below 2^31 (buffer loads)
+  if (T >= (1 << 24)) return false;
   // element counts must fit the kernels' 64-bit offsets and 32-bit grids
   const size_t BH = (size_t)B * H;
   if (BH > (size_t)INT32_MAX / 1024) return false;
@@ -165,7 +169,8 @@ attn::FwdArgs make_args(const void *q, const void *k, const void *v, void *out, 
   a.v = v;
   a.out = out;
   a.BH = B * H;
-  a.T = T;
+  a.T = a.Tq = a.kstride = T;
+  a.vrow0 = 0;
   // logits are tau <q,k> / sqrt(d); the kernels work in base 2
   a.c2 = (float)((double)tau / std::sqrt((double)d) * 1.4426950408889634);
   a.eps = eps;
@@ -276,6 +281,82 @@ int attn_fwd(const void *q, const void *k, const void *v, void *out, int B, int 
                      nullptr, nullptr, nullptr, hip_stream);
 }
 
+size_t attn_prefill_workspace_bytes(int B, int H, int Tq, int Tk, int d, int mode, int dtype) {
+  if (!shape_ok(B, H, Tk) || Tq < 1 || Tq > Tk || d != attn::kHeadDim) return 0;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
+  if (mode != ATTN_DILUTION) return 0;
+  FwdWorkspace ws;
+  if (!prefill_workspace(B, H, Tq, Tk, &ws)) return 0;
+  return ws.total;
+}
+
+int attn_prefill(const void *q, const void *kcache, const void *vcache, void *out, int B, int H,
+                 int Tq, int Tk, int Lcap, int d, float tau, int mode, float eps, int dtype,
+                 const float *demand_in, float *demand_out, float *lse_out, void *workspace,
+                 size_t workspace_bytes, void *hip_stream) {
+  if (!q || !kcache || !vcache || !out) return ATTN_EINVAL;
+  if (mode != ATTN_TEMPERED && mode != ATTN_DILUTION) return ATTN_EINVAL;
+  if (mode == ATTN_TEMPERED && (demand_in || demand_out)) return ATTN_EINVAL;
+  if (!shape_ok(B, H, Lcap) || Tq < 1 || Tk < Tq || Lcap < Tk) return ATTN_EINVAL;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EINVAL;
+  if (!std::isfinite(tau) || tau < 0.0f) return ATTN_EINVAL;
+  if (!std::isfinite(eps) || eps < 0.0f) return ATTN_EINVAL;
+  if (d != attn::kHeadDim) return ATTN_ENOTSUP;
+  const void *ptrs[7] = {q, kcache, vcache, out, demand_in, demand_out, lse_out};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return ATTN_EINVAL;
+  const size_t BH = (size_t)B * H, esz = dtype == ATTN_BF16 ? 2 : 4;
+  const size_t qbytes = BH * Tq * d * esz, cbytes = BH * (size_t)Lcap * d * esz;
+  const size_t rbytes = BH * Tq * sizeof(float), dbytes = BH * (size_t)Lcap * sizeof(float);
+  if (overlaps(out, qbytes, q, qbytes) || overlaps(out, qbytes, kcache, cbytes) ||
+      overlaps(out, qbytes, vcache, cbytes))
+    return ATTN_EINVAL;
+  // every fp32 output is disjoint from the tensors and the other outputs;
+  // demand_out may be demand_in itself (an in-place update) but no partial overlap
+  auto hits_tensor = [&](const void *p, size_t n) {
+    return overlaps(p, n, q, qbytes) || overlaps(p, n, kcache, cbytes) ||
+           overlaps(p, n, vcache, cbytes) || overlaps(p, n, out, qbytes);
+  };
+  if (lse_out && hits_tensor(lse_out, rbytes)) return ATTN_EINVAL;
+  if (demand_out && hits_tensor(demand_out, dbytes)) return ATTN_EINVAL;
+  if (lse_out && demand_out && overlaps(lse_out, rbytes, demand_out, dbytes)) return ATTN_EINVAL;
+  if (demand_in && lse_out && overlaps(demand_in, dbytes, lse_out, rbytes)) return ATTN_EINVAL;
+  if (demand_in && overlaps(demand_in, dbytes, out, qbytes)) return ATTN_EINVAL;
+  if (demand_in && demand_out && demand_in != demand_out &&
+      overlaps(demand_in, dbytes, demand_out, dbytes))
+    return ATTN_EINVAL;
+  FwdWorkspace ws{};
+  if (mode == ATTN_DILUTION) {
+    if (!prefill_workspace(B, H, Tq, Tk, &ws)) return ATTN_EINVAL;
+    if (!workspace || workspace_bytes < ws.total || !aligned16(workspace)) return ATTN_EWORKSPACE;
+  }
+  int st = check_device();
+  if (st != ATTN_OK) return st;
+  attn::FwdArgs a = make_args(q, kcache, vcache, out, B, H, Tk, d, tau, eps,
+                              mode == ATTN_DILUTION ? workspace : nullptr, ws);
+  a.Tq = Tq;
+  a.kstride = Lcap;
+  a.vrow0 = attn::first_block_row(Tk, Tq);
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  const bool bf16 = dtype == ATTN_BF16;
+  a.lse_nat = lse_out;
+  if (mode == ATTN_TEMPERED)
+    return finish(bf16 ? attn::launch_rows_bf16(attn::kRowTempered, a, s)
+                       : attn::launch_rows_f32(attn::kRowTempered, a, s));
+  hipError_t e = bf16 ? attn::launch_rows_bf16(attn::kRowLse, a, s)
+                      : attn::launch_rows_f32(attn::kRowLse, a, s);
+  if (e != hipSuccess) return fail_hip(e);
+  a.lse_nat = nullptr;
+  a.demand_in = demand_in;
+  a.demand_out = demand_out;
+  e = bf16 ? attn::launch_colsum_bf16(a, s) : attn::launch_colsum_f32(a, s);
+  if (e != hipSuccess) return fail_hip(e);
+  a.demand_in = nullptr;
+  a.demand_out = nullptr;
+  return finish(bf16 ? attn::launch_rows_bf16(attn::kRowShare, a, s)
+                     : attn::launch_rows_f32(attn::kRowShare, a, s));
+}
+
 }  // extern "C"
 
 namespace {
@@ -292,7 +373,7 @@ bool bwd_workspace(int B, int H, int T, int mode, BwdWorkspace *ws) {
   const size_t BH = (size_t)B * H;
   if (BH > (size_t)INT32_MAX) return false;
   ws->row_bytes = round_up(BH * (size_t)T * sizeof(float));
-  ws->cin_bytes = mode == ATTN_DILUTION ? round_up(BH * attn::cin_floats_per_head(T) * 4) : 0;
+  ws->cin_bytes = mode == ATTN_DILUTION ? round_up(BH * attn::cin_floats_per_head(T, 0) * 4) : 0;
   ws->gin_bytes = mode == ATTN_DILUTION ? round_up(BH * attn::gin_floats_per_head(T) * 4) : 0;
   ws->pk_bytes = mode == ATTN_DILUTION ? round_up(BH * (size_t)T * attn::kHeadDim * 2) : 0;
   ws->total = 4 * ws->row_bytes + ws->cin_bytes + ws->gin_bytes + ws->pk_bytes;

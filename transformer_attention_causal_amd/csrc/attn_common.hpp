@@ -131,6 +131,10 @@ __device__ __forceinline__ float both_halves_sum(float x) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
 }
+// A byte offset past every range make_rsrc is given (those stay below 2^31
+// bytes): a load there returns zeros, the usual way to mask single lanes of a
+// buffer load.
+constexpr uint32_t kNoOffset = 0x80000000u;
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0);
 }

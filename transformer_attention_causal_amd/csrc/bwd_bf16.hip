@@ -210,7 +210,7 @@ __global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdArgs a, int nqs) {
   const float *L2 = a.lse2 + (size_t)bh * T;
   const float *IR = a.invr + (size_t)bh * T;
   const float *DR = a.dri + (size_t)bh * T;
-  const uint32_t *cin = reinterpret_cast<const uint32_t *>(a.cin) + (size_t)bh * cin_floats_per_head(T);
+  const uint32_t *cin = reinterpret_cast<const uint32_t *>(a.cin) + (size_t)bh * cin_floats_per_head(T, 0);
   uint32_t *gin = reinterpret_cast<uint32_t *>(a.gin) + (size_t)bh * gin_floats_per_head(T);
   const uint32_t eps_word = split2_bf16(fmaxf(a.eps, FLT_MIN));
 
@@ -260,7 +260,7 @@ __global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdArgs a, int nqs) {
     if (wave_live && 32 * qs + 31 >= kw0) {
       f32x16 s, da;
       col_scores(sb[buf], kf, vf, l32, h, s, da);
-      const uint32_t cw = key < 32 * qs ? cin[(size_t)16 * qs * (qs - 1) + key] : eps_word;
+      const uint32_t cw = key < 32 * qs ? cin[cin_block_offset(qs, 0) + key] : eps_word;
       ColTerms t;
       if (32 * qs == kw0) col_terms<true>(s, da, sb[buf], sc, cw, a.c2, l32, h, t);
       else col_terms<false>(s, da, sb[buf], sc, cw, a.c2, l32, h, t);
@@ -377,7 +377,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nqs) {
   const float *RH = a.rho + (size_t)bh * T;
   const uint32_t *cin = nullptr, *gin = nullptr;
   if constexpr (DIL) {
-    cin = reinterpret_cast<const uint32_t *>(a.cin) + (size_t)bh * cin_floats_per_head(T);
+    cin = reinterpret_cast<const uint32_t *>(a.cin) + (size_t)bh * cin_floats_per_head(T, 0);
     gin = reinterpret_cast<const uint32_t *>(a.gin) + (size_t)bh * gin_floats_per_head(T);
   }
   const uint32_t eps_word = split2_bf16(fmaxf(a.eps, FLT_MIN));
@@ -441,7 +441,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nqs) {
     if (wave_live && 32 * qs + 31 >= kw0) {
       uint32_t cw = 0u, gw = 0u;
       if constexpr (DIL) {
-        cw = key < 32 * qs ? cin[(size_t)16 * qs * (qs - 1) + key] : eps_word;
+        cw = key < 32 * qs ? cin[cin_block_offset(qs, 0) + key] : eps_word;
         gw = (key < 32 * (qs + 1) && key < T) ? gin[(size_t)16 * qs * (qs + 1) + key] : 0u;
       }
       if (32 * qs == kw0)
@@ -622,8 +622,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
   const uint32_t *cin_blk = nullptr, *gin_blk = nullptr;
   const int qsb = qw0 >> 5;   // this wave's 32-row block
   if constexpr (DIL) {
-    cin_blk = reinterpret_cast<const uint32_t *>(a.cin) + (size_t)bh * cin_floats_per_head(T) +
-              (size_t)16 * qsb * (qsb - 1);
+    cin_blk = reinterpret_cast<const uint32_t *>(a.cin) + (size_t)bh * cin_floats_per_head(T, 0) +
+              cin_block_offset(qsb, 0);
     gin_blk = reinterpret_cast<const uint32_t *>(a.gin) + (size_t)bh * gin_floats_per_head(T) +
               (size_t)16 * qsb * (qsb + 1);
   }
@@ -758,7 +758,7 @@ hipError_t launch_bwd_bf16(int mode, const BwdArgs &a, hipStream_t s) {
     f.lse2 = a.lse2;
     f.cin = a.cin;
     f.BH = a.BH;
-    f.T = a.T;
+    f.T = f.Tq = f.kstride = a.T;
     f.c2 = a.c2;
     f.eps = a.eps;
     e = launch_colsum_bf16(f, s);
@@ -773,7 +773,7 @@ hipError_t launch_bwd_bf16(int mode, const BwdArgs &a, hipStream_t s) {
     t.v = a.k;
     t.out = a.pk;
     t.BH = a.BH;
-    t.T = a.T;
+    t.T = t.Tq = t.kstride = a.T;
     t.c2 = a.c2;
     e = launch_rows_bf16(kRowTempered, t, s);
     if (e != hipSuccess) return e;

@@ -311,17 +311,21 @@ __global__ void __launch_bounds__(256, RowOccupancy<MODE>::value) rows_bf16_kern
   // heaviest query blocks first; consecutive workgroups take different heads.
   // Workgroups go to the 8 XCDs round-robin, so with B*H a multiple of 8 each
   // XCD serves the same B*H/8 heads throughout and keeps their K/V in its L2.
+  // Rows are positions: query row r of Q is position P + r, and keys are
+  // indexed from 0.  A whole prefill has P = 0; a later chunk starts at P > 0
+  // and the blocks cover positions from vrow0 = P rounded down to kBM, the
+  // positions before P standing for no row (no loads, no stores, no bids).
   const int bh = blockIdx.x % a.BH;
-  const int qb = nqb - 1 - blockIdx.x / a.BH;
-  const int T = a.T;
+  const int qb = a.vrow0 / kBM + nqb - 1 - blockIdx.x / a.BH;
+  const int T = a.T, Tq = a.Tq, P = T - Tq;
   const int q0 = qb * kBM;
-  const int qw0 = q0 + 32 * w;              // first row of this wave
-  const bool wave_live = qw0 < T;
+  const int qw0 = q0 + 32 * w;              // first position of this wave
+  const bool wave_live = qw0 < T && qw0 + 32 > P;
   const int kd = qw0 / kBN;                 // the tile holding this wave's diagonal
-  const size_t head = (size_t)bh * T * kHeadDim;
-  const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + head;
-  const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + head;
-  const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + head;
+  const size_t qhead = (size_t)bh * Tq * kHeadDim, khead = (size_t)bh * a.kstride * kHeadDim;
+  const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + qhead;
+  const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + khead;
+  const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + khead;
 
   const int kend = min(q0 + kBM, T);        // keys [0, kend) are visible to some row
   const int nkt = (kend + kBN - 1) / kBN;
@@ -331,7 +335,7 @@ __global__ void __launch_bounds__(256, RowOccupancy<MODE>::value) rows_bf16_kern
   bf16x8 qf[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c)
-    qf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(Q, qw0 + l32, T, 2 * c + h));
+    qf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(Q, qw0 + l32 - P, Tq, 2 * c + h));
 
   // tile loaders: K as [key][d] rows; V transposed to [d][key] on the way in.
   // Buffer loads with per-lane byte offsets fixed for the whole loop; keys
@@ -380,7 +384,7 @@ __global__ void __launch_bounds__(256, RowOccupancy<MODE>::value) rows_bf16_kern
   st.lsum = zero4();
   const bf16x8 sel = rowsum_selector(lane);
 
-  float lseq[16];      // pass 2b: lse2 of this lane's 16 query rows (kNoRow past the end)
+  float lseq[16];      // pass 2b: lse2 of this lane's 16 query rows (kNoRow for no row)
   ShareConsts sc;      // pass 2b: constant operands of the prefix and transpose
   const uint32_t *cin_blk = nullptr;
   uint32_t cin_next[2] = {0u, 0u};
@@ -389,21 +393,22 @@ __global__ void __launch_bounds__(256, RowOccupancy<MODE>::value) rows_bf16_kern
   if constexpr (MODE == kRowShare) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = qw0 + acc_row(r, h);
-      lseq[r] = row < T ? a.lse2[(size_t)bh * T + row] : kNoRow;
+      const int lr = qw0 + acc_row(r, h) - P;
+      lseq[r] = (unsigned)lr < (unsigned)Tq ? a.lse2[(size_t)bh * Tq + lr] : kNoRow;
     }
     sc = share_consts(l32, h);
-    const int qs = qw0 >> 5;
-    cin_blk = reinterpret_cast<const uint32_t *>(a.cin) + (size_t)bh * cin_floats_per_head(T) +
-              (size_t)16 * qs * (qs - 1);
+    cin_blk = reinterpret_cast<const uint32_t *>(a.cin) + (size_t)bh * cin_floats_per_head(T, a.vrow0) +
+              cin_block_offset(qw0 >> 5, a.vrow0);
   }
   // committed demand (+ eps, as a bf16 pair) of this wave's block on keys
-  // kt*64 + 32t + l32; on and past the diagonal no earlier row sees the key
+  // kt*64 + 32t + l32; past the diagonal block no row of it sees the key, and
+  // the table holds no entry for keys past the end
+  const int cin_end = min(qw0 + 32, T);
   auto load_cin = [&](int kt) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int key = kt * kBN + 32 * t + l32;
-      cin_next[t] = (wave_live && key < qw0) ? cin_blk[key] : eps_word;
+      cin_next[t] = (wave_live && key < cin_end) ? cin_blk[key] : eps_word;
     }
   };
 
@@ -446,21 +451,22 @@ __global__ void __launch_bounds__(256, RowOccupancy<MODE>::value) rows_bf16_kern
   }
 
   if (!wave_live) return;
-  const int row = qw0 + l32;
+  const int lr = qw0 + l32 - P;               // this lane's query row
+  const bool row_ok = (unsigned)lr < (unsigned)Tq;
   const float denom = FP32SUM ? both_halves_sum(st.l_run) : st.lsum[0];
   if constexpr (MODE == kRowShare) {
-    if (a.rowsum_out && h == 0 && row < T) a.rowsum_out[(size_t)bh * T + row] = denom;
+    if (a.rowsum_out && h == 0 && row_ok) a.rowsum_out[(size_t)bh * Tq + lr] = denom;
   } else {
-    if (h == 0 && row < T) {
+    if (h == 0 && row_ok) {
       const float lse2 = st.m_run + __builtin_log2f(denom);
-      if (a.lse2) a.lse2[(size_t)bh * T + row] = lse2;
-      if (a.lse_nat) a.lse_nat[(size_t)bh * T + row] = lse2 * kLn2;
+      if (a.lse2) a.lse2[(size_t)bh * Tq + lr] = lse2;
+      if (a.lse_nat) a.lse_nat[(size_t)bh * Tq + lr] = lse2 * kLn2;
     }
   }
   if constexpr (MODE != kRowLse) {
-    if (row < T) {
+    if (row_ok) {
       const float inv = 1.0f / denom;
-      __bf16 *O = reinterpret_cast<__bf16 *>(a.out) + head + (size_t)row * kHeadDim;
+      __bf16 *O = reinterpret_cast<__bf16 *>(a.out) + qhead + (size_t)lr * kHeadDim;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 8 * g + 4 * h;
@@ -502,41 +508,52 @@ __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, in
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  // Query tiles are walked by position (query row r of Q is position P + r);
+  // positions before P, from vrow0 on, are no row and bid nothing.
   const int bh = blockIdx.x % a.BH;
   const int kb = blockIdx.x / a.BH;          // longest column walks first
-  const int T = a.T;
+  const int T = a.T, Tq = a.Tq, P = T - Tq;
   const int kw0 = kb * kCB + 32 * w;          // first key of this wave
   const bool wave_live = kw0 < T;
   const int key = kw0 + l32;
-  const size_t head = (size_t)bh * T * kHeadDim;
-  const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + head;
-  const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + head;
-  const float *L2 = a.lse2 + (size_t)bh * T;
+  const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + (size_t)bh * Tq * kHeadDim;
+  const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + (size_t)bh * a.kstride * kHeadDim;
+  const float *L2 = a.lse2 + (size_t)bh * Tq;
   // committed demand + eps of each (32-row block, key), stored as a bf16 pair
-  uint32_t *cin = reinterpret_cast<uint32_t *>(a.cin) + (size_t)bh * cin_floats_per_head(T);
+  uint32_t *cin = reinterpret_cast<uint32_t *>(a.cin) + (size_t)bh * cin_floats_per_head(T, a.vrow0);
   const float eps_floor = fmaxf(a.eps, FLT_MIN);
   auto committed_word = [&](float total) { return split2_bf16(fmaxf(total + a.eps, eps_floor)); };
 
   bf16x8 kf[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) kf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(K, key, T, 2 * c + h));
+  // demand this half-lane's rows have put on `key` so far; the lower half
+  // starts from the demand committed before position P
+  float run = 0.0f;
+  if (a.demand_in && h == 0 && key < T) run = a.demand_in[(size_t)bh * a.kstride + key];
 
   __builtin_amdgcn_s_waitcnt(0);             // K fragments: see the row kernels
 
-  const int qt0 = (kb * kCB) / kCQ;          // first 64-row query tile
+  const int qt0 = max(kb * kCB, a.vrow0) / kCQ;   // first 64-row query tile
   const int nqt = (T + kCQ - 1) / kCQ;
   u32x4 qreg[2];
   float lreg = 0.0f;
   bool lvalid = false;
   auto load_q = [&](int qt) {
-    const int row0 = qt * kCQ;                         // < T for every tile loaded
-    const auto rq = make_rsrc(Q + (size_t)row0 * kHeadDim, (T - row0) * (kHeadDim * 2));
-    qreg[0] = buf_load16(rq, 16u * tid);
-    qreg[1] = buf_load16(rq, 16u * (tid + 256));
+    // rows lr0.. of Q; only a chunk's first tiles start before row 0 (lr0 < 0),
+    // and their lanes for positions before P get an offset past the range
+    const int lr0 = qt * kCQ - P, b0 = max(lr0, 0);   // b0 < Tq for every tile loaded
+    const auto rq = make_rsrc(Q + (size_t)b0 * kHeadDim, (Tq - b0) * (kHeadDim * 2));
+    const int sh = (lr0 - b0) * (kHeadDim * 2);       // <= 0
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int off = 16 * (tid + 256 * i) + sh;
+      qreg[i] = buf_load16(rq, off < 0 ? kNoOffset : (uint32_t)off);
+    }
     if (tid < kCQ) {
-      const int row = qt * kCQ + tid;
-      lvalid = row < T;
-      lreg = L2[lvalid ? row : T - 1];
+      const int lr = lr0 + tid;
+      lvalid = (unsigned)lr < (unsigned)Tq;
+      lreg = L2[lvalid ? lr : 0];
     }
   };
   auto store_q = [&](int buf) {
@@ -545,7 +562,7 @@ __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, in
       const int u = tid + 256 * i;
       *reinterpret_cast<u32x4 *>(&sQ[buf][(u >> 3) * kKRow + (u & 7) * 8]) = qreg[i];
     }
-    if (tid < kCQ) sL[buf][tid] = lvalid ? -lreg : -kNoRow;   // rows past the end bid nothing
+    if (tid < kCQ) sL[buf][tid] = lvalid ? -lreg : -kNoRow;   // no row: bids nothing
   };
 
   // Scores of the 32x32 block (rows 32 sb.. of Q buffer `buf`, this wave's
@@ -570,10 +587,9 @@ __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, in
   // demand committed before block qs (rows < 32 qs, both halves)
   auto commit = [&](int qs, float r) {
     const float total = both_halves_sum(r);
-    if (h == 0 && key < T) cin[(size_t)16 * qs * (qs - 1) + key] = committed_word(total);
+    if (h == 0 && key < T) cin[cin_block_offset(qs, a.vrow0) + key] = committed_word(total);
   };
 
-  float run = 0.0f;  // demand this half-lane's rows have put on `key` so far
   load_q(qt0);
   store_q(0);
   __syncthreads();
@@ -591,8 +607,8 @@ __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, in
         run = r1 + colsum_bids<false>(s1, l32, h);
         const float t0 = both_halves_sum(r0), t1 = both_halves_sum(r1);
         if (h == 0 && key < T) {
-          cin[(size_t)16 * qs0 * (qs0 - 1) + key] = committed_word(t0);
-          cin[(size_t)16 * (qs0 + 1) * qs0 + key] = committed_word(t1);
+          cin[cin_block_offset(qs0, a.vrow0) + key] = committed_word(t0);
+          cin[cin_block_offset(qs0 + 1, a.vrow0) + key] = committed_word(t1);
         }
       } else {
 #pragma unroll
@@ -600,7 +616,7 @@ __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, in
           const int qs = qs0 + sb;                  // 32-row block
           if (qs >= nqs || 32 * qs + 31 < kw0) continue;   // past the end, or before the keys
           const f32x16 sc = block_scores(buf, sb);
-          if (32 * qs > kw0) commit(qs, run);
+          commit(qs, run);
           run += (32 * qs == kw0) ? colsum_bids<true>(sc, l32, h) : colsum_bids<false>(sc, l32, h);
         }
       }
@@ -610,12 +626,12 @@ __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, in
   }
   if (a.demand_out && wave_live) {
     const float total = both_halves_sum(run);
-    if (h == 0 && key < T) a.demand_out[(size_t)bh * T + key] = total;
+    if (h == 0 && key < T) a.demand_out[(size_t)bh * a.kstride + key] = total;
   }
 }
 
 hipError_t launch_rows_bf16(int mode, const FwdArgs &a, hipStream_t s) {
-  const int nqb = (a.T + kBM - 1) / kBM;
+  const int nqb = (a.T + kBM - 1) / kBM - a.vrow0 / kBM;   // blocks from position vrow0
   dim3 grid((unsigned)(nqb * a.BH)), block(256);
   switch (mode) {
     case kRowTempered:

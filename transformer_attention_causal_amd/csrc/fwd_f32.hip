@@ -17,34 +17,40 @@
 namespace attn {
 
 constexpr int kFR = 64;  // rows per workgroup / tile
+constexpr float kNoRowF32 = 1e30f;  // log-sum-exp of a position that holds no row
 
 template <int MODE>
 __global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
   __shared__ __attribute__((aligned(16))) float sK[kFR * kHeadDim];
   __shared__ __attribute__((aligned(16))) float sV[MODE == kRowLse ? 4 : kFR * kHeadDim];
+  // Rows are positions: query row r of Q is position P + r (P = 0 for a
+  // whole prefill); blocks start at position vrow0 <= P, and lanes at
+  // positions before P hold no row.
   const int t = threadIdx.x;
   const int bh = blockIdx.x % a.BH;
-  const int qb = nqb - 1 - blockIdx.x / a.BH;
-  const int T = a.T;
+  const int qb = a.vrow0 / kFR + nqb - 1 - blockIdx.x / a.BH;
+  const int T = a.T, Tq = a.Tq, P = T - Tq;
   const int q0 = qb * kFR;
-  const int i = q0 + t;  // this lane's query row
-  const size_t head = (size_t)bh * T * kHeadDim;
-  const float *Q = reinterpret_cast<const float *>(a.q) + head;
-  const float *K = reinterpret_cast<const float *>(a.k) + head;
-  const float *V = reinterpret_cast<const float *>(a.v) + head;
+  const int i = q0 + t;  // this lane's position
+  const int li = i - P;  // and its query row
+  const bool live = (unsigned)li < (unsigned)Tq;
+  const size_t qhead = (size_t)bh * Tq * kHeadDim, khead = (size_t)bh * a.kstride * kHeadDim;
+  const float *Q = reinterpret_cast<const float *>(a.q) + qhead;
+  const float *K = reinterpret_cast<const float *>(a.k) + khead;
+  const float *V = reinterpret_cast<const float *>(a.v) + khead;
 
   float q[kHeadDim], acc[kHeadDim];
 #pragma unroll
   for (int e = 0; e < kHeadDim; ++e) {
-    q[e] = (i < T) ? Q[(size_t)i * kHeadDim + e] : 0.0f;
+    q[e] = live ? Q[(size_t)li * kHeadDim + e] : 0.0f;
     acc[e] = 0.0f;
   }
   float m = -INFINITY, l = 0.0f, lse2 = 0.0f;
   const int qs = i >> 5;
   const float *cin_blk = nullptr;
   if constexpr (MODE == kRowShare) {
-    lse2 = (i < T) ? a.lse2[(size_t)bh * T + i] : 0.0f;
-    cin_blk = a.cin + (size_t)bh * cin_floats_per_head(T) + (size_t)16 * qs * (qs - 1);
+    lse2 = live ? a.lse2[(size_t)bh * Tq + li] : 0.0f;
+    cin_blk = a.cin + (size_t)bh * cin_floats_per_head(T, a.vrow0) + cin_block_offset(qs, a.vrow0);
   }
   const float eps_floor = fmaxf(a.eps, FLT_MIN);
   const int kend = min(q0 + kFR, T);
@@ -63,7 +69,7 @@ __global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
       float s = 0.0f;
 #pragma unroll
       for (int e = 0; e < kHeadDim; ++e) s = __builtin_fmaf(q[e], sK[jj * kHeadDim + e], s);
-      const bool vis = (j <= i) && (i < T);
+      const bool vis = (j <= i) && live;
       if constexpr (MODE == kRowTempered || MODE == kRowLse) {
         if (vis) {
           const float x = s * a.c2;
@@ -86,7 +92,7 @@ __global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
           const float o = __shfl_up(incl, off, 32);
           if ((t & 31) >= off) incl += o;
         }
-        float base = (j < 32 * qs) ? cin_blk[j] : 0.0f;
+        float base = (j < 32 * (qs + 1)) ? cin_blk[j] : 0.0f;
         base = fmaxf(base + a.eps, eps_floor);
         const float share = p / (base + incl);
         l += share;
@@ -95,17 +101,17 @@ __global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
       }
     }
   }
-  if (i >= T) return;
+  if (!live) return;
   if constexpr (MODE == kRowTempered || MODE == kRowLse) {
     const float l2 = m + log2f(l);
-    if (a.lse2) a.lse2[(size_t)bh * T + i] = l2;
-    if (a.lse_nat) a.lse_nat[(size_t)bh * T + i] = l2 * kLn2;
+    if (a.lse2) a.lse2[(size_t)bh * Tq + li] = l2;
+    if (a.lse_nat) a.lse_nat[(size_t)bh * Tq + li] = l2 * kLn2;
   }
   if constexpr (MODE == kRowShare) {
-    if (a.rowsum_out) a.rowsum_out[(size_t)bh * T + i] = l;
+    if (a.rowsum_out) a.rowsum_out[(size_t)bh * Tq + li] = l;
   }
   if constexpr (MODE != kRowLse) {
-    float *O = reinterpret_cast<float *>(a.out) + head + (size_t)i * kHeadDim;
+    float *O = reinterpret_cast<float *>(a.out) + qhead + (size_t)li * kHeadDim;
     const float inv = 1.0f / l;
 #pragma unroll
     for (int e = 0; e < kHeadDim; ++e) O[e] = acc[e] * inv;
@@ -115,45 +121,47 @@ __global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
 __global__ void __launch_bounds__(64) colsum_f32_kernel(FwdArgs a, int nkb) {
   __shared__ __attribute__((aligned(16))) float sQ[kFR * kHeadDim];
   __shared__ float sL[kFR];
+  // Positions i of the walk are query row i - P (P = 0 for a whole prefill);
+  // positions before P, from vrow0 on, are no row and bid nothing.
   const int t = threadIdx.x;
   const int bh = blockIdx.x % a.BH;
   const int kb = blockIdx.x / a.BH;
-  const int T = a.T;
+  const int T = a.T, Tq = a.Tq, P = T - Tq;
   const int k0 = kb * kFR;
   const int j = k0 + t;  // this lane's key column
-  const size_t head = (size_t)bh * T * kHeadDim;
-  const float *Q = reinterpret_cast<const float *>(a.q) + head;
-  const float *K = reinterpret_cast<const float *>(a.k) + head;
-  float *cin = a.cin + (size_t)bh * cin_floats_per_head(T);
+  const float *Q = reinterpret_cast<const float *>(a.q) + (size_t)bh * Tq * kHeadDim;
+  const float *K = reinterpret_cast<const float *>(a.k) + (size_t)bh * a.kstride * kHeadDim;
+  float *cin = a.cin + (size_t)bh * cin_floats_per_head(T, a.vrow0);
 
   float kv[kHeadDim];
 #pragma unroll
   for (int e = 0; e < kHeadDim; ++e) kv[e] = (j < T) ? K[(size_t)j * kHeadDim + e] : 0.0f;
-  float run = 0.0f;
-  for (int i0 = k0; i0 < T; i0 += kFR) {
+  float run = (a.demand_in && j < T) ? a.demand_in[(size_t)bh * a.kstride + j] : 0.0f;
+  for (int i0 = max(k0, a.vrow0); i0 < T; i0 += kFR) {
     __syncthreads();
     for (int u = t; u < kFR * kHeadDim; u += 64) {
-      const int row = i0 + u / kHeadDim;
-      sQ[u] = row < T ? Q[(size_t)i0 * kHeadDim + u] : 0.0f;
+      const int lr = i0 + u / kHeadDim - P;
+      sQ[u] = (unsigned)lr < (unsigned)Tq ? Q[(size_t)lr * kHeadDim + u % kHeadDim] : 0.0f;
     }
-    sL[t] = (i0 + t < T) ? a.lse2[(size_t)bh * T + i0 + t] : 0.0f;
+    const int lt = i0 + t - P;
+    sL[t] = (unsigned)lt < (unsigned)Tq ? a.lse2[(size_t)bh * Tq + lt] : kNoRowF32;
     __syncthreads();
     const int in = min(kFR, T - i0);
     for (int ii = 0; ii < in; ++ii) {
       const int i = i0 + ii;
-      if ((i & 31) == 0 && (i >> 5) > (j >> 5) && j < T)
-        cin[(size_t)16 * (i >> 5) * ((i >> 5) - 1) + j] = run;  // demand before block i/32
+      if ((i & 31) == 0 && (i >> 5) >= (j >> 5) && j < T)
+        cin[cin_block_offset(i >> 5, a.vrow0) + j] = run;  // demand before block i/32
       float s = 0.0f;
 #pragma unroll
       for (int e = 0; e < kHeadDim; ++e) s = __builtin_fmaf(sQ[ii * kHeadDim + e], kv[e], s);
-      if (j <= i) run += exp2f(__builtin_fmaf(s, a.c2, -sL[ii]));
+      if (j <= i && i >= P) run += exp2f(__builtin_fmaf(s, a.c2, -sL[ii]));
     }
   }
-  if (a.demand_out && j < T) a.demand_out[(size_t)bh * T + j] = run;
+  if (a.demand_out && j < T) a.demand_out[(size_t)bh * a.kstride + j] = run;
 }
 
 hipError_t launch_rows_f32(int mode, const FwdArgs &a, hipStream_t s) {
-  const int nqb = (a.T + kFR - 1) / kFR;
+  const int nqb = (a.T + kFR - 1) / kFR - a.vrow0 / kFR;   // blocks from position vrow0
   dim3 grid((unsigned)(nqb * a.BH)), block(64);
   switch (mode) {
     case kRowTempered: hipLaunchKernelGGL(rows_f32_kernel<kRowTempered>, grid, block, 0, s, a, nqb); break;

@@ -16,23 +16,41 @@ enum RowMode { kRowTempered = 0, kRowLse = 1, kRowShare = 2 };
 struct FwdArgs {
   const void *q, *k, *v;
   void *out;
-  float *lse2;          // [BH*T] workspace (dilution) or NULL
-  float *lse_nat;       // [BH*T] optional natural-log output
+  float *lse2;          // [BH*Tq] workspace (dilution) or NULL
+  float *lse_nat;       // [BH*Tq] optional natural-log output
   float *cin;           // committed demand per 32-row query block (dilution); the
                         // bf16 path stores each entry as a bf16 (hi, lo) pair of
                         // committed + eps in the same 32 bits
-  float *demand_out;    // [BH*T] optional final column totals (dilution)
-  float *rowsum_out;    // [BH*T] optional row sums of the shares (dilution)
-  int BH, T;
+  const float *demand_in;  // [BH*kstride] demand committed before the first query
+                           // row (dilution), or NULL for none
+  float *demand_out;    // [BH*kstride] optional final column totals (dilution);
+                        // may be demand_in itself
+  float *rowsum_out;    // [BH*Tq] optional row sums of the shares (dilution)
+  int BH;
+  int T;                // keys 0..T-1; query row r sits at position T - Tq + r
+  int Tq;               // query rows per head (Q, out and the per-row arrays)
+  int kstride;          // rows per head of K, V and the demand arrays (>= T)
+  int vrow0;            // first position the row kernels cover: T - Tq rounded
+                        // down to a multiple of 128 (0 for a whole prefill)
   float c2;             // tau / sqrt(d) * log2(e)
   float eps;
 };
 
-// Committed-demand storage: query sub-block qs (32 rows) keeps one float per
-// key j < 32*qs, at offset 16*qs*(qs-1) inside its head's region.
-__host__ __device__ inline size_t cin_floats_per_head(int T) {
-  const size_t n = ((size_t)T + 31) / 32;
-  return 16 * n * (n - 1);
+// First position the row kernels cover for keys 0..T-1 and Tq query rows at
+// positions T-Tq..T-1: the first row's position rounded down to the largest
+// query block (128 rows).
+__host__ __device__ inline int first_block_row(int T, int Tq) { return ((T - Tq) / 128) * 128; }
+
+// Committed-demand storage: 32-row query block qs keeps one entry per key
+// j < 32*(qs+1) -- the demand its rows inherit from every earlier row,
+// including rows before a prefill chunk -- at offset cin_block_offset(qs)
+// inside its head's region.  Blocks start at qs0 = vrow0/32.
+__host__ __device__ inline size_t cin_block_offset(int qs, int vrow0) {
+  const size_t b = (size_t)qs, b0 = (size_t)(vrow0 / 32);
+  return 16 * b * (b + 1) - 16 * b0 * (b0 + 1);
+}
+__host__ __device__ inline size_t cin_floats_per_head(int T, int vrow0) {
+  return cin_block_offset((T + 31) / 32, vrow0);
 }
 
 hipError_t launch_rows_bf16(int mode, const FwdArgs &a, hipStream_t s);

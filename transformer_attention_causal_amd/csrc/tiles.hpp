@@ -16,10 +16,11 @@ constexpr float kNoRow = 1e30f;            // log-sum-exp given to rows past the
 // Query index (within a wave's 32 rows) of accumulator element r in lane half h.
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-// Load one 16-byte chunk of a [BH][T][64] bf16 tensor, zeros past the end.
+// Load one 16-byte chunk of row `row` of a [T][64] bf16 array; zeros for rows
+// outside [0, T).
 __device__ __forceinline__ u32x4 load_row_chunk(const __bf16 *base, int row, int T, int chunk) {
   u32x4 z = {0u, 0u, 0u, 0u};
-  if (row < T) z = *reinterpret_cast<const u32x4 *>(base + (size_t)row * kHeadDim + chunk * 8);
+  if ((unsigned)row < (unsigned)T) z = *reinterpret_cast<const u32x4 *>(base + (size_t)row * kHeadDim + chunk * 8);
   return z;
 }
 
