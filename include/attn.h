@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_EINVAL = -1,     /* bad argument: null/misaligned pointer, size <= 0, tau/eps out of range */
-  ATTN_ENOTSUP = -2,    /* valid but unsupported: d != 64, fp32 decode, device not gfx950 */
+  ATTN_ENOTSUP = -2,    /* valid but unsupported: head dim, fp32 decode/backward, not gfx950 */
   ATTN_EWORKSPACE = -3, /* workspace missing or smaller than *_workspace_bytes() */
   ATTN_EHIP = -4        /* a HIP runtime call or kernel launch failed */
 } attn_status;
@@ -73,7 +73,7 @@ size_t attn_fwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype)
  *   out        [B,H,T,d] device array of `dtype` (output; may not alias q/k/v)
  *   B, H, T    batch, heads, sequence length (each >= 1; T < 16777216, the
  *              kernels address one head's rows with byte offsets below 2^31)
- *   d          head dimension; only 64 is supported (else ATTN_ENOTSUP)
+ *   d          head dimension: 64, or 128 with ATTN_BF16 (else ATTN_ENOTSUP)
  *   tau        logit multiplier, finite and >= 0 (tau = 0 gives uniform bids)
  *   mode       ATTN_TEMPERED or ATTN_DILUTION
  *   eps        share-denominator constant (dilution), finite and >= 0
@@ -178,6 +178,13 @@ size_t attn_prefill_workspace_bytes(int B, int H, int Tq, int Tk, int d, int mod
  *   out        [B,H,Tq,d] of `dtype` (may not alias q or the caches)
  *   B, H       >= 1;  1 <= Tq <= Tk <= Lcap < 16777216
  *   d, tau, mode, eps, dtype  as for attn_fwd
+ *   tau_bh     [B,H] fp32 device array or NULL: when given, head (b,h) uses
+ *              the multiplier tau_bh[b*H+h] in place of tau -- the per-
+ *              sequence temperature a learned-temperature layer produces
+ *              ("Learning to Focus", sec. 2.2: tau_learned = clip(mean(X w),
+ *              tau_min, tau_max) replaces sqrt(d), i.e. a multiplier
+ *              sqrt(d)/tau_learned).  Values must be finite and >= 0; they
+ *              are read on the device and not checked.
  *   demand_in  [B,H,Lcap] fp32 (dilution): each key's demand from the rows
  *              before P (the new keys' entries are normally 0), or NULL for
  *              none; entries >= Tk are not read
@@ -190,9 +197,9 @@ size_t attn_prefill_workspace_bytes(int B, int H, int Tq, int Tk, int d, int mod
  * demand_in and demand_out must be NULL for ATTN_TEMPERED (else ATTN_EINVAL).
  * Outputs may not alias each other or any tensor argument. */
 int attn_prefill(const void *q, const void *kcache, const void *vcache, void *out, int B, int H,
-                 int Tq, int Tk, int Lcap, int d, float tau, int mode, float eps, int dtype,
-                 const float *demand_in, float *demand_out, float *lse_out, void *workspace,
-                 size_t workspace_bytes, void *hip_stream);
+                 int Tq, int Tk, int Lcap, int d, float tau, const float *tau_bh, int mode,
+                 float eps, int dtype, const float *demand_in, float *demand_out, float *lse_out,
+                 void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /* Bytes of device workspace attn_decode needs (per-(sequence,head,split)
  * partial maxima, sums and weighted values plus one fp32 score per cached
@@ -211,12 +218,22 @@ size_t attn_decode_workspace_bytes(int S, int H, int Lcap, int d);
  *            for Lcap everywhere.  To decode with the new token's own key, the
  *            caller writes its k/v at index kv_len-1 and zeroes its demand.
  *            A kv_len outside [1, Lcap] is clamped to that range on device.
+ *   d        64 or 128
  *   tau, eps as for attn_fwd; dtype must be ATTN_BF16 (else ATTN_ENOTSUP).
  * Consecutive steps must be ordered on one stream (each reads the demand the
  * previous one wrote). */
 int attn_decode(const void *q, const void *kcache, const void *vcache, float *demand, void *out,
                 int S, int H, int Lcap, const int32_t *kv_len, int d, float tau, float eps,
                 int dtype, void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* attn_decode with a per-(sequence, head) multiplier: tau_sh is an [S,H] fp32
+ * device array (or NULL for `tau` everywhere); (s,h) uses tau_sh[s*H+h] in
+ * place of tau, as attn_prefill's tau_bh (values finite and >= 0, not
+ * checked). */
+int attn_decode_ex(const void *q, const void *kcache, const void *vcache, float *demand, void *out,
+                   int S, int H, int Lcap, const int32_t *kv_len, int d, float tau,
+                   const float *tau_sh, float eps, int dtype, void *workspace,
+                   size_t workspace_bytes, void *hip_stream);
 
 /* YaRN attention temperature ("YaRN > Attention Temperature Scaling"):
  * returns sqrt(t) with t = 0.1 ln(s) + 1, the multiplier for extension

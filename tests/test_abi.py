@@ -79,7 +79,9 @@ def fwd(**kw):
     (dict(rowsum_out=FAKE + 0x4000000), ab.ATTN_EINVAL),  # rowsum_out in tempered mode
     (dict(mode=1, lse_out=FAKE + 0x4000000, rowsum_out=FAKE + 0x4000010,
           workspace=FAKE + 0x5000000, workspace_bytes=1 << 30), ab.ATTN_EINVAL),  # outputs overlap
-    (dict(d=128), ab.ATTN_ENOTSUP),
+    (dict(d=96), ab.ATTN_ENOTSUP),
+    (dict(d=128, dtype=0), ab.ATTN_ENOTSUP),         # fp32 runs at d = 64 only
+    (dict(d=128, mode=1), ab.ATTN_EWORKSPACE),       # bf16 at d = 128 is supported
     (dict(T=1 << 24), ab.ATTN_EINVAL),               # one head's rows need offsets >= 2^31
     (dict(mode=1, T=(1 << 24) - 1, k=FAKE + (1 << 32), v=FAKE + (2 << 32),
           out=FAKE + (3 << 32)), ab.ATTN_EWORKSPACE),   # largest T passes the shape check
@@ -97,10 +99,15 @@ def test_workspace_sizes():
     want = 16 * 16384 * 4 + 16 * 16 * n * (n + 1) * 4
     got = ab.attn_fwd_workspace_bytes(1, 16, 16384, 64, 1, 1)
     assert want <= got <= want + 512
-    assert ab.attn_fwd_workspace_bytes(1, 1, 16, 128, 1, 1) == 0
+    assert ab.attn_fwd_workspace_bytes(1, 1, 16, 96, 1, 1) == 0
+    assert ab.attn_fwd_workspace_bytes(1, 1, 16, 128, 1, 0) == 0      # fp32 at d = 128
+    assert (ab.attn_fwd_workspace_bytes(1, 16, 16384, 128, 1, 1)
+            == ab.attn_fwd_workspace_bytes(1, 16, 16384, 64, 1, 1))  # independent of d
     assert ab.attn_fwd_workspace_bytes(0, 1, 16, 64, 1, 1) == 0
     assert ab.attn_decode_workspace_bytes(64, 16, 32768, 64) >= 64 * 16 * 32768 * 4
     assert ab.attn_decode_workspace_bytes(64, 16, 32768, 32) == 0
+    assert (ab.attn_decode_workspace_bytes(64, 16, 32768, 128)
+            > ab.attn_decode_workspace_bytes(64, 16, 32768, 64))
 
 
 def test_bwd_workspace_sizes():
@@ -128,12 +135,14 @@ def test_prefill_workspace_sizes():
     assert ab.attn_prefill_workspace_bytes(1, 16, Tq, Tk, 64, 0, 1) == 0   # tempered
     assert ab.attn_prefill_workspace_bytes(1, 16, 10, 9, 64, 1, 1) == 0    # Tq > Tk
     assert ab.attn_prefill_workspace_bytes(1, 16, 0, 9, 64, 1, 1) == 0
-    assert ab.attn_prefill_workspace_bytes(1, 16, 8, 9, 128, 1, 1) == 0
+    assert ab.attn_prefill_workspace_bytes(1, 16, 8, 9, 96, 1, 1) == 0
+    assert ab.attn_prefill_workspace_bytes(1, 16, 8, 9, 128, 1, 0) == 0
 
 
 def pre(**kw):
     args = dict(q=FAKE, kcache=FAKE + 0x1000000, vcache=FAKE + 0x2000000, out=FAKE + 0x3000000,
-                B=1, H=2, Tq=16, Tk=40, Lcap=64, d=64, tau=1.0, mode=1, eps=1e-6, dtype=1,
+                B=1, H=2, Tq=16, Tk=40, Lcap=64, d=64, tau=1.0, tau_bh=None, mode=1, eps=1e-6,
+                dtype=1,
                 demand_in=FAKE + 0x4000000, demand_out=FAKE + 0x4000000, lse_out=None,
                 workspace=None, workspace_bytes=0, hip_stream=None)
     args.update(kw)
@@ -158,7 +167,12 @@ def pre(**kw):
     (dict(lse_out=FAKE + 0x4000000 + 256), ab.ATTN_EINVAL),  # lse inside the demand
     (dict(lse_out=FAKE), ab.ATTN_EINVAL),               # lse aliases q
     (dict(demand_out=FAKE + 0x2000000), ab.ATTN_EINVAL),   # demand inside the V cache
-    (dict(d=128), ab.ATTN_ENOTSUP),
+    (dict(d=96), ab.ATTN_ENOTSUP),
+    (dict(d=128, dtype=0), ab.ATTN_ENOTSUP),            # fp32 runs at d = 64 only
+    (dict(d=128), ab.ATTN_EWORKSPACE),                  # bf16 at d = 128 is supported
+    (dict(tau_bh=FAKE + 0x6000004), ab.ATTN_EINVAL),    # misaligned tau array
+    (dict(tau_bh=FAKE + 0x4000000 + 64), ab.ATTN_EINVAL),  # tau array inside the demand
+    (dict(tau_bh=FAKE + 0x6000000), ab.ATTN_EWORKSPACE),
     (dict(), ab.ATTN_EWORKSPACE),                       # in-place demand is accepted
     (dict(demand_in=None, demand_out=None), ab.ATTN_EWORKSPACE),
     (dict(workspace=FAKE + 0x5000000, workspace_bytes=64), ab.ATTN_EWORKSPACE),
@@ -201,10 +215,13 @@ def test_bwd_rejects_bad_arguments(kw, status):
 def dec(**kw):
     args = dict(q=FAKE, kcache=FAKE + 0x1000000, vcache=FAKE + 0x20000000,
                 demand=FAKE + 0x40000000, out=FAKE + 0x60000000, S=2, H=2, Lcap=100,
-                kv_len=None, d=64, tau=1.0, eps=1e-6, dtype=1, workspace=None,
+                kv_len=None, d=64, tau=1.0, tau_sh=None, eps=1e-6, dtype=1, workspace=None,
                 workspace_bytes=0, hip_stream=None)
     args.update(kw)
-    return ab.attn_decode(**args)
+    if args["tau_sh"] is None and "tau_sh" not in kw:
+        del args["tau_sh"]
+        return ab.attn_decode(**args)
+    return ab.attn_decode_ex(**args)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -215,7 +232,11 @@ def dec(**kw):
     (dict(tau=-0.5), ab.ATTN_EINVAL),
     (dict(eps=float("inf")), ab.ATTN_EINVAL),
     (dict(dtype=0), ab.ATTN_ENOTSUP),                # fp32 decode
-    (dict(d=128), ab.ATTN_ENOTSUP),
+    (dict(d=96), ab.ATTN_ENOTSUP),
+    (dict(d=128), ab.ATTN_EWORKSPACE),               # d = 128 is supported
+    (dict(tau_sh=FAKE + 0x70000004), ab.ATTN_EINVAL),   # misaligned tau array
+    (dict(tau_sh=FAKE + 0x40000000), ab.ATTN_EINVAL),   # tau array inside the demand
+    (dict(tau_sh=FAKE + 0x70000000), ab.ATTN_EWORKSPACE),
     (dict(out=FAKE + 0x1000000), ab.ATTN_EINVAL),     # out inside the K cache
     (dict(), ab.ATTN_EWORKSPACE),
 ])

@@ -1,0 +1,182 @@
+"""GPU parity at head dimension 128 (the focal models' heads) and with
+per-(batch, head) temperature multipliers, against the fp64 oracle through
+the C ABI: forward of both operators, chunked prefill, and decode."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import DEMAND_TOTAL_REL, assert_close, oracle_qkv, sample_rows, to_device
+from transformer_attention_causal_amd import binding as ab
+from transformer_attention_causal_amd.workloads import (PREFILL, decode_initial_demand,
+                                                        decode_queries, draw_qkv, learned_tau,
+                                                        prefill_inputs)
+
+pytestmark = pytest.mark.gpu
+
+TAU4 = math.sqrt(0.1 * math.log(4.0) + 1.0)
+
+
+def head_inputs(inp, bh_list):
+    """The oracle's view of the listed flattened heads, each as a [1,1,T,d] array."""
+    B, H = inp.q.shape[:2]
+    out = []
+    for bh in bh_list:
+        b, h = divmod(bh, H)
+        out.append(tuple(oracle.Bf16(np.ascontiguousarray(x[b:b + 1, h:h + 1]))
+                         for x in (inp.q, inp.k, inp.v)))
+    return out
+
+
+def run_prefill(inp, tau, mode, eps=1e-6, tau_bh=None, want_demand=False):
+    import torch
+
+    q, k, v = (to_device(a, inp.dtype) for a in (inp.q, inp.k, inp.v))
+    B, H, T, _ = q.shape
+    dem = torch.zeros((B, H, T), dtype=torch.float32, device="cuda") if want_demand else None
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    tb = torch.from_numpy(tau_bh).cuda() if tau_bh is not None else None
+    out = ab.prefill(q, k, v, T, tau=tau, mode=mode, eps=eps, demand_in=dem, demand_out=dem,
+                     lse_out=lse, tau_bh=tb)
+    torch.cuda.synchronize()
+    return (out.float().cpu().numpy(), lse.cpu().numpy(),
+            dem.cpu().numpy() if dem is not None else None)
+
+
+@pytest.mark.parametrize("T", [1, 7, 33, 64, 129, 300, 1000])
+def test_d128_ragged_lengths(T):
+    inp = draw_qkv(2, 2, T, 128, "bf16", seed=6000 + T, heavy_frac=0.05)
+    out, lse, dem = run_prefill(inp, 1.0, ab.ATTN_DILUTION, want_demand=True)
+    ref, rlse, rdem = oracle.dilution_fwd(*oracle_qkv(inp), 1.0, 1e-6)
+    assert_close(out, ref, "bf16", f"d128 dilution T={T}")
+    assert np.max(np.abs(lse - rlse)) <= 2e-3
+    assert np.max(np.abs(dem.sum(axis=-1) / T - 1.0)) <= DEMAND_TOTAL_REL
+    assert np.max(np.abs(dem - rdem)) <= 2e-2 * max(1.0, float(np.max(rdem)))
+    out, lse, _ = run_prefill(inp, TAU4, ab.ATTN_TEMPERED)
+    ref, rlse = oracle.tempered_fwd(*oracle_qkv(inp), TAU4)
+    assert_close(out, ref, "bf16", f"d128 tempered T={T}")
+    assert np.max(np.abs(lse - rlse)) <= 2e-3
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_per_head_tau(d):
+    """Per-(b,h) multipliers sqrt(d)/t, t ~ U[5, 10] (learned-temperature
+    range): every head matches the oracle run with its own scalar tau."""
+    B, H, T = 2, 3, 300
+    inp = draw_qkv(B, H, T, d, "bf16", seed=6100 + d, heavy_frac=0.05)
+    taus = learned_tau(B, H, d, seed=6100 + d)
+    for mode in (ab.ATTN_TEMPERED, ab.ATTN_DILUTION):
+        out, lse, _ = run_prefill(inp, 1.0, mode, tau_bh=taus)
+        for bh, (q1, k1, v1) in enumerate(head_inputs(inp, range(B * H))):
+            b, h = divmod(bh, H)
+            tau = float(taus[b, h])
+            if mode == ab.ATTN_TEMPERED:
+                ref, rlse = oracle.tempered_fwd(q1, k1, v1, tau)
+            else:
+                ref, rlse, _ = oracle.dilution_fwd(q1, k1, v1, tau, 1e-6)
+            assert_close(out[b:b + 1, h:h + 1], ref, "bf16", f"d={d} mode={mode} head {bh} tau={tau:.3f}")
+            assert np.max(np.abs(lse[b, h] - rlse[0, 0])) <= 2e-3
+
+
+def test_d128_chunks_and_carried_demand():
+    """Chunked prefill at d = 128 with per-head multipliers: chunks over a
+    NaN-tailed cache reproduce the whole prefill and its column totals."""
+    import torch
+
+    B, H, T, d, Lcap = 1, 2, 700, 128, 769
+    inp = draw_qkv(B, H, T, d, "bf16", seed=6200, heavy_frac=0.05)
+    taus = learned_tau(B, H, d, seed=6200)
+    q, k, v = (to_device(a, "bf16") for a in (inp.q, inp.k, inp.v))
+    kc = torch.full((B, H, Lcap, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    D = torch.full((B, H, Lcap), 7.0, dtype=torch.float32, device="cuda")
+    D[:, :, :T] = 0.0
+    tb = torch.from_numpy(taus).cuda()
+    outs = []
+    for a, b in zip((0, 200, 333, 640), (200, 333, 640, 700)):
+        kc[:, :, a:b] = k[:, :, a:b]
+        vc[:, :, a:b] = v[:, :, a:b]
+        outs.append(ab.prefill(q[:, :, a:b].contiguous(), kc, vc, b, tau=1.0,
+                               mode=ab.ATTN_DILUTION, eps=1e-6, demand_in=D, demand_out=D,
+                               tau_bh=tb))
+    torch.cuda.synchronize()
+    out = torch.cat(outs, dim=2).float().cpu().numpy()
+    dem = D.cpu().numpy()
+    assert np.all(dem[..., T:] == 7.0)
+    for bh, (q1, k1, v1) in enumerate(head_inputs(inp, range(B * H))):
+        tau = float(taus[0, bh])
+        ref, _, rdem = oracle.dilution_fwd(q1, k1, v1, tau, 1e-6)
+        assert_close(out[:, bh:bh + 1], ref, "bf16", f"d128 chunks head {bh}")
+        assert np.max(np.abs(dem[0, bh, :T] - rdem[0, 0])) <= 2e-2 * max(1.0, float(rdem.max()))
+
+
+def test_d128_decode_steps():
+    """Four cached-decode steps at d = 128 with per-(sequence, head)
+    multipliers, demand carried between steps, against the oracle."""
+    import torch
+
+    S, H, L, d = 3, 4, 5000, 128
+    inp = draw_qkv(S, H, L, d, "bf16", seed=6300)
+    taus = learned_tau(S, H, d, seed=6300)
+    D0 = decode_initial_demand(S, H, L, seed=6300)
+    qs = decode_queries(4, S, H, d, seed=6300)
+    kc, vc = to_device(inp.k, "bf16"), to_device(inp.v, "bf16")
+    Dd = torch.from_numpy(D0.copy()).cuda()
+    tb = torch.from_numpy(taus).cuda()
+    kv_len = torch.tensor([L, 4097, 1], dtype=torch.int32, device="cuda")
+    Dr = D0.astype(np.float64)
+    for step in range(4):
+        out = ab.decode(to_device(qs[step], "bf16"), kc, vc, Dd, tau=1.0, eps=1e-6,
+                        kv_len=kv_len, tau_sh=tb)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy()
+        for s in range(S):
+            for h in range(H):
+                Dsh = np.ascontiguousarray(Dr[s:s + 1, h:h + 1])
+                ref = oracle.dilution_decode_step(
+                    oracle.Bf16(np.ascontiguousarray(qs[step][s:s + 1, h:h + 1])),
+                    oracle.Bf16(np.ascontiguousarray(inp.k[s:s + 1, h:h + 1])),
+                    oracle.Bf16(np.ascontiguousarray(inp.v[s:s + 1, h:h + 1])), Dsh,
+                    float(taus[s, h]), 1e-6, kv_len=[int(kv_len[s])])
+                Dr[s, h] = Dsh[0, 0]
+                assert_close(got[s:s + 1, h:h + 1], ref, "bf16", f"decode step {step} s={s} h={h}")
+        Dg = Dd.cpu().numpy().astype(np.float64)
+        rel = np.abs(Dg.sum(-1) / Dr.sum(-1) - 1.0)
+        assert np.max(rel) <= DEMAND_TOTAL_REL, f"step {step}: demand totals {np.max(rel):.2e}"
+
+
+@pytest.mark.timeout(600)
+def test_focal_d128_t16k_workload():
+    """B=1, H=20, T=16384, d=128 (a 2.7B focal model's attention at 16K),
+    per-head learned temperatures: sampled rows of three heads against the
+    oracle for both operators, and every head's demand totals."""
+    import torch
+
+    w = PREFILL["focal_d128_t16k"]
+    inp = prefill_inputs(w)
+    taus = learned_tau(w.B, w.H, w.d, seed=w.seed)
+    rows = sample_rows(w.T, 24, seed=161)
+    out, _, dem = run_prefill(inp, 1.0, ab.ATTN_DILUTION, w.eps, tau_bh=taus, want_demand=True)
+    torch.cuda.empty_cache()
+    assert np.max(np.abs(dem.sum(axis=-1) / w.T - 1.0)) <= DEMAND_TOTAL_REL
+    out_t, _, _ = run_prefill(inp, 1.0, ab.ATTN_TEMPERED, tau_bh=taus)
+    for bh, (q1, k1, v1) in zip((0, 7, 19), head_inputs(inp, (0, 7, 19))):
+        tau = float(taus[0, bh])
+        ref, _, _ = oracle.dilution_fwd(q1, k1, v1, tau, w.eps, rows=rows)
+        assert_close(out[:, bh:bh + 1, rows], ref[:, :, rows], "bf16", f"focal d128 dilution head {bh}")
+        ref_t, _ = oracle.tempered_fwd(q1, k1, v1, tau, rows=rows)
+        assert_close(out_t[:, bh:bh + 1, rows], ref_t[:, :, rows], "bf16",
+                     f"focal d128 tempered head {bh}")
+
+
+def test_d128_deterministic():
+    import torch
+
+    inp = draw_qkv(1, 4, 777, 128, "bf16", seed=6400, heavy_frac=0.05)
+    q, k, v = (to_device(a, "bf16") for a in (inp.q, inp.k, inp.v))
+    for mode in (ab.ATTN_TEMPERED, ab.ATTN_DILUTION):
+        a = ab.fwd(q, k, v, tau=1.0, mode=mode)
+        b = ab.fwd(q, k, v, tau=1.0, mode=mode)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)

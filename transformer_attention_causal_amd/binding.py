@@ -26,7 +26,7 @@ ATTN_F32, ATTN_BF16 = 0, 1
 EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_bytes", "attn_dilution_lse",
             "attn_dilution_committed", "attn_dilution_shares", "attn_bwd",
             "attn_bwd_workspace_bytes", "attn_prefill", "attn_prefill_workspace_bytes",
-            "attn_decode", "attn_decode_workspace_bytes",
+            "attn_decode", "attn_decode_ex", "attn_decode_workspace_bytes",
             "attn_yarn_tau", "attn_strerror")
 
 
@@ -60,8 +60,8 @@ def load() -> ctypes.CDLL:
         lib.attn_bwd_workspace_bytes.restype = sz
         lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
         lib.attn_prefill.restype = i
-        lib.attn_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, f, i, vp, vp, vp,
-                                     vp, sz, vp]
+        lib.attn_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i, f, i, vp, vp,
+                                     vp, vp, sz, vp]
         lib.attn_prefill_workspace_bytes.restype = sz
         lib.attn_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
         lib.attn_dilution_lse.restype = i
@@ -74,6 +74,9 @@ def load() -> ctypes.CDLL:
         lib.attn_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
         lib.attn_decode.restype = i
         lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, vp, i, f, f, i, vp, sz, vp]
+        lib.attn_decode_ex.restype = i
+        lib.attn_decode_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, vp, i, f, vp, f, i, vp, sz,
+                                       vp]
         lib.attn_decode_workspace_bytes.restype = sz
         lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
         lib.attn_yarn_tau.restype = ctypes.c_double
@@ -108,11 +111,11 @@ def attn_bwd_workspace_bytes(B, H, T, d, mode, dtype) -> int:
     return int(load().attn_bwd_workspace_bytes(B, H, T, d, mode, dtype))
 
 
-def attn_prefill(q, kcache, vcache, out, B, H, Tq, Tk, Lcap, d, tau, mode, eps, dtype,
+def attn_prefill(q, kcache, vcache, out, B, H, Tq, Tk, Lcap, d, tau, tau_bh, mode, eps, dtype,
                  demand_in, demand_out, lse_out, workspace, workspace_bytes, hip_stream) -> int:
-    return load().attn_prefill(q, kcache, vcache, out, B, H, Tq, Tk, Lcap, d, tau, mode, eps,
-                               dtype, demand_in, demand_out, lse_out, workspace, workspace_bytes,
-                               hip_stream)
+    return load().attn_prefill(q, kcache, vcache, out, B, H, Tq, Tk, Lcap, d, tau, tau_bh, mode,
+                               eps, dtype, demand_in, demand_out, lse_out, workspace,
+                               workspace_bytes, hip_stream)
 
 
 def attn_prefill_workspace_bytes(B, H, Tq, Tk, d, mode, dtype) -> int:
@@ -147,6 +150,12 @@ def attn_decode(q, kcache, vcache, demand, out, S, H, Lcap, kv_len, d, tau, eps,
                               dtype, workspace, workspace_bytes, hip_stream)
 
 
+def attn_decode_ex(q, kcache, vcache, demand, out, S, H, Lcap, kv_len, d, tau, tau_sh, eps,
+                   dtype, workspace, workspace_bytes, hip_stream) -> int:
+    return load().attn_decode_ex(q, kcache, vcache, demand, out, S, H, Lcap, kv_len, d, tau,
+                                 tau_sh, eps, dtype, workspace, workspace_bytes, hip_stream)
+
+
 def attn_decode_workspace_bytes(S, H, Lcap, d) -> int:
     return int(load().attn_decode_workspace_bytes(S, H, Lcap, d))
 
@@ -177,10 +186,10 @@ def _stream_handle(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def fwd_workspace(B, H, T, mode, dtype_code, device):
+def fwd_workspace(B, H, T, mode, dtype_code, device, d=64):
     import torch
 
-    n = attn_fwd_workspace_bytes(B, H, T, 64, mode, dtype_code)
+    n = attn_fwd_workspace_bytes(B, H, T, d, mode, dtype_code)
     if n == 0:
         return None, 0
     return torch.empty(n, dtype=torch.uint8, device=device), n
@@ -201,7 +210,7 @@ def fwd(q, k, v, tau: float = 1.0, mode: int = ATTN_TEMPERED, eps: float = 1e-6,
         out = torch.empty_like(q)
     ws_bytes = 0
     if workspace is None:
-        workspace, ws_bytes = fwd_workspace(B, H, T, mode, code, q.device)
+        workspace, ws_bytes = fwd_workspace(B, H, T, mode, code, q.device, d)
     else:
         ws_bytes = workspace.numel() * workspace.element_size()
     st = attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, T, d,
@@ -254,10 +263,11 @@ def bwd(q, k, v, out, dout, lse, rowsum=None, tau: float = 1.0, mode: int = ATTN
 
 def prefill(q, kcache, vcache, Tk: int, tau: float = 1.0, mode: int = ATTN_DILUTION,
             eps: float = 1e-6, demand_in=None, demand_out=None, lse_out=None, out=None,
-            workspace=None):
-    """Run attn_prefill: q [B,H,Tq,64] holds the rows at positions Tk-Tq..Tk-1,
-    the caches [B,H,Lcap,64] keys/values 0..Tk-1; ``demand_in``/``demand_out``
-    are [B,H,Lcap] fp32 (may be one tensor: updated in place).  Returns ``out``."""
+            workspace=None, tau_bh=None):
+    """Run attn_prefill: q [B,H,Tq,d] holds the rows at positions Tk-Tq..Tk-1,
+    the caches [B,H,Lcap,d] keys/values 0..Tk-1; ``demand_in``/``demand_out``
+    are [B,H,Lcap] fp32 (may be one tensor: updated in place); ``tau_bh`` an
+    optional [B,H] fp32 tensor of per-head multipliers.  Returns ``out``."""
     import torch
 
     if q.dim() != 4 or kcache.dim() != 4 or vcache.shape != kcache.shape:
@@ -273,6 +283,9 @@ def prefill(q, kcache, vcache, Tk: int, tau: float = 1.0, mode: int = ATTN_DILUT
         if t is not None and (t.shape != (B, H, Lcap) or t.dtype != torch.float32
                               or not t.is_contiguous()):
             raise ValueError("demand arrays must be contiguous float32 [B,H,Lcap]")
+    if tau_bh is not None and (tau_bh.shape != (B, H) or tau_bh.dtype != torch.float32
+                               or not tau_bh.is_contiguous()):
+        raise ValueError("tau_bh must be a contiguous float32 [B,H] tensor")
     code = _dtype_code(q)
     if out is None:
         out = torch.empty_like(q)
@@ -284,7 +297,8 @@ def prefill(q, kcache, vcache, Tk: int, tau: float = 1.0, mode: int = ATTN_DILUT
     else:
         ws_bytes = workspace.numel() * workspace.element_size()
     st = attn_prefill(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), out.data_ptr(), B, H,
-                      Tq, int(Tk), Lcap, d, float(tau), int(mode), float(eps), code,
+                      Tq, int(Tk), Lcap, d, float(tau),
+                      tau_bh.data_ptr() if tau_bh is not None else None, int(mode), float(eps), code,
                       demand_in.data_ptr() if demand_in is not None else None,
                       demand_out.data_ptr() if demand_out is not None else None,
                       lse_out.data_ptr() if lse_out is not None else None,
@@ -335,16 +349,17 @@ def dilution_stages(q, k, v, tau: float = 1.0, eps: float = 1e-6, out=None, work
     return [lse, committed, shares], out
 
 
-def decode_workspace(S, H, Lcap, device):
+def decode_workspace(S, H, Lcap, device, d=64):
     import torch
 
-    n = attn_decode_workspace_bytes(S, H, Lcap, 64)
+    n = attn_decode_workspace_bytes(S, H, Lcap, d)
     return torch.empty(n, dtype=torch.uint8, device=device), n
 
 
 def decode(q, kcache, vcache, demand, tau: float = 1.0, eps: float = 1e-6, kv_len=None,
-           out=None, workspace=None):
-    """Run one attn_decode step; ``demand`` is updated in place.  Returns ``out``."""
+           out=None, workspace=None, tau_sh=None):
+    """Run one attn_decode_ex step; ``demand`` is updated in place; ``tau_sh`` an
+    optional [S,H] fp32 tensor of per-(sequence, head) multipliers.  Returns ``out``."""
     import torch
 
     S, H, Lcap, d = kcache.shape
@@ -358,16 +373,19 @@ def decode(q, kcache, vcache, demand, tau: float = 1.0, eps: float = 1e-6, kv_le
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
-        workspace, ws_bytes = decode_workspace(S, H, Lcap, q.device)
+        workspace, ws_bytes = decode_workspace(S, H, Lcap, q.device, d)
     else:
         ws_bytes = workspace.numel() * workspace.element_size()
     if kv_len is not None and (kv_len.dtype != torch.int32 or kv_len.numel() != S):
         raise ValueError("kv_len must be an int32 device tensor of length S")
-    st = attn_decode(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), demand.data_ptr(),
-                     out.data_ptr(), S, H, Lcap,
-                     kv_len.data_ptr() if kv_len is not None else None, d, float(tau),
-                     float(eps), _dtype_code(q), workspace.data_ptr(), ws_bytes,
-                     _stream_handle(q.device))
+    if tau_sh is not None and (tau_sh.shape != (S, H) or tau_sh.dtype != torch.float32
+                               or not tau_sh.is_contiguous()):
+        raise ValueError("tau_sh must be a contiguous float32 [S,H] tensor")
+    st = attn_decode_ex(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), demand.data_ptr(),
+                        out.data_ptr(), S, H, Lcap,
+                        kv_len.data_ptr() if kv_len is not None else None, d, float(tau),
+                        tau_sh.data_ptr() if tau_sh is not None else None, float(eps),
+                        _dtype_code(q), workspace.data_ptr(), ws_bytes, _stream_handle(q.device))
     if st != ATTN_OK:
-        raise AttnError(st, "attn_decode")
+        raise AttnError(st, "attn_decode_ex")
     return out

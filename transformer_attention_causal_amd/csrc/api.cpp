@@ -80,17 +80,20 @@ struct DecWorkspace {
   size_t scores_bytes, ml_bytes, o_bytes, total;
 };
 
-bool dec_workspace(int S, int H, int Lcap, DecWorkspace *ws) {
+bool dec_workspace(int S, int H, int Lcap, int d, DecWorkspace *ws) {
   const size_t SH = (size_t)S * H;
   if (SH > (size_t)INT32_MAX) return false;
   ws->splits = (Lcap + kDecChunk - 1) / kDecChunk;
   if (SH * (size_t)ws->splits > (size_t)INT32_MAX) return false;
   ws->scores_bytes = round_up(SH * (size_t)Lcap * sizeof(float));
   ws->ml_bytes = round_up(SH * ws->splits * 2 * sizeof(float));
-  ws->o_bytes = round_up(SH * ws->splits * (attn::kHeadDim + 1) * sizeof(float));
+  ws->o_bytes = round_up(SH * ws->splits * (size_t)(d + 1) * sizeof(float));
   ws->total = ws->scores_bytes + ws->ml_bytes + ws->o_bytes;
   return true;
 }
+
+// Head dimensions with kernels: 64 for both storage types, 128 for bf16.
+bool head_dim_ok(int d, int dtype) { return d == 64 || (d == 128 && dtype == ATTN_BF16); }
 
 bool shape_ok(int B, int H, int T) {
   if (B <= 0 || H <= 0 || T <= 0) return false;
@@ -107,7 +110,7 @@ bool shape_ok(int B, int H, int T) {
 extern "C" {
 
 size_t attn_fwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype) {
-  if (!shape_ok(B, H, T) || d != attn::kHeadDim) return 0;
+  if (!shape_ok(B, H, T) || !head_dim_ok(d, dtype)) return 0;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
   if (mode != ATTN_DILUTION) return 0;
   FwdWorkspace ws;
@@ -131,7 +134,7 @@ int check_fwd(const void *q, const void *k, const void *v, const void *out, int 
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EINVAL;
   if (!std::isfinite(tau) || tau < 0.0f) return ATTN_EINVAL;
   if (!std::isfinite(eps) || eps < 0.0f) return ATTN_EINVAL;
-  if (d != attn::kHeadDim) return ATTN_ENOTSUP;
+  if (!head_dim_ok(d, dtype)) return ATTN_ENOTSUP;
   const size_t esz = dtype == ATTN_BF16 ? 2 : 4;
   const size_t nbytes = (size_t)B * H * (size_t)T * d * esz;
   if (out && (overlaps(out, nbytes, q, nbytes) || overlaps(out, nbytes, k, nbytes) ||
@@ -171,6 +174,7 @@ attn::FwdArgs make_args(const void *q, const void *k, const void *v, void *out, 
   a.BH = B * H;
   a.T = a.Tq = a.kstride = T;
   a.vrow0 = 0;
+  a.D = d;
   // logits are tau <q,k> / sqrt(d); the kernels work in base 2
   a.c2 = (float)((double)tau / std::sqrt((double)d) * 1.4426950408889634);
   a.eps = eps;
@@ -282,7 +286,7 @@ int attn_fwd(const void *q, const void *k, const void *v, void *out, int B, int 
 }
 
 size_t attn_prefill_workspace_bytes(int B, int H, int Tq, int Tk, int d, int mode, int dtype) {
-  if (!shape_ok(B, H, Tk) || Tq < 1 || Tq > Tk || d != attn::kHeadDim) return 0;
+  if (!shape_ok(B, H, Tk) || Tq < 1 || Tq > Tk || !head_dim_ok(d, dtype)) return 0;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
   if (mode != ATTN_DILUTION) return 0;
   FwdWorkspace ws;
@@ -291,9 +295,9 @@ size_t attn_prefill_workspace_bytes(int B, int H, int Tq, int Tk, int d, int mod
 }
 
 int attn_prefill(const void *q, const void *kcache, const void *vcache, void *out, int B, int H,
-                 int Tq, int Tk, int Lcap, int d, float tau, int mode, float eps, int dtype,
-                 const float *demand_in, float *demand_out, float *lse_out, void *workspace,
-                 size_t workspace_bytes, void *hip_stream) {
+                 int Tq, int Tk, int Lcap, int d, float tau, const float *tau_bh, int mode,
+                 float eps, int dtype, const float *demand_in, float *demand_out, float *lse_out,
+                 void *workspace, size_t workspace_bytes, void *hip_stream) {
   if (!q || !kcache || !vcache || !out) return ATTN_EINVAL;
   if (mode != ATTN_TEMPERED && mode != ATTN_DILUTION) return ATTN_EINVAL;
   if (mode == ATTN_TEMPERED && (demand_in || demand_out)) return ATTN_EINVAL;
@@ -301,8 +305,8 @@ int attn_prefill(const void *q, const void *kcache, const void *vcache, void *ou
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EINVAL;
   if (!std::isfinite(tau) || tau < 0.0f) return ATTN_EINVAL;
   if (!std::isfinite(eps) || eps < 0.0f) return ATTN_EINVAL;
-  if (d != attn::kHeadDim) return ATTN_ENOTSUP;
-  const void *ptrs[7] = {q, kcache, vcache, out, demand_in, demand_out, lse_out};
+  if (!head_dim_ok(d, dtype)) return ATTN_ENOTSUP;
+  const void *ptrs[8] = {q, kcache, vcache, out, demand_in, demand_out, lse_out, tau_bh};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return ATTN_EINVAL;
   const size_t BH = (size_t)B * H, esz = dtype == ATTN_BF16 ? 2 : 4;
@@ -322,6 +326,10 @@ int attn_prefill(const void *q, const void *kcache, const void *vcache, void *ou
   if (lse_out && demand_out && overlaps(lse_out, rbytes, demand_out, dbytes)) return ATTN_EINVAL;
   if (demand_in && lse_out && overlaps(demand_in, dbytes, lse_out, rbytes)) return ATTN_EINVAL;
   if (demand_in && overlaps(demand_in, dbytes, out, qbytes)) return ATTN_EINVAL;
+  const size_t tbytes = BH * sizeof(float);
+  if (tau_bh && (hits_tensor(tau_bh, tbytes) || (lse_out && overlaps(tau_bh, tbytes, lse_out, rbytes)) ||
+                 (demand_out && overlaps(tau_bh, tbytes, demand_out, dbytes))))
+    return ATTN_EINVAL;
   if (demand_in && demand_out && demand_in != demand_out &&
       overlaps(demand_in, dbytes, demand_out, dbytes))
     return ATTN_EINVAL;
@@ -337,6 +345,11 @@ int attn_prefill(const void *q, const void *kcache, const void *vcache, void *ou
   a.Tq = Tq;
   a.kstride = Lcap;
   a.vrow0 = attn::first_block_row(Tk, Tq);
+  if (tau_bh) {
+    // the kernels scale by tau_bh[bh] * log2(e) / sqrt(d)
+    a.tau_bh = tau_bh;
+    a.c2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
   const bool bf16 = dtype == ATTN_BF16;
   a.lse_nat = lse_out;
@@ -458,26 +471,27 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *out, const
 }
 
 size_t attn_decode_workspace_bytes(int S, int H, int Lcap, int d) {
-  if (S <= 0 || H <= 0 || Lcap <= 0 || d != attn::kHeadDim) return 0;
+  if (S <= 0 || H <= 0 || Lcap <= 0 || (d != 64 && d != 128)) return 0;
   DecWorkspace ws;
-  if (!dec_workspace(S, H, Lcap, &ws)) return 0;
+  if (!dec_workspace(S, H, Lcap, d, &ws)) return 0;
   return ws.total;
 }
 
-int attn_decode(const void *q, const void *kcache, const void *vcache, float *demand, void *out,
-                int S, int H, int Lcap, const int32_t *kv_len, int d, float tau, float eps,
-                int dtype, void *workspace, size_t workspace_bytes, void *hip_stream) {
+int attn_decode_ex(const void *q, const void *kcache, const void *vcache, float *demand, void *out,
+                   int S, int H, int Lcap, const int32_t *kv_len, int d, float tau,
+                   const float *tau_sh, float eps, int dtype, void *workspace,
+                   size_t workspace_bytes, void *hip_stream) {
   if (!q || !kcache || !vcache || !demand || !out) return ATTN_EINVAL;
   if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(demand) ||
-      !aligned16(out))
+      !aligned16(out) || (tau_sh && !aligned16(tau_sh)))
     return ATTN_EINVAL;
   if (S <= 0 || H <= 0 || Lcap <= 0) return ATTN_EINVAL;
   if (!std::isfinite(tau) || tau < 0.0f) return ATTN_EINVAL;
   if (!std::isfinite(eps) || eps < 0.0f) return ATTN_EINVAL;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EINVAL;
-  if (d != attn::kHeadDim || dtype != ATTN_BF16) return ATTN_ENOTSUP;
+  if ((d != 64 && d != 128) || dtype != ATTN_BF16) return ATTN_ENOTSUP;
   DecWorkspace ws;
-  if (!dec_workspace(S, H, Lcap, &ws)) return ATTN_EINVAL;
+  if (!dec_workspace(S, H, Lcap, d, &ws)) return ATTN_EINVAL;
   const size_t cache_bytes = (size_t)S * H * (size_t)Lcap * d * 2;
   const size_t out_bytes = (size_t)S * H * d * 2;
   const size_t dem_bytes = (size_t)S * H * (size_t)Lcap * 4;
@@ -485,6 +499,9 @@ int attn_decode(const void *q, const void *kcache, const void *vcache, float *de
       overlaps(out, out_bytes, demand, dem_bytes) || overlaps(out, out_bytes, q, out_bytes) ||
       overlaps(demand, dem_bytes, kcache, cache_bytes) ||
       overlaps(demand, dem_bytes, vcache, cache_bytes) || overlaps(demand, dem_bytes, q, out_bytes))
+    return ATTN_EINVAL;
+  const size_t tau_bytes = (size_t)S * H * 4;
+  if (tau_sh && (overlaps(tau_sh, tau_bytes, out, out_bytes) || overlaps(tau_sh, tau_bytes, demand, dem_bytes)))
     return ATTN_EINVAL;
   if (!workspace || workspace_bytes < ws.total || !aligned16(workspace)) return ATTN_EWORKSPACE;
   const int dev_status = check_device();
@@ -502,7 +519,11 @@ int attn_decode(const void *q, const void *kcache, const void *vcache, float *de
   a.Lcap = Lcap;
   a.splits = ws.splits;
   a.chunk = kDecChunk;
-  a.c2 = (float)((double)tau / std::sqrt((double)d) * 1.4426950408889634);
+  a.D = d;
+  a.tau_sh = tau_sh;
+  // logits in base 2: tau <q,k> / sqrt(d) * log2(e); with tau_sh the kernels
+  // multiply by tau_sh[s*H+h] themselves
+  a.c2 = (float)((tau_sh ? 1.0 : (double)tau) / std::sqrt((double)d) * 1.4426950408889634);
   a.eps = eps;
   char *wsp = static_cast<char *>(workspace);
   a.scores = reinterpret_cast<float *>(wsp);
@@ -510,6 +531,13 @@ int attn_decode(const void *q, const void *kcache, const void *vcache, float *de
   a.part_o = reinterpret_cast<float *>(wsp + ws.scores_bytes + ws.ml_bytes);
   hipError_t e = attn::launch_decode(a, reinterpret_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? ATTN_OK : fail_hip(e);
+}
+
+int attn_decode(const void *q, const void *kcache, const void *vcache, float *demand, void *out,
+                int S, int H, int Lcap, const int32_t *kv_len, int d, float tau, float eps,
+                int dtype, void *workspace, size_t workspace_bytes, void *hip_stream) {
+  return attn_decode_ex(q, kcache, vcache, demand, out, S, H, Lcap, kv_len, d, tau, nullptr, eps,
+                        dtype, workspace, workspace_bytes, hip_stream);
 }
 
 double attn_yarn_tau(double s) {
@@ -521,7 +549,9 @@ const char *attn_strerror(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_EINVAL: return "invalid argument";
-    case ATTN_ENOTSUP: return "unsupported (head dim must be 64, decode needs bf16, device must be gfx950)";
+    case ATTN_ENOTSUP:
+      return "unsupported (head dim 64, or 128 with bf16 storage; backward: 64 and bf16; decode: bf16; "
+             "device must be gfx950)";
     case ATTN_EWORKSPACE: return "workspace missing, misaligned or too small";
     case ATTN_EHIP: return g_hip_error;
     default: return "unknown status";

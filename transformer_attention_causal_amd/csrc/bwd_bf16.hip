@@ -759,6 +759,7 @@ hipError_t launch_bwd_bf16(int mode, const BwdArgs &a, hipStream_t s) {
     f.cin = a.cin;
     f.BH = a.BH;
     f.T = f.Tq = f.kstride = a.T;
+    f.D = kHeadDim;
     f.c2 = a.c2;
     f.eps = a.eps;
     e = launch_colsum_bf16(f, s);
@@ -774,6 +775,7 @@ hipError_t launch_bwd_bf16(int mode, const BwdArgs &a, hipStream_t s) {
     t.out = a.pk;
     t.BH = a.BH;
     t.T = t.Tq = t.kstride = a.T;
+    t.D = kHeadDim;
     t.c2 = a.c2;
     e = launch_rows_bf16(kRowTempered, t, s);
     if (e != hipSuccess) return e;

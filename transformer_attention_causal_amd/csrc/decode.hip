@@ -13,8 +13,9 @@
 //   dec_share_v  : global log-sum-exp from the partials, p_j, share_j, the
 //                  in-place demand update, and partial (sum share v, sum share)
 //   dec_combine  : out = sum of partial numerators / sum of partial row sums
-// Loads are 16 bytes per lane; eight lanes cover one 128-byte key row, so one
-// wave instruction reads eight consecutive rows (1 KB, fully coalesced).  The
+// Loads are 16 bytes per lane; d/8 lanes cover one key row (128 bytes at
+// d = 64, 256 at d = 128), so one wave instruction reads 1 KB of consecutive
+// rows, fully coalesced, and d/8 such loads bring 64 keys per wave.  The
 // caches are read exactly once per step, so they stream with non-temporal
 // loads (measured on MI355X: ~7.1 TB/s against ~6.3 TB/s for ordinary loads).
 #include "attn_common.hpp"
@@ -25,7 +26,6 @@
 namespace attn {
 
 constexpr int kDecThreads = 256;
-constexpr int kDecUnroll = 8;  // 16-byte loads in flight per lane
 
 __device__ __forceinline__ int visible_keys(const int32_t *kv_len, int s, int Lcap) {
   if (!kv_len) return Lcap;
@@ -47,7 +47,17 @@ __device__ __forceinline__ float dot8_bf16(const u32x4 &kw, const u32x4 &qw) {
   return acc;
 }
 
+// Lane geometry for head dimension D: kLanes lanes (one 16-byte chunk each)
+// per key row, kRows rows per wave instruction.
+template <int D>
+struct DecGeom {
+  static constexpr int kLanes = D / 8;
+  static constexpr int kRows = 64 / kLanes;
+};
+
+template <int D>
 __global__ void __launch_bounds__(kDecThreads) dec_scores(DecodeArgs a) {
+  using G = DecGeom<D>;
   __shared__ float sm[kDecThreads / 64], sl[kDecThreads / 64];
   const int split = blockIdx.x % a.splits;
   const int sh = blockIdx.x / a.splits;
@@ -55,39 +65,41 @@ __global__ void __launch_bounds__(kDecThreads) dec_scores(DecodeArgs a) {
   const int L = visible_keys(a.kv_len, seq, a.Lcap);
   const int c0 = split * a.chunk, c1 = min(c0 + a.chunk, L);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int slot = lane >> 3, dc = lane & 7;
+  const int slot = lane / G::kLanes, dc = lane % G::kLanes;
+  const float c2 = a.tau_sh ? a.tau_sh[sh] * a.c2 : a.c2;
 
   const u32x4 qw = *reinterpret_cast<const u32x4 *>(
-      reinterpret_cast<const __bf16 *>(a.q) + (size_t)sh * kHeadDim + 8 * dc);
-  const __bf16 *K = reinterpret_cast<const __bf16 *>(a.kc) + (size_t)sh * a.Lcap * kHeadDim;
+      reinterpret_cast<const __bf16 *>(a.q) + (size_t)sh * D + 8 * dc);
+  const __bf16 *K = reinterpret_cast<const __bf16 *>(a.kc) + (size_t)sh * a.Lcap * D;
   float *S = a.scores + (size_t)sh * a.Lcap;
   float m = -INFINITY, l = 0.0f;
 
   // Each wave-iteration covers 64 consecutive keys: load u brings keys
-  // base + 8u + slot (8 lanes each).  After the dot products every lane keeps
-  // the score of key base + 8 dc + slot, so the 64 lanes hold 64 distinct keys.
-  constexpr int kWaveKeys = 8 * kDecUnroll;
+  // base + kRows u + slot (kLanes lanes each).  After the dot products every
+  // lane keeps the score of key base + kRows dc + slot, so the 64 lanes hold
+  // 64 distinct keys.
+  constexpr int kU = G::kLanes;            // loads in flight per lane
+  constexpr int kWaveKeys = G::kRows * kU;  // = 64
   for (int base = c0 + w * kWaveKeys; base < c1; base += (kDecThreads / 64) * kWaveKeys) {
-    u32x4 kw[kDecUnroll];
+    u32x4 kw[kU];
 #pragma unroll
-    for (int u = 0; u < kDecUnroll; ++u) {
-      const int j = base + 8 * u + slot;
+    for (int u = 0; u < kU; ++u) {
+      const int j = base + G::kRows * u + slot;
       kw[u] = (j < c1) ? __builtin_nontemporal_load(
-                             reinterpret_cast<const u32x4 *>(K + (size_t)j * kHeadDim + 8 * dc))
+                             reinterpret_cast<const u32x4 *>(K + (size_t)j * D + 8 * dc))
                        : u32x4{0u, 0u, 0u, 0u};
     }
     float mine = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kDecUnroll; ++u) {
+    for (int u = 0; u < kU; ++u) {
       float s = dot8_bf16(kw[u], qw);
-      s += __shfl_xor(s, 1, 8);
-      s += __shfl_xor(s, 2, 8);
-      s += __shfl_xor(s, 4, 8);
+#pragma unroll
+      for (int off = 1; off < G::kLanes; off <<= 1) s += __shfl_xor(s, off, G::kLanes);
       mine = (dc == u) ? s : mine;
     }
-    const int j = base + 8 * dc + slot;
+    const int j = base + G::kRows * dc + slot;
     if (j < c1) {
-      const float x = mine * a.c2;   // log2-domain logit
+      const float x = mine * c2;   // log2-domain logit
       S[j] = x;
       const float m_new = fmaxf(m, x);
       l = l * fast_exp2(m - m_new) + fast_exp2(x - m_new);
@@ -116,16 +128,18 @@ __global__ void __launch_bounds__(kDecThreads) dec_scores(DecodeArgs a) {
   }
 }
 
+template <int D>
 __global__ void __launch_bounds__(kDecThreads) dec_share_v(DecodeArgs a) {
+  using G = DecGeom<D>;
   __shared__ float sShare[kDecThreads / 64][64];
-  __shared__ float sO[kDecThreads / 64][kHeadDim + 1];
+  __shared__ float sO[kDecThreads / 64][D + 1];
   const int split = blockIdx.x % a.splits;
   const int sh = blockIdx.x / a.splits;
   const int seq = sh / a.H;
   const int L = visible_keys(a.kv_len, seq, a.Lcap);
   const int c0 = split * a.chunk, c1 = min(c0 + a.chunk, L);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int slot = lane >> 3, dc = lane & 7;
+  const int slot = lane / G::kLanes, dc = lane % G::kLanes;
 
   // log-sum-exp of this query's scores over all chunks (fixed order)
   float M = -INFINITY, Ls = 0.0f;
@@ -139,9 +153,9 @@ __global__ void __launch_bounds__(kDecThreads) dec_share_v(DecodeArgs a) {
   const float lse2 = M + __builtin_log2f(Ls);
   const float eps_floor = fmaxf(a.eps, FLT_MIN);
 
-  const __bf16 *Vc = reinterpret_cast<const __bf16 *>(a.vc) + (size_t)sh * a.Lcap * kHeadDim;
+  const __bf16 *Vc = reinterpret_cast<const __bf16 *>(a.vc) + (size_t)sh * a.Lcap * D;
   const float *S = a.scores + (size_t)sh * a.Lcap;
-  float *D = a.demand + (size_t)sh * a.Lcap;
+  float *Dm = a.demand + (size_t)sh * a.Lcap;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float rsum = 0.0f;
 
@@ -151,25 +165,25 @@ __global__ void __launch_bounds__(kDecThreads) dec_share_v(DecodeArgs a) {
     float share = 0.0f;
     if (j < c1) {
       const float p = fast_exp2(S[j] - lse2);
-      const float dj = D[j];
+      const float dj = Dm[j];
       share = p * fast_rcp(fmaxf(dj + p + a.eps, eps_floor));
-      D[j] = dj + p;
+      Dm[j] = dj + p;
     }
     rsum += share;
     sShare[w][lane] = share;
-    // eight lanes per key row for the values
-    u32x4 vw[8];
+    // kLanes lanes per key row for the values
+    u32x4 vw[G::kLanes];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int jj = base + 8 * u + slot;
+    for (int u = 0; u < G::kLanes; ++u) {
+      const int jj = base + G::kRows * u + slot;
       vw[u] = (jj < c1) ? __builtin_nontemporal_load(
-                              reinterpret_cast<const u32x4 *>(Vc + (size_t)jj * kHeadDim + 8 * dc))
+                              reinterpret_cast<const u32x4 *>(Vc + (size_t)jj * D + 8 * dc))
                         : u32x4{0u, 0u, 0u, 0u};
     }
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float sj = sShare[w][8 * u + slot];
+    for (int u = 0; u < G::kLanes; ++u) {
+      const float sj = sShare[w][G::kRows * u + slot];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[2 * i] = __builtin_fmaf(sj, bf16_lo(vw[u][i]), acc[2 * i]);
@@ -178,50 +192,59 @@ __global__ void __launch_bounds__(kDecThreads) dec_share_v(DecodeArgs a) {
     }
     __builtin_amdgcn_wave_barrier();
   }
-  // reduce over the 8 key slots of the wave (lanes with equal dc), then waves
+  // reduce over the key slots of the wave (lanes with equal dc), then waves
 #pragma unroll
-  for (int off = 8; off < 64; off <<= 1) {
+  for (int off = G::kLanes; off < 64; off <<= 1) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
   }
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) rsum += __shfl_xor(rsum, off, 64);
-  if (lane < 8) {
+  if (lane < G::kLanes) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) sO[w][8 * dc + e] = acc[e];
   }
-  if (lane == 0) sO[w][kHeadDim] = rsum;
+  if (lane == 0) sO[w][D] = rsum;
   __syncthreads();
-  if (tid <= kHeadDim) {
+  if (tid <= D) {
     float v = 0.0f;
     for (int i = 0; i < kDecThreads / 64; ++i) v += sO[i][tid];
-    a.part_o[((size_t)sh * a.splits + split) * (kHeadDim + 1) + tid] = v;
+    a.part_o[((size_t)sh * a.splits + split) * (D + 1) + tid] = v;
   }
 }
 
+// One thread per output element; 128 threads cover 128/D (sequence, head) pairs.
+template <int D>
 __global__ void __launch_bounds__(128) dec_combine(DecodeArgs a) {
-  const int sh = blockIdx.x * 2 + (threadIdx.x >> 6);
-  const int d = threadIdx.x & 63;
+  const int sh = blockIdx.x * (128 / D) + threadIdx.x / D;
+  const int d = threadIdx.x % D;
   if (sh >= a.S * a.H) return;
   float num = 0.0f, den = 0.0f;
   for (int i = 0; i < a.splits; ++i) {
-    const float *po = a.part_o + ((size_t)sh * a.splits + i) * (kHeadDim + 1);
+    const float *po = a.part_o + ((size_t)sh * a.splits + i) * (D + 1);
     num += po[d];
-    den += po[kHeadDim];
+    den += po[D];
   }
-  reinterpret_cast<__bf16 *>(a.out)[(size_t)sh * kHeadDim + d] = (__bf16)(num / den);
+  reinterpret_cast<__bf16 *>(a.out)[(size_t)sh * D + d] = (__bf16)(num / den);
+}
+
+template <int D>
+static hipError_t launch_decode_d(const DecodeArgs &a, hipStream_t s) {
+  const unsigned nwg = (unsigned)(a.S * a.H * a.splits);
+  hipLaunchKernelGGL(dec_scores<D>, dim3(nwg), dim3(kDecThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dec_share_v<D>, dim3(nwg), dim3(kDecThreads), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int kPer = 128 / D;
+  hipLaunchKernelGGL(dec_combine<D>, dim3((unsigned)((a.S * a.H + kPer - 1) / kPer)), dim3(128), 0, s,
+                     a);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
-  const unsigned nwg = (unsigned)(a.S * a.H * a.splits);
-  hipLaunchKernelGGL(dec_scores, dim3(nwg), dim3(kDecThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dec_share_v, dim3(nwg), dim3(kDecThreads), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dec_combine, dim3((unsigned)((a.S * a.H + 1) / 2)), dim3(128), 0, s, a);
-  return hipGetLastError();
+  return a.D == 128 ? launch_decode_d<128>(a, s) : launch_decode_d<64>(a, s);
 }
 
 }  // namespace attn

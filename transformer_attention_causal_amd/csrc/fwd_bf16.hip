@@ -20,8 +20,8 @@
 //  * row kernels: a workgroup owns 128 query rows, wave w the 32 rows
 //    [q0+32w, q0+32w+32); K and V stream through LDS in 64-key tiles (double
 //    buffered, one barrier per tile).  Scores of a 32x32 (key, query) block
-//    come from four 32x32x16 bf16 MFMAs over d = 64; a 64-key tile is two such
-//    blocks, handled together.  Only the one tile holding a wave's diagonal
+//    come from d/16 32x32x16 bf16 MFMAs (head dimension d = 64 or 128); a
+//    64-key tile is two such blocks, handled together.  Only the one tile holding a wave's diagonal
 //    applies the causal mask.
 //  * tempered / pass 1 keep scores as S^T (lane = query, 16 keys in
 //    registers), so row maxima and sums are in-lane plus one exchange between
@@ -49,8 +49,9 @@ constexpr float kRescaleSlack = 8.0f;      // log2 units the running max may lag
 constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64: largest tile sum kept
 
 // Per-wave state of the row kernels.
+template <int D>
 struct RowState {
-  f32x16 o0, o1;   // O^T[d][query]: d in [0,32) and [32,64)
+  f32x16 o[Geom<D>::kOBlocks];   // O^T[d][query]: o[i] holds d in [32i, 32i+32)
   float m_run;     // running max of the scaled logits (log2 units)
   float l_run;     // fp32 row sum of exp2(x - m_run) over this half's keys (kernels
                    // that output the log-sum-exp)
@@ -60,8 +61,8 @@ struct RowState {
 
 // Bring the running max up to the tile's (masked) maximum and rescale what
 // has been accumulated against the old one.
-template <int MODE, bool FP32SUM, bool DIAG>
-__device__ __forceinline__ void st_rescale(RowState &st, const f32x16 *s, int qrel, int h,
+template <int MODE, bool FP32SUM, bool DIAG, int D>
+__device__ __forceinline__ void st_rescale(RowState<D> &st, const f32x16 *s, int qrel, int h,
                                            float c2) {
   float tmax = -INFINITY;
 #pragma unroll
@@ -79,10 +80,9 @@ __device__ __forceinline__ void st_rescale(RowState &st, const f32x16 *s, int qr
   else st.lsum *= alpha;
   if constexpr (MODE == kRowTempered) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      st.o0[r] *= alpha;
-      st.o1[r] *= alpha;
-    }
+    for (int i = 0; i < Geom<D>::kOBlocks; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[i][r] *= alpha;
   }
   st.m_run = m_new;
 }
@@ -109,15 +109,15 @@ __device__ __forceinline__ void st_weights(const f32x16 *s, float m_run, int qre
 // bf16; an overflow or the first tile, where m_run = -inf, shows up there as
 // inf).  Otherwise the tile max is taken first and m_run moves when it is
 // exceeded by more than kRescaleSlack.
-template <int MODE, bool FP32SUM, bool DIAG>
-__device__ __forceinline__ void st_tile(RowState &st, const bf16x8 *qf, const bf16x8 &sel,
+template <int MODE, bool FP32SUM, bool DIAG, int D>
+__device__ __forceinline__ void st_tile(RowState<D> &st, const bf16x8 *qf, const bf16x8 &sel,
                                         const __bf16 *kt_lds, const __bf16 *vt_lds, int kb,
                                         int qw0, int l32, int h, float c2) {
   f32x16 s[2] = {zero16(), zero16()};
-  const __bf16 *krow0 = kt_lds + l32 * kKRow;
-  const __bf16 *krow1 = kt_lds + (32 + l32) * kKRow;
+  const __bf16 *krow0 = kt_lds + l32 * Geom<D>::kKRow;
+  const __bf16 *krow1 = kt_lds + (32 + l32) * Geom<D>::kKRow;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < Geom<D>::kChunks; ++c) {
     s[0] = mfma32(lds_frag(krow0, c, h), qf[c], s[0]);
     s[1] = mfma32(lds_frag(krow1, c, h), qf[c], s[1]);
   }
@@ -130,7 +130,7 @@ __device__ __forceinline__ void st_tile(RowState &st, const bf16x8 *qf, const bf
 #pragma unroll
     for (int i = 0; i < 32; ++i) ts += p[i];
     if (__ballot(!(ts <= kSumLimit)) != 0ull) {
-      st_rescale<MODE, FP32SUM, DIAG>(st, s, qrel, h, c2);
+      st_rescale<MODE, FP32SUM, DIAG, D>(st, s, qrel, h, c2);
       st_weights<DIAG>(s, st.m_run, qrel, h, c2, p);
       ts = 0.0f;
 #pragma unroll
@@ -140,7 +140,7 @@ __device__ __forceinline__ void st_tile(RowState &st, const bf16x8 *qf, const bf
     if constexpr (MODE == kRowTempered) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        pv_update(st.o0, st.o1, vt_lds, t, l32, h, pack8(p + 16 * t), pack8(p + 16 * t + 8));
+        pv_update_d<D>(st.o, vt_lds, t, l32, h, pack8(p + 16 * t), pack8(p + 16 * t + 8));
     }
   } else {
     float tmax = -INFINITY;
@@ -154,7 +154,7 @@ __device__ __forceinline__ void st_tile(RowState &st, const bf16x8 *qf, const bf
     }
     tmax = both_halves_max(tmax);
     if (__ballot(tmax * c2 > st.m_run + kRescaleSlack) != 0ull)
-      st_rescale<MODE, FP32SUM, DIAG>(st, s, qrel, h, c2);
+      st_rescale<MODE, FP32SUM, DIAG, D>(st, s, qrel, h, c2);
     const float mneg = -st.m_run;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -168,7 +168,7 @@ __device__ __forceinline__ void st_tile(RowState &st, const bf16x8 *qf, const bf
       const bf16x8 pf0 = pack8(p), pf1 = pack8(p + 8);
       st.lsum = mfma16(sel, pf0, st.lsum);
       st.lsum = mfma16(sel, pf1, st.lsum);
-      if constexpr (MODE == kRowTempered) pv_update(st.o0, st.o1, vt_lds, t, l32, h, pf0, pf1);
+      if constexpr (MODE == kRowTempered) pv_update_d<D>(st.o, vt_lds, t, l32, h, pf0, pf1);
     }
   }
 }
@@ -211,13 +211,16 @@ __device__ __forceinline__ ShareConsts share_consts(int l32, int h) {
 //           committed + eps enters as its stored bf16 (hi, lo) pair);
 //       P = the bids themselves.
 //  3. share = P / D, the row sums, and share @ V on the matrix cores.
-template <bool DIAG>
+// lseq: the lse2 of the lane's 16 queries in accumulator order (registers),
+// or with LDS_LSE the wave's 32 row values in row order (LDS).
+template <bool DIAG, bool LDS_LSE = false>
 __device__ __forceinline__ void share_bids(const f32x16 &s, const float *lseq, int krel, int h,
                                            float c2, bf16x8 &pa0, bf16x8 &pa1) {
   float p[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    float e = fast_exp2(__builtin_fmaf(s[r], c2, -lseq[r]));
+    const float l = LDS_LSE ? lseq[acc_row(r, h)] : lseq[r];
+    float e = fast_exp2(__builtin_fmaf(s[r], c2, -l));
     if (DIAG && acc_row(r, h) < krel) e = 0.0f;
     p[r] = e;
   }
@@ -245,9 +248,9 @@ __device__ __forceinline__ void share_values(const f32x16 &d, const f32x16 &pt, 
   sf1 = pack8(sh + 8);
 }
 
-template <bool DIAG>
-__device__ __forceinline__ void share_tile(RowState &st, const bf16x8 *qf, const float *lseq,
-                                           const ShareConsts &sc, const bf16x8 &sel,
+template <bool DIAG, int D>
+__device__ __forceinline__ void share_tile(RowState<D> &st, const bf16x8 *qf, const float *lseq,
+                                           const ShareConsts &sc_, const bf16x8 &sel,
                                            const uint32_t *base,
                                            const __bf16 *kt_lds, const __bf16 *vt_lds, int kb,
                                            int qw0, int l32, int h, float c2) {
@@ -257,54 +260,70 @@ __device__ __forceinline__ void share_tile(RowState &st, const bf16x8 *qf, const
   //   scores 0,1 | bids 0 | prefix 0, bids 1 | prefix 1, shares 0 |
   //   P@V 0, shares 1 | P@V 1
   // sub-tile t, lane: key kb + 32t + l32; element r: query qw0 + acc_row(r, h)
-  const __bf16 *krow0 = kt_lds + l32 * kKRow;
-  const __bf16 *krow1 = kt_lds + (32 + l32) * kKRow;
+  const __bf16 *krow0 = kt_lds + l32 * Geom<D>::kKRow;
+  const __bf16 *krow1 = kt_lds + (32 + l32) * Geom<D>::kKRow;
+  const int krel0 = kb + l32 - qw0;   // key visible to rows with acc_row >= krel
+  if constexpr (D > 64) {
+    // d = 128: one sub-tile after the other, so that only one sub-tile's
+    // scores, prefix and shares are live at a time; the row LSEs are read
+    // from LDS (lseq: the wave's 32 rows)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const __bf16 *krow = t == 0 ? krow0 : krow1;
+      f32x16 sc = zero16();
+#pragma unroll
+      for (int c = 0; c < Geom<D>::kChunks; ++c) sc = mfma32(qf[c], lds_frag(krow, c, h), sc);
+      bf16x8 pa0, pa1, sf0, sf1;
+      share_bids<DIAG, true>(sc, lseq, krel0 + 32 * t, h, c2, pa0, pa1);
+      f32x16 dd, pt;
+      share_prefix(pa0, pa1, base[t], sc_, dd, pt);
+      share_values(dd, pt, sf0, sf1);
+      st.lsum = mfma16(sel, sf0, st.lsum);
+      st.lsum = mfma16(sel, sf1, st.lsum);
+      pv_update_d<D>(st.o, vt_lds, t, l32, h, sf0, sf1);
+    }
+    return;
+  }
   f32x16 s0 = zero16(), s1 = zero16();
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < Geom<D>::kChunks; ++c) {
     s0 = mfma32(qf[c], lds_frag(krow0, c, h), s0);
     s1 = mfma32(qf[c], lds_frag(krow1, c, h), s1);
   }
-  const int krel0 = kb + l32 - qw0;   // key visible to rows with acc_row >= krel
   bf16x8 pa00, pa01, pa10, pa11;
   share_bids<DIAG>(s0, lseq, krel0, h, c2, pa00, pa01);
   // sub-tile t transposed, lane: query qw0 + l32; element r: key kb + 32t + acc_row(r, h)
   f32x16 d0, pt0, d1, pt1;
-  share_prefix(pa00, pa01, base[0], sc, d0, pt0);
+  share_prefix(pa00, pa01, base[0], sc_, d0, pt0);
   share_bids<DIAG>(s1, lseq, krel0 + 32, h, c2, pa10, pa11);
-  share_prefix(pa10, pa11, base[1], sc, d1, pt1);
+  share_prefix(pa10, pa11, base[1], sc_, d1, pt1);
   bf16x8 sf00, sf01, sf10, sf11;
   share_values(d0, pt0, sf00, sf01);
   st.lsum = mfma16(sel, sf00, st.lsum);
   st.lsum = mfma16(sel, sf01, st.lsum);
-  pv_update(st.o0, st.o1, vt_lds, 0, l32, h, sf00, sf01);
+  pv_update_d<D>(st.o, vt_lds, 0, l32, h, sf00, sf01);
   share_values(d1, pt1, sf10, sf11);
   st.lsum = mfma16(sel, sf10, st.lsum);
   st.lsum = mfma16(sel, sf11, st.lsum);
-  pv_update(st.o0, st.o1, vt_lds, 1, l32, h, sf10, sf11);
-#ifdef ATTN_SHARE_SCHED
-  // issue pattern for the tile: one matrix-core op, then vector ops
-#pragma unroll
-  for (int i = 0; i < 30; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, ATTN_SHARE_SCHED, 0);
-  }
-#endif
+  pv_update_d<D>(st.o, vt_lds, 1, l32, h, sf10, sf11);
 }
 
 // Waves per SIMD each mode is compiled for (register budget 512/n per lane).
-template <int MODE>
+template <int MODE, int D>
 struct RowOccupancy {
-  static constexpr int value = MODE == kRowLse ? 4 : (MODE == kRowShare ? 2 : 3);
+  static constexpr int value =
+      MODE == kRowLse ? (D > 64 ? 3 : 4) : (MODE == kRowShare || D > 64 ? 2 : 3);
 };
 
 // FP32SUM: row sums in fp32 on the vector ALUs (exact log-sum-exp output);
 // otherwise on the matrix cores over the bf16 weights.
-template <int MODE, bool FP32SUM>
-__global__ void __launch_bounds__(256, RowOccupancy<MODE>::value) rows_bf16_kernel(FwdArgs a, int nqb) {
+template <int MODE, bool FP32SUM, int D>
+__global__ void __launch_bounds__(256, (RowOccupancy<MODE, D>::value))
+    rows_bf16_kernel(FwdArgs a, int nqb) {
+  using G = Geom<D>;
   constexpr bool kNeedV = (MODE != kRowLse);
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2 * kKTile];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[kNeedV ? 2 * kVTile : 8];
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2 * G::kKTile];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[kNeedV ? 2 * G::kVTile : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
@@ -322,7 +341,8 @@ __global__ void __launch_bounds__(256, RowOccupancy<MODE>::value) rows_bf16_kern
   const int qw0 = q0 + 32 * w;              // first position of this wave
   const bool wave_live = qw0 < T && qw0 + 32 > P;
   const int kd = qw0 / kBN;                 // the tile holding this wave's diagonal
-  const size_t qhead = (size_t)bh * Tq * kHeadDim, khead = (size_t)bh * a.kstride * kHeadDim;
+  const size_t qhead = (size_t)bh * Tq * D, khead = (size_t)bh * a.kstride * D;
+  const float c2 = head_c2(a, bh);
   const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + qhead;
   const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + khead;
   const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + khead;
@@ -332,69 +352,80 @@ __global__ void __launch_bounds__(256, RowOccupancy<MODE>::value) rows_bf16_kern
 
   // Q fragments: lane holds Q[qw0 + l32][16c + 8h .. +8) -- usable as the B
   // operand of S^T = K Q^T and as the A operand of S = Q K^T.
-  bf16x8 qf[4];
+  bf16x8 qf[G::kChunks];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-    qf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(Q, qw0 + l32 - P, Tq, 2 * c + h));
+  for (int c = 0; c < G::kChunks; ++c)
+    qf[c] = __builtin_bit_cast(bf16x8, load_row_chunk<D>(Q, qw0 + l32 - P, Tq, 2 * c + h));
 
   // tile loaders: K as [key][d] rows; V transposed to [d][key] on the way in.
   // Buffer loads with per-lane byte offsets fixed for the whole loop; keys
-  // past the end of the sequence read as zeros.
-  u32x4 kreg[2], vreg[2];
-  const uint32_t koff0 = 16u * tid, koff1 = 16u * (tid + 256);
-  const uint32_t voff0 = 256u * (tid & 31) + 16u * (tid >> 5), voff1 = voff0 + 128u;
+  // past the end of the sequence read as zeros.  Each thread moves D/32
+  // 16-byte chunks of K and D/64 (row pair, d-chunk) items of V per tile.
+  constexpr int kRowBytes = 2 * D, kRowChunks = D / 8;
+  constexpr int kKL = D / 32, kVI = D / 64;
+  u32x4 kreg[kKL], vreg[2 * kVI];
   auto load_tile = [&](int kt) {
     const int key0 = kt * kBN;                          // < T for every tile loaded
-    const int bytes = (T - key0) * (kHeadDim * 2);
-    const auto rk = make_rsrc(K + (size_t)key0 * kHeadDim, bytes);
-    kreg[0] = buf_load16(rk, koff0);
-    kreg[1] = buf_load16(rk, koff1);
+    const int bytes = (T - key0) * kRowBytes;
+    const auto rk = make_rsrc(K + (size_t)key0 * D, bytes);
+#pragma unroll
+    for (int i = 0; i < kKL; ++i) kreg[i] = buf_load16(rk, 16u * (tid + 256 * i));
     if constexpr (kNeedV) {
-      const auto rv = make_rsrc(V + (size_t)key0 * kHeadDim, bytes);
-      vreg[0] = buf_load16(rv, voff0);
-      vreg[1] = buf_load16(rv, voff1);
+      const auto rv = make_rsrc(V + (size_t)key0 * D, bytes);
+#pragma unroll
+      for (int i = 0; i < kVI; ++i) {
+        const int u = tid + 256 * i, kp = u & 31, dc = u >> 5;
+        const uint32_t off = 2u * kRowBytes * kp + 16u * dc;
+        vreg[2 * i] = buf_load16(rv, off);
+        vreg[2 * i + 1] = buf_load16(rv, off + kRowBytes);
+      }
     }
   };
   auto store_tile = [&](int buf) {
-    __bf16 *k = sK + buf * kKTile;
+    __bf16 *k = sK + buf * G::kKTile;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kKL; ++i) {
       const int u = tid + 256 * i;
-      *reinterpret_cast<u32x4 *>(k + (u >> 3) * kKRow + (u & 7) * 8) = kreg[i];
+      *reinterpret_cast<u32x4 *>(k + (u / kRowChunks) * G::kKRow + (u % kRowChunks) * 8) = kreg[i];
     }
     if constexpr (kNeedV) {
-      __bf16 *vt = sV + buf * kVTile;
-      const int kp = tid & 31, dc = tid >> 5;
+      __bf16 *vt = sV + buf * G::kVTile;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t a0 = vreg[0][i], a1 = vreg[1][i];
-        const uint32_t even = __builtin_amdgcn_perm(a1, a0, 0x05040100u);  // d = 8dc + 2i
-        const uint32_t odd = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // d = 8dc + 2i + 1
-        *reinterpret_cast<uint32_t *>(vt + (8 * dc + 2 * i) * kVRow + 2 * kp) = even;
-        *reinterpret_cast<uint32_t *>(vt + (8 * dc + 2 * i + 1) * kVRow + 2 * kp) = odd;
+      for (int i = 0; i < kVI; ++i) {
+        const int u = tid + 256 * i;
+        store_rows_transposed(vt, kVRow, u & 31, u >> 5, vreg[2 * i], vreg[2 * i + 1]);
       }
     }
   };
 
-  RowState st;
-  st.o0 = zero16();
-  st.o1 = zero16();
+  RowState<D> st;
+#pragma unroll
+  for (int i = 0; i < G::kOBlocks; ++i) st.o[i] = zero16();
   st.m_run = -INFINITY;
   st.l_run = 0.0f;
   st.lsum = zero4();
   const bf16x8 sel = rowsum_selector(lane);
 
-  float lseq[16];      // pass 2b: lse2 of this lane's 16 query rows (kNoRow for no row)
+  // pass 2b: lse2 of this lane's 16 query rows (kNoRow for no row); at d = 128
+  // the wave's 32 values sit in LDS instead
+  constexpr bool kLdsLse = D > 64;
+  float lseq[kLdsLse ? 1 : 16];
+  __shared__ float sLse[MODE == kRowShare && kLdsLse ? kBM : 1];
   ShareConsts sc;      // pass 2b: constant operands of the prefix and transpose
   const uint32_t *cin_blk = nullptr;
   uint32_t cin_next[2] = {0u, 0u};
   // committed + eps of a key no earlier row sees (on and past the diagonal)
   const uint32_t eps_word = split2_bf16(fmaxf(a.eps, FLT_MIN));
   if constexpr (MODE == kRowShare) {
+    if constexpr (kLdsLse) {
+      const int lr = qw0 + l32 - P;
+      if (h == 0) sLse[32 * w + l32] = (unsigned)lr < (unsigned)Tq ? a.lse2[(size_t)bh * Tq + lr] : kNoRow;
+    } else {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int lr = qw0 + acc_row(r, h) - P;
-      lseq[r] = (unsigned)lr < (unsigned)Tq ? a.lse2[(size_t)bh * Tq + lr] : kNoRow;
+      for (int r = 0; r < 16; ++r) {
+        const int lr = qw0 + acc_row(r, h) - P;
+        lseq[r] = (unsigned)lr < (unsigned)Tq ? a.lse2[(size_t)bh * Tq + lr] : kNoRow;
+      }
     }
     sc = share_consts(l32, h);
     cin_blk = reinterpret_cast<const uint32_t *>(a.cin) + (size_t)bh * cin_floats_per_head(T, a.vrow0) +
@@ -434,16 +465,17 @@ __global__ void __launch_bounds__(256, RowOccupancy<MODE>::value) rows_bf16_kern
       load_tile(kt + 1);
       if constexpr (MODE == kRowShare) load_cin(kt + 1);
     }
-    const __bf16 *kt_lds = sK + buf * kKTile;
-    const __bf16 *vt_lds = sV + (kNeedV ? buf * kVTile : 0);
+    const __bf16 *kt_lds = sK + buf * G::kKTile;
+    const __bf16 *vt_lds = sV + (kNeedV ? buf * G::kVTile : 0);
     const int kb = kt * kBN;
     if (wave_live && kt <= kd) {
       if constexpr (MODE == kRowShare) {
-        if (kt < kd) share_tile<false>(st, qf, lseq, sc, sel, base, kt_lds, vt_lds, kb, qw0, l32, h, a.c2);
-        else share_tile<true>(st, qf, lseq, sc, sel, base, kt_lds, vt_lds, kb, qw0, l32, h, a.c2);
+        const float *lsrc = kLdsLse ? sLse + 32 * w : lseq;
+        if (kt < kd) share_tile<false, D>(st, qf, lsrc, sc, sel, base, kt_lds, vt_lds, kb, qw0, l32, h, c2);
+        else share_tile<true, D>(st, qf, lsrc, sc, sel, base, kt_lds, vt_lds, kb, qw0, l32, h, c2);
       } else {
-        if (kt < kd) st_tile<MODE, FP32SUM, false>(st, qf, sel, kt_lds, vt_lds, kb, qw0, l32, h, a.c2);
-        else st_tile<MODE, FP32SUM, true>(st, qf, sel, kt_lds, vt_lds, kb, qw0, l32, h, a.c2);
+        if (kt < kd) st_tile<MODE, FP32SUM, false, D>(st, qf, sel, kt_lds, vt_lds, kb, qw0, l32, h, c2);
+        else st_tile<MODE, FP32SUM, true, D>(st, qf, sel, kt_lds, vt_lds, kb, qw0, l32, h, c2);
       }
     }
     if (kt + 1 < nkt) store_tile(buf ^ 1);
@@ -466,17 +498,16 @@ __global__ void __launch_bounds__(256, RowOccupancy<MODE>::value) rows_bf16_kern
   if constexpr (MODE != kRowLse) {
     if (row_ok) {
       const float inv = 1.0f / denom;
-      __bf16 *O = reinterpret_cast<__bf16 *>(a.out) + qhead + (size_t)lr * kHeadDim;
+      __bf16 *O = reinterpret_cast<__bf16 *>(a.out) + qhead + (size_t)lr * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 8 * g + 4 * h;
-        u32x2 lo, hi;
-        lo[0] = pack_bf16x2(st.o0[4 * g] * inv, st.o0[4 * g + 1] * inv);
-        lo[1] = pack_bf16x2(st.o0[4 * g + 2] * inv, st.o0[4 * g + 3] * inv);
-        hi[0] = pack_bf16x2(st.o1[4 * g] * inv, st.o1[4 * g + 1] * inv);
-        hi[1] = pack_bf16x2(st.o1[4 * g + 2] * inv, st.o1[4 * g + 3] * inv);
-        *reinterpret_cast<u32x2 *>(O + d0) = lo;
-        *reinterpret_cast<u32x2 *>(O + 32 + d0) = hi;
+      for (int i = 0; i < G::kOBlocks; ++i) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2 w;
+          w[0] = pack_bf16x2(st.o[i][4 * g] * inv, st.o[i][4 * g + 1] * inv);
+          w[1] = pack_bf16x2(st.o[i][4 * g + 2] * inv, st.o[i][4 * g + 3] * inv);
+          *reinterpret_cast<u32x2 *>(O + 32 * i + 8 * g + 4 * h) = w;
+        }
       }
     }
   }
@@ -502,8 +533,10 @@ __device__ __forceinline__ float colsum_bids(const f32x16 &sc, int l32, int h) {
   return part;
 }
 
+template <int D>
 __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, int nqs) {
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[2][kCQ * kKRow];
+  using G = Geom<D>;
+  __shared__ __attribute__((aligned(16))) __bf16 sQ[2][kCQ * G::kKRow];
   __shared__ __attribute__((aligned(16))) float sL[2][kCQ];
 
   const int tid = threadIdx.x;
@@ -516,17 +549,19 @@ __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, in
   const int kw0 = kb * kCB + 32 * w;          // first key of this wave
   const bool wave_live = kw0 < T;
   const int key = kw0 + l32;
-  const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + (size_t)bh * Tq * kHeadDim;
-  const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + (size_t)bh * a.kstride * kHeadDim;
+  const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + (size_t)bh * Tq * D;
+  const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + (size_t)bh * a.kstride * D;
+  const float c2 = head_c2(a, bh);
   const float *L2 = a.lse2 + (size_t)bh * Tq;
   // committed demand + eps of each (32-row block, key), stored as a bf16 pair
   uint32_t *cin = reinterpret_cast<uint32_t *>(a.cin) + (size_t)bh * cin_floats_per_head(T, a.vrow0);
   const float eps_floor = fmaxf(a.eps, FLT_MIN);
   auto committed_word = [&](float total) { return split2_bf16(fmaxf(total + a.eps, eps_floor)); };
 
-  bf16x8 kf[4];
+  bf16x8 kf[G::kChunks];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) kf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(K, key, T, 2 * c + h));
+  for (int c = 0; c < G::kChunks; ++c)
+    kf[c] = __builtin_bit_cast(bf16x8, load_row_chunk<D>(K, key, T, 2 * c + h));
   // demand this half-lane's rows have put on `key` so far; the lower half
   // starts from the demand committed before position P
   float run = 0.0f;
@@ -536,17 +571,18 @@ __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, in
 
   const int qt0 = max(kb * kCB, a.vrow0) / kCQ;   // first 64-row query tile
   const int nqt = (T + kCQ - 1) / kCQ;
-  u32x4 qreg[2];
+  constexpr int kQL = D / 32, kRowChunks = D / 8;   // 16-byte Q loads per thread per tile
+  u32x4 qreg[kQL];
   float lreg = 0.0f;
   bool lvalid = false;
   auto load_q = [&](int qt) {
     // rows lr0.. of Q; only a chunk's first tiles start before row 0 (lr0 < 0),
     // and their lanes for positions before P get an offset past the range
     const int lr0 = qt * kCQ - P, b0 = max(lr0, 0);   // b0 < Tq for every tile loaded
-    const auto rq = make_rsrc(Q + (size_t)b0 * kHeadDim, (Tq - b0) * (kHeadDim * 2));
-    const int sh = (lr0 - b0) * (kHeadDim * 2);       // <= 0
+    const auto rq = make_rsrc(Q + (size_t)b0 * D, (Tq - b0) * (D * 2));
+    const int sh = (lr0 - b0) * (D * 2);              // <= 0
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kQL; ++i) {
       const int off = 16 * (tid + 256 * i) + sh;
       qreg[i] = buf_load16(rq, off < 0 ? kNoOffset : (uint32_t)off);
     }
@@ -558,9 +594,9 @@ __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, in
   };
   auto store_q = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kQL; ++i) {
       const int u = tid + 256 * i;
-      *reinterpret_cast<u32x4 *>(&sQ[buf][(u >> 3) * kKRow + (u & 7) * 8]) = qreg[i];
+      *reinterpret_cast<u32x4 *>(&sQ[buf][(u / kRowChunks) * G::kKRow + (u % kRowChunks) * 8]) = qreg[i];
     }
     if (tid < kCQ) sL[buf][tid] = lvalid ? -lreg : -kNoRow;   // no row: bids nothing
   };
@@ -570,9 +606,9 @@ __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, in
   // (element r: query acc_row(r, h)).
   auto block_scores = [&](int buf, int sb) {
     f32x16 sc = zero16();
-    const __bf16 *qrow = &sQ[buf][(32 * sb + l32) * kKRow];
+    const __bf16 *qrow = &sQ[buf][(32 * sb + l32) * G::kKRow];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < G::kChunks; ++c) {
       const bf16x8 qa = lds_frag(qrow, c, h);
       sc = mfma32(qa, kf[c], sc);
     }
@@ -580,7 +616,7 @@ __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, in
     for (int g = 0; g < 4; ++g) {
       const f32x4 nl = *reinterpret_cast<const f32x4 *>(&sL[buf][32 * sb + 8 * g + 4 * h]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[4 * g + i] = __builtin_fmaf(sc[4 * g + i], a.c2, nl[i]);
+      for (int i = 0; i < 4; ++i) sc[4 * g + i] = __builtin_fmaf(sc[4 * g + i], c2, nl[i]);
     }
     return sc;
   };
@@ -630,27 +666,39 @@ __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, in
   }
 }
 
-hipError_t launch_rows_bf16(int mode, const FwdArgs &a, hipStream_t s) {
-  const int nqb = (a.T + kBM - 1) / kBM - a.vrow0 / kBM;   // blocks from position vrow0
+template <int D>
+static void launch_rows_d(int mode, const FwdArgs &a, int nqb, hipStream_t s) {
   dim3 grid((unsigned)(nqb * a.BH)), block(256);
   switch (mode) {
     case kRowTempered:
       // an exact log-sum-exp output needs fp32 row sums
       if (a.lse2 || a.lse_nat)
-        hipLaunchKernelGGL((rows_bf16_kernel<kRowTempered, true>), grid, block, 0, s, a, nqb);
+        hipLaunchKernelGGL((rows_bf16_kernel<kRowTempered, true, D>), grid, block, 0, s, a, nqb);
       else
-        hipLaunchKernelGGL((rows_bf16_kernel<kRowTempered, false>), grid, block, 0, s, a, nqb);
+        hipLaunchKernelGGL((rows_bf16_kernel<kRowTempered, false, D>), grid, block, 0, s, a, nqb);
       break;
-    case kRowLse: hipLaunchKernelGGL((rows_bf16_kernel<kRowLse, true>), grid, block, 0, s, a, nqb); break;
-    default: hipLaunchKernelGGL((rows_bf16_kernel<kRowShare, false>), grid, block, 0, s, a, nqb); break;
+    case kRowLse:
+      hipLaunchKernelGGL((rows_bf16_kernel<kRowLse, true, D>), grid, block, 0, s, a, nqb);
+      break;
+    default:
+      hipLaunchKernelGGL((rows_bf16_kernel<kRowShare, false, D>), grid, block, 0, s, a, nqb);
+      break;
   }
+}
+
+hipError_t launch_rows_bf16(int mode, const FwdArgs &a, hipStream_t s) {
+  const int nqb = (a.T + kBM - 1) / kBM - a.vrow0 / kBM;   // blocks from position vrow0
+  if (a.D == 128) launch_rows_d<128>(mode, a, nqb, s);
+  else launch_rows_d<64>(mode, a, nqb, s);
   return hipGetLastError();
 }
 
 hipError_t launch_colsum_bf16(const FwdArgs &a, hipStream_t s) {
   const int nkb = (a.T + kCB - 1) / kCB;
   const int nqs = (a.T + 31) / 32;
-  hipLaunchKernelGGL(colsum_bf16_kernel, dim3((unsigned)(nkb * a.BH)), dim3(256), 0, s, a, nkb, nqs);
+  const dim3 grid((unsigned)(nkb * a.BH)), block(256);
+  if (a.D == 128) hipLaunchKernelGGL(colsum_bf16_kernel<128>, grid, block, 0, s, a, nkb, nqs);
+  else hipLaunchKernelGGL(colsum_bf16_kernel<64>, grid, block, 0, s, a, nkb, nqs);
   return hipGetLastError();
 }
 

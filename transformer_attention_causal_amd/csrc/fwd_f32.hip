@@ -35,6 +35,7 @@ __global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
   const int li = i - P;  // and its query row
   const bool live = (unsigned)li < (unsigned)Tq;
   const size_t qhead = (size_t)bh * Tq * kHeadDim, khead = (size_t)bh * a.kstride * kHeadDim;
+  const float c2 = head_c2(a, bh);
   const float *Q = reinterpret_cast<const float *>(a.q) + qhead;
   const float *K = reinterpret_cast<const float *>(a.k) + khead;
   const float *V = reinterpret_cast<const float *>(a.v) + khead;
@@ -72,7 +73,7 @@ __global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
       const bool vis = (j <= i) && live;
       if constexpr (MODE == kRowTempered || MODE == kRowLse) {
         if (vis) {
-          const float x = s * a.c2;
+          const float x = s * c2;
           const float m_new = fmaxf(m, x);
           const float alpha = exp2f(m - m_new);
           const float p = exp2f(x - m_new);
@@ -84,7 +85,7 @@ __global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
           m = m_new;
         }
       } else {
-        const float p = vis ? exp2f(__builtin_fmaf(s, a.c2, -lse2)) : 0.0f;
+        const float p = vis ? exp2f(__builtin_fmaf(s, c2, -lse2)) : 0.0f;
         // inclusive prefix of the bids over the 32 rows of this lane's block
         float incl = p;
 #pragma unroll
@@ -131,6 +132,7 @@ __global__ void __launch_bounds__(64) colsum_f32_kernel(FwdArgs a, int nkb) {
   const int j = k0 + t;  // this lane's key column
   const float *Q = reinterpret_cast<const float *>(a.q) + (size_t)bh * Tq * kHeadDim;
   const float *K = reinterpret_cast<const float *>(a.k) + (size_t)bh * a.kstride * kHeadDim;
+  const float c2 = head_c2(a, bh);
   float *cin = a.cin + (size_t)bh * cin_floats_per_head(T, a.vrow0);
 
   float kv[kHeadDim];
@@ -154,7 +156,7 @@ __global__ void __launch_bounds__(64) colsum_f32_kernel(FwdArgs a, int nkb) {
       float s = 0.0f;
 #pragma unroll
       for (int e = 0; e < kHeadDim; ++e) s = __builtin_fmaf(sQ[ii * kHeadDim + e], kv[e], s);
-      if (j <= i && i >= P) run += exp2f(__builtin_fmaf(s, a.c2, -sL[ii]));
+      if (j <= i && i >= P) run += exp2f(__builtin_fmaf(s, c2, -sL[ii]));
     }
   }
   if (a.demand_out && j < T) a.demand_out[(size_t)bh * a.kstride + j] = run;

@@ -7,7 +7,7 @@
 
 namespace attn {
 
-constexpr int kHeadDim = 64;  // the head dimension every kernel is built for
+constexpr int kHeadDim = 64;  // the head dimension of the fp32 path and the backward
 
 // Row-major passes over the causal score matrix (one workgroup per query
 // block).  lse2 is the log2-domain log-sum-exp of each row.
@@ -32,9 +32,17 @@ struct FwdArgs {
   int kstride;          // rows per head of K, V and the demand arrays (>= T)
   int vrow0;            // first position the row kernels cover: T - Tq rounded
                         // down to a multiple of 128 (0 for a whole prefill)
-  float c2;             // tau / sqrt(d) * log2(e)
+  int D;                // head dimension: 64 (both storage types) or 128 (bf16)
+  const float *tau_bh;  // [BH] per-(batch, head) multipliers, or NULL
+  float c2;             // tau / sqrt(d) * log2(e); with tau_bh: log2(e) / sqrt(d),
+                        // and head bh uses tau_bh[bh] * c2
   float eps;
 };
+
+// The logit scale (log2 units) of head bh.
+__device__ __forceinline__ float head_c2(const FwdArgs &a, int bh) {
+  return a.tau_bh ? a.tau_bh[bh] * a.c2 : a.c2;
+}
 
 // First position the row kernels cover for keys 0..T-1 and Tq query rows at
 // positions T-Tq..T-1: the first row's position rounded down to the largest
@@ -90,11 +98,13 @@ struct DecodeArgs {
   float *demand;
   void *out;
   const int32_t *kv_len;
+  const float *tau_sh;   // [S*H] per-(sequence, head) multipliers, or NULL
   int S, H, Lcap, splits, chunk;
-  float c2, eps;
+  int D;                 // head dimension: 64 or 128
+  float c2, eps;         // c2: tau / sqrt(d) * log2(e), or log2(e) / sqrt(d) with tau_sh
   float *scores;   // [S*H*Lcap]
   float *part_ml;  // [S*H*splits*2]  (max, sum) in log2 domain
-  float *part_o;   // [S*H*splits*(64+1)]
+  float *part_o;   // [S*H*splits*(D+1)]
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);

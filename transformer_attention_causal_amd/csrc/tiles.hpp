@@ -3,24 +3,36 @@
 #pragma once
 
 #include "attn_common.hpp"
+#include "launch.hpp"
 
 namespace attn {
 
 constexpr int kBN = 64;         // keys per LDS tile (row kernels)
-constexpr int kKRow = 72;       // LDS row stride of K tiles, bf16 (64 + 8 pad)
 constexpr int kVRow = 68;       // LDS row stride of V^T tiles, bf16 (64 keys + 4 pad)
-constexpr int kKTile = kBN * kKRow;        // bf16 elements per K buffer
-constexpr int kVTile = kHeadDim * kVRow;   // bf16 elements per V^T buffer
-constexpr float kNoRow = 1e30f;            // log-sum-exp given to rows past the end
+constexpr float kNoRow = 1e30f;            // log-sum-exp given to positions with no row
+
+// LDS tile geometry for head dimension D (64 or 128).
+template <int D>
+struct Geom {
+  static constexpr int kKRow = D + 8;          // K / Q rows in LDS: D bf16 + 8 pad
+  static constexpr int kKTile = kBN * kKRow;   // bf16 elements per K buffer
+  static constexpr int kVTile = D * kVRow;     // bf16 elements per V^T buffer
+  static constexpr int kChunks = D / 16;       // 32x32x16 MFMA steps over d
+  static constexpr int kOBlocks = D / 32;      // 32-row blocks of O^T
+};
+constexpr int kKRow = Geom<64>::kKRow;
+constexpr int kKTile = Geom<64>::kKTile;
+constexpr int kVTile = Geom<64>::kVTile;
 
 // Query index (within a wave's 32 rows) of accumulator element r in lane half h.
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-// Load one 16-byte chunk of row `row` of a [T][64] bf16 array; zeros for rows
+// Load one 16-byte chunk of row `row` of a [T][D] bf16 array; zeros for rows
 // outside [0, T).
+template <int D = kHeadDim>
 __device__ __forceinline__ u32x4 load_row_chunk(const __bf16 *base, int row, int T, int chunk) {
   u32x4 z = {0u, 0u, 0u, 0u};
-  if ((unsigned)row < (unsigned)T) z = *reinterpret_cast<const u32x4 *>(base + (size_t)row * kHeadDim + chunk * 8);
+  if ((unsigned)row < (unsigned)T) z = *reinterpret_cast<const u32x4 *>(base + (size_t)row * D + chunk * 8);
   return z;
 }
 
@@ -41,9 +53,23 @@ __device__ __forceinline__ bf16x8 pack8(const float *v) {
   return to_bf16x8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
 }
 
-// O^T[d][query] += V^T[d][keys of sub-tile t] * P^T[keys][query] for both
-// 32-row halves of d.  pf0/pf1 hold keys 0..15 / 16..31 of the sub-tile in
-// the accumulator-layout order.
+// O^T[d][query] += V^T[d][keys of sub-tile t] * P^T[keys][query] for every
+// 32-row block o[i] of d.  pf0/pf1 hold keys 0..15 / 16..31 of the sub-tile
+// in the accumulator-layout order.
+template <int D>
+__device__ __forceinline__ void pv_update_d(f32x16 *o, const __bf16 *vt_lds, int t, int l32, int h,
+                                            const bf16x8 &pf0, const bf16x8 &pf1) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int i = 0; i < Geom<D>::kOBlocks; ++i) {
+      const __bf16 *vr = vt_lds + (32 * i + l32) * kVRow + 32 * t;
+      o[i] = mfma32(lds_vfrag(vr, c, h), c == 0 ? pf0 : pf1, o[i]);
+    }
+  }
+}
+
+// The d = 64 form with the two blocks of O^T held separately.
 __device__ __forceinline__ void pv_update(f32x16 &o0, f32x16 &o1, const __bf16 *vt_lds, int t,
                                           int l32, int h, const bf16x8 &pf0, const bf16x8 &pf1) {
   const __bf16 *v0 = vt_lds + l32 * kVRow + 32 * t;

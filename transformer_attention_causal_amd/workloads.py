@@ -13,6 +13,10 @@ fp32, then -- for bf16 storage -- to bf16 with round-to-nearest-even):
 * ``heavy_frac`` > 0: per (b,h), in order, round(heavy_frac*T) distinct key
   positions are drawn without replacement and those K rows are multiplied by
   ``heavy_scale`` (5 % of keys with 3x norm concentrate demand).
+* Learned temperatures (head dimension 128): per (b,h) a temperature
+  t ~ U[tau_min, tau_max] = U[5, 10] (the clip range the focal page settles
+  on) is drawn from its own stream, and the kernels get the multiplier
+  tau = sqrt(d) / t.
 * Decode: the initial demand D0[s,h,pos] ~ U[0, 4 (L-pos)/L] (fp64 draw,
   stored fp32); the per-step queries are N(0,1) bf16, drawn as one
   [steps,S,H,d] block from their own seed.  Caches too large to draw on the
@@ -95,6 +99,10 @@ PREFILL = {
     "long_t128k": Prefill("long_t128k", 1, 16, 131072, 64, "bf16", seed=20264,
                           heavy_frac=0.05, yarn_s=8.0,
                           note="8x the training context; oracle on head 0"),
+    "focal_d128_t16k": Prefill("focal_d128_t16k", 1, 20, 16384, 128, "bf16", seed=20266,
+                               heavy_frac=0.05,
+                               note="2.7B focal model's attention shape (20 heads of 128) at "
+                                    "16K, per-head learned temperatures"),
 }
 
 DECODE = {
@@ -143,6 +151,15 @@ def draw_qkv(B: int, H: int, T: int, d: int, dtype: str, seed: int, scale: float
     if dtype == "bf16":
         q, k, v = bf16_round_bits(q), bf16_round_bits(k), bf16_round_bits(v)
     return HostInputs(q, k, v, dtype, heavy)
+
+
+def learned_tau(B: int, H: int, d: int, seed: int, t_min: float = 5.0,
+                t_max: float = 10.0) -> np.ndarray:
+    """Per-(b,h) multipliers sqrt(d)/t with t ~ U[t_min, t_max], fp32 [B,H]
+    (stream seed+37)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 37))
+    t = rng.uniform(t_min, t_max, size=(B, H))
+    return (math.sqrt(d) / t).astype(np.float32)
 
 
 def draw_grad(B: int, H: int, T: int, d: int, seed: int) -> np.ndarray:
