@@ -13,7 +13,13 @@ One step runs the whole path once over resident synthetic inputs:
 After the timed steps, the exact backward of both operators (attn_bwd, from
 the forward's saved out / lse / row sums and a synthetic dO) is timed the same
 way and reported under ``components`` at 10*d flops per causal pair (the
-usual 2.5x of the forward's 4*d).
+usual 2.5x of the forward's 4*d).  Then, also under ``components``:
+  * chunked prefill: the same 16K dilution forward run as 8 chunks of 2048
+    rows through attn_prefill, the demand carried in place between chunks;
+  * head dimension 128: dilution and tempered forward at B=1, H=20,
+    T=16384, d=128 (a 2.7B focal model's attention) with per-head learned
+    temperature multipliers, and one decode step over a 32-sequence x
+    32768-key cache at H=20, d=128 with per-(sequence, head) multipliers.
 
 Printed: one JSON line.  ``value`` is the dilution forward's algorithmic
 TFLOP/s (4*d flops per causal (query, key) pair: q.k and the weighted v, once)
@@ -50,7 +56,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E peak
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_dilution_t16k_decode_32k.md")
 CSRC = os.path.join(ROOT, "transformer_attention_causal_amd", "csrc")
-FWD_SOURCES = ("attn_common.hpp", "launch.hpp", "fwd_bf16.hip")
+FWD_SOURCES = ("attn_common.hpp", "launch.hpp", "tiles.hpp", "fwd_bf16.hip")
 DEC_SOURCES = ("attn_common.hpp", "launch.hpp", "decode.hip")
 
 
@@ -218,6 +224,95 @@ def main():
               "tempered_bwd": float(np.mean([e[1].elapsed_time(e[2]) for e in bevs]))}
     log("bench: backward ms " + json.dumps({n: round(x, 4) for n, x in bwd_ms.items()}))
     del bws, grads
+
+    def time_launches(fn, n_marks):
+        """Mean ms between consecutive marks of ``fn(events)`` over the timed
+        iterations (warm-up iterations first)."""
+        for _ in range(args.warmup):
+            fn(None)
+        evs_ = [[torch.cuda.Event(enable_timing=True) for _ in range(n_marks)]
+                for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            fn(evs_[i])
+        torch.cuda.synchronize()
+        return [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs_]))
+                for j in range(n_marks - 1)]
+
+    # ------------------------------------------------------- chunked prefill
+    chunk = 2048
+    dem_c = torch.zeros((w.B, w.H, w.T), dtype=torch.float32, device=dev)
+    pws_need = [ab.attn_prefill_workspace_bytes(w.B, w.H, chunk, e, w.d, 1, 1)
+                for e in range(chunk, w.T + 1, chunk)]
+    pws = torch.empty(max(pws_need), dtype=torch.uint8, device=dev)
+    q_chunks = [q[:, :, a:a + chunk].contiguous() for a in range(0, w.T, chunk)]
+    out_c = torch.empty_like(q_chunks[0])
+
+    def chunked(events):
+        if events is not None:
+            events[0].record(stream)
+        dem_c.zero_()
+        for c, qc in enumerate(q_chunks):
+            ab.prefill(qc, k, v, (c + 1) * chunk, tau=1.0, mode=ab.ATTN_DILUTION, eps=w.eps,
+                       demand_in=dem_c, demand_out=dem_c, out=out_c, workspace=pws)
+        if events is not None:
+            events[1].record(stream)
+
+    chunk_ms = time_launches(chunked, 2)[0]
+    log(f"bench: chunked prefill ({w.T // chunk} x {chunk} rows) {chunk_ms:.4f} ms")
+    del pws, q_chunks, out_c, dem_c
+
+    # ------------------------------------------------------ head dimension 128
+    from transformer_attention_causal_amd.workloads import learned_tau
+
+    w8 = PREFILL["focal_d128_t16k"]
+    log(f"bench: drawing {w8.name} inputs B={w8.B} H={w8.H} T={w8.T} d={w8.d}")
+    inp8 = prefill_inputs(w8)
+    q8, k8, v8 = dev_bf16(inp8.q), dev_bf16(inp8.k), dev_bf16(inp8.v)
+    del inp8
+    tau8 = torch.from_numpy(learned_tau(w8.B, w8.H, w8.d, seed=w8.seed)).to(dev)
+    out8 = torch.empty_like(q8)
+    ws8 = torch.empty(ab.attn_prefill_workspace_bytes(w8.B, w8.H, w8.T, w8.T, w8.d, 1, 1),
+                      dtype=torch.uint8, device=dev)
+
+    def d128(events):
+        if events is not None:
+            events[0].record(stream)
+        ab.prefill(q8, k8, v8, w8.T, tau=1.0, mode=ab.ATTN_DILUTION, eps=w8.eps, out=out8,
+                   workspace=ws8, tau_bh=tau8)
+        if events is not None:
+            events[1].record(stream)
+        ab.prefill(q8, k8, v8, w8.T, tau=1.0, mode=ab.ATTN_TEMPERED, out=out8, tau_bh=tau8)
+        if events is not None:
+            events[2].record(stream)
+
+    d128_ms = time_launches(d128, 3)
+    log(f"bench: d=128 forward ms dilution {d128_ms[0]:.4f} tempered {d128_ms[1]:.4f}")
+    del q8, k8, v8, out8, ws8
+
+    S8, H8, L8 = 32, 20, 32768
+    kc8, vc8 = decode_cache_device(S8, H8, L8, 128, dw.seed + 1, device=dev)
+    dem8 = torch.from_numpy(decode_initial_demand(S8, H8, L8, dw.seed + 1)).to(dev)
+    qs8 = dev_bf16(decode_queries(dw.steps, S8, H8, 128, dw.seed + 1))
+    tsh8 = torch.from_numpy(learned_tau(S8, H8, 128, seed=dw.seed + 1)).to(dev)
+    dws8, _ = ab.decode_workspace(S8, H8, L8, dev, 128)
+    dout8 = torch.empty((S8, H8, 128), dtype=torch.bfloat16, device=dev)
+    dstep = [0]
+
+    def dec128(events):
+        if events is not None:
+            events[0].record(stream)
+        ab.decode(qs8[dstep[0] % dw.steps], kc8, vc8, dem8, tau=1.0, eps=dw.eps, out=dout8,
+                  workspace=dws8, tau_sh=tsh8)
+        dstep[0] += 1
+        if events is not None:
+            events[1].record(stream)
+
+    dec8_ms = time_launches(dec128, 2)[0]
+    dec8_bytes = (2.0 * S8 * H8 * L8 * 128 * 2 + 2.0 * S8 * H8 * L8 * 4 + 2.0 * S8 * H8 * 128 * 2)
+    log(f"bench: d=128 decode step {dec8_ms:.4f} ms")
+    del kc8, vc8, dem8, dws8
+
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -240,6 +335,7 @@ def main():
                  + 2.0 * dw.S * dw.H * dw.d * 2)            # query in, output out
     dec_gbps = dec_bytes / (ms["decode"] * 1e-3) / 1e9
     shares_tflops = flops / (ms["dil_shares"] * 1e-3) / 1e12
+    flops8 = 4.0 * w8.d * causal_pairs(w8.B, w8.H, w8.T)
 
     result = {
         "metric": METRIC,
@@ -274,6 +370,20 @@ def main():
                              "tflops": round(2.5 * flops / (bwd_ms["dilution_bwd"] * 1e-3) / 1e12, 3)},
             "tempered_bwd": {"ms": round(bwd_ms["tempered_bwd"], 4),
                              "tflops": round(2.5 * flops / (bwd_ms["tempered_bwd"] * 1e-3) / 1e12, 3)},
+            "dilution_chunked_prefill": {
+                "chunks": w.T // chunk, "rows_per_chunk": chunk, "ms": round(chunk_ms, 4),
+                "tflops": round(flops / (chunk_ms * 1e-3) / 1e12, 3),
+                "vs_whole_prefill": round(dil_ms / chunk_ms, 4)},
+            "focal_d128_t16k": {
+                "B": w8.B, "H": w8.H, "T": w8.T, "d": w8.d, "tau": "per head, sqrt(d)/U[5,10]",
+                "dilution_ms": round(d128_ms[0], 4),
+                "dilution_tflops": round(flops8 / (d128_ms[0] * 1e-3) / 1e12, 3),
+                "tempered_ms": round(d128_ms[1], 4),
+                "tempered_tflops": round(flops8 / (d128_ms[1] * 1e-3) / 1e12, 3)},
+            "decode_d128_32k": {
+                "S": S8, "H": H8, "L": L8, "d": 128, "ms": round(dec8_ms, 4),
+                "gbps": round(dec8_bytes / (dec8_ms * 1e-3) / 1e9, 2), "bytes": dec8_bytes,
+                "frac_of_hbm_peak": round(dec8_bytes / (dec8_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
         },
         "roofline": {
             "bound": "mfma",
