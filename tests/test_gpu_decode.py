@@ -20,7 +20,7 @@ def _host_bits(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("L", [1, 5, 64, 1000, 2048, 2049, 5000])
+@pytest.mark.parametrize("L", [1, 5, 64, 1000, 2048, 2049, 5000, 32768, 32769])
 def test_decode_small_matches_oracle(L):
     import torch
 

@@ -7,8 +7,10 @@
 //   share_j = p_j / (D_j + p_j + eps),  out = sum_j share_j v_j / sum_j share_j,
 //   then D_j += p_j in place (the bid, not the share).
 //
-// The step streams K once and V once, so it is bound by HBM bandwidth.  Keys
-// of a (sequence, head) are split into chunks, one workgroup each:
+// The step streams K once and V once, so it is bound by HBM bandwidth.  For
+// caches of up to 32768 keys one workgroup per (sequence, head) does the whole
+// step with the scores in LDS (dec_fused).  Longer caches split the keys of a
+// (sequence, head) into chunks, one workgroup each:
 //   dec_scores   : s_j (kept in fp32 scratch) and a partial (max, sum exp)
 //   dec_share_v  : global log-sum-exp from the partials, p_j, share_j, the
 //                  in-place demand update, and partial (sum share v, sum share)
@@ -228,8 +230,163 @@ __global__ void __launch_bounds__(128) dec_combine(DecodeArgs a) {
   reinterpret_cast<__bf16 *>(a.out)[(size_t)sh * D + d] = (__bf16)(num / den);
 }
 
+// ------------------------------------------------------------ fused form
+//
+// Caches of up to kFusedKeys keys: one workgroup per (sequence, head) keeps
+// every score in LDS, so K and V are each streamed once and
+// nothing else touches HBM but the demand.  Three phases, separated by
+// workgroup barriers: scores (and their maximum) from K; the log-sum-exp from
+// the scores in LDS; then bids, shares, the demand update and share @ V from
+// V.  Reductions run in a fixed order.
+
+constexpr int kFusedKeys = 32768;
+
+// 16 waves at d = 64; 8 at d = 128, whose 16 loads in flight per lane need
+// the larger register budget.  Either way 128 KB of loads are in flight per
+// workgroup.
+template <int D>
+struct FusedGeom {
+  static constexpr int kThreads = D > 64 ? 512 : 1024;
+  static constexpr int kWaves = kThreads / 64;
+};
+
+template <int D>
+__global__ void __launch_bounds__(FusedGeom<D>::kThreads) dec_fused(DecodeArgs a) {
+  using G = DecGeom<D>;
+  constexpr int kFusedThreads = FusedGeom<D>::kThreads, kFusedWaves = FusedGeom<D>::kWaves;
+  __shared__ float sS[kFusedKeys];
+  __shared__ float sRed[kFusedWaves];
+  __shared__ float sShare[kFusedWaves][64];
+  const int sh = blockIdx.x;
+  const int seq = sh / a.H;
+  const int L = visible_keys(a.kv_len, seq, a.Lcap);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int slot = lane / G::kLanes, dc = lane % G::kLanes;
+  const float c2 = a.tau_sh ? a.tau_sh[sh] * a.c2 : a.c2;
+  const u32x4 qw = *reinterpret_cast<const u32x4 *>(
+      reinterpret_cast<const __bf16 *>(a.q) + (size_t)sh * D + 8 * dc);
+  const __bf16 *K = reinterpret_cast<const __bf16 *>(a.kc) + (size_t)sh * a.Lcap * D;
+  const __bf16 *Vc = reinterpret_cast<const __bf16 *>(a.vc) + (size_t)sh * a.Lcap * D;
+  float *Dm = a.demand + (size_t)sh * a.Lcap;
+  constexpr int kU = G::kLanes;
+  constexpr int kStride = 64 * kFusedWaves;   // keys per workgroup iteration
+
+  // phase 1: scores (log2 domain) into LDS and their maximum
+  float m = -INFINITY;
+  for (int base = 64 * w; base < L; base += kStride) {
+    u32x4 kw[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int j = base + G::kRows * u + slot;
+      kw[u] = (j < L) ? __builtin_nontemporal_load(
+                            reinterpret_cast<const u32x4 *>(K + (size_t)j * D + 8 * dc))
+                      : u32x4{0u, 0u, 0u, 0u};
+    }
+    float mine = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      float sc = dot8_bf16(kw[u], qw);
+#pragma unroll
+      for (int off = 1; off < G::kLanes; off <<= 1) sc += __shfl_xor(sc, off, G::kLanes);
+      mine = (dc == u) ? sc : mine;
+    }
+    const int j = base + G::kRows * dc + slot;
+    if (j < L) {
+      const float x = mine * c2;
+      sS[j] = x;
+      m = fmaxf(m, x);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if (lane == 0) sRed[w] = m;
+  __syncthreads();
+  float M = sRed[0];
+#pragma unroll
+  for (int i = 1; i < kFusedWaves; ++i) M = fmaxf(M, sRed[i]);
+  __syncthreads();   // every wave has read sRed before it is reused
+
+  // phase 2: sum of exp2(s - M) over the scores in LDS
+  float l = 0.0f;
+  for (int j = tid; j < L; j += kFusedThreads) l += fast_exp2(sS[j] - M);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off, 64);
+  if (lane == 0) sRed[w] = l;
+  __syncthreads();
+  float Ls = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kFusedWaves; ++i) Ls += sRed[i];
+  const float lse2 = M + __builtin_log2f(Ls);
+  const float eps_floor = fmaxf(a.eps, FLT_MIN);
+
+  // phase 3: bids, shares and the demand update (one lane per key), then
+  // share @ V with kLanes lanes per value row
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float rsum = 0.0f;
+  for (int base = 64 * w; base < L; base += kStride) {
+    const int j = base + lane;
+    float share = 0.0f;
+    if (j < L) {
+      const float p = fast_exp2(sS[j] - lse2);
+      const float dj = Dm[j];
+      share = p * fast_rcp(fmaxf(dj + p + a.eps, eps_floor));
+      Dm[j] = dj + p;
+    }
+    rsum += share;
+    sShare[w][lane] = share;
+    u32x4 vw[G::kLanes];
+#pragma unroll
+    for (int u = 0; u < G::kLanes; ++u) {
+      const int jj = base + G::kRows * u + slot;
+      vw[u] = (jj < L) ? __builtin_nontemporal_load(
+                             reinterpret_cast<const u32x4 *>(Vc + (size_t)jj * D + 8 * dc))
+                       : u32x4{0u, 0u, 0u, 0u};
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < G::kLanes; ++u) {
+      const float sj = sShare[w][G::kRows * u + slot];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = __builtin_fmaf(sj, bf16_lo(vw[u][i]), acc[2 * i]);
+        acc[2 * i + 1] = __builtin_fmaf(sj, bf16_hi(vw[u][i]), acc[2 * i + 1]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+#pragma unroll
+  for (int off = G::kLanes; off < 64; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) rsum += __shfl_xor(rsum, off, 64);
+  __syncthreads();   // the scores are no longer needed: sS holds the partials
+  float *sO = sS;    // [kFusedWaves][D + 1]
+  if (lane < G::kLanes) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sO[w * (D + 1) + 8 * dc + e] = acc[e];
+  }
+  if (lane == 0) sO[w * (D + 1) + D] = rsum;
+  __syncthreads();
+  if (tid < D) {
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kFusedWaves; ++i) {
+      num += sO[i * (D + 1) + tid];
+      den += sO[i * (D + 1) + D];
+    }
+    reinterpret_cast<__bf16 *>(a.out)[(size_t)sh * D + tid] = (__bf16)(num / den);
+  }
+}
+
 template <int D>
 static hipError_t launch_decode_d(const DecodeArgs &a, hipStream_t s) {
+  if (a.Lcap <= kFusedKeys) {
+    hipLaunchKernelGGL(dec_fused<D>, dim3((unsigned)(a.S * a.H)), dim3(FusedGeom<D>::kThreads), 0,
+                       s, a);
+    return hipGetLastError();
+  }
   const unsigned nwg = (unsigned)(a.S * a.H * a.splits);
   hipLaunchKernelGGL(dec_scores<D>, dim3(nwg), dim3(kDecThreads), 0, s, a);
   hipError_t e = hipGetLastError();
