@@ -191,9 +191,10 @@ __device__ __forceinline__ void col_terms(const f32x16 &s, const f32x16 &da, con
   }
 }
 
-// Pass 3: sums of g over the blocks below each block, walking up.
+// Pass 3: sums of g over the blocks below each block, walking up two 32-row
+// blocks (one 64-row LDS tile) per barrier.
 __global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdArgs a, int nqs) {
-  __shared__ __attribute__((aligned(16))) ColBlock sb[2];
+  __shared__ __attribute__((aligned(16))) ColBlock sb[2][2];
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int bh = blockIdx.x % a.BH;
@@ -223,55 +224,70 @@ __global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdArgs a, int nqs) {
   const ScanConsts sc = scan_consts(l32, h);
   __builtin_amdgcn_s_waitcnt(0);
 
-  const int qs_lo = (kb * kColKeys) / 32;   // first block that sees a key of this workgroup
-  u32x4 qreg, greg;
+  // walk pairs of 32-row blocks (2P, 2P + 1), last pair first
+  const int qs_lo = (kb * kColKeys) / 32;
+  const int p_lo = qs_lo / 2, p_hi = (nqs - 1) / 2;
+  u32x4 qreg[2], greg[2];
   float lreg = 0.0f, ireg = 0.0f, rreg = 0.0f;
-  auto load_block = [&](int qs) {           // 32 qs < T for every block loaded
-    const int row0 = 32 * qs;
+  auto load_pair = [&](int P) {             // 64 P < T for every pair loaded
+    const int row0 = 64 * P;
     const int bytes = (T - row0) * (kHeadDim * 2);
-    qreg = buf_load16(make_rsrc(Q + (size_t)row0 * kHeadDim, bytes), 16u * tid);
-    greg = buf_load16(make_rsrc(G + (size_t)row0 * kHeadDim, bytes), 16u * tid);
-    if (tid < 32) {
+    const auto rq = make_rsrc(Q + (size_t)row0 * kHeadDim, bytes);
+    const auto rg = make_rsrc(G + (size_t)row0 * kHeadDim, bytes);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      qreg[i] = buf_load16(rq, 16u * (tid + 256 * i));
+      greg[i] = buf_load16(rg, 16u * (tid + 256 * i));
+    }
+    if (tid < 64) {
       const int row = row0 + tid;
       const bool ok = row < T;
       const int rr = ok ? row : T - 1;
-      lreg = ok ? L2[rr] : kNoRow;   // rows past the end bid nothing
+      lreg = ok ? L2[rr] : kNoRow;
       ireg = ok ? IR[rr] : 0.0f;
       rreg = ok ? DR[rr] : 0.0f;
     }
   };
-  auto store_block = [&](int buf) {
-    *reinterpret_cast<u32x4 *>(&sb[buf].q[(tid >> 3) * kKRow + (tid & 7) * 8]) = qreg;
-    *reinterpret_cast<u32x4 *>(&sb[buf].g[(tid >> 3) * kKRow + (tid & 7) * 8]) = greg;
-    if (tid < 32) {
-      sb[buf].lse2[tid] = lreg;
-      sb[buf].invr[tid] = ireg;
-      sb[buf].dri[tid] = rreg;
+  auto store_pair = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      *reinterpret_cast<u32x4 *>(&sb[buf][i].q[(tid >> 3) * kKRow + (tid & 7) * 8]) = qreg[i];
+      *reinterpret_cast<u32x4 *>(&sb[buf][i].g[(tid >> 3) * kKRow + (tid & 7) * 8]) = greg[i];
+    }
+    if (tid < 64) {
+      sb[buf][tid >> 5].lse2[tid & 31] = lreg;
+      sb[buf][tid >> 5].invr[tid & 31] = ireg;
+      sb[buf][tid >> 5].dri[tid & 31] = rreg;
     }
   };
 
   float running = 0.0f;   // sum of g over this half-lane's rows in blocks below
-  load_block(nqs - 1);
-  store_block(0);
+  load_pair(p_hi);
+  store_pair(0);
   __syncthreads();
-  for (int qs = nqs - 1; qs >= qs_lo; --qs) {
-    const int buf = (nqs - 1 - qs) & 1;
-    if (qs - 1 >= qs_lo) load_block(qs - 1);
-    if (wave_live && 32 * qs + 31 >= kw0) {
-      f32x16 s, da;
-      col_scores(sb[buf], kf, vf, l32, h, s, da);
-      const uint32_t cw = key < 32 * qs ? cin[cin_block_offset(qs, 0) + key] : eps_word;
-      ColTerms t;
-      if (32 * qs == kw0) col_terms<true>(s, da, sb[buf], sc, cw, a.c2, l32, h, t);
-      else col_terms<false>(s, da, sb[buf], sc, cw, a.c2, l32, h, t);
-      float part = 0.0f;
+  for (int P = p_hi; P >= p_lo; --P) {
+    const int buf = (p_hi - P) & 1;
+    if (P - 1 >= p_lo) load_pair(P - 1);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) part += t.g[r];
-      const float below = both_halves_sum(running);
-      if (h == 0 && key < T) gin[(size_t)16 * qs * (qs + 1) + key] = split2_bf16(below);
-      running += part;
+    for (int i = 1; i >= 0; --i) {
+      const int qs = 2 * P + i;
+      if (qs >= nqs || qs < qs_lo) continue;
+      if (wave_live && 32 * qs + 31 >= kw0) {
+        f32x16 s, da;
+        col_scores(sb[buf][i], kf, vf, l32, h, s, da);
+        const uint32_t cw = key < 32 * qs ? cin[cin_block_offset(qs, 0) + key] : eps_word;
+        ColTerms t;
+        if (32 * qs == kw0) col_terms<true>(s, da, sb[buf][i], sc, cw, a.c2, l32, h, t);
+        else col_terms<false>(s, da, sb[buf][i], sc, cw, a.c2, l32, h, t);
+        float part = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) part += t.g[r];
+        const float below = both_halves_sum(running);
+        if (h == 0 && key < T) gin[(size_t)16 * qs * (qs + 1) + key] = split2_bf16(below);
+        running += part;
+      }
     }
-    if (qs - 1 >= qs_lo) store_block(buf ^ 1);
+    if (P - 1 >= p_lo) store_pair(buf ^ 1);
     __syncthreads();
   }
 }
@@ -358,6 +374,10 @@ template <bool DIL>
 __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nqs) {
   __shared__ __attribute__((aligned(16))) ColBlock sb[2];
   __shared__ __attribute__((aligned(16))) ColBlockT st[2];
+  // dilution: this workgroup's K and V rows (the B operands of S and dA) sit
+  // in LDS and are read per block, which keeps the kernel within two waves'
+  // registers per SIMD without spills; the tempered form keeps them in registers
+  __shared__ __attribute__((aligned(16))) __bf16 sKV[DIL ? 2 : 1][DIL ? kColKeys * kKRow : 8];
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int bh = blockIdx.x % a.BH;
@@ -383,10 +403,21 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nqs) {
   const uint32_t eps_word = split2_bf16(fmaxf(a.eps, FLT_MIN));
 
   bf16x8 kf[4], vf[4];
+  const __bf16 *krow = nullptr, *vrow = nullptr;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    kf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(K, key, T, 2 * c + h));
-    vf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(V, key, T, 2 * c + h));
+    const u32x4 kc = load_row_chunk(K, key, T, 2 * c + h), vc = load_row_chunk(V, key, T, 2 * c + h);
+    if constexpr (DIL) {
+      *reinterpret_cast<u32x4 *>(&sKV[0][(32 * w + l32) * kKRow + 16 * c + 8 * h]) = kc;
+      *reinterpret_cast<u32x4 *>(&sKV[1][(32 * w + l32) * kKRow + 16 * c + 8 * h]) = vc;
+    } else {
+      kf[c] = __builtin_bit_cast(bf16x8, kc);
+      vf[c] = __builtin_bit_cast(bf16x8, vc);
+    }
+  }
+  if constexpr (DIL) {
+    krow = &sKV[0][(32 * w + l32) * kKRow];
+    vrow = &sKV[1][(32 * w + l32) * kKRow];
   }
   const ScanConsts sc = scan_consts(l32, h);
   f32x16 dkt[2] = {zero16(), zero16()}, dvt[2] = {zero16(), zero16()};
@@ -443,6 +474,13 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nqs) {
       if constexpr (DIL) {
         cw = key < 32 * qs ? cin[cin_block_offset(qs, 0) + key] : eps_word;
         gw = (key < 32 * (qs + 1) && key < T) ? gin[(size_t)16 * qs * (qs + 1) + key] : 0u;
+      }
+      if constexpr (DIL) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          kf[c] = lds_frag(krow, c, h);
+          vf[c] = lds_frag(vrow, c, h);
+        }
       }
       if (32 * qs == kw0)
         dkdv_block<DIL, true>(sb[buf], st[buf], kf, vf, sc, cw, gw, a.c2, l32, h, dkt, dvt);
