@@ -55,22 +55,30 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace layout of a dilution forward over keys 0..Tk-1 with Tq query rows
-// (Tq = Tk for a whole prefill): [lse2: BH*Tq][committed demand].
+// (Tq = Tk for a whole prefill): [lse2: BH*Tq][committed demand], then, when
+// the row stages split their keys (small grids), the per-range partials
+// [BH*Tq*ks*2][BH*Tq*ks*d].
 struct FwdWorkspace {
-  size_t lse_bytes, cin_bytes, total;
+  int ksplit;
+  size_t lse_bytes, cin_bytes, ml_bytes, o_bytes, total;
 };
 
-bool prefill_workspace(int B, int H, int Tq, int Tk, FwdWorkspace *ws) {
+bool prefill_workspace(int B, int H, int Tq, int Tk, int d, int dtype, FwdWorkspace *ws) {
   const size_t BH = (size_t)B * H;
   if (BH > (size_t)INT32_MAX) return false;
   const int vrow0 = attn::first_block_row(Tk, Tq);
+  ws->ksplit = attn::row_ksplit((int)BH, Tk, Tq, dtype == ATTN_BF16);
   ws->lse_bytes = round_up(BH * (size_t)Tq * sizeof(float));
   ws->cin_bytes = round_up(BH * attn::cin_floats_per_head(Tk, vrow0) * sizeof(float));
-  ws->total = ws->lse_bytes + ws->cin_bytes;
+  ws->ml_bytes = ws->ksplit > 1 ? round_up(BH * (size_t)Tq * ws->ksplit * 2 * sizeof(float)) : 0;
+  ws->o_bytes = ws->ksplit > 1 ? round_up(BH * (size_t)Tq * ws->ksplit * d * sizeof(float)) : 0;
+  ws->total = ws->lse_bytes + ws->cin_bytes + ws->ml_bytes + ws->o_bytes;
   return true;
 }
 
-bool fwd_workspace(int B, int H, int T, FwdWorkspace *ws) { return prefill_workspace(B, H, T, T, ws); }
+bool fwd_workspace(int B, int H, int T, int d, int dtype, FwdWorkspace *ws) {
+  return prefill_workspace(B, H, T, T, d, dtype, ws);
+}
 
 // Decode: chunk of keys per workgroup.
 constexpr int kDecChunk = 2048;
@@ -114,7 +122,7 @@ size_t attn_fwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype)
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
   if (mode != ATTN_DILUTION) return 0;
   FwdWorkspace ws;
-  if (!fwd_workspace(B, H, T, &ws)) return 0;
+  if (!fwd_workspace(B, H, T, d, dtype, &ws)) return 0;
   return ws.total;
 }
 
@@ -156,9 +164,9 @@ int check_fwd(const void *q, const void *k, const void *v, const void *out, int 
   return ATTN_OK;
 }
 
-int check_workspace(int B, int H, int T, void *workspace, size_t workspace_bytes,
-                    FwdWorkspace *ws) {
-  if (!fwd_workspace(B, H, T, ws)) return ATTN_EINVAL;
+int check_workspace(int B, int H, int T, int d, int dtype, void *workspace,
+                    size_t workspace_bytes, FwdWorkspace *ws) {
+  if (!fwd_workspace(B, H, T, d, dtype, ws)) return ATTN_EINVAL;
   if (!workspace || workspace_bytes < ws->total || !aligned16(workspace)) return ATTN_EWORKSPACE;
   return ATTN_OK;
 }
@@ -178,10 +186,16 @@ attn::FwdArgs make_args(const void *q, const void *k, const void *v, void *out, 
   // logits are tau <q,k> / sqrt(d); the kernels work in base 2
   a.c2 = (float)((double)tau / std::sqrt((double)d) * 1.4426950408889634);
   a.eps = eps;
+  a.ksplit = 1;
   if (workspace) {
     char *wsp = static_cast<char *>(workspace);
     a.lse2 = reinterpret_cast<float *>(wsp);
     a.cin = reinterpret_cast<float *>(wsp + ws.lse_bytes);
+    if (ws.ksplit > 1) {
+      a.ksplit = ws.ksplit;
+      a.part_ml = reinterpret_cast<float *>(wsp + ws.lse_bytes + ws.cin_bytes);
+      a.part_o = reinterpret_cast<float *>(wsp + ws.lse_bytes + ws.cin_bytes + ws.ml_bytes);
+    }
   }
   return a;
 }
@@ -197,7 +211,7 @@ int attn_dilution_lse(const void *q, const void *k, int B, int H, int T, int d, 
                       void *hip_stream) {
   int st = check_fwd(q, k, nullptr, nullptr, B, H, T, d, tau, 0.0f, dtype, lse_out, nullptr);
   FwdWorkspace ws{};
-  if (st == ATTN_OK) st = check_workspace(B, H, T, workspace, workspace_bytes, &ws);
+  if (st == ATTN_OK) st = check_workspace(B, H, T, d, dtype, workspace, workspace_bytes, &ws);
   if (st == ATTN_OK) st = check_device();
   if (st != ATTN_OK) return st;
   attn::FwdArgs a = make_args(q, k, nullptr, nullptr, B, H, T, d, tau, 0.0f, workspace, ws);
@@ -212,7 +226,7 @@ int attn_dilution_committed(const void *q, const void *k, int B, int H, int T, i
                             float *demand_out, void *hip_stream) {
   int st = check_fwd(q, k, nullptr, nullptr, B, H, T, d, tau, 0.0f, dtype, nullptr, demand_out);
   FwdWorkspace ws{};
-  if (st == ATTN_OK) st = check_workspace(B, H, T, workspace, workspace_bytes, &ws);
+  if (st == ATTN_OK) st = check_workspace(B, H, T, d, dtype, workspace, workspace_bytes, &ws);
   if (st == ATTN_OK) st = check_device();
   if (st != ATTN_OK) return st;
   attn::FwdArgs a = make_args(q, k, nullptr, nullptr, B, H, T, d, tau, 0.0f, workspace, ws);
@@ -227,7 +241,7 @@ int attn_dilution_shares(const void *q, const void *k, const void *v, void *out,
   if (!v || !out) return ATTN_EINVAL;
   int st = check_fwd(q, k, v, out, B, H, T, d, tau, eps, dtype, nullptr, nullptr);
   FwdWorkspace ws{};
-  if (st == ATTN_OK) st = check_workspace(B, H, T, workspace, workspace_bytes, &ws);
+  if (st == ATTN_OK) st = check_workspace(B, H, T, d, dtype, workspace, workspace_bytes, &ws);
   if (st == ATTN_OK) st = check_device();
   if (st != ATTN_OK) return st;
   attn::FwdArgs a = make_args(q, k, v, out, B, H, T, d, tau, eps, workspace, ws);
@@ -247,7 +261,7 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, int B, i
   if (st != ATTN_OK) return st;
   FwdWorkspace ws{};
   if (mode == ATTN_DILUTION) {
-    st = check_workspace(B, H, T, workspace, workspace_bytes, &ws);
+    st = check_workspace(B, H, T, d, dtype, workspace, workspace_bytes, &ws);
     if (st != ATTN_OK) return st;
   }
   st = check_device();
@@ -290,7 +304,7 @@ size_t attn_prefill_workspace_bytes(int B, int H, int Tq, int Tk, int d, int mod
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
   if (mode != ATTN_DILUTION) return 0;
   FwdWorkspace ws;
-  if (!prefill_workspace(B, H, Tq, Tk, &ws)) return 0;
+  if (!prefill_workspace(B, H, Tq, Tk, d, dtype, &ws)) return 0;
   return ws.total;
 }
 
@@ -335,7 +349,7 @@ int attn_prefill(const void *q, const void *kcache, const void *vcache, void *ou
     return ATTN_EINVAL;
   FwdWorkspace ws{};
   if (mode == ATTN_DILUTION) {
-    if (!prefill_workspace(B, H, Tq, Tk, &ws)) return ATTN_EINVAL;
+    if (!prefill_workspace(B, H, Tq, Tk, d, dtype, &ws)) return ATTN_EINVAL;
     if (!workspace || workspace_bytes < ws.total || !aligned16(workspace)) return ATTN_EWORKSPACE;
   }
   int st = check_device();

@@ -798,6 +798,7 @@ hipError_t launch_bwd_bf16(int mode, const BwdArgs &a, hipStream_t s) {
     f.BH = a.BH;
     f.T = f.Tq = f.kstride = a.T;
     f.D = kHeadDim;
+    f.ksplit = 1;
     f.c2 = a.c2;
     f.eps = a.eps;
     e = launch_colsum_bf16(f, s);
@@ -814,6 +815,7 @@ hipError_t launch_bwd_bf16(int mode, const BwdArgs &a, hipStream_t s) {
     t.BH = a.BH;
     t.T = t.Tq = t.kstride = a.T;
     t.D = kHeadDim;
+    t.ksplit = 1;
     t.c2 = a.c2;
     e = launch_rows_bf16(kRowTempered, t, s);
     if (e != hipSuccess) return e;

@@ -317,7 +317,7 @@ struct RowOccupancy {
 
 // FP32SUM: row sums in fp32 on the vector ALUs (exact log-sum-exp output);
 // otherwise on the matrix cores over the bf16 weights.
-template <int MODE, bool FP32SUM, int D>
+template <int MODE, bool FP32SUM, int D, bool SPLIT = false>
 __global__ void __launch_bounds__(256, (RowOccupancy<MODE, D>::value))
     rows_bf16_kernel(FwdArgs a, int nqb) {
   using G = Geom<D>;
@@ -334,8 +334,14 @@ __global__ void __launch_bounds__(256, (RowOccupancy<MODE, D>::value))
   // indexed from 0.  A whole prefill has P = 0; a later chunk starts at P > 0
   // and the blocks cover positions from vrow0 = P rounded down to kBM, the
   // positions before P standing for no row (no loads, no stores, no bids).
-  const int bh = blockIdx.x % a.BH;
-  const int qb = a.vrow0 / kBM + nqb - 1 - blockIdx.x / a.BH;
+  // With a key split (SPLIT: dilution stages on small grids) workgroup b
+  // takes range b / (nqb * BH) of its query block's key tiles.
+  const int ks = SPLIT ? a.ksplit : 1;
+  const int nitems = nqb * a.BH;
+  const int split = SPLIT ? (int)blockIdx.x / nitems : 0;
+  const int item = SPLIT ? (int)blockIdx.x % nitems : (int)blockIdx.x;
+  const int bh = item % a.BH;
+  const int qb = a.vrow0 / kBM + nqb - 1 - item / a.BH;
   const int T = a.T, Tq = a.Tq, P = T - Tq;
   const int q0 = qb * kBM;
   const int qw0 = q0 + 32 * w;              // first position of this wave
@@ -348,7 +354,9 @@ __global__ void __launch_bounds__(256, (RowOccupancy<MODE, D>::value))
   const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + khead;
 
   const int kend = min(q0 + kBM, T);        // keys [0, kend) are visible to some row
-  const int nkt = (kend + kBN - 1) / kBN;
+  const int nkt_all = (kend + kBN - 1) / kBN;
+  const int kt0 = SPLIT ? split * nkt_all / ks : 0;                 // tiles [kt0, nkt)
+  const int nkt = SPLIT ? (split + 1) * nkt_all / ks : nkt_all;
 
   // Q fragments: lane holds Q[qw0 + l32][16c + 8h .. +8) -- usable as the B
   // operand of S^T = K Q^T and as the A operand of S = Q K^T.
@@ -449,13 +457,15 @@ __global__ void __launch_bounds__(256, (RowOccupancy<MODE, D>::value))
   // first use in every iteration.
   __builtin_amdgcn_s_waitcnt(0);
 
-  load_tile(0);
-  store_tile(0);
-  if constexpr (MODE == kRowShare) load_cin(0);
+  if (!SPLIT || kt0 < nkt) {                 // an empty range loads nothing
+    load_tile(kt0);
+    store_tile(0);
+    if constexpr (MODE == kRowShare) load_cin(kt0);
+  }
   __syncthreads();
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
+  for (int kt = kt0; kt < nkt; ++kt) {
+    const int buf = (kt - kt0) & 1;
     uint32_t base[2];
     if constexpr (MODE == kRowShare) {
 #pragma unroll
@@ -486,6 +496,27 @@ __global__ void __launch_bounds__(256, (RowOccupancy<MODE, D>::value))
   const int lr = qw0 + l32 - P;               // this lane's query row
   const bool row_ok = (unsigned)lr < (unsigned)Tq;
   const float denom = FP32SUM ? both_halves_sum(st.l_run) : st.lsum[0];
+  if constexpr (SPLIT) {
+    // partial results of this key range: (max, sum) or the row sum, and the
+    // unnormalised share @ V; a range past a wave's diagonal leaves (-inf, 0, 0)
+    if (!row_ok) return;
+    const size_t rec = ((size_t)bh * Tq + lr) * ks + split;
+    if (h == 0) {
+      a.part_ml[2 * rec] = st.m_run;
+      a.part_ml[2 * rec + 1] = denom;
+    }
+    if constexpr (MODE == kRowShare) {
+      float *po = a.part_o + rec * D;
+#pragma unroll
+      for (int i = 0; i < G::kOBlocks; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v = {st.o[i][4 * g], st.o[i][4 * g + 1], st.o[i][4 * g + 2], st.o[i][4 * g + 3]};
+          *reinterpret_cast<f32x4 *>(po + 32 * i + 8 * g + 4 * h) = v;
+        }
+    }
+    return;
+  }
   if constexpr (MODE == kRowShare) {
     if (a.rowsum_out && h == 0 && row_ok) a.rowsum_out[(size_t)bh * Tq + lr] = denom;
   } else {
@@ -666,9 +697,57 @@ __global__ void __launch_bounds__(256) colsum_bf16_kernel(FwdArgs a, int nkb, in
   }
 }
 
+// Combine the key ranges of the dilution row stages, in range order.
+// LSE stage: lse2 = M + log2 sum_s l_s 2^(m_s - M), one thread per row.
+__global__ void __launch_bounds__(256) combine_lse_kernel(FwdArgs a) {
+  const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= (size_t)a.BH * a.Tq) return;
+  const int ks = a.ksplit;
+  const float *ml = a.part_ml + row * ks * 2;
+  float M = -INFINITY;
+  for (int i = 0; i < ks; ++i) M = fmaxf(M, ml[2 * i]);
+  float L = 0.0f;
+  for (int i = 0; i < ks; ++i)
+    if (ml[2 * i + 1] > 0.0f) L += ml[2 * i + 1] * fast_exp2(ml[2 * i] - M);
+  const float lse2 = M + __builtin_log2f(L);
+  if (a.lse2) a.lse2[row] = lse2;
+  if (a.lse_nat) a.lse_nat[row] = lse2 * kLn2;
+}
+
+// Shares stage: out = sum_s o_s / sum_s r_s; one thread per (row, d).
+template <int D>
+__global__ void __launch_bounds__(256) combine_share_kernel(FwdArgs a) {
+  const size_t row = (size_t)blockIdx.x * (256 / D) + threadIdx.x / D;
+  const int d = threadIdx.x % D;
+  if (row >= (size_t)a.BH * a.Tq) return;
+  const int ks = a.ksplit;
+  const float *ml = a.part_ml + row * ks * 2;
+  const float *po = a.part_o + row * ks * D;
+  float l = 0.0f, o = 0.0f;
+  for (int i = 0; i < ks; ++i) {
+    l += ml[2 * i + 1];
+    o += po[(size_t)i * D + d];
+  }
+  reinterpret_cast<__bf16 *>(a.out)[row * D + d] = (__bf16)(o / l);
+  if (a.rowsum_out && d == 0) a.rowsum_out[row] = l;
+}
+
 template <int D>
 static void launch_rows_d(int mode, const FwdArgs &a, int nqb, hipStream_t s) {
-  dim3 grid((unsigned)(nqb * a.BH)), block(256);
+  const int ks = mode == kRowTempered ? 1 : a.ksplit;
+  dim3 grid((unsigned)(nqb * a.BH * ks)), block(256);
+  if (ks > 1) {
+    const size_t rows = (size_t)a.BH * a.Tq;
+    if (mode == kRowLse) {
+      hipLaunchKernelGGL((rows_bf16_kernel<kRowLse, true, D, true>), grid, block, 0, s, a, nqb);
+      hipLaunchKernelGGL(combine_lse_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((rows_bf16_kernel<kRowShare, false, D, true>), grid, block, 0, s, a, nqb);
+      hipLaunchKernelGGL(combine_share_kernel<D>, dim3((unsigned)((rows * D + 255) / 256)), dim3(256),
+                         0, s, a);
+    }
+    return;
+  }
   switch (mode) {
     case kRowTempered:
       // an exact log-sum-exp output needs fp32 row sums

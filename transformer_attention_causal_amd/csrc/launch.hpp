@@ -33,6 +33,11 @@ struct FwdArgs {
   int vrow0;            // first position the row kernels cover: T - Tq rounded
                         // down to a multiple of 128 (0 for a whole prefill)
   int D;                // head dimension: 64 (both storage types) or 128 (bf16)
+  int ksplit;           // dilution row stages: key-tile ranges per query block
+                        // (1: none; >1: partials in part_ml / part_o, then a
+                        // combine pass)
+  float *part_ml;       // [BH*Tq*ksplit*2] per-range (max, sum) / row sum
+  float *part_o;        // [BH*Tq*ksplit*D] per-range unnormalised share @ V
   const float *tau_bh;  // [BH] per-(batch, head) multipliers, or NULL
   float c2;             // tau / sqrt(d) * log2(e); with tau_bh: log2(e) / sqrt(d),
                         // and head bh uses tau_bh[bh] * c2
@@ -48,6 +53,21 @@ __device__ __forceinline__ float head_c2(const FwdArgs &a, int bh) {
 // positions T-Tq..T-1: the first row's position rounded down to the largest
 // query block (128 rows).
 __host__ __device__ inline int first_block_row(int T, int Tq) { return ((T - Tq) / 128) * 128; }
+
+// Key-tile ranges per query block for the bf16 dilution row stages: grids of
+// fewer than 512 workgroups (a chunk of a prefill, few heads) leave CUs with a
+// single wave per SIMD, so each query block's keys are split over up to 8
+// workgroups whose partial results a combine pass adds in a fixed order.
+__host__ __device__ inline int row_ksplit(int BH, int T, int Tq, int dtype_bf16) {
+  if (!dtype_bf16) return 1;
+  const int vrow0 = first_block_row(T, Tq);
+  const long items = (long)((T + 127) / 128 - vrow0 / 128) * BH;
+  if (items >= 512) return 1;
+  int ks = (int)((1024 + items - 1) / items);
+  const int tiles = (T + 63) / 64;
+  if (ks > tiles) ks = tiles;
+  return ks > 8 ? 8 : (ks < 1 ? 1 : ks);
+}
 
 // Committed-demand storage: 32-row query block qs keeps one entry per key
 // j < 32*(qs+1) -- the demand its rows inherit from every earlier row,
