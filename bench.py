@@ -35,6 +35,11 @@ them is stored with it), else null.  ``--copy-calibration-mib N`` appends a
 plain streaming fp32 copy kernel of N MiB read and N MiB written after the
 timed steps: the known-size reference that scales the HBM byte counters.
 
+The MI355X ceilings the roofline fractions use are the published ones (bf16
+MFMA 2.5 PFLOP/s, HBM 8 TB/s); each roofline object also carries the same
+fraction against ceilings measured in the run (``measured_peaks``: a loop of
+independent MFMAs and a streaming read of 8 GiB, libattn_peaks.so).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--copy-calibration-mib N]
 """
@@ -92,6 +97,58 @@ def measured_traffic(key, files):
     except OSError:
         pass
     return None
+
+
+def measured_peaks(torch, dev, stream):
+    """The GPU's own ceilings, measured in this process with events on the
+    library's stream: a loop of independent bf16 32x32x16 MFMAs (8 waves per
+    SIMD) and a non-temporal streaming read of an 8 GiB buffer
+    (libattn_peaks.so)."""
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "transformer_attention_causal_amd", "libattn_peaks.so"))
+    lib.attn_peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.attn_peak_mfma_bf16_flops.restype = ctypes.c_double
+    lib.attn_peak_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.attn_peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.c_int, ctypes.c_void_p]
+    h = stream.cuda_stream
+
+    def timed(fn, reps=3):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    wgs, iters = 256 * 8, 4096
+    out = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+
+    def mfma():
+        if lib.attn_peak_mfma_bf16(iters, wgs, out.data_ptr(), h) != 0:
+            raise RuntimeError("attn_peak_mfma_bf16 failed")
+
+    mfma_ms = timed(mfma)
+    mfma_tflops = lib.attn_peak_mfma_bf16_flops(iters, wgs) / (mfma_ms * 1e-3) / 1e12
+    nbytes = 8 << 30
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def read():
+        if lib.attn_peak_stream_read(buf.data_ptr(), nbytes, flag.data_ptr(), 256 * 8, h) != 0:
+            raise RuntimeError("attn_peak_stream_read failed")
+
+    read_ms = timed(read)
+    del buf
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": round(mfma_tflops, 1),
+            "hbm_stream_read_gbps": round(nbytes / (read_ms * 1e-3) / 1e9, 1),
+            "how": "independent 32x32x16 bf16 MFMA loop at 8 waves/SIMD; non-temporal "
+                   "16-byte streaming read of 8 GiB; events on the bench stream"}
 
 
 def main():
@@ -324,6 +381,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    log("bench: measured peaks (MFMA loop, 8 GiB streaming read)")
+    peaks = measured_peaks(torch, dev, stream)
+    log("bench: measured peaks " + json.dumps({k: v for k, v in peaks.items() if k != "how"}))
+
     # ------------------------------------------------------------ throughputs
     d = w.d
     flops = 4.0 * d * causal_pairs(w.B, w.H, w.T)            # algorithmic, per forward
@@ -392,18 +453,24 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(shares_tflops / PEAK_BF16_TFLOPS, 4),
+            "measured_peak": peaks["mfma_bf16_tflops"],
+            "frac_of_measured_peak": round(shares_tflops / peaks["mfma_bf16_tflops"], 4),
             "traffic": measured_traffic("rows_bf16_kernel<kRowShare>", FWD_SOURCES),
             "units": f"{causal_pairs(w.B, w.H, w.T)} causal pairs x {4 * d} flops",
         },
         "roofline_decode": {
             "bound": "hbm",
-            "kernel": "attn_decode step (dec_scores + dec_share_v + dec_combine)",
+            "kernel": "attn_decode step (dec_fused<64>: one workgroup per (sequence, head), "
+                      "scores in LDS)",
             "achieved": round(dec_gbps, 2),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
+            "measured_peak": peaks["hbm_stream_read_gbps"],
+            "frac_of_measured_peak": round(dec_gbps / peaks["hbm_stream_read_gbps"], 4),
             "traffic": measured_traffic("attn_decode", DEC_SOURCES),
         },
+        "measured_peaks": peaks,
     }
 
     if not args.no_cpu_baseline:

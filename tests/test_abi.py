@@ -16,10 +16,10 @@ HEADER = os.path.join(ROOT, "include", "attn.h")
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
 
 
-def declared_functions():
-    src = open(HEADER).read()
+def declared_functions(header=HEADER):
+    src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declarations_are_exported():
@@ -30,8 +30,30 @@ def test_header_declarations_are_exported():
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", ab.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (attn_[a-z_]+)\b", out))
+    exported = set(re.findall(r"\bT (attn_[a-z0-9_]+)\b", out))
     assert set(names) <= exported
+
+
+def test_peaks_library_exports_its_header():
+    """The benchmark's measured-ceiling kernels: libattn_peaks.so exports what
+    include/attn_peaks.h declares, and rejects bad arguments on the host."""
+    path = os.path.join(os.path.dirname(ab.LIB_PATH), "libattn_peaks.so")
+    names = declared_functions(os.path.join(ROOT, "include", "attn_peaks.h"))
+    assert names == ["attn_peak_mfma_bf16", "attn_peak_mfma_bf16_flops", "attn_peak_stream_read"]
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    assert set(names) <= set(re.findall(r"\bT (attn_[a-z0-9_]+)\b", out))
+    lib = ctypes.CDLL(path)
+    lib.attn_peak_mfma_bf16_flops.restype = ctypes.c_double
+    lib.attn_peak_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    assert lib.attn_peak_mfma_bf16_flops(10, 3) == 10 * 3 * 4 * 4 * 2 * 32 * 32 * 16
+    lib.attn_peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.attn_peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.c_int, ctypes.c_void_p]
+    assert lib.attn_peak_mfma_bf16(0, 1, FAKE, None) == -1
+    assert lib.attn_peak_mfma_bf16(1, 1, None, None) == -1
+    assert lib.attn_peak_stream_read(FAKE + 4, 1 << 20, FAKE, 8, None) == -1   # misaligned
+    assert lib.attn_peak_stream_read(FAKE, 8, FAKE, 8, None) == -1             # under 16 bytes
 
 
 def test_yarn_tau_against_page_table():

@@ -1,4 +1,5 @@
-"""Build libattn.so (the HIP kernels and the C ABI) for gfx950 with hipcc."""
+"""Build libattn.so (the HIP kernels and the C ABI) for gfx950 with hipcc, and
+libattn_peaks.so (the benchmark's measured-ceiling kernels)."""
 from __future__ import annotations
 
 import os
@@ -9,8 +10,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
+PEAKS_LIB = os.path.join(PKG, "libattn_peaks.so")
 
 SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "bwd_bf16.hip"]
+PEAKS_SOURCES = ["peaks.hip"]
 
 # Packed fp32 VALU forms are disabled: every fp32 operation is a plain
 # single-lane instruction.
@@ -22,10 +25,10 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def _hipcc(sources, out, verbose):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = out + ".tmp"
     cmd = [hipcc, *FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so;
@@ -36,8 +39,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    _hipcc(PEAKS_SOURCES, PEAKS_LIB, verbose)
+    return _hipcc(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":
