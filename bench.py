@@ -28,7 +28,10 @@ the decode step's HBM GB/s (K + V + demand read + demand write) are reported
 under ``components``.  Kernel durations come from HIP events recorded on the
 stream the library launches on, inside the timed region.
 
-``roofline.traffic`` is the measured HBM bytes per launch of the roofline
+``executed_mfma_busy_rocprof`` is rocprof's matrix-core busy fraction of the
+dilution stages (SQ_VALU_MFMA_BUSY_CYCLES over 4 x SQ_BUSY_CU_CYCLES), read
+from the committed counter summary under the same digest rule as
+``traffic``.  ``roofline.traffic`` is the measured HBM bytes per launch of the roofline
 kernel, read from the committed counter summary under ``profiles/`` when that
 summary was taken from the same kernel sources and build flags (a SHA-256 over
 them is stored with it), else null.  ``--copy-calibration-mib N`` appends a
@@ -60,6 +63,7 @@ METRIC = "fwd TFLOP/s (dilution & tempered) at T=16K; decode HBM GB/s at 32K cac
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E peak
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_dilution_t16k_decode_32k.md")
+BUSY_SUMMARY = os.path.join(ROOT, "profiles", "mfma_utilisation_dilution_t16k.md")
 CSRC = os.path.join(ROOT, "transformer_attention_causal_amd", "csrc")
 FWD_SOURCES = ("attn_common.hpp", "launch.hpp", "tiles.hpp", "fwd_bf16.hip")
 DEC_SOURCES = ("attn_common.hpp", "launch.hpp", "decode.hip")
@@ -83,20 +87,30 @@ def source_digest(files):
     return h.hexdigest()
 
 
-def measured_traffic(key, files):
-    """HBM bytes per launch of kernel ``key`` from the committed counter summary,
-    or None when it is absent or was taken from other sources."""
+def _record(path, tag, key, field, files):
+    """Field ``field`` of entry ``key`` of the ``tag`` line of a committed
+    counter summary, or None when absent or taken from other sources."""
     try:
-        with open(TRAFFIC_SUMMARY) as fh:
+        with open(path) as fh:
             for line in fh:
-                if line.startswith("traffic-record: "):
-                    rec = json.loads(line[len("traffic-record: "):])
+                if line.startswith(tag + ": "):
+                    rec = json.loads(line[len(tag) + 2:])
                     ent = rec.get(key)
                     if ent and ent.get("sources_sha256") == source_digest(files):
-                        return ent["bytes_per_launch"]
+                        return ent[field]
     except OSError:
         pass
     return None
+
+
+def measured_traffic(key, files):
+    """HBM bytes per launch of kernel ``key`` from the committed counter summary."""
+    return _record(TRAFFIC_SUMMARY, "traffic-record", key, "bytes_per_launch", files)
+
+
+def measured_busy(key, files):
+    """rocprof MFMA-busy fraction of ``key`` from the committed counter summary."""
+    return _record(BUSY_SUMMARY, "utilisation-record", key, "mfma_busy", files)
 
 
 def measured_peaks(torch, dev, stream):
@@ -420,7 +434,8 @@ def main():
         "components": {
             "dilution_fwd": {"ms": round(dil_ms, 4), "tflops": round(dil_tflops, 3),
                              "stage_ms": {n: round(ms[n], 4) for n in names[:3]},
-                             "frac_of_bf16_peak": round(dil_tflops / PEAK_BF16_TFLOPS, 4)},
+                             "frac_of_bf16_peak": round(dil_tflops / PEAK_BF16_TFLOPS, 4),
+                             "executed_mfma_busy_rocprof": measured_busy("dilution_fwd", FWD_SOURCES)},
             "tempered_fwd": {"ms": round(ms["tempered"], 4), "tflops": round(tmp_tflops, 3),
                              "frac_of_bf16_peak": round(tmp_tflops / PEAK_BF16_TFLOPS, 4)},
             "decode_step": {"ms": round(ms["decode"], 4), "gbps": round(dec_gbps, 2),
@@ -455,6 +470,7 @@ def main():
             "frac": round(shares_tflops / PEAK_BF16_TFLOPS, 4),
             "measured_peak": peaks["mfma_bf16_tflops"],
             "frac_of_measured_peak": round(shares_tflops / peaks["mfma_bf16_tflops"], 4),
+            "executed_mfma_busy_rocprof": measured_busy("rows_bf16_kernel<kRowShare>", FWD_SOURCES),
             "traffic": measured_traffic("rows_bf16_kernel<kRowShare>", FWD_SOURCES),
             "units": f"{causal_pairs(w.B, w.H, w.T)} causal pairs x {4 * d} flops",
         },
