@@ -114,7 +114,8 @@ def _declare(lib):
         lib.oracle_prefill.restype = i
         lib.oracle_prefill.argtypes = [vp, vp, vp, i, dp, dp, dp, i, i, i, i, i, i, d, d, i]
         lib.oracle_attn_bwd.restype = i
-        lib.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, i, dp, dp, dp, dp, i, i, i, i, d, d, i]
+        lib.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, i, dp, dp, dp, dp, dp, i, i, i, i, d, dp,
+                                        d, i]
 
 
 def _as_input(x):
@@ -270,11 +271,13 @@ def prefill(q, kcache, vcache, Tk: int, tau: float = 1.0, eps: float = 1e-6, mod
     return out, lse
 
 
-def attn_bwd(q, k, v, dout, tau: float = 1.0, eps: float = 1e-6, mode: int = 1):
+def attn_bwd(q, k, v, dout, tau: float = 1.0, eps: float = 1e-6, mode: int = 1, tau_bh=None,
+             want_dtau: bool = False):
     """Exact gradients of the scalar sum(out * dout).  q,k,v,dout: [B,H,T,d] in
-    one storage type; mode 0 tempered, 1 dilution.  Returns (dq, dk, dv, rsum)
-    in fp64; rsum [B,H,T] holds the dilution row sums of the shares (NaN for
-    tempered)."""
+    one storage type; mode 0 tempered, 1 dilution; ``tau_bh`` ([B,H]) replaces
+    tau per head.  Returns (dq, dk, dv, rsum) in fp64 -- plus dtau [B,H], the
+    gradient with respect to each head's multiplier, when ``want_dtau``; rsum
+    [B,H,T] holds the dilution row sums of the shares (NaN for tempered)."""
     lib = _load()
     qa, c1 = _as_input(q)
     ka, c2 = _as_input(k)
@@ -286,9 +289,16 @@ def attn_bwd(q, k, v, dout, tau: float = 1.0, eps: float = 1e-6, mode: int = 1):
     dk = np.zeros((B, H, T, d))
     dv = np.zeros((B, H, T, d))
     rs = np.full((B, H, T), np.nan)
+    dt = np.full((B, H), np.nan)
+    tb = None
+    if tau_bh is not None:
+        tb = np.ascontiguousarray(np.asarray(tau_bh, dtype=np.float64).reshape(B, H))
     rc = lib.oracle_attn_bwd(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, ga.ctypes.data,
-                             code, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(rs), B, H, T, d,
-                             float(tau), float(eps), int(mode))
+                             code, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(rs),
+                             _ptr(dt) if want_dtau else None, B, H, T, d, float(tau),
+                             _ptr(tb) if tb is not None else None, float(eps), int(mode))
     if rc != 0:
         raise RuntimeError(f"oracle_attn_bwd failed ({rc})")
+    if want_dtau:
+        return dq, dk, dv, rs, dt
     return dq, dk, dv, rs

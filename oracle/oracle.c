@@ -482,12 +482,19 @@ int oracle_dilution_decode_step(const void *q, const void *kc, const void *vc, i
  *   dQ_i = c sum_j dS_ij k_j,  dK_j = c sum_i dS_ij q_i,  c = tau / sqrt(d).
  * Tempered is the same with a = p, so dp_ij = dA_ij.
  *
+ * With logits tau <q_i, k_j> / sqrt(d) the multiplier's own gradient is
+ *   dL/dtau = sum_ij dS_ij <q_i, k_j> / sqrt(d)
+ * (the per-head temperature a learned-temperature layer feeds in, [FOCAL]
+ * sec. 2.2 eq. learn-temp).
+ *
  * q,k,v,dout: [B,H,T,d] in dtype; dq,dk,dv: [B,H,T,d] fp64.  rsum (optional,
- * dilution): [B,H,T] fp64, the row sums r_i.  mode: 0 tempered, 1 dilution.
+ * dilution): [B,H,T] fp64, the row sums r_i.  dtau (optional): [B,H] fp64.
+ * tau_bh (optional): [B,H] per-head multipliers in place of tau.  mode: 0
+ * tempered, 1 dilution.
  */
 static int bwd_one_head(const void *q, const void *k, const void *v, const void *dout, int dtype,
-                        double *dq, double *dk, double *dv, double *rsum, int T, int d, double c,
-                        double eps, int mode, int bh) {
+                        double *dq, double *dk, double *dv, double *rsum, double *dtau, int T,
+                        int d, double c, double eps, int mode, int bh) {
   const size_t base = (size_t)bh * T * d, TT = (size_t)T * T;
   double *Q = malloc(sizeof(double) * (size_t)T * d), *K = malloc(sizeof(double) * (size_t)T * d);
   double *V = malloc(sizeof(double) * (size_t)T * d), *dO = malloc(sizeof(double) * (size_t)T * d);
@@ -556,6 +563,15 @@ static int bwd_one_head(const void *q, const void *k, const void *v, const void 
     for (int j = 0; j <= i; ++j) rho += Pi[j] * dPi[j];
     for (int j = 0; j <= i; ++j) dPi[j] = Pi[j] * (dPi[j] - rho);
   }
+  /* the multiplier: logits are tau <q_i, k_j> / sqrt(d), so
+     dL/dtau = sum_ij dS_ij <q_i, k_j> / sqrt(d) */
+  if (dtau) {
+    double acc = 0.0;
+    for (int i = 0; i < T; ++i)
+      for (int j = 0; j <= i; ++j)
+        acc += dP[(size_t)i * T + j] * dot(Q + (size_t)i * d, K + (size_t)j * d, d);
+    dtau[bh] = acc / sqrt((double)d);
+  }
   for (int i = 0; i < T; ++i) {
     const double *Si = dP + (size_t)i * T;
     double *dqi = dq + base + (size_t)i * d;
@@ -580,14 +596,14 @@ done:
 }
 
 int oracle_attn_bwd(const void *q, const void *k, const void *v, const void *dout, int dtype,
-                    double *dq, double *dk, double *dv, double *rsum, int B, int H, int T, int d,
-                    double tau, double eps, int mode) {
+                    double *dq, double *dk, double *dv, double *rsum, double *dtau, int B, int H,
+                    int T, int d, double tau, const double *tau_bh, double eps, int mode) {
   if (B <= 0 || H <= 0 || T <= 0 || d <= 0 || (mode != 0 && mode != 1)) return -1;
-  const double c = tau / sqrt((double)d);
   int failed = 0;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int bh = 0; bh < B * H; ++bh)
-    if (bwd_one_head(q, k, v, dout, dtype, dq, dk, dv, rsum, T, d, c, eps, mode, bh) != 0) {
+    if (bwd_one_head(q, k, v, dout, dtype, dq, dk, dv, rsum, dtau, T, d,
+                     (tau_bh ? tau_bh[bh] : tau) / sqrt((double)d), eps, mode, bh) != 0) {
 #pragma omp atomic write
       failed = 1;
     }

@@ -448,6 +448,32 @@ def pin_bwd_finite_differences():
                 assert np.max(np.abs(g - n)) <= 2e-7 * scale, (T, tau, eps, mode)
 
 
+def pin_bwd_tau_finite_differences():
+    """The gradient with respect to each head's multiplier agrees with central
+    differences of the pinned forwards in that multiplier (tau = 0 included),
+    and per-head multipliers give each head exactly its scalar-tau gradients."""
+    rng = _rng(27)
+    for T, eps in [(1, 1e-6), (6, 1e-6), (9, 0.0), (7, 0.3)]:
+        q, k, v, do = (rng.standard_normal((1, 3, T, 4)) for _ in range(4))
+        taus = np.array([[0.0, 0.8, 1.4]])
+        for mode in (0, 1):
+            def loss(head, tau):
+                sl = [np.ascontiguousarray(x[:, head:head + 1]) for x in (q, k, v)]
+                out = (oracle.tempered_fwd(*sl, tau)[0] if mode == 0
+                       else oracle.dilution_fwd(*sl, tau, eps)[0])
+                return float(np.sum(out * do[:, head:head + 1]))
+            got = oracle.attn_bwd(q, k, v, do, 1.0, eps, mode, tau_bh=taus, want_dtau=True)
+            h = 1e-6
+            for head in range(3):
+                t = float(taus[0, head])
+                fd = (loss(head, t + h) - loss(head, t - h)) / (2 * h)
+                assert abs(got[4][0, head] - fd) <= 2e-7 * max(1.0, abs(fd)), (T, eps, mode, head)
+                sl = [np.ascontiguousarray(x[:, head:head + 1]) for x in (q, k, v, do)]
+                ref = oracle.attn_bwd(*sl, t, eps, mode)
+                for g, r in zip(got[:3], ref[:3]):
+                    assert np.array_equal(g[:, head:head + 1], r), (T, eps, mode, head)
+
+
 def pin_bwd_tempered_vs_library():
     """Tempered gradients equal torch autograd through CPU fp64 SDPA."""
     import torch

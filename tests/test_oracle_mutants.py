@@ -52,6 +52,9 @@ MUTANTS = [
     ("prefill_tempered_keys_from_chunk_start",
      "causal_bids(Qh + (size_t)(i - P) * d, Kh, i, d, c, p, 0)",
      "causal_bids(Qh + (size_t)(i - P) * d, Kh, i - P, d, c, p, 0)"),
+    ("bwd_dtau_without_sqrt_d", "dtau[bh] = acc / sqrt((double)d);", "dtau[bh] = acc;"),
+    ("bwd_dtau_from_bids", "acc += dP[(size_t)i * T + j] * dot(Q + (size_t)i * d, K + (size_t)j * d, d);",
+     "acc += P[(size_t)i * T + j] * dot(Q + (size_t)i * d, K + (size_t)j * d, d);"),
     ("bwd_suffix_exclusive",
      "          col[j] += dPi[j] * Pi[j] / (Di[j] * Di[j]);\n          dPi[j] = dPi[j] / Di[j] - col[j];",
      "          dPi[j] = dPi[j] / Di[j] - col[j];\n          col[j] += dPi[j] * Pi[j] / (Di[j] * Di[j]);"),
