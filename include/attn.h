@@ -100,7 +100,8 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, int B, i
                 size_t workspace_bytes, float *lse_out, float *demand_out, float *rowsum_out,
                 void *hip_stream);
 
-/* Bytes of device workspace attn_bwd needs: four fp32 values per query row,
+/* Bytes of device workspace attn_bwd and attn_bwd_ex need: five fp32 values
+ * per query row,
  * and for dilution the committed demand and the later rows' gradient sums
  * per (32-row query block, key): B*H*16*n*(n+1) floats each,
  * n = ceil(T/32), plus a bf16 [B,H,T,d] array.  0 for an unsupported shape,
@@ -121,11 +122,32 @@ size_t attn_bwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype)
  *   dtype               ATTN_BF16 (ATTN_F32 returns ATTN_ENOTSUP)
  *   workspace           device scratch of >= attn_bwd_workspace_bytes(...)
  *                       bytes; contents on entry are ignored
- * Deterministic: fixed reduction orders, no atomics. */
+ * Deterministic: fixed reduction orders, no atomics.  attn_bwd is
+ * attn_bwd_ex with tau_bh = dtau_out = NULL. */
 int attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout,
              const float *lse, const float *rowsum, void *dq, void *dk, void *dv, int B, int H,
              int T, int d, float tau, int mode, float eps, int dtype, void *workspace,
              size_t workspace_bytes, void *hip_stream);
+
+/* attn_bwd with per-head multipliers and the gradient with respect to them
+ * ("Learning to Focus", sec. 2.2: the temperature is learned, so training
+ * needs dL/dtau).  Arguments as attn_bwd, and:
+ *   tau_bh    [B,H] fp32 device array or NULL: head (b,h)'s multiplier, as
+ *             given to attn_prefill (which produces the matching lse and
+ *             rowsum through lse_out/rowsum_out); tau is then ignored.
+ *             Values finite and >= 0, read on the device and not checked.
+ *   dtau_out  [B,H] fp32 device array or NULL: receives, per head,
+ *             dL/dtau_bh = sum_ij dS_ij <q_i, k_j> / sqrt(d) with dS the
+ *             gradient of the logits (for a scalar tau shared by all heads,
+ *             dL/dtau is the sum over heads).  It is formed as
+ *             sum_i <q_i, dQ_i / c> / sqrt(d) with fp32 row terms, so it is
+ *             defined at tau = 0 too.  May not overlap any other argument.
+ * tau_bh may not overlap dq, dk, dv or dtau_out. */
+int attn_bwd_ex(const void *q, const void *k, const void *v, const void *out, const void *dout,
+                const float *lse, const float *rowsum, void *dq, void *dk, void *dv, int B,
+                int H, int T, int d, float tau, const float *tau_bh, int mode, float eps,
+                int dtype, float *dtau_out, void *workspace, size_t workspace_bytes,
+                void *hip_stream);
 
 /* The dilution forward pass, one stage per call (attn_fwd with ATTN_DILUTION
  * runs exactly these three in order on one stream).  All three take the same
@@ -193,13 +215,15 @@ size_t attn_prefill_workspace_bytes(int B, int H, int Tq, int Tk, int d, int mod
  *              not written).  May be demand_in itself (updated in place);
  *              otherwise no overlap with it.
  *   lse_out    [B,H,Tq] fp32, optional: natural-log log-sum-exp per row
+ *   rowsum_out [B,H,Tq] fp32 (dilution), optional: each row's sum of shares,
+ *              the renormaliser of A (with lse_out, what attn_bwd_ex needs)
  *   workspace  >= attn_prefill_workspace_bytes(B,H,Tq,Tk,d,mode,dtype) bytes
- * demand_in and demand_out must be NULL for ATTN_TEMPERED (else ATTN_EINVAL).
- * Outputs may not alias each other or any tensor argument. */
+ * demand_in, demand_out and rowsum_out must be NULL for ATTN_TEMPERED (else
+ * ATTN_EINVAL).  Outputs may not alias each other or any tensor argument. */
 int attn_prefill(const void *q, const void *kcache, const void *vcache, void *out, int B, int H,
                  int Tq, int Tk, int Lcap, int d, float tau, const float *tau_bh, int mode,
                  float eps, int dtype, const float *demand_in, float *demand_out, float *lse_out,
-                 void *workspace, size_t workspace_bytes, void *hip_stream);
+                 float *rowsum_out, void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /* Bytes of device workspace attn_decode needs (per-(sequence,head,split)
  * partial maxima, sums and weighted values plus one fp32 score per cached

@@ -135,10 +135,11 @@ def test_workspace_sizes():
 def test_bwd_workspace_sizes():
     n = 16384 // 32
     rows = 16 * 16384 * 4
-    want = 4 * rows + 2 * 16 * 16 * n * (n + 1) * 4 + 16 * 16384 * 64 * 2
+    # five per-row arrays: lse2, 1/r, delta/r, rho and the rows' dL/dtau terms
+    want = 5 * rows + 2 * 16 * 16 * n * (n + 1) * 4 + 16 * 16384 * 64 * 2
     got = ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 1)
-    assert want <= got <= want + 7 * 256
-    assert 4 * rows <= ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 0, 1) <= 4 * rows + 4 * 256
+    assert want <= got <= want + 8 * 256
+    assert 5 * rows <= ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 0, 1) <= 5 * rows + 5 * 256
     assert ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 0) == 0   # fp32: not supported
     assert ab.attn_bwd_workspace_bytes(1, 16, 16384, 128, 1, 1) == 0
 
@@ -170,7 +171,7 @@ def pre(**kw):
                 B=1, H=2, Tq=16, Tk=40, Lcap=64, d=64, tau=1.0, tau_bh=None, mode=1, eps=1e-6,
                 dtype=1,
                 demand_in=FAKE + 0x4000000, demand_out=FAKE + 0x4000000, lse_out=None,
-                workspace=None, workspace_bytes=0, hip_stream=None)
+                rowsum_out=None, workspace=None, workspace_bytes=0, hip_stream=None)
     args.update(kw)
     return ab.attn_prefill(**args)
 
@@ -193,6 +194,13 @@ def pre(**kw):
     (dict(lse_out=FAKE + 0x4000000 + 256), ab.ATTN_EINVAL),  # lse inside the demand
     (dict(lse_out=FAKE), ab.ATTN_EINVAL),               # lse aliases q
     (dict(demand_out=FAKE + 0x2000000), ab.ATTN_EINVAL),   # demand inside the V cache
+    (dict(rowsum_out=FAKE + 0x6000004), ab.ATTN_EINVAL),   # misaligned
+    (dict(rowsum_out=FAKE + 0x4000000 + 64), ab.ATTN_EINVAL),  # row sums inside the demand
+    (dict(rowsum_out=FAKE + 0x6000000, lse_out=FAKE + 0x6000040), ab.ATTN_EINVAL),  # overlap
+    (dict(rowsum_out=FAKE + 0x6000000, tau_bh=FAKE + 0x6000000), ab.ATTN_EINVAL),
+    (dict(mode=0, demand_in=None, demand_out=None, rowsum_out=FAKE + 0x6000000),
+     ab.ATTN_EINVAL),                                   # row sums in tempered mode
+    (dict(rowsum_out=FAKE + 0x6000000, lse_out=FAKE + 0x6000100), ab.ATTN_EWORKSPACE),
     (dict(d=96), ab.ATTN_ENOTSUP),
     (dict(d=128, dtype=0), ab.ATTN_ENOTSUP),            # fp32 runs at d = 64 only
     (dict(d=128), ab.ATTN_EWORKSPACE),                  # bf16 at d = 128 is supported
@@ -212,10 +220,13 @@ def bwd(**kw):
     args = dict(q=base, k=base + 0x1000000, v=base + 0x2000000, out=base + 0x3000000,
                 dout=base + 0x4000000, lse=base + 0x5000000, rowsum=base + 0x6000000,
                 dq=base + 0x7000000, dk=base + 0x8000000, dv=base + 0x9000000, B=1, H=1, T=16,
-                d=64, tau=1.0, mode=1, eps=1e-6, dtype=1, workspace=None, workspace_bytes=0,
-                hip_stream=None)
+                d=64, tau=1.0, tau_bh=None, mode=1, eps=1e-6, dtype=1, dtau_out=None,
+                workspace=None, workspace_bytes=0, hip_stream=None)
     args.update(kw)
-    return ab.attn_bwd(**args)
+    if "tau_bh" not in kw and "dtau_out" not in kw:
+        del args["tau_bh"], args["dtau_out"]
+        return ab.attn_bwd(**args)
+    return ab.attn_bwd_ex(**args)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -233,6 +244,14 @@ def bwd(**kw):
     (dict(dv=FAKE), ab.ATTN_EINVAL),                  # dv aliases q
     (dict(), ab.ATTN_EWORKSPACE),
     (dict(mode=0, rowsum=None), ab.ATTN_EWORKSPACE),  # tempered: row sums not needed
+    (dict(tau_bh=FAKE + 0xa000004), ab.ATTN_EINVAL),  # misaligned tau array
+    (dict(dtau_out=FAKE + 0xa000008), ab.ATTN_EINVAL),
+    (dict(tau_bh=FAKE + 0x8000000), ab.ATTN_EINVAL),  # tau array inside dk
+    (dict(dtau_out=FAKE + 0x5000000), ab.ATTN_EINVAL),  # dL/dtau inside lse
+    (dict(dtau_out=FAKE + 0x9000040), ab.ATTN_EINVAL),  # dL/dtau inside dv
+    (dict(tau_bh=FAKE + 0xa000000, dtau_out=FAKE + 0xa000000), ab.ATTN_EINVAL),
+    (dict(tau_bh=FAKE + 0xa000000, dtau_out=FAKE + 0xb000000), ab.ATTN_EWORKSPACE),
+    (dict(tau_bh=None, dtau_out=FAKE + 0xb000000), ab.ATTN_EWORKSPACE),
 ])
 def test_bwd_rejects_bad_arguments(kw, status):
     assert bwd(**kw) == status

@@ -10,7 +10,8 @@ import pytest
 import oracle
 from gpu_util import errors, to_device
 from transformer_attention_causal_amd import binding as ab
-from transformer_attention_causal_amd.workloads import PREFILL, draw_grad, draw_qkv, prefill_inputs
+from transformer_attention_causal_amd.workloads import (PREFILL, draw_grad, draw_qkv, learned_tau,
+                                                        prefill_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -40,10 +41,16 @@ def run_bwd(inp, dout_bits, tau, mode, eps=1e-6):
 
 
 def check_grads(got, ref, what):
+    big = max(float(np.max(np.abs(r))) for r in ref)
     for name, g, r in zip(("dq", "dk", "dv"), got, ref):
         max_abs, rel_rms = errors(g, r)
-        scale = max(1e-30, float(np.max(np.abs(r))))
+        scale = float(np.max(np.abs(r)))
         print(f"{what} {name}: max-abs {max_abs:.3e} (scale {scale:.3e}) rel-RMS {rel_rms:.3e}")
+        if scale == 0.0:
+            # vanishes identically (dQ and dK at T = 1: one key, so dS = 0):
+            # fp32 rounding of terms the size of the other gradients
+            assert max_abs <= 1e-5 * big, (what, name)
+            continue
         assert rel_rms <= GRAD_REL_RMS and max_abs <= GRAD_MAX_REL * scale, (what, name)
 
 
@@ -115,3 +122,104 @@ def test_bwd_deterministic():
     b = run_bwd(inp, g, 1.0, 1)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+# dL/dtau per head is a sum over T rows of <q_i, u_i> (u_i = dQ_i / c).  By
+# Cauchy-Schwarz its magnitude is at most sum_i |q_i| |u_i| / sqrt(d); the
+# per-row errors of u (the dQ bar above, ~2^-9 relative per bf16 operand)
+# enter that sum, so the bar is a fraction of this bound.
+DTAU_REL = 2e-3
+
+
+def run_bwd_heads(inp, dout_bits, mode, tau_bh=None, tau=1.0, eps=1e-6):
+    """Forward through attn_prefill (whole prefill, per-head multipliers) and
+    backward through attn_bwd_ex with dL/dtau; returns dq, dk, dv, dtau."""
+    import torch
+
+    q, k, v = (to_device(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    dout = to_device(dout_bits, "bf16")
+    B, H, T, _ = q.shape
+    tb = torch.from_numpy(np.ascontiguousarray(tau_bh)).cuda() if tau_bh is not None else None
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    rs = torch.empty((B, H, T), dtype=torch.float32, device="cuda") if mode == 1 else None
+    dt = torch.full((B, H), float("nan"), dtype=torch.float32, device="cuda")
+    out = ab.prefill(q, k, v, T, tau=tau, mode=mode, eps=eps, lse_out=lse, rowsum_out=rs,
+                     tau_bh=tb)
+    dq, dk, dv = ab.bwd(q, k, v, out, dout, lse, rs, tau=tau, mode=mode, eps=eps, tau_bh=tb,
+                        dtau_out=dt)
+    torch.cuda.synchronize()
+    return [t.float().cpu().numpy() for t in (dq, dk, dv)] + [dt.cpu().numpy()]
+
+
+def check_dtau(got, ref_dq, inp, g, taus, dtau_ref, what):
+    """got, dtau_ref: [B,H]; the bound uses the oracle's dQ rows / c, each no
+    less than fp32 rounding of its terms <dO_i, v_j> k_j (which also covers
+    rows where u vanishes identically, as at T = 1)."""
+    q, k, v, do = (oracle.Bf16(x).to_f64() for x in (inp.q, inp.k, inp.v, g))
+    d = q.shape[-1]
+    c = np.asarray(taus, dtype=np.float64).reshape(q.shape[0], q.shape[1], 1) / math.sqrt(d)
+    qn = np.linalg.norm(q, axis=-1)
+    un = np.linalg.norm(ref_dq, axis=-1) / np.where(c > 0, c, 1.0)
+    terms = (np.linalg.norm(do, axis=-1) * np.max(np.linalg.norm(v, axis=-1), axis=-1, keepdims=True)
+             * np.max(np.linalg.norm(k, axis=-1), axis=-1, keepdims=True))
+    un = np.maximum(un, 1e-5 * terms)
+    bound = np.sum(qn * un, axis=-1) / math.sqrt(d)
+    err = np.abs(got.astype(np.float64) - dtau_ref)
+    print(f"{what} dtau: max err/bound {np.max(err / bound):.3e}, "
+          f"max err/|ref| {np.max(err / np.maximum(np.abs(dtau_ref), 1e-30)):.3e}")
+    assert np.all(np.isfinite(got))
+    assert np.all(err <= DTAU_REL * bound), what
+
+
+@pytest.mark.parametrize("mode", [0, 1], ids=["tempered", "dilution"])
+@pytest.mark.parametrize("T", [1, 33, 300])
+def test_bwd_per_head_tau_and_dtau(mode, T):
+    """Per-(b,h) multipliers sqrt(d)/t, t ~ U[5, 10]: the gradients and
+    dL/dtau of every head against the oracle with the same multipliers."""
+    B, H = 2, 3
+    inp = draw_qkv(B, H, T, 64, "bf16", seed=2100 + T)
+    g = draw_grad(B, H, T, 64, seed=2100 + T)
+    taus = learned_tau(B, H, 64, seed=2100 + T)
+    got = run_bwd_heads(inp, g, mode, tau_bh=taus)
+    ref = oracle.attn_bwd(oracle.Bf16(inp.q), oracle.Bf16(inp.k), oracle.Bf16(inp.v),
+                          oracle.Bf16(g), 1.0, 1e-6, mode, tau_bh=taus, want_dtau=True)
+    check_grads(got[:3], ref[:3], f"per-head mode={mode} T={T}")
+    check_dtau(got[3], ref[0], inp, g, taus, ref[4], f"per-head mode={mode} T={T}")
+
+
+@pytest.mark.parametrize("mode", [0, 1], ids=["tempered", "dilution"])
+def test_bwd_dtau_scalar_and_zero_tau(mode):
+    """A scalar tau shared by all heads still gives each head's dL/dtau; at
+    tau = 0 dQ and dK vanish but dL/dtau does not."""
+    B, H, T = 1, 2, 200
+    inp = draw_qkv(B, H, T, 64, "bf16", seed=2200)
+    g = draw_grad(B, H, T, 64, seed=2200)
+    for tau in (TAU4, 0.0):
+        got = run_bwd_heads(inp, g, mode, tau=tau)
+        ref = oracle.attn_bwd(oracle.Bf16(inp.q), oracle.Bf16(inp.k), oracle.Bf16(inp.v),
+                              oracle.Bf16(g), tau, 1e-6, mode, want_dtau=True)
+        taus = np.full((B, H), tau)
+        if tau == 0.0:
+            assert np.all(got[0] == 0.0) and np.all(got[1] == 0.0)
+            # the bound needs u = dQ / c, which the oracle's dQ no longer
+            # carries at c = 0: the relative bar on the value itself instead
+            err = np.abs(got[3] - ref[4]) / np.abs(ref[4])
+            print(f"tau=0 mode={mode} dtau rel err {np.max(err):.3e}")
+            assert np.all(err <= 2e-2)
+        else:
+            check_grads(got[:3], ref[:3], f"scalar tau mode={mode}")
+            check_dtau(got[3], ref[0], inp, g, taus, ref[4], f"scalar tau mode={mode}")
+
+
+def test_bwd_dtau_heavy_keys_t1024():
+    """dL/dtau on the dilution_t16k recipe (5 % of key rows at 3x norm) at
+    T=1024 with learned per-head multipliers."""
+    w = PREFILL["dilution_t16k"]
+    inp = prefill_inputs(w, T=1024, H=2)
+    g = draw_grad(1, 2, 1024, 64, seed=w.seed)
+    taus = learned_tau(1, 2, 64, seed=w.seed)
+    got = run_bwd_heads(inp, g, 1, tau_bh=taus, eps=w.eps)
+    ref = oracle.attn_bwd(oracle.Bf16(inp.q), oracle.Bf16(inp.k), oracle.Bf16(inp.v),
+                          oracle.Bf16(g), 1.0, w.eps, 1, tau_bh=taus, want_dtau=True)
+    check_grads(got[:3], ref[:3], "heavy per-head")
+    check_dtau(got[3], ref[0], inp, g, taus, ref[4], "heavy per-head")

@@ -25,7 +25,7 @@ ATTN_F32, ATTN_BF16 = 0, 1
 
 EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_bytes", "attn_dilution_lse",
             "attn_dilution_committed", "attn_dilution_shares", "attn_bwd",
-            "attn_bwd_workspace_bytes", "attn_prefill", "attn_prefill_workspace_bytes",
+            "attn_bwd_ex", "attn_bwd_workspace_bytes", "attn_prefill", "attn_prefill_workspace_bytes",
             "attn_decode", "attn_decode_ex", "attn_decode_workspace_bytes",
             "attn_yarn_tau", "attn_strerror")
 
@@ -57,11 +57,14 @@ def load() -> ctypes.CDLL:
         lib.attn_bwd.restype = i
         lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, f, i,
                                  vp, sz, vp]
+        lib.attn_bwd_ex.restype = i
+        lib.attn_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, vp, i,
+                                    f, i, vp, vp, sz, vp]
         lib.attn_bwd_workspace_bytes.restype = sz
         lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
         lib.attn_prefill.restype = i
         lib.attn_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i, f, i, vp, vp,
-                                     vp, vp, sz, vp]
+                                     vp, vp, vp, sz, vp]
         lib.attn_prefill_workspace_bytes.restype = sz
         lib.attn_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
         lib.attn_dilution_lse.restype = i
@@ -107,14 +110,22 @@ def attn_bwd(q, k, v, out, dout, lse, rowsum, dq, dk, dv, B, H, T, d, tau, mode,
                            eps, dtype, workspace, workspace_bytes, hip_stream)
 
 
+def attn_bwd_ex(q, k, v, out, dout, lse, rowsum, dq, dk, dv, B, H, T, d, tau, tau_bh, mode, eps,
+                dtype, dtau_out, workspace, workspace_bytes, hip_stream) -> int:
+    return load().attn_bwd_ex(q, k, v, out, dout, lse, rowsum, dq, dk, dv, B, H, T, d, tau,
+                              tau_bh, mode, eps, dtype, dtau_out, workspace, workspace_bytes,
+                              hip_stream)
+
+
 def attn_bwd_workspace_bytes(B, H, T, d, mode, dtype) -> int:
     return int(load().attn_bwd_workspace_bytes(B, H, T, d, mode, dtype))
 
 
 def attn_prefill(q, kcache, vcache, out, B, H, Tq, Tk, Lcap, d, tau, tau_bh, mode, eps, dtype,
-                 demand_in, demand_out, lse_out, workspace, workspace_bytes, hip_stream) -> int:
+                 demand_in, demand_out, lse_out, rowsum_out, workspace, workspace_bytes,
+                 hip_stream) -> int:
     return load().attn_prefill(q, kcache, vcache, out, B, H, Tq, Tk, Lcap, d, tau, tau_bh, mode,
-                               eps, dtype, demand_in, demand_out, lse_out, workspace,
+                               eps, dtype, demand_in, demand_out, lse_out, rowsum_out, workspace,
                                workspace_bytes, hip_stream)
 
 
@@ -235,9 +246,13 @@ def bwd_workspace(B, H, T, mode, dtype_code, device):
 
 
 def bwd(q, k, v, out, dout, lse, rowsum=None, tau: float = 1.0, mode: int = ATTN_TEMPERED,
-        eps: float = 1e-6, dq=None, dk=None, dv=None, workspace=None):
-    """Run attn_bwd on [B,H,T,64] tensors (``lse``/``rowsum`` from ``fwd``'s
-    ``lse_out``/``rowsum_out``); returns (dq, dk, dv)."""
+        eps: float = 1e-6, dq=None, dk=None, dv=None, workspace=None, tau_bh=None,
+        dtau_out=None):
+    """Run attn_bwd_ex on [B,H,T,64] tensors (``lse``/``rowsum`` from the
+    forward's ``lse_out``/``rowsum_out``); ``tau_bh`` an optional [B,H] fp32
+    tensor of per-head multipliers (as given to ``prefill``), ``dtau_out`` an
+    optional [B,H] fp32 tensor that receives dL/dtau per head.  Returns
+    (dq, dk, dv)."""
     import torch
 
     for t in (q, k, v, out, dout):
@@ -252,22 +267,29 @@ def bwd(q, k, v, out, dout, lse, rowsum=None, tau: float = 1.0, mode: int = ATTN
         workspace, ws_bytes = bwd_workspace(B, H, T, mode, code, q.device)
     else:
         ws_bytes = workspace.numel() * workspace.element_size()
-    st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
-                  lse.data_ptr(), rowsum.data_ptr() if rowsum is not None else None,
-                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, T, d, float(tau), int(mode),
-                  float(eps), code, workspace.data_ptr(), ws_bytes, _stream_handle(q.device))
+    for name, t in (("tau_bh", tau_bh), ("dtau_out", dtau_out)):
+        if t is not None and (t.shape != (B, H) or t.dtype != torch.float32
+                              or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 [B,H] tensor")
+    st = attn_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                     lse.data_ptr(), rowsum.data_ptr() if rowsum is not None else None,
+                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, T, d, float(tau),
+                     tau_bh.data_ptr() if tau_bh is not None else None, int(mode), float(eps),
+                     code, dtau_out.data_ptr() if dtau_out is not None else None,
+                     workspace.data_ptr(), ws_bytes, _stream_handle(q.device))
     if st != ATTN_OK:
-        raise AttnError(st, "attn_bwd")
+        raise AttnError(st, "attn_bwd_ex")
     return dq, dk, dv
 
 
 def prefill(q, kcache, vcache, Tk: int, tau: float = 1.0, mode: int = ATTN_DILUTION,
             eps: float = 1e-6, demand_in=None, demand_out=None, lse_out=None, out=None,
-            workspace=None, tau_bh=None):
+            workspace=None, tau_bh=None, rowsum_out=None):
     """Run attn_prefill: q [B,H,Tq,d] holds the rows at positions Tk-Tq..Tk-1,
     the caches [B,H,Lcap,d] keys/values 0..Tk-1; ``demand_in``/``demand_out``
     are [B,H,Lcap] fp32 (may be one tensor: updated in place); ``tau_bh`` an
-    optional [B,H] fp32 tensor of per-head multipliers.  Returns ``out``."""
+    optional [B,H] fp32 tensor of per-head multipliers; ``lse_out`` and
+    ``rowsum_out`` optional [B,H,Tq] fp32 (what ``bwd`` needs).  Returns ``out``."""
     import torch
 
     if q.dim() != 4 or kcache.dim() != 4 or vcache.shape != kcache.shape:
@@ -302,6 +324,7 @@ def prefill(q, kcache, vcache, Tk: int, tau: float = 1.0, mode: int = ATTN_DILUT
                       demand_in.data_ptr() if demand_in is not None else None,
                       demand_out.data_ptr() if demand_out is not None else None,
                       lse_out.data_ptr() if lse_out is not None else None,
+                      rowsum_out.data_ptr() if rowsum_out is not None else None,
                       workspace.data_ptr() if workspace is not None else None, ws_bytes,
                       _stream_handle(q.device))
     if st != ATTN_OK:

@@ -46,8 +46,10 @@ int check_device() {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Do [a, a+na) and [b, b+nb) share a byte?
+// Do [a, a+na) and [b, b+nb) share a byte?  A NULL pointer (an absent
+// optional argument) overlaps nothing.
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b) return false;
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return x < y + nb && y < x + na;
 }
@@ -311,16 +313,16 @@ size_t attn_prefill_workspace_bytes(int B, int H, int Tq, int Tk, int d, int mod
 int attn_prefill(const void *q, const void *kcache, const void *vcache, void *out, int B, int H,
                  int Tq, int Tk, int Lcap, int d, float tau, const float *tau_bh, int mode,
                  float eps, int dtype, const float *demand_in, float *demand_out, float *lse_out,
-                 void *workspace, size_t workspace_bytes, void *hip_stream) {
+                 float *rowsum_out, void *workspace, size_t workspace_bytes, void *hip_stream) {
   if (!q || !kcache || !vcache || !out) return ATTN_EINVAL;
   if (mode != ATTN_TEMPERED && mode != ATTN_DILUTION) return ATTN_EINVAL;
-  if (mode == ATTN_TEMPERED && (demand_in || demand_out)) return ATTN_EINVAL;
+  if (mode == ATTN_TEMPERED && (demand_in || demand_out || rowsum_out)) return ATTN_EINVAL;
   if (!shape_ok(B, H, Lcap) || Tq < 1 || Tk < Tq || Lcap < Tk) return ATTN_EINVAL;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EINVAL;
   if (!std::isfinite(tau) || tau < 0.0f) return ATTN_EINVAL;
   if (!std::isfinite(eps) || eps < 0.0f) return ATTN_EINVAL;
   if (!head_dim_ok(d, dtype)) return ATTN_ENOTSUP;
-  const void *ptrs[8] = {q, kcache, vcache, out, demand_in, demand_out, lse_out, tau_bh};
+  const void *ptrs[9] = {q, kcache, vcache, out, demand_in, demand_out, lse_out, rowsum_out, tau_bh};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return ATTN_EINVAL;
   const size_t BH = (size_t)B * H, esz = dtype == ATTN_BF16 ? 2 : 4;
@@ -335,14 +337,19 @@ int attn_prefill(const void *q, const void *kcache, const void *vcache, void *ou
     return overlaps(p, n, q, qbytes) || overlaps(p, n, kcache, cbytes) ||
            overlaps(p, n, vcache, cbytes) || overlaps(p, n, out, qbytes);
   };
-  if (lse_out && hits_tensor(lse_out, rbytes)) return ATTN_EINVAL;
-  if (demand_out && hits_tensor(demand_out, dbytes)) return ATTN_EINVAL;
-  if (lse_out && demand_out && overlaps(lse_out, rbytes, demand_out, dbytes)) return ATTN_EINVAL;
-  if (demand_in && lse_out && overlaps(demand_in, dbytes, lse_out, rbytes)) return ATTN_EINVAL;
-  if (demand_in && overlaps(demand_in, dbytes, out, qbytes)) return ATTN_EINVAL;
+  if (hits_tensor(lse_out, rbytes) || hits_tensor(rowsum_out, rbytes) ||
+      hits_tensor(demand_out, dbytes))
+    return ATTN_EINVAL;
+  if (overlaps(lse_out, rbytes, demand_out, dbytes) || overlaps(lse_out, rbytes, rowsum_out, rbytes) ||
+      overlaps(rowsum_out, rbytes, demand_out, dbytes))
+    return ATTN_EINVAL;
+  if (overlaps(demand_in, dbytes, lse_out, rbytes) || overlaps(demand_in, dbytes, rowsum_out, rbytes))
+    return ATTN_EINVAL;
+  if (overlaps(demand_in, dbytes, out, qbytes)) return ATTN_EINVAL;
   const size_t tbytes = BH * sizeof(float);
-  if (tau_bh && (hits_tensor(tau_bh, tbytes) || (lse_out && overlaps(tau_bh, tbytes, lse_out, rbytes)) ||
-                 (demand_out && overlaps(tau_bh, tbytes, demand_out, dbytes))))
+  if (tau_bh && (hits_tensor(tau_bh, tbytes) || overlaps(tau_bh, tbytes, lse_out, rbytes) ||
+                 overlaps(tau_bh, tbytes, rowsum_out, rbytes) ||
+                 overlaps(tau_bh, tbytes, demand_out, dbytes)))
     return ATTN_EINVAL;
   if (demand_in && demand_out && demand_in != demand_out &&
       overlaps(demand_in, dbytes, demand_out, dbytes))
@@ -380,6 +387,7 @@ int attn_prefill(const void *q, const void *kcache, const void *vcache, void *ou
   if (e != hipSuccess) return fail_hip(e);
   a.demand_in = nullptr;
   a.demand_out = nullptr;
+  a.rowsum_out = rowsum_out;
   return finish(bf16 ? attn::launch_rows_bf16(attn::kRowShare, a, s)
                      : attn::launch_rows_f32(attn::kRowShare, a, s));
 }
@@ -388,10 +396,11 @@ int attn_prefill(const void *q, const void *kcache, const void *vcache, void *ou
 
 namespace {
 
-// Workspace layout of a backward pass: four per-row fp32 arrays (lse2, 1/r,
-// delta/r, rho), then for dilution the committed demand and the later blocks'
+// Workspace layout of a backward pass: five per-row fp32 arrays (lse2, 1/r,
+// delta/r, rho, <q_i, dQ_i / c>), then for dilution the committed demand and the later blocks'
 // gradient sums, per (32-row block, key), and the bf16 [B,H,T,d] array of
 // softmax-weighted keys.
+constexpr size_t kBwdRowArrays = 5;
 struct BwdWorkspace {
   size_t row_bytes, cin_bytes, gin_bytes, pk_bytes, total;
 };
@@ -403,7 +412,7 @@ bool bwd_workspace(int B, int H, int T, int mode, BwdWorkspace *ws) {
   ws->cin_bytes = mode == ATTN_DILUTION ? round_up(BH * attn::cin_floats_per_head(T, 0) * 4) : 0;
   ws->gin_bytes = mode == ATTN_DILUTION ? round_up(BH * attn::gin_floats_per_head(T) * 4) : 0;
   ws->pk_bytes = mode == ATTN_DILUTION ? round_up(BH * (size_t)T * attn::kHeadDim * 2) : 0;
-  ws->total = 4 * ws->row_bytes + ws->cin_bytes + ws->gin_bytes + ws->pk_bytes;
+  ws->total = kBwdRowArrays * ws->row_bytes + ws->cin_bytes + ws->gin_bytes + ws->pk_bytes;
   return true;
 }
 
@@ -419,10 +428,10 @@ size_t attn_bwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype)
   return ws.total;
 }
 
-int attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout,
-             const float *lse, const float *rowsum, void *dq, void *dk, void *dv, int B, int H,
-             int T, int d, float tau, int mode, float eps, int dtype, void *workspace,
-             size_t workspace_bytes, void *hip_stream) {
+int attn_bwd_ex(const void *q, const void *k, const void *v, const void *out, const void *dout,
+                const float *lse, const float *rowsum, void *dq, void *dk, void *dv, int B, int H,
+                int T, int d, float tau, const float *tau_bh, int mode, float eps, int dtype,
+                float *dtau_out, void *workspace, size_t workspace_bytes, void *hip_stream) {
   if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv) return ATTN_EINVAL;
   if (mode != ATTN_TEMPERED && mode != ATTN_DILUTION) return ATTN_EINVAL;
   if (mode == ATTN_DILUTION && !rowsum) return ATTN_EINVAL;
@@ -430,6 +439,7 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *out, const
   for (const void *p : ptrs)
     if (!aligned16(p)) return ATTN_EINVAL;
   if (rowsum && !aligned16(rowsum)) return ATTN_EINVAL;
+  if ((tau_bh && !aligned16(tau_bh)) || (dtau_out && !aligned16(dtau_out))) return ATTN_EINVAL;
   if (!shape_ok(B, H, T)) return ATTN_EINVAL;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EINVAL;
   if (!std::isfinite(tau) || tau < 0.0f) return ATTN_EINVAL;
@@ -446,6 +456,19 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *out, const
       return ATTN_EINVAL;
     for (int j = 0; j < i; ++j)
       if (overlaps(grads[i], nbytes, grads[j], nbytes)) return ATTN_EINVAL;
+  }
+  const size_t tbytes = (size_t)B * H * sizeof(float);
+  if (tau_bh)
+    for (const void *g : grads)
+      if (overlaps(g, nbytes, tau_bh, tbytes)) return ATTN_EINVAL;
+  if (dtau_out) {
+    const void *tensors[8] = {q, k, v, out, dout, dq, dk, dv};
+    for (const void *in : tensors)
+      if (overlaps(dtau_out, tbytes, in, nbytes)) return ATTN_EINVAL;
+    if (overlaps(dtau_out, tbytes, lse, rbytes) ||
+        (rowsum && overlaps(dtau_out, tbytes, rowsum, rbytes)) ||
+        (tau_bh && overlaps(dtau_out, tbytes, tau_bh, tbytes)))
+      return ATTN_EINVAL;
   }
   BwdWorkspace ws;
   if (!bwd_workspace(B, H, T, mode, &ws)) return ATTN_EINVAL;
@@ -469,19 +492,34 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *out, const
   a.invr = reinterpret_cast<float *>(wsp + ws.row_bytes);
   a.dri = reinterpret_cast<float *>(wsp + 2 * ws.row_bytes);
   a.rho = reinterpret_cast<float *>(wsp + 3 * ws.row_bytes);
+  a.trow = reinterpret_cast<float *>(wsp + 4 * ws.row_bytes);
+  char *wtail = wsp + kBwdRowArrays * ws.row_bytes;
   if (mode == ATTN_DILUTION) {
-    a.cin = reinterpret_cast<float *>(wsp + 4 * ws.row_bytes);
-    a.gin = reinterpret_cast<float *>(wsp + 4 * ws.row_bytes + ws.cin_bytes);
-    a.pk = wsp + 4 * ws.row_bytes + ws.cin_bytes + ws.gin_bytes;
+    a.cin = reinterpret_cast<float *>(wtail);
+    a.gin = reinterpret_cast<float *>(wtail + ws.cin_bytes);
+    a.pk = wtail + ws.cin_bytes + ws.gin_bytes;
   }
   a.BH = B * H;
   a.T = T;
-  const double c = (double)tau / std::sqrt((double)d);
+  const double rsd = 1.0 / std::sqrt((double)d);
+  // with tau_bh the kernels multiply c and c2 by head bh's multiplier
+  const double c = tau_bh ? rsd : (double)tau * rsd;
   a.c = (float)c;
   a.c2 = (float)(c * 1.4426950408889634);
+  a.rsd = (float)rsd;
+  a.tau_bh = tau_bh;
+  a.dtau = dtau_out;
   a.eps = eps;
   hipError_t e = attn::launch_bwd_bf16(mode, a, reinterpret_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? ATTN_OK : fail_hip(e);
+}
+
+int attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout,
+             const float *lse, const float *rowsum, void *dq, void *dk, void *dv, int B, int H,
+             int T, int d, float tau, int mode, float eps, int dtype, void *workspace,
+             size_t workspace_bytes, void *hip_stream) {
+  return attn_bwd_ex(q, k, v, out, dout, lse, rowsum, dq, dk, dv, B, H, T, d, tau, nullptr, mode,
+                     eps, dtype, nullptr, workspace, workspace_bytes, hip_stream);
 }
 
 size_t attn_decode_workspace_bytes(int S, int H, int Lcap, int d) {

@@ -12,8 +12,11 @@
 //   dp_ij     = dsigma_ij / D_ij - G_ij,   G_ij = sum_{i'' >= i} g_i''j
 //               (every later row's committed demand contains p_ij)
 //   dS_ij     = p_ij (dp_ij - rho_i),      rho_i = sum_j p_ij dp_ij
-//   dQ_i = c sum_j dS_ij k_j,   dK_j = c sum_i dS_ij q_i,   c = tau / sqrt(d).
+//   dQ_i = c sum_j dS_ij k_j,   dK_j = c sum_i dS_ij q_i,   c = tau / sqrt(d),
+//   dL/dtau = sum_ij dS_ij <q_i, k_j> / sqrt(d) = sum_i <q_i, dQ_i / c> / sqrt(d)
+// (the last form needs no division by tau, so it holds at tau = 0 too).
 // Tempered attention is the same with a = p: dS_ij = p_ij (dA_ij - delta_i).
+// With per-head multipliers (a learned temperature) c and tau are head bh's.
 //
 // Passes (dilution; tempered skips 2, 3 and 4):
 //   1 bwd_prep_kernel   per row: log2-domain lse, 1/r, delta/r
@@ -22,7 +25,8 @@
 //                       the sum of g over every later block (G's block part)
 //   4 rows_bf16_kernel  (the tempered forward with V := K) PK_i = sum_j p_ij k_j
 //   5 bwd_dq_kernel     per 32 query rows: X_i = sum_j p_ij dp_ij k_j and rho,
-//                       then dQ_i = c (X_i - rho_i PK_i)
+//                       then dQ_i = c (X_i - rho_i PK_i) and <q_i, dQ_i / c>
+//   5b bwd_dtau_kernel  (when dL/dtau is asked for) per head: the rows' sum
 //   6 bwd_dkdv_kernel   per 32 keys: dK, dV
 // Both in-block scans (the column prefix inside D and the column suffix
 // inside G) are matrix-core products against constant triangular operands,
@@ -38,6 +42,11 @@ namespace attn {
 constexpr int kColKeys = 128;   // keys per workgroup in the column kernels (4 waves x 32)
 constexpr int kTRow = 36;       // LDS row stride of the transposed 32-row blocks (32 + 4 pad)
 constexpr float kInvDMax = 18446744073709551616.0f;   // 2^64: clamp on 1/D (eps = 0 only)
+
+// The multiplier of head bh (1 when the scales carry a scalar tau).
+__device__ __forceinline__ float head_tau(const BwdArgs &a, int bh) {
+  return a.tau_bh ? a.tau_bh[bh] : 1.0f;
+}
 
 __device__ __forceinline__ bf16x8 word_operand(uint32_t w) {
   const u32x4 u = {w, 0u, 0u, 0u};
@@ -199,6 +208,7 @@ __global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdArgs a, int nqs) {
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int bh = blockIdx.x % a.BH;
   const int kb = blockIdx.x / a.BH;
+  const float c2 = a.c2 * head_tau(a, bh);
   const int T = a.T;
   const int kw0 = kb * kColKeys + 32 * w;
   const bool wave_live = kw0 < T;
@@ -277,8 +287,8 @@ __global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdArgs a, int nqs) {
         col_scores(sb[buf][i], kf, vf, l32, h, s, da);
         const uint32_t cw = key < 32 * qs ? cin[cin_block_offset(qs, 0) + key] : eps_word;
         ColTerms t;
-        if (32 * qs == kw0) col_terms<true>(s, da, sb[buf][i], sc, cw, a.c2, l32, h, t);
-        else col_terms<false>(s, da, sb[buf][i], sc, cw, a.c2, l32, h, t);
+        if (32 * qs == kw0) col_terms<true>(s, da, sb[buf][i], sc, cw, c2, l32, h, t);
+        else col_terms<false>(s, da, sb[buf][i], sc, cw, c2, l32, h, t);
         float part = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) part += t.g[r];
@@ -382,6 +392,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nqs) {
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int bh = blockIdx.x % a.BH;
   const int kb = blockIdx.x / a.BH;
+  const float tb = head_tau(a, bh), c2 = a.c2 * tb, cs = a.c * tb;
   const int T = a.T;
   const int kw0 = kb * kColKeys + 32 * w;
   const bool wave_live = kw0 < T;
@@ -483,9 +494,9 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nqs) {
         }
       }
       if (32 * qs == kw0)
-        dkdv_block<DIL, true>(sb[buf], st[buf], kf, vf, sc, cw, gw, a.c2, l32, h, dkt, dvt);
+        dkdv_block<DIL, true>(sb[buf], st[buf], kf, vf, sc, cw, gw, c2, l32, h, dkt, dvt);
       else
-        dkdv_block<DIL, false>(sb[buf], st[buf], kf, vf, sc, cw, gw, a.c2, l32, h, dkt, dvt);
+        dkdv_block<DIL, false>(sb[buf], st[buf], kf, vf, sc, cw, gw, c2, l32, h, dkt, dvt);
     }
     if (qs + 1 < nqs) store_block(buf ^ 1);
     __syncthreads();
@@ -500,8 +511,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nqs) {
     for (int g = 0; g < 4; ++g) {
       const int d0 = 32 * u + 8 * g + 4 * h;
       u32x2 kk, vv;
-      kk[0] = pack_bf16x2(dkt[u][4 * g] * a.c, dkt[u][4 * g + 1] * a.c);
-      kk[1] = pack_bf16x2(dkt[u][4 * g + 2] * a.c, dkt[u][4 * g + 3] * a.c);
+      kk[0] = pack_bf16x2(dkt[u][4 * g] * cs, dkt[u][4 * g + 1] * cs);
+      kk[1] = pack_bf16x2(dkt[u][4 * g + 2] * cs, dkt[u][4 * g + 3] * cs);
       vv[0] = pack_bf16x2(dvt[u][4 * g], dvt[u][4 * g + 1]);
       vv[1] = pack_bf16x2(dvt[u][4 * g + 2], dvt[u][4 * g + 3]);
       *reinterpret_cast<u32x2 *>(dK + d0) = kk;
@@ -629,6 +640,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int bh = blockIdx.x % a.BH;
   const int qb = nqb - 1 - blockIdx.x / a.BH;   // heaviest query blocks first
+  const float tb = head_tau(a, bh), c2 = a.c2 * tb, cs = a.c * tb;
   const int T = a.T;
   const int q0 = qb * 128;
   const int qw0 = q0 + 32 * w;
@@ -733,10 +745,10 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
       for (int t = 0; t < 2; ++t) {
         if (kt < kd)
           dq_subtile<DIL, false>(st, qf, gf, dc, sel, kl, vl, tl, t, cw[t], gw[t], lse2, invr, dri,
-                                 qrel, l32, h, a.c2);
+                                 qrel, l32, h, c2);
         else
           dq_subtile<DIL, true>(st, qf, gf, dc, sel, kl, vl, tl, t, cw[t], gw[t], lse2, invr, dri,
-                                qrel, l32, h, a.c2);
+                                qrel, l32, h, c2);
       }
     }
     if (kt + 1 < nkt) store_tile(buf ^ 1);
@@ -751,7 +763,10 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
     if (h == 0) a.rho[ridx] = rho;
     PK = reinterpret_cast<const __bf16 *>(a.pk) + head + (size_t)row * kHeadDim;
   }
-  // lane: query; element (half u, r): dim 32u + acc_row(r, h)
+  // lane: query; element (half u, r): dim 32u + acc_row(r, h).  With u_i =
+  // dQ_i / c, <q_i, u_i> = sum_j dS_ij <q_i, k_j>: this row's share of dL/dtau.
+  const __bf16 *Qr = Q + (size_t)row * kHeadDim;
+  float tq = 0.0f;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int d0 = 8 * g + 4 * h;
@@ -766,8 +781,26 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
     float lo[4], hi[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      lo[i] = a.c * __builtin_fmaf(-rho, pk[i], st.x0[4 * g + i]);
-      hi[i] = a.c * __builtin_fmaf(-rho, pk[4 + i], st.x1[4 * g + i]);
+      lo[i] = __builtin_fmaf(-rho, pk[i], st.x0[4 * g + i]);
+      hi[i] = __builtin_fmaf(-rho, pk[4 + i], st.x1[4 * g + i]);
+    }
+    if (a.dtau) {
+      const u32x2 ql = *reinterpret_cast<const u32x2 *>(Qr + d0);
+      const u32x2 qh = *reinterpret_cast<const u32x2 *>(Qr + 32 + d0);
+      const uint32_t q0w = ql[0], q1w = ql[1], q2w = qh[0], q3w = qh[1];
+      tq = __builtin_fmaf(bf16_lo(q0w), lo[0], tq);
+      tq = __builtin_fmaf(bf16_hi(q0w), lo[1], tq);
+      tq = __builtin_fmaf(bf16_lo(q1w), lo[2], tq);
+      tq = __builtin_fmaf(bf16_hi(q1w), lo[3], tq);
+      tq = __builtin_fmaf(bf16_lo(q2w), hi[0], tq);
+      tq = __builtin_fmaf(bf16_hi(q2w), hi[1], tq);
+      tq = __builtin_fmaf(bf16_lo(q3w), hi[2], tq);
+      tq = __builtin_fmaf(bf16_hi(q3w), hi[3], tq);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo[i] *= cs;
+      hi[i] *= cs;
     }
     u32x2 l2, h2;
     l2[0] = pack_bf16x2(lo[0], lo[1]);
@@ -777,6 +810,33 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
     *reinterpret_cast<u32x2 *>(dQ + d0) = l2;
     *reinterpret_cast<u32x2 *>(dQ + 32 + d0) = h2;
   }
+  if (a.dtau) {
+    tq = both_halves_sum(tq);
+    if (h == 0) a.trow[ridx] = tq;
+  }
+}
+
+// dL/dtau of each head: the rows' <q_i, u_i> summed in a fixed order (strided
+// per thread, then a tree over the workgroup), times 1/sqrt(d).
+__global__ void __launch_bounds__(256) bwd_dtau_kernel(BwdArgs a) {
+  __shared__ float red[256];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const float *tr = a.trow + (size_t)bh * a.T;
+  float acc = 0.0f;
+  for (int i = tid; i < a.T; i += 256) acc += tr[i];
+  red[tid] = acc;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) red[tid] += red[tid + off];
+    __syncthreads();
+  }
+  if (tid == 0) a.dtau[bh] = red[0] * a.rsd;
+}
+
+hipError_t launch_dtau(const BwdArgs &a, hipStream_t s) {
+  if (!a.dtau) return hipSuccess;
+  hipLaunchKernelGGL(bwd_dtau_kernel, dim3((unsigned)a.BH), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_bf16(int mode, const BwdArgs &a, hipStream_t s) {
@@ -799,6 +859,7 @@ hipError_t launch_bwd_bf16(int mode, const BwdArgs &a, hipStream_t s) {
     f.T = f.Tq = f.kstride = a.T;
     f.D = kHeadDim;
     f.ksplit = 1;
+    f.tau_bh = a.tau_bh;
     f.c2 = a.c2;
     f.eps = a.eps;
     e = launch_colsum_bf16(f, s);
@@ -816,11 +877,14 @@ hipError_t launch_bwd_bf16(int mode, const BwdArgs &a, hipStream_t s) {
     t.T = t.Tq = t.kstride = a.T;
     t.D = kHeadDim;
     t.ksplit = 1;
+    t.tau_bh = a.tau_bh;
     t.c2 = a.c2;
     e = launch_rows_bf16(kRowTempered, t, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3((unsigned)(nqb * a.BH)), dim3(256), 0, s, a, nqb);
     e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_dtau(a, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3((unsigned)(nkb * a.BH)), dim3(256), 0, s, a,
                        nqs);
@@ -828,6 +892,8 @@ hipError_t launch_bwd_bf16(int mode, const BwdArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3((unsigned)(nqb * a.BH)), dim3(256), 0, s, a,
                        nqb);
     e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_dtau(a, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3((unsigned)(nkb * a.BH)), dim3(256), 0, s, a,
                        nqs);

@@ -105,9 +105,13 @@ struct BwdArgs {
   float *cin;             // committed demand + eps per (32-row block, key), bf16 pairs
   float *gin;             // later blocks' share-gradient sums per (block, key), bf16 pairs
   void *pk;               // [BH*T*64] bf16 workspace: sum_j p_ij k_j (dilution)
+  const float *tau_bh;    // [BH] per-head multipliers, or NULL (then c2, c carry tau)
+  float *dtau;            // [BH] output: dL/dtau per head, or NULL
+  float *trow;            // [BH*T] workspace: <q_i, dQ_i / c> per row (for dtau)
   int BH, T;
-  float c2;               // tau / sqrt(d) * log2(e)
-  float c;                // tau / sqrt(d)
+  float c2;               // tau / sqrt(d) * log2(e)  (with tau_bh: log2(e) / sqrt(d))
+  float c;                // tau / sqrt(d)            (with tau_bh: 1 / sqrt(d))
+  float rsd;              // 1 / sqrt(d)
   float eps;
 };
 
