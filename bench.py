@@ -18,7 +18,9 @@ usual 2.5x of the forward's 4*d).  Then, also under ``components``:
     rows through attn_prefill, the demand carried in place between chunks;
   * head dimension 128: dilution and tempered forward at B=1, H=20,
     T=16384, d=128 (a 2.7B focal model's attention) with per-head learned
-    temperature multipliers, and one decode step over a 32-sequence x
+    temperature multipliers, their backward (attn_bwd_ex with those
+    multipliers, returning dL/dtau per head as well), and one decode step
+    over a 32-sequence x
     32768-key cache at H=20, d=128 with per-(sequence, head) multipliers.
 
 Printed: one JSON line.  ``value`` is the dilution forward's algorithmic
@@ -359,7 +361,39 @@ def main():
 
     d128_ms = time_launches(d128, 3)
     log(f"bench: d=128 forward ms dilution {d128_ms[0]:.4f} tempered {d128_ms[1]:.4f}")
-    del q8, k8, v8, out8, ws8
+
+    # d = 128 backward with the per-head multipliers and their gradient
+    g8 = dev_bf16(draw_grad(w8.B, w8.H, w8.T, w8.d, w8.seed))
+    lse8 = torch.empty((w8.B, w8.H, w8.T), dtype=torch.float32, device=dev)
+    rs8, lse8t = torch.empty_like(lse8), torch.empty_like(lse8)
+    out8t = torch.empty_like(q8)
+    dtau8 = torch.empty((w8.B, w8.H), dtype=torch.float32, device=dev)
+    ab.prefill(q8, k8, v8, w8.T, tau=1.0, mode=ab.ATTN_DILUTION, eps=w8.eps, out=out8,
+               workspace=ws8, tau_bh=tau8, lse_out=lse8, rowsum_out=rs8)
+    ab.prefill(q8, k8, v8, w8.T, tau=1.0, mode=ab.ATTN_TEMPERED, out=out8t, tau_bh=tau8,
+               lse_out=lse8t)
+    del ws8
+    bws8, _ = ab.bwd_workspace(w8.B, w8.H, w8.T, ab.ATTN_DILUTION, ab.ATTN_BF16, dev, w8.d)
+    grads8 = [torch.empty_like(q8) for _ in range(3)]
+
+    def bwd128(events):
+        if events is not None:
+            events[0].record(stream)
+        ab.bwd(q8, k8, v8, out8, g8, lse8, rs8, mode=ab.ATTN_DILUTION, eps=w8.eps,
+               dq=grads8[0], dk=grads8[1], dv=grads8[2], workspace=bws8, tau_bh=tau8,
+               dtau_out=dtau8)
+        if events is not None:
+            events[1].record(stream)
+        ab.bwd(q8, k8, v8, out8t, g8, lse8t, None, mode=ab.ATTN_TEMPERED,
+               dq=grads8[0], dk=grads8[1], dv=grads8[2], workspace=bws8, tau_bh=tau8,
+               dtau_out=dtau8)
+        if events is not None:
+            events[2].record(stream)
+
+    bwd8_ms = time_launches(bwd128, 3)
+    log(f"bench: d=128 backward ms (per-head tau, dL/dtau) dilution {bwd8_ms[0]:.4f} "
+        f"tempered {bwd8_ms[1]:.4f}")
+    del q8, k8, v8, out8, out8t, g8, bws8, grads8, lse8, rs8, lse8t
 
     S8, H8, L8 = 32, 20, 32768
     kc8, vc8 = decode_cache_device(S8, H8, L8, 128, dw.seed + 1, device=dev)
@@ -455,7 +489,12 @@ def main():
                 "dilution_ms": round(d128_ms[0], 4),
                 "dilution_tflops": round(flops8 / (d128_ms[0] * 1e-3) / 1e12, 3),
                 "tempered_ms": round(d128_ms[1], 4),
-                "tempered_tflops": round(flops8 / (d128_ms[1] * 1e-3) / 1e12, 3)},
+                "tempered_tflops": round(flops8 / (d128_ms[1] * 1e-3) / 1e12, 3),
+                "dilution_bwd_ms": round(bwd8_ms[0], 4),
+                "dilution_bwd_tflops": round(2.5 * flops8 / (bwd8_ms[0] * 1e-3) / 1e12, 3),
+                "tempered_bwd_ms": round(bwd8_ms[1], 4),
+                "tempered_bwd_tflops": round(2.5 * flops8 / (bwd8_ms[1] * 1e-3) / 1e12, 3),
+                "bwd_outputs": "dq, dk, dv and dL/dtau per head"},
             "decode_d128_32k": {
                 "S": S8, "H": H8, "L": L8, "d": 128, "ms": round(dec8_ms, 4),
                 "gbps": round(dec8_bytes / (dec8_ms * 1e-3) / 1e9, 2), "bytes": dec8_bytes,

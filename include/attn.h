@@ -118,7 +118,7 @@ size_t attn_bwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype)
  *                       ignored and may be NULL for ATTN_TEMPERED)
  *   dq, dk, dv          [B,H,T,d] bf16 outputs, overwritten; may not alias
  *                       each other or any input
- *   B, H, T, d, tau, mode, eps  as passed to the forward
+ *   B, H, T, d, tau, mode, eps  as passed to the forward (d = 64 or 128)
  *   dtype               ATTN_BF16 (ATTN_F32 returns ATTN_ENOTSUP)
  *   workspace           device scratch of >= attn_bwd_workspace_bytes(...)
  *                       bytes; contents on entry are ignored

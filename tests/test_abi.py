@@ -141,7 +141,12 @@ def test_bwd_workspace_sizes():
     assert want <= got <= want + 8 * 256
     assert 5 * rows <= ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 0, 1) <= 5 * rows + 5 * 256
     assert ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 0) == 0   # fp32: not supported
-    assert ab.attn_bwd_workspace_bytes(1, 16, 16384, 128, 1, 1) == 0
+    assert ab.attn_bwd_workspace_bytes(1, 16, 16384, 96, 1, 1) == 0
+    # d = 128: the softmax-weighted keys are twice as wide
+    assert (ab.attn_bwd_workspace_bytes(1, 16, 16384, 128, 1, 1)
+            - ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 1)) == 16 * 16384 * 64 * 2
+    assert (ab.attn_bwd_workspace_bytes(1, 16, 16384, 128, 0, 1)
+            == ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 0, 1))
 
 
 def test_prefill_workspace_sizes():
@@ -239,7 +244,9 @@ def bwd(**kw):
     (dict(tau=-1.0), ab.ATTN_EINVAL),
     (dict(eps=float("nan")), ab.ATTN_EINVAL),
     (dict(dtype=0), ab.ATTN_ENOTSUP),                 # fp32 backward
-    (dict(d=128), ab.ATTN_ENOTSUP),
+    (dict(d=96), ab.ATTN_ENOTSUP),
+    (dict(d=128), ab.ATTN_EWORKSPACE),                # d = 128 is supported
+    (dict(d=128, dtype=0), ab.ATTN_ENOTSUP),
     (dict(dk=FAKE + 0x7000000), ab.ATTN_EINVAL),      # dk aliases dq
     (dict(dv=FAKE), ab.ATTN_EINVAL),                  # dv aliases q
     (dict(), ab.ATTN_EWORKSPACE),

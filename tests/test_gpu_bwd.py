@@ -223,3 +223,65 @@ def test_bwd_dtau_heavy_keys_t1024():
                           oracle.Bf16(g), 1.0, w.eps, 1, tau_bh=taus, want_dtau=True)
     check_grads(got[:3], ref[:3], "heavy per-head")
     check_dtau(got[3], ref[0], inp, g, taus, ref[4], "heavy per-head")
+
+
+# ---------------------------------------------------------------- d = 128
+
+@pytest.mark.parametrize("mode", [0, 1], ids=["tempered", "dilution"])
+@pytest.mark.parametrize("T", [1, 33, 129, 300])
+def test_bwd_d128_ragged_lengths(mode, T):
+    """Head dimension 128 (the focal models' heads), scalar tau."""
+    inp = draw_qkv(1, 2, T, 128, "bf16", seed=2300 + T)
+    g = draw_grad(1, 2, T, 128, seed=2300 + T)
+    got = run_bwd(inp, g, 1.0, mode)
+    ref = oracle_grads(inp, g, 1.0, mode)
+    check_grads(got[:3], ref[:3], f"d128 mode={mode} T={T}")
+    if mode == 1:
+        assert np.max(np.abs(got[3] - ref[3]) / ref[3]) <= 1e-2
+
+
+@pytest.mark.parametrize("mode", [0, 1], ids=["tempered", "dilution"])
+def test_bwd_d128_per_head_tau_and_dtau(mode):
+    """d = 128 with learned per-head multipliers sqrt(128)/t, t ~ U[5, 10],
+    on the heavy-key recipe at T = 1024: gradients and dL/dtau per head."""
+    w = PREFILL["focal_d128_t16k"]
+    inp = prefill_inputs(w, T=1024, H=3)
+    g = draw_grad(1, 3, 1024, 128, seed=w.seed)
+    taus = learned_tau(1, 3, 128, seed=w.seed)
+    got = run_bwd_heads(inp, g, mode, tau_bh=taus, eps=w.eps)
+    ref = oracle.attn_bwd(oracle.Bf16(inp.q), oracle.Bf16(inp.k), oracle.Bf16(inp.v),
+                          oracle.Bf16(g), 1.0, w.eps, mode, tau_bh=taus, want_dtau=True)
+    check_grads(got[:3], ref[:3], f"d128 per-head mode={mode}")
+    check_dtau(got[3], ref[0], inp, g, taus, ref[4], f"d128 per-head mode={mode}")
+
+
+def test_bwd_d128_value_totals_focal_t16k():
+    """At the focal workload's full length (T = 16384, d = 128, learned
+    per-head multipliers; 4 of its 20 heads): the dV rows sum to the dO rows'
+    sum in either mode, and every gradient and dL/dtau is finite."""
+    import torch
+
+    w = PREFILL["focal_d128_t16k"]
+    inp = prefill_inputs(w, H=4)
+    g = draw_grad(1, 4, w.T, 128, seed=w.seed)
+    taus = learned_tau(1, 4, 128, seed=w.seed)
+    do_sum = (g.astype(np.uint32) << 16).view(np.float32).astype(np.float64).sum(axis=2)
+    for mode in (0, 1):
+        got = run_bwd_heads(inp, g, mode, tau_bh=taus, eps=w.eps)
+        dv_sum = got[2].astype(np.float64).sum(axis=2)
+        err = np.max(np.abs(dv_sum - do_sum)) / np.max(np.abs(do_sum))
+        print(f"focal d128 t16k mode={mode} dV total rel err {err:.3e}")
+        assert err <= 5e-3
+        for x in (got[0], got[1], got[3]):
+            assert np.all(np.isfinite(x))
+        torch.cuda.empty_cache()
+
+
+def test_bwd_d128_deterministic():
+    inp = draw_qkv(1, 2, 300, 128, "bf16", seed=78)
+    g = draw_grad(1, 2, 300, 128, seed=78)
+    taus = learned_tau(1, 2, 128, seed=78)
+    a = run_bwd_heads(inp, g, 1, tau_bh=taus)
+    b = run_bwd_heads(inp, g, 1, tau_bh=taus)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)

@@ -236,10 +236,10 @@ def fwd(q, k, v, tau: float = 1.0, mode: int = ATTN_TEMPERED, eps: float = 1e-6,
     return out
 
 
-def bwd_workspace(B, H, T, mode, dtype_code, device):
+def bwd_workspace(B, H, T, mode, dtype_code, device, d=64):
     import torch
 
-    n = attn_bwd_workspace_bytes(B, H, T, 64, mode, dtype_code)
+    n = attn_bwd_workspace_bytes(B, H, T, d, mode, dtype_code)
     if n == 0:
         raise AttnError(ATTN_ENOTSUP, "attn_bwd_workspace_bytes")
     return torch.empty(n, dtype=torch.uint8, device=device), n
@@ -248,7 +248,7 @@ def bwd_workspace(B, H, T, mode, dtype_code, device):
 def bwd(q, k, v, out, dout, lse, rowsum=None, tau: float = 1.0, mode: int = ATTN_TEMPERED,
         eps: float = 1e-6, dq=None, dk=None, dv=None, workspace=None, tau_bh=None,
         dtau_out=None):
-    """Run attn_bwd_ex on [B,H,T,64] tensors (``lse``/``rowsum`` from the
+    """Run attn_bwd_ex on [B,H,T,d] tensors, d = 64 or 128 (``lse``/``rowsum`` from the
     forward's ``lse_out``/``rowsum_out``); ``tau_bh`` an optional [B,H] fp32
     tensor of per-head multipliers (as given to ``prefill``), ``dtau_out`` an
     optional [B,H] fp32 tensor that receives dL/dtau per head.  Returns
@@ -264,7 +264,7 @@ def bwd(q, k, v, out, dout, lse, rowsum=None, tau: float = 1.0, mode: int = ATTN
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     if workspace is None:
-        workspace, ws_bytes = bwd_workspace(B, H, T, mode, code, q.device)
+        workspace, ws_bytes = bwd_workspace(B, H, T, mode, code, q.device, d)
     else:
         ws_bytes = workspace.numel() * workspace.element_size()
     for name, t in (("tau_bh", tau_bh), ("dtau_out", dtau_out)):

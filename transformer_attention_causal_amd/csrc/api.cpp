@@ -405,13 +405,13 @@ struct BwdWorkspace {
   size_t row_bytes, cin_bytes, gin_bytes, pk_bytes, total;
 };
 
-bool bwd_workspace(int B, int H, int T, int mode, BwdWorkspace *ws) {
+bool bwd_workspace(int B, int H, int T, int d, int mode, BwdWorkspace *ws) {
   const size_t BH = (size_t)B * H;
   if (BH > (size_t)INT32_MAX) return false;
   ws->row_bytes = round_up(BH * (size_t)T * sizeof(float));
   ws->cin_bytes = mode == ATTN_DILUTION ? round_up(BH * attn::cin_floats_per_head(T, 0) * 4) : 0;
   ws->gin_bytes = mode == ATTN_DILUTION ? round_up(BH * attn::gin_floats_per_head(T) * 4) : 0;
-  ws->pk_bytes = mode == ATTN_DILUTION ? round_up(BH * (size_t)T * attn::kHeadDim * 2) : 0;
+  ws->pk_bytes = mode == ATTN_DILUTION ? round_up(BH * (size_t)T * d * 2) : 0;
   ws->total = kBwdRowArrays * ws->row_bytes + ws->cin_bytes + ws->gin_bytes + ws->pk_bytes;
   return true;
 }
@@ -421,10 +421,10 @@ bool bwd_workspace(int B, int H, int T, int mode, BwdWorkspace *ws) {
 extern "C" {
 
 size_t attn_bwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype) {
-  if (!shape_ok(B, H, T) || d != attn::kHeadDim || dtype != ATTN_BF16) return 0;
+  if (!shape_ok(B, H, T) || dtype != ATTN_BF16 || !head_dim_ok(d, dtype)) return 0;
   if (mode != ATTN_TEMPERED && mode != ATTN_DILUTION) return 0;
   BwdWorkspace ws;
-  if (!bwd_workspace(B, H, T, mode, &ws)) return 0;
+  if (!bwd_workspace(B, H, T, d, mode, &ws)) return 0;
   return ws.total;
 }
 
@@ -444,7 +444,7 @@ int attn_bwd_ex(const void *q, const void *k, const void *v, const void *out, co
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EINVAL;
   if (!std::isfinite(tau) || tau < 0.0f) return ATTN_EINVAL;
   if (!std::isfinite(eps) || eps < 0.0f) return ATTN_EINVAL;
-  if (d != attn::kHeadDim || dtype != ATTN_BF16) return ATTN_ENOTSUP;
+  if (dtype != ATTN_BF16 || !head_dim_ok(d, dtype)) return ATTN_ENOTSUP;
   // the three gradients may not alias each other or any input
   const size_t nbytes = (size_t)B * H * (size_t)T * d * 2;
   const size_t rbytes = (size_t)B * H * (size_t)T * sizeof(float);
@@ -471,7 +471,7 @@ int attn_bwd_ex(const void *q, const void *k, const void *v, const void *out, co
       return ATTN_EINVAL;
   }
   BwdWorkspace ws;
-  if (!bwd_workspace(B, H, T, mode, &ws)) return ATTN_EINVAL;
+  if (!bwd_workspace(B, H, T, d, mode, &ws)) return ATTN_EINVAL;
   if (!workspace || workspace_bytes < ws.total || !aligned16(workspace)) return ATTN_EWORKSPACE;
   const int dev_status = check_device();
   if (dev_status != ATTN_OK) return dev_status;
@@ -501,6 +501,7 @@ int attn_bwd_ex(const void *q, const void *k, const void *v, const void *out, co
   }
   a.BH = B * H;
   a.T = T;
+  a.D = d;
   const double rsd = 1.0 / std::sqrt((double)d);
   // with tau_bh the kernels multiply c and c2 by head bh's multiplier
   const double c = tau_bh ? rsd : (double)tau * rsd;

@@ -18,6 +18,10 @@
 // Tempered attention is the same with a = p: dS_ij = p_ij (dA_ij - delta_i).
 // With per-head multipliers (a learned temperature) c and tau are head bh's.
 //
+// Head dimension D = 64 or 128 (a template parameter of every kernel); at
+// D = 128 the dQ and dK/dV kernels run one workgroup per CU, which doubles
+// the registers per lane for the doubled operands and accumulators.
+//
 // Passes (dilution; tempered skips 2, 3 and 4):
 //   1 bwd_prep_kernel   per row: log2-domain lse, 1/r, delta/r
 //   2 colsum_bf16_kernel (the forward's) committed demand per 32-row block
@@ -55,8 +59,9 @@ __device__ __forceinline__ bf16x8 word_operand(uint32_t w) {
 
 // ------------------------------------------------------------------ prep
 
-// Eight lanes per row: delta = <dO_i, o_i> from 16-byte loads, then the
-// per-row scalars the other passes read.
+// Eight lanes per row: delta = <dO_i, o_i> from 16-byte loads (D/64 per
+// lane), then the per-row scalars the other passes read.
+template <int D>
 __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a, int dilution) {
   const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
   const size_t row = gid >> 3;
@@ -64,15 +69,18 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a, int dilution) 
   const bool live = row < (size_t)a.BH * a.T;
   float acc = 0.0f;
   if (live) {
-    const u32x4 ov = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const __bf16 *>(a.o) +
-                                                      row * kHeadDim + 8 * dc);
-    const u32x4 gv = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const __bf16 *>(a.dout) +
-                                                      row * kHeadDim + 8 * dc);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t x = ov[i], y = gv[i];
-      acc = __builtin_fmaf(bf16_lo(x), bf16_lo(y), acc);
-      acc = __builtin_fmaf(bf16_hi(x), bf16_hi(y), acc);
+    for (int j = 0; j < D / 64; ++j) {
+      const size_t off = row * D + 64 * j + 8 * dc;
+      const u32x4 ov = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const __bf16 *>(a.o) + off);
+      const u32x4 gv =
+          *reinterpret_cast<const u32x4 *>(reinterpret_cast<const __bf16 *>(a.dout) + off);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t x = ov[i], y = gv[i];
+        acc = __builtin_fmaf(bf16_lo(x), bf16_lo(y), acc);
+        acc = __builtin_fmaf(bf16_hi(x), bf16_hi(y), acc);
+      }
     }
   }
   acc += __shfl_xor(acc, 1, 8);
@@ -127,9 +135,10 @@ __device__ __forceinline__ ScanConsts scan_consts(int l32, int h) {
 // Per-block LDS staging shared by the column kernels: Q and dO rows of one
 // 32-row block (row-major, the A operands of S = Q K^T and dA = dO V^T), and
 // the per-row scalars.
+template <int D>
 struct ColBlock {
-  __bf16 q[32 * kKRow];
-  __bf16 g[32 * kKRow];
+  __bf16 q[32 * Geom<D>::kKRow];
+  __bf16 g[32 * Geom<D>::kKRow];
   float lse2[32], invr[32], dri[32], rho[32];
 };
 
@@ -157,14 +166,16 @@ __device__ __forceinline__ void col_rowvals(const float *src, int h, float *dst)
 }
 
 // The block's S = Q K^T and dA = dO V^T for this wave's keys.
-__device__ __forceinline__ void col_scores(const ColBlock &b, const bf16x8 *kf, const bf16x8 *vf,
-                                           int l32, int h, f32x16 &s, f32x16 &da) {
-  const __bf16 *qrow = b.q + l32 * kKRow;
-  const __bf16 *grow = b.g + l32 * kKRow;
+template <int D>
+__device__ __forceinline__ void col_scores(const ColBlock<D> &b, const bf16x8 *kf,
+                                           const bf16x8 *vf, int l32, int h, f32x16 &s,
+                                           f32x16 &da) {
+  const __bf16 *qrow = b.q + l32 * Geom<D>::kKRow;
+  const __bf16 *grow = b.g + l32 * Geom<D>::kKRow;
   s = zero16();
   da = zero16();
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < Geom<D>::kChunks; ++c) {
     s = mfma32(lds_frag(qrow, c, h), kf[c], s);
     da = mfma32(lds_frag(grow, c, h), vf[c], da);
   }
@@ -176,8 +187,8 @@ struct ColTerms {
   float p[16], invd[16], sg[16], dsg[16], g[16];
 };
 
-template <bool DIAG>
-__device__ __forceinline__ void col_terms(const f32x16 &s, const f32x16 &da, const ColBlock &b,
+template <bool DIAG, int D>
+__device__ __forceinline__ void col_terms(const f32x16 &s, const f32x16 &da, const ColBlock<D> &b,
                                           const ScanConsts &sc, uint32_t cin_word, float c2,
                                           int l32, int h, ColTerms &t) {
   float lq[16], iq[16], rq[16];
@@ -202,8 +213,11 @@ __device__ __forceinline__ void col_terms(const f32x16 &s, const f32x16 &da, con
 
 // Pass 3: sums of g over the blocks below each block, walking up two 32-row
 // blocks (one 64-row LDS tile) per barrier.
+template <int D>
 __global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdArgs a, int nqs) {
-  __shared__ __attribute__((aligned(16))) ColBlock sb[2][2];
+  constexpr int kRowChunks = D / 8;              // 16-byte chunks per row
+  constexpr int kPairLoads = 64 * kRowChunks / 256;   // per thread, per tensor
+  __shared__ __attribute__((aligned(16))) ColBlock<D> sb[2][2];
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int bh = blockIdx.x % a.BH;
@@ -213,7 +227,7 @@ __global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdArgs a, int nqs) {
   const int kw0 = kb * kColKeys + 32 * w;
   const bool wave_live = kw0 < T;
   const int key = kw0 + l32;
-  const size_t head = (size_t)bh * T * kHeadDim;
+  const size_t head = (size_t)bh * T * D;
   const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + head;
   const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + head;
   const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + head;
@@ -225,11 +239,11 @@ __global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdArgs a, int nqs) {
   uint32_t *gin = reinterpret_cast<uint32_t *>(a.gin) + (size_t)bh * gin_floats_per_head(T);
   const uint32_t eps_word = split2_bf16(fmaxf(a.eps, FLT_MIN));
 
-  bf16x8 kf[4], vf[4];
+  bf16x8 kf[Geom<D>::kChunks], vf[Geom<D>::kChunks];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    kf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(K, key, T, 2 * c + h));
-    vf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(V, key, T, 2 * c + h));
+  for (int c = 0; c < Geom<D>::kChunks; ++c) {
+    kf[c] = __builtin_bit_cast(bf16x8, load_row_chunk<D>(K, key, T, 2 * c + h));
+    vf[c] = __builtin_bit_cast(bf16x8, load_row_chunk<D>(V, key, T, 2 * c + h));
   }
   const ScanConsts sc = scan_consts(l32, h);
   __builtin_amdgcn_s_waitcnt(0);
@@ -237,15 +251,15 @@ __global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdArgs a, int nqs) {
   // walk pairs of 32-row blocks (2P, 2P + 1), last pair first
   const int qs_lo = (kb * kColKeys) / 32;
   const int p_lo = qs_lo / 2, p_hi = (nqs - 1) / 2;
-  u32x4 qreg[2], greg[2];
+  u32x4 qreg[kPairLoads], greg[kPairLoads];
   float lreg = 0.0f, ireg = 0.0f, rreg = 0.0f;
   auto load_pair = [&](int P) {             // 64 P < T for every pair loaded
     const int row0 = 64 * P;
-    const int bytes = (T - row0) * (kHeadDim * 2);
-    const auto rq = make_rsrc(Q + (size_t)row0 * kHeadDim, bytes);
-    const auto rg = make_rsrc(G + (size_t)row0 * kHeadDim, bytes);
+    const int bytes = (T - row0) * (D * 2);
+    const auto rq = make_rsrc(Q + (size_t)row0 * D, bytes);
+    const auto rg = make_rsrc(G + (size_t)row0 * D, bytes);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kPairLoads; ++i) {
       qreg[i] = buf_load16(rq, 16u * (tid + 256 * i));
       greg[i] = buf_load16(rg, 16u * (tid + 256 * i));
     }
@@ -260,9 +274,12 @@ __global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdArgs a, int nqs) {
   };
   auto store_pair = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *reinterpret_cast<u32x4 *>(&sb[buf][i].q[(tid >> 3) * kKRow + (tid & 7) * 8]) = qreg[i];
-      *reinterpret_cast<u32x4 *>(&sb[buf][i].g[(tid >> 3) * kKRow + (tid & 7) * 8]) = greg[i];
+    for (int i = 0; i < kPairLoads; ++i) {
+      // chunk u of the 64-row tile: row u / kRowChunks (block row / 32)
+      const int u = tid + 256 * i, row = u / kRowChunks, ch = u % kRowChunks;
+      const int off = (row & 31) * Geom<D>::kKRow + ch * 8;
+      *reinterpret_cast<u32x4 *>(&sb[buf][row >> 5].q[off]) = qreg[i];
+      *reinterpret_cast<u32x4 *>(&sb[buf][row >> 5].g[off]) = greg[i];
     }
     if (tid < 64) {
       sb[buf][tid >> 5].lse2[tid & 31] = lreg;
@@ -305,13 +322,14 @@ __global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdArgs a, int nqs) {
 // Pass 5: dK and dV for this wave's keys.  The transposed Q and dO blocks
 // (dim-major) are the A operands of dK^T += Q^T dS and dV^T += dO^T a; the
 // packed dS and a (S layout) are their B operands.
+template <int D>
 struct ColBlockT {
-  __bf16 qt[kHeadDim * kTRow];
-  __bf16 gt[kHeadDim * kTRow];
+  __bf16 qt[D * kTRow];
+  __bf16 gt[D * kTRow];
 };
 
-template <bool DIL, bool DIAG>
-__device__ __forceinline__ void dkdv_block(const ColBlock &b, const ColBlockT &bt,
+template <bool DIL, bool DIAG, int D>
+__device__ __forceinline__ void dkdv_block(const ColBlock<D> &b, const ColBlockT<D> &bt,
                                            const bf16x8 *kf, const bf16x8 *vf,
                                            const ScanConsts &sc, uint32_t cin_word,
                                            uint32_t gin_word, float c2, int l32, int h,
@@ -369,7 +387,7 @@ __device__ __forceinline__ void dkdv_block(const ColBlock &b, const ColBlockT &b
   const bf16x8 sf[2] = {pack8(ds), pack8(ds + 8)};
   const bf16x8 af[2] = {pack8(aw), pack8(aw + 8)};
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < Geom<D>::kOBlocks; ++u) {
     const __bf16 *qtr = bt.qt + (32 * u + l32) * kTRow;
     const __bf16 *gtr = bt.gt + (32 * u + l32) * kTRow;
 #pragma unroll
@@ -380,14 +398,25 @@ __device__ __forceinline__ void dkdv_block(const ColBlock &b, const ColBlockT &b
   }
 }
 
-template <bool DIL>
-__global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nqs) {
-  __shared__ __attribute__((aligned(16))) ColBlock sb[2];
-  __shared__ __attribute__((aligned(16))) ColBlockT st[2];
+// Waves per SIMD the dQ and dK/dV kernels are built for: two at d = 64; one
+// at d = 128, whose operand fragments and accumulators need twice the registers.
+template <int D>
+struct BwdOccupancy {
+  static constexpr int value = D > 64 ? 1 : 2;
+};
+
+template <bool DIL, int D>
+__global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel(BwdArgs a,
+                                                                                 int nqs) {
+  constexpr int kKR = Geom<D>::kKRow, kCh = Geom<D>::kChunks, kOB = Geom<D>::kOBlocks;
+  constexpr int kRowChunks = D / 8;   // 16-byte chunks per row
+  constexpr int kBlkLoads = 32 * kRowChunks / 256;   // per thread, per tensor
+  __shared__ __attribute__((aligned(16))) ColBlock<D> sb[2];
+  __shared__ __attribute__((aligned(16))) ColBlockT<D> st[2];
   // dilution: this workgroup's K and V rows (the B operands of S and dA) sit
   // in LDS and are read per block, which keeps the kernel within two waves'
   // registers per SIMD without spills; the tempered form keeps them in registers
-  __shared__ __attribute__((aligned(16))) __bf16 sKV[DIL ? 2 : 1][DIL ? kColKeys * kKRow : 8];
+  __shared__ __attribute__((aligned(16))) __bf16 sKV[DIL ? 2 : 1][DIL ? kColKeys * kKR : 8];
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int bh = blockIdx.x % a.BH;
@@ -397,7 +426,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nqs) {
   const int kw0 = kb * kColKeys + 32 * w;
   const bool wave_live = kw0 < T;
   const int key = kw0 + l32;
-  const size_t head = (size_t)bh * T * kHeadDim;
+  const size_t head = (size_t)bh * T * D;
   const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + head;
   const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + head;
   const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + head;
@@ -413,45 +442,52 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nqs) {
   }
   const uint32_t eps_word = split2_bf16(fmaxf(a.eps, FLT_MIN));
 
-  bf16x8 kf[4], vf[4];
+  bf16x8 kf[kCh], vf[kCh];
   const __bf16 *krow = nullptr, *vrow = nullptr;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const u32x4 kc = load_row_chunk(K, key, T, 2 * c + h), vc = load_row_chunk(V, key, T, 2 * c + h);
+  for (int c = 0; c < kCh; ++c) {
+    const u32x4 kc = load_row_chunk<D>(K, key, T, 2 * c + h);
+    const u32x4 vc = load_row_chunk<D>(V, key, T, 2 * c + h);
     if constexpr (DIL) {
-      *reinterpret_cast<u32x4 *>(&sKV[0][(32 * w + l32) * kKRow + 16 * c + 8 * h]) = kc;
-      *reinterpret_cast<u32x4 *>(&sKV[1][(32 * w + l32) * kKRow + 16 * c + 8 * h]) = vc;
+      *reinterpret_cast<u32x4 *>(&sKV[0][(32 * w + l32) * kKR + 16 * c + 8 * h]) = kc;
+      *reinterpret_cast<u32x4 *>(&sKV[1][(32 * w + l32) * kKR + 16 * c + 8 * h]) = vc;
     } else {
       kf[c] = __builtin_bit_cast(bf16x8, kc);
       vf[c] = __builtin_bit_cast(bf16x8, vc);
     }
   }
   if constexpr (DIL) {
-    krow = &sKV[0][(32 * w + l32) * kKRow];
-    vrow = &sKV[1][(32 * w + l32) * kKRow];
+    krow = &sKV[0][(32 * w + l32) * kKR];
+    vrow = &sKV[1][(32 * w + l32) * kKR];
   }
   const ScanConsts sc = scan_consts(l32, h);
-  f32x16 dkt[2] = {zero16(), zero16()}, dvt[2] = {zero16(), zero16()};
+  f32x16 dkt[kOB], dvt[kOB];
+#pragma unroll
+  for (int u = 0; u < kOB; ++u) dkt[u] = dvt[u] = zero16();
   __builtin_amdgcn_s_waitcnt(0);
 
   const int qs_lo = (kb * kColKeys) / 32;
-  // loaders: thread tid holds row tid >> 3, chunk tid & 7 of the Q and dO
-  // blocks; for the transposed copies, rows 2 kp, 2 kp + 1 (kp = tid & 15)
-  // and chunk (tid >> 4) & 7 of the two tensors (Q for tid < 128, dO above).
-  u32x4 qreg, greg, tr0, tr1;
+  // loaders: chunk u = tid + 256 i of the Q and dO blocks is row
+  // u / kRowChunks, chunk u % kRowChunks; for the transposed copies, item
+  // u = tid + 256 i covers rows 2 kp, 2 kp + 1 (kp = u & 15) and chunk
+  // (u >> 4) % kRowChunks of Q (when (u >> 4) < kRowChunks) or dO.
+  u32x4 qreg[kBlkLoads], greg[kBlkLoads], tr0[kBlkLoads], tr1[kBlkLoads];
   float lreg = 0.0f, ireg = 0.0f, rreg = 0.0f, hreg = 0.0f;
-  const int kp = tid & 15, tdc = (tid >> 4) & 7;
-  const bool tq = tid < 128;
+  const int kp = tid & 15;
   auto load_block = [&](int qs) {
     const int row0 = 32 * qs;
-    const int bytes = (T - row0) * (kHeadDim * 2);
-    const auto rq = make_rsrc(Q + (size_t)row0 * kHeadDim, bytes);
-    const auto rg = make_rsrc(G + (size_t)row0 * kHeadDim, bytes);
-    qreg = buf_load16(rq, 16u * tid);
-    greg = buf_load16(rg, 16u * tid);
-    const auto rt = tq ? rq : rg;
-    tr0 = buf_load16(rt, 256u * kp + 16u * tdc);
-    tr1 = buf_load16(rt, 256u * kp + 128u + 16u * tdc);
+    const int bytes = (T - row0) * (D * 2);
+    const auto rq = make_rsrc(Q + (size_t)row0 * D, bytes);
+    const auto rg = make_rsrc(G + (size_t)row0 * D, bytes);
+#pragma unroll
+    for (int i = 0; i < kBlkLoads; ++i) {
+      const int u = tid + 256 * i, tdc = (u >> 4) % kRowChunks;
+      qreg[i] = buf_load16(rq, 16u * u);
+      greg[i] = buf_load16(rg, 16u * u);
+      const auto rt = (u >> 4) < kRowChunks ? rq : rg;
+      tr0[i] = buf_load16(rt, 4u * D * kp + 16u * tdc);
+      tr1[i] = buf_load16(rt, 4u * D * kp + 2u * D + 16u * tdc);
+    }
     if (tid < 32) {
       const int row = row0 + tid;
       const bool ok = row < T;
@@ -463,9 +499,15 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nqs) {
     }
   };
   auto store_block = [&](int buf) {
-    *reinterpret_cast<u32x4 *>(&sb[buf].q[(tid >> 3) * kKRow + (tid & 7) * 8]) = qreg;
-    *reinterpret_cast<u32x4 *>(&sb[buf].g[(tid >> 3) * kKRow + (tid & 7) * 8]) = greg;
-    store_rows_transposed(tq ? st[buf].qt : st[buf].gt, kTRow, kp, tdc, tr0, tr1);
+#pragma unroll
+    for (int i = 0; i < kBlkLoads; ++i) {
+      const int u = tid + 256 * i, tdc = (u >> 4) % kRowChunks;
+      const int off = (u / kRowChunks) * kKR + (u % kRowChunks) * 8;
+      *reinterpret_cast<u32x4 *>(&sb[buf].q[off]) = qreg[i];
+      *reinterpret_cast<u32x4 *>(&sb[buf].g[off]) = greg[i];
+      store_rows_transposed((u >> 4) < kRowChunks ? st[buf].qt : st[buf].gt, kTRow, kp, tdc,
+                            tr0[i], tr1[i]);
+    }
     if (tid < 32) {
       sb[buf].lse2[tid] = lreg;
       sb[buf].invr[tid] = ireg;
@@ -488,7 +530,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nqs) {
       }
       if constexpr (DIL) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < kCh; ++c) {
           kf[c] = lds_frag(krow, c, h);
           vf[c] = lds_frag(vrow, c, h);
         }
@@ -503,10 +545,10 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nqs) {
   }
   if (!wave_live || key >= T) return;
   // lane: key; element (u, r): dim 32u + acc_row(r, h)
-  __bf16 *dK = reinterpret_cast<__bf16 *>(a.dk) + head + (size_t)key * kHeadDim;
-  __bf16 *dV = reinterpret_cast<__bf16 *>(a.dv) + head + (size_t)key * kHeadDim;
+  __bf16 *dK = reinterpret_cast<__bf16 *>(a.dk) + head + (size_t)key * D;
+  __bf16 *dV = reinterpret_cast<__bf16 *>(a.dv) + head + (size_t)key * D;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < kOB; ++u) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d0 = 32 * u + 8 * g + 4 * h;
@@ -558,24 +600,26 @@ __device__ __forceinline__ DqConsts dq_consts(int l32, int h) {
   return c;
 }
 
+template <int D>
 struct DqState {
-  f32x16 x0, x1;   // X^T[d][query] = sum_j p_ij dp_ij k_j (tempered: sum_j dS_ij k_j)
+  f32x16 x[Geom<D>::kOBlocks];   // X^T[d][query] = sum_j p_ij dp_ij k_j (tempered:
+                                 // sum_j dS_ij k_j); x[u] holds d in [32u, 32u + 32)
   f32x4 rho;       // sum_j p_ij dp_ij, every element equal (dilution)
 };
 
-template <bool DIL, bool DIAG>
-__device__ __forceinline__ void dq_subtile(DqState &st, const bf16x8 *qf, const bf16x8 *gf,
+template <bool DIL, bool DIAG, int D>
+__device__ __forceinline__ void dq_subtile(DqState<D> &st, const bf16x8 *qf, const bf16x8 *gf,
                                            const DqConsts &dc, const bf16x8 &sel,
                                            const __bf16 *kt_lds, const __bf16 *vt_lds,
                                            const __bf16 *ktt_lds, int t, uint32_t cin_word,
                                            uint32_t gin_word, float lse2, float invr, float dri,
                                            int qrel, int l32, int h, float c2) {
   // S^T and dA^T for keys 32t.. of the tile (lane = query)
-  const __bf16 *krow = kt_lds + (32 * t + l32) * kKRow;
-  const __bf16 *vrow = vt_lds + (32 * t + l32) * kKRow;
+  const __bf16 *krow = kt_lds + (32 * t + l32) * Geom<D>::kKRow;
+  const __bf16 *vrow = vt_lds + (32 * t + l32) * Geom<D>::kKRow;
   f32x16 s = zero16(), da = zero16();
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < Geom<D>::kChunks; ++c) {
     s = mfma32(lds_frag(krow, c, h), qf[c], s);
     da = mfma32(lds_frag(vrow, c, h), gf[c], da);
   }
@@ -619,22 +663,28 @@ __device__ __forceinline__ void dq_subtile(DqState &st, const bf16x8 *qf, const 
 #pragma unroll
     for (int r = 0; r < 16; ++r) e[r] = p[r] * __builtin_fmaf(dsg[r], invd[r], -G[r]);
     const bf16x8 ef0 = pack8(e), ef1 = pack8(e + 8);
-    pv_update(st.x0, st.x1, ktt_lds, t, l32, h, ef0, ef1);
+    pv_update_d<D>(st.x, ktt_lds, t, l32, h, ef0, ef1);
     st.rho = mfma16(sel, ef0, st.rho);
     st.rho = mfma16(sel, ef1, st.rho);
   } else {
     float ds[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) ds[r] = p[r] * (da[r] - dri);
-    pv_update(st.x0, st.x1, ktt_lds, t, l32, h, pack8(ds), pack8(ds + 8));
+    pv_update_d<D>(st.x, ktt_lds, t, l32, h, pack8(ds), pack8(ds + 8));
   }
 }
 
-template <bool DIL>
-__global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2 * kKTile];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[2 * kKTile];
-  __shared__ __attribute__((aligned(16))) __bf16 sKt[2 * kVTile];
+template <bool DIL, int D>
+__global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dq_kernel(BwdArgs a,
+                                                                               int nqb) {
+  constexpr int kKR = Geom<D>::kKRow, kKT = Geom<D>::kKTile, kVT = Geom<D>::kVTile;
+  constexpr int kCh = Geom<D>::kChunks, kOB = Geom<D>::kOBlocks;
+  constexpr int kRowChunks = D / 8;                     // 16-byte chunks per row
+  constexpr int kTileLoads = kBN * kRowChunks / 256;    // per thread, per tensor
+  constexpr int kTrLoads = (kBN / 2) * kRowChunks / 256;   // transposed row pairs
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2 * kKT];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[2 * kKT];
+  __shared__ __attribute__((aligned(16))) __bf16 sKt[2 * kVT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
@@ -646,7 +696,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
   const int qw0 = q0 + 32 * w;
   const bool wave_live = qw0 < T;
   const int kd = qw0 / kBN;
-  const size_t head = (size_t)bh * T * kHeadDim;
+  const size_t head = (size_t)bh * T * D;
   const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + head;
   const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + head;
   const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + head;
@@ -656,11 +706,11 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
   const int row = qw0 + l32;
   const bool row_ok = row < T;
 
-  bf16x8 qf[4], gf[4];
+  bf16x8 qf[kCh], gf[kCh];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    qf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(Q, row, T, 2 * c + h));
-    gf[c] = __builtin_bit_cast(bf16x8, load_row_chunk(G, row, T, 2 * c + h));
+  for (int c = 0; c < kCh; ++c) {
+    qf[c] = __builtin_bit_cast(bf16x8, load_row_chunk<D>(Q, row, T, 2 * c + h));
+    gf[c] = __builtin_bit_cast(bf16x8, load_row_chunk<D>(G, row, T, 2 * c + h));
   }
   const size_t ridx = (size_t)bh * T + (row_ok ? row : T - 1);
   const float lse2 = row_ok ? a.lse2[ridx] : kNoRow;
@@ -678,31 +728,43 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
               (size_t)16 * qsb * (qsb + 1);
   }
 
-  u32x4 kreg[2], vreg[2], treg[2];
-  const uint32_t koff0 = 16u * tid, koff1 = 16u * (tid + 256);
-  const uint32_t toff0 = 256u * (tid & 31) + 16u * (tid >> 5), toff1 = toff0 + 128u;
+  // loaders: chunk u = tid + 256 i of the K and V tiles is key u / kRowChunks,
+  // chunk u % kRowChunks; transposed item u covers keys 2 (u & 31) and
+  // 2 (u & 31) + 1, chunk u >> 5.
+  u32x4 kreg[kTileLoads], vreg[kTileLoads], treg[kTrLoads][2];
   auto load_tile = [&](int kt) {   // kt < nkt, so its first key is < T
     const int key0 = kt * kBN;
-    const int bytes = (T - key0) * (kHeadDim * 2);
-    const auto rk = make_rsrc(K + (size_t)key0 * kHeadDim, bytes);
-    const auto rv = make_rsrc(V + (size_t)key0 * kHeadDim, bytes);
-    kreg[0] = buf_load16(rk, koff0);
-    kreg[1] = buf_load16(rk, koff1);
-    vreg[0] = buf_load16(rv, koff0);
-    vreg[1] = buf_load16(rv, koff1);
-    treg[0] = buf_load16(rk, toff0);
-    treg[1] = buf_load16(rk, toff1);
+    const int bytes = (T - key0) * (D * 2);
+    const auto rk = make_rsrc(K + (size_t)key0 * D, bytes);
+    const auto rv = make_rsrc(V + (size_t)key0 * D, bytes);
+#pragma unroll
+    for (int i = 0; i < kTileLoads; ++i) {
+      kreg[i] = buf_load16(rk, 16u * (tid + 256 * i));
+      vreg[i] = buf_load16(rv, 16u * (tid + 256 * i));
+    }
+#pragma unroll
+    for (int i = 0; i < kTrLoads; ++i) {
+      const int u = tid + 256 * i;
+      const uint32_t off = 4u * D * (u & 31) + 16u * (u >> 5);
+      treg[i][0] = buf_load16(rk, off);
+      treg[i][1] = buf_load16(rk, off + 2u * D);
+    }
   };
   auto store_tile = [&](int buf) {
-    __bf16 *k = sK + buf * kKTile;
-    __bf16 *v = sV + buf * kKTile;
+    __bf16 *k = sK + buf * kKT;
+    __bf16 *v = sV + buf * kKT;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kTileLoads; ++i) {
       const int u = tid + 256 * i;
-      *reinterpret_cast<u32x4 *>(k + (u >> 3) * kKRow + (u & 7) * 8) = kreg[i];
-      *reinterpret_cast<u32x4 *>(v + (u >> 3) * kKRow + (u & 7) * 8) = vreg[i];
+      const int off = (u / kRowChunks) * kKR + (u % kRowChunks) * 8;
+      *reinterpret_cast<u32x4 *>(k + off) = kreg[i];
+      *reinterpret_cast<u32x4 *>(v + off) = vreg[i];
     }
-    store_rows_transposed(sKt + buf * kVTile, kVRow, tid & 31, tid >> 5, treg[0], treg[1]);
+#pragma unroll
+    for (int i = 0; i < kTrLoads; ++i) {
+      const int u = tid + 256 * i;
+      store_rows_transposed(sKt + buf * kVT, kVRow, u & 31, u >> 5, treg[i][0], treg[i][1]);
+    }
   };
   // committed demand (+eps) and later blocks' g sums of this wave's block on
   // keys kt*64 + 32t + l32
@@ -719,9 +781,9 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
     }
   };
 
-  DqState st;
-  st.x0 = zero16();
-  st.x1 = zero16();
+  DqState<D> st;
+#pragma unroll
+  for (int u = 0; u < kOB; ++u) st.x[u] = zero16();
   st.rho = zero4();
   __builtin_amdgcn_s_waitcnt(0);
 
@@ -737,78 +799,63 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
       load_words(kt + 1);
     }
     if (wave_live && kt <= kd) {
-      const __bf16 *kl = sK + buf * kKTile, *vl = sV + buf * kKTile, *tl = sKt + buf * kVTile;
+      const __bf16 *kl = sK + buf * kKT, *vl = sV + buf * kKT, *tl = sKt + buf * kVT;
       const int qrel = qw0 + l32 - kt * kBN;
       // one sub-tile at a time: the per-sub-tile temporaries would not fit
       // twice beside the accumulators
 #pragma unroll 1
       for (int t = 0; t < 2; ++t) {
         if (kt < kd)
-          dq_subtile<DIL, false>(st, qf, gf, dc, sel, kl, vl, tl, t, cw[t], gw[t], lse2, invr, dri,
-                                 qrel, l32, h, c2);
+          dq_subtile<DIL, false, D>(st, qf, gf, dc, sel, kl, vl, tl, t, cw[t], gw[t], lse2, invr,
+                                    dri, qrel, l32, h, c2);
         else
-          dq_subtile<DIL, true>(st, qf, gf, dc, sel, kl, vl, tl, t, cw[t], gw[t], lse2, invr, dri,
-                                qrel, l32, h, c2);
+          dq_subtile<DIL, true, D>(st, qf, gf, dc, sel, kl, vl, tl, t, cw[t], gw[t], lse2, invr,
+                                   dri, qrel, l32, h, c2);
       }
     }
     if (kt + 1 < nkt) store_tile(buf ^ 1);
     __syncthreads();
   }
   if (!wave_live || !row_ok) return;
-  __bf16 *dQ = reinterpret_cast<__bf16 *>(a.dq) + head + (size_t)row * kHeadDim;
+  __bf16 *dQ = reinterpret_cast<__bf16 *>(a.dq) + head + (size_t)row * D;
   float rho = 0.0f;
   const __bf16 *PK = nullptr;
   if constexpr (DIL) {
     rho = st.rho[0];
     if (h == 0) a.rho[ridx] = rho;
-    PK = reinterpret_cast<const __bf16 *>(a.pk) + head + (size_t)row * kHeadDim;
+    PK = reinterpret_cast<const __bf16 *>(a.pk) + head + (size_t)row * D;
   }
-  // lane: query; element (half u, r): dim 32u + acc_row(r, h).  With u_i =
+  // lane: query; element (block u, r): dim 32u + acc_row(r, h).  With u_i =
   // dQ_i / c, <q_i, u_i> = sum_j dS_ij <q_i, k_j>: this row's share of dL/dtau.
-  const __bf16 *Qr = Q + (size_t)row * kHeadDim;
+  const __bf16 *Qr = Q + (size_t)row * D;
   float tq = 0.0f;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int d0 = 8 * g + 4 * h;
-    float pk[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (DIL) {
-      const u32x2 lo = *reinterpret_cast<const u32x2 *>(PK + d0);
-      const u32x2 hi = *reinterpret_cast<const u32x2 *>(PK + 32 + d0);
-      const uint32_t w0 = lo[0], w1 = lo[1], w2 = hi[0], w3 = hi[1];
-      pk[0] = bf16_lo(w0); pk[1] = bf16_hi(w0); pk[2] = bf16_lo(w1); pk[3] = bf16_hi(w1);
-      pk[4] = bf16_lo(w2); pk[5] = bf16_hi(w2); pk[6] = bf16_lo(w3); pk[7] = bf16_hi(w3);
-    }
-    float lo[4], hi[4];
+  for (int u = 0; u < kOB; ++u) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo[i] = __builtin_fmaf(-rho, pk[i], st.x0[4 * g + i]);
-      hi[i] = __builtin_fmaf(-rho, pk[4 + i], st.x1[4 * g + i]);
-    }
-    if (a.dtau) {
-      const u32x2 ql = *reinterpret_cast<const u32x2 *>(Qr + d0);
-      const u32x2 qh = *reinterpret_cast<const u32x2 *>(Qr + 32 + d0);
-      const uint32_t q0w = ql[0], q1w = ql[1], q2w = qh[0], q3w = qh[1];
-      tq = __builtin_fmaf(bf16_lo(q0w), lo[0], tq);
-      tq = __builtin_fmaf(bf16_hi(q0w), lo[1], tq);
-      tq = __builtin_fmaf(bf16_lo(q1w), lo[2], tq);
-      tq = __builtin_fmaf(bf16_hi(q1w), lo[3], tq);
-      tq = __builtin_fmaf(bf16_lo(q2w), hi[0], tq);
-      tq = __builtin_fmaf(bf16_hi(q2w), hi[1], tq);
-      tq = __builtin_fmaf(bf16_lo(q3w), hi[2], tq);
-      tq = __builtin_fmaf(bf16_hi(q3w), hi[3], tq);
-    }
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * u + 8 * g + 4 * h;
+      float x[4];
+      if constexpr (DIL) {
+        const u32x2 pw = *reinterpret_cast<const u32x2 *>(PK + d0);
+        const float pk[4] = {bf16_lo(pw[0]), bf16_hi(pw[0]), bf16_lo(pw[1]), bf16_hi(pw[1])};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo[i] *= cs;
-      hi[i] *= cs;
+        for (int i = 0; i < 4; ++i) x[i] = __builtin_fmaf(-rho, pk[i], st.x[u][4 * g + i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = st.x[u][4 * g + i];
+      }
+      if (a.dtau) {
+        const u32x2 qw = *reinterpret_cast<const u32x2 *>(Qr + d0);
+        tq = __builtin_fmaf(bf16_lo(qw[0]), x[0], tq);
+        tq = __builtin_fmaf(bf16_hi(qw[0]), x[1], tq);
+        tq = __builtin_fmaf(bf16_lo(qw[1]), x[2], tq);
+        tq = __builtin_fmaf(bf16_hi(qw[1]), x[3], tq);
+      }
+      u32x2 o2;
+      o2[0] = pack_bf16x2(x[0] * cs, x[1] * cs);
+      o2[1] = pack_bf16x2(x[2] * cs, x[3] * cs);
+      *reinterpret_cast<u32x2 *>(dQ + d0) = o2;
     }
-    u32x2 l2, h2;
-    l2[0] = pack_bf16x2(lo[0], lo[1]);
-    l2[1] = pack_bf16x2(lo[2], lo[3]);
-    h2[0] = pack_bf16x2(hi[0], hi[1]);
-    h2[1] = pack_bf16x2(hi[2], hi[3]);
-    *reinterpret_cast<u32x2 *>(dQ + d0) = l2;
-    *reinterpret_cast<u32x2 *>(dQ + 32 + d0) = h2;
   }
   if (a.dtau) {
     tq = both_halves_sum(tq);
@@ -839,11 +886,12 @@ hipError_t launch_dtau(const BwdArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_bf16(int mode, const BwdArgs &a, hipStream_t s) {
+template <int D>
+hipError_t launch_bwd_d(int mode, const BwdArgs &a, hipStream_t s) {
   const bool dil = mode == 1;
   const size_t rows = (size_t)a.BH * a.T;
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, s,
-                     a, dil ? 1 : 0);
+  hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0,
+                     s, a, dil ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqs = (a.T + 31) / 32;
@@ -857,14 +905,14 @@ hipError_t launch_bwd_bf16(int mode, const BwdArgs &a, hipStream_t s) {
     f.cin = a.cin;
     f.BH = a.BH;
     f.T = f.Tq = f.kstride = a.T;
-    f.D = kHeadDim;
+    f.D = D;
     f.ksplit = 1;
     f.tau_bh = a.tau_bh;
     f.c2 = a.c2;
     f.eps = a.eps;
     e = launch_colsum_bf16(f, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_gsum_kernel, dim3((unsigned)(nkb * a.BH)), dim3(256), 0, s, a, nqs);
+    hipLaunchKernelGGL(bwd_gsum_kernel<D>, dim3((unsigned)(nkb * a.BH)), dim3(256), 0, s, a, nqs);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // PK = softmax-weighted keys: the tempered forward with the keys as values
@@ -875,30 +923,39 @@ hipError_t launch_bwd_bf16(int mode, const BwdArgs &a, hipStream_t s) {
     t.out = a.pk;
     t.BH = a.BH;
     t.T = t.Tq = t.kstride = a.T;
-    t.D = kHeadDim;
+    t.D = D;
     t.ksplit = 1;
     t.tau_bh = a.tau_bh;
     t.c2 = a.c2;
     e = launch_rows_bf16(kRowTempered, t, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3((unsigned)(nqb * a.BH)), dim3(256), 0, s, a, nqb);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    e = launch_dtau(a, s);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3((unsigned)(nkb * a.BH)), dim3(256), 0, s, a,
-                       nqs);
-  } else {
-    hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3((unsigned)(nqb * a.BH)), dim3(256), 0, s, a,
+    hipLaunchKernelGGL((bwd_dq_kernel<true, D>), dim3((unsigned)(nqb * a.BH)), dim3(256), 0, s, a,
                        nqb);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_dtau(a, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3((unsigned)(nkb * a.BH)), dim3(256), 0, s, a,
-                       nqs);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<true, D>), dim3((unsigned)(nkb * a.BH)), dim3(256), 0, s,
+                       a, nqs);
+  } else {
+    hipLaunchKernelGGL((bwd_dq_kernel<false, D>), dim3((unsigned)(nqb * a.BH)), dim3(256), 0, s,
+                       a, nqb);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_dtau(a, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<false, D>), dim3((unsigned)(nkb * a.BH)), dim3(256), 0, s,
+                       a, nqs);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_bf16(int mode, const BwdArgs &a, hipStream_t s) {
+  switch (a.D) {
+    case 64: return launch_bwd_d<64>(mode, a, s);
+    case 128: return launch_bwd_d<128>(mode, a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace attn

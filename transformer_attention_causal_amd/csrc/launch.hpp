@@ -7,7 +7,7 @@
 
 namespace attn {
 
-constexpr int kHeadDim = 64;  // the head dimension of the fp32 path and the backward
+constexpr int kHeadDim = 64;  // the head dimension of the fp32 path
 
 // Row-major passes over the causal score matrix (one workgroup per query
 // block).  lse2 is the log2-domain log-sum-exp of each row.
@@ -104,11 +104,11 @@ struct BwdArgs {
   float *rho;             // [BH*T] workspace: sum_j p_ij dp_ij (dilution)
   float *cin;             // committed demand + eps per (32-row block, key), bf16 pairs
   float *gin;             // later blocks' share-gradient sums per (block, key), bf16 pairs
-  void *pk;               // [BH*T*64] bf16 workspace: sum_j p_ij k_j (dilution)
+  void *pk;               // [BH*T*D] bf16 workspace: sum_j p_ij k_j (dilution)
   const float *tau_bh;    // [BH] per-head multipliers, or NULL (then c2, c carry tau)
   float *dtau;            // [BH] output: dL/dtau per head, or NULL
   float *trow;            // [BH*T] workspace: <q_i, dQ_i / c> per row (for dtau)
-  int BH, T;
+  int BH, T, D;           // D: head dimension, 64 or 128
   float c2;               // tau / sqrt(d) * log2(e)  (with tau_bh: log2(e) / sqrt(d))
   float c;                // tau / sqrt(d)            (with tau_bh: 1 / sqrt(d))
   float rsd;              // 1 / sqrt(d)
