@@ -503,7 +503,9 @@ def pin_bwd_dilution_softmax_limit():
 
 def pin_bwd_tau0_and_value_totals():
     """tau = 0 makes the bids independent of q and k (zero dq, dk); in either
-    mode the rows of A sum to one, so the dv rows sum to the dO rows' sum."""
+    mode the rows of A sum to one, so the dv rows sum to the dO rows' sum; and
+    adding one vector to every key adds a per-row constant to the logits,
+    which the softmax bids do not see, so the dk rows sum to zero."""
     rng = _rng(24)
     q, k, v, do = (rng.standard_normal((1, 1, 12, 8)) for _ in range(4))
     for mode in (0, 1):
@@ -511,6 +513,7 @@ def pin_bwd_tau0_and_value_totals():
         assert np.all(dq == 0.0) and np.all(dk == 0.0)
         dq, dk, dv, _ = oracle.attn_bwd(q, k, v, do, 1.1, 1e-6, mode)
         assert np.allclose(dv.sum(axis=2), do.sum(axis=2), rtol=0, atol=1e-12)
+        assert np.allclose(dk.sum(axis=2), 0.0, rtol=0, atol=1e-12)
 
 
 def pin_bwd_rowsums_brute_force():
