@@ -46,6 +46,17 @@ namespace attn {
 constexpr int kColKeys = 128;   // keys per workgroup in the column kernels (4 waves x 32)
 constexpr int kTRow = 36;       // LDS row stride of the transposed 32-row blocks (32 + 4 pad)
 constexpr float kInvDMax = 18446744073709551616.0f;   // 2^64: clamp on 1/D (eps = 0 only)
+constexpr float kNoClampEps = 1.0842021724855044e-19f;   // 2^-63
+
+// 1/D.  D >= eps (the committed demand and the bids are non-negative, and
+// committed + eps is stored to 2^-17 relative), so for eps >= 2^-63 the
+// reciprocal stays below 2^64: the clamp that keeps eps = 0 finite is then
+// left out (CLAMP = false), with the same bits.
+template <bool CLAMP>
+__device__ __forceinline__ float inv_denominator(float d) {
+  const float r = fast_rcp(d);
+  return CLAMP ? fminf(r, kInvDMax) : r;
+}
 
 // The multiplier of head bh (1 when the scales carry a scalar tau).
 __device__ __forceinline__ float head_tau(const BwdArgs &a, int bh) {
@@ -187,7 +198,7 @@ struct ColTerms {
   float p[16], invd[16], sg[16], dsg[16], g[16];
 };
 
-template <bool DIAG, int D>
+template <bool DIAG, bool CLAMP, int D>
 __device__ __forceinline__ void col_terms(const f32x16 &s, const f32x16 &da, const ColBlock<D> &b,
                                           const ScanConsts &sc, uint32_t cin_word, float c2,
                                           int l32, int h, ColTerms &t) {
@@ -203,7 +214,7 @@ __device__ __forceinline__ void col_terms(const f32x16 &s, const f32x16 &da, con
   d = mfma32(sc.ones, word_operand(cin_word), d);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float invd = fminf(fast_rcp(d[r]), kInvDMax);
+    const float invd = inv_denominator<CLAMP>(d[r]);
     t.invd[r] = invd;
     t.sg[r] = t.p[r] * invd;
     t.dsg[r] = __builtin_fmaf(da[r], iq[r], -rq[r]);
@@ -213,7 +224,7 @@ __device__ __forceinline__ void col_terms(const f32x16 &s, const f32x16 &da, con
 
 // Pass 3: sums of g over the blocks below each block, walking up two 32-row
 // blocks (one 64-row LDS tile) per barrier.
-template <int D>
+template <int D, bool CLAMP>
 __global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdArgs a, int nqs) {
   constexpr int kRowChunks = D / 8;              // 16-byte chunks per row
   constexpr int kPairLoads = 64 * kRowChunks / 256;   // per thread, per tensor
@@ -304,8 +315,8 @@ __global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdArgs a, int nqs) {
         col_scores(sb[buf][i], kf, vf, l32, h, s, da);
         const uint32_t cw = key < 32 * qs ? cin[cin_block_offset(qs, 0) + key] : eps_word;
         ColTerms t;
-        if (32 * qs == kw0) col_terms<true>(s, da, sb[buf][i], sc, cw, c2, l32, h, t);
-        else col_terms<false>(s, da, sb[buf][i], sc, cw, c2, l32, h, t);
+        if (32 * qs == kw0) col_terms<true, CLAMP>(s, da, sb[buf][i], sc, cw, c2, l32, h, t);
+        else col_terms<false, CLAMP>(s, da, sb[buf][i], sc, cw, c2, l32, h, t);
         float part = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) part += t.g[r];
@@ -328,7 +339,7 @@ struct ColBlockT {
   __bf16 gt[D * kTRow];
 };
 
-template <bool DIL, bool DIAG, int D>
+template <bool DIL, bool DIAG, bool CLAMP, int D>
 __device__ __forceinline__ void dkdv_block(const ColBlock<D> &b, const ColBlockT<D> &bt,
                                            const bf16x8 *kf, const bf16x8 *vf,
                                            const ScanConsts &sc, uint32_t cin_word,
@@ -350,7 +361,7 @@ __device__ __forceinline__ void dkdv_block(const ColBlock<D> &b, const ColBlockT
     float invd[16], sg[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      invd[r] = fminf(fast_rcp(d[r]), kInvDMax);
+      invd[r] = inv_denominator<CLAMP>(d[r]);
       sg[r] = p[r] * invd[r];
     }
     float iq[16];
@@ -405,7 +416,7 @@ struct BwdOccupancy {
   static constexpr int value = D > 64 ? 1 : 2;
 };
 
-template <bool DIL, int D>
+template <bool DIL, int D, bool CLAMP>
 __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel(BwdArgs a,
                                                                                  int nqs) {
   constexpr int kKR = Geom<D>::kKRow, kCh = Geom<D>::kChunks, kOB = Geom<D>::kOBlocks;
@@ -536,9 +547,10 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
         }
       }
       if (32 * qs == kw0)
-        dkdv_block<DIL, true>(sb[buf], st[buf], kf, vf, sc, cw, gw, c2, l32, h, dkt, dvt);
+        dkdv_block<DIL, true, CLAMP>(sb[buf], st[buf], kf, vf, sc, cw, gw, c2, l32, h, dkt, dvt);
       else
-        dkdv_block<DIL, false>(sb[buf], st[buf], kf, vf, sc, cw, gw, c2, l32, h, dkt, dvt);
+        dkdv_block<DIL, false, CLAMP>(sb[buf], st[buf], kf, vf, sc, cw, gw, c2, l32, h, dkt,
+                                      dvt);
     }
     if (qs + 1 < nqs) store_block(buf ^ 1);
     __syncthreads();
@@ -607,7 +619,7 @@ struct DqState {
   f32x4 rho;       // sum_j p_ij dp_ij, every element equal (dilution)
 };
 
-template <bool DIL, bool DIAG, int D>
+template <bool DIL, bool DIAG, bool CLAMP, int D>
 __device__ __forceinline__ void dq_subtile(DqState<D> &st, const bf16x8 *qf, const bf16x8 *gf,
                                            const DqConsts &dc, const bf16x8 &sel,
                                            const __bf16 *kt_lds, const __bf16 *vt_lds,
@@ -645,7 +657,7 @@ __device__ __forceinline__ void dq_subtile(DqState<D> &st, const bf16x8 *qf, con
     float invd[16], dsg[16], g[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      invd[r] = fminf(fast_rcp(d[r]), kInvDMax);
+      invd[r] = inv_denominator<CLAMP>(d[r]);
       const float sg = p[r] * invd[r];
       dsg[r] = __builtin_fmaf(da[r], invr, -dri);
       g[r] = dsg[r] * sg * invd[r];
@@ -674,7 +686,7 @@ __device__ __forceinline__ void dq_subtile(DqState<D> &st, const bf16x8 *qf, con
   }
 }
 
-template <bool DIL, int D>
+template <bool DIL, int D, bool CLAMP>
 __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dq_kernel(BwdArgs a,
                                                                                int nqb) {
   constexpr int kKR = Geom<D>::kKRow, kKT = Geom<D>::kKTile, kVT = Geom<D>::kVTile;
@@ -806,11 +818,11 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dq_kernel(B
 #pragma unroll 1
       for (int t = 0; t < 2; ++t) {
         if (kt < kd)
-          dq_subtile<DIL, false, D>(st, qf, gf, dc, sel, kl, vl, tl, t, cw[t], gw[t], lse2, invr,
-                                    dri, qrel, l32, h, c2);
+          dq_subtile<DIL, false, CLAMP, D>(st, qf, gf, dc, sel, kl, vl, tl, t, cw[t], gw[t], lse2,
+                                           invr, dri, qrel, l32, h, c2);
         else
-          dq_subtile<DIL, true, D>(st, qf, gf, dc, sel, kl, vl, tl, t, cw[t], gw[t], lse2, invr,
-                                   dri, qrel, l32, h, c2);
+          dq_subtile<DIL, true, CLAMP, D>(st, qf, gf, dc, sel, kl, vl, tl, t, cw[t], gw[t], lse2,
+                                          invr, dri, qrel, l32, h, c2);
       }
     }
     if (kt + 1 < nkt) store_tile(buf ^ 1);
@@ -886,7 +898,7 @@ hipError_t launch_dtau(const BwdArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool CLAMP>
 hipError_t launch_bwd_d(int mode, const BwdArgs &a, hipStream_t s) {
   const bool dil = mode == 1;
   const size_t rows = (size_t)a.BH * a.T;
@@ -912,7 +924,8 @@ hipError_t launch_bwd_d(int mode, const BwdArgs &a, hipStream_t s) {
     f.eps = a.eps;
     e = launch_colsum_bf16(f, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_gsum_kernel<D>, dim3((unsigned)(nkb * a.BH)), dim3(256), 0, s, a, nqs);
+    hipLaunchKernelGGL((bwd_gsum_kernel<D, CLAMP>), dim3((unsigned)(nkb * a.BH)), dim3(256), 0, s,
+                       a, nqs);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // PK = softmax-weighted keys: the tempered forward with the keys as values
@@ -929,31 +942,34 @@ hipError_t launch_bwd_d(int mode, const BwdArgs &a, hipStream_t s) {
     t.c2 = a.c2;
     e = launch_rows_bf16(kRowTempered, t, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<true, D>), dim3((unsigned)(nqb * a.BH)), dim3(256), 0, s, a,
-                       nqb);
+    hipLaunchKernelGGL((bwd_dq_kernel<true, D, CLAMP>), dim3((unsigned)(nqb * a.BH)), dim3(256), 0,
+                       s, a, nqb);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_dtau(a, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<true, D>), dim3((unsigned)(nkb * a.BH)), dim3(256), 0, s,
-                       a, nqs);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<true, D, CLAMP>), dim3((unsigned)(nkb * a.BH)), dim3(256),
+                       0, s, a, nqs);
   } else {
-    hipLaunchKernelGGL((bwd_dq_kernel<false, D>), dim3((unsigned)(nqb * a.BH)), dim3(256), 0, s,
-                       a, nqb);
+    hipLaunchKernelGGL((bwd_dq_kernel<false, D, false>), dim3((unsigned)(nqb * a.BH)), dim3(256),
+                       0, s, a, nqb);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_dtau(a, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<false, D>), dim3((unsigned)(nkb * a.BH)), dim3(256), 0, s,
-                       a, nqs);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<false, D, false>), dim3((unsigned)(nkb * a.BH)), dim3(256),
+                       0, s, a, nqs);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_bf16(int mode, const BwdArgs &a, hipStream_t s) {
+  // the 1/D clamp matters only for dilution with eps below 2^-63 (eps = 0)
+  const bool clamp = mode == 1 && !(a.eps >= kNoClampEps);
   switch (a.D) {
-    case 64: return launch_bwd_d<64>(mode, a, s);
-    case 128: return launch_bwd_d<128>(mode, a, s);
+    case 64: return clamp ? launch_bwd_d<64, true>(mode, a, s) : launch_bwd_d<64, false>(mode, a, s);
+    case 128:
+      return clamp ? launch_bwd_d<128, true>(mode, a, s) : launch_bwd_d<128, false>(mode, a, s);
     default: return hipErrorInvalidValue;
   }
 }
