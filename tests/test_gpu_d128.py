@@ -180,3 +180,41 @@ def test_d128_deterministic():
         b = ab.fwd(q, k, v, tau=1.0, mode=mode)
         torch.cuda.synchronize()
         assert torch.equal(a, b)
+
+
+def test_d128_decode_split_path():
+    """Caches longer than 32768 keys take the chunked decode path (scores
+    through the workspace, per-chunk partials combined in order): two steps
+    at d = 128 with per-(sequence, head) multipliers and mixed lengths,
+    demand carried between steps."""
+    import torch
+
+    S, H, L, d = 2, 2, 40000, 128
+    inp = draw_qkv(S, H, L, d, "bf16", seed=6500)
+    taus = learned_tau(S, H, d, seed=6500)
+    D0 = decode_initial_demand(S, H, L, seed=6500)
+    qs = decode_queries(2, S, H, d, seed=6500)
+    kc, vc = to_device(inp.k, "bf16"), to_device(inp.v, "bf16")
+    Dd = torch.from_numpy(D0.copy()).cuda()
+    tb = torch.from_numpy(taus).cuda()
+    kv_len = torch.tensor([L, 32769], dtype=torch.int32, device="cuda")
+    Dr = D0.astype(np.float64)
+    for step in range(2):
+        out = ab.decode(to_device(qs[step], "bf16"), kc, vc, Dd, tau=1.0, eps=1e-6,
+                        kv_len=kv_len, tau_sh=tb)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy()
+        for s in range(S):
+            for h in range(H):
+                Dsh = np.ascontiguousarray(Dr[s:s + 1, h:h + 1])
+                ref = oracle.dilution_decode_step(
+                    oracle.Bf16(np.ascontiguousarray(qs[step][s:s + 1, h:h + 1])),
+                    oracle.Bf16(np.ascontiguousarray(inp.k[s:s + 1, h:h + 1])),
+                    oracle.Bf16(np.ascontiguousarray(inp.v[s:s + 1, h:h + 1])), Dsh,
+                    float(taus[s, h]), 1e-6, kv_len=[int(kv_len[s])])
+                Dr[s, h] = Dsh[0, 0]
+                assert_close(got[s:s + 1, h:h + 1], ref, "bf16", f"split decode step {step} s={s} h={h}")
+        Dg = Dd.cpu().numpy().astype(np.float64)
+        rel = np.abs(Dg.sum(-1) / Dr.sum(-1) - 1.0)
+        assert np.max(rel) <= DEMAND_TOTAL_REL, f"step {step}: demand totals {np.max(rel):.2e}"
+        assert np.max(np.abs(Dg - Dr)) <= 1e-4 * max(1.0, float(Dr.max()))
