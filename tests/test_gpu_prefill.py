@@ -205,3 +205,57 @@ def test_long_chunk_after_long_cache():
     added = got.sum(-1) - D0.astype(np.float64).sum(-1)
     assert np.max(np.abs(added / Tq - 1.0)) <= 1e-3
     assert np.max(np.abs(got - Dref)) <= 2e-2 * max(1.0, float(Dref.max()))
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+def test_whole_prefill_is_the_forward(dtype, d):
+    """attn_prefill over a whole sequence (Tq = Tk = T, no carried demand) runs
+    the forward's launches: out, lse, row sums and final column demand equal
+    attn_fwd_ex's bit for bit (tempered: out and lse)."""
+    import torch
+
+    B, H, T = 2, 3, 300
+    inp = draw_qkv(B, H, T, d, dtype, seed=5600 + d)
+    q, k, v = (to_device(a, dtype) for a in (inp.q, inp.k, inp.v))
+
+    def f32(*shape):
+        return torch.empty(shape, dtype=torch.float32, device="cuda")
+
+    for mode in (ab.ATTN_TEMPERED, ab.ATTN_DILUTION):
+        dil = mode == ab.ATTN_DILUTION
+        l1, l2 = f32(B, H, T), f32(B, H, T)
+        r1, r2 = (f32(B, H, T), f32(B, H, T)) if dil else (None, None)
+        d1, d2 = (f32(B, H, T), f32(B, H, T)) if dil else (None, None)
+        o1 = ab.fwd(q, k, v, tau=TAU4, mode=mode, eps=1e-6, lse_out=l1, rowsum_out=r1,
+                    demand_out=d1)
+        o2 = ab.prefill(q, k, v, T, tau=TAU4, mode=mode, eps=1e-6, lse_out=l2, rowsum_out=r2,
+                        demand_out=d2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), (dtype, d, mode)
+        if dil:
+            assert torch.equal(r1, r2) and torch.equal(d1, d2), (dtype, d, mode)
+
+
+def test_chunk_row_sums_match_whole_prefill():
+    """The row sums a chunked prefill returns (rowsum_out, what the backward
+    needs) agree with the whole prefill's, chunk by chunk (bf16, d = 64)."""
+    import torch
+
+    B, H, T, d = 1, 2, 700, 64
+    inp = draw_qkv(B, H, T, d, "bf16", seed=5700, heavy_frac=0.05)
+    q, k, v = (to_device(a, "bf16") for a in (inp.q, inp.k, inp.v))
+    rs_whole = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    ab.prefill(q, k, v, T, tau=1.0, mode=ab.ATTN_DILUTION, eps=1e-6, rowsum_out=rs_whole)
+    D = torch.zeros((B, H, T), dtype=torch.float32, device="cuda")
+    parts = []
+    for a, b in zip((0, 200, 333, 640), (200, 333, 640, 700)):
+        rs = torch.empty((B, H, b - a), dtype=torch.float32, device="cuda")
+        ab.prefill(q[:, :, a:b].contiguous(), k, v, b, tau=1.0, mode=ab.ATTN_DILUTION, eps=1e-6,
+                   demand_in=D, demand_out=D, rowsum_out=rs)
+        parts.append(rs)
+    torch.cuda.synchronize()
+    got = torch.cat(parts, dim=2).cpu().numpy().astype(np.float64)
+    ref = rs_whole.cpu().numpy().astype(np.float64)
+    rel = float(np.max(np.abs(got / ref - 1.0)))
+    print(f"chunk row sums vs whole: max rel {rel:.3e}")
+    assert np.all(ref > 0) and rel <= 5e-3
