@@ -163,8 +163,10 @@ int attn_bwd_ex(const void *q, const void *k, const void *v, const void *out, co
  *                          earlier key, the demand committed by all earlier
  *                          rows -- the exclusive cumulative sum of the bids
  *                          down each key column ("The operator", committed),
- *                          taken block by block.  demand_out: optional
- *                          [B,H,T] fp32 final column totals.
+ *                          taken block by block.  It stores committed +
+ *                          eps, so stage 3 must be given the same eps.
+ *                          demand_out: optional [B,H,T] fp32 final column
+ *                          totals.
  * attn_dilution_shares     stage 3: shares p / (committed + p + eps) with the
  *                          prefix finished inside each block, then out = A @ v
  *                          with A the row-renormalised shares ("The operator",
@@ -173,7 +175,7 @@ int attn_dilution_lse(const void *q, const void *k, int B, int H, int T, int d, 
                       int dtype, void *workspace, size_t workspace_bytes, float *lse_out,
                       void *hip_stream);
 int attn_dilution_committed(const void *q, const void *k, int B, int H, int T, int d, float tau,
-                            int dtype, void *workspace, size_t workspace_bytes,
+                            float eps, int dtype, void *workspace, size_t workspace_bytes,
                             float *demand_out, void *hip_stream);
 int attn_dilution_shares(const void *q, const void *k, const void *v, void *out, int B, int H,
                          int T, int d, float tau, float eps, int dtype, void *workspace,

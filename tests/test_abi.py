@@ -296,6 +296,41 @@ def test_decode_rejects_bad_arguments(kw, status):
     assert dec(**kw) == status
 
 
+def stage(name, **kw):
+    args = dict(q=FAKE, k=FAKE + 0x1000000, B=1, H=2, T=40, d=64, tau=1.0, dtype=1,
+                workspace=None, workspace_bytes=0, hip_stream=None)
+    if name == "attn_dilution_lse":
+        args.update(lse_out=None)
+    elif name == "attn_dilution_committed":
+        args.update(eps=1e-6, demand_out=None)
+    else:
+        args.update(v=FAKE + 0x2000000, out=FAKE + 0x3000000, eps=1e-6)
+    args.update(kw)
+    return getattr(ab, name)(**args)
+
+
+@pytest.mark.parametrize("name", ["attn_dilution_lse", "attn_dilution_committed",
+                                  "attn_dilution_shares"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ab.ATTN_EINVAL),
+    (dict(k=FAKE + 0x1000004), ab.ATTN_EINVAL),       # misaligned
+    (dict(T=0), ab.ATTN_EINVAL),
+    (dict(tau=float("inf")), ab.ATTN_EINVAL),
+    (dict(d=96), ab.ATTN_ENOTSUP),
+    (dict(), ab.ATTN_EWORKSPACE),                     # every stage reads or writes the workspace
+    (dict(workspace=FAKE + 0x5000000, workspace_bytes=64), ab.ATTN_EWORKSPACE),
+])
+def test_stage_calls_reject_bad_arguments(name, kw, status):
+    assert stage(name, **kw) == status
+
+
+@pytest.mark.parametrize("name", ["attn_dilution_committed", "attn_dilution_shares"])
+def test_stage_calls_check_eps(name):
+    # the committed stage stores committed + eps, so it validates eps too
+    assert stage(name, eps=-1.0) == ab.ATTN_EINVAL
+    assert stage(name, eps=float("nan")) == ab.ATTN_EINVAL
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(ab, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(ab, "_lib", None)

@@ -187,3 +187,28 @@ def test_dilution_rows_sum_to_one_via_identity_values():
     assert np.all(np.triu(A, 1) == 0.0)
     assert np.all(A >= 0.0)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("eps", [1e-6, 0.3])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+def test_stage_calls_are_the_forward(dtype, d, eps):
+    """attn_dilution_lse, attn_dilution_committed and attn_dilution_shares,
+    enqueued one by one on one workspace, produce attn_fwd's output, LSE and
+    final column demand bit for bit; the output also matches the oracle (a
+    large eps makes a missing eps in any stage visible at the tolerance)."""
+    import torch
+
+    B, H, T = 1, 3, 333
+    inp = draw_qkv(B, H, T, d, dtype, seed=4100 + d, heavy_frac=0.05)
+    q, k, v = device_qkv(inp)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    l1, d1 = torch.empty((B, H, T), **f32), torch.empty((B, H, T), **f32)
+    l2, d2 = torch.empty((B, H, T), **f32), torch.empty((B, H, T), **f32)
+    o1 = ab.fwd(q, k, v, tau=TAU4, mode=ab.ATTN_DILUTION, eps=eps, lse_out=l1, demand_out=d1)
+    stages, o2 = ab.dilution_stages(q, k, v, tau=TAU4, eps=eps, lse_out=l2, demand_out=d2)
+    for stage in stages:
+        stage()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(d1, d2)
+    ref, _, _ = oracle.dilution_fwd(*oracle_qkv(inp), TAU4, eps)
+    assert_close(o2.float().cpu().numpy(), ref, dtype, f"stage calls {dtype} d={d} eps={eps}")

@@ -70,7 +70,7 @@ def load() -> ctypes.CDLL:
         lib.attn_dilution_lse.restype = i
         lib.attn_dilution_lse.argtypes = [vp, vp, i, i, i, i, f, i, vp, sz, vp, vp]
         lib.attn_dilution_committed.restype = i
-        lib.attn_dilution_committed.argtypes = [vp, vp, i, i, i, i, f, i, vp, sz, vp, vp]
+        lib.attn_dilution_committed.argtypes = [vp, vp, i, i, i, i, f, f, i, vp, sz, vp, vp]
         lib.attn_dilution_shares.restype = i
         lib.attn_dilution_shares.argtypes = [vp, vp, vp, vp, i, i, i, i, f, f, i, vp, sz, vp]
         lib.attn_fwd_workspace_bytes.restype = sz
@@ -139,9 +139,9 @@ def attn_dilution_lse(q, k, B, H, T, d, tau, dtype, workspace, workspace_bytes, 
                                     lse_out, hip_stream)
 
 
-def attn_dilution_committed(q, k, B, H, T, d, tau, dtype, workspace, workspace_bytes,
+def attn_dilution_committed(q, k, B, H, T, d, tau, eps, dtype, workspace, workspace_bytes,
                             demand_out, hip_stream) -> int:
-    return load().attn_dilution_committed(q, k, B, H, T, d, tau, dtype, workspace,
+    return load().attn_dilution_committed(q, k, B, H, T, d, tau, eps, dtype, workspace,
                                           workspace_bytes, demand_out, hip_stream)
 
 
@@ -344,7 +344,7 @@ def dilution_stages(q, k, v, tau: float = 1.0, eps: float = 1e-6, out=None, work
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
-        workspace, ws_bytes = fwd_workspace(B, H, T, ATTN_DILUTION, code, q.device)
+        workspace, ws_bytes = fwd_workspace(B, H, T, ATTN_DILUTION, code, q.device, d)
     else:
         ws_bytes = workspace.numel() * workspace.element_size()
     wp = workspace.data_ptr()
@@ -360,8 +360,9 @@ def dilution_stages(q, k, v, tau: float = 1.0, eps: float = 1e-6, out=None, work
                                 ws_bytes, lp, _stream_handle(q.device)), "attn_dilution_lse")
 
     def committed():
-        check(attn_dilution_committed(q.data_ptr(), k.data_ptr(), B, H, T, d, float(tau), code,
-                                      wp, ws_bytes, dp, _stream_handle(q.device)),
+        check(attn_dilution_committed(q.data_ptr(), k.data_ptr(), B, H, T, d, float(tau),
+                                      float(eps), code, wp, ws_bytes, dp,
+                                      _stream_handle(q.device)),
               "attn_dilution_committed")
 
     def shares():

@@ -224,14 +224,15 @@ int attn_dilution_lse(const void *q, const void *k, int B, int H, int T, int d, 
 }
 
 int attn_dilution_committed(const void *q, const void *k, int B, int H, int T, int d, float tau,
-                            int dtype, void *workspace, size_t workspace_bytes,
+                            float eps, int dtype, void *workspace, size_t workspace_bytes,
                             float *demand_out, void *hip_stream) {
-  int st = check_fwd(q, k, nullptr, nullptr, B, H, T, d, tau, 0.0f, dtype, nullptr, demand_out);
+  int st = check_fwd(q, k, nullptr, nullptr, B, H, T, d, tau, eps, dtype, nullptr, demand_out);
   FwdWorkspace ws{};
   if (st == ATTN_OK) st = check_workspace(B, H, T, d, dtype, workspace, workspace_bytes, &ws);
   if (st == ATTN_OK) st = check_device();
   if (st != ATTN_OK) return st;
-  attn::FwdArgs a = make_args(q, k, nullptr, nullptr, B, H, T, d, tau, 0.0f, workspace, ws);
+  // the table holds committed + eps: stage 3 adds no eps for these keys
+  attn::FwdArgs a = make_args(q, k, nullptr, nullptr, B, H, T, d, tau, eps, workspace, ws);
   a.demand_out = demand_out;
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
   return finish(dtype == ATTN_BF16 ? attn::launch_colsum_bf16(a, s) : attn::launch_colsum_f32(a, s));
