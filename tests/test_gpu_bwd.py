@@ -319,3 +319,26 @@ def test_bwd_d128_deterministic():
     b = run_bwd_heads(inp, g, 1, tau_bh=taus)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_bwd_dtau_request_leaves_gradients_unchanged():
+    """Asking for dL/dtau adds work to the dQ epilogue only: dq, dk and dv are
+    the same bits with and without it (per-head multipliers, both modes)."""
+    import torch
+
+    B, H, T = 1, 2, 257
+    inp = draw_qkv(B, H, T, 64, "bf16", seed=2400)
+    g = draw_grad(B, H, T, 64, seed=2400)
+    taus = torch.from_numpy(learned_tau(B, H, 64, seed=2400)).cuda()
+    q, k, v = (to_device(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    dout = to_device(g, "bf16")
+    for mode in (0, 1):
+        lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+        rs = torch.empty_like(lse) if mode == 1 else None
+        out = ab.prefill(q, k, v, T, mode=mode, lse_out=lse, rowsum_out=rs, tau_bh=taus)
+        dt = torch.empty((B, H), dtype=torch.float32, device="cuda")
+        a = ab.bwd(q, k, v, out, dout, lse, rs, mode=mode, tau_bh=taus, dtau_out=dt)
+        b = ab.bwd(q, k, v, out, dout, lse, rs, mode=mode, tau_bh=taus)
+        torch.cuda.synchronize()
+        for x, y in zip(a, b):
+            assert torch.equal(x, y), mode

@@ -130,3 +130,32 @@ def test_decode_deterministic_and_resumable():
     assert torch.equal(Da, Dc)
     for x, y in zip(outs_a, outs_b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fused_and_chunked_decode_agree(d):
+    """The same keys through the two decode implementations: a cache of
+    exactly L = 30000 keys takes the fused path (scores in LDS), the same keys
+    inside a 40000-key cache (kv_len = 30000) the chunked path (scores through
+    the workspace, per-chunk partials).  Outputs and demand agree to rounding."""
+    import torch
+
+    S, H, L, Lbig = 2, 2, 30000, 40000
+    inp = draw_qkv(S, H, Lbig, d, "bf16", seed=3300 + d)
+    D0 = decode_initial_demand(S, H, Lbig, seed=3300 + d)
+    q = to_device(decode_queries(1, S, H, d, seed=3300 + d)[0], "bf16")
+    kb, vb = to_device(inp.k, "bf16"), to_device(inp.v, "bf16")
+    ks, vs = kb[:, :, :L].contiguous(), vb[:, :, :L].contiguous()
+    Db = torch.from_numpy(D0.copy()).cuda()
+    Ds = Db[:, :, :L].contiguous()
+    kv_len = torch.full((S,), L, dtype=torch.int32, device="cuda")
+    o_fused = ab.decode(q, ks, vs, Ds, tau=1.0, eps=1e-6)
+    o_chunk = ab.decode(q, kb, vb, Db, tau=1.0, eps=1e-6, kv_len=kv_len)
+    torch.cuda.synchronize()
+    a, b = o_fused.float().cpu().numpy(), o_chunk.float().cpu().numpy()
+    err = float(np.max(np.abs(a - b)))
+    print(f"d={d}: fused vs chunked max-abs {err:.3e}")
+    assert err <= 2e-2 * max(1.0, float(np.max(np.abs(a))))
+    dd = np.abs(Ds.cpu().numpy() - Db[:, :, :L].cpu().numpy())
+    assert float(dd.max()) <= 1e-5 * max(1.0, float(D0.max()) + 1.0)
+    assert np.array_equal(Db[:, :, L:].cpu().numpy(), D0[:, :, L:])   # past kv_len: untouched
