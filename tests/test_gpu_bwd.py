@@ -342,3 +342,14 @@ def test_bwd_dtau_request_leaves_gradients_unchanged():
         torch.cuda.synchronize()
         for x, y in zip(a, b):
             assert torch.equal(x, y), mode
+
+
+@pytest.mark.parametrize("eps", [0.0, 0.3])
+def test_bwd_d128_dilution_eps(eps):
+    """d = 128 dilution gradients at eps = 0 (the kernels' clamped 1/D form)
+    and at a large eps, against the oracle."""
+    inp = draw_qkv(1, 2, 129, 128, "bf16", seed=2500)
+    g = draw_grad(1, 2, 129, 128, seed=2500)
+    got = run_bwd(inp, g, 1.0, 1, eps)
+    ref = oracle_grads(inp, g, 1.0, 1, eps)
+    check_grads(got[:3], ref[:3], f"d128 eps={eps}")

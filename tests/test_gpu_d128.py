@@ -7,7 +7,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import DEMAND_TOTAL_REL, assert_close, oracle_qkv, sample_rows, to_device
+from gpu_util import (DEMAND_TOTAL_REL, assert_close, oracle_qkv, oracle_view, sample_rows,
+                      to_device)
 from transformer_attention_causal_amd import binding as ab
 from transformer_attention_causal_amd.workloads import (PREFILL, decode_initial_demand,
                                                         decode_queries, draw_qkv, learned_tau,
@@ -24,7 +25,7 @@ def head_inputs(inp, bh_list):
     out = []
     for bh in bh_list:
         b, h = divmod(bh, H)
-        out.append(tuple(oracle.Bf16(np.ascontiguousarray(x[b:b + 1, h:h + 1]))
+        out.append(tuple(oracle_view(np.ascontiguousarray(x[b:b + 1, h:h + 1]), inp.dtype)
                          for x in (inp.q, inp.k, inp.v)))
     return out
 
@@ -59,12 +60,12 @@ def test_d128_ragged_lengths(T):
     assert np.max(np.abs(lse - rlse)) <= 2e-3
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_per_head_tau(d):
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+def test_per_head_tau(dtype, d):
     """Per-(b,h) multipliers sqrt(d)/t, t ~ U[5, 10] (learned-temperature
     range): every head matches the oracle run with its own scalar tau."""
     B, H, T = 2, 3, 300
-    inp = draw_qkv(B, H, T, d, "bf16", seed=6100 + d, heavy_frac=0.05)
+    inp = draw_qkv(B, H, T, d, dtype, seed=6100 + d, heavy_frac=0.05)
     taus = learned_tau(B, H, d, seed=6100 + d)
     for mode in (ab.ATTN_TEMPERED, ab.ATTN_DILUTION):
         out, lse, _ = run_prefill(inp, 1.0, mode, tau_bh=taus)
@@ -75,8 +76,9 @@ def test_per_head_tau(d):
                 ref, rlse = oracle.tempered_fwd(q1, k1, v1, tau)
             else:
                 ref, rlse, _ = oracle.dilution_fwd(q1, k1, v1, tau, 1e-6)
-            assert_close(out[b:b + 1, h:h + 1], ref, "bf16", f"d={d} mode={mode} head {bh} tau={tau:.3f}")
-            assert np.max(np.abs(lse[b, h] - rlse[0, 0])) <= 2e-3
+            assert_close(out[b:b + 1, h:h + 1], ref, dtype,
+                         f"{dtype} d={d} mode={mode} head {bh} tau={tau:.3f}")
+            assert np.max(np.abs(lse[b, h] - rlse[0, 0])) <= (2e-3 if dtype == "bf16" else 1e-5)
 
 
 def test_d128_chunks_and_carried_demand():

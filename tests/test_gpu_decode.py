@@ -159,3 +159,40 @@ def test_fused_and_chunked_decode_agree(d):
     dd = np.abs(Ds.cpu().numpy() - Db[:, :, :L].cpu().numpy())
     assert float(dd.max()) <= 1e-5 * max(1.0, float(D0.max()) + 1.0)
     assert np.array_equal(Db[:, :, L:].cpu().numpy(), D0[:, :, L:])   # past kv_len: untouched
+
+
+@pytest.mark.parametrize("L", [5000, 33000])
+def test_decode_per_head_tau_d64(L):
+    """Per-(sequence, head) multipliers at d = 64 on both decode paths (fused
+    up to 32768 keys, chunked beyond): two steps against the oracle with the
+    demand carried."""
+    import torch
+
+    from transformer_attention_causal_amd.workloads import learned_tau
+
+    S, H, d = 2, 3, 64
+    inp = draw_qkv(S, H, L, d, "bf16", seed=3400 + L)
+    taus = learned_tau(S, H, d, seed=3400 + L)
+    D0 = decode_initial_demand(S, H, L, seed=3400 + L)
+    qs = decode_queries(2, S, H, d, seed=3400 + L)
+    kc, vc = to_device(inp.k, "bf16"), to_device(inp.v, "bf16")
+    Dd = torch.from_numpy(D0.copy()).cuda()
+    tb = torch.from_numpy(taus).cuda()
+    Dr = D0.astype(np.float64)
+    for step in range(2):
+        got = ab.decode(to_device(qs[step], "bf16"), kc, vc, Dd, tau=1.0, eps=1e-6,
+                        tau_sh=tb).float().cpu().numpy()
+        for s in range(S):
+            for h in range(H):
+                Dsh = np.ascontiguousarray(Dr[s:s + 1, h:h + 1])
+                ref = oracle.dilution_decode_step(
+                    oracle.Bf16(np.ascontiguousarray(qs[step][s:s + 1, h:h + 1])),
+                    oracle.Bf16(np.ascontiguousarray(inp.k[s:s + 1, h:h + 1])),
+                    oracle.Bf16(np.ascontiguousarray(inp.v[s:s + 1, h:h + 1])), Dsh,
+                    float(taus[s, h]), 1e-6)
+                Dr[s, h] = Dsh[0, 0]
+                assert_close(got[s:s + 1, h:h + 1], ref, "bf16",
+                             f"L={L} step {step} s={s} h={h} tau={taus[s, h]:.3f}")
+        Dg = Dd.cpu().numpy().astype(np.float64)
+        assert np.max(np.abs(Dg.sum(-1) / Dr.sum(-1) - 1.0)) <= DEMAND_TOTAL_REL
+        assert np.max(np.abs(Dg - Dr)) <= 1e-4 * max(1.0, float(Dr.max()))
