@@ -353,3 +353,14 @@ def test_bwd_d128_dilution_eps(eps):
     got = run_bwd(inp, g, 1.0, 1, eps)
     ref = oracle_grads(inp, g, 1.0, 1, eps)
     check_grads(got[:3], ref[:3], f"d128 eps={eps}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_dilution_with_huge_eps_is_tempered(d):
+    """With eps far above every demand the dilution operator is the softmax,
+    so its device gradients reproduce the tempered backward's."""
+    inp = draw_qkv(1, 2, 300, d, "bf16", seed=2600 + d)
+    g = draw_grad(1, 2, 300, d, seed=2600 + d)
+    dil = run_bwd(inp, g, 1.0, 1, 1e9)
+    tmp = run_bwd(inp, g, 1.0, 0)
+    check_grads(dil[:3], tmp[:3], f"d={d} dilution(eps=1e9) vs tempered")

@@ -212,3 +212,17 @@ def test_stage_calls_are_the_forward(dtype, d, eps):
     assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(d1, d2)
     ref, _, _ = oracle.dilution_fwd(*oracle_qkv(inp), TAU4, eps)
     assert_close(o2.float().cpu().numpy(), ref, dtype, f"stage calls {dtype} d={d} eps={eps}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_dilution_with_huge_eps_is_tempered(d):
+    """With eps far above every demand the shares are p / eps, whose row
+    renormalisation is the softmax: the device's dilution forward reproduces
+    its tempered forward (bf16 rounding of the shares aside)."""
+    inp = draw_qkv(2, 2, 300, d, "bf16", seed=4200 + d, heavy_frac=0.05)
+    dil = run_fwd(inp, TAU4, ab.ATTN_DILUTION, eps=1e9)
+    tmp = run_fwd(inp, TAU4, ab.ATTN_TEMPERED)
+    ma, rr = errors(dil, tmp)
+    print(f"d={d}: dilution(eps=1e9) vs tempered max-abs {ma:.3e} rel-RMS {rr:.3e}")
+    # two bf16 outputs of one value differ by at most a rounding step or two
+    assert ma <= 2e-2 * max(1.0, float(np.max(np.abs(tmp)))) and rr <= 1e-2
