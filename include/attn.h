@@ -101,25 +101,26 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, int B, i
                 void *hip_stream);
 
 /* Bytes of device workspace attn_bwd and attn_bwd_ex need: five fp32 values
- * per query row,
- * and for dilution the committed demand and the later rows' gradient sums
- * per (32-row query block, key): B*H*16*n*(n+1) floats each,
- * n = ceil(T/32), plus a bf16 [B,H,T,d] array.  0 for an unsupported shape,
- * mode or dtype (bf16 only). */
+ * per query row, and for dilution the committed demand and the later rows'
+ * gradient sums per (32-row query block, key): B*H*16*n*(n+1) 32-bit values
+ * each, n = ceil(T/32), plus a [B,H,T,d] array of `dtype`.  0 for an
+ * unsupported shape, mode, head dimension or dtype. */
 size_t attn_bwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype);
 
 /* Exact gradients of either operator (DilutionAttention v0.1.0: the release's
  * kernels train with exact gradients; "The operator" defines what is
  * differentiated).  For the loss L with dL/dout = dout:
- *   q, k, v, out, dout  [B,H,T,d] bf16 device arrays: the forward's inputs,
- *                       its output, and the incoming gradient
+ *   q, k, v, out, dout  [B,H,T,d] device arrays of `dtype`: the forward's
+ *                       inputs, its output, and the incoming gradient
  *   lse                 [B,H,T] fp32: the forward's lse_out (natural log)
  *   rowsum              [B,H,T] fp32: the forward's rowsum_out (dilution;
  *                       ignored and may be NULL for ATTN_TEMPERED)
- *   dq, dk, dv          [B,H,T,d] bf16 outputs, overwritten; may not alias
- *                       each other or any input
- *   B, H, T, d, tau, mode, eps  as passed to the forward (d = 64 or 128)
- *   dtype               ATTN_BF16 (ATTN_F32 returns ATTN_ENOTSUP)
+ *   dq, dk, dv          [B,H,T,d] outputs of `dtype`, overwritten; may not
+ *                       alias each other or any input
+ *   B, H, T, d, tau, mode, eps  as passed to the forward
+ *   dtype               ATTN_BF16 (d = 64 or 128; matrix-core kernels) or
+ *                       ATTN_F32 (d = 64; vector-ALU kernels in full single
+ *                       precision); else ATTN_ENOTSUP
  *   workspace           device scratch of >= attn_bwd_workspace_bytes(...)
  *                       bytes; contents on entry are ignored
  * Deterministic: fixed reduction orders, no atomics.  attn_bwd is

@@ -140,7 +140,11 @@ def test_bwd_workspace_sizes():
     got = ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 1)
     assert want <= got <= want + 8 * 256
     assert 5 * rows <= ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 0, 1) <= 5 * rows + 5 * 256
-    assert ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 0) == 0   # fp32: not supported
+    # fp32 (d = 64): the softmax-weighted keys are fp32
+    assert (ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 0)
+            - ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 1)) == 16 * 16384 * 64 * 2
+    assert ab.attn_bwd_workspace_bytes(1, 16, 16384, 128, 1, 0) == 0   # fp32 at d = 128
+    assert ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 2) == 0    # unknown dtype
     assert ab.attn_bwd_workspace_bytes(1, 16, 16384, 96, 1, 1) == 0
     # d = 128: the softmax-weighted keys are twice as wide
     assert (ab.attn_bwd_workspace_bytes(1, 16, 16384, 128, 1, 1)
@@ -243,10 +247,11 @@ def bwd(**kw):
     (dict(T=0), ab.ATTN_EINVAL),
     (dict(tau=-1.0), ab.ATTN_EINVAL),
     (dict(eps=float("nan")), ab.ATTN_EINVAL),
-    (dict(dtype=0), ab.ATTN_ENOTSUP),                 # fp32 backward
+    (dict(dtype=0), ab.ATTN_EWORKSPACE),              # fp32 backward (d = 64) is supported
+    (dict(dtype=2), ab.ATTN_EINVAL),
     (dict(d=96), ab.ATTN_ENOTSUP),
     (dict(d=128), ab.ATTN_EWORKSPACE),                # d = 128 is supported
-    (dict(d=128, dtype=0), ab.ATTN_ENOTSUP),
+    (dict(d=128, dtype=0), ab.ATTN_ENOTSUP),          # fp32 runs at d = 64 only
     (dict(dk=FAKE + 0x7000000), ab.ATTN_EINVAL),      # dk aliases dq
     (dict(dv=FAKE), ab.ATTN_EINVAL),                  # dv aliases q
     (dict(), ab.ATTN_EWORKSPACE),

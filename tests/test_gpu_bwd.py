@@ -364,3 +364,76 @@ def test_bwd_dilution_with_huge_eps_is_tempered(d):
     dil = run_bwd(inp, g, 1.0, 1, 1e9)
     tmp = run_bwd(inp, g, 1.0, 0)
     check_grads(dil[:3], tmp[:3], f"d={d} dilution(eps=1e9) vs tempered")
+
+
+# ------------------------------------------------------------------ fp32
+
+# The fp32 backward runs in full single precision on the vector ALUs: the
+# forward's fp32 bar (1e-5) applied to each gradient relative to its largest
+# magnitude, with rel-RMS held to the same figure.
+F32_GRAD_REL = 1e-5
+
+
+def run_bwd_f32(inp, g32, mode, tau=1.0, eps=1e-6, tau_bh=None):
+    import torch
+
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (inp.q, inp.k, inp.v))
+    dout = torch.from_numpy(np.ascontiguousarray(g32)).cuda()
+    B, H, T, _ = q.shape
+    tb = torch.from_numpy(np.ascontiguousarray(tau_bh)).cuda() if tau_bh is not None else None
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    rs = torch.empty_like(lse) if mode == 1 else None
+    dt = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    out = ab.prefill(q, k, v, T, tau=tau, mode=mode, eps=eps, lse_out=lse, rowsum_out=rs,
+                     tau_bh=tb)
+    grads = ab.bwd(q, k, v, out, dout, lse, rs, tau=tau, mode=mode, eps=eps, tau_bh=tb,
+                   dtau_out=dt)
+    torch.cuda.synchronize()
+    return [x.cpu().numpy() for x in grads] + [dt.cpu().numpy()]
+
+
+def check_grads_f32(got, ref, what):
+    big = max(float(np.max(np.abs(r))) for r in ref)
+    for name, gg, r in zip(("dq", "dk", "dv"), got, ref):
+        max_abs, rel_rms = errors(gg, r)
+        scale = float(np.max(np.abs(r)))
+        print(f"{what} {name}: max-abs {max_abs:.3e} (scale {scale:.3e}) rel-RMS {rel_rms:.3e}")
+        if scale == 0.0:
+            assert max_abs <= 1e-6 * big, (what, name)
+            continue
+        assert rel_rms <= F32_GRAD_REL and max_abs <= F32_GRAD_REL * scale, (what, name)
+
+
+def grad_f32(B, H, T, d, seed):
+    """An incoming gradient for the fp32 path: the seeded bf16 draw, widened
+    exactly to fp32."""
+    return (draw_grad(B, H, T, d, seed).astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("mode", [0, 1], ids=["tempered", "dilution"])
+@pytest.mark.parametrize("T", [1, 7, 33, 64, 100, 129, 300])
+def test_bwd_fp32_ragged_lengths(mode, T):
+    inp = draw_qkv(1, 2, T, 64, "f32", seed=2700 + T)
+    g = grad_f32(1, 2, T, 64, seed=2700 + T)
+    got = run_bwd_f32(inp, g, mode, tau=TAU4)
+    ref = oracle.attn_bwd(inp.q, inp.k, inp.v, g, TAU4, 1e-6, mode, want_dtau=True)
+    check_grads_f32(got[:3], ref[:3], f"fp32 mode={mode} T={T}")
+    err = np.abs(got[3] - ref[4]) / np.maximum(np.abs(ref[4]), 1.0)
+    print(f"fp32 mode={mode} T={T} dtau rel err {np.max(err):.3e}")
+    assert np.max(err) <= 2e-5
+
+
+@pytest.mark.parametrize("eps", [0.0, 0.3])
+def test_bwd_fp32_dilution_eps_and_per_head_tau(eps):
+    """fp32 dilution at eps = 0 (the clamped 1/D form) and a large eps, with
+    learned per-head multipliers and their gradient, on heavy keys."""
+    B, H, T = 2, 2, 200
+    inp = draw_qkv(B, H, T, 64, "f32", seed=2800, heavy_frac=0.05)
+    g = grad_f32(B, H, T, 64, seed=2800)
+    taus = learned_tau(B, H, 64, seed=2800)
+    got = run_bwd_f32(inp, g, 1, eps=eps, tau_bh=taus)
+    ref = oracle.attn_bwd(inp.q, inp.k, inp.v, g, 1.0, eps, 1, tau_bh=taus, want_dtau=True)
+    check_grads_f32(got[:3], ref[:3], f"fp32 eps={eps}")
+    err = np.abs(got[3] - ref[4]) / np.maximum(np.abs(ref[4]), 1.0)
+    print(f"fp32 eps={eps} dtau rel err {np.max(err):.3e}")
+    assert np.max(err) <= 2e-5

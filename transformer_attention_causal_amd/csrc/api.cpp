@@ -406,13 +406,14 @@ struct BwdWorkspace {
   size_t row_bytes, cin_bytes, gin_bytes, pk_bytes, total;
 };
 
-bool bwd_workspace(int B, int H, int T, int d, int mode, BwdWorkspace *ws) {
+bool bwd_workspace(int B, int H, int T, int d, int mode, int dtype, BwdWorkspace *ws) {
   const size_t BH = (size_t)B * H;
   if (BH > (size_t)INT32_MAX) return false;
   ws->row_bytes = round_up(BH * (size_t)T * sizeof(float));
   ws->cin_bytes = mode == ATTN_DILUTION ? round_up(BH * attn::cin_floats_per_head(T, 0) * 4) : 0;
   ws->gin_bytes = mode == ATTN_DILUTION ? round_up(BH * attn::gin_floats_per_head(T) * 4) : 0;
-  ws->pk_bytes = mode == ATTN_DILUTION ? round_up(BH * (size_t)T * d * 2) : 0;
+  const size_t esz = dtype == ATTN_BF16 ? 2 : 4;
+  ws->pk_bytes = mode == ATTN_DILUTION ? round_up(BH * (size_t)T * d * esz) : 0;
   ws->total = kBwdRowArrays * ws->row_bytes + ws->cin_bytes + ws->gin_bytes + ws->pk_bytes;
   return true;
 }
@@ -422,10 +423,11 @@ bool bwd_workspace(int B, int H, int T, int d, int mode, BwdWorkspace *ws) {
 extern "C" {
 
 size_t attn_bwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype) {
-  if (!shape_ok(B, H, T) || dtype != ATTN_BF16 || !head_dim_ok(d, dtype)) return 0;
+  if (!shape_ok(B, H, T) || (dtype != ATTN_BF16 && dtype != ATTN_F32)) return 0;
+  if (!head_dim_ok(d, dtype)) return 0;
   if (mode != ATTN_TEMPERED && mode != ATTN_DILUTION) return 0;
   BwdWorkspace ws;
-  if (!bwd_workspace(B, H, T, d, mode, &ws)) return 0;
+  if (!bwd_workspace(B, H, T, d, mode, dtype, &ws)) return 0;
   return ws.total;
 }
 
@@ -445,9 +447,9 @@ int attn_bwd_ex(const void *q, const void *k, const void *v, const void *out, co
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EINVAL;
   if (!std::isfinite(tau) || tau < 0.0f) return ATTN_EINVAL;
   if (!std::isfinite(eps) || eps < 0.0f) return ATTN_EINVAL;
-  if (dtype != ATTN_BF16 || !head_dim_ok(d, dtype)) return ATTN_ENOTSUP;
+  if (!head_dim_ok(d, dtype)) return ATTN_ENOTSUP;
   // the three gradients may not alias each other or any input
-  const size_t nbytes = (size_t)B * H * (size_t)T * d * 2;
+  const size_t nbytes = (size_t)B * H * (size_t)T * d * (dtype == ATTN_BF16 ? 2 : 4);
   const size_t rbytes = (size_t)B * H * (size_t)T * sizeof(float);
   const void *grads[3] = {dq, dk, dv};
   for (int i = 0; i < 3; ++i) {
@@ -472,7 +474,7 @@ int attn_bwd_ex(const void *q, const void *k, const void *v, const void *out, co
       return ATTN_EINVAL;
   }
   BwdWorkspace ws;
-  if (!bwd_workspace(B, H, T, d, mode, &ws)) return ATTN_EINVAL;
+  if (!bwd_workspace(B, H, T, d, mode, dtype, &ws)) return ATTN_EINVAL;
   if (!workspace || workspace_bytes < ws.total || !aligned16(workspace)) return ATTN_EWORKSPACE;
   const int dev_status = check_device();
   if (dev_status != ATTN_OK) return dev_status;
@@ -512,7 +514,9 @@ int attn_bwd_ex(const void *q, const void *k, const void *v, const void *out, co
   a.tau_bh = tau_bh;
   a.dtau = dtau_out;
   a.eps = eps;
-  hipError_t e = attn::launch_bwd_bf16(mode, a, reinterpret_cast<hipStream_t>(hip_stream));
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  hipError_t e = dtype == ATTN_BF16 ? attn::launch_bwd_bf16(mode, a, s)
+                                    : attn::launch_bwd_f32(mode, a, s);
   return e == hipSuccess ? ATTN_OK : fail_hip(e);
 }
 

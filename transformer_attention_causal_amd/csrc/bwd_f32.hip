@@ -1,0 +1,414 @@
+// bwd_f32.hip -- fp32 backward kernels (vector ALU only), head dimension 64.
+//
+// The exact gradients of both operators, for fp32 storage where full single
+// precision is required.  The chain rule is the bf16 backward's
+// ("DilutionAttention v0.1.0 - results", "The operator", differentiated; the
+// release trains with exact gradients, "Everything behind these charts"):
+//   dsigma_ij = (dA_ij - delta_i) / r_i,  g_ij = dsigma_ij p_ij / D_ij^2,
+//   dp_ij = dsigma_ij / D_ij - G_ij (G: inclusive suffix of g down column j),
+//   dS_ij = p_ij (dp_ij - rho_i),  rho_i = sum_j p_ij dp_ij,
+//   dQ_i = c sum_j dS_ij k_j,  dK_j = c sum_i dS_ij q_i,  dV_j = sum_i a_ij dO_i,
+// and dL/dtau = sum_i <q_i, dQ_i / c> / sqrt(d) ("Learning to Focus", sec. 2.2:
+// the temperature is learned).  Tempered: dS_ij = p_ij (dA_ij - delta_i).
+//
+// One lane owns one query row (dQ) or one key column (the column passes); the
+// other operand's rows stream through LDS in 64-row tiles and are read as
+// broadcasts.  The denominators match the fp32 forward's exactly: D =
+// max(committed + eps, FLT_MIN) + the inclusive prefix of the bids inside the
+// 32-row query block, with committed read from the fp32 forward's table.  The
+// scans inside a block run over lanes in the dQ kernel (shuffles across the 32
+// lanes of the block) and over the rows a lane walks in the column kernels.
+#include "attn_common.hpp"
+#include "launch.hpp"
+
+#include <float.h>
+
+namespace attn {
+
+constexpr int kBR = 64;   // rows or keys per workgroup and per LDS tile
+constexpr float kInvDMaxF32 = 18446744073709551616.0f;   // 2^64: 1/D clamp (eps = 0 only)
+constexpr float kNoRowBwdF32 = 1e30f;                    // lse2 of a position past T
+
+__device__ __forceinline__ float head_tau_f32(const BwdArgs &a, int bh) {
+  return a.tau_bh ? a.tau_bh[bh] : 1.0f;
+}
+
+__device__ __forceinline__ float dot64(const float *x, const float *y) {
+  float s = 0.0f;
+#pragma unroll
+  for (int e = 0; e < kHeadDim; ++e) s = __builtin_fmaf(x[e], y[e], s);
+  return s;
+}
+
+// Per row: log2-domain lse, 1/r and delta/r (tempered: 1 and delta).
+__global__ void __launch_bounds__(256) bwd_prep_f32_kernel(BwdArgs a, int dilution) {
+  const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= (size_t)a.BH * a.T) return;
+  const float *O = reinterpret_cast<const float *>(a.o) + row * kHeadDim;
+  const float *G = reinterpret_cast<const float *>(a.dout) + row * kHeadDim;
+  const float delta = dot64(O, G);
+  a.lse2[row] = a.lse[row] * kLog2e;
+  if (dilution) {
+    const float ir = 1.0f / a.rowsum[row];
+    a.invr[row] = ir;
+    a.dri[row] = delta * ir;
+  } else {
+    a.invr[row] = 1.0f;
+    a.dri[row] = delta;
+  }
+}
+
+// Rows [i0, i0 + 64) of Q and dO and their per-row scalars into LDS; rows
+// past T read as zeros with an lse2 that makes their bids 0.
+struct RowTileF32 {
+  float q[kBR * kHeadDim], g[kBR * kHeadDim];
+  float lse2[kBR], invr[kBR], dri[kBR], rho[kBR];
+};
+
+__device__ __forceinline__ void load_row_tile(RowTileF32 &s, const BwdArgs &a, const float *Q,
+                                              const float *G, size_t rbase, int i0, int t,
+                                              bool with_rho) {
+  const int T = a.T;
+  for (int u = t; u < kBR * kHeadDim; u += kBR) {
+    const int row = i0 + u / kHeadDim;
+    const bool ok = row < T;
+    s.q[u] = ok ? Q[(size_t)i0 * kHeadDim + u] : 0.0f;
+    s.g[u] = ok ? G[(size_t)i0 * kHeadDim + u] : 0.0f;
+  }
+  const int row = i0 + t;
+  const bool ok = row < T;
+  s.lse2[t] = ok ? a.lse2[rbase + row] : kNoRowBwdF32;
+  s.invr[t] = ok ? a.invr[rbase + row] : 0.0f;
+  s.dri[t] = ok ? a.dri[rbase + row] : 0.0f;
+  s.rho[t] = (ok && with_rho) ? a.rho[rbase + row] : 0.0f;
+}
+
+// The terms of one (row, key) pair of a dilution block walk: the bid, the
+// running inclusive prefix, 1/D, sigma, dsigma and g.
+struct PairF32 {
+  float p, invd, sg, dsg, g;
+};
+
+template <bool CLAMP>
+__device__ __forceinline__ PairF32 pair_terms(float s, float da, float c2, float lse2, float invr,
+                                              float dri, bool vis, float basev, float &incl) {
+  PairF32 t;
+  t.p = vis ? exp2f(__builtin_fmaf(s, c2, -lse2)) : 0.0f;
+  incl += t.p;
+  const float r = 1.0f / (basev + incl);
+  t.invd = CLAMP ? fminf(r, kInvDMaxF32) : r;
+  t.sg = t.p * t.invd;
+  t.dsg = __builtin_fmaf(da, invr, -dri);
+  t.g = t.dsg * t.sg * t.invd;
+  return t;
+}
+
+// Later blocks' g sums: for each key (lane) and 32-row block, the sum of g
+// over every block below it, walking the blocks from the last one up.
+template <bool CLAMP>
+__global__ void __launch_bounds__(kBR) bwd_gsum_f32_kernel(BwdArgs a, int ntiles) {
+  __shared__ __attribute__((aligned(16))) RowTileF32 st;
+  const int t = threadIdx.x;
+  const int bh = blockIdx.x % a.BH, kb = blockIdx.x / a.BH;
+  const int T = a.T, j = kb * kBR + t;
+  const size_t head = (size_t)bh * T * kHeadDim, rbase = (size_t)bh * T;
+  const float *Q = reinterpret_cast<const float *>(a.q) + head;
+  const float *K = reinterpret_cast<const float *>(a.k) + head;
+  const float *V = reinterpret_cast<const float *>(a.v) + head;
+  const float *G = reinterpret_cast<const float *>(a.dout) + head;
+  const float *cin = a.cin + (size_t)bh * cin_floats_per_head(T, 0);
+  float *gin = a.gin + (size_t)bh * gin_floats_per_head(T);
+  const float c2 = a.c2 * head_tau_f32(a, bh);
+  const float eps_floor = fmaxf(a.eps, FLT_MIN);
+  float kv[kHeadDim], vv[kHeadDim];
+#pragma unroll
+  for (int e = 0; e < kHeadDim; ++e) {
+    kv[e] = j < T ? K[(size_t)j * kHeadDim + e] : 0.0f;
+    vv[e] = j < T ? V[(size_t)j * kHeadDim + e] : 0.0f;
+  }
+  float running = 0.0f;
+  for (int tile = ntiles - 1; tile >= kb; --tile) {
+    const int i0 = tile * kBR;
+    __syncthreads();
+    load_row_tile(st, a, Q, G, rbase, i0, t, false);
+    __syncthreads();
+    for (int half = 1; half >= 0; --half) {
+      const int b = 2 * tile + half;
+      if (32 * b >= T) continue;
+      const bool has = j < 32 * (b + 1) && j < T;   // the key has an entry for block b
+      const float basev = fmaxf((has ? cin[cin_block_offset(b, 0) + j] : 0.0f) + a.eps, eps_floor);
+      float incl = 0.0f, gsum = 0.0f;
+      for (int r = 0; r < 32; ++r) {
+        const int i = 32 * b + r, li = 32 * half + r;
+        if (i >= T) break;
+        const float s = dot64(&st.q[li * kHeadDim], kv), da = dot64(&st.g[li * kHeadDim], vv);
+        const PairF32 pt = pair_terms<CLAMP>(s, da, c2, st.lse2[li], st.invr[li], st.dri[li],
+                                             j <= i, basev, incl);
+        gsum += pt.g;
+      }
+      if (has) gin[(size_t)16 * b * (b + 1) + j] = running;
+      running += gsum;
+    }
+  }
+}
+
+// dQ (and rho, and the rows' dL/dtau terms): lane = query row.
+template <bool DIL, bool CLAMP>
+__global__ void __launch_bounds__(kBR) bwd_dq_f32_kernel(BwdArgs a, int nqb) {
+  __shared__ __attribute__((aligned(16))) float sK[kBR * kHeadDim];
+  __shared__ __attribute__((aligned(16))) float sV[kBR * kHeadDim];
+  const int t = threadIdx.x;
+  const int bh = blockIdx.x % a.BH, qb = nqb - 1 - blockIdx.x / a.BH;   // heaviest first
+  const int T = a.T, i = qb * kBR + t;
+  const bool live = i < T;
+  const int qs = i >> 5;
+  const size_t head = (size_t)bh * T * kHeadDim, rbase = (size_t)bh * T;
+  const float *Q = reinterpret_cast<const float *>(a.q) + head;
+  const float *K = reinterpret_cast<const float *>(a.k) + head;
+  const float *V = reinterpret_cast<const float *>(a.v) + head;
+  const float *G = reinterpret_cast<const float *>(a.dout) + head;
+  const float tb = head_tau_f32(a, bh), c2 = a.c2 * tb, cs = a.c * tb;
+  const float eps_floor = fmaxf(a.eps, FLT_MIN);
+  float q[kHeadDim], gd[kHeadDim], x[kHeadDim];
+#pragma unroll
+  for (int e = 0; e < kHeadDim; ++e) {
+    q[e] = live ? Q[(size_t)i * kHeadDim + e] : 0.0f;
+    gd[e] = live ? G[(size_t)i * kHeadDim + e] : 0.0f;
+    x[e] = 0.0f;
+  }
+  const float lse2 = live ? a.lse2[rbase + i] : kNoRowBwdF32;
+  const float invr = live ? a.invr[rbase + i] : 0.0f;
+  const float dri = live ? a.dri[rbase + i] : 0.0f;
+  const float *cin_blk = a.cin + (size_t)bh * cin_floats_per_head(T, 0) + cin_block_offset(qs, 0);
+  const float *gin_blk = a.gin + (size_t)bh * gin_floats_per_head(T) + (size_t)16 * qs * (qs + 1);
+  float rho = 0.0f;
+  const int kend = min(qb * kBR + kBR, T);
+  for (int j0 = 0; j0 < kend; j0 += kBR) {
+    __syncthreads();
+    for (int u = t; u < kBR * kHeadDim; u += kBR) {
+      const bool ok = j0 + u / kHeadDim < T;
+      sK[u] = ok ? K[(size_t)j0 * kHeadDim + u] : 0.0f;
+      sV[u] = ok ? V[(size_t)j0 * kHeadDim + u] : 0.0f;
+    }
+    __syncthreads();
+    const int jn = min(kBR, kend - j0);
+    for (int jj = 0; jj < jn; ++jj) {
+      const int j = j0 + jj;
+      const float s = dot64(q, &sK[jj * kHeadDim]), da = dot64(gd, &sV[jj * kHeadDim]);
+      const bool vis = live && j <= i;
+      float e;
+      if constexpr (DIL) {
+        // every lane of the 32-row block runs this for the same key: the
+        // prefix of the bids and the suffix of g are scans over those lanes
+        // lanes past T may sit in a block past the last one: they read nothing
+        // (their bids and g are 0, so the scans are unchanged)
+        const bool has = live && j < 32 * (qs + 1);
+        const float basev = fmaxf((has ? cin_blk[j] : 0.0f) + a.eps, eps_floor);
+        const float p = vis ? exp2f(__builtin_fmaf(s, c2, -lse2)) : 0.0f;
+        float incl = p;
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) {
+          const float o = __shfl_up(incl, off, 32);
+          if ((t & 31) >= off) incl += o;
+        }
+        const float rr = 1.0f / (basev + incl);
+        const float invd = CLAMP ? fminf(rr, kInvDMaxF32) : rr;
+        const float dsg = __builtin_fmaf(da, invr, -dri);
+        const float g = dsg * (p * invd) * invd;
+        float suf = g;
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) {
+          const float o = __shfl_down(suf, off, 32);
+          if ((t & 31) + off < 32) suf += o;
+        }
+        const float Gij = (has ? gin_blk[j] : 0.0f) + suf;
+        e = p * __builtin_fmaf(dsg, invd, -Gij);
+        rho += e;
+      } else {
+        const float p = vis ? exp2f(__builtin_fmaf(s, c2, -lse2)) : 0.0f;
+        e = p * (da - dri);
+      }
+#pragma unroll
+      for (int d = 0; d < kHeadDim; ++d) x[d] = __builtin_fmaf(e, sK[jj * kHeadDim + d], x[d]);
+    }
+  }
+  if (!live) return;
+  const size_t ridx = rbase + i;
+  float *dQ = reinterpret_cast<float *>(a.dq) + head + (size_t)i * kHeadDim;
+  const float *PK = DIL ? reinterpret_cast<const float *>(a.pk) + head + (size_t)i * kHeadDim
+                        : nullptr;
+  if constexpr (DIL) a.rho[ridx] = rho;
+  float tq = 0.0f;
+#pragma unroll
+  for (int d = 0; d < kHeadDim; ++d) {
+    const float u = DIL ? __builtin_fmaf(-rho, PK[d], x[d]) : x[d];
+    tq = __builtin_fmaf(q[d], u, tq);
+    dQ[d] = u * cs;
+  }
+  if (a.dtau) a.trow[ridx] = tq;
+}
+
+// dK and dV: lane = key column, walking the 32-row blocks that see it, top
+// down.  A block is walked twice: first for g of each row (kept in LDS, then
+// summed from the bottom row up into its inclusive suffix), then for the
+// gradients with G = (later blocks) + that suffix.
+template <bool DIL, bool CLAMP>
+__global__ void __launch_bounds__(kBR) bwd_dkdv_f32_kernel(BwdArgs a, int ntiles) {
+  __shared__ __attribute__((aligned(16))) RowTileF32 st;
+  __shared__ float sSuf[DIL ? 32 : 1][kBR];   // per row of a block, per key (lane)
+  const int t = threadIdx.x;
+  const int bh = blockIdx.x % a.BH, kb = blockIdx.x / a.BH;
+  const int T = a.T, j = kb * kBR + t;
+  const size_t head = (size_t)bh * T * kHeadDim, rbase = (size_t)bh * T;
+  const float *Q = reinterpret_cast<const float *>(a.q) + head;
+  const float *K = reinterpret_cast<const float *>(a.k) + head;
+  const float *V = reinterpret_cast<const float *>(a.v) + head;
+  const float *G = reinterpret_cast<const float *>(a.dout) + head;
+  const float *cin = a.cin + (size_t)bh * cin_floats_per_head(T, 0);
+  const float *gin = a.gin + (size_t)bh * gin_floats_per_head(T);
+  const float tb = head_tau_f32(a, bh), c2 = a.c2 * tb, cs = a.c * tb;
+  const float eps_floor = fmaxf(a.eps, FLT_MIN);
+  float kv[kHeadDim], vv[kHeadDim], dk[kHeadDim], dv[kHeadDim];
+#pragma unroll
+  for (int e = 0; e < kHeadDim; ++e) {
+    kv[e] = j < T ? K[(size_t)j * kHeadDim + e] : 0.0f;
+    vv[e] = j < T ? V[(size_t)j * kHeadDim + e] : 0.0f;
+    dk[e] = dv[e] = 0.0f;
+  }
+  for (int tile = kb; tile < ntiles; ++tile) {
+    const int i0 = tile * kBR;
+    __syncthreads();
+    load_row_tile(st, a, Q, G, rbase, i0, t, DIL);
+    __syncthreads();
+    for (int half = 0; half < 2; ++half) {
+      const int b = 2 * tile + half;
+      if (32 * b >= T) break;
+      if constexpr (DIL) {
+        const bool has = j < 32 * (b + 1) && j < T;
+        const float basev =
+            fmaxf((has ? cin[cin_block_offset(b, 0) + j] : 0.0f) + a.eps, eps_floor);
+        const float later = has ? gin[(size_t)16 * b * (b + 1) + j] : 0.0f;
+        const int nr = min(32, T - 32 * b);   // rows of the block
+        float incl = 0.0f;
+        for (int r = 0; r < nr; ++r) {
+          const int i = 32 * b + r, li = 32 * half + r;
+          const float s = dot64(&st.q[li * kHeadDim], kv), da = dot64(&st.g[li * kHeadDim], vv);
+          sSuf[r][t] = pair_terms<CLAMP>(s, da, c2, st.lse2[li], st.invr[li], st.dri[li], j <= i,
+                                         basev, incl).g;
+        }
+        // G inside the block: inclusive suffix of g, summed from the last row up
+        float suf = later;
+        for (int r = nr - 1; r >= 0; --r) {
+          suf += sSuf[r][t];
+          sSuf[r][t] = suf;
+        }
+        incl = 0.0f;
+        for (int r = 0; r < nr; ++r) {
+          const int i = 32 * b + r, li = 32 * half + r;
+          const float s = dot64(&st.q[li * kHeadDim], kv), da = dot64(&st.g[li * kHeadDim], vv);
+          const PairF32 pt = pair_terms<CLAMP>(s, da, c2, st.lse2[li], st.invr[li], st.dri[li],
+                                               j <= i, basev, incl);
+          const float Gij = sSuf[r][t];
+          const float ds = pt.p * (__builtin_fmaf(pt.dsg, pt.invd, -Gij) - st.rho[li]);
+          const float aw = pt.sg * st.invr[li];
+#pragma unroll
+          for (int e = 0; e < kHeadDim; ++e) {
+            dk[e] = __builtin_fmaf(ds, st.q[li * kHeadDim + e], dk[e]);
+            dv[e] = __builtin_fmaf(aw, st.g[li * kHeadDim + e], dv[e]);
+          }
+        }
+      } else {
+        for (int r = 0; r < 32; ++r) {
+          const int i = 32 * b + r, li = 32 * half + r;
+          if (i >= T) break;
+          const float s = dot64(&st.q[li * kHeadDim], kv), da = dot64(&st.g[li * kHeadDim], vv);
+          const float p = j <= i ? exp2f(__builtin_fmaf(s, c2, -st.lse2[li])) : 0.0f;
+          const float ds = p * (da - st.dri[li]);
+#pragma unroll
+          for (int e = 0; e < kHeadDim; ++e) {
+            dk[e] = __builtin_fmaf(ds, st.q[li * kHeadDim + e], dk[e]);
+            dv[e] = __builtin_fmaf(p, st.g[li * kHeadDim + e], dv[e]);
+          }
+        }
+      }
+    }
+  }
+  if (j >= T) return;
+  float *dK = reinterpret_cast<float *>(a.dk) + head + (size_t)j * kHeadDim;
+  float *dV = reinterpret_cast<float *>(a.dv) + head + (size_t)j * kHeadDim;
+#pragma unroll
+  for (int e = 0; e < kHeadDim; ++e) {
+    dK[e] = dk[e] * cs;
+    dV[e] = dv[e];
+  }
+}
+
+hipError_t launch_dtau(const BwdArgs &a, hipStream_t s);
+
+template <bool CLAMP>
+static hipError_t launch_bwd_f32_c(int mode, const BwdArgs &a, hipStream_t s) {
+  const bool dil = mode == 1;
+  const size_t rows = (size_t)a.BH * a.T;
+  hipLaunchKernelGGL(bwd_prep_f32_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
+                     a, dil ? 1 : 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int ntiles = (a.T + kBR - 1) / kBR;
+  const dim3 grid((unsigned)(ntiles * a.BH)), block(kBR);
+  if (dil) {
+    FwdArgs f{};
+    f.q = a.q;
+    f.k = a.k;
+    f.lse2 = a.lse2;
+    f.cin = a.cin;
+    f.BH = a.BH;
+    f.T = f.Tq = f.kstride = a.T;
+    f.D = kHeadDim;
+    f.ksplit = 1;
+    f.tau_bh = a.tau_bh;
+    f.c2 = a.c2;
+    f.eps = a.eps;
+    e = launch_colsum_f32(f, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_gsum_f32_kernel<CLAMP>, grid, block, 0, s, a, ntiles);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // PK = softmax-weighted keys: the fp32 tempered forward with the keys as values
+    FwdArgs t{};
+    t.q = a.q;
+    t.k = a.k;
+    t.v = a.k;
+    t.out = a.pk;
+    t.BH = a.BH;
+    t.T = t.Tq = t.kstride = a.T;
+    t.D = kHeadDim;
+    t.ksplit = 1;
+    t.tau_bh = a.tau_bh;
+    t.c2 = a.c2;
+    e = launch_rows_f32(kRowTempered, t, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<true, CLAMP>), grid, block, 0, s, a, ntiles);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_dtau(a, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<true, CLAMP>), grid, block, 0, s, a, ntiles);
+  } else {
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<false, false>), grid, block, 0, s, a, ntiles);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_dtau(a, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<false, false>), grid, block, 0, s, a, ntiles);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_f32(int mode, const BwdArgs &a, hipStream_t s) {
+  if (a.D != kHeadDim) return hipErrorInvalidValue;
+  // as in the bf16 kernels, the 1/D clamp matters only for eps below 2^-63
+  const bool clamp = mode == 1 && !(a.eps >= 1.0842021724855044e-19f);
+  return clamp ? launch_bwd_f32_c<true>(mode, a, s) : launch_bwd_f32_c<false>(mode, a, s);
+}
+
+}  // namespace attn

@@ -102,9 +102,11 @@ struct BwdArgs {
   float *invr;            // [BH*T] workspace: 1 / rowsum (dilution)
   float *dri;             // [BH*T] workspace: <dO_i, o_i> / rowsum (tempered: <dO_i, o_i>)
   float *rho;             // [BH*T] workspace: sum_j p_ij dp_ij (dilution)
-  float *cin;             // committed demand + eps per (32-row block, key), bf16 pairs
-  float *gin;             // later blocks' share-gradient sums per (block, key), bf16 pairs
-  void *pk;               // [BH*T*D] bf16 workspace: sum_j p_ij k_j (dilution)
+  float *cin;             // committed demand per (32-row block, key): bf16 path
+                          // committed + eps as bf16 pairs, fp32 path fp32
+  float *gin;             // later blocks' share-gradient sums per (block, key): bf16
+                          // pairs (bf16 path) or fp32
+  void *pk;               // [BH*T*D] workspace in the storage type: sum_j p_ij k_j (dilution)
   const float *tau_bh;    // [BH] per-head multipliers, or NULL (then c2, c carry tau)
   float *dtau;            // [BH] output: dL/dtau per head, or NULL
   float *trow;            // [BH*T] workspace: <q_i, dQ_i / c> per row (for dtau)
@@ -116,6 +118,7 @@ struct BwdArgs {
 };
 
 hipError_t launch_bwd_bf16(int mode, const BwdArgs &a, hipStream_t s);
+hipError_t launch_bwd_f32(int mode, const BwdArgs &a, hipStream_t s);
 
 struct DecodeArgs {
   const void *q, *kc, *vc;
