@@ -255,3 +255,30 @@ def test_t16k_bf16_against_fp32_kernels_all_rows():
             ref = run_fwd(f32, tau, mode)
         assert_close(out, ref.astype(np.float64), "bf16", f"t16k mode={mode} all rows vs fp32 kernels")
         torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+def test_t128k_bf16_against_fp32_kernels_all_rows():
+    """T = 131072 (8x the training context), every row of 4 of the 16 heads
+    (the oracle checks sampled rows of head 0): bf16 outputs and final demand
+    against the fp32 kernels on the same values, at the bf16 bar."""
+    import torch
+
+    w = PREFILL["long_t128k"]
+    inp = prefill_inputs(w, H=4)
+    wide = {n: (getattr(inp, n).astype(np.uint32) << 16).view(np.float32) for n in ("q", "k", "v")}
+    f32 = type(inp)(**{**inp.__dict__, **wide, "dtype": "f32"})
+    out, dem = run_fwd(inp, 1.0, ab.ATTN_DILUTION, w.eps, want_demand=True)
+    torch.cuda.empty_cache()
+    ref, rdem = run_fwd(f32, 1.0, ab.ATTN_DILUTION, w.eps, want_demand=True)
+    torch.cuda.empty_cache()
+    exact = [float(np.max(np.abs(x.astype(np.float64).sum(-1) / w.T - 1.0))) for x in (dem, rdem)]
+    print(f"t128k demand totals vs T: bf16 {exact[0]:.3e}, fp32 kernels {exact[1]:.3e}")
+    assert max(exact) <= DEMAND_TOTAL_REL
+    assert np.max(np.abs(dem.sum(-1) / rdem.sum(-1) - 1.0)) <= DEMAND_TOTAL_REL
+    assert np.max(np.abs(dem - rdem)) <= 2e-2 * max(1.0, float(rdem.max()))
+    assert_close(out, ref.astype(np.float64), "bf16", "t128k dilution all rows vs fp32 kernels")
+    out = run_fwd(inp, TAU8, ab.ATTN_TEMPERED)
+    torch.cuda.empty_cache()
+    ref = run_fwd(f32, TAU8, ab.ATTN_TEMPERED)
+    assert_close(out, ref.astype(np.float64), "bf16", "t128k tempered all rows vs fp32 kernels")

@@ -138,7 +138,12 @@ __global__ void __launch_bounds__(64) colsum_f32_kernel(FwdArgs a, int nkb) {
   float kv[kHeadDim];
 #pragma unroll
   for (int e = 0; e < kHeadDim; ++e) kv[e] = (j < T) ? K[(size_t)j * kHeadDim + e] : 0.0f;
+  // Each key's running demand is a compensated (Kahan) sum: a column can
+  // receive a bid from every later row, up to T of them, and a plain fp32
+  // running sum would lose the low bits of the small ones.  run - lost is
+  // the demand so far.
   float run = (a.demand_in && j < T) ? a.demand_in[(size_t)bh * a.kstride + j] : 0.0f;
+  float lost = 0.0f;
   for (int i0 = max(k0, a.vrow0); i0 < T; i0 += kFR) {
     __syncthreads();
     for (int u = t; u < kFR * kHeadDim; u += 64) {
@@ -152,14 +157,19 @@ __global__ void __launch_bounds__(64) colsum_f32_kernel(FwdArgs a, int nkb) {
     for (int ii = 0; ii < in; ++ii) {
       const int i = i0 + ii;
       if ((i & 31) == 0 && (i >> 5) >= (j >> 5) && j < T)
-        cin[cin_block_offset(i >> 5, a.vrow0) + j] = run;  // demand before block i/32
+        cin[cin_block_offset(i >> 5, a.vrow0) + j] = run - lost;  // demand before block i/32
       float s = 0.0f;
 #pragma unroll
       for (int e = 0; e < kHeadDim; ++e) s = __builtin_fmaf(sQ[ii * kHeadDim + e], kv[e], s);
-      if (j <= i && i >= P) run += exp2f(__builtin_fmaf(s, c2, -sL[ii]));
+      if (j <= i && i >= P) {
+        const float y = exp2f(__builtin_fmaf(s, c2, -sL[ii])) - lost;
+        const float t2 = run + y;
+        lost = (t2 - run) - y;
+        run = t2;
+      }
     }
   }
-  if (a.demand_out && j < T) a.demand_out[(size_t)bh * a.kstride + j] = run;
+  if (a.demand_out && j < T) a.demand_out[(size_t)bh * a.kstride + j] = run - lost;
 }
 
 hipError_t launch_rows_f32(int mode, const FwdArgs &a, hipStream_t s) {
