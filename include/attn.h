@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_EINVAL = -1,     /* bad argument: null/misaligned pointer, size <= 0, tau/eps out of range */
-  ATTN_ENOTSUP = -2,    /* valid but unsupported: head dim, fp32 decode/backward, not gfx950 */
+  ATTN_ENOTSUP = -2,    /* valid but unsupported: head dim, fp32 decode, not gfx950 */
   ATTN_EWORKSPACE = -3, /* workspace missing or smaller than *_workspace_bytes() */
   ATTN_EHIP = -4        /* a HIP runtime call or kernel launch failed */
 } attn_status;
@@ -73,7 +73,7 @@ size_t attn_fwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype)
  *   out        [B,H,T,d] device array of `dtype` (output; may not alias q/k/v)
  *   B, H, T    batch, heads, sequence length (each >= 1; T < 16777216, the
  *              kernels address one head's rows with byte offsets below 2^31)
- *   d          head dimension: 64, or 128 with ATTN_BF16 (else ATTN_ENOTSUP)
+ *   d          head dimension: 64 or 128 (else ATTN_ENOTSUP)
  *   tau        logit multiplier, finite and >= 0 (tau = 0 gives uniform bids)
  *   mode       ATTN_TEMPERED or ATTN_DILUTION
  *   eps        share-denominator constant (dilution), finite and >= 0
@@ -101,9 +101,10 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, int B, i
                 void *hip_stream);
 
 /* Bytes of device workspace attn_bwd and attn_bwd_ex need: five fp32 values
- * per query row, and for dilution the committed demand and the later rows'
- * gradient sums per (32-row query block, key): B*H*16*n*(n+1) 32-bit values
- * each, n = ceil(T/32), plus a [B,H,T,d] array of `dtype`.  0 for an
+ * per query row (six for ATTN_F32 at d = 128), and for dilution the committed
+ * demand and the later rows' gradient sums per (32-row query block, key):
+ * B*H*16*n*(n+1) 32-bit values each, n = ceil(T/32), plus a [B,H,T,d] array
+ * of `dtype`.  0 for an
  * unsupported shape, mode, head dimension or dtype. */
 size_t attn_bwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype);
 
@@ -118,9 +119,9 @@ size_t attn_bwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype)
  *   dq, dk, dv          [B,H,T,d] outputs of `dtype`, overwritten; may not
  *                       alias each other or any input
  *   B, H, T, d, tau, mode, eps  as passed to the forward
- *   dtype               ATTN_BF16 (d = 64 or 128; matrix-core kernels) or
- *                       ATTN_F32 (d = 64; vector-ALU kernels in full single
- *                       precision); else ATTN_ENOTSUP
+ *   dtype               ATTN_BF16 (matrix-core kernels) or ATTN_F32
+ *                       (vector-ALU kernels in full single precision), each
+ *                       at d = 64 or 128; else ATTN_ENOTSUP
  *   workspace           device scratch of >= attn_bwd_workspace_bytes(...)
  *                       bytes; contents on entry are ignored
  * Deterministic: fixed reduction orders, no atomics.  attn_bwd is

@@ -45,6 +45,23 @@ def errors(got: np.ndarray, ref: np.ndarray):
     return max_abs, rel_rms
 
 
+def assert_close_scaled(got, ref, what: str = ""):
+    """The bf16 bars with max-abs taken relative to max(1, |ref|) element by
+    element: the absolute bar is for O(1) outputs, and above 1 a bf16 output
+    alone carries up to half a spacing of |ref| * 2^-8 (0.0156 at 4 <= |ref| < 8),
+    so the scaled bar stays the same number of bf16 spacings at every
+    magnitude.  For whole-workload comparisons whose outputs reach several
+    units (sharp heads, V ~ N(0, 1))."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    _, rel_rms = errors(got, ref)
+    scaled = np.abs(got - ref) / np.maximum(1.0, np.abs(ref))
+    w = np.unravel_index(int(np.argmax(scaled)), scaled.shape)
+    print(f"{what}: scaled max-abs {scaled[w]:.3e} (at |ref| {abs(ref[w]):.3f}, "
+          f"abs err {abs(got[w] - ref[w]):.3e}) rel-RMS {rel_rms:.3e}")
+    assert scaled[w] <= BF16_MAX_ABS and rel_rms <= BF16_REL_RMS, what
+
+
 def assert_close(got, ref, dtype: str, what: str = ""):
     max_abs, rel_rms = errors(got, ref)
     print(f"{what}: max-abs {max_abs:.3e} rel-RMS {rel_rms:.3e}")

@@ -102,7 +102,7 @@ def fwd(**kw):
     (dict(mode=1, lse_out=FAKE + 0x4000000, rowsum_out=FAKE + 0x4000010,
           workspace=FAKE + 0x5000000, workspace_bytes=1 << 30), ab.ATTN_EINVAL),  # outputs overlap
     (dict(d=96), ab.ATTN_ENOTSUP),
-    (dict(d=128, dtype=0), ab.ATTN_ENOTSUP),         # fp32 runs at d = 64 only
+    (dict(d=128, dtype=0, mode=1), ab.ATTN_EWORKSPACE),   # fp32 at d = 128 is supported
     (dict(d=128, mode=1), ab.ATTN_EWORKSPACE),       # bf16 at d = 128 is supported
     (dict(T=1 << 24), ab.ATTN_EINVAL),               # one head's rows need offsets >= 2^31
     (dict(mode=1, T=(1 << 24) - 1, k=FAKE + (1 << 32), v=FAKE + (2 << 32),
@@ -122,7 +122,9 @@ def test_workspace_sizes():
     got = ab.attn_fwd_workspace_bytes(1, 16, 16384, 64, 1, 1)
     assert want <= got <= want + 512
     assert ab.attn_fwd_workspace_bytes(1, 1, 16, 96, 1, 1) == 0
-    assert ab.attn_fwd_workspace_bytes(1, 1, 16, 128, 1, 0) == 0      # fp32 at d = 128
+    # fp32 keeps no per-range partials: its workspace does not depend on d
+    assert (ab.attn_fwd_workspace_bytes(1, 3, 1000, 128, 1, 0)
+            == ab.attn_fwd_workspace_bytes(1, 3, 1000, 64, 1, 0) > 0)
     assert (ab.attn_fwd_workspace_bytes(1, 16, 16384, 128, 1, 1)
             == ab.attn_fwd_workspace_bytes(1, 16, 16384, 64, 1, 1))  # independent of d
     assert ab.attn_fwd_workspace_bytes(0, 1, 16, 64, 1, 1) == 0
@@ -143,7 +145,12 @@ def test_bwd_workspace_sizes():
     # fp32 (d = 64): the softmax-weighted keys are fp32
     assert (ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 0)
             - ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 1)) == 16 * 16384 * 64 * 2
-    assert ab.attn_bwd_workspace_bytes(1, 16, 16384, 128, 1, 0) == 0   # fp32 at d = 128
+    # fp32 at d = 128: dq runs in two 64-wide slices of d, so one more row
+    # array (the second slice's dL/dtau terms), and fp32 keys twice as wide
+    assert (ab.attn_bwd_workspace_bytes(1, 16, 16384, 128, 1, 0)
+            - ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 0)) == rows + 16 * 16384 * 64 * 4
+    assert (ab.attn_bwd_workspace_bytes(1, 16, 16384, 128, 0, 0)
+            - ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 0, 0)) == rows
     assert ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 2) == 0    # unknown dtype
     assert ab.attn_bwd_workspace_bytes(1, 16, 16384, 96, 1, 1) == 0
     # d = 128: the softmax-weighted keys are twice as wide
@@ -172,7 +179,8 @@ def test_prefill_workspace_sizes():
     assert ab.attn_prefill_workspace_bytes(1, 16, 10, 9, 64, 1, 1) == 0    # Tq > Tk
     assert ab.attn_prefill_workspace_bytes(1, 16, 0, 9, 64, 1, 1) == 0
     assert ab.attn_prefill_workspace_bytes(1, 16, 8, 9, 96, 1, 1) == 0
-    assert ab.attn_prefill_workspace_bytes(1, 16, 8, 9, 128, 1, 0) == 0
+    assert (ab.attn_prefill_workspace_bytes(1, 16, 8, 9, 128, 1, 0)
+            == ab.attn_prefill_workspace_bytes(1, 16, 8, 9, 64, 1, 0) > 0)
 
 
 def pre(**kw):
@@ -211,7 +219,7 @@ def pre(**kw):
      ab.ATTN_EINVAL),                                   # row sums in tempered mode
     (dict(rowsum_out=FAKE + 0x6000000, lse_out=FAKE + 0x6000100), ab.ATTN_EWORKSPACE),
     (dict(d=96), ab.ATTN_ENOTSUP),
-    (dict(d=128, dtype=0), ab.ATTN_ENOTSUP),            # fp32 runs at d = 64 only
+    (dict(d=128, dtype=0), ab.ATTN_EWORKSPACE),         # fp32 at d = 128 is supported
     (dict(d=128), ab.ATTN_EWORKSPACE),                  # bf16 at d = 128 is supported
     (dict(tau_bh=FAKE + 0x6000004), ab.ATTN_EINVAL),    # misaligned tau array
     (dict(tau_bh=FAKE + 0x4000000 + 64), ab.ATTN_EINVAL),  # tau array inside the demand
@@ -247,11 +255,11 @@ def bwd(**kw):
     (dict(T=0), ab.ATTN_EINVAL),
     (dict(tau=-1.0), ab.ATTN_EINVAL),
     (dict(eps=float("nan")), ab.ATTN_EINVAL),
-    (dict(dtype=0), ab.ATTN_EWORKSPACE),              # fp32 backward (d = 64) is supported
+    (dict(dtype=0), ab.ATTN_EWORKSPACE),              # fp32 backward is supported
     (dict(dtype=2), ab.ATTN_EINVAL),
     (dict(d=96), ab.ATTN_ENOTSUP),
     (dict(d=128), ab.ATTN_EWORKSPACE),                # d = 128 is supported
-    (dict(d=128, dtype=0), ab.ATTN_ENOTSUP),          # fp32 runs at d = 64 only
+    (dict(d=128, dtype=0), ab.ATTN_EWORKSPACE),       # fp32 at d = 128 is supported
     (dict(dk=FAKE + 0x7000000), ab.ATTN_EINVAL),      # dk aliases dq
     (dict(dv=FAKE), ab.ATTN_EINVAL),                  # dv aliases q
     (dict(), ab.ATTN_EWORKSPACE),

@@ -58,16 +58,17 @@ def test_fp32_dilution_matches_oracle(tau, eps):
     assert np.max(np.abs(dem - rdem) / np.maximum(1.0, np.abs(rdem))) <= 1e-5
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("T", [1, 7, 31, 33, 100, 257])
-def test_fp32_ragged_lengths(T):
-    inp = draw_qkv(2, 2, T, 64, "f32", seed=900 + T)
+def test_fp32_ragged_lengths(T, d):
+    inp = draw_qkv(2, 2, T, d, "f32", seed=900 + T + d)
     for mode in (ab.ATTN_TEMPERED, ab.ATTN_DILUTION):
         out = run_fwd(inp, 1.3, mode)
         if mode == ab.ATTN_TEMPERED:
             ref, _ = oracle.tempered_fwd(*oracle_qkv(inp), 1.3)
         else:
             ref, _, _ = oracle.dilution_fwd(*oracle_qkv(inp), 1.3, 1e-6)
-        assert_close(out, ref, "f32", f"T={T} mode={mode}")
+        assert_close(out, ref, "f32", f"d={d} T={T} mode={mode}")
 
 
 # ------------------------------------------------------------------ bf16 path
@@ -190,7 +191,7 @@ def test_dilution_rows_sum_to_one_via_identity_values():
 
 
 @pytest.mark.parametrize("eps", [1e-6, 0.3])
-@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
 def test_stage_calls_are_the_forward(dtype, d, eps):
     """attn_dilution_lse, attn_dilution_committed and attn_dilution_shares,
     enqueued one by one on one workspace, produce attn_fwd's output, LSE and

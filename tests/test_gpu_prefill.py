@@ -207,7 +207,7 @@ def test_long_chunk_after_long_cache():
     assert np.max(np.abs(got - Dref)) <= 2e-2 * max(1.0, float(Dref.max()))
 
 
-@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
 def test_whole_prefill_is_the_forward(dtype, d):
     """attn_prefill over a whole sequence (Tq = Tk = T, no carried demand) runs
     the forward's launches: out, lse, row sums and final column demand equal

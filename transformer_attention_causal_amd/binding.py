@@ -208,7 +208,7 @@ def fwd_workspace(B, H, T, mode, dtype_code, device, d=64):
 
 def fwd(q, k, v, tau: float = 1.0, mode: int = ATTN_TEMPERED, eps: float = 1e-6,
         out=None, workspace=None, lse_out=None, demand_out=None, rowsum_out=None):
-    """Run attn_fwd_ex on [B,H,T,d] tensors (d = 64, or 128 with bf16); returns ``out``."""
+    """Run attn_fwd_ex on [B,H,T,d] tensors (d = 64 or 128); returns ``out``."""
     import torch
 
     if not (q.shape == k.shape == v.shape) or q.dim() != 4:

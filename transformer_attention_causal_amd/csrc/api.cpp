@@ -102,8 +102,11 @@ bool dec_workspace(int S, int H, int Lcap, int d, DecWorkspace *ws) {
   return true;
 }
 
-// Head dimensions with kernels: 64 for both storage types, 128 for bf16.
-bool head_dim_ok(int d, int dtype) { return d == 64 || (d == 128 && dtype == ATTN_BF16); }
+// Head dimensions with kernels (forward, prefill, backward): 64 and 128 for
+// both storage types.
+bool head_dim_ok(int d, int dtype) {
+  return (d == 64 || d == 128) && (dtype == ATTN_BF16 || dtype == ATTN_F32);
+}
 
 bool shape_ok(int B, int H, int T) {
   if (B <= 0 || H <= 0 || T <= 0) return false;
@@ -397,24 +400,32 @@ int attn_prefill(const void *q, const void *kcache, const void *vcache, void *ou
 
 namespace {
 
-// Workspace layout of a backward pass: five per-row fp32 arrays (lse2, 1/r,
-// delta/r, rho, <q_i, dQ_i / c>), then for dilution the committed demand and the later blocks'
-// gradient sums, per (32-row block, key), and the bf16 [B,H,T,d] array of
-// softmax-weighted keys.
-constexpr size_t kBwdRowArrays = 5;
+// Workspace layout of a backward pass: per-row fp32 arrays (lse2, 1/r,
+// delta/r, rho, then <q_i, dQ_i / c> in one partial sum per slice of d that
+// the dq kernel splits the head dimension into), then for dilution the
+// committed demand and the later blocks' gradient sums, per (32-row block,
+// key), and the [B,H,T,d] array (storage type) of softmax-weighted keys.
+constexpr size_t kBwdFixedRowArrays = 4;
 struct BwdWorkspace {
+  int tslices;
   size_t row_bytes, cin_bytes, gin_bytes, pk_bytes, total;
 };
+
+// The bf16 dq kernel covers all of d in one workgroup; the fp32 one splits d
+// into 64-wide slices.
+int bwd_tslices(int d, int dtype) { return dtype == ATTN_BF16 ? 1 : d / 64; }
 
 bool bwd_workspace(int B, int H, int T, int d, int mode, int dtype, BwdWorkspace *ws) {
   const size_t BH = (size_t)B * H;
   if (BH > (size_t)INT32_MAX) return false;
+  ws->tslices = bwd_tslices(d, dtype);
   ws->row_bytes = round_up(BH * (size_t)T * sizeof(float));
   ws->cin_bytes = mode == ATTN_DILUTION ? round_up(BH * attn::cin_floats_per_head(T, 0) * 4) : 0;
   ws->gin_bytes = mode == ATTN_DILUTION ? round_up(BH * attn::gin_floats_per_head(T) * 4) : 0;
   const size_t esz = dtype == ATTN_BF16 ? 2 : 4;
   ws->pk_bytes = mode == ATTN_DILUTION ? round_up(BH * (size_t)T * d * esz) : 0;
-  ws->total = kBwdRowArrays * ws->row_bytes + ws->cin_bytes + ws->gin_bytes + ws->pk_bytes;
+  ws->total = (kBwdFixedRowArrays + ws->tslices) * ws->row_bytes + ws->cin_bytes + ws->gin_bytes +
+              ws->pk_bytes;
   return true;
 }
 
@@ -495,8 +506,9 @@ int attn_bwd_ex(const void *q, const void *k, const void *v, const void *out, co
   a.invr = reinterpret_cast<float *>(wsp + ws.row_bytes);
   a.dri = reinterpret_cast<float *>(wsp + 2 * ws.row_bytes);
   a.rho = reinterpret_cast<float *>(wsp + 3 * ws.row_bytes);
-  a.trow = reinterpret_cast<float *>(wsp + 4 * ws.row_bytes);
-  char *wtail = wsp + kBwdRowArrays * ws.row_bytes;
+  a.trow = reinterpret_cast<float *>(wsp + kBwdFixedRowArrays * ws.row_bytes);
+  a.tslices = ws.tslices;
+  char *wtail = wsp + (kBwdFixedRowArrays + ws.tslices) * ws.row_bytes;
   if (mode == ATTN_DILUTION) {
     a.cin = reinterpret_cast<float *>(wtail);
     a.gin = reinterpret_cast<float *>(wtail + ws.cin_bytes);

@@ -875,14 +875,17 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dq_kernel(B
   }
 }
 
-// dL/dtau of each head: the rows' <q_i, u_i> summed in a fixed order (strided
-// per thread, then a tree over the workgroup), times 1/sqrt(d).
+// dL/dtau of each head: the rows' <q_i, u_i> (in tslices partial sums) summed
+// in a fixed order (strided per thread, then a tree over the workgroup),
+// times 1/sqrt(d).
 __global__ void __launch_bounds__(256) bwd_dtau_kernel(BwdArgs a) {
   __shared__ float red[256];
   const int bh = blockIdx.x, tid = threadIdx.x;
-  const float *tr = a.trow + (size_t)bh * a.T;
   float acc = 0.0f;
-  for (int i = tid; i < a.T; i += 256) acc += tr[i];
+  for (int sl = 0; sl < a.tslices; ++sl) {
+    const float *tr = a.trow + ((size_t)sl * a.BH + bh) * a.T;
+    for (int i = tid; i < a.T; i += 256) acc += tr[i];
+  }
   red[tid] = acc;
   __syncthreads();
   for (int off = 128; off > 0; off >>= 1) {

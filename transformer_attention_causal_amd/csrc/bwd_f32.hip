@@ -1,4 +1,5 @@
-// bwd_f32.hip -- fp32 backward kernels (vector ALU only), head dimension 64.
+// bwd_f32.hip -- fp32 backward kernels (vector ALU only), head dimension D =
+// 64 or 128 (a template parameter of every kernel).
 //
 // The exact gradients of both operators, for fp32 storage where full single
 // precision is required.  The chain rule is the bf16 backward's
@@ -26,6 +27,7 @@
 namespace attn {
 
 constexpr int kBR = 64;   // rows or keys per workgroup and per LDS tile
+constexpr int kDS = 64;   // output dims per workgroup: d = 128 runs two slices of d
 constexpr float kInvDMaxF32 = 18446744073709551616.0f;   // 2^64: 1/D clamp (eps = 0 only)
 constexpr float kNoRowBwdF32 = 1e30f;                    // lse2 of a position past T
 
@@ -33,20 +35,24 @@ __device__ __forceinline__ float head_tau_f32(const BwdArgs &a, int bh) {
   return a.tau_bh ? a.tau_bh[bh] : 1.0f;
 }
 
-__device__ __forceinline__ float dot64(const float *x, const float *y) {
+// <x, y> over D elements (LDS or registers).  Unrolled by 16 only: full
+// unrolling hoists every operand load and spills at D = 128.
+template <int D>
+__device__ __forceinline__ float dotd(const float *x, const float *y) {
   float s = 0.0f;
-#pragma unroll
-  for (int e = 0; e < kHeadDim; ++e) s = __builtin_fmaf(x[e], y[e], s);
+#pragma unroll 16
+  for (int e = 0; e < D; ++e) s = __builtin_fmaf(x[e], y[e], s);
   return s;
 }
 
 // Per row: log2-domain lse, 1/r and delta/r (tempered: 1 and delta).
+template <int D>
 __global__ void __launch_bounds__(256) bwd_prep_f32_kernel(BwdArgs a, int dilution) {
   const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (row >= (size_t)a.BH * a.T) return;
-  const float *O = reinterpret_cast<const float *>(a.o) + row * kHeadDim;
-  const float *G = reinterpret_cast<const float *>(a.dout) + row * kHeadDim;
-  const float delta = dot64(O, G);
+  const float *O = reinterpret_cast<const float *>(a.o) + row * D;
+  const float *G = reinterpret_cast<const float *>(a.dout) + row * D;
+  const float delta = dotd<D>(O, G);
   a.lse2[row] = a.lse[row] * kLog2e;
   if (dilution) {
     const float ir = 1.0f / a.rowsum[row];
@@ -60,20 +66,22 @@ __global__ void __launch_bounds__(256) bwd_prep_f32_kernel(BwdArgs a, int diluti
 
 // Rows [i0, i0 + 64) of Q and dO and their per-row scalars into LDS; rows
 // past T read as zeros with an lse2 that makes their bids 0.
+template <int D>
 struct RowTileF32 {
-  float q[kBR * kHeadDim], g[kBR * kHeadDim];
+  float q[kBR * D], g[kBR * D];
   float lse2[kBR], invr[kBR], dri[kBR], rho[kBR];
 };
 
-__device__ __forceinline__ void load_row_tile(RowTileF32 &s, const BwdArgs &a, const float *Q,
+template <int D>
+__device__ __forceinline__ void load_row_tile(RowTileF32<D> &s, const BwdArgs &a, const float *Q,
                                               const float *G, size_t rbase, int i0, int t,
                                               bool with_rho) {
   const int T = a.T;
-  for (int u = t; u < kBR * kHeadDim; u += kBR) {
-    const int row = i0 + u / kHeadDim;
+  for (int u = t; u < kBR * D; u += kBR) {
+    const int row = i0 + u / D;
     const bool ok = row < T;
-    s.q[u] = ok ? Q[(size_t)i0 * kHeadDim + u] : 0.0f;
-    s.g[u] = ok ? G[(size_t)i0 * kHeadDim + u] : 0.0f;
+    s.q[u] = ok ? Q[(size_t)i0 * D + u] : 0.0f;
+    s.g[u] = ok ? G[(size_t)i0 * D + u] : 0.0f;
   }
   const int row = i0 + t;
   const bool ok = row < T;
@@ -105,13 +113,15 @@ __device__ __forceinline__ PairF32 pair_terms(float s, float da, float c2, float
 
 // Later blocks' g sums: for each key (lane) and 32-row block, the sum of g
 // over every block below it, walking the blocks from the last one up.
-template <bool CLAMP>
+template <bool CLAMP, int D>
 __global__ void __launch_bounds__(kBR) bwd_gsum_f32_kernel(BwdArgs a, int ntiles) {
-  __shared__ __attribute__((aligned(16))) RowTileF32 st;
+  __shared__ __attribute__((aligned(16))) RowTileF32<D> st;
+  // each lane's own K and V row, stride D + 1 (bank-conflict free)
+  __shared__ float sKr[kBR * (D + 1)], sVr[kBR * (D + 1)];
   const int t = threadIdx.x;
   const int bh = blockIdx.x % a.BH, kb = blockIdx.x / a.BH;
   const int T = a.T, j = kb * kBR + t;
-  const size_t head = (size_t)bh * T * kHeadDim, rbase = (size_t)bh * T;
+  const size_t head = (size_t)bh * T * D, rbase = (size_t)bh * T;
   const float *Q = reinterpret_cast<const float *>(a.q) + head;
   const float *K = reinterpret_cast<const float *>(a.k) + head;
   const float *V = reinterpret_cast<const float *>(a.v) + head;
@@ -120,11 +130,10 @@ __global__ void __launch_bounds__(kBR) bwd_gsum_f32_kernel(BwdArgs a, int ntiles
   float *gin = a.gin + (size_t)bh * gin_floats_per_head(T);
   const float c2 = a.c2 * head_tau_f32(a, bh);
   const float eps_floor = fmaxf(a.eps, FLT_MIN);
-  float kv[kHeadDim], vv[kHeadDim];
-#pragma unroll
-  for (int e = 0; e < kHeadDim; ++e) {
-    kv[e] = j < T ? K[(size_t)j * kHeadDim + e] : 0.0f;
-    vv[e] = j < T ? V[(size_t)j * kHeadDim + e] : 0.0f;
+  float *kv = &sKr[t * (D + 1)], *vv = &sVr[t * (D + 1)];
+  for (int e = 0; e < D; ++e) {
+    kv[e] = j < T ? K[(size_t)j * D + e] : 0.0f;
+    vv[e] = j < T ? V[(size_t)j * D + e] : 0.0f;
   }
   float running = 0.0f;
   for (int tile = ntiles - 1; tile >= kb; --tile) {
@@ -141,7 +150,7 @@ __global__ void __launch_bounds__(kBR) bwd_gsum_f32_kernel(BwdArgs a, int ntiles
       for (int r = 0; r < 32; ++r) {
         const int i = 32 * b + r, li = 32 * half + r;
         if (i >= T) break;
-        const float s = dot64(&st.q[li * kHeadDim], kv), da = dot64(&st.g[li * kHeadDim], vv);
+        const float s = dotd<D>(&st.q[li * D], kv), da = dotd<D>(&st.g[li * D], vv);
         const PairF32 pt = pair_terms<CLAMP>(s, da, c2, st.lse2[li], st.invr[li], st.dri[li],
                                              j <= i, basev, incl);
         gsum += pt.g;
@@ -153,29 +162,36 @@ __global__ void __launch_bounds__(kBR) bwd_gsum_f32_kernel(BwdArgs a, int ntiles
 }
 
 // dQ (and rho, and the rows' dL/dtau terms): lane = query row.
-template <bool DIL, bool CLAMP>
+template <bool DIL, bool CLAMP, int D>
 __global__ void __launch_bounds__(kBR) bwd_dq_f32_kernel(BwdArgs a, int nqb) {
-  __shared__ __attribute__((aligned(16))) float sK[kBR * kHeadDim];
-  __shared__ __attribute__((aligned(16))) float sV[kBR * kHeadDim];
+  __shared__ __attribute__((aligned(16))) float sK[kBR * D];
+  __shared__ __attribute__((aligned(16))) float sV[kBR * D];
+  // each lane's own Q and dO row, stride D + 1 so that the lanes' reads of
+  // one element fall in different banks (registers hold the dQ accumulator)
+  __shared__ float sQ[kBR * (D + 1)], sGd[kBR * (D + 1)];
+  constexpr int kSl = D / kDS;   // slices of d: each workgroup accumulates one
   const int t = threadIdx.x;
-  const int bh = blockIdx.x % a.BH, qb = nqb - 1 - blockIdx.x / a.BH;   // heaviest first
+  const int sl = blockIdx.x % kSl, wg = blockIdx.x / kSl;
+  const int bh = wg % a.BH, qb = nqb - 1 - wg / a.BH;   // heaviest first
+  const int d0 = kDS * sl;
   const int T = a.T, i = qb * kBR + t;
   const bool live = i < T;
   const int qs = i >> 5;
-  const size_t head = (size_t)bh * T * kHeadDim, rbase = (size_t)bh * T;
+  const size_t head = (size_t)bh * T * D, rbase = (size_t)bh * T;
   const float *Q = reinterpret_cast<const float *>(a.q) + head;
   const float *K = reinterpret_cast<const float *>(a.k) + head;
   const float *V = reinterpret_cast<const float *>(a.v) + head;
   const float *G = reinterpret_cast<const float *>(a.dout) + head;
   const float tb = head_tau_f32(a, bh), c2 = a.c2 * tb, cs = a.c * tb;
   const float eps_floor = fmaxf(a.eps, FLT_MIN);
-  float q[kHeadDim], gd[kHeadDim], x[kHeadDim];
-#pragma unroll
-  for (int e = 0; e < kHeadDim; ++e) {
-    q[e] = live ? Q[(size_t)i * kHeadDim + e] : 0.0f;
-    gd[e] = live ? G[(size_t)i * kHeadDim + e] : 0.0f;
-    x[e] = 0.0f;
+  float *q = &sQ[t * (D + 1)], *gd = &sGd[t * (D + 1)];
+  float x[kDS];   // dims d0 .. d0 + kDS - 1
+  for (int e = 0; e < D; ++e) {
+    q[e] = live ? Q[(size_t)i * D + e] : 0.0f;
+    gd[e] = live ? G[(size_t)i * D + e] : 0.0f;
   }
+#pragma unroll
+  for (int e = 0; e < kDS; ++e) x[e] = 0.0f;
   const float lse2 = live ? a.lse2[rbase + i] : kNoRowBwdF32;
   const float invr = live ? a.invr[rbase + i] : 0.0f;
   const float dri = live ? a.dri[rbase + i] : 0.0f;
@@ -185,16 +201,16 @@ __global__ void __launch_bounds__(kBR) bwd_dq_f32_kernel(BwdArgs a, int nqb) {
   const int kend = min(qb * kBR + kBR, T);
   for (int j0 = 0; j0 < kend; j0 += kBR) {
     __syncthreads();
-    for (int u = t; u < kBR * kHeadDim; u += kBR) {
-      const bool ok = j0 + u / kHeadDim < T;
-      sK[u] = ok ? K[(size_t)j0 * kHeadDim + u] : 0.0f;
-      sV[u] = ok ? V[(size_t)j0 * kHeadDim + u] : 0.0f;
+    for (int u = t; u < kBR * D; u += kBR) {
+      const bool ok = j0 + u / D < T;
+      sK[u] = ok ? K[(size_t)j0 * D + u] : 0.0f;
+      sV[u] = ok ? V[(size_t)j0 * D + u] : 0.0f;
     }
     __syncthreads();
     const int jn = min(kBR, kend - j0);
     for (int jj = 0; jj < jn; ++jj) {
       const int j = j0 + jj;
-      const float s = dot64(q, &sK[jj * kHeadDim]), da = dot64(gd, &sV[jj * kHeadDim]);
+      const float s = dotd<D>(q, &sK[jj * D]), da = dotd<D>(gd, &sV[jj * D]);
       const bool vis = live && j <= i;
       float e;
       if constexpr (DIL) {
@@ -229,37 +245,42 @@ __global__ void __launch_bounds__(kBR) bwd_dq_f32_kernel(BwdArgs a, int nqb) {
         e = p * (da - dri);
       }
 #pragma unroll
-      for (int d = 0; d < kHeadDim; ++d) x[d] = __builtin_fmaf(e, sK[jj * kHeadDim + d], x[d]);
+      for (int d = 0; d < kDS; ++d) x[d] = __builtin_fmaf(e, sK[jj * D + d0 + d], x[d]);
     }
   }
   if (!live) return;
   const size_t ridx = rbase + i;
-  float *dQ = reinterpret_cast<float *>(a.dq) + head + (size_t)i * kHeadDim;
-  const float *PK = DIL ? reinterpret_cast<const float *>(a.pk) + head + (size_t)i * kHeadDim
+  float *dQ = reinterpret_cast<float *>(a.dq) + head + (size_t)i * D + d0;
+  const float *PK = DIL ? reinterpret_cast<const float *>(a.pk) + head + (size_t)i * D + d0
                         : nullptr;
-  if constexpr (DIL) a.rho[ridx] = rho;
+  if (DIL && sl == 0) a.rho[ridx] = rho;   // every slice forms the same rho
   float tq = 0.0f;
 #pragma unroll
-  for (int d = 0; d < kHeadDim; ++d) {
+  for (int d = 0; d < kDS; ++d) {
     const float u = DIL ? __builtin_fmaf(-rho, PK[d], x[d]) : x[d];
-    tq = __builtin_fmaf(q[d], u, tq);
+    tq = __builtin_fmaf(q[d0 + d], u, tq);
     dQ[d] = u * cs;
   }
-  if (a.dtau) a.trow[ridx] = tq;
+  if (a.dtau) a.trow[(size_t)sl * a.BH * T + ridx] = tq;   // this slice's part
 }
 
 // dK and dV: lane = key column, walking the 32-row blocks that see it, top
 // down.  A block is walked twice: first for g of each row (kept in LDS, then
 // summed from the bottom row up into its inclusive suffix), then for the
 // gradients with G = (later blocks) + that suffix.
-template <bool DIL, bool CLAMP>
+template <bool DIL, bool CLAMP, int D>
 __global__ void __launch_bounds__(kBR) bwd_dkdv_f32_kernel(BwdArgs a, int ntiles) {
-  __shared__ __attribute__((aligned(16))) RowTileF32 st;
+  __shared__ __attribute__((aligned(16))) RowTileF32<D> st;
   __shared__ float sSuf[DIL ? 32 : 1][kBR];   // per row of a block, per key (lane)
+  // each lane's own K and V row, stride D + 1 (registers hold dK and dV)
+  __shared__ float sKr[kBR * (D + 1)], sVr[kBR * (D + 1)];
+  constexpr int kSl = D / kDS;   // slices of d: each workgroup accumulates one
   const int t = threadIdx.x;
-  const int bh = blockIdx.x % a.BH, kb = blockIdx.x / a.BH;
+  const int sl = blockIdx.x % kSl, wg = blockIdx.x / kSl;
+  const int bh = wg % a.BH, kb = wg / a.BH;
+  const int d0 = kDS * sl;
   const int T = a.T, j = kb * kBR + t;
-  const size_t head = (size_t)bh * T * kHeadDim, rbase = (size_t)bh * T;
+  const size_t head = (size_t)bh * T * D, rbase = (size_t)bh * T;
   const float *Q = reinterpret_cast<const float *>(a.q) + head;
   const float *K = reinterpret_cast<const float *>(a.k) + head;
   const float *V = reinterpret_cast<const float *>(a.v) + head;
@@ -268,13 +289,14 @@ __global__ void __launch_bounds__(kBR) bwd_dkdv_f32_kernel(BwdArgs a, int ntiles
   const float *gin = a.gin + (size_t)bh * gin_floats_per_head(T);
   const float tb = head_tau_f32(a, bh), c2 = a.c2 * tb, cs = a.c * tb;
   const float eps_floor = fmaxf(a.eps, FLT_MIN);
-  float kv[kHeadDim], vv[kHeadDim], dk[kHeadDim], dv[kHeadDim];
-#pragma unroll
-  for (int e = 0; e < kHeadDim; ++e) {
-    kv[e] = j < T ? K[(size_t)j * kHeadDim + e] : 0.0f;
-    vv[e] = j < T ? V[(size_t)j * kHeadDim + e] : 0.0f;
-    dk[e] = dv[e] = 0.0f;
+  float *kv = &sKr[t * (D + 1)], *vv = &sVr[t * (D + 1)];
+  float dk[kDS], dv[kDS];   // dims d0 .. d0 + kDS - 1
+  for (int e = 0; e < D; ++e) {
+    kv[e] = j < T ? K[(size_t)j * D + e] : 0.0f;
+    vv[e] = j < T ? V[(size_t)j * D + e] : 0.0f;
   }
+#pragma unroll
+  for (int e = 0; e < kDS; ++e) dk[e] = dv[e] = 0.0f;
   for (int tile = kb; tile < ntiles; ++tile) {
     const int i0 = tile * kBR;
     __syncthreads();
@@ -292,7 +314,7 @@ __global__ void __launch_bounds__(kBR) bwd_dkdv_f32_kernel(BwdArgs a, int ntiles
         float incl = 0.0f;
         for (int r = 0; r < nr; ++r) {
           const int i = 32 * b + r, li = 32 * half + r;
-          const float s = dot64(&st.q[li * kHeadDim], kv), da = dot64(&st.g[li * kHeadDim], vv);
+          const float s = dotd<D>(&st.q[li * D], kv), da = dotd<D>(&st.g[li * D], vv);
           sSuf[r][t] = pair_terms<CLAMP>(s, da, c2, st.lse2[li], st.invr[li], st.dri[li], j <= i,
                                          basev, incl).g;
         }
@@ -305,39 +327,39 @@ __global__ void __launch_bounds__(kBR) bwd_dkdv_f32_kernel(BwdArgs a, int ntiles
         incl = 0.0f;
         for (int r = 0; r < nr; ++r) {
           const int i = 32 * b + r, li = 32 * half + r;
-          const float s = dot64(&st.q[li * kHeadDim], kv), da = dot64(&st.g[li * kHeadDim], vv);
+          const float s = dotd<D>(&st.q[li * D], kv), da = dotd<D>(&st.g[li * D], vv);
           const PairF32 pt = pair_terms<CLAMP>(s, da, c2, st.lse2[li], st.invr[li], st.dri[li],
                                                j <= i, basev, incl);
           const float Gij = sSuf[r][t];
           const float ds = pt.p * (__builtin_fmaf(pt.dsg, pt.invd, -Gij) - st.rho[li]);
           const float aw = pt.sg * st.invr[li];
 #pragma unroll
-          for (int e = 0; e < kHeadDim; ++e) {
-            dk[e] = __builtin_fmaf(ds, st.q[li * kHeadDim + e], dk[e]);
-            dv[e] = __builtin_fmaf(aw, st.g[li * kHeadDim + e], dv[e]);
+          for (int e = 0; e < kDS; ++e) {
+            dk[e] = __builtin_fmaf(ds, st.q[li * D + d0 + e], dk[e]);
+            dv[e] = __builtin_fmaf(aw, st.g[li * D + d0 + e], dv[e]);
           }
         }
       } else {
         for (int r = 0; r < 32; ++r) {
           const int i = 32 * b + r, li = 32 * half + r;
           if (i >= T) break;
-          const float s = dot64(&st.q[li * kHeadDim], kv), da = dot64(&st.g[li * kHeadDim], vv);
+          const float s = dotd<D>(&st.q[li * D], kv), da = dotd<D>(&st.g[li * D], vv);
           const float p = j <= i ? exp2f(__builtin_fmaf(s, c2, -st.lse2[li])) : 0.0f;
           const float ds = p * (da - st.dri[li]);
 #pragma unroll
-          for (int e = 0; e < kHeadDim; ++e) {
-            dk[e] = __builtin_fmaf(ds, st.q[li * kHeadDim + e], dk[e]);
-            dv[e] = __builtin_fmaf(p, st.g[li * kHeadDim + e], dv[e]);
+          for (int e = 0; e < kDS; ++e) {
+            dk[e] = __builtin_fmaf(ds, st.q[li * D + d0 + e], dk[e]);
+            dv[e] = __builtin_fmaf(p, st.g[li * D + d0 + e], dv[e]);
           }
         }
       }
     }
   }
   if (j >= T) return;
-  float *dK = reinterpret_cast<float *>(a.dk) + head + (size_t)j * kHeadDim;
-  float *dV = reinterpret_cast<float *>(a.dv) + head + (size_t)j * kHeadDim;
+  float *dK = reinterpret_cast<float *>(a.dk) + head + (size_t)j * D + d0;
+  float *dV = reinterpret_cast<float *>(a.dv) + head + (size_t)j * D + d0;
 #pragma unroll
-  for (int e = 0; e < kHeadDim; ++e) {
+  for (int e = 0; e < kDS; ++e) {
     dK[e] = dk[e] * cs;
     dV[e] = dv[e];
   }
@@ -345,16 +367,17 @@ __global__ void __launch_bounds__(kBR) bwd_dkdv_f32_kernel(BwdArgs a, int ntiles
 
 hipError_t launch_dtau(const BwdArgs &a, hipStream_t s);
 
-template <bool CLAMP>
+template <bool CLAMP, int D>
 static hipError_t launch_bwd_f32_c(int mode, const BwdArgs &a, hipStream_t s) {
   const bool dil = mode == 1;
   const size_t rows = (size_t)a.BH * a.T;
-  hipLaunchKernelGGL(bwd_prep_f32_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
-                     a, dil ? 1 : 0);
+  hipLaunchKernelGGL(bwd_prep_f32_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                     s, a, dil ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int ntiles = (a.T + kBR - 1) / kBR;
   const dim3 grid((unsigned)(ntiles * a.BH)), block(kBR);
+  const dim3 grid_sl((unsigned)(ntiles * a.BH * (D / kDS)));   // dQ and dK/dV: slices of d
   if (dil) {
     FwdArgs f{};
     f.q = a.q;
@@ -363,14 +386,14 @@ static hipError_t launch_bwd_f32_c(int mode, const BwdArgs &a, hipStream_t s) {
     f.cin = a.cin;
     f.BH = a.BH;
     f.T = f.Tq = f.kstride = a.T;
-    f.D = kHeadDim;
+    f.D = D;
     f.ksplit = 1;
     f.tau_bh = a.tau_bh;
     f.c2 = a.c2;
     f.eps = a.eps;
     e = launch_colsum_f32(f, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_gsum_f32_kernel<CLAMP>, grid, block, 0, s, a, ntiles);
+    hipLaunchKernelGGL((bwd_gsum_f32_kernel<CLAMP, D>), grid, block, 0, s, a, ntiles);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // PK = softmax-weighted keys: the fp32 tempered forward with the keys as values
@@ -381,34 +404,42 @@ static hipError_t launch_bwd_f32_c(int mode, const BwdArgs &a, hipStream_t s) {
     t.out = a.pk;
     t.BH = a.BH;
     t.T = t.Tq = t.kstride = a.T;
-    t.D = kHeadDim;
+    t.D = D;
     t.ksplit = 1;
     t.tau_bh = a.tau_bh;
     t.c2 = a.c2;
     e = launch_rows_f32(kRowTempered, t, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_f32_kernel<true, CLAMP>), grid, block, 0, s, a, ntiles);
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<true, CLAMP, D>), grid_sl, block, 0, s, a, ntiles);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_dtau(a, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<true, CLAMP>), grid, block, 0, s, a, ntiles);
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<true, CLAMP, D>), grid_sl, block, 0, s, a, ntiles);
   } else {
-    hipLaunchKernelGGL((bwd_dq_f32_kernel<false, false>), grid, block, 0, s, a, ntiles);
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<false, false, D>), grid_sl, block, 0, s, a, ntiles);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_dtau(a, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<false, false>), grid, block, 0, s, a, ntiles);
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<false, false, D>), grid_sl, block, 0, s, a, ntiles);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_f32(int mode, const BwdArgs &a, hipStream_t s) {
-  if (a.D != kHeadDim) return hipErrorInvalidValue;
+template <int D>
+static hipError_t launch_bwd_f32_d(int mode, const BwdArgs &a, hipStream_t s) {
   // as in the bf16 kernels, the 1/D clamp matters only for eps below 2^-63
   const bool clamp = mode == 1 && !(a.eps >= 1.0842021724855044e-19f);
-  return clamp ? launch_bwd_f32_c<true>(mode, a, s) : launch_bwd_f32_c<false>(mode, a, s);
+  return clamp ? launch_bwd_f32_c<true, D>(mode, a, s) : launch_bwd_f32_c<false, D>(mode, a, s);
+}
+
+hipError_t launch_bwd_f32(int mode, const BwdArgs &a, hipStream_t s) {
+  switch (a.D) {
+    case 64: return launch_bwd_f32_d<64>(mode, a, s);
+    case 128: return launch_bwd_f32_d<128>(mode, a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace attn

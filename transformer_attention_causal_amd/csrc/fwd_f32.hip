@@ -1,4 +1,5 @@
-// fwd_f32.hip -- fp32 forward kernels (vector ALU only; no bf16 anywhere).
+// fwd_f32.hip -- fp32 forward kernels (vector ALU only; no bf16 anywhere),
+// head dimension D = 64 or 128 (a template parameter).
 //
 // Same operations and the same three-pass structure as the bf16 kernels
 // (tempered causal softmax attention -- "Learning to Focus: Focal Attention"
@@ -19,10 +20,10 @@ namespace attn {
 constexpr int kFR = 64;  // rows per workgroup / tile
 constexpr float kNoRowF32 = 1e30f;  // log-sum-exp of a position that holds no row
 
-template <int MODE>
+template <int MODE, int D>
 __global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
-  __shared__ __attribute__((aligned(16))) float sK[kFR * kHeadDim];
-  __shared__ __attribute__((aligned(16))) float sV[MODE == kRowLse ? 4 : kFR * kHeadDim];
+  __shared__ __attribute__((aligned(16))) float sK[kFR * D];
+  __shared__ __attribute__((aligned(16))) float sV[MODE == kRowLse ? 4 : kFR * D];
   // Rows are positions: query row r of Q is position P + r (P = 0 for a
   // whole prefill); blocks start at position vrow0 <= P, and lanes at
   // positions before P hold no row.
@@ -34,16 +35,16 @@ __global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
   const int i = q0 + t;  // this lane's position
   const int li = i - P;  // and its query row
   const bool live = (unsigned)li < (unsigned)Tq;
-  const size_t qhead = (size_t)bh * Tq * kHeadDim, khead = (size_t)bh * a.kstride * kHeadDim;
+  const size_t qhead = (size_t)bh * Tq * D, khead = (size_t)bh * a.kstride * D;
   const float c2 = head_c2(a, bh);
   const float *Q = reinterpret_cast<const float *>(a.q) + qhead;
   const float *K = reinterpret_cast<const float *>(a.k) + khead;
   const float *V = reinterpret_cast<const float *>(a.v) + khead;
 
-  float q[kHeadDim], acc[kHeadDim];
+  float q[D], acc[D];
 #pragma unroll
-  for (int e = 0; e < kHeadDim; ++e) {
-    q[e] = live ? Q[(size_t)li * kHeadDim + e] : 0.0f;
+  for (int e = 0; e < D; ++e) {
+    q[e] = live ? Q[(size_t)li * D + e] : 0.0f;
     acc[e] = 0.0f;
   }
   float m = -INFINITY, l = 0.0f, lse2 = 0.0f;
@@ -58,10 +59,10 @@ __global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
 
   for (int j0 = 0; j0 < kend; j0 += kFR) {
     __syncthreads();
-    for (int u = t; u < kFR * kHeadDim; u += 64) {
-      const int row = j0 + u / kHeadDim;
-      sK[u] = row < T ? K[(size_t)j0 * kHeadDim + u] : 0.0f;
-      if constexpr (MODE != kRowLse) sV[u] = row < T ? V[(size_t)j0 * kHeadDim + u] : 0.0f;
+    for (int u = t; u < kFR * D; u += 64) {
+      const int row = j0 + u / D;
+      sK[u] = row < T ? K[(size_t)j0 * D + u] : 0.0f;
+      if constexpr (MODE != kRowLse) sV[u] = row < T ? V[(size_t)j0 * D + u] : 0.0f;
     }
     __syncthreads();
     const int jn = min(kFR, kend - j0);
@@ -69,7 +70,7 @@ __global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
       const int j = j0 + jj;
       float s = 0.0f;
 #pragma unroll
-      for (int e = 0; e < kHeadDim; ++e) s = __builtin_fmaf(q[e], sK[jj * kHeadDim + e], s);
+      for (int e = 0; e < D; ++e) s = __builtin_fmaf(q[e], sK[jj * D + e], s);
       const bool vis = (j <= i) && live;
       if constexpr (MODE == kRowTempered || MODE == kRowLse) {
         if (vis) {
@@ -80,7 +81,7 @@ __global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
           l = l * alpha + p;
           if constexpr (MODE == kRowTempered) {
 #pragma unroll
-            for (int e = 0; e < kHeadDim; ++e) acc[e] = __builtin_fmaf(p, sV[jj * kHeadDim + e], acc[e] * alpha);
+            for (int e = 0; e < D; ++e) acc[e] = __builtin_fmaf(p, sV[jj * D + e], acc[e] * alpha);
           }
           m = m_new;
         }
@@ -98,7 +99,7 @@ __global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
         const float share = p / (base + incl);
         l += share;
 #pragma unroll
-        for (int e = 0; e < kHeadDim; ++e) acc[e] = __builtin_fmaf(share, sV[jj * kHeadDim + e], acc[e]);
+        for (int e = 0; e < D; ++e) acc[e] = __builtin_fmaf(share, sV[jj * D + e], acc[e]);
       }
     }
   }
@@ -112,15 +113,16 @@ __global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
     if (a.rowsum_out) a.rowsum_out[(size_t)bh * Tq + li] = l;
   }
   if constexpr (MODE != kRowLse) {
-    float *O = reinterpret_cast<float *>(a.out) + qhead + (size_t)li * kHeadDim;
+    float *O = reinterpret_cast<float *>(a.out) + qhead + (size_t)li * D;
     const float inv = 1.0f / l;
 #pragma unroll
-    for (int e = 0; e < kHeadDim; ++e) O[e] = acc[e] * inv;
+    for (int e = 0; e < D; ++e) O[e] = acc[e] * inv;
   }
 }
 
+template <int D>
 __global__ void __launch_bounds__(64) colsum_f32_kernel(FwdArgs a, int nkb) {
-  __shared__ __attribute__((aligned(16))) float sQ[kFR * kHeadDim];
+  __shared__ __attribute__((aligned(16))) float sQ[kFR * D];
   __shared__ float sL[kFR];
   // Positions i of the walk are query row i - P (P = 0 for a whole prefill);
   // positions before P, from vrow0 on, are no row and bid nothing.
@@ -130,14 +132,14 @@ __global__ void __launch_bounds__(64) colsum_f32_kernel(FwdArgs a, int nkb) {
   const int T = a.T, Tq = a.Tq, P = T - Tq;
   const int k0 = kb * kFR;
   const int j = k0 + t;  // this lane's key column
-  const float *Q = reinterpret_cast<const float *>(a.q) + (size_t)bh * Tq * kHeadDim;
-  const float *K = reinterpret_cast<const float *>(a.k) + (size_t)bh * a.kstride * kHeadDim;
+  const float *Q = reinterpret_cast<const float *>(a.q) + (size_t)bh * Tq * D;
+  const float *K = reinterpret_cast<const float *>(a.k) + (size_t)bh * a.kstride * D;
   const float c2 = head_c2(a, bh);
   float *cin = a.cin + (size_t)bh * cin_floats_per_head(T, a.vrow0);
 
-  float kv[kHeadDim];
+  float kv[D];
 #pragma unroll
-  for (int e = 0; e < kHeadDim; ++e) kv[e] = (j < T) ? K[(size_t)j * kHeadDim + e] : 0.0f;
+  for (int e = 0; e < D; ++e) kv[e] = (j < T) ? K[(size_t)j * D + e] : 0.0f;
   // Each key's running demand is a compensated (Kahan) sum: a column can
   // receive a bid from every later row, up to T of them, and a plain fp32
   // running sum would lose the low bits of the small ones.  run - lost is
@@ -146,9 +148,9 @@ __global__ void __launch_bounds__(64) colsum_f32_kernel(FwdArgs a, int nkb) {
   float lost = 0.0f;
   for (int i0 = max(k0, a.vrow0); i0 < T; i0 += kFR) {
     __syncthreads();
-    for (int u = t; u < kFR * kHeadDim; u += 64) {
-      const int lr = i0 + u / kHeadDim - P;
-      sQ[u] = (unsigned)lr < (unsigned)Tq ? Q[(size_t)lr * kHeadDim + u % kHeadDim] : 0.0f;
+    for (int u = t; u < kFR * D; u += 64) {
+      const int lr = i0 + u / D - P;
+      sQ[u] = (unsigned)lr < (unsigned)Tq ? Q[(size_t)lr * D + u % D] : 0.0f;
     }
     const int lt = i0 + t - P;
     sL[t] = (unsigned)lt < (unsigned)Tq ? a.lse2[(size_t)bh * Tq + lt] : kNoRowF32;
@@ -160,7 +162,7 @@ __global__ void __launch_bounds__(64) colsum_f32_kernel(FwdArgs a, int nkb) {
         cin[cin_block_offset(i >> 5, a.vrow0) + j] = run - lost;  // demand before block i/32
       float s = 0.0f;
 #pragma unroll
-      for (int e = 0; e < kHeadDim; ++e) s = __builtin_fmaf(sQ[ii * kHeadDim + e], kv[e], s);
+      for (int e = 0; e < D; ++e) s = __builtin_fmaf(sQ[ii * D + e], kv[e], s);
       if (j <= i && i >= P) {
         const float y = exp2f(__builtin_fmaf(s, c2, -sL[ii])) - lost;
         const float t2 = run + y;
@@ -172,20 +174,36 @@ __global__ void __launch_bounds__(64) colsum_f32_kernel(FwdArgs a, int nkb) {
   if (a.demand_out && j < T) a.demand_out[(size_t)bh * a.kstride + j] = run - lost;
 }
 
-hipError_t launch_rows_f32(int mode, const FwdArgs &a, hipStream_t s) {
+template <int D>
+static hipError_t launch_rows_f32_d(int mode, const FwdArgs &a, hipStream_t s) {
   const int nqb = (a.T + kFR - 1) / kFR - a.vrow0 / kFR;   // blocks from position vrow0
   dim3 grid((unsigned)(nqb * a.BH)), block(64);
   switch (mode) {
-    case kRowTempered: hipLaunchKernelGGL(rows_f32_kernel<kRowTempered>, grid, block, 0, s, a, nqb); break;
-    case kRowLse: hipLaunchKernelGGL(rows_f32_kernel<kRowLse>, grid, block, 0, s, a, nqb); break;
-    default: hipLaunchKernelGGL(rows_f32_kernel<kRowShare>, grid, block, 0, s, a, nqb); break;
+    case kRowTempered:
+      hipLaunchKernelGGL((rows_f32_kernel<kRowTempered, D>), grid, block, 0, s, a, nqb);
+      break;
+    case kRowLse: hipLaunchKernelGGL((rows_f32_kernel<kRowLse, D>), grid, block, 0, s, a, nqb); break;
+    default: hipLaunchKernelGGL((rows_f32_kernel<kRowShare, D>), grid, block, 0, s, a, nqb); break;
   }
   return hipGetLastError();
 }
 
+hipError_t launch_rows_f32(int mode, const FwdArgs &a, hipStream_t s) {
+  switch (a.D) {
+    case 64: return launch_rows_f32_d<64>(mode, a, s);
+    case 128: return launch_rows_f32_d<128>(mode, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_colsum_f32(const FwdArgs &a, hipStream_t s) {
   const int nkb = (a.T + kFR - 1) / kFR;
-  hipLaunchKernelGGL(colsum_f32_kernel, dim3((unsigned)(nkb * a.BH)), dim3(64), 0, s, a, nkb);
+  const dim3 grid((unsigned)(nkb * a.BH)), block(64);
+  switch (a.D) {
+    case 64: hipLaunchKernelGGL(colsum_f32_kernel<64>, grid, block, 0, s, a, nkb); break;
+    case 128: hipLaunchKernelGGL(colsum_f32_kernel<128>, grid, block, 0, s, a, nkb); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -7,7 +7,7 @@
 
 namespace attn {
 
-constexpr int kHeadDim = 64;  // the head dimension of the fp32 path
+constexpr int kHeadDim = 64;  // default head dimension of the row-load helpers
 
 // Row-major passes over the causal score matrix (one workgroup per query
 // block).  lse2 is the log2-domain log-sum-exp of each row.
@@ -109,7 +109,9 @@ struct BwdArgs {
   void *pk;               // [BH*T*D] workspace in the storage type: sum_j p_ij k_j (dilution)
   const float *tau_bh;    // [BH] per-head multipliers, or NULL (then c2, c carry tau)
   float *dtau;            // [BH] output: dL/dtau per head, or NULL
-  float *trow;            // [BH*T] workspace: <q_i, dQ_i / c> per row (for dtau)
+  float *trow;            // [tslices][BH*T] workspace: <q_i, dQ_i / c> per row (for
+                          // dtau), in tslices partial sums over slices of d
+  int tslices;            // 1, or the fp32 kernels' number of 64-wide slices of d
   int BH, T, D;           // D: head dimension, 64 or 128
   float c2;               // tau / sqrt(d) * log2(e)  (with tau_bh: log2(e) / sqrt(d))
   float c;                // tau / sqrt(d)            (with tau_bh: 1 / sqrt(d))
