@@ -104,8 +104,7 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, int B, i
  * per query row (six for ATTN_F32 at d = 128), and for dilution the committed
  * demand and the later rows' gradient sums per (32-row query block, key):
  * B*H*16*n*(n+1) 32-bit values each, n = ceil(T/32), plus a [B,H,T,d] array
- * of `dtype`.  0 for an
- * unsupported shape, mode, head dimension or dtype. */
+ * of `dtype`.  0 for an unsupported shape, mode, head dimension or dtype. */
 size_t attn_bwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype);
 
 /* Exact gradients of either operator (DilutionAttention v0.1.0: the release's
@@ -125,7 +124,7 @@ size_t attn_bwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype)
  *   workspace           device scratch of >= attn_bwd_workspace_bytes(...)
  *                       bytes; contents on entry are ignored
  * Deterministic: fixed reduction orders, no atomics.  attn_bwd is
- * attn_bwd_ex with tau_bh = dtau_out = NULL. */
+ * attn_bwd_ex with tau_bh = dtau_out = fwd_workspace = NULL. */
 int attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout,
              const float *lse, const float *rowsum, void *dq, void *dk, void *dv, int B, int H,
              int T, int d, float tau, int mode, float eps, int dtype, void *workspace,
@@ -133,7 +132,8 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *out, const
 
 /* attn_bwd with per-head multipliers and the gradient with respect to them
  * ("Learning to Focus", sec. 2.2: the temperature is learned, so training
- * needs dL/dtau).  Arguments as attn_bwd, and:
+ * needs dL/dtau), and optionally the dilution forward's own workspace.
+ * Arguments as attn_bwd, and:
  *   tau_bh    [B,H] fp32 device array or NULL: head (b,h)'s multiplier, as
  *             given to attn_prefill (which produces the matching lse and
  *             rowsum through lse_out/rowsum_out); tau is then ignored.
@@ -144,11 +144,26 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *out, const
  *             dL/dtau is the sum over heads).  It is formed as
  *             sum_i <q_i, dQ_i / c> / sqrt(d) with fp32 row terms, so it is
  *             defined at tau = 0 too.  May not overlap any other argument.
+ *   fwd_workspace, fwd_workspace_bytes
+ *             NULL and 0, or (ATTN_DILUTION; ignored for ATTN_TEMPERED) the
+ *             workspace of the forward that produced `out`, `lse` and
+ *             `rowsum` from these q, k, v (attn_fwd / attn_fwd_ex, the three
+ *             stage calls, or attn_prefill of the whole sequence with
+ *             Tq = Tk = T and no carried demand), with the same B, H, T, d,
+ *             tau or tau_bh, eps and dtype, and not written since.  Read
+ *             only: its committed-demand table is used as is instead of
+ *             being recomputed (one pass over all pairs fewer).  The caller
+ *             vouches for it as for lse and rowsum; nothing on the device
+ *             checks it.  fwd_workspace_bytes must be >=
+ *             attn_fwd_workspace_bytes(B,H,T,d,ATTN_DILUTION,dtype) and the
+ *             pointer 16-byte aligned (else ATTN_EWORKSPACE); it may not
+ *             overlap dq, dk, dv, dtau_out or `workspace` (else ATTN_EINVAL).
  * tau_bh may not overlap dq, dk, dv or dtau_out. */
 int attn_bwd_ex(const void *q, const void *k, const void *v, const void *out, const void *dout,
                 const float *lse, const float *rowsum, void *dq, void *dk, void *dv, int B,
                 int H, int T, int d, float tau, const float *tau_bh, int mode, float eps,
-                int dtype, float *dtau_out, void *workspace, size_t workspace_bytes,
+                int dtype, float *dtau_out, const void *fwd_workspace,
+                size_t fwd_workspace_bytes, void *workspace, size_t workspace_bytes,
                 void *hip_stream);
 
 /* The dilution forward pass, one stage per call (attn_fwd with ATTN_DILUTION

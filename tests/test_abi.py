@@ -232,16 +232,22 @@ def test_prefill_rejects_bad_arguments(kw, status):
     assert pre(**kw) == status
 
 
+BWD_WS = dict(workspace=FAKE + 0xc000000, workspace_bytes=1 << 24)
+
+
 def bwd(**kw):
     base = FAKE
     args = dict(q=base, k=base + 0x1000000, v=base + 0x2000000, out=base + 0x3000000,
                 dout=base + 0x4000000, lse=base + 0x5000000, rowsum=base + 0x6000000,
                 dq=base + 0x7000000, dk=base + 0x8000000, dv=base + 0x9000000, B=1, H=1, T=16,
                 d=64, tau=1.0, tau_bh=None, mode=1, eps=1e-6, dtype=1, dtau_out=None,
-                workspace=None, workspace_bytes=0, hip_stream=None)
+                fwd_workspace=None, fwd_workspace_bytes=0, workspace=None, workspace_bytes=0,
+                hip_stream=None)
     args.update(kw)
-    if "tau_bh" not in kw and "dtau_out" not in kw:
-        del args["tau_bh"], args["dtau_out"]
+    ex_only = ("tau_bh", "dtau_out", "fwd_workspace", "fwd_workspace_bytes")
+    if not any(n in kw for n in ex_only):
+        for n in ex_only:
+            del args[n]
         return ab.attn_bwd(**args)
     return ab.attn_bwd_ex(**args)
 
@@ -272,6 +278,16 @@ def bwd(**kw):
     (dict(tau_bh=FAKE + 0xa000000, dtau_out=FAKE + 0xa000000), ab.ATTN_EINVAL),
     (dict(tau_bh=FAKE + 0xa000000, dtau_out=FAKE + 0xb000000), ab.ATTN_EWORKSPACE),
     (dict(tau_bh=None, dtau_out=FAKE + 0xb000000), ab.ATTN_EWORKSPACE),
+    # the forward's workspace (read only; its committed-demand table is reused)
+    (dict(fwd_workspace=FAKE + 0xd000000, fwd_workspace_bytes=64, **BWD_WS), ab.ATTN_EWORKSPACE),
+    (dict(fwd_workspace=FAKE + 0xd000004, fwd_workspace_bytes=1 << 20, **BWD_WS),
+     ab.ATTN_EWORKSPACE),                                # misaligned
+    (dict(fwd_workspace=FAKE + 0x6ffff00, fwd_workspace_bytes=1 << 20, **BWD_WS),
+     ab.ATTN_EINVAL),                                    # runs into dq
+    (dict(fwd_workspace=FAKE + 0xc000100, fwd_workspace_bytes=1 << 20, **BWD_WS),
+     ab.ATTN_EINVAL),                                    # inside the backward's workspace
+    (dict(fwd_workspace=FAKE + 0xd000000, fwd_workspace_bytes=1 << 20,
+          dtau_out=FAKE + 0xd000100, **BWD_WS), ab.ATTN_EINVAL),
 ])
 def test_bwd_rejects_bad_arguments(kw, status):
     assert bwd(**kw) == status

@@ -509,3 +509,64 @@ def test_bwd_focal_d128_bf16_against_fp32_kernels():
         check_grads(got[:3], ref[:3], f"focal d128 bf16 vs fp32 kernels mode={mode}")
         check_dtau(got[3], ref[0].astype(np.float64), inp, g, taus, ref[3].astype(np.float64),
                    f"focal d128 bf16 vs fp32 kernels mode={mode}")
+
+
+@pytest.mark.parametrize("dtype,d,per_head", [("bf16", 64, False), ("bf16", 128, True),
+                                              ("f32", 64, False), ("f32", 128, True)])
+def test_bwd_reads_the_forwards_committed_table(dtype, d, per_head):
+    """attn_bwd_ex given the dilution forward's workspace reads its
+    committed-demand table instead of recomputing it: the gradients and
+    dL/dtau match the recomputing call (the two tables differ only by the
+    rounding of lse between its natural-log output and the base-2 form the
+    forward kept) and the oracle, and the forward's workspace is left as it
+    was."""
+    import torch
+
+    from gpu_util import to_device
+
+    B, H, T = 1, 3, 333
+    inp = draw_qkv(B, H, T, d, dtype, seed=2900 + d, heavy_frac=0.05)
+    g = draw_grad(B, H, T, d, seed=2900 + d)
+    if dtype == "f32":
+        g = (g.astype(np.uint32) << 16).view(np.float32)
+    taus = learned_tau(B, H, d, seed=2900 + d) if per_head else None
+    q, k, v = (to_device(x, dtype) for x in (inp.q, inp.k, inp.v))
+    dout = to_device(g, dtype)
+    code = ab.ATTN_BF16 if dtype == "bf16" else ab.ATTN_F32
+    f32 = dict(dtype=torch.float32, device="cuda")
+    lse, rs = torch.empty((B, H, T), **f32), torch.empty((B, H, T), **f32)
+    fws, _ = ab.fwd_workspace(B, H, T, ab.ATTN_DILUTION, code, q.device, d)
+    tb = torch.from_numpy(taus).cuda() if per_head else None
+    if per_head:
+        out = ab.prefill(q, k, v, T, tau=1.0, tau_bh=tb, mode=ab.ATTN_DILUTION, eps=1e-6,
+                         lse_out=lse, rowsum_out=rs, workspace=fws)
+    else:
+        out = ab.fwd(q, k, v, tau=TAU4, mode=ab.ATTN_DILUTION, eps=1e-6, workspace=fws,
+                     lse_out=lse, rowsum_out=rs)
+    torch.cuda.synchronize()
+    fws_before = fws.clone()
+    tau = 1.0 if per_head else TAU4
+    res = []
+    for reuse in (False, True):
+        dt = torch.full((B, H), float("nan"), **f32)
+        grads = ab.bwd(q, k, v, out, dout, lse, rs, tau=tau, mode=ab.ATTN_DILUTION, eps=1e-6,
+                       tau_bh=tb, dtau_out=dt, fwd_workspace=fws if reuse else None)
+        torch.cuda.synchronize()
+        res.append([x.float().cpu().numpy() for x in grads] + [dt.cpu().numpy()])
+    assert torch.equal(fws, fws_before)
+    bar = 1e-6 if dtype == "f32" else 1e-3
+    for name, a, b in zip(("dq", "dk", "dv", "dtau"), res[0], res[1]):
+        ma, rr = errors(b, a)
+        print(f"{dtype} d={d} reuse vs recompute {name}: max-abs {ma:.3e} rel-RMS {rr:.3e}")
+        assert rr <= bar, name
+    ov = (lambda x: x) if dtype == "f32" else oracle.Bf16
+    ref = oracle.attn_bwd(ov(inp.q), ov(inp.k), ov(inp.v), ov(g), tau, 1e-6, 1, tau_bh=taus,
+                          want_dtau=True)
+    if dtype == "f32":
+        check_grads_f32(res[1][:3], ref[:3], f"reuse f32 d={d}")
+        check_dtau_f32(res[1][3], ref[0], inp, g, taus if per_head else tau, ref[4],
+                       f"reuse f32 d={d}")
+    else:
+        check_grads(res[1][:3], ref[:3], f"reuse bf16 d={d}")
+        check_dtau(res[1][3], ref[0], inp, g, taus if per_head else np.full((B, H), tau), ref[4],
+                   f"reuse bf16 d={d}")

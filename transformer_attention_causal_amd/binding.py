@@ -59,7 +59,7 @@ def load() -> ctypes.CDLL:
                                  vp, sz, vp]
         lib.attn_bwd_ex.restype = i
         lib.attn_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, vp, i,
-                                    f, i, vp, vp, sz, vp]
+                                    f, i, vp, vp, sz, vp, sz, vp]
         lib.attn_bwd_workspace_bytes.restype = sz
         lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
         lib.attn_prefill.restype = i
@@ -111,10 +111,11 @@ def attn_bwd(q, k, v, out, dout, lse, rowsum, dq, dk, dv, B, H, T, d, tau, mode,
 
 
 def attn_bwd_ex(q, k, v, out, dout, lse, rowsum, dq, dk, dv, B, H, T, d, tau, tau_bh, mode, eps,
-                dtype, dtau_out, workspace, workspace_bytes, hip_stream) -> int:
+                dtype, dtau_out, fwd_workspace, fwd_workspace_bytes, workspace, workspace_bytes,
+                hip_stream) -> int:
     return load().attn_bwd_ex(q, k, v, out, dout, lse, rowsum, dq, dk, dv, B, H, T, d, tau,
-                              tau_bh, mode, eps, dtype, dtau_out, workspace, workspace_bytes,
-                              hip_stream)
+                              tau_bh, mode, eps, dtype, dtau_out, fwd_workspace,
+                              fwd_workspace_bytes, workspace, workspace_bytes, hip_stream)
 
 
 def attn_bwd_workspace_bytes(B, H, T, d, mode, dtype) -> int:
@@ -247,12 +248,13 @@ def bwd_workspace(B, H, T, mode, dtype_code, device, d=64):
 
 def bwd(q, k, v, out, dout, lse, rowsum=None, tau: float = 1.0, mode: int = ATTN_TEMPERED,
         eps: float = 1e-6, dq=None, dk=None, dv=None, workspace=None, tau_bh=None,
-        dtau_out=None):
+        dtau_out=None, fwd_workspace=None):
     """Run attn_bwd_ex on [B,H,T,d] tensors, d = 64 or 128 (``lse``/``rowsum`` from the
     forward's ``lse_out``/``rowsum_out``); ``tau_bh`` an optional [B,H] fp32
     tensor of per-head multipliers (as given to ``prefill``), ``dtau_out`` an
-    optional [B,H] fp32 tensor that receives dL/dtau per head.  Returns
-    (dq, dk, dv)."""
+    optional [B,H] fp32 tensor that receives dL/dtau per head, ``fwd_workspace``
+    optionally the dilution forward's workspace tensor (its committed-demand
+    table is then read instead of recomputed).  Returns (dq, dk, dv)."""
     import torch
 
     for t in (q, k, v, out, dout):
@@ -276,6 +278,9 @@ def bwd(q, k, v, out, dout, lse, rowsum=None, tau: float = 1.0, mode: int = ATTN
                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, T, d, float(tau),
                      tau_bh.data_ptr() if tau_bh is not None else None, int(mode), float(eps),
                      code, dtau_out.data_ptr() if dtau_out is not None else None,
+                     fwd_workspace.data_ptr() if fwd_workspace is not None else None,
+                     (fwd_workspace.numel() * fwd_workspace.element_size()
+                      if fwd_workspace is not None else 0),
                      workspace.data_ptr(), ws_bytes, _stream_handle(q.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd_ex")

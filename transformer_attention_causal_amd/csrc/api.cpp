@@ -78,7 +78,7 @@ bool prefill_workspace(int B, int H, int Tq, int Tk, int d, int dtype, FwdWorksp
   return true;
 }
 
-bool fwd_workspace(int B, int H, int T, int d, int dtype, FwdWorkspace *ws) {
+bool fwd_workspace_layout(int B, int H, int T, int d, int dtype, FwdWorkspace *ws) {
   return prefill_workspace(B, H, T, T, d, dtype, ws);
 }
 
@@ -127,7 +127,7 @@ size_t attn_fwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype)
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
   if (mode != ATTN_DILUTION) return 0;
   FwdWorkspace ws;
-  if (!fwd_workspace(B, H, T, d, dtype, &ws)) return 0;
+  if (!fwd_workspace_layout(B, H, T, d, dtype, &ws)) return 0;
   return ws.total;
 }
 
@@ -171,7 +171,7 @@ int check_fwd(const void *q, const void *k, const void *v, const void *out, int 
 
 int check_workspace(int B, int H, int T, int d, int dtype, void *workspace,
                     size_t workspace_bytes, FwdWorkspace *ws) {
-  if (!fwd_workspace(B, H, T, d, dtype, ws)) return ATTN_EINVAL;
+  if (!fwd_workspace_layout(B, H, T, d, dtype, ws)) return ATTN_EINVAL;
   if (!workspace || workspace_bytes < ws->total || !aligned16(workspace)) return ATTN_EWORKSPACE;
   return ATTN_OK;
 }
@@ -445,7 +445,8 @@ size_t attn_bwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype)
 int attn_bwd_ex(const void *q, const void *k, const void *v, const void *out, const void *dout,
                 const float *lse, const float *rowsum, void *dq, void *dk, void *dv, int B, int H,
                 int T, int d, float tau, const float *tau_bh, int mode, float eps, int dtype,
-                float *dtau_out, void *workspace, size_t workspace_bytes, void *hip_stream) {
+                float *dtau_out, const void *fwd_workspace, size_t fwd_workspace_bytes,
+                void *workspace, size_t workspace_bytes, void *hip_stream) {
   if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv) return ATTN_EINVAL;
   if (mode != ATTN_TEMPERED && mode != ATTN_DILUTION) return ATTN_EINVAL;
   if (mode == ATTN_DILUTION && !rowsum) return ATTN_EINVAL;
@@ -487,6 +488,21 @@ int attn_bwd_ex(const void *q, const void *k, const void *v, const void *out, co
   BwdWorkspace ws;
   if (!bwd_workspace(B, H, T, d, mode, dtype, &ws)) return ATTN_EINVAL;
   if (!workspace || workspace_bytes < ws.total || !aligned16(workspace)) return ATTN_EWORKSPACE;
+  // the dilution forward's workspace (read only): its committed-demand table
+  // replaces the backward's own; ignored for ATTN_TEMPERED
+  const char *fwd_cin = nullptr;
+  if (fwd_workspace && mode == ATTN_DILUTION) {
+    FwdWorkspace fw;
+    if (!fwd_workspace_layout(B, H, T, d, dtype, &fw)) return ATTN_EINVAL;
+    if (fwd_workspace_bytes < fw.total || !aligned16(fwd_workspace)) return ATTN_EWORKSPACE;
+    const size_t fbytes = fw.total;
+    for (const void *g : grads)
+      if (overlaps(g, nbytes, fwd_workspace, fbytes)) return ATTN_EINVAL;
+    if (overlaps(workspace, ws.total, fwd_workspace, fbytes) ||
+        overlaps(dtau_out, tbytes, fwd_workspace, fbytes))
+      return ATTN_EINVAL;
+    fwd_cin = static_cast<const char *>(fwd_workspace) + fw.lse_bytes;
+  }
   const int dev_status = check_device();
   if (dev_status != ATTN_OK) return dev_status;
 
@@ -510,7 +526,10 @@ int attn_bwd_ex(const void *q, const void *k, const void *v, const void *out, co
   a.tslices = ws.tslices;
   char *wtail = wsp + (kBwdFixedRowArrays + ws.tslices) * ws.row_bytes;
   if (mode == ATTN_DILUTION) {
-    a.cin = reinterpret_cast<float *>(wtail);
+    // the kernels only read the table when the forward's is given
+    a.cin = fwd_cin ? reinterpret_cast<float *>(const_cast<char *>(fwd_cin))
+                    : reinterpret_cast<float *>(wtail);
+    a.cin_given = fwd_cin ? 1 : 0;
     a.gin = reinterpret_cast<float *>(wtail + ws.cin_bytes);
     a.pk = wtail + ws.cin_bytes + ws.gin_bytes;
   }
@@ -537,7 +556,7 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *out, const
              int T, int d, float tau, int mode, float eps, int dtype, void *workspace,
              size_t workspace_bytes, void *hip_stream) {
   return attn_bwd_ex(q, k, v, out, dout, lse, rowsum, dq, dk, dv, B, H, T, d, tau, nullptr, mode,
-                     eps, dtype, nullptr, workspace, workspace_bytes, hip_stream);
+                     eps, dtype, nullptr, nullptr, 0, workspace, workspace_bytes, hip_stream);
 }
 
 size_t attn_decode_workspace_bytes(int S, int H, int Lcap, int d) {

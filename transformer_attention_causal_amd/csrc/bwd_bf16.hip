@@ -925,7 +925,8 @@ hipError_t launch_bwd_d(int mode, const BwdArgs &a, hipStream_t s) {
     f.tau_bh = a.tau_bh;
     f.c2 = a.c2;
     f.eps = a.eps;
-    e = launch_colsum_bf16(f, s);
+    // the forward's table, when the caller passes it, holds the same values
+    if (!a.cin_given) e = launch_colsum_bf16(f, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_gsum_kernel<D, CLAMP>), dim3((unsigned)(nkb * a.BH)), dim3(256), 0, s,
                        a, nqs);

@@ -391,7 +391,8 @@ static hipError_t launch_bwd_f32_c(int mode, const BwdArgs &a, hipStream_t s) {
     f.tau_bh = a.tau_bh;
     f.c2 = a.c2;
     f.eps = a.eps;
-    e = launch_colsum_f32(f, s);
+    // the forward's table, when the caller passes it, holds the same values
+    if (!a.cin_given) e = launch_colsum_f32(f, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_gsum_f32_kernel<CLAMP, D>), grid, block, 0, s, a, ntiles);
     e = hipGetLastError();
