@@ -86,7 +86,9 @@ class Decode:
     note: str = ""
 
 
-# The workloads the pages' hot path is measured on (see the design doc for sources).
+# The named workloads: the shapes the pages train and evaluate at (16K context,
+# 128K evaluation, 64-dim heads; the focal models' 20 heads of 128), the
+# oracle-sized fp32 case, and the 32K-key decode cache.
 PREFILL = {
     "fp32_t256": Prefill("fp32_t256", 1, 2, 256, 64, "f32", seed=20261,
                          note="fp32, tau=1 and YaRN s=4, dilution eps=1e-6"),
