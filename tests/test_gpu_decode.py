@@ -196,3 +196,29 @@ def test_decode_per_head_tau_d64(L):
         Dg = Dd.cpu().numpy().astype(np.float64)
         assert np.max(np.abs(Dg.sum(-1) / Dr.sum(-1) - 1.0)) <= DEMAND_TOTAL_REL
         assert np.max(np.abs(Dg - Dr)) <= 1e-4 * max(1.0, float(Dr.max()))
+
+
+@pytest.mark.parametrize("Lcap", [5000, 40000])
+def test_decode_kv_len_out_of_range_is_clamped(Lcap):
+    """kv_len values outside [1, Lcap] are clamped on the device: 0 and a
+    negative length act as 1 and a length past the cache as Lcap, on the
+    fused path (Lcap <= 32768) and the chunked one.  Outputs and demand equal
+    those of the clamped lengths bit for bit."""
+    import torch
+
+    S, H = 3, 2
+    kc, vc = decode_cache_host(S, H, Lcap, 64, seed=5300 + Lcap)
+    D0 = decode_initial_demand(S, H, Lcap, seed=5300 + Lcap)
+    q = to_device(decode_queries(1, S, H, 64, seed=5300 + Lcap)[0], "bf16")
+    kc_d, vc_d = to_device(kc, "bf16"), to_device(vc, "bf16")
+    outs, dems = [], []
+    for lens in ([0, -7, Lcap + 100], [1, 1, Lcap]):
+        D = torch.from_numpy(D0.copy()).cuda()
+        kv_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        outs.append(ab.decode(q, kc_d, vc_d, D, tau=1.0, eps=1e-6, kv_len=kv_len))
+        dems.append(D)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(dems[0], dems[1])
+    # a one-key decode attends to key 0 alone: the output is v_0
+    v0 = to_device(vc[:2, :, 0], "bf16")
+    assert torch.equal(outs[0][:2], v0)
