@@ -547,15 +547,20 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_heads)
+        result["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_heads, tau_t, dw)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(inp, w, nheads):
-    """The fp64 oracle (untuned) on a bounded sample of the same workload."""
+def cpu_baseline(inp, w, nheads, tau_t, dw):
+    """The fp64 oracle (untuned) on a bounded sample of the same workloads:
+    the dilution forward (the headline figure), and beside it the tempered
+    forward on the same heads and one decode step over a few sequences."""
     import numpy as np
 
     import oracle
+    from transformer_attention_causal_amd.workloads import (decode_cache_host,
+                                                            decode_initial_demand,
+                                                            decode_queries)
 
     heads = list(range(min(nheads, w.H)))
     log(f"bench: cpu baseline (oracle) on {len(heads)} head(s) of T={w.T} dilution")
@@ -564,6 +569,20 @@ def cpu_baseline(inp, w, nheads):
     oracle.dilution_fwd(*sub, 1.0, w.eps)
     dt = time.perf_counter() - t0
     flops = 4.0 * w.d * causal_pairs(1, len(heads), w.T)
+    t0 = time.perf_counter()
+    oracle.tempered_fwd(*sub, tau_t)
+    dt_t = time.perf_counter() - t0
+    # one decode step: the first sequences of a cache drawn by the same recipe
+    ns = 4
+    kc, vc = decode_cache_host(ns, dw.H, dw.L, dw.d, dw.seed)
+    dem = decode_initial_demand(ns, dw.H, dw.L, dw.seed).astype(np.float64)
+    qd = decode_queries(1, ns, dw.H, dw.d, dw.seed)[0]
+    t0 = time.perf_counter()
+    oracle.dilution_decode_step(oracle.Bf16(qd), oracle.Bf16(kc), oracle.Bf16(vc), dem, dw.tau,
+                                dw.eps)
+    dt_d = time.perf_counter() - t0
+    dec_bytes = ns * dw.H * (2.0 * dw.L * dw.d * 2 + 2.0 * dw.L * 4 + 2.0 * dw.d * 2)
+    log(f"bench: cpu baseline {dt:.2f} s dilution, {dt_t:.2f} s tempered, {dt_d:.3f} s decode")
     return {
         "value": round(flops / dt / 1e12, 6),
         "unit": "TFLOP/s",
@@ -571,6 +590,14 @@ def cpu_baseline(inp, w, nheads):
         "kind": "oracle",
         "sample": f"dilution forward, {len(heads)} of {w.H} heads at T={w.T} (all rows), "
                   f"{dt:.2f} s, fp64",
+        "also": {
+            "tempered_fwd": {"value": round(flops / dt_t / 1e12, 6), "unit": "TFLOP/s",
+                             "sample": f"the same {len(heads)} heads, tau={tau_t:.7f}, "
+                                       f"{dt_t:.2f} s"},
+            "decode_step": {"value": round(dec_bytes / dt_d / 1e9, 3), "unit": "GB/s",
+                            "sample": f"one step, {ns} of {dw.S} sequences x {dw.H} heads x "
+                                      f"{dw.L} keys, {dt_d:.3f} s"},
+        },
     }
 
 
