@@ -10,6 +10,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 #include <cstring>
 #include <mutex>
 
@@ -639,8 +640,8 @@ const char *attn_strerror(int status) {
     case ATTN_OK: return "ok";
     case ATTN_EINVAL: return "invalid argument";
     case ATTN_ENOTSUP:
-      return "unsupported (head dim 64, or 128 with bf16 storage; backward: 64 and bf16; decode: bf16; "
-             "device must be gfx950)";
+      return "unsupported (head dim must be 64 or 128; decode needs bf16 storage; device must be "
+             "gfx950)";
     case ATTN_EWORKSPACE: return "workspace missing, misaligned or too small";
     case ATTN_EHIP: return g_hip_error;
     default: return "unknown status";
