@@ -34,6 +34,53 @@ def test_header_declarations_are_exported():
     assert set(names) <= exported
 
 
+def declared_signatures(header=HEADER):
+    """{name: (return type, [parameter types])} of every prototype in the header."""
+    src = open(header).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    sigs = {}
+    for ret, name, params in re.findall(
+            r"([A-Za-z_][\w\s\*]*?)\b(attn_[a-z0-9_]+)\s*\(([^;{]*?)\)\s*;", src):
+        ps = [x.strip() for x in params.split(",") if x.strip() and x.strip() != "void"]
+        # drop the parameter name: what is left is its type
+        types = [re.sub(r"\b\w+$", "", x).strip() if not x.endswith("*") else x for x in ps]
+        sigs[name] = (ret.strip(), types)
+    return sigs
+
+
+def _ctype_of(decl):
+    import ctypes
+
+    if "*" in decl:
+        return ctypes.c_char_p if decl.replace(" ", "") == "constchar*" else ctypes.c_void_p
+    words = decl.replace("const", "").split()
+    kind = words[-1] if words else ""
+    return {"int": ctypes.c_int, "int32_t": ctypes.c_int, "float": ctypes.c_float,
+            "double": ctypes.c_double, "size_t": ctypes.c_size_t}[kind]
+
+
+def test_binding_argtypes_match_the_header():
+    """Every prototype's parameter count and types (pointer, int, float,
+    double, size_t) agree with the ctypes binding, so a changed signature
+    cannot be called with a stale argument list."""
+    import ctypes
+
+    lib = ab.load()
+    sigs = declared_signatures()
+    assert set(sigs) == set(ab.EXPORTED)
+    for name, (ret, params) in sigs.items():
+        fn = getattr(lib, name)
+        want = [_ctype_of(t) for t in params]
+        got = list(fn.argtypes or [])
+        assert len(got) == len(want), (name, len(got), len(want))
+        for i, (g, w) in enumerate(zip(got, want)):
+            if w is ctypes.c_char_p:
+                w = ctypes.c_void_p
+            assert g is w or (g is ctypes.c_char_p and w is ctypes.c_void_p), (name, i, g, w)
+        assert fn.restype is _ctype_of(ret) or (ret.endswith("*") and fn.restype in
+                                                (ctypes.c_char_p, ctypes.c_void_p)), name
+
+
 def test_peaks_library_exports_its_header():
     """The benchmark's measured-ceiling kernels: libattn_peaks.so exports what
     include/attn_peaks.h declares, and rejects bad arguments on the host."""
