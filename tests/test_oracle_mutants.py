@@ -66,6 +66,8 @@ MUTANTS = [
      "dkj[e] += c * s * K[(size_t)i * d + e];"),
     ("bwd_dv_from_bids", "dvj[e] += a * dO[(size_t)i * d + e];",
      "dvj[e] += P[(size_t)i * T + j] * dO[(size_t)i * d + e];"),
+    ("bwd_per_head_tau_ignored", "(tau_bh ? tau_bh[bh] : tau) / sqrt((double)d)",
+     "tau / sqrt((double)d)"),
 ]
 
 RUNNER = r"""
