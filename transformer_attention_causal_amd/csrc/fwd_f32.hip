@@ -17,21 +17,24 @@
 
 namespace attn {
 
-constexpr int kFR = 64;  // rows per workgroup / tile
+constexpr int kFR = 64;           // rows per wave, and keys (or rows) per LDS tile
+constexpr int kFW = 4;            // waves per workgroup: they share each LDS tile
+constexpr int kFB = kFR * kFW;    // rows (row kernels) or keys (column sums) per workgroup
 constexpr float kNoRowF32 = 1e30f;  // log-sum-exp of a position that holds no row
 
 template <int MODE, int D>
-__global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
+__global__ void __launch_bounds__(kFB) rows_f32_kernel(FwdArgs a, int nqb) {
   __shared__ __attribute__((aligned(16))) float sK[kFR * D];
   __shared__ __attribute__((aligned(16))) float sV[MODE == kRowLse ? 4 : kFR * D];
   // Rows are positions: query row r of Q is position P + r (P = 0 for a
   // whole prefill); blocks start at position vrow0 <= P, and lanes at
   // positions before P hold no row.
-  const int t = threadIdx.x;
+  const int tid = threadIdx.x, t = tid & 63, w = tid >> 6;
   const int bh = blockIdx.x % a.BH;
-  const int qb = a.vrow0 / kFR + nqb - 1 - blockIdx.x / a.BH;
+  // heaviest blocks first; block b covers positions vrow0 + kFB b ..
+  const int qb = nqb - 1 - blockIdx.x / a.BH;
   const int T = a.T, Tq = a.Tq, P = T - Tq;
-  const int q0 = qb * kFR;
+  const int q0 = a.vrow0 + qb * kFB + kFR * w;   // this wave's first position
   const int i = q0 + t;  // this lane's position
   const int li = i - P;  // and its query row
   const bool live = (unsigned)li < (unsigned)Tq;
@@ -55,17 +58,20 @@ __global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
     cin_blk = a.cin + (size_t)bh * cin_floats_per_head(T, a.vrow0) + cin_block_offset(qs, a.vrow0);
   }
   const float eps_floor = fmaxf(a.eps, FLT_MIN);
-  const int kend = min(q0 + kFR, T);
+  // this wave's keys: none when all its positions lie past T or before P
+  // (it still takes part in every barrier)
+  const int kend = (q0 < T && q0 + kFR > P) ? min(q0 + kFR, T) : 0;
+  const int kend_wg = min(a.vrow0 + qb * kFB + kFB, T);          // the workgroup's
 
-  for (int j0 = 0; j0 < kend; j0 += kFR) {
+  for (int j0 = 0; j0 < kend_wg; j0 += kFR) {
     __syncthreads();
-    for (int u = t; u < kFR * D; u += 64) {
+    for (int u = tid; u < kFR * D; u += kFB) {
       const int row = j0 + u / D;
       sK[u] = row < T ? K[(size_t)j0 * D + u] : 0.0f;
       if constexpr (MODE != kRowLse) sV[u] = row < T ? V[(size_t)j0 * D + u] : 0.0f;
     }
     __syncthreads();
-    const int jn = min(kFR, kend - j0);
+    const int jn = min(kFR, kend - j0);   // <= 0 once the wave's keys are done
     for (int jj = 0; jj < jn; ++jj) {
       const int j = j0 + jj;
       float s = 0.0f;
@@ -94,7 +100,9 @@ __global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
           const float o = __shfl_up(incl, off, 32);
           if ((t & 31) >= off) incl += o;
         }
-        float base = (j < 32 * (qs + 1)) ? cin_blk[j] : 0.0f;
+        // lanes with no row (past T, or before P) read nothing: past T their
+        // block can lie beyond the table, and their bids are 0 anyway
+        float base = (live && j < 32 * (qs + 1)) ? cin_blk[j] : 0.0f;
         base = fmaxf(base + a.eps, eps_floor);
         const float share = p / (base + incl);
         l += share;
@@ -121,17 +129,17 @@ __global__ void __launch_bounds__(64) rows_f32_kernel(FwdArgs a, int nqb) {
 }
 
 template <int D>
-__global__ void __launch_bounds__(64) colsum_f32_kernel(FwdArgs a, int nkb) {
+__global__ void __launch_bounds__(kFB) colsum_f32_kernel(FwdArgs a, int nkb) {
   __shared__ __attribute__((aligned(16))) float sQ[kFR * D];
   __shared__ float sL[kFR];
   // Positions i of the walk are query row i - P (P = 0 for a whole prefill);
   // positions before P, from vrow0 on, are no row and bid nothing.
-  const int t = threadIdx.x;
+  const int tid = threadIdx.x;
   const int bh = blockIdx.x % a.BH;
   const int kb = blockIdx.x / a.BH;
   const int T = a.T, Tq = a.Tq, P = T - Tq;
-  const int k0 = kb * kFR;
-  const int j = k0 + t;  // this lane's key column
+  const int k0 = kb * kFB;
+  const int j = k0 + tid;  // this lane's key column
   const float *Q = reinterpret_cast<const float *>(a.q) + (size_t)bh * Tq * D;
   const float *K = reinterpret_cast<const float *>(a.k) + (size_t)bh * a.kstride * D;
   const float c2 = head_c2(a, bh);
@@ -148,12 +156,14 @@ __global__ void __launch_bounds__(64) colsum_f32_kernel(FwdArgs a, int nkb) {
   float lost = 0.0f;
   for (int i0 = max(k0, a.vrow0); i0 < T; i0 += kFR) {
     __syncthreads();
-    for (int u = t; u < kFR * D; u += 64) {
+    for (int u = tid; u < kFR * D; u += kFB) {
       const int lr = i0 + u / D - P;
       sQ[u] = (unsigned)lr < (unsigned)Tq ? Q[(size_t)lr * D + u % D] : 0.0f;
     }
-    const int lt = i0 + t - P;
-    sL[t] = (unsigned)lt < (unsigned)Tq ? a.lse2[(size_t)bh * Tq + lt] : kNoRowF32;
+    if (tid < kFR) {
+      const int lt = i0 + tid - P;
+      sL[tid] = (unsigned)lt < (unsigned)Tq ? a.lse2[(size_t)bh * Tq + lt] : kNoRowF32;
+    }
     __syncthreads();
     const int in = min(kFR, T - i0);
     for (int ii = 0; ii < in; ++ii) {
@@ -176,8 +186,8 @@ __global__ void __launch_bounds__(64) colsum_f32_kernel(FwdArgs a, int nkb) {
 
 template <int D>
 static hipError_t launch_rows_f32_d(int mode, const FwdArgs &a, hipStream_t s) {
-  const int nqb = (a.T + kFR - 1) / kFR - a.vrow0 / kFR;   // blocks from position vrow0
-  dim3 grid((unsigned)(nqb * a.BH)), block(64);
+  const int nqb = (a.T - a.vrow0 + kFB - 1) / kFB;   // blocks from position vrow0
+  dim3 grid((unsigned)(nqb * a.BH)), block(kFB);
   switch (mode) {
     case kRowTempered:
       hipLaunchKernelGGL((rows_f32_kernel<kRowTempered, D>), grid, block, 0, s, a, nqb);
@@ -197,8 +207,8 @@ hipError_t launch_rows_f32(int mode, const FwdArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_colsum_f32(const FwdArgs &a, hipStream_t s) {
-  const int nkb = (a.T + kFR - 1) / kFR;
-  const dim3 grid((unsigned)(nkb * a.BH)), block(64);
+  const int nkb = (a.T + kFB - 1) / kFB;
+  const dim3 grid((unsigned)(nkb * a.BH)), block(kFB);
   switch (a.D) {
     case 64: hipLaunchKernelGGL(colsum_f32_kernel<64>, grid, block, 0, s, a, nkb); break;
     case 128: hipLaunchKernelGGL(colsum_f32_kernel<128>, grid, block, 0, s, a, nkb); break;
