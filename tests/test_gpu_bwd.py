@@ -570,3 +570,35 @@ def test_bwd_reads_the_forwards_committed_table(dtype, d, per_head):
         check_grads(res[1][:3], ref[:3], f"reuse bf16 d={d}")
         check_dtau(res[1][3], ref[0], inp, g, taus if per_head else np.full((B, H), tau), ref[4],
                    f"reuse bf16 d={d}")
+
+
+@pytest.mark.timeout(600)
+def test_bwd_t16k_reading_the_forwards_table():
+    """At the full T = 16384 workload (4 of its 16 heads): the dilution
+    backward given the forward's workspace matches the recomputing call to
+    rounding, and keeps the sum invariants."""
+    import torch
+
+    w = PREFILL["dilution_t16k"]
+    B, H, T = 1, 4, w.T
+    inp = prefill_inputs(w, H=H)
+    g = draw_grad(B, H, T, 64, seed=w.seed)
+    q, k, v = (to_device(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    dout = to_device(g, "bf16")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    lse, rs = torch.empty((B, H, T), **f32), torch.empty((B, H, T), **f32)
+    fws, _ = ab.fwd_workspace(B, H, T, ab.ATTN_DILUTION, ab.ATTN_BF16, q.device)
+    out = ab.fwd(q, k, v, tau=1.0, mode=ab.ATTN_DILUTION, eps=w.eps, workspace=fws, lse_out=lse,
+                 rowsum_out=rs)
+    res = []
+    for reuse in (False, True):
+        grads = ab.bwd(q, k, v, out, dout, lse, rs, tau=1.0, mode=ab.ATTN_DILUTION, eps=w.eps,
+                       fwd_workspace=fws if reuse else None)
+        torch.cuda.synchronize()
+        res.append([x.float().cpu().numpy() for x in grads])
+        torch.cuda.empty_cache()
+    for name, a, b in zip(("dq", "dk", "dv"), res[0], res[1]):
+        ma, rr = errors(b, a)
+        print(f"t16k reuse vs recompute {name}: max-abs {ma:.3e} rel-RMS {rr:.3e}")
+        assert rr <= 1e-3, name
+    check_sum_invariants(res[1], g, 1, "t16k reading the forward's table")
