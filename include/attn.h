@@ -71,8 +71,11 @@ size_t attn_fwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype)
 /* Causal attention forward pass (both modes; see top of file).
  *   q, k, v    [B,H,T,d] device arrays of `dtype` (inputs, not modified)
  *   out        [B,H,T,d] device array of `dtype` (output; may not alias q/k/v)
- *   B, H, T    batch, heads, sequence length (each >= 1; T < 16777216, the
- *              kernels address one head's rows with byte offsets below 2^31)
+ *   B, H, T    batch, heads, sequence length (each >= 1; T < 16777216 and
+ *              T * d * element size < 2^31: the kernels address one head's
+ *              rows with 32-bit byte offsets -- for bf16 T < 2^24 at d = 64
+ *              and T < 2^23 at d = 128, for fp32 half of that; else
+ *              ATTN_EINVAL)
  *   d          head dimension: 64 or 128 (else ATTN_ENOTSUP)
  *   tau        logit multiplier, finite and >= 0 (tau = 0 gives uniform bids)
  *   mode       ATTN_TEMPERED or ATTN_DILUTION
@@ -217,7 +220,8 @@ size_t attn_prefill_workspace_bytes(int B, int H, int Tq, int Tk, int d, int mod
  *              has written the chunk's own keys/values at P..Tk-1); rows
  *              Tk..Lcap-1 are not read
  *   out        [B,H,Tq,d] of `dtype` (may not alias q or the caches)
- *   B, H       >= 1;  1 <= Tq <= Tk <= Lcap < 16777216
+ *   B, H       >= 1;  1 <= Tq <= Tk <= Lcap < 16777216, and Lcap * d *
+ *              element size < 2^31 (as T for attn_fwd)
  *   d, tau, mode, eps, dtype  as for attn_fwd
  *   tau_bh     [B,H] fp32 device array or NULL: when given, head (b,h) uses
  *              the multiplier tau_bh[b*H+h] in place of tau -- the per-
@@ -243,6 +247,39 @@ int attn_prefill(const void *q, const void *kcache, const void *vcache, void *ou
                  int Tq, int Tk, int Lcap, int d, float tau, const float *tau_bh, int mode,
                  float eps, int dtype, const float *demand_in, float *demand_out, float *lse_out,
                  float *rowsum_out, void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Bytes of device workspace attn_prefill_rope needs: the rotated query rows
+ * [B,H,Tq,d] and rotated keys [B,H,Lcap,d] in `dtype`, then (ATTN_DILUTION)
+ * attn_prefill_workspace_bytes(B,H,Tq,Tk,d,mode,dtype).  0 for an invalid
+ * shape, mode, head dimension or dtype. */
+size_t attn_prefill_rope_workspace_bytes(int B, int H, int Tq, int Tk, int Lcap, int d, int mode,
+                                         int dtype);
+
+/* attn_prefill with rotary position embedding applied to Q and K first
+ * ("YaRN > Attention Temperature Scaling", code cell In[16]: each token's
+ * query and key are rotated at its position with the per-pair frequencies
+ * times YaRN's gamma, then the scores are taken and multiplied by sqrt(t) --
+ * here the multiplier tau or tau_bh).  Arguments as attn_prefill, with the
+ * cache holding the keys BEFORE rotation, and:
+ *   rope_freq  [d/2] fp32 device array: the frequency of dimension pair
+ *              (2m, 2m+1), YaRN's per-pair gamma already applied by the
+ *              caller (the page leaves gamma's helpers undefined); not
+ *              checked on the host (NULL: ATTN_EINVAL)
+ *   pos0       position of key 0 (>= 0, pos0 + Tk < 2^31): key j sits at
+ *              pos0 + j and the chunk's query row r at pos0 + Tk - Tq + r
+ * Row x at position n has pair m turned counter-clockwise by the angle
+ * n * rope_freq[m]: (a, b) -> (a cos - b sin, a sin + b cos).  The angle is
+ * reduced in double precision; the rotated rows are rounded once to `dtype`
+ * in the workspace, and the attention kernels read them from there.
+ * Scores then depend on the distance between positions only, so pos0 moves
+ * nothing but rounding.  workspace: >= attn_prefill_rope_workspace_bytes(...)
+ * bytes (needed in both modes), not overlapping any argument. */
+int attn_prefill_rope(const void *q, const void *kcache, const void *vcache, void *out, int B,
+                      int H, int Tq, int Tk, int Lcap, int d, float tau, const float *tau_bh,
+                      int mode, float eps, int dtype, const float *rope_freq, int pos0,
+                      const float *demand_in, float *demand_out, float *lse_out,
+                      float *rowsum_out, void *workspace, size_t workspace_bytes,
+                      void *hip_stream);
 
 /* Bytes of device workspace attn_decode needs (per-(sequence,head,split)
  * partial maxima, sums and weighted values plus one fp32 score per cached

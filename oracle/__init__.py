@@ -21,6 +21,8 @@ module only builds/loads that library and marshals numpy arrays.  Functions:
 * ``attn_bwd`` -- exact gradients (dq, dk, dv) of either operator by the
   chain rule through its definition (the dilution page ships training kernels
   with exact gradients), plus the dilution row sums of the shares.
+* ``rope`` -- the rotary position embedding YaRN's code cell applies to Q and
+  K before the scores, with caller-supplied per-pair frequencies.
 * ``yarn_t`` / ``yarn_tau`` -- t = 0.1 ln s + 1 and sqrt(t) (YaRN page).
 
 Inputs may be numpy float64/float32 arrays or ``Bf16`` wrappers around raw
@@ -56,10 +58,30 @@ class Bf16:
         return (self.bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def build(src: str = _SRC, out: str = _LIB) -> str:
-    """Compile oracle.c into liboracle.so (gcc, OpenMP, IEEE arithmetic)."""
+_LIB_SAN = os.path.join(_HERE, "liboracle_san.so")
+
+# Host sanitizers for the oracle (ORACLE_SANITIZE=1): AddressSanitizer and
+# UndefinedBehaviorSanitizer, any report fatal.  The process must have the
+# ASan runtime loaded first (oracle/sanitize.sh does that).
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                  "-fno-omit-frame-pointer", "-g"]
+
+
+def _sanitized() -> bool:
+    return os.environ.get("ORACLE_SANITIZE", "") == "1"
+
+
+def build(src: str = _SRC, out: str | None = None, sanitize: bool | None = None) -> str:
+    """Compile oracle.c into liboracle.so (gcc, OpenMP, IEEE arithmetic); with
+    ``sanitize`` (default: the ORACLE_SANITIZE environment variable) into an
+    ASan + UBSan build, liboracle_san.so by default."""
+    if sanitize is None:
+        sanitize = _sanitized()
+    if out is None:
+        out = _LIB_SAN if sanitize else _LIB
     cmd = ["gcc", "-O3", "-mavx2", "-mfma", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-           "-Wall", "-Wno-unknown-pragmas", src, "-o", out + ".tmp", "-lm"]
+           "-Wall", "-Wno-unknown-pragmas", *(SANITIZE_FLAGS if sanitize else []), src,
+           "-o", out + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)
     return out
@@ -84,9 +106,10 @@ def use_library(lib) -> None:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        path = _LIB_SAN if _sanitized() else _LIB
+        if not os.path.exists(path):
             build()
-        _lib = load_library(_LIB)
+        _lib = load_library(path)
     return _lib
 
 
@@ -113,6 +136,8 @@ def _declare(lib):
                                                     d, d, ip, i]
         lib.oracle_prefill.restype = i
         lib.oracle_prefill.argtypes = [vp, vp, vp, i, dp, dp, dp, i, i, i, i, i, i, d, d, i]
+        lib.oracle_rope.restype = i
+        lib.oracle_rope.argtypes = [vp, i, dp, i, i, i, i, dp, ctypes.c_long, i]
         lib.oracle_attn_bwd.restype = i
         lib.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, i, dp, dp, dp, dp, dp, i, i, i, i, d, dp,
                                         d, i]
@@ -235,6 +260,28 @@ def dilution_decode_step(q, kcache, vcache, demand: np.ndarray, tau: float = 1.0
         float(tau), float(eps), _ptr(pa, ctypes.c_int) if pa is not None else None, npairs)
     if rc != 0:
         raise RuntimeError(f"oracle_dilution_decode_step failed ({rc})")
+    return out
+
+
+def rope(x, freq, pos0: int = 0, round_to_bf16: bool = False) -> np.ndarray:
+    """Rotary position embedding of x [B,H,T,d]: row t of every head is at
+    position pos0 + t, and dimension pair (2m, 2m+1) turns by that position
+    times freq[m] (freq: [d/2], the per-pair frequencies with YaRN's gamma
+    applied; widened exactly from its float32 values when given as float32).
+    Returns the rotated rows in fp64; with ``round_to_bf16`` each value is
+    rounded to the nearest bf16 (ties to even), as a method that stores the
+    rotated rows in bf16 would hold them."""
+    lib = _load()
+    xa, code = _as_input(x)
+    B, H, T, d = xa.shape
+    f = np.ascontiguousarray(np.asarray(freq), dtype=np.float64)
+    if f.shape != (d // 2,):
+        raise ValueError("freq must hold d/2 values")
+    out = np.empty((B, H, T, d))
+    rc = lib.oracle_rope(xa.ctypes.data, code, _ptr(out), B, H, T, d, _ptr(f), int(pos0),
+                         1 if round_to_bf16 else 0)
+    if rc != 0:
+        raise RuntimeError(f"oracle_rope failed ({rc})")
     return out
 
 

@@ -347,8 +347,13 @@ int oracle_prefill(const void *q, const void *kc, const void *vc, int dtype, dou
   if (B <= 0 || H <= 0 || Tq <= 0 || Tk < Tq || Lcap < Tk || d <= 0 || d > 512) return -1;
   const double c = tau / sqrt((double)d);
   const int P = Tk - Tq;
+  /* Heads are independent: with enough of them each thread takes whole heads;
+     otherwise heads run one after another and each row's sums are split
+     across the threads (the same arithmetic, partial sums added in a fixed
+     order), as in oracle_dilution_fwd. */
+  const int inner = B * H < nthreads();
   int failed = 0;
-#pragma omp parallel for schedule(dynamic, 1)
+#pragma omp parallel for schedule(dynamic, 1) if (!inner)
   for (int bh = 0; bh < B * H; ++bh) {
     const size_t qbase = (size_t)bh * Tq * d, kbase = (size_t)bh * Lcap * d;
     double *Qh = malloc(sizeof(double) * (size_t)Tq * d);
@@ -366,11 +371,11 @@ int oracle_prefill(const void *q, const void *kc, const void *vc, int dtype, dou
       double *lse_h = lse ? lse + (size_t)bh * Tq : NULL;
       if (mode == 1) {
         if (demand) memcpy(D, demand + (size_t)bh * Lcap, sizeof(double) * (size_t)Tk);
-        dilution_head(Qh, Kh, Vh, P, Tk, d, c, eps, NULL, out + qbase, lse_h, D, p, 0);
+        dilution_head(Qh, Kh, Vh, P, Tk, d, c, eps, NULL, out + qbase, lse_h, D, p, inner);
         if (demand) memcpy(demand + (size_t)bh * Lcap, D, sizeof(double) * (size_t)Tk);
       } else {
         for (int i = P; i < Tk; ++i) {
-          const double l = causal_bids(Qh + (size_t)(i - P) * d, Kh, i, d, c, p, 0);
+          const double l = causal_bids(Qh + (size_t)(i - P) * d, Kh, i, d, c, p, inner);
           double *o = out + qbase + (size_t)(i - P) * d;
           for (int e = 0; e < d; ++e) o[e] = 0.0;
           for (int j = 0; j <= i; ++j)
@@ -608,6 +613,57 @@ int oracle_attn_bwd(const void *q, const void *k, const void *v, const void *dou
       failed = 1;
     }
   return failed ? -2 : 0;
+}
+
+/*
+ * Rotary position embedding, applied to Q and K before the scores ([YARN]
+ * code cell In[16]: apply_yarn_rope rotates each token's query and key at its
+ * position with the per-pair frequencies times YaRN's gamma, then the scores
+ * are Q_rot K_rot^T / sqrt(d) times sqrt(t)).  The page leaves apply_rope,
+ * the pair layout and gamma undefined; read here as: the caller passes the
+ * frequencies with gamma already applied, dimension pair m is (2m, 2m+1), and
+ * the pair turns counter-clockwise by the angle
+ *   theta = (pos0 + t) * freq[m]
+ * for row t:  (x, y) -> (x cos theta - y sin theta, x sin theta + y cos theta).
+ * x: [B,H,T,d] in dtype; out: [B,H,T,d] fp64; freq: [d/2] fp64; d even.
+ */
+/*
+ * x rounded to the nearest bfloat16 value (8 significant bits, the exponent
+ * range of binary32), ties to the even significand.  Used where a method
+ * stores an intermediate row in bf16.  Finite inputs within binary32's normal
+ * range only (the rows rotated here); others are returned unchanged.
+ */
+static double round_bf16(double x) {
+  if (x == 0.0 || !isfinite(x)) return x;
+  int e;
+  const double m = frexp(x, &e);          /* x = m 2^e, 0.5 <= |m| < 1 */
+  if (e < -125 || e > 128) return x;
+  const double scaled = ldexp(m, 8);      /* 8 significant bits left of the point */
+  double r = floor(scaled);
+  const double frac = scaled - r;
+  if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+  return ldexp(r, e - 8);
+}
+
+int oracle_rope(const void *x, int dtype, double *out, int B, int H, int T, int d,
+                const double *freq, long pos0, int round_to_bf16) {
+  if (B <= 0 || H <= 0 || T <= 0 || d <= 0 || (d & 1)) return -1;
+  const long rows = (long)B * H * T;
+#pragma omp parallel for schedule(static)
+  for (long r = 0; r < rows; ++r) {
+    const long t = r % T;
+    for (int m = 0; m < d / 2; ++m) {
+      const double theta = (double)(pos0 + t) * freq[m];
+      const double c = cos(theta), sn = sin(theta);
+      const double a = widen(x, dtype, (size_t)r * d + 2 * m);
+      const double b = widen(x, dtype, (size_t)r * d + 2 * m + 1);
+      out[(size_t)r * d + 2 * m] = a * c - b * sn;
+      out[(size_t)r * d + 2 * m + 1] = a * sn + b * c;
+    }
+    if (round_to_bf16)
+      for (int e = 0; e < d; ++e) out[(size_t)r * d + e] = round_bf16(out[(size_t)r * d + e]);
+  }
+  return 0;
 }
 
 int oracle_num_threads(void) { return nthreads(); }

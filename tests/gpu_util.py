@@ -2,6 +2,9 @@
 hand the same values to the oracle, and measure the error."""
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 
 import oracle
@@ -45,23 +48,6 @@ def errors(got: np.ndarray, ref: np.ndarray):
     return max_abs, rel_rms
 
 
-def assert_close_scaled(got, ref, what: str = ""):
-    """The bf16 bars with max-abs taken relative to max(1, |ref|) element by
-    element: the absolute bar is for O(1) outputs, and above 1 a bf16 output
-    alone carries up to half a spacing of |ref| * 2^-8 (0.0156 at 4 <= |ref| < 8),
-    so the scaled bar stays the same number of bf16 spacings at every
-    magnitude.  For whole-workload comparisons whose outputs reach several
-    units (sharp heads, V ~ N(0, 1))."""
-    got = np.asarray(got, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    _, rel_rms = errors(got, ref)
-    scaled = np.abs(got - ref) / np.maximum(1.0, np.abs(ref))
-    w = np.unravel_index(int(np.argmax(scaled)), scaled.shape)
-    print(f"{what}: scaled max-abs {scaled[w]:.3e} (at |ref| {abs(ref[w]):.3f}, "
-          f"abs err {abs(got[w] - ref[w]):.3e}) rel-RMS {rel_rms:.3e}")
-    assert scaled[w] <= BF16_MAX_ABS and rel_rms <= BF16_REL_RMS, what
-
-
 def assert_close(got, ref, dtype: str, what: str = ""):
     max_abs, rel_rms = errors(got, ref)
     print(f"{what}: max-abs {max_abs:.3e} rel-RMS {rel_rms:.3e}")
@@ -70,6 +56,38 @@ def assert_close(got, ref, dtype: str, what: str = ""):
             f"{what}: max-abs {max_abs:.3e} rel-RMS {rel_rms:.3e}"
     else:
         assert max_abs <= F32_MAX_ABS, f"{what}: max-abs {max_abs:.3e}"
+    return max_abs, rel_rms
+
+
+def worst_element(got, ref):
+    """Index, reference value and device value of the largest absolute error."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    w = np.unravel_index(int(np.argmax(np.abs(got - ref))), ref.shape)
+    return tuple(int(i) for i in w), float(ref[w]), float(got[w])
+
+
+def record(name: str, **fields):
+    """Append one parity figure to the JSON-lines file named by the
+    ATTN_PARITY_RECORD environment variable (nothing when it is unset)."""
+    path = os.environ.get("ATTN_PARITY_RECORD")
+    if not path:
+        return
+    with open(path, "a") as f:
+        f.write(json.dumps({"name": name, **fields}) + "\n")
+
+
+def assert_workload(got, ref, what: str):
+    """The bf16 bars, absolute, on a whole workload's compared elements; the
+    figures and the worst element are printed and recorded."""
+    max_abs, rel_rms = errors(got, ref)
+    where, r, g = worst_element(got, ref)
+    print(f"{what}: max-abs {max_abs:.3e} rel-RMS {rel_rms:.3e} "
+          f"(worst at {where}: ref {r:.5f}, got {g:.5f})", flush=True)
+    record(what, max_abs=max_abs, rel_rms=rel_rms, worst_at=list(where), worst_ref=r,
+           worst_got=g, elements=int(np.asarray(ref).size))
+    assert max_abs <= BF16_MAX_ABS and rel_rms <= BF16_REL_RMS, \
+        f"{what}: max-abs {max_abs:.3e} rel-RMS {rel_rms:.3e}"
     return max_abs, rel_rms
 
 

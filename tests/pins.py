@@ -525,4 +525,109 @@ def pin_bwd_rowsums_brute_force():
     assert np.allclose(rs[0, 0], share.sum(axis=1), rtol=1e-13, atol=0)
 
 
+# ------------------------------------------------------- rotary position embedding
+# YaRN's code cell rotates Q and K at their positions before the scores; the
+# rotation itself is not defined on the page, so it is pinned by what any
+# rotation of dimension pairs must satisfy and by its fixed special cases.
+
+def _pairs(x):
+    return x.reshape(x.shape[:-1] + (x.shape[-1] // 2, 2))
+
+
+def pin_rope_zero_frequency_is_identity():
+    """Zero frequencies leave every row unchanged, exactly, at any position."""
+    rng = _rng(60)
+    x = rng.standard_normal((2, 3, 17, 8))
+    for pos0 in (0, 5, 100000):
+        assert np.array_equal(oracle.rope(x, np.zeros(4), pos0), x)
+
+
+def pin_rope_quarter_turns():
+    """A pair turned by a quarter turn maps (a, b) to (-b, a) (counter-
+    clockwise), by a half turn to (-a, -b); each pair turns by its own
+    frequency and the pairs are consecutive dimensions (2m, 2m+1)."""
+    x = np.arange(1.0, 9.0).reshape(1, 1, 1, 8)        # pairs (1,2) (3,4) (5,6) (7,8)
+    f = np.array([math.pi / 2, math.pi, 0.0, 3 * math.pi / 2])
+    got = oracle.rope(x, f, pos0=1)[0, 0, 0]
+    want = np.array([-2.0, 1.0, -3.0, -4.0, 5.0, 6.0, 8.0, -7.0])
+    assert np.max(np.abs(got - want)) < 1e-14, got
+    # row t sits at position pos0 + t: two rows later it has turned twice as far
+    x2 = np.tile(x, (1, 1, 3, 1))
+    got2 = oracle.rope(x2, np.array([math.pi / 2, 0.0, 0.0, 0.0]), pos0=0)[0, 0]
+    assert np.max(np.abs(got2[0, :2] - [1.0, 2.0])) < 1e-14
+    assert np.max(np.abs(got2[1, :2] - [-2.0, 1.0])) < 1e-14
+    assert np.max(np.abs(got2[2, :2] - [-1.0, -2.0])) < 1e-14
+
+
+def pin_rope_preserves_pair_norms():
+    """Every pair keeps its length (a rotation), whatever the angle."""
+    rng = _rng(61)
+    x = rng.standard_normal((1, 2, 33, 16))
+    f = rng.uniform(0.0, 2.0, size=8)
+    y = oracle.rope(x, f, pos0=1234)
+    nx = np.linalg.norm(_pairs(x), axis=-1)
+    ny = np.linalg.norm(_pairs(y), axis=-1)
+    assert np.max(np.abs(ny - nx) / nx) < 1e-13
+
+
+def pin_rope_turns_compose():
+    """Turning by position a and then by position b is turning by a + b."""
+    rng = _rng(62)
+    x = rng.standard_normal((1, 1, 1, 12))
+    f = rng.uniform(0.0, 1.5, size=6)
+    for a, b in ((3, 4), (0, 17), (1000, 25)):
+        twice = oracle.rope(oracle.rope(x, f, pos0=a), f, pos0=b)
+        once = oracle.rope(x, f, pos0=a + b)
+        assert np.max(np.abs(twice - once)) < 1e-12, (a, b)
+
+
+def pin_rope_scores_depend_on_distance_only():
+    """<rot_i q, rot_j k> equals <q, rot_(j-i) k>: the scores of rotated rows
+    depend on the distance j - i alone, so shifting every position by one
+    constant leaves them unchanged."""
+    rng = _rng(63)
+    T, d = 20, 16
+    q = rng.standard_normal((1, 1, T, d))
+    k = rng.standard_normal((1, 1, T, d))
+    f = rng.uniform(0.0, 1.0, size=d // 2)
+    qa, ka = oracle.rope(q, f, 0)[0, 0], oracle.rope(k, f, 0)[0, 0]
+    qb, kb = oracle.rope(q, f, 777)[0, 0], oracle.rope(k, f, 777)[0, 0]
+    assert np.max(np.abs(qa @ ka.T - qb @ kb.T)) < 1e-11
+    for i, j in ((0, 0), (3, 11), (19, 2)):
+        kj = oracle.rope(k[:, :, j:j + 1], f, j - i)[0, 0, 0]   # k_j turned by j - i
+        assert abs(qa[i] @ ka[j] - q[0, 0, i] @ kj) < 1e-12, (i, j)
+
+
+def pin_rope_widens_float32_frequencies_exactly():
+    """float32 frequencies enter as their exact values: position 1 turns a
+    pair by exactly the stored float."""
+    f32 = np.array([0.1, 0.7], dtype=np.float32)
+    x = np.array([1.0, 0.0, 0.0, 1.0]).reshape(1, 1, 1, 4)
+    got = oracle.rope(x, f32, pos0=1)[0, 0, 0]
+    th = f32.astype(np.float64)
+    want = [math.cos(th[0]), math.sin(th[0]), -math.sin(th[1]), math.cos(th[1])]
+    assert np.max(np.abs(got - np.array(want))) < 1e-15
+
+
+def pin_rope_bf16_rounding():
+    """The bf16 rounding of rotated rows: values already in bf16 stay as they
+    are (zero frequencies), halfway cases go to the even significand, and
+    every rounded value is within half a bf16 spacing of the unrounded one
+    (8 significant bits: at most 2^-8 relative)."""
+    x = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 3.0 + 2.0 ** -7,
+                  0.15625, -2.0 ** -120, 1.0 + 2.0 ** -9]).reshape(1, 1, 1, 8)
+    got = oracle.rope(x, np.zeros(4), 0, round_to_bf16=True)[0, 0, 0]
+    want = [1.0, 1.0, 1.0 + 2.0 ** -6, -1.0, 3.0, 0.15625, -2.0 ** -120, 1.0]
+    assert np.array_equal(got, want), got
+    rng = _rng(64)
+    y = rng.standard_normal((1, 2, 40, 16))
+    f = rng.uniform(0.0, 1.0, size=8)
+    exact = oracle.rope(y, f, 11)
+    r = oracle.rope(y, f, 11, round_to_bf16=True)
+    assert np.all(np.abs(r - exact) <= 2.0 ** -8 * np.abs(exact) * (1 + 1e-12))
+    # the rounded values have at most 8 significant bits
+    m, _ = np.frexp(r)
+    assert np.array_equal(m * 256, np.round(m * 256))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

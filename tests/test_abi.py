@@ -154,6 +154,10 @@ def fwd(**kw):
     (dict(T=1 << 24), ab.ATTN_EINVAL),               # one head's rows need offsets >= 2^31
     (dict(mode=1, T=(1 << 24) - 1, k=FAKE + (1 << 32), v=FAKE + (2 << 32),
           out=FAKE + (3 << 32)), ab.ATTN_EWORKSPACE),   # largest T passes the shape check
+    (dict(d=128, T=1 << 23), ab.ATTN_EINVAL),        # bf16 rows of 256 B: T < 2^23
+    (dict(mode=1, d=128, T=(1 << 23) - 1, k=FAKE + (1 << 32), v=FAKE + (2 << 32),
+          out=FAKE + (3 << 32)), ab.ATTN_EWORKSPACE),   # largest T at d = 128
+    (dict(dtype=0, T=1 << 23), ab.ATTN_EINVAL),      # fp32 rows of 256 B: T < 2^23
     (dict(mode=1), ab.ATTN_EWORKSPACE),              # dilution without workspace
     (dict(mode=1, workspace=FAKE + 0x5000000, workspace_bytes=16), ab.ATTN_EWORKSPACE),
 ])
@@ -277,6 +281,59 @@ def pre(**kw):
 ])
 def test_prefill_rejects_bad_arguments(kw, status):
     assert pre(**kw) == status
+
+
+def pre_rope(**kw):
+    args = dict(q=FAKE, kcache=FAKE + 0x1000000, vcache=FAKE + 0x2000000, out=FAKE + 0x3000000,
+                B=1, H=2, Tq=16, Tk=40, Lcap=64, d=64, tau=1.0, tau_bh=None, mode=1, eps=1e-6,
+                dtype=1, rope_freq=FAKE + 0x7000000, pos0=0,
+                demand_in=FAKE + 0x4000000, demand_out=FAKE + 0x4000000, lse_out=None,
+                rowsum_out=None, workspace=None, workspace_bytes=0, hip_stream=None)
+    args.update(kw)
+    return ab.attn_prefill_rope(**args)
+
+
+ROPE_WS = FAKE + 0x8000000
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rope_freq=None), ab.ATTN_EINVAL),
+    (dict(rope_freq=FAKE + 0x7000002), ab.ATTN_EINVAL),    # misaligned frequencies
+    (dict(rope_freq=FAKE + 0x1000000 + 128), ab.ATTN_EINVAL),  # inside the K cache
+    (dict(pos0=-1), ab.ATTN_EINVAL),
+    (dict(pos0=(1 << 31) - 40), ab.ATTN_EINVAL),           # last key past 2^31 - 1
+    (dict(pos0=(1 << 31) - 41, workspace=ROPE_WS, workspace_bytes=1 << 20),
+     ab.ATTN_EHIP),                                        # largest pos0 passes the checks
+    (dict(q=None), ab.ATTN_EINVAL),
+    (dict(d=96), ab.ATTN_ENOTSUP),
+    (dict(mode=0, demand_in=None, demand_out=None), ab.ATTN_EWORKSPACE),  # tempered needs it too
+    (dict(), ab.ATTN_EWORKSPACE),
+    (dict(workspace=ROPE_WS, workspace_bytes=64), ab.ATTN_EWORKSPACE),
+    (dict(workspace=FAKE + 0x2000000, workspace_bytes=1 << 20), ab.ATTN_EINVAL),  # on the V cache
+    (dict(workspace=FAKE + 0x7000000 - 64, workspace_bytes=1 << 20), ab.ATTN_EINVAL),  # on freq
+])
+def test_prefill_rope_rejects_bad_arguments(kw, status):
+    """Every status is decided on the host; the one call that passes every
+    check reaches the device query, which fails without a GPU (ATTN_EHIP)."""
+    import torch
+
+    if status == ab.ATTN_EHIP and torch.cuda.is_available():
+        pytest.skip("a GPU is present: the call would launch")
+    assert pre_rope(**kw) == status
+
+
+def test_prefill_rope_workspace_sizes():
+    # rotated Q [B,H,Tq,d] and keys [B,H,Lcap,d], then the attention workspace
+    for (B, H, Tq, Tk, Lcap, d, dt) in ((1, 2, 16, 40, 64, 64, 1), (2, 3, 100, 100, 100, 128, 0)):
+        esz = 2 if dt == 1 else 4
+        qk = B * H * Tq * d * esz + B * H * Lcap * d * esz
+        t = ab.attn_prefill_rope_workspace_bytes(B, H, Tq, Tk, Lcap, d, 0, dt)
+        assert qk <= t <= qk + 512
+        dil = ab.attn_prefill_rope_workspace_bytes(B, H, Tq, Tk, Lcap, d, 1, dt)
+        assert dil - t == ab.attn_prefill_workspace_bytes(B, H, Tq, Tk, d, 1, dt)
+    assert ab.attn_prefill_rope_workspace_bytes(1, 2, 16, 40, 39, 64, 1, 1) == 0   # Tk > Lcap
+    assert ab.attn_prefill_rope_workspace_bytes(1, 2, 16, 40, 64, 96, 1, 1) == 0
+    assert ab.attn_prefill_rope_workspace_bytes(1, 2, 16, 40, 64, 64, 2, 1) == 0
 
 
 BWD_WS = dict(workspace=FAKE + 0xc000000, workspace_bytes=1 << 24)

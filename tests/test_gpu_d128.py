@@ -7,8 +7,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import (DEMAND_TOTAL_REL, assert_close, assert_close_scaled, oracle_qkv,
-                      oracle_view, sample_rows, to_device)
+from gpu_util import (DEMAND_TOTAL_REL, assert_close, assert_workload, oracle_qkv,
+                      oracle_view, to_device)
 from transformer_attention_causal_amd import binding as ab
 from transformer_attention_causal_amd.workloads import (PREFILL, decode_initial_demand,
                                                         decode_queries, draw_qkv, learned_tau,
@@ -157,38 +157,12 @@ def test_d128_decode_steps():
 
 
 @pytest.mark.timeout(600)
-def test_focal_d128_t16k_workload():
-    """B=1, H=20, T=16384, d=128 (a 2.7B focal model's attention at 16K),
-    per-head learned temperatures: sampled rows of three heads against the
-    oracle for both operators, and every head's demand totals."""
-    import torch
-
-    w = PREFILL["focal_d128_t16k"]
-    inp = prefill_inputs(w)
-    taus = learned_tau(w.B, w.H, w.d, seed=w.seed)
-    rows = sample_rows(w.T, 24, seed=161)
-    out, _, dem = run_prefill(inp, 1.0, ab.ATTN_DILUTION, w.eps, tau_bh=taus, want_demand=True)
-    torch.cuda.empty_cache()
-    assert np.max(np.abs(dem.sum(axis=-1) / w.T - 1.0)) <= DEMAND_TOTAL_REL
-    out_t, _, _ = run_prefill(inp, 1.0, ab.ATTN_TEMPERED, tau_bh=taus)
-    for bh, (q1, k1, v1) in zip((0, 7, 19), head_inputs(inp, (0, 7, 19))):
-        tau = float(taus[0, bh])
-        ref, _, _ = oracle.dilution_fwd(q1, k1, v1, tau, w.eps, rows=rows)
-        assert_close(out[:, bh:bh + 1, rows], ref[:, :, rows], "bf16", f"focal d128 dilution head {bh}")
-        ref_t, _ = oracle.tempered_fwd(q1, k1, v1, tau, rows=rows)
-        assert_close(out_t[:, bh:bh + 1, rows], ref_t[:, :, rows], "bf16",
-                     f"focal d128 tempered head {bh}")
-
-
-@pytest.mark.timeout(600)
 def test_focal_d128_t16k_bf16_against_fp32_kernels_all_rows():
     """The whole focal workload (H=20, T=16384, d=128, learned per-head
-    multipliers), every row of every head, where the oracle checks sampled
-    rows: bf16 outputs, LSE and final column demand agree with the fp32
-    kernels' on the same values, to the bf16 bars with max-abs relative to
-    max(1, |ref|): these heads are sharp, so outputs reach several units,
-    where one bf16 spacing is 2^-5 or more (the fp32 kernels are held to the
-    oracle at 1e-5)."""
+    multipliers), every row of every head (the oracle checks every row of
+    the four sharpest heads): bf16 outputs, LSE and final column demand agree
+    with the fp32 kernels' on the same values, to the absolute bf16 bars (the
+    fp32 kernels are held to the oracle at 1e-5)."""
     import torch
 
     w = PREFILL["focal_d128_t16k"]
@@ -202,7 +176,7 @@ def test_focal_d128_t16k_bf16_against_fp32_kernels_all_rows():
         torch.cuda.empty_cache()
         ref, rlse, rdem = run_prefill(f32, 1.0, mode, w.eps, tau_bh=taus, want_demand=dil)
         torch.cuda.empty_cache()
-        assert_close_scaled(out, ref, f"focal d128 mode={mode} all rows vs fp32 kernels")
+        assert_workload(out, ref.astype(np.float64), f"focal d128 mode={mode} all rows vs fp32 kernels")
         assert np.max(np.abs(lse - rlse)) <= LSE_TOL["bf16"]
         if dil:
             tot = np.max(np.abs(dem.astype(np.float64).sum(-1) / rdem.astype(np.float64).sum(-1) - 1.0))

@@ -1,0 +1,169 @@
+"""GPU parity of attn_prefill_rope (rotary position embedding of Q and K ahead
+of either operator, as YaRN's code cell applies it) against the oracle: the
+oracle rotates Q and K in fp64 at the same positions -- and, for bf16
+storage, rounds the rotated rows to bf16 as the device stores them -- and
+runs its pinned forward on the rotated rows."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import assert_close, errors, oracle_view, to_device
+from transformer_attention_causal_amd import binding as ab
+from transformer_attention_causal_amd.workloads import draw_qkv, learned_tau
+
+pytestmark = pytest.mark.gpu
+
+
+def rope_freqs(d, base=10000.0, gamma_low=0.25):
+    """Per-pair frequencies base^(-2m/d); the lower half of the frequencies
+    slowed by a factor, as an extension ramp would (the values are the
+    caller's; any float32 array serves)."""
+    m = np.arange(d // 2, dtype=np.float64)
+    f = base ** (-2.0 * m / d)
+    f[d // 4:] *= gamma_low
+    return f.astype(np.float32)
+
+
+def wide(x, dtype):
+    """The exact fp64 values of a stored array."""
+    v = oracle_view(x, dtype)
+    return v.to_f64() if isinstance(v, oracle.Bf16) else np.asarray(v, dtype=np.float64)
+
+
+def oracle_rope_forward(inp, freq, pos0, tau, mode, eps=1e-6, tau_bh=None, rounded=False):
+    """The oracle on the rotated rows: Q at positions pos0.., K likewise;
+    ``rounded``: the rotated rows rounded to bf16, as the device stores them."""
+    qr = oracle.rope(oracle_view(inp.q, inp.dtype), freq, pos0, round_to_bf16=rounded)
+    kr = oracle.rope(oracle_view(inp.k, inp.dtype), freq, pos0, round_to_bf16=rounded)
+    vv = wide(inp.v, inp.dtype)
+    if tau_bh is None:
+        if mode == ab.ATTN_DILUTION:
+            return oracle.dilution_fwd(qr, kr, vv, tau, eps)[0]
+        return oracle.tempered_fwd(qr, kr, vv, tau)[0]
+    B, H = inp.q.shape[:2]
+    out = np.empty(qr.shape)
+    for b in range(B):
+        for h in range(H):
+            args = (qr[b:b + 1, h:h + 1], kr[b:b + 1, h:h + 1],
+                    np.ascontiguousarray(vv[b:b + 1, h:h + 1]), float(tau_bh[b, h]))
+            if mode == ab.ATTN_DILUTION:
+                out[b, h] = oracle.dilution_fwd(*args, eps)[0][0, 0]
+            else:
+                out[b, h] = oracle.tempered_fwd(*args)[0][0, 0]
+    return out
+
+
+def check_rope(out, inp, freq, pos0, tau, mode, what, tau_bh=None):
+    """fp32: against the exact rotation at 1e-5.  bf16: both bars against the
+    rotation rounded to bf16 (the device stores the rotated rows in bf16, as
+    an unfused rotary step would); against the exact rotation rel-RMS holds
+    the bar and max-abs is reported."""
+    got = out.float().cpu().numpy()
+    exact = oracle_rope_forward(inp, freq, pos0, tau, mode, tau_bh=tau_bh)
+    if inp.dtype == "f32":
+        assert_close(got, exact, "f32", what)
+        return
+    rounded = oracle_rope_forward(inp, freq, pos0, tau, mode, tau_bh=tau_bh, rounded=True)
+    assert_close(got, rounded, "bf16", what + " (rotated rows in bf16)")
+    ma, rr = errors(got, exact)
+    print(f"{what} against the exact rotation: max-abs {ma:.3e} rel-RMS {rr:.3e}")
+    assert rr <= 1e-2, what
+
+
+def device_rope(inp, freq, pos0, tau, mode, eps=1e-6, tau_bh=None, dem=None):
+    import torch
+
+    q, k, v = (to_device(a, inp.dtype) for a in (inp.q, inp.k, inp.v))
+    T = q.shape[2]
+    f = torch.from_numpy(freq).cuda()
+    tb = torch.from_numpy(tau_bh).cuda() if tau_bh is not None else None
+    out = ab.prefill(q, k, v, T, tau=tau, mode=mode, eps=eps, tau_bh=tb, rope_freq=f, pos0=pos0,
+                     demand_in=dem, demand_out=dem)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("mode", [ab.ATTN_DILUTION, ab.ATTN_TEMPERED])
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)])
+@pytest.mark.parametrize("T,pos0", [(1, 0), (33, 5), (300, 0), (257, 40000)])
+def test_rope_matches_oracle(T, pos0, dtype, d, mode):
+    inp = draw_qkv(2, 2, T, d, dtype, seed=9000 + T + d, heavy_frac=0.05)
+    freq = rope_freqs(d)
+    tau = math.sqrt(0.1 * math.log(4.0) + 1.0)
+    out = device_rope(inp, freq, pos0, tau, mode)
+    check_rope(out, inp, freq, pos0, tau, mode, f"rope {dtype} d={d} mode={mode} T={T} pos0={pos0}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_rope_per_head_tau_matches_oracle(d):
+    """Learned per-head multipliers with the rotation (both operators)."""
+    inp = draw_qkv(1, 3, 200, d, "bf16", seed=9100 + d, heavy_frac=0.05)
+    freq = rope_freqs(d)
+    taus = learned_tau(1, 3, d, seed=9100 + d)
+    for mode in (ab.ATTN_DILUTION, ab.ATTN_TEMPERED):
+        out = device_rope(inp, freq, 7, 1.0, mode, tau_bh=taus)
+        check_rope(out, inp, freq, 7, 1.0, mode, f"rope per-head tau d={d} mode={mode}", tau_bh=taus)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)])
+def test_rope_zero_frequencies_are_the_plain_prefill(dtype, d):
+    """With every frequency zero the rotation is the identity: the output is
+    attn_prefill's bit for bit, in both operators."""
+    import torch
+
+    inp = draw_qkv(2, 2, 301, d, dtype, seed=9200 + d, heavy_frac=0.05)
+    q, k, v = (to_device(a, dtype) for a in (inp.q, inp.k, inp.v))
+    zero = torch.zeros(d // 2, dtype=torch.float32, device="cuda")
+    for mode in (ab.ATTN_DILUTION, ab.ATTN_TEMPERED):
+        plain = ab.prefill(q, k, v, 301, tau=1.1, mode=mode)
+        rot = ab.prefill(q, k, v, 301, tau=1.1, mode=mode, rope_freq=zero, pos0=999)
+        torch.cuda.synchronize()
+        assert torch.equal(plain, rot), (dtype, d, mode)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_rope_shifted_positions_leave_outputs(d):
+    """Scores depend on distances only: moving every position by one constant
+    changes the fp32 outputs by rounding alone."""
+    inp = draw_qkv(1, 2, 150, d, "f32", seed=9300 + d, heavy_frac=0.05)
+    freq = rope_freqs(d)
+    for mode in (ab.ATTN_DILUTION, ab.ATTN_TEMPERED):
+        a = device_rope(inp, freq, 0, 1.0, mode).cpu().numpy()
+        b = device_rope(inp, freq, 123457, 1.0, mode).cpu().numpy()
+        assert np.max(np.abs(a - b)) <= 1e-5, (d, mode)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 128)])
+def test_rope_chunks_carry_demand(dtype, d):
+    """A rotated prefill in chunks over a cache of unrotated keys (NaN past
+    the keys so far), the demand carried in place, equals the oracle's whole
+    rotated prefill; key positions start at pos0 = 1000."""
+    import torch
+
+    B, H, T, Lcap, pos0 = 1, 2, 450, 513, 1000
+    inp = draw_qkv(B, H, T, d, dtype, seed=9400 + d, heavy_frac=0.05)
+    freq = rope_freqs(d)
+    q, k, v = (to_device(a, dtype) for a in (inp.q, inp.k, inp.v))
+    kc = torch.full((B, H, Lcap, d), float("nan"), dtype=q.dtype, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    D = torch.zeros((B, H, Lcap), dtype=torch.float32, device="cuda")
+    f = torch.from_numpy(freq).cuda()
+    outs = []
+    for a, b in zip((0, 130, 131, 400), (130, 131, 400, 450)):
+        kc[:, :, a:b] = k[:, :, a:b]
+        vc[:, :, a:b] = v[:, :, a:b]
+        outs.append(ab.prefill(q[:, :, a:b].contiguous(), kc, vc, b, tau=1.0,
+                               mode=ab.ATTN_DILUTION, eps=1e-6, demand_in=D, demand_out=D,
+                               rope_freq=f, pos0=pos0))
+    torch.cuda.synchronize()
+    out = torch.cat(outs, dim=2).float().cpu().numpy()
+    rounded = dtype == "bf16"
+    qr = oracle.rope(oracle_view(inp.q, dtype), freq, pos0, round_to_bf16=rounded)
+    kr = oracle.rope(oracle_view(inp.k, dtype), freq, pos0, round_to_bf16=rounded)
+    ref, _, rdem = oracle.dilution_fwd(qr, kr, wide(inp.v, dtype), 1.0, 1e-6)
+    assert_close(out, ref, dtype, f"rope chunks {dtype} d={d}")
+    dem = D.cpu().numpy()[:, :, :T]
+    tol = 2e-2 if dtype == "bf16" else 1e-5
+    assert np.max(np.abs(dem - rdem)) <= tol * max(1.0, float(rdem.max()))

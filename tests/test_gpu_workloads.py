@@ -1,0 +1,241 @@
+"""The named workloads at their full sizes against the fp64 oracle, element by
+element, at the absolute bf16 bars (max-abs 2e-2, rel-RMS 1e-2) and the
+1e-4 demand-total bar:
+
+* dilution_t16k (B=1, H=16, T=16384, d=64): every row of every head, both
+  operators, with the LSE and each key's final demand;
+* long_t128k (T=131072): every row of head 0, both operators (the oracle runs
+  head 0 in chunks of rows, carrying the demand between them), every head's
+  demand totals;
+* decode_32k (64 sequences x 32768 keys, H=16, 128 steps): every (sequence,
+  head) pair at every step, and the demand totals after every step;
+* focal_d128_t16k (H=20, d=128, learned per-head multipliers): every row of
+  the four sharpest heads, both operators.
+
+The device runs the whole workload in the launch configuration the benchmark
+times; the oracle receives the exact values the device receives."""
+import math
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import (DEMAND_TOTAL_REL, assert_workload, device_qkv, oracle_qkv, record,
+                      to_device)
+from transformer_attention_causal_amd import binding as ab
+from transformer_attention_causal_amd.workloads import (DECODE, PREFILL, decode_cache_device,
+                                                        decode_initial_demand, decode_queries,
+                                                        learned_tau, prefill_inputs)
+
+pytestmark = pytest.mark.gpu
+
+TAU4 = math.sqrt(0.1 * math.log(4.0) + 1.0)   # YaRN multiplier for 4x extension
+TAU8 = math.sqrt(0.1 * math.log(8.0) + 1.0)   # and for 8x
+LSE_BAR = 2e-3         # natural-log LSE, bf16 inputs
+DEMAND_KEY_BAR = 2e-2  # each key's final demand, relative to max(1, largest)
+
+
+def _device_fwd(inp, tau, mode, eps, tau_bh=None):
+    """One forward over the whole workload: (out, lse, demand or None) on the host."""
+    import torch
+
+    q, k, v = device_qkv(inp)
+    B, H, T, _ = q.shape
+    f32 = dict(dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H, T), **f32)
+    dil = mode == ab.ATTN_DILUTION
+    if tau_bh is None:
+        rs = torch.empty((B, H, T), **f32) if dil else None
+        dem = torch.empty((B, H, T), **f32) if dil else None
+        out = ab.fwd(q, k, v, tau=tau, mode=mode, eps=eps, lse_out=lse, demand_out=dem,
+                     rowsum_out=rs)
+    else:
+        dem = torch.zeros((B, H, T), **f32) if dil else None
+        out = ab.prefill(q, k, v, T, tau=1.0, mode=mode, eps=eps, demand_in=dem,
+                         demand_out=dem, lse_out=lse, tau_bh=torch.from_numpy(tau_bh).cuda())
+    torch.cuda.synchronize()
+    res = (out.float().cpu().numpy(), lse.cpu().numpy(),
+           dem.cpu().numpy() if dem is not None else None)
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def _check_lse(lse, rlse, what):
+    err = float(np.max(np.abs(lse.astype(np.float64) - rlse)))
+    print(f"{what} LSE max-abs {err:.3e}", flush=True)
+    record(f"{what} lse", max_abs=err)
+    assert err <= LSE_BAR, f"{what}: LSE max-abs {err:.3e}"
+
+
+def _check_demand(dem, rdem, T, what):
+    dem = dem.astype(np.float64)
+    tot = float(np.max(np.abs(dem.sum(-1) / T - 1.0)))
+    key = float(np.max(np.abs(dem - rdem)) / max(1.0, float(np.max(rdem))))
+    print(f"{what} demand totals vs T {tot:.3e}, per key {key:.3e}", flush=True)
+    record(f"{what} demand", total_rel=tot, per_key_rel=key)
+    assert tot <= DEMAND_TOTAL_REL, f"{what}: demand totals {tot:.3e}"
+    assert key <= DEMAND_KEY_BAR, f"{what}: per-key demand {key:.3e}"
+
+
+@pytest.mark.timeout(600)
+def test_dilution_t16k_every_row_every_head():
+    """B=1, H=16, T=16384, d=64, 5% heavy keys: dilution (tau=1, eps=1e-6) and
+    tempered (tau=YaRN(4)), every output of every head against the oracle."""
+    w = PREFILL["dilution_t16k"]
+    inp = prefill_inputs(w)
+    oqkv = oracle_qkv(inp)
+    out, lse, dem = _device_fwd(inp, 1.0, ab.ATTN_DILUTION, w.eps)
+    t0 = time.time()
+    ref, rlse, rdem = oracle.dilution_fwd(*oqkv, 1.0, w.eps)
+    print(f"oracle dilution_t16k: {time.time() - t0:.1f} s", flush=True)
+    assert_workload(out, ref, "dilution_t16k dilution all rows")
+    _check_lse(lse, rlse, "dilution_t16k dilution")
+    _check_demand(dem, rdem, w.T, "dilution_t16k dilution")
+    out, lse, _ = _device_fwd(inp, TAU4, ab.ATTN_TEMPERED, w.eps)
+    t0 = time.time()
+    ref, rlse = oracle.tempered_fwd(*oqkv, TAU4)
+    print(f"oracle tempered_t16k: {time.time() - t0:.1f} s", flush=True)
+    assert_workload(out, ref, "dilution_t16k tempered all rows")
+    _check_lse(lse, rlse, "dilution_t16k tempered")
+
+
+def _head0(inp):
+    return tuple(np.ascontiguousarray(x[:, :1]) for x in (inp.q, inp.k, inp.v))
+
+
+@pytest.mark.timeout(900)
+def test_long_t128k_head0_every_row_dilution():
+    """T=131072, H=16 (8x the training context), dilution tau=1, eps=1e-6:
+    all heads on the device, every row of head 0 against the oracle (run in 8
+    chunks of rows over the keys so far, the demand carried between them),
+    head 0's LSE and per-key demand, and every head's demand totals."""
+    w = PREFILL["long_t128k"]
+    inp = prefill_inputs(w)
+    out, lse, dem = _device_fwd(inp, 1.0, ab.ATTN_DILUTION, w.eps)
+    tot = float(np.max(np.abs(dem.astype(np.float64).sum(-1) / w.T - 1.0)))
+    print(f"long_t128k all heads: demand totals vs T {tot:.3e}", flush=True)
+    assert tot <= DEMAND_TOTAL_REL
+    q0, k0, v0 = _head0(inp)
+    del inp
+    kc, vc = oracle.Bf16(k0), oracle.Bf16(v0)
+    D = np.zeros((1, 1, w.T))
+    ref = np.empty((1, 1, w.T, w.d))
+    rlse = np.empty((1, 1, w.T))
+    bounds = np.linspace(0, w.T, 9).astype(int)
+    t0 = time.time()
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        o, l = oracle.prefill(oracle.Bf16(np.ascontiguousarray(q0[:, :, a:b])), kc, vc, int(b),
+                              1.0, w.eps, 1, D)
+        ref[:, :, a:b], rlse[:, :, a:b] = o, l
+        print(f"oracle long_t128k head 0 dilution rows [{a}, {b}): {time.time() - t0:.1f} s",
+              flush=True)
+    assert_workload(out[:, :1], ref, "long_t128k dilution head 0 all rows")
+    _check_lse(lse[:, :1], rlse, "long_t128k dilution head 0")
+    _check_demand(dem[:, :1], D, w.T, "long_t128k dilution head 0")
+
+
+@pytest.mark.timeout(900)
+def test_long_t128k_head0_every_row_tempered():
+    """T=131072, H=16, tempered tau=YaRN(8): all heads on the device, every row
+    of head 0 against the oracle (in 8 chunks of rows) with its LSE."""
+    w = PREFILL["long_t128k"]
+    inp = prefill_inputs(w)
+    out, lse, _ = _device_fwd(inp, TAU8, ab.ATTN_TEMPERED, w.eps)
+    q0, k0, v0 = (oracle.Bf16(x) for x in _head0(inp))
+    del inp
+    ref = np.empty((1, 1, w.T, w.d))
+    rlse = np.empty((1, 1, w.T))
+    bounds = np.linspace(0, w.T, 9).astype(int)
+    t0 = time.time()
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        rows = np.arange(a, b, dtype=np.int32)
+        o, l = oracle.tempered_fwd(q0, k0, v0, TAU8, rows=rows)
+        ref[:, :, a:b], rlse[:, :, a:b] = o[:, :, a:b], l[:, :, a:b]
+        print(f"oracle long_t128k head 0 tempered rows [{a}, {b}): {time.time() - t0:.1f} s",
+              flush=True)
+    assert_workload(out[:, :1], ref, "long_t128k tempered head 0 all rows")
+    _check_lse(lse[:, :1], rlse, "long_t128k tempered head 0")
+
+
+def _host_bits(t):
+    import torch
+
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.timeout(900)
+def test_decode_32k_every_pair_every_step():
+    """64 sequences x 32768-key cache, H=16, d=64, 128 steps, demand updated in
+    place: every (sequence, head) output at every step against the oracle,
+    which replays the steps from the same fp32 initial demand in fp64; the
+    demand totals after every step against the closed form sum(D0) + steps
+    and against the oracle's; each key's final demand."""
+    import torch
+
+    w = DECODE["decode_32k"]
+    kc_d, vc_d = decode_cache_device(w.S, w.H, w.L, w.d, w.seed)
+    D0 = decode_initial_demand(w.S, w.H, w.L, w.seed, w.demand_max)
+    qs = decode_queries(w.steps, w.S, w.H, w.d, w.seed)
+    kc = oracle.Bf16(_host_bits(kc_d))
+    vc = oracle.Bf16(_host_bits(vc_d))
+    D_d = torch.from_numpy(D0).cuda()
+    D_ref = D0.astype(np.float64)
+    total0 = D_ref.sum(-1)
+    ws, _ = ab.decode_workspace(w.S, w.H, w.L, "cuda")
+    outs, refs = [], []
+    worst_tot = 0.0
+    t0 = time.time()
+    for step in range(w.steps):
+        out = ab.decode(to_device(qs[step], "bf16"), kc_d, vc_d, D_d, tau=w.tau, eps=w.eps,
+                        workspace=ws)
+        tot = D_d.double().sum(-1).cpu().numpy()
+        outs.append(out.float().cpu().numpy())
+        refs.append(oracle.dilution_decode_step(oracle.Bf16(qs[step]), kc, vc, D_ref, w.tau,
+                                                w.eps))
+        closed = np.max(np.abs(tot / (total0 + step + 1) - 1.0))
+        vs_ref = np.max(np.abs(tot / D_ref.sum(-1) - 1.0))
+        worst_tot = max(worst_tot, float(closed), float(vs_ref))
+        assert closed <= DEMAND_TOTAL_REL, f"step {step}: totals vs closed form {closed:.2e}"
+        assert vs_ref <= DEMAND_TOTAL_REL, f"step {step}: totals vs oracle {vs_ref:.2e}"
+        if step % 16 == 15:
+            print(f"decode_32k step {step + 1}: oracle replay {time.time() - t0:.1f} s, "
+                  f"worst demand-total rel {worst_tot:.2e}", flush=True)
+    torch.cuda.synchronize()
+    assert_workload(np.stack(outs), np.stack(refs), "decode_32k every pair every step")
+    Dg = D_d.double().cpu().numpy()
+    key = float(np.max(np.abs(Dg - D_ref)))
+    print(f"decode_32k final demand per key max-abs {key:.3e}, totals worst {worst_tot:.3e}",
+          flush=True)
+    record("decode_32k demand", total_rel=worst_tot, per_key_abs=key)
+    assert key <= 1e-3
+
+
+@pytest.mark.timeout(600)
+def test_focal_d128_t16k_sharpest_heads_every_row():
+    """B=1, H=20, T=16384, d=128 with learned per-head multipliers sqrt(d)/t,
+    t ~ U[5,10]: the whole workload on the device, every row of the four
+    heads with the largest multipliers (the sharpest bids) against the oracle,
+    both operators, with LSE and per-key demand."""
+    w = PREFILL["focal_d128_t16k"]
+    inp = prefill_inputs(w)
+    taus = learned_tau(w.B, w.H, w.d, seed=w.seed)
+    sharp = [int(i) for i in np.argsort(-taus[0])[:4]]
+    print(f"focal sharpest heads {sharp}, tau {[round(float(taus[0, h]), 3) for h in sharp]}",
+          flush=True)
+    outs = {m: _device_fwd(inp, 1.0, m, w.eps, tau_bh=taus)
+            for m in (ab.ATTN_DILUTION, ab.ATTN_TEMPERED)}
+    for h in sharp:
+        q1, k1, v1 = (oracle.Bf16(np.ascontiguousarray(x[:, h:h + 1]))
+                      for x in (inp.q, inp.k, inp.v))
+        tau = float(taus[0, h])
+        out, lse, dem = outs[ab.ATTN_DILUTION]
+        ref, rlse, rdem = oracle.dilution_fwd(q1, k1, v1, tau, w.eps)
+        assert_workload(out[:, h:h + 1], ref, f"focal d128 dilution head {h} all rows")
+        _check_lse(lse[:, h:h + 1], rlse, f"focal d128 dilution head {h}")
+        _check_demand(dem[:, h:h + 1], rdem, w.T, f"focal d128 dilution head {h}")
+        out, lse, _ = outs[ab.ATTN_TEMPERED]
+        ref, rlse = oracle.tempered_fwd(q1, k1, v1, tau)
+        assert_workload(out[:, h:h + 1], ref, f"focal d128 tempered head {h} all rows")
+        _check_lse(lse[:, h:h + 1], rlse, f"focal d128 tempered head {h}")

@@ -50,8 +50,8 @@ MUTANTS = [
      "causal_bids(Qh + (size_t)li * d, Kh, li, d, c, p, inner_parallel)"),
     ("prefill_cache_stride", "kbase = (size_t)bh * Lcap * d", "kbase = (size_t)bh * Tk * d"),
     ("prefill_tempered_keys_from_chunk_start",
-     "causal_bids(Qh + (size_t)(i - P) * d, Kh, i, d, c, p, 0)",
-     "causal_bids(Qh + (size_t)(i - P) * d, Kh, i - P, d, c, p, 0)"),
+     "causal_bids(Qh + (size_t)(i - P) * d, Kh, i, d, c, p, inner)",
+     "causal_bids(Qh + (size_t)(i - P) * d, Kh, i - P, d, c, p, inner)"),
     ("bwd_dtau_without_sqrt_d", "dtau[bh] = acc / sqrt((double)d);", "dtau[bh] = acc;"),
     ("bwd_dtau_from_bids", "acc += dP[(size_t)i * T + j] * dot(Q + (size_t)i * d, K + (size_t)j * d, d);",
      "acc += P[(size_t)i * T + j] * dot(Q + (size_t)i * d, K + (size_t)j * d, d);"),
@@ -68,6 +68,18 @@ MUTANTS = [
      "dvj[e] += P[(size_t)i * T + j] * dO[(size_t)i * d + e];"),
     ("bwd_per_head_tau_ignored", "(tau_bh ? tau_bh[bh] : tau) / sqrt((double)d)",
      "tau / sqrt((double)d)"),
+    ("rope_turns_clockwise",
+     "      out[(size_t)r * d + 2 * m] = a * c - b * sn;\n      out[(size_t)r * d + 2 * m + 1] = a * sn + b * c;",
+     "      out[(size_t)r * d + 2 * m] = a * c + b * sn;\n      out[(size_t)r * d + 2 * m + 1] = -a * sn + b * c;"),
+    ("rope_position_offset_ignored",
+     "const double theta = (double)(pos0 + t) * freq[m];",
+     "const double theta = (double)t * freq[m];"),
+    ("rope_half_split_pairs",
+     "      const double a = widen(x, dtype, (size_t)r * d + 2 * m);\n      const double b = widen(x, dtype, (size_t)r * d + 2 * m + 1);\n      out[(size_t)r * d + 2 * m] = a * c - b * sn;\n      out[(size_t)r * d + 2 * m + 1] = a * sn + b * c;",
+     "      const double a = widen(x, dtype, (size_t)r * d + m);\n      const double b = widen(x, dtype, (size_t)r * d + m + d / 2);\n      out[(size_t)r * d + m] = a * c - b * sn;\n      out[(size_t)r * d + m + d / 2] = a * sn + b * c;"),
+    ("rope_bf16_seven_bits", "const double scaled = ldexp(m, 8);", "const double scaled = ldexp(m, 7);"),
+    ("rope_bf16_ties_up", "if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;",
+     "if (frac >= 0.5) r += 1.0;"),
 ]
 
 RUNNER = r"""

@@ -17,7 +17,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libattn.so")
+# ATTN_LIB names another build of the same library (the host-sanitized one
+# the CPU-side ABI tests can run against); by default the in-tree libattn.so.
+LIB_PATH = os.environ.get("ATTN_LIB") or os.path.join(PKG, "libattn.so")
 
 ATTN_OK, ATTN_EINVAL, ATTN_ENOTSUP, ATTN_EWORKSPACE, ATTN_EHIP = 0, -1, -2, -3, -4
 ATTN_TEMPERED, ATTN_DILUTION = 0, 1
@@ -26,6 +28,7 @@ ATTN_F32, ATTN_BF16 = 0, 1
 EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_bytes", "attn_dilution_lse",
             "attn_dilution_committed", "attn_dilution_shares", "attn_bwd",
             "attn_bwd_ex", "attn_bwd_workspace_bytes", "attn_prefill", "attn_prefill_workspace_bytes",
+            "attn_prefill_rope", "attn_prefill_rope_workspace_bytes",
             "attn_decode", "attn_decode_ex", "attn_decode_workspace_bytes",
             "attn_yarn_tau", "attn_strerror")
 
@@ -65,6 +68,11 @@ def load() -> ctypes.CDLL:
         lib.attn_prefill.restype = i
         lib.attn_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i, f, i, vp, vp,
                                      vp, vp, vp, sz, vp]
+        lib.attn_prefill_rope.restype = i
+        lib.attn_prefill_rope.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i, f, i, vp, i,
+                                          vp, vp, vp, vp, vp, sz, vp]
+        lib.attn_prefill_rope_workspace_bytes.restype = sz
+        lib.attn_prefill_rope_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
         lib.attn_prefill_workspace_bytes.restype = sz
         lib.attn_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
         lib.attn_dilution_lse.restype = i
@@ -128,6 +136,18 @@ def attn_prefill(q, kcache, vcache, out, B, H, Tq, Tk, Lcap, d, tau, tau_bh, mod
     return load().attn_prefill(q, kcache, vcache, out, B, H, Tq, Tk, Lcap, d, tau, tau_bh, mode,
                                eps, dtype, demand_in, demand_out, lse_out, rowsum_out, workspace,
                                workspace_bytes, hip_stream)
+
+
+def attn_prefill_rope(q, kcache, vcache, out, B, H, Tq, Tk, Lcap, d, tau, tau_bh, mode, eps,
+                      dtype, rope_freq, pos0, demand_in, demand_out, lse_out, rowsum_out,
+                      workspace, workspace_bytes, hip_stream) -> int:
+    return load().attn_prefill_rope(q, kcache, vcache, out, B, H, Tq, Tk, Lcap, d, tau, tau_bh,
+                                    mode, eps, dtype, rope_freq, pos0, demand_in, demand_out,
+                                    lse_out, rowsum_out, workspace, workspace_bytes, hip_stream)
+
+
+def attn_prefill_rope_workspace_bytes(B, H, Tq, Tk, Lcap, d, mode, dtype) -> int:
+    return int(load().attn_prefill_rope_workspace_bytes(B, H, Tq, Tk, Lcap, d, mode, dtype))
 
 
 def attn_prefill_workspace_bytes(B, H, Tq, Tk, d, mode, dtype) -> int:
@@ -198,6 +218,28 @@ def _stream_handle(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _check_like(t, ref, name):
+    """``t`` must be a contiguous tensor of ``ref``'s shape, dtype and device."""
+    if t is None:
+        return
+    if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous() \
+            or t.device != ref.device:
+        raise ValueError(f"{name} must be a contiguous {ref.dtype} tensor of shape "
+                         f"{tuple(ref.shape)} on {ref.device}")
+
+
+def _check_rows(t, shape, device, name):
+    """``t`` (optional) must be a contiguous float32 tensor of ``shape`` on ``device``."""
+    import torch
+
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != torch.float32 or not t.is_contiguous() \
+            or t.device != device:
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)} "
+                         f"on {device}")
+
+
 def fwd_workspace(B, H, T, mode, dtype_code, device, d=64):
     import torch
 
@@ -212,12 +254,16 @@ def fwd(q, k, v, tau: float = 1.0, mode: int = ATTN_TEMPERED, eps: float = 1e-6,
     """Run attn_fwd_ex on [B,H,T,d] tensors (d = 64 or 128); returns ``out``."""
     import torch
 
-    if not (q.shape == k.shape == v.shape) or q.dim() != 4:
+    if q.dim() != 4:
         raise ValueError("q, k, v must share one [B,H,T,d] shape")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
-    B, H, T, d = q.shape
     code = _dtype_code(q)
+    _check_like(q, q, "q")
+    _check_like(k, q, "k")
+    _check_like(v, q, "v")
+    _check_like(out, q, "out")
+    B, H, T, d = q.shape
+    for name, t in (("lse_out", lse_out), ("demand_out", demand_out), ("rowsum_out", rowsum_out)):
+        _check_rows(t, (B, H, T), q.device, name)
     if out is None:
         out = torch.empty_like(q)
     ws_bytes = 0
@@ -257,11 +303,19 @@ def bwd(q, k, v, out, dout, lse, rowsum=None, tau: float = 1.0, mode: int = ATTN
     table is then read instead of recomputed).  Returns (dq, dk, dv)."""
     import torch
 
-    for t in (q, k, v, out, dout):
-        if t.shape != q.shape or not t.is_contiguous():
-            raise ValueError("q, k, v, out, dout must be contiguous and share one shape")
-    B, H, T, d = q.shape
+    if q.dim() != 4:
+        raise ValueError("q, k, v, out, dout must share one [B,H,T,d] shape")
     code = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq),
+                    ("dk", dk), ("dv", dv)):
+        _check_like(t, q, name)
+    B, H, T, d = q.shape
+    if lse is None:
+        raise ValueError("lse (the forward's lse_out) is required")
+    _check_rows(lse, (B, H, T), q.device, "lse")
+    _check_rows(rowsum, (B, H, T), q.device, "rowsum")
+    if mode == ATTN_DILUTION and rowsum is None:
+        raise ValueError("rowsum (the forward's rowsum_out) is required for dilution")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
@@ -289,12 +343,15 @@ def bwd(q, k, v, out, dout, lse, rowsum=None, tau: float = 1.0, mode: int = ATTN
 
 def prefill(q, kcache, vcache, Tk: int, tau: float = 1.0, mode: int = ATTN_DILUTION,
             eps: float = 1e-6, demand_in=None, demand_out=None, lse_out=None, out=None,
-            workspace=None, tau_bh=None, rowsum_out=None):
+            workspace=None, tau_bh=None, rowsum_out=None, rope_freq=None, pos0: int = 0):
     """Run attn_prefill: q [B,H,Tq,d] holds the rows at positions Tk-Tq..Tk-1,
     the caches [B,H,Lcap,d] keys/values 0..Tk-1; ``demand_in``/``demand_out``
     are [B,H,Lcap] fp32 (may be one tensor: updated in place); ``tau_bh`` an
     optional [B,H] fp32 tensor of per-head multipliers; ``lse_out`` and
-    ``rowsum_out`` optional [B,H,Tq] fp32 (what ``bwd`` needs).  Returns ``out``."""
+    ``rowsum_out`` optional [B,H,Tq] fp32 (what ``bwd`` needs).  With
+    ``rope_freq`` (a [d/2] fp32 tensor) it runs attn_prefill_rope instead: Q
+    and the (unrotated) cached keys are rotated at positions pos0 + index
+    first.  Returns ``out``."""
     import torch
 
     if q.dim() != 4 or kcache.dim() != 4 or vcache.shape != kcache.shape:
@@ -314,15 +371,37 @@ def prefill(q, kcache, vcache, Tk: int, tau: float = 1.0, mode: int = ATTN_DILUT
                                or not tau_bh.is_contiguous()):
         raise ValueError("tau_bh must be a contiguous float32 [B,H] tensor")
     code = _dtype_code(q)
+    _check_like(out, q, "out")
+    for name, t in (("lse_out", lse_out), ("rowsum_out", rowsum_out)):
+        _check_rows(t, (B, H, Tq), q.device, name)
+    if rope_freq is not None:
+        _check_rows(rope_freq, (d // 2,), q.device, "rope_freq")
     if out is None:
         out = torch.empty_like(q)
     ws_bytes = 0
     if workspace is None:
-        n = attn_prefill_workspace_bytes(B, H, Tq, int(Tk), d, mode, code)
+        if rope_freq is not None:
+            n = attn_prefill_rope_workspace_bytes(B, H, Tq, int(Tk), Lcap, d, mode, code)
+        else:
+            n = attn_prefill_workspace_bytes(B, H, Tq, int(Tk), d, mode, code)
         if n:
             workspace, ws_bytes = torch.empty(n, dtype=torch.uint8, device=q.device), n
     else:
         ws_bytes = workspace.numel() * workspace.element_size()
+    if rope_freq is not None:
+        st = attn_prefill_rope(
+            q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), out.data_ptr(), B, H, Tq,
+            int(Tk), Lcap, d, float(tau), tau_bh.data_ptr() if tau_bh is not None else None,
+            int(mode), float(eps), code, rope_freq.data_ptr(), int(pos0),
+            demand_in.data_ptr() if demand_in is not None else None,
+            demand_out.data_ptr() if demand_out is not None else None,
+            lse_out.data_ptr() if lse_out is not None else None,
+            rowsum_out.data_ptr() if rowsum_out is not None else None,
+            workspace.data_ptr() if workspace is not None else None, ws_bytes,
+            _stream_handle(q.device))
+        if st != ATTN_OK:
+            raise AttnError(st, "attn_prefill_rope")
+        return out
     st = attn_prefill(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), out.data_ptr(), B, H,
                       Tq, int(Tk), Lcap, d, float(tau),
                       tau_bh.data_ptr() if tau_bh is not None else None, int(mode), float(eps), code,
@@ -344,8 +423,14 @@ def dilution_stages(q, k, v, tau: float = 1.0, eps: float = 1e-6, out=None, work
     stage each on the current stream, and the output tensor they fill."""
     import torch
 
-    B, H, T, d = q.shape
+    if q.dim() != 4:
+        raise ValueError("q, k, v must share one [B,H,T,d] shape")
     code = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _check_like(t, q, name)
+    B, H, T, d = q.shape
+    for name, t in (("lse_out", lse_out), ("demand_out", demand_out)):
+        _check_rows(t, (B, H, T), q.device, name)
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:

@@ -12,7 +12,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
 PEAKS_LIB = os.path.join(PKG, "libattn_peaks.so")
 
-SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "bwd_bf16.hip", "bwd_f32.hip"]
+SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "bwd_bf16.hip", "bwd_f32.hip",
+           "rope.hip"]
 PEAKS_SOURCES = ["peaks.hip"]
 
 # Packed fp32 VALU forms are disabled: every fp32 operation is a plain
@@ -48,5 +49,30 @@ def build(verbose: bool = False) -> str:
     return _hipcc(SOURCES, LIB, verbose)
 
 
+# Host sanitizers for the C ABI's host code (argument checks, workspace
+# carving): AddressSanitizer and UndefinedBehaviorSanitizer on the host pass
+# only -- the device code is built as usual.  The resulting library is for the
+# CPU-side ABI tests (transformer_attention_causal_amd/sanitize.sh); it needs
+# the ASan runtime loaded first.
+SAN_LIB = os.path.join(PKG, "libattn_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-shared-libasan"]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    global FLAGS
+    saved = FLAGS
+    FLAGS = FLAGS + SAN_FLAGS
+    try:
+        return _hipcc(SOURCES, SAN_LIB, verbose)
+    finally:
+        FLAGS = saved
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys as _sys
+    if "--sanitized" in _sys.argv:
+        print(build_sanitized(verbose=True))
+    else:
+        print(build(verbose=True))

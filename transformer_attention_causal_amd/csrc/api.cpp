@@ -111,7 +111,6 @@ bool head_dim_ok(int d, int dtype) {
 
 bool shape_ok(int B, int H, int T) {
   if (B <= 0 || H <= 0 || T <= 0) return false;
-  // one head's rows are addressed with byte offsets below 2^31 (buffer loads)
   if (T >= (1 << 24)) return false;
   // element counts must fit the kernels' 64-bit offsets and 32-bit grids
   const size_t BH = (size_t)B * H;
@@ -119,12 +118,20 @@ bool shape_ok(int B, int H, int T) {
   return true;
 }
 
+// The kernels address one head's T rows of d elements with 32-bit byte
+// offsets (buffer loads whose range is the bytes from a tile to the end of
+// the head): T * d * element size must stay below 2^31.
+bool rows_fit(int T, int d, int dtype) {
+  const size_t esz = dtype == ATTN_BF16 ? 2 : 4;
+  return (size_t)T * (size_t)d * esz <= (size_t)INT32_MAX;
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t attn_fwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype) {
-  if (!shape_ok(B, H, T) || !head_dim_ok(d, dtype)) return 0;
+  if (!shape_ok(B, H, T) || !head_dim_ok(d, dtype) || !rows_fit(T, d, dtype)) return 0;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
   if (mode != ATTN_DILUTION) return 0;
   FwdWorkspace ws;
@@ -149,6 +156,7 @@ int check_fwd(const void *q, const void *k, const void *v, const void *out, int 
   if (!std::isfinite(tau) || tau < 0.0f) return ATTN_EINVAL;
   if (!std::isfinite(eps) || eps < 0.0f) return ATTN_EINVAL;
   if (!head_dim_ok(d, dtype)) return ATTN_ENOTSUP;
+  if (!rows_fit(T, d, dtype)) return ATTN_EINVAL;
   const size_t esz = dtype == ATTN_BF16 ? 2 : 4;
   const size_t nbytes = (size_t)B * H * (size_t)T * d * esz;
   if (out && (overlaps(out, nbytes, q, nbytes) || overlaps(out, nbytes, k, nbytes) ||
@@ -308,6 +316,7 @@ int attn_fwd(const void *q, const void *k, const void *v, void *out, int B, int 
 
 size_t attn_prefill_workspace_bytes(int B, int H, int Tq, int Tk, int d, int mode, int dtype) {
   if (!shape_ok(B, H, Tk) || Tq < 1 || Tq > Tk || !head_dim_ok(d, dtype)) return 0;
+  if (!rows_fit(Tk, d, dtype)) return 0;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
   if (mode != ATTN_DILUTION) return 0;
   FwdWorkspace ws;
@@ -315,10 +324,34 @@ size_t attn_prefill_workspace_bytes(int B, int H, int Tq, int Tk, int d, int mod
   return ws.total;
 }
 
-int attn_prefill(const void *q, const void *kcache, const void *vcache, void *out, int B, int H,
-                 int Tq, int Tk, int Lcap, int d, float tau, const float *tau_bh, int mode,
-                 float eps, int dtype, const float *demand_in, float *demand_out, float *lse_out,
-                 float *rowsum_out, void *workspace, size_t workspace_bytes, void *hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// The rotated rows of a prefill with rotary position embedding: Q [B,H,Tq,d]
+// and the cache's first Tk keys at the cache's stride [B,H,Lcap,d], in the
+// storage type, ahead of the attention workspace.
+struct RopeWorkspace {
+  size_t q_bytes, k_bytes, total;
+};
+
+bool rope_workspace(int B, int H, int Tq, int Lcap, int d, int dtype, RopeWorkspace *rw) {
+  const size_t esz = dtype == ATTN_BF16 ? 2 : 4;
+  rw->q_bytes = round_up((size_t)B * H * (size_t)Tq * d * esz);
+  rw->k_bytes = round_up((size_t)B * H * (size_t)Lcap * d * esz);
+  rw->total = rw->q_bytes + rw->k_bytes;
+  return true;
+}
+
+// attn_prefill and attn_prefill_rope.  With rope_freq, Q and the keys are
+// rotated into the head of the workspace first and the attention kernels
+// read them from there; the attention workspace follows.
+int prefill_common(const void *q, const void *kcache, const void *vcache, void *out, int B, int H,
+                   int Tq, int Tk, int Lcap, int d, float tau, const float *tau_bh, int mode,
+                   float eps, int dtype, const float *rope_freq, int pos0,
+                   const float *demand_in, float *demand_out, float *lse_out, float *rowsum_out,
+                   void *workspace, size_t workspace_bytes, void *hip_stream) {
+
   if (!q || !kcache || !vcache || !out) return ATTN_EINVAL;
   if (mode != ATTN_TEMPERED && mode != ATTN_DILUTION) return ATTN_EINVAL;
   if (mode == ATTN_TEMPERED && (demand_in || demand_out || rowsum_out)) return ATTN_EINVAL;
@@ -327,6 +360,7 @@ int attn_prefill(const void *q, const void *kcache, const void *vcache, void *ou
   if (!std::isfinite(tau) || tau < 0.0f) return ATTN_EINVAL;
   if (!std::isfinite(eps) || eps < 0.0f) return ATTN_EINVAL;
   if (!head_dim_ok(d, dtype)) return ATTN_ENOTSUP;
+  if (!rows_fit(Lcap, d, dtype)) return ATTN_EINVAL;
   const void *ptrs[9] = {q, kcache, vcache, out, demand_in, demand_out, lse_out, rowsum_out, tau_bh};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return ATTN_EINVAL;
@@ -359,15 +393,66 @@ int attn_prefill(const void *q, const void *kcache, const void *vcache, void *ou
   if (demand_in && demand_out && demand_in != demand_out &&
       overlaps(demand_in, dbytes, demand_out, dbytes))
     return ATTN_EINVAL;
+  if (rope_freq) {
+    if ((reinterpret_cast<uintptr_t>(rope_freq) & 3u) != 0) return ATTN_EINVAL;
+    if (pos0 < 0 || (long)pos0 + Tk > (long)INT32_MAX) return ATTN_EINVAL;
+    const size_t fbytes = (size_t)(d / 2) * sizeof(float);
+    if (hits_tensor(rope_freq, fbytes) || overlaps(rope_freq, fbytes, lse_out, rbytes) ||
+        overlaps(rope_freq, fbytes, rowsum_out, rbytes) ||
+        overlaps(rope_freq, fbytes, demand_out, dbytes))
+      return ATTN_EINVAL;
+  }
+  RopeWorkspace rw{};
+  if (rope_freq) rope_workspace(B, H, Tq, Lcap, d, dtype, &rw);
   FwdWorkspace ws{};
+  size_t need = rw.total;
   if (mode == ATTN_DILUTION) {
     if (!prefill_workspace(B, H, Tq, Tk, d, dtype, &ws)) return ATTN_EINVAL;
-    if (!workspace || workspace_bytes < ws.total || !aligned16(workspace)) return ATTN_EWORKSPACE;
+    need += ws.total;
+  }
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return ATTN_EWORKSPACE;
+    // the workspace is written: it may not overlap any argument
+    if (hits_tensor(workspace, need) || overlaps(workspace, need, lse_out, rbytes) ||
+        overlaps(workspace, need, rowsum_out, rbytes) ||
+        overlaps(workspace, need, demand_out, dbytes) ||
+        overlaps(workspace, need, demand_in, dbytes) ||
+        overlaps(workspace, need, tau_bh, BH * sizeof(float)) ||
+        overlaps(workspace, need, rope_freq, (size_t)(d / 2) * sizeof(float)))
+      return ATTN_EINVAL;
   }
   int st = check_device();
   if (st != ATTN_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  const bool bf16 = dtype == ATTN_BF16;
+  char *attn_ws = workspace ? static_cast<char *>(workspace) + rw.total : nullptr;
+  if (rope_freq) {
+    // rotate the chunk's query rows (positions pos0 + P ..) and the keys
+    // (positions pos0 ..) into the workspace; the kernels read those
+    char *wq = static_cast<char *>(workspace), *wk = wq + rw.q_bytes;
+    attn::RopeArgs r{};
+    r.BH = (int)BH;
+    r.D = d;
+    r.freq = rope_freq;
+    r.x = q;
+    r.y = wq;
+    r.rows = Tq;
+    r.in_stride = r.out_stride = (size_t)Tq;
+    r.pos0 = (long)pos0 + (Tk - Tq);
+    hipError_t e = attn::launch_rope(r, bf16, s);
+    if (e != hipSuccess) return fail_hip(e);
+    r.x = kcache;
+    r.y = wk;
+    r.rows = Tk;
+    r.in_stride = r.out_stride = (size_t)Lcap;
+    r.pos0 = pos0;
+    e = attn::launch_rope(r, bf16, s);
+    if (e != hipSuccess) return fail_hip(e);
+    q = wq;
+    kcache = wk;
+  }
   attn::FwdArgs a = make_args(q, kcache, vcache, out, B, H, Tk, d, tau, eps,
-                              mode == ATTN_DILUTION ? workspace : nullptr, ws);
+                              mode == ATTN_DILUTION ? attn_ws : nullptr, ws);
   a.Tq = Tq;
   a.kstride = Lcap;
   a.vrow0 = attn::first_block_row(Tk, Tq);
@@ -376,8 +461,6 @@ int attn_prefill(const void *q, const void *kcache, const void *vcache, void *ou
     a.tau_bh = tau_bh;
     a.c2 = (float)(1.4426950408889634 / std::sqrt((double)d));
   }
-  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  const bool bf16 = dtype == ATTN_BF16;
   a.lse_nat = lse_out;
   if (mode == ATTN_TEMPERED)
     return finish(bf16 ? attn::launch_rows_bf16(attn::kRowTempered, a, s)
@@ -395,6 +478,47 @@ int attn_prefill(const void *q, const void *kcache, const void *vcache, void *ou
   a.rowsum_out = rowsum_out;
   return finish(bf16 ? attn::launch_rows_bf16(attn::kRowShare, a, s)
                      : attn::launch_rows_f32(attn::kRowShare, a, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_prefill(const void *q, const void *kcache, const void *vcache, void *out, int B, int H,
+                 int Tq, int Tk, int Lcap, int d, float tau, const float *tau_bh, int mode,
+                 float eps, int dtype, const float *demand_in, float *demand_out, float *lse_out,
+                 float *rowsum_out, void *workspace, size_t workspace_bytes, void *hip_stream) {
+  return prefill_common(q, kcache, vcache, out, B, H, Tq, Tk, Lcap, d, tau, tau_bh, mode, eps,
+                        dtype, nullptr, 0, demand_in, demand_out, lse_out, rowsum_out, workspace,
+                        workspace_bytes, hip_stream);
+}
+
+size_t attn_prefill_rope_workspace_bytes(int B, int H, int Tq, int Tk, int Lcap, int d, int mode,
+                                         int dtype) {
+  if (!shape_ok(B, H, Lcap) || Tq < 1 || Tq > Tk || Tk > Lcap || !head_dim_ok(d, dtype)) return 0;
+  if (!rows_fit(Lcap, d, dtype)) return 0;
+  if (mode != ATTN_TEMPERED && mode != ATTN_DILUTION) return 0;
+  RopeWorkspace rw;
+  rope_workspace(B, H, Tq, Lcap, d, dtype, &rw);
+  size_t total = rw.total;
+  if (mode == ATTN_DILUTION) {
+    FwdWorkspace ws;
+    if (!prefill_workspace(B, H, Tq, Tk, d, dtype, &ws)) return 0;
+    total += ws.total;
+  }
+  return total;
+}
+
+int attn_prefill_rope(const void *q, const void *kcache, const void *vcache, void *out, int B,
+                      int H, int Tq, int Tk, int Lcap, int d, float tau, const float *tau_bh,
+                      int mode, float eps, int dtype, const float *rope_freq, int pos0,
+                      const float *demand_in, float *demand_out, float *lse_out,
+                      float *rowsum_out, void *workspace, size_t workspace_bytes,
+                      void *hip_stream) {
+  if (!rope_freq) return ATTN_EINVAL;
+  return prefill_common(q, kcache, vcache, out, B, H, Tq, Tk, Lcap, d, tau, tau_bh, mode, eps,
+                        dtype, rope_freq, pos0, demand_in, demand_out, lse_out, rowsum_out,
+                        workspace, workspace_bytes, hip_stream);
 }
 
 }  // extern "C"
@@ -436,7 +560,7 @@ extern "C" {
 
 size_t attn_bwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype) {
   if (!shape_ok(B, H, T) || (dtype != ATTN_BF16 && dtype != ATTN_F32)) return 0;
-  if (!head_dim_ok(d, dtype)) return 0;
+  if (!head_dim_ok(d, dtype) || !rows_fit(T, d, dtype)) return 0;
   if (mode != ATTN_TEMPERED && mode != ATTN_DILUTION) return 0;
   BwdWorkspace ws;
   if (!bwd_workspace(B, H, T, d, mode, dtype, &ws)) return 0;
@@ -461,6 +585,7 @@ int attn_bwd_ex(const void *q, const void *k, const void *v, const void *out, co
   if (!std::isfinite(tau) || tau < 0.0f) return ATTN_EINVAL;
   if (!std::isfinite(eps) || eps < 0.0f) return ATTN_EINVAL;
   if (!head_dim_ok(d, dtype)) return ATTN_ENOTSUP;
+  if (!rows_fit(T, d, dtype)) return ATTN_EINVAL;
   // the three gradients may not alias each other or any input
   const size_t nbytes = (size_t)B * H * (size_t)T * d * (dtype == ATTN_BF16 ? 2 : 4);
   const size_t rbytes = (size_t)B * H * (size_t)T * sizeof(float);

@@ -56,7 +56,9 @@ struct RowState {
   float l_run;     // fp32 row sum of exp2(x - m_run) over this half's keys (kernels
                    // that output the log-sum-exp)
   f32x4 lsum;      // row sum, on the matrix cores, of the bf16 weights fed to P@V
-                   // (tempered: exp2(x - m_run), pass 2b: the shares), all elements equal
+                   // (tempered: exp2(x - m_run), pass 2b: the shares), all elements
+                   // equal: the output's normaliser, so that the weights' bf16 rounding
+                   // enters numerator and denominator alike
 };
 
 // Bring the running max up to the tile's (masked) maximum and rescale what
@@ -77,7 +79,7 @@ __device__ __forceinline__ void st_rescale(RowState<D> &st, const f32x16 *s, int
   const float m_new = fmaxf(st.m_run, tmax * c2);   // finite: every row sees its first key
   const float alpha = fast_exp2(st.m_run - m_new);  // 0 while m_run is still -inf
   if constexpr (FP32SUM) st.l_run *= alpha;
-  else st.lsum *= alpha;
+  if constexpr (!FP32SUM || MODE == kRowTempered) st.lsum *= alpha;
   if constexpr (MODE == kRowTempered) {
 #pragma unroll
     for (int i = 0; i < Geom<D>::kOBlocks; ++i)
@@ -138,9 +140,15 @@ __device__ __forceinline__ void st_tile(RowState<D> &st, const bf16x8 *qf, const
     }
     st.l_run += ts;
     if constexpr (MODE == kRowTempered) {
+      // the output is normalised by the sum of the same bf16 weights (on the
+      // matrix cores), the log-sum-exp by the fp32 sum
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-        pv_update_d<D>(st.o, vt_lds, t, l32, h, pack8(p + 16 * t), pack8(p + 16 * t + 8));
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 pf0 = pack8(p + 16 * t), pf1 = pack8(p + 16 * t + 8);
+        st.lsum = mfma16(sel, pf0, st.lsum);
+        st.lsum = mfma16(sel, pf1, st.lsum);
+        pv_update_d<D>(st.o, vt_lds, t, l32, h, pf0, pf1);
+      }
     }
   } else {
     float tmax = -INFINITY;
@@ -495,7 +503,9 @@ __global__ void __launch_bounds__(256, (RowOccupancy<MODE, D>::value))
   if (!wave_live) return;
   const int lr = qw0 + l32 - P;               // this lane's query row
   const bool row_ok = (unsigned)lr < (unsigned)Tq;
+  // log-sum-exp: the fp32 sum; output: the sum of its bf16 weights
   const float denom = FP32SUM ? both_halves_sum(st.l_run) : st.lsum[0];
+  const float onorm = MODE == kRowTempered ? st.lsum[0] : denom;
   if constexpr (SPLIT) {
     // partial results of this key range: (max, sum) or the row sum, and the
     // unnormalised share @ V; a range past a wave's diagonal leaves (-inf, 0, 0)
@@ -528,7 +538,7 @@ __global__ void __launch_bounds__(256, (RowOccupancy<MODE, D>::value))
   }
   if constexpr (MODE != kRowLse) {
     if (row_ok) {
-      const float inv = 1.0f / denom;
+      const float inv = 1.0f / onorm;
       __bf16 *O = reinterpret_cast<__bf16 *>(a.out) + qhead + (size_t)lr * D;
 #pragma unroll
       for (int i = 0; i < G::kOBlocks; ++i) {

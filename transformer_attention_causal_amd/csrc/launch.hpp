@@ -139,4 +139,18 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 
+// Rotary position embedding of `rows` rows per head (rope.hip): row t of head
+// bh is read at x[(bh * in_stride + t) * D] and written at
+// y[(bh * out_stride + t) * D], turned at position pos0 + t by freq[m] per
+// dimension pair (2m, 2m+1).
+struct RopeArgs {
+  const void *x;
+  void *y;
+  int BH, rows, D;
+  size_t in_stride, out_stride;
+  const float *freq;     // [D/2]
+  long pos0;
+};
+hipError_t launch_rope(const RopeArgs &a, int bf16, hipStream_t s);
+
 }  // namespace attn
