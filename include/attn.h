@@ -55,8 +55,13 @@ typedef enum {
   ATTN_EINVAL = -1,     /* bad argument: null/misaligned pointer, size <= 0, tau/eps out of range */
   ATTN_ENOTSUP = -2,    /* valid but unsupported: head dim, fp32 decode, not gfx950 */
   ATTN_EWORKSPACE = -3, /* workspace missing or smaller than *_workspace_bytes() */
-  ATTN_EHIP = -4        /* a HIP runtime call or kernel launch failed */
+  ATTN_EHIP = -4,       /* a HIP runtime call or kernel launch failed */
+  ATTN_ESCRATCH = -5    /* attn_fwd_noalloc: the shape needs more workspace than
+                           the library's fixed scratch array holds */
 } attn_status;
+
+/* Size of the fixed device scratch array behind attn_fwd_noalloc. */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 
 typedef enum { ATTN_TEMPERED = 0, ATTN_DILUTION = 1 } attn_mode;
 typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
@@ -102,6 +107,23 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, int B, i
                 int d, float tau, int mode, float eps, int dtype, void *workspace,
                 size_t workspace_bytes, float *lse_out, float *demand_out, float *rowsum_out,
                 void *hip_stream);
+
+/* attn_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * arguments are attn_fwd's without the workspace: the dilution workspace is
+ * a fixed array of ATTN_NOALLOC_SCRATCH_BYTES (128 MiB) inside the library,
+ * one per GPU, held from the time the library's code is loaded on that GPU
+ * until the process ends.  The call allocates, frees and clears nothing.
+ * Limit: shapes whose attn_fwd_workspace_bytes(...) exceeds that size (for
+ * dilution, about B*H*T*T/16 bytes: B*H = 16 heads at T = 8192 fit) return
+ * ATTN_ESCRATCH with nothing enqueued; ATTN_TEMPERED needs no workspace and
+ * has no limit beyond attn_fwd's.  Every call on one GPU shares that GPU's
+ * array and leaves its contents behind: calls on one GPU whose executions
+ * overlap (other streams, other host threads) race on it and must be
+ * ordered by the caller.  No kernel needs the array cleared between calls.
+ * Results are bit for bit those of attn_fwd with a workspace of its own. */
+int attn_fwd_noalloc(const void *q, const void *k, const void *v, void *out, int B, int H, int T,
+                     int d, float tau, int mode, float eps, int dtype, void *hip_stream);
 
 /* Bytes of device workspace attn_bwd and attn_bwd_ex need: five fp32 values
  * per query row (six for ATTN_F32 at d = 128), and for dilution the committed

@@ -117,7 +117,7 @@ def test_yarn_tau_against_page_table():
 
 
 def test_strerror_is_static_text():
-    for st in (0, -1, -2, -3, -4, 7):
+    for st in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(ab.attn_strerror(st), str) and ab.attn_strerror(st)
 
 
@@ -163,6 +163,34 @@ def fwd(**kw):
 ])
 def test_fwd_rejects_bad_arguments(kw, status):
     assert fwd(**kw) == status
+
+
+def noalloc(**kw):
+    args = dict(q=FAKE, k=FAKE + (1 << 32), v=FAKE + (2 << 32), out=FAKE + (3 << 32), B=1, H=16,
+                T=16384, d=64, tau=1.0, mode=1, eps=1e-6, dtype=1, hip_stream=None)
+    args.update(kw)
+    return ab.attn_fwd_noalloc(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), ab.ATTN_ESCRATCH),                      # 16 heads at T = 16384: ~270 MB
+    (dict(T=8193 * 2), ab.ATTN_ESCRATCH),
+    (dict(B=2, H=16, T=8192, d=128), ab.ATTN_ESCRATCH),
+    (dict(q=None, T=64), ab.ATTN_EINVAL),
+    (dict(q=None, mode=0), ab.ATTN_EINVAL),          # tempered: attn_fwd's checks
+    (dict(mode=3), ab.ATTN_EINVAL),
+    (dict(d=96, T=64), ab.ATTN_ENOTSUP),
+])
+def test_noalloc_rejects_before_the_device(kw, status):
+    """attn_fwd_noalloc refuses shapes beyond its fixed scratch array (and bad
+    arguments) on the host, before any device call."""
+    assert noalloc(**kw) == status
+
+
+def test_noalloc_limit_covers_16_heads_at_8k():
+    need = ab.attn_fwd_workspace_bytes(1, 16, 8192, 128, 1, 1)
+    assert 0 < need <= ab.ATTN_NOALLOC_SCRATCH_BYTES
+    assert ab.attn_fwd_workspace_bytes(1, 16, 16384, 64, 1, 1) > ab.ATTN_NOALLOC_SCRATCH_BYTES
 
 
 def test_workspace_sizes():

@@ -21,11 +21,13 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 # the CPU-side ABI tests can run against); by default the in-tree libattn.so.
 LIB_PATH = os.environ.get("ATTN_LIB") or os.path.join(PKG, "libattn.so")
 
-ATTN_OK, ATTN_EINVAL, ATTN_ENOTSUP, ATTN_EWORKSPACE, ATTN_EHIP = 0, -1, -2, -3, -4
+ATTN_OK, ATTN_EINVAL, ATTN_ENOTSUP, ATTN_EWORKSPACE, ATTN_EHIP, ATTN_ESCRATCH = 0, -1, -2, -3, -4, -5
+ATTN_NOALLOC_SCRATCH_BYTES = 128 << 20
 ATTN_TEMPERED, ATTN_DILUTION = 0, 1
 ATTN_F32, ATTN_BF16 = 0, 1
 
-EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_bytes", "attn_dilution_lse",
+EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_bytes", "attn_fwd_noalloc",
+            "attn_dilution_lse",
             "attn_dilution_committed", "attn_dilution_shares", "attn_bwd",
             "attn_bwd_ex", "attn_bwd_workspace_bytes", "attn_prefill", "attn_prefill_workspace_bytes",
             "attn_prefill_rope", "attn_prefill_rope_workspace_bytes",
@@ -57,6 +59,8 @@ def load() -> ctypes.CDLL:
         lib.attn_fwd_ex.restype = i
         lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, f, i, vp, sz, vp, vp, vp,
                                     vp]
+        lib.attn_fwd_noalloc.restype = i
+        lib.attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, f, i, vp]
         lib.attn_bwd.restype = i
         lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, f, i,
                                  vp, sz, vp]
@@ -110,6 +114,10 @@ def attn_fwd_ex(q, k, v, out, B, H, T, d, tau, mode, eps, dtype, workspace, work
                 lse_out, demand_out, rowsum_out, hip_stream) -> int:
     return load().attn_fwd_ex(q, k, v, out, B, H, T, d, tau, mode, eps, dtype, workspace,
                               workspace_bytes, lse_out, demand_out, rowsum_out, hip_stream)
+
+
+def attn_fwd_noalloc(q, k, v, out, B, H, T, d, tau, mode, eps, dtype, hip_stream) -> int:
+    return load().attn_fwd_noalloc(q, k, v, out, B, H, T, d, tau, mode, eps, dtype, hip_stream)
 
 
 def attn_bwd(q, k, v, out, dout, lse, rowsum, dq, dk, dv, B, H, T, d, tau, mode, eps, dtype,
@@ -280,6 +288,23 @@ def fwd(q, k, v, tau: float = 1.0, mode: int = ATTN_TEMPERED, eps: float = 1e-6,
                      _stream_handle(q.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_ex")
+    return out
+
+
+def fwd_noalloc(q, k, v, out, tau: float = 1.0, mode: int = ATTN_TEMPERED, eps: float = 1e-6):
+    """Run attn_fwd_noalloc on [B,H,T,d] tensors into the caller's ``out``
+    (nothing is allocated: the dilution workspace is the library's fixed
+    scratch array); returns ``out``."""
+    if q.dim() != 4 or out is None:
+        raise ValueError("q, k, v, out must share one [B,H,T,d] shape")
+    code = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _check_like(t, q, name)
+    B, H, T, d = q.shape
+    st = attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, T, d,
+                          float(tau), int(mode), float(eps), code, _stream_handle(q.device))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_noalloc")
     return out
 
 

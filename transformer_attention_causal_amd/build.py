@@ -13,7 +13,7 @@ LIB = os.path.join(PKG, "libattn.so")
 PEAKS_LIB = os.path.join(PKG, "libattn_peaks.so")
 
 SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "bwd_bf16.hip", "bwd_f32.hip",
-           "rope.hip"]
+           "noalloc.hip", "rope.hip"]
 PEAKS_SOURCES = ["peaks.hip"]
 
 # Packed fp32 VALU forms are disabled: every fp32 operation is a plain

@@ -25,6 +25,14 @@ int fail_hip(hipError_t e) {
   return ATTN_EHIP;
 }
 
+}  // namespace
+
+namespace attn {
+int record_hip_error(hipError_t e) { return fail_hip(e); }
+}  // namespace attn
+
+namespace {
+
 // gfx950 check, once per device.
 constexpr int kMaxDevices = 64;
 std::once_flag g_dev_once[kMaxDevices];
@@ -177,6 +185,19 @@ int check_fwd(const void *q, const void *k, const void *v, const void *out, int 
   }
   return ATTN_OK;
 }
+
+}  // namespace
+
+namespace attn {
+int validate_fwd(const void *q, const void *k, const void *v, const void *out, int B, int H, int T,
+                 int d, float tau, int mode, float eps, int dtype) {
+  if (!v || !out) return ATTN_EINVAL;
+  if (mode != ATTN_TEMPERED && mode != ATTN_DILUTION) return ATTN_EINVAL;
+  return check_fwd(q, k, v, out, B, H, T, d, tau, eps, dtype, nullptr, nullptr);
+}
+}  // namespace attn
+
+namespace {
 
 int check_workspace(int B, int H, int T, int d, int dtype, void *workspace,
                     size_t workspace_bytes, FwdWorkspace *ws) {
@@ -769,6 +790,9 @@ const char *attn_strerror(int status) {
              "gfx950)";
     case ATTN_EWORKSPACE: return "workspace missing, misaligned or too small";
     case ATTN_EHIP: return g_hip_error;
+    case ATTN_ESCRATCH:
+      return "shape needs more workspace than attn_fwd_noalloc's fixed scratch array holds "
+             "(ATTN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -153,4 +153,12 @@ struct RopeArgs {
 };
 hipError_t launch_rope(const RopeArgs &a, int bf16, hipStream_t s);
 
+// Record a HIP error as the text attn_strerror(ATTN_EHIP) reports; returns ATTN_EHIP.
+int record_hip_error(hipError_t e);
+
+// attn_fwd's host-side argument checks (everything but the workspace and the
+// device): ATTN_OK or the status attn_fwd would return for these arguments.
+int validate_fwd(const void *q, const void *k, const void *v, const void *out, int B, int H, int T,
+                 int d, float tau, int mode, float eps, int dtype);
+
 }  // namespace attn
