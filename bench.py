@@ -25,10 +25,14 @@ usual 2.5x of the forward's 4*d).  Then, also under ``components``:
 
 Printed: one JSON line.  ``value`` is the dilution forward's algorithmic
 TFLOP/s (4*d flops per causal (query, key) pair: q.k and the weighted v, once)
-over the measured time of its three launches; the tempered forward TFLOP/s and
-the decode step's HBM GB/s (K + V + demand read + demand write) are reported
-under ``components``.  Kernel durations come from HIP events recorded on the
-stream the library launches on, inside the timed region.
+over the sum of its three launches' median durations; ``roofline`` is that
+whole forward against the bf16 matrix peak, with each stage's figures under
+``components.dilution_fwd.stages``.  The tempered forward TFLOP/s and the
+decode step's HBM GB/s (K + V + demand read + demand write) are reported
+under ``components``.  Kernel durations are medians over the timed steps of
+HIP events recorded on the stream the library launches on, inside the timed
+region.  ``parity`` holds the device's errors against the oracle on the
+CPU baseline's sample (the full-size comparisons are the GPU tests').
 
 ``executed_mfma_busy_rocprof`` is rocprof's matrix-core busy fraction of the
 dilution stages (SQ_VALU_MFMA_BUSY_CYCLES over 4 x SQ_BUSY_CU_CYCLES), read
@@ -170,7 +174,8 @@ def measured_peaks(torch, dev, stream):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=20,
+                    help="timed steps; every figure is the median over them (>= 20 by default)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -257,7 +262,7 @@ def main():
     for e in evs:
         for j, n in enumerate(names):
             seg[n].append(e[j].elapsed_time(e[j + 1]))
-    ms = {n: float(np.mean(seg[n])) for n in names}
+    ms = {n: float(np.median(seg[n])) for n in names}
     ms_min = {n: float(np.min(seg[n])) for n in names}
     log("bench: per-launch ms " + json.dumps({n: round(ms[n], 4) for n in names}))
 
@@ -300,14 +305,14 @@ def main():
     for i in range(args.steps):
         bwd_step(bevs[i])
     torch.cuda.synchronize()
-    bwd_ms = {"dilution_bwd": float(np.mean([e[0].elapsed_time(e[1]) for e in bevs])),
-              "tempered_bwd": float(np.mean([e[1].elapsed_time(e[2]) for e in bevs])),
-              "dilution_bwd_fwd_table": float(np.mean([e[2].elapsed_time(e[3]) for e in bevs]))}
+    bwd_ms = {"dilution_bwd": float(np.median([e[0].elapsed_time(e[1]) for e in bevs])),
+              "tempered_bwd": float(np.median([e[1].elapsed_time(e[2]) for e in bevs])),
+              "dilution_bwd_fwd_table": float(np.median([e[2].elapsed_time(e[3]) for e in bevs]))}
     log("bench: backward ms " + json.dumps({n: round(x, 4) for n, x in bwd_ms.items()}))
     del bws, grads
 
     def time_launches(fn, n_marks):
-        """Mean ms between consecutive marks of ``fn(events)`` over the timed
+        """Median ms between consecutive marks of ``fn(events)`` over the timed
         iterations (warm-up iterations first)."""
         for _ in range(args.warmup):
             fn(None)
@@ -317,7 +322,7 @@ def main():
         for i in range(args.steps):
             fn(evs_[i])
         torch.cuda.synchronize()
-        return [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs_]))
+        return [float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs_]))
                 for j in range(n_marks - 1)]
 
     # ------------------------------------------------------- chunked prefill
@@ -456,8 +461,24 @@ def main():
                  + 2.0 * dw.S * dw.H * dw.L * 4             # demand read + write, fp32
                  + 2.0 * dw.S * dw.H * dw.d * 2)            # query in, output out
     dec_gbps = dec_bytes / (ms["decode"] * 1e-3) / 1e9
-    shares_tflops = flops / (ms["dil_shares"] * 1e-3) / 1e12
     flops8 = 4.0 * w8.d * causal_pairs(w8.B, w8.H, w8.T)
+    # per-stage figures of the dilution forward: each stage's share of the
+    # forward's time, its executed matrix-core busy fraction and measured HBM
+    # bytes per launch (counter summaries), and the forward's algorithmic
+    # flops over the stage's own time (what the forward would reach if every
+    # stage ran as fast as this one)
+    stage_kernels = {"dil_lse": "rows_bf16_kernel<kRowLse>",
+                     "dil_committed": "colsum_bf16_kernel",
+                     "dil_shares": "rows_bf16_kernel<kRowShare>"}
+    stages_out = {}
+    for n, kname in stage_kernels.items():
+        stages_out[n] = {
+            "kernel": kname, "ms": round(ms[n], 4), "min_ms": round(ms_min[n], 4),
+            "share_of_forward": round(ms[n] / dil_ms, 4),
+            "executed_mfma_busy_rocprof": measured_busy(kname, FWD_SOURCES),
+            "traffic": measured_traffic(kname, FWD_SOURCES)}
+    tr = [stages_out[n]["traffic"] for n in stage_kernels]
+    fwd_traffic = sum(tr) if all(t is not None for t in tr) else None
 
     result = {
         "metric": METRIC,
@@ -480,11 +501,16 @@ def main():
         },
         "components": {
             "dilution_fwd": {"ms": round(dil_ms, 4), "tflops": round(dil_tflops, 3),
-                             "stage_ms": {n: round(ms[n], 4) for n in names[:3]},
                              "frac_of_bf16_peak": round(dil_tflops / PEAK_BF16_TFLOPS, 4),
+                             "stages": stages_out,
                              "executed_mfma_busy_rocprof": measured_busy("dilution_fwd", FWD_SOURCES)},
             "tempered_fwd": {"ms": round(ms["tempered"], 4), "tflops": round(tmp_tflops, 3),
-                             "frac_of_bf16_peak": round(tmp_tflops / PEAK_BF16_TFLOPS, 4)},
+                             "frac_of_bf16_peak": round(tmp_tflops / PEAK_BF16_TFLOPS, 4),
+                             "kernel": "rows_bf16_kernel<kRowTempered>",
+                             "executed_mfma_busy_rocprof": measured_busy(
+                                 "rows_bf16_kernel<kRowTempered>", FWD_SOURCES),
+                             "traffic": measured_traffic("rows_bf16_kernel<kRowTempered>",
+                                                         FWD_SOURCES)},
             "decode_step": {"ms": round(ms["decode"], 4), "gbps": round(dec_gbps, 2),
                             "bytes": dec_bytes,
                             "frac_of_hbm_peak": round(dec_gbps / PEAK_HBM_GBPS, 4)},
@@ -520,16 +546,19 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "rows_bf16_kernel<kRowShare> (dilution stage 3: shares and share@V)",
-            "achieved": round(shares_tflops, 3),
+            "kernel": "dilution forward, its three launches: rows_bf16_kernel<kRowLse> "
+                      "(log-sum-exp), colsum_bf16_kernel (committed demand), "
+                      "rows_bf16_kernel<kRowShare> (shares and share@V)",
+            "achieved": round(dil_tflops, 3),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(shares_tflops / PEAK_BF16_TFLOPS, 4),
+            "frac": round(dil_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": fwd_traffic,
             "measured_peak": peaks["mfma_bf16_tflops"],
-            "frac_of_measured_peak": round(shares_tflops / peaks["mfma_bf16_tflops"], 4),
-            "executed_mfma_busy_rocprof": measured_busy("rows_bf16_kernel<kRowShare>", FWD_SOURCES),
-            "traffic": measured_traffic("rows_bf16_kernel<kRowShare>", FWD_SOURCES),
-            "units": f"{causal_pairs(w.B, w.H, w.T)} causal pairs x {4 * d} flops",
+            "frac_of_measured_peak": round(dil_tflops / peaks["mfma_bf16_tflops"], 4),
+            "executed_mfma_busy_rocprof": measured_busy("dilution_fwd", FWD_SOURCES),
+            "units": f"{causal_pairs(w.B, w.H, w.T)} causal pairs x {4 * d} flops (q.k and the "
+                     f"weighted v, once) over the sum of the three launches' median durations",
         },
         "roofline_decode": {
             "bound": "hbm",
@@ -547,49 +576,115 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_heads, tau_t, dw)
+        # the device's results on the oracle's sample, for the parity figures:
+        # the first heads of the 16K forward (both operators, with LSE and
+        # final demand) and one decode step from the initial demand on the
+        # first sequences of the device's own cache
+        heads = list(range(min(args.cpu_heads, w.H)))
+        ns = 4
+        lse_s = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=dev)
+        dem_s = torch.empty_like(lse_s)
+        ab.fwd(q, k, v, tau=1.0, mode=ab.ATTN_DILUTION, eps=w.eps, out=out_d, workspace=ws,
+               lse_out=lse_s, demand_out=dem_s)
+        ab.fwd(q, k, v, tau=tau_t, mode=ab.ATTN_TEMPERED, out=out_t)
+        dem0 = torch.from_numpy(decode_initial_demand(dw.S, dw.H, dw.L, dw.seed,
+                                                      dw.demand_max)).to(dev)
+        ab.decode(qs[0], kc, vc, dem0, tau=dw.tau, eps=dw.eps, out=dec_out, workspace=dws)
+        torch.cuda.synchronize()
+        got = {"dil": out_d[:, heads].float().cpu().numpy(),
+               "dil_lse": lse_s[:, heads].cpu().numpy(),
+               "dil_dem": dem_s[:, heads].cpu().numpy(),
+               "tmp": out_t[:, heads].float().cpu().numpy(),
+               "dec": dec_out[:ns].float().cpu().numpy(),
+               "dec_dem": dem0[:ns].cpu().numpy(),
+               "kc": kc[:ns].contiguous().view(torch.int16).cpu().numpy().view(np.uint16),
+               "vc": vc[:ns].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)}
+        del dem0
+        result["cpu_baseline"], result["parity"] = cpu_baseline(inp, w, heads, tau_t, dw, ns, got)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(inp, w, nheads, tau_t, dw):
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _parity(got, ref):
+    import numpy as np
+
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    diff = got - ref
+    return {"max_abs": float(np.max(np.abs(diff))),
+            "rel_rms": float(np.linalg.norm(diff) / np.linalg.norm(ref))}
+
+
+def cpu_baseline(inp, w, heads, tau_t, dw, ns, got):
     """The fp64 oracle (untuned) on a bounded sample of the same workloads:
-    the dilution forward (the headline figure), and beside it the tempered
-    forward on the same heads and one decode step over a few sequences."""
+    the dilution forward (the headline figure) on the first heads of the 16K
+    workload, and beside it the tempered forward on the same heads and one
+    decode step over the first sequences of the device's cache.  The oracle's
+    results on that sample also give the device's parity figures."""
     import numpy as np
 
     import oracle
-    from transformer_attention_causal_amd.workloads import (decode_cache_host,
-                                                            decode_initial_demand,
+    from transformer_attention_causal_amd.workloads import (decode_initial_demand,
                                                             decode_queries)
 
-    heads = list(range(min(nheads, w.H)))
     log(f"bench: cpu baseline (oracle) on {len(heads)} head(s) of T={w.T} dilution")
     sub = [oracle.Bf16(np.ascontiguousarray(x[:, heads])) for x in (inp.q, inp.k, inp.v)]
     t0 = time.perf_counter()
-    oracle.dilution_fwd(*sub, 1.0, w.eps)
+    ref_d, lse_d, dem_d = oracle.dilution_fwd(*sub, 1.0, w.eps)
     dt = time.perf_counter() - t0
     flops = 4.0 * w.d * causal_pairs(1, len(heads), w.T)
     t0 = time.perf_counter()
-    oracle.tempered_fwd(*sub, tau_t)
+    ref_t, _ = oracle.tempered_fwd(*sub, tau_t)
     dt_t = time.perf_counter() - t0
-    # one decode step: the first sequences of a cache drawn by the same recipe
-    ns = 4
-    kc, vc = decode_cache_host(ns, dw.H, dw.L, dw.d, dw.seed)
-    dem = decode_initial_demand(ns, dw.H, dw.L, dw.seed).astype(np.float64)
-    qd = decode_queries(1, ns, dw.H, dw.d, dw.seed)[0]
+    # one decode step: the first sequences of the device's cache, from the
+    # initial demand, with the first step's queries
+    dem = decode_initial_demand(dw.S, dw.H, dw.L, dw.seed, dw.demand_max)[:ns].astype(np.float64)
+    qd = np.ascontiguousarray(decode_queries(1, dw.S, dw.H, dw.d, dw.seed)[0][:ns])
     t0 = time.perf_counter()
-    oracle.dilution_decode_step(oracle.Bf16(qd), oracle.Bf16(kc), oracle.Bf16(vc), dem, dw.tau,
-                                dw.eps)
+    ref_dec = oracle.dilution_decode_step(oracle.Bf16(qd), oracle.Bf16(got["kc"]),
+                                          oracle.Bf16(got["vc"]), dem, dw.tau, dw.eps)
     dt_d = time.perf_counter() - t0
     dec_bytes = ns * dw.H * (2.0 * dw.L * dw.d * 2 + 2.0 * dw.L * 4 + 2.0 * dw.d * 2)
     log(f"bench: cpu baseline {dt:.2f} s dilution, {dt_t:.2f} s tempered, {dt_d:.3f} s decode")
-    return {
+    dem_tot = np.max(np.abs(got["dil_dem"].astype(np.float64).sum(-1) / w.T - 1.0))
+    dec_tot = np.max(np.abs(got["dec_dem"].astype(np.float64).sum(-1) / dem.sum(-1) - 1.0))
+    parity = {
+        "bars": {"bf16_max_abs": 2e-2, "bf16_rel_rms": 1e-2, "demand_total_rel": 1e-4},
+        "dilution_t16k": {"heads": heads, "rows": "all",
+                          **_parity(got["dil"], ref_d),
+                          "lse_max_abs": float(np.max(np.abs(got["dil_lse"] - lse_d))),
+                          "demand_total_rel": float(dem_tot),
+                          "demand_per_key_max_abs": float(np.max(np.abs(got["dil_dem"] - dem_d)))},
+        "tempered_t16k": {"heads": heads, "rows": "all", "tau": tau_t,
+                          **_parity(got["tmp"], ref_t)},
+        "decode_32k": {"sequences": ns, "heads": dw.H, "step": "first, from the initial demand",
+                       **_parity(got["dec"], ref_dec),
+                       "demand_total_rel": float(dec_tot),
+                       "demand_per_key_max_abs": float(np.max(np.abs(got["dec_dem"] - dem)))},
+        "full_coverage": "tests/test_gpu_workloads.py: every row of every head at T=16384, "
+                         "every row of head 0 at T=131072, every decode pair at every step",
+    }
+    threads = oracle.num_threads()
+    base = {
         "value": round(flops / dt / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": oracle.num_threads(),
+        "cores": threads,
+        "host_cores_available": len(os.sched_getaffinity(0)),
+        "cpu_model": _cpu_model(),
         "kind": "oracle",
         "sample": f"dilution forward, {len(heads)} of {w.H} heads at T={w.T} (all rows), "
-                  f"{dt:.2f} s, fp64",
+                  f"{dt:.2f} s, fp64, {threads} OpenMP threads; a bounded sample, not the "
+                  f"whole workload",
         "also": {
             "tempered_fwd": {"value": round(flops / dt_t / 1e12, 6), "unit": "TFLOP/s",
                              "sample": f"the same {len(heads)} heads, tau={tau_t:.7f}, "
@@ -599,6 +694,7 @@ def cpu_baseline(inp, w, nheads, tau_t, dw):
                                       f"{dw.L} keys, {dt_d:.3f} s"},
         },
     }
+    return base, parity
 
 
 if __name__ == "__main__":
