@@ -45,7 +45,6 @@
 namespace attn {
 
 constexpr int kBM = 128;        // query rows per workgroup (row kernels)
-constexpr float kRescaleSlack = 8.0f;      // log2 units the running max may lag
 constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64: largest tile sum kept
 
 // Per-wave state of the row kernels.
@@ -105,12 +104,13 @@ __device__ __forceinline__ void st_weights(const f32x16 *s, float m_run, int qre
 }
 
 // Tempered softmax / pass-1 update for one 64-key tile (S^T orientation).
-// The running max m_run is lazy.  With fp32 row sums the tile is weighted
-// against the current m_run directly and the max is only taken when a lane's
-// tile sum leaves [0, 2^64] (weights that large are still exact in fp32 and
-// bf16; an overflow or the first tile, where m_run = -inf, shows up there as
-// inf).  Otherwise the tile max is taken first and m_run moves when it is
-// exceeded by more than kRescaleSlack.
+// The running max m_run is lazy: the tile is weighted against the current
+// m_run directly, and the tile max is only taken (and the tile weighted
+// again) when a lane's tile sum leaves [0, 2^64].  Weights that large are
+// still exact in fp32 and bf16; an overflow, or the first tile, where
+// m_run = -inf, shows up there as inf or NaN.  The tile sum is the fp32 one
+// (FP32SUM) or the matrix-core row sum of the bf16 weights, which the output
+// normaliser accumulates anyway.
 template <int MODE, bool FP32SUM, bool DIAG, int D>
 __device__ __forceinline__ void st_tile(RowState<D> &st, const bf16x8 *qf, const bf16x8 &sel,
                                         const __bf16 *kt_lds, const __bf16 *vt_lds, int kb,
@@ -128,15 +128,15 @@ __device__ __forceinline__ void st_tile(RowState<D> &st, const bf16x8 *qf, const
   if constexpr (FP32SUM) {
     float p[32];
     st_weights<DIAG>(s, st.m_run, qrel, h, c2, p);
-    float ts = 0.0f;
+    float ts = p[0];   // the weights are >= +0: the same bits as 0 + p[0] + ...
 #pragma unroll
-    for (int i = 0; i < 32; ++i) ts += p[i];
+    for (int i = 1; i < 32; ++i) ts += p[i];
     if (__ballot(!(ts <= kSumLimit)) != 0ull) {
       st_rescale<MODE, FP32SUM, DIAG, D>(st, s, qrel, h, c2);
       st_weights<DIAG>(s, st.m_run, qrel, h, c2, p);
-      ts = 0.0f;
+      ts = p[0];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) ts += p[i];
+      for (int i = 1; i < 32; ++i) ts += p[i];
     }
     st.l_run += ts;
     if constexpr (MODE == kRowTempered) {
@@ -151,32 +151,36 @@ __device__ __forceinline__ void st_tile(RowState<D> &st, const bf16x8 *qf, const
       }
     }
   } else {
-    float tmax = -INFINITY;
+    // the bf16 weights and their matrix-core row sum, the output's normaliser
+    f32x4 tsum;
+    bf16x8 pf[4];
+    auto weigh = [&]() {
+      const float mneg = -st.m_run;
+      tsum = zero4();
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 2; ++t) {
+        float p[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float v = (!DIAG || 32 * t + acc_row(r, h) <= qrel) ? s[t][r] : -INFINITY;
-        tmax = fmaxf(tmax, v);
+        for (int r = 0; r < 16; ++r) {
+          float e = fast_exp2(__builtin_fmaf(s[t][r], c2, mneg));
+          if (DIAG && 32 * t + acc_row(r, h) > qrel) e = 0.0f;
+          p[r] = e;
+        }
+        pf[2 * t] = pack8(p);
+        pf[2 * t + 1] = pack8(p + 8);
+        tsum = mfma16(sel, pf[2 * t], tsum);
+        tsum = mfma16(sel, pf[2 * t + 1], tsum);
       }
-    }
-    tmax = both_halves_max(tmax);
-    if (__ballot(tmax * c2 > st.m_run + kRescaleSlack) != 0ull)
+    };
+    weigh();
+    if (__ballot(!(tsum[0] <= kSumLimit)) != 0ull) {
       st_rescale<MODE, FP32SUM, DIAG, D>(st, s, qrel, h, c2);
-    const float mneg = -st.m_run;
+      weigh();
+    }
+    st.lsum += tsum;
+    if constexpr (MODE == kRowTempered) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float e = fast_exp2(__builtin_fmaf(s[t][r], c2, mneg));
-        if (DIAG && 32 * t + acc_row(r, h) > qrel) e = 0.0f;
-        p[r] = e;
-      }
-      const bf16x8 pf0 = pack8(p), pf1 = pack8(p + 8);
-      st.lsum = mfma16(sel, pf0, st.lsum);
-      st.lsum = mfma16(sel, pf1, st.lsum);
-      if constexpr (MODE == kRowTempered) pv_update_d<D>(st.o, vt_lds, t, l32, h, pf0, pf1);
+      for (int t = 0; t < 2; ++t) pv_update_d<D>(st.o, vt_lds, t, l32, h, pf[2 * t], pf[2 * t + 1]);
     }
   }
 }
