@@ -129,7 +129,8 @@ int attn_fwd_noalloc(const void *q, const void *k, const void *v, void *out, int
  * per query row (six for ATTN_F32 at d = 128), and for dilution the committed
  * demand and the later rows' gradient sums per (32-row query block, key):
  * B*H*16*n*(n+1) 32-bit values each, n = ceil(T/32), plus a [B,H,T,d] array
- * of `dtype`.  0 for an unsupported shape, mode, head dimension or dtype. */
+ * of `dtype` and, for ATTN_BF16, a [B,H,T,d] fp32 array.  0 for an
+ * unsupported shape, mode, head dimension or dtype. */
 size_t attn_bwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype);
 
 /* Exact gradients of either operator (DilutionAttention v0.1.0: the release's

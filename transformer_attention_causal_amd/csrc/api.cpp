@@ -550,11 +550,12 @@ namespace {
 // delta/r, rho, then <q_i, dQ_i / c> in one partial sum per slice of d that
 // the dq kernel splits the head dimension into), then for dilution the
 // committed demand and the later blocks' gradient sums, per (32-row block,
-// key), and the [B,H,T,d] array (storage type) of softmax-weighted keys.
+// key), the [B,H,T,d] array (storage type) of softmax-weighted keys and, for
+// bf16, the fp32 [B,H,T,d] partial key gradients sum_i p_ij dp_ij q_i.
 constexpr size_t kBwdFixedRowArrays = 4;
 struct BwdWorkspace {
   int tslices;
-  size_t row_bytes, cin_bytes, gin_bytes, pk_bytes, total;
+  size_t row_bytes, cin_bytes, gin_bytes, pk_bytes, dkp_bytes, total;
 };
 
 // The bf16 dq kernel covers all of d in one workgroup; the fp32 one splits d
@@ -570,8 +571,10 @@ bool bwd_workspace(int B, int H, int T, int d, int mode, int dtype, BwdWorkspace
   ws->gin_bytes = mode == ATTN_DILUTION ? round_up(BH * attn::gin_floats_per_head(T) * 4) : 0;
   const size_t esz = dtype == ATTN_BF16 ? 2 : 4;
   ws->pk_bytes = mode == ATTN_DILUTION ? round_up(BH * (size_t)T * d * esz) : 0;
+  ws->dkp_bytes =
+      mode == ATTN_DILUTION && dtype == ATTN_BF16 ? round_up(BH * (size_t)T * d * sizeof(float)) : 0;
   ws->total = (kBwdFixedRowArrays + ws->tslices) * ws->row_bytes + ws->cin_bytes + ws->gin_bytes +
-              ws->pk_bytes;
+              ws->pk_bytes + ws->dkp_bytes;
   return true;
 }
 
@@ -679,6 +682,7 @@ int attn_bwd_ex(const void *q, const void *k, const void *v, const void *out, co
     a.cin_given = fwd_cin ? 1 : 0;
     a.gin = reinterpret_cast<float *>(wtail + ws.cin_bytes);
     a.pk = wtail + ws.cin_bytes + ws.gin_bytes;
+    if (ws.dkp_bytes) a.dkp = reinterpret_cast<float *>(wtail + ws.cin_bytes + ws.gin_bytes + ws.pk_bytes);
   }
   a.BH = B * H;
   a.T = T;

@@ -22,16 +22,22 @@
 // D = 128 the dQ and dK/dV kernels run one workgroup per CU, which doubles
 // the registers per lane for the doubled operands and accumulators.
 //
-// Passes (dilution; tempered skips 2, 3 and 4):
+// Passes (dilution; tempered runs 1, 5, 5b and 3 only, dK/dV top-down):
 //   1 bwd_prep_kernel   per row: log2-domain lse, 1/r, delta/r
 //   2 colsum_bf16_kernel (the forward's) committed demand per 32-row block
-//   3 bwd_gsum_kernel   per key, walking 32-row blocks from the last one up:
-//                       the sum of g over every later block (G's block part)
+//   3 bwd_dkdv_kernel   per 32 keys, walking 32-row blocks from the last one
+//                       up: the sum of g over every later block (G's block
+//                       part, carried in a register and stored for pass 5),
+//                       dV, and dK' = sum_i p_ij dp_ij q_i (fp32 workspace)
 //   4 rows_bf16_kernel  (the tempered forward with V := K) PK_i = sum_j p_ij k_j
 //   5 bwd_dq_kernel     per 32 query rows: X_i = sum_j p_ij dp_ij k_j and rho,
 //                       then dQ_i = c (X_i - rho_i PK_i) and <q_i, dQ_i / c>
 //   5b bwd_dtau_kernel  (when dL/dtau is asked for) per head: the rows' sum
-//   6 bwd_dkdv_kernel   per 32 keys: dK, dV
+//   6 bwd_dkrho_kernel  per 32 keys: dK_j = c (dK'_j - sum_i p_ij rho_i q_i)
+// Splitting dK_j = c sum_i p_ij (dp_ij - rho_i) q_i at rho lets the dK/dV
+// pass run before rho is known (rho needs every key of a row, and dp needs
+// G, the column sums that pass carries), so one column pass over all pairs
+// does both G and dK/dV.
 // Both in-block scans (the column prefix inside D and the column suffix
 // inside G) are matrix-core products against constant triangular operands,
 // as in the forward shares pass.
@@ -150,7 +156,7 @@ template <int D>
 struct ColBlock {
   __bf16 q[32 * Geom<D>::kKRow];
   __bf16 g[32 * Geom<D>::kKRow];
-  float lse2[32], invr[32], dri[32], rho[32];
+  float lse2[32], invr[32], dri[32];
 };
 
 // Bids of a block in the S layout; on the diagonal block rows before the key
@@ -192,147 +198,12 @@ __device__ __forceinline__ void col_scores(const ColBlock<D> &b, const bf16x8 *k
   }
 }
 
-// dilution quantities of one block (S layout): p, 1/D (clamped), sigma,
-// dsigma and g = dsigma sigma / D.
-struct ColTerms {
-  float p[16], invd[16], sg[16], dsg[16], g[16];
-};
-
-template <bool DIAG, bool CLAMP, int D>
-__device__ __forceinline__ void col_terms(const f32x16 &s, const f32x16 &da, const ColBlock<D> &b,
-                                          const ScanConsts &sc, uint32_t cin_word, float c2,
-                                          int l32, int h, ColTerms &t) {
-  float lq[16], iq[16], rq[16];
-  col_rowvals(b.lse2, h, lq);
-  col_rowvals(b.invr, h, iq);
-  col_rowvals(b.dri, h, rq);
-  col_bids<DIAG>(s, lq, c2, l32, h, t.p);
-  const bf16x8 pa0 = pack8(t.p), pa1 = pack8(t.p + 8);
-  // D = committed + eps + inclusive column prefix of the bids (S layout)
-  f32x16 d = mfma32(sc.le[0], pa0, zero16());
-  d = mfma32(sc.le[1], pa1, d);
-  d = mfma32(sc.ones, word_operand(cin_word), d);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float invd = inv_denominator<CLAMP>(d[r]);
-    t.invd[r] = invd;
-    t.sg[r] = t.p[r] * invd;
-    t.dsg[r] = __builtin_fmaf(da[r], iq[r], -rq[r]);
-    t.g[r] = t.dsg[r] * t.sg[r] * invd;
-  }
-}
-
-// Pass 3: sums of g over the blocks below each block, walking up two 32-row
-// blocks (one 64-row LDS tile) per barrier.
-template <int D, bool CLAMP>
-__global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdArgs a, int nqs) {
-  constexpr int kRowChunks = D / 8;              // 16-byte chunks per row
-  constexpr int kPairLoads = 64 * kRowChunks / 256;   // per thread, per tensor
-  __shared__ __attribute__((aligned(16))) ColBlock<D> sb[2][2];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
-  const int bh = blockIdx.x % a.BH;
-  const int kb = blockIdx.x / a.BH;
-  const float c2 = a.c2 * head_tau(a, bh);
-  const int T = a.T;
-  const int kw0 = kb * kColKeys + 32 * w;
-  const bool wave_live = kw0 < T;
-  const int key = kw0 + l32;
-  const size_t head = (size_t)bh * T * D;
-  const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + head;
-  const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + head;
-  const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + head;
-  const __bf16 *G = reinterpret_cast<const __bf16 *>(a.dout) + head;
-  const float *L2 = a.lse2 + (size_t)bh * T;
-  const float *IR = a.invr + (size_t)bh * T;
-  const float *DR = a.dri + (size_t)bh * T;
-  const uint32_t *cin = reinterpret_cast<const uint32_t *>(a.cin) + (size_t)bh * cin_floats_per_head(T, 0);
-  uint32_t *gin = reinterpret_cast<uint32_t *>(a.gin) + (size_t)bh * gin_floats_per_head(T);
-  const uint32_t eps_word = split2_bf16(fmaxf(a.eps, FLT_MIN));
-
-  bf16x8 kf[Geom<D>::kChunks], vf[Geom<D>::kChunks];
-#pragma unroll
-  for (int c = 0; c < Geom<D>::kChunks; ++c) {
-    kf[c] = __builtin_bit_cast(bf16x8, load_row_chunk<D>(K, key, T, 2 * c + h));
-    vf[c] = __builtin_bit_cast(bf16x8, load_row_chunk<D>(V, key, T, 2 * c + h));
-  }
-  const ScanConsts sc = scan_consts(l32, h);
-  __builtin_amdgcn_s_waitcnt(0);
-
-  // walk pairs of 32-row blocks (2P, 2P + 1), last pair first
-  const int qs_lo = (kb * kColKeys) / 32;
-  const int p_lo = qs_lo / 2, p_hi = (nqs - 1) / 2;
-  u32x4 qreg[kPairLoads], greg[kPairLoads];
-  float lreg = 0.0f, ireg = 0.0f, rreg = 0.0f;
-  auto load_pair = [&](int P) {             // 64 P < T for every pair loaded
-    const int row0 = 64 * P;
-    const int bytes = (T - row0) * (D * 2);
-    const auto rq = make_rsrc(Q + (size_t)row0 * D, bytes);
-    const auto rg = make_rsrc(G + (size_t)row0 * D, bytes);
-#pragma unroll
-    for (int i = 0; i < kPairLoads; ++i) {
-      qreg[i] = buf_load16(rq, 16u * (tid + 256 * i));
-      greg[i] = buf_load16(rg, 16u * (tid + 256 * i));
-    }
-    if (tid < 64) {
-      const int row = row0 + tid;
-      const bool ok = row < T;
-      const int rr = ok ? row : T - 1;
-      lreg = ok ? L2[rr] : kNoRow;
-      ireg = ok ? IR[rr] : 0.0f;
-      rreg = ok ? DR[rr] : 0.0f;
-    }
-  };
-  auto store_pair = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kPairLoads; ++i) {
-      // chunk u of the 64-row tile: row u / kRowChunks (block row / 32)
-      const int u = tid + 256 * i, row = u / kRowChunks, ch = u % kRowChunks;
-      const int off = (row & 31) * Geom<D>::kKRow + ch * 8;
-      *reinterpret_cast<u32x4 *>(&sb[buf][row >> 5].q[off]) = qreg[i];
-      *reinterpret_cast<u32x4 *>(&sb[buf][row >> 5].g[off]) = greg[i];
-    }
-    if (tid < 64) {
-      sb[buf][tid >> 5].lse2[tid & 31] = lreg;
-      sb[buf][tid >> 5].invr[tid & 31] = ireg;
-      sb[buf][tid >> 5].dri[tid & 31] = rreg;
-    }
-  };
-
-  float running = 0.0f;   // sum of g over this half-lane's rows in blocks below
-  load_pair(p_hi);
-  store_pair(0);
-  __syncthreads();
-  for (int P = p_hi; P >= p_lo; --P) {
-    const int buf = (p_hi - P) & 1;
-    if (P - 1 >= p_lo) load_pair(P - 1);
-#pragma unroll
-    for (int i = 1; i >= 0; --i) {
-      const int qs = 2 * P + i;
-      if (qs >= nqs || qs < qs_lo) continue;
-      if (wave_live && 32 * qs + 31 >= kw0) {
-        f32x16 s, da;
-        col_scores(sb[buf][i], kf, vf, l32, h, s, da);
-        const uint32_t cw = key < 32 * qs ? cin[cin_block_offset(qs, 0) + key] : eps_word;
-        ColTerms t;
-        if (32 * qs == kw0) col_terms<true, CLAMP>(s, da, sb[buf][i], sc, cw, c2, l32, h, t);
-        else col_terms<false, CLAMP>(s, da, sb[buf][i], sc, cw, c2, l32, h, t);
-        float part = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) part += t.g[r];
-        const float below = both_halves_sum(running);
-        if (h == 0 && key < T) gin[(size_t)16 * qs * (qs + 1) + key] = split2_bf16(below);
-        running += part;
-      }
-    }
-    if (P - 1 >= p_lo) store_pair(buf ^ 1);
-    __syncthreads();
-  }
-}
-
-// Pass 5: dK and dV for this wave's keys.  The transposed Q and dO blocks
+// Pass 3: dK and dV for this wave's keys.  The transposed Q and dO blocks
 // (dim-major) are the A operands of dK^T += Q^T dS and dV^T += dO^T a; the
-// packed dS and a (S layout) are their B operands.
+// packed dS and a (S layout) are their B operands.  Dilution takes p dp in
+// place of dS (rho enters in pass 6) and, walking bottom-up, carries in
+// `running` each half-lane's sum of g over the blocks below; `gin_word`
+// returns that sum over both halves (bf16 pair) for the dQ pass.
 template <int D>
 struct ColBlockT {
   __bf16 qt[D * kTRow];
@@ -343,8 +214,8 @@ template <bool DIL, bool DIAG, bool CLAMP, int D>
 __device__ __forceinline__ void dkdv_block(const ColBlock<D> &b, const ColBlockT<D> &bt,
                                            const bf16x8 *kf, const bf16x8 *vf,
                                            const ScanConsts &sc, uint32_t cin_word,
-                                           uint32_t gin_word, float c2, int l32, int h,
-                                           f32x16 *dkt, f32x16 *dvt) {
+                                           float &running, uint32_t &gin_word, float c2, int l32,
+                                           int h, f32x16 *dkt, f32x16 *dvt) {
   f32x16 s, da;
   col_scores(b, kf, vf, l32, h, s, da);
   float ds[16], aw[16];
@@ -377,16 +248,16 @@ __device__ __forceinline__ void dkdv_block(const ColBlock<D> &b, const ColBlockT
       g[r] = dsg[r] * sg[r] * invd[r];
     }
     // G = gradient terms of the later blocks + inclusive suffix in this one
+    gin_word = split2_bf16(both_halves_sum(running));
     f32x16 G = mfma32(sc.ge[0], pack8(g), zero16());
     G = mfma32(sc.ge[1], pack8(g + 8), G);
     G = mfma32(sc.ones, word_operand(gin_word), G);
-    float pq[16];
-    col_rowvals(b.rho, h, pq);
+    float part = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float dp = __builtin_fmaf(dsg[r], invd[r], -G[r]);
-      ds[r] = p[r] * (dp - pq[r]);
-    }
+    for (int r = 0; r < 16; ++r) part += g[r];
+    running += part;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ds[r] = p[r] * __builtin_fmaf(dsg[r], invd[r], -G[r]);
   } else {
     float lq[16], rq[16];
     col_rowvals(b.lse2, h, lq);
@@ -445,11 +316,11 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
   const float *L2 = a.lse2 + (size_t)bh * T;
   const float *IR = a.invr + (size_t)bh * T;
   const float *DR = a.dri + (size_t)bh * T;
-  const float *RH = a.rho + (size_t)bh * T;
-  const uint32_t *cin = nullptr, *gin = nullptr;
+  const uint32_t *cin = nullptr;
+  uint32_t *gin = nullptr;
   if constexpr (DIL) {
     cin = reinterpret_cast<const uint32_t *>(a.cin) + (size_t)bh * cin_floats_per_head(T, 0);
-    gin = reinterpret_cast<const uint32_t *>(a.gin) + (size_t)bh * gin_floats_per_head(T);
+    gin = reinterpret_cast<uint32_t *>(a.gin) + (size_t)bh * gin_floats_per_head(T);
   }
   const uint32_t eps_word = split2_bf16(fmaxf(a.eps, FLT_MIN));
 
@@ -483,7 +354,7 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
   // u = tid + 256 i covers rows 2 kp, 2 kp + 1 (kp = u & 15) and chunk
   // (u >> 4) % kRowChunks of Q (when (u >> 4) < kRowChunks) or dO.
   u32x4 qreg[kBlkLoads], greg[kBlkLoads], tr0[kBlkLoads], tr1[kBlkLoads];
-  float lreg = 0.0f, ireg = 0.0f, rreg = 0.0f, hreg = 0.0f;
+  float lreg = 0.0f, ireg = 0.0f, rreg = 0.0f;
   const int kp = tid & 15;
   auto load_block = [&](int qs) {
     const int row0 = 32 * qs;
@@ -506,7 +377,6 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
       lreg = ok ? L2[rr] : kNoRow;
       ireg = ok ? IR[rr] : 0.0f;
       rreg = ok ? DR[rr] : 0.0f;
-      hreg = (DIL && ok) ? RH[rr] : 0.0f;
     }
   };
   auto store_block = [&](int buf) {
@@ -523,23 +393,25 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
       sb[buf].lse2[tid] = lreg;
       sb[buf].invr[tid] = ireg;
       sb[buf].dri[tid] = rreg;
-      sb[buf].rho[tid] = hreg;
     }
   };
 
-  load_block(qs_lo);
+  // blocks qs_lo .. nqs - 1, dilution from the last one up (G's carried
+  // part is a sum over the rows below), tempered from the first one down
+  const int nblk = nqs - qs_lo;
+  auto block_at = [&](int n) { return DIL ? nqs - 1 - n : qs_lo + n; };
+  float running = 0.0f;   // dilution: sum of g over this half-lane's rows below
+  load_block(block_at(0));
   store_block(0);
   __syncthreads();
-  for (int qs = qs_lo; qs < nqs; ++qs) {
-    const int buf = (qs - qs_lo) & 1;
-    if (qs + 1 < nqs) load_block(qs + 1);
+  for (int n = 0; n < nblk; ++n) {
+    const int qs = block_at(n);
+    const int buf = n & 1;
+    if (n + 1 < nblk) load_block(block_at(n + 1));
     if (wave_live && 32 * qs + 31 >= kw0) {
       uint32_t cw = 0u, gw = 0u;
       if constexpr (DIL) {
         cw = key < 32 * qs ? cin[cin_block_offset(qs, 0) + key] : eps_word;
-        gw = (key < 32 * (qs + 1) && key < T) ? gin[(size_t)16 * qs * (qs + 1) + key] : 0u;
-      }
-      if constexpr (DIL) {
 #pragma unroll
         for (int c = 0; c < kCh; ++c) {
           kf[c] = lds_frag(krow, c, h);
@@ -547,30 +419,180 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
         }
       }
       if (32 * qs == kw0)
-        dkdv_block<DIL, true, CLAMP>(sb[buf], st[buf], kf, vf, sc, cw, gw, c2, l32, h, dkt, dvt);
+        dkdv_block<DIL, true, CLAMP>(sb[buf], st[buf], kf, vf, sc, cw, running, gw, c2, l32, h,
+                                     dkt, dvt);
       else
-        dkdv_block<DIL, false, CLAMP>(sb[buf], st[buf], kf, vf, sc, cw, gw, c2, l32, h, dkt,
-                                      dvt);
+        dkdv_block<DIL, false, CLAMP>(sb[buf], st[buf], kf, vf, sc, cw, running, gw, c2, l32, h,
+                                      dkt, dvt);
+      // the wave's keys are all below 32 (qs + 1): block qs keeps an entry for each
+      if (DIL && h == 0 && key < T) gin[(size_t)16 * qs * (qs + 1) + key] = gw;
     }
-    if (qs + 1 < nqs) store_block(buf ^ 1);
+    if (n + 1 < nblk) store_block(buf ^ 1);
     __syncthreads();
   }
   if (!wave_live || key >= T) return;
   // lane: key; element (u, r): dim 32u + acc_row(r, h)
   __bf16 *dK = reinterpret_cast<__bf16 *>(a.dk) + head + (size_t)key * D;
   __bf16 *dV = reinterpret_cast<__bf16 *>(a.dv) + head + (size_t)key * D;
+  float *dKp = DIL ? a.dkp + head + (size_t)key * D : nullptr;
 #pragma unroll
   for (int u = 0; u < kOB; ++u) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d0 = 32 * u + 8 * g + 4 * h;
-      u32x2 kk, vv;
-      kk[0] = pack_bf16x2(dkt[u][4 * g] * cs, dkt[u][4 * g + 1] * cs);
-      kk[1] = pack_bf16x2(dkt[u][4 * g + 2] * cs, dkt[u][4 * g + 3] * cs);
+      u32x2 vv;
       vv[0] = pack_bf16x2(dvt[u][4 * g], dvt[u][4 * g + 1]);
       vv[1] = pack_bf16x2(dvt[u][4 * g + 2], dvt[u][4 * g + 3]);
-      *reinterpret_cast<u32x2 *>(dK + d0) = kk;
       *reinterpret_cast<u32x2 *>(dV + d0) = vv;
+      if constexpr (DIL) {
+        const f32x4 kp = {dkt[u][4 * g], dkt[u][4 * g + 1], dkt[u][4 * g + 2], dkt[u][4 * g + 3]};
+        *reinterpret_cast<f32x4 *>(dKp + d0) = kp;
+      } else {
+        u32x2 kk;
+        kk[0] = pack_bf16x2(dkt[u][4 * g] * cs, dkt[u][4 * g + 1] * cs);
+        kk[1] = pack_bf16x2(dkt[u][4 * g + 2] * cs, dkt[u][4 * g + 3] * cs);
+        *reinterpret_cast<u32x2 *>(dK + d0) = kk;
+      }
+    }
+  }
+}
+
+// Pass 6 (dilution): dK_j = c (dK'_j - Y_j), Y_j = sum_i p_ij rho_i q_i, with
+// dK' from pass 3 (fp32 workspace) and rho from pass 5.  A workgroup owns 128
+// keys (wave w 32 of them, the key row in registers as the B operand of
+// S = Q K^T) and walks the 32-row blocks that see them, two per barrier; per
+// block the bids are recomputed (S layout), scaled by their rows' rho,
+// packed and accumulated as Y^T += Q^T (p rho) against the block's
+// transposed Q rows.
+template <int D>
+struct RhoBlock {
+  __bf16 q[32 * Geom<D>::kKRow];   // Q rows (A operand of S)
+  __bf16 qt[D * kTRow];            // Q^T, dim-major (A operand of Y^T)
+  float lse2[32], rho[32];
+};
+
+template <int D>
+__global__ void __launch_bounds__(256, 2) bwd_dkrho_kernel(BwdArgs a, int nqs) {
+  constexpr int kKR = Geom<D>::kKRow, kCh = Geom<D>::kChunks, kOB = Geom<D>::kOBlocks;
+  constexpr int kRowChunks = D / 8;                  // 16-byte chunks per row
+  constexpr int kRowLoads = 64 * kRowChunks / 256;   // row-major chunks per thread and stage
+  constexpr int kTrLoads = 32 * kRowChunks / 256;    // (row pair, chunk) items per thread
+  __shared__ __attribute__((aligned(16))) RhoBlock<D> sb[2][2];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int bh = blockIdx.x % a.BH;
+  const int kb = blockIdx.x / a.BH;
+  const float tb = head_tau(a, bh), c2 = a.c2 * tb, cs = a.c * tb;
+  const int T = a.T;
+  const int kw0 = kb * kColKeys + 32 * w;
+  const bool wave_live = kw0 < T;
+  const int key = kw0 + l32;
+  const size_t head = (size_t)bh * T * D;
+  const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + head;
+  const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + head;
+  const float *L2 = a.lse2 + (size_t)bh * T;
+  const float *RH = a.rho + (size_t)bh * T;
+
+  bf16x8 kf[kCh];
+#pragma unroll
+  for (int c = 0; c < kCh; ++c) kf[c] = __builtin_bit_cast(bf16x8, load_row_chunk<D>(K, key, T, 2 * c + h));
+  f32x16 yt[kOB];
+#pragma unroll
+  for (int u = 0; u < kOB; ++u) yt[u] = zero16();
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // a stage is the 64 rows of blocks (2P, 2P + 1).  Loaders: chunk
+  // u = tid + 256 i is row u / kRowChunks, chunk u % kRowChunks; transposed
+  // item u = tid + 256 i covers rows 2 kp, 2 kp + 1 (kp = u & 31) and chunk u >> 5
+  u32x4 qreg[kRowLoads], tr0[kTrLoads], tr1[kTrLoads];
+  float lreg = 0.0f, hreg = 0.0f;
+  auto load_stage = [&](int P) {              // 64 P < T for every stage loaded
+    const int row0 = 64 * P;
+    const auto rq = make_rsrc(Q + (size_t)row0 * D, (T - row0) * (D * 2));
+#pragma unroll
+    for (int i = 0; i < kRowLoads; ++i) qreg[i] = buf_load16(rq, 16u * (tid + 256 * i));
+#pragma unroll
+    for (int i = 0; i < kTrLoads; ++i) {
+      const int u = tid + 256 * i, kp = u & 31, tdc = u >> 5;
+      tr0[i] = buf_load16(rq, 4u * D * kp + 16u * tdc);
+      tr1[i] = buf_load16(rq, 4u * D * kp + 2u * D + 16u * tdc);
+    }
+    if (tid < 64) {
+      const int row = row0 + tid;
+      const bool ok = row < T;
+      const int rr = ok ? row : T - 1;
+      lreg = ok ? L2[rr] : kNoRow;
+      hreg = ok ? RH[rr] : 0.0f;
+    }
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kRowLoads; ++i) {
+      const int u = tid + 256 * i, row = u / kRowChunks;
+      *reinterpret_cast<u32x4 *>(&sb[buf][row >> 5].q[(row & 31) * kKR + (u % kRowChunks) * 8]) =
+          qreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kTrLoads; ++i) {
+      const int u = tid + 256 * i, kp = u & 31, tdc = u >> 5;
+      store_rows_transposed(sb[buf][kp >> 4].qt, kTRow, kp & 15, tdc, tr0[i], tr1[i]);
+    }
+    if (tid < 64) {
+      sb[buf][tid >> 5].lse2[tid & 31] = lreg;
+      sb[buf][tid >> 5].rho[tid & 31] = hreg;
+    }
+  };
+
+  // qs_lo = 4 kb is even: stages p_lo .. p_hi cover blocks qs_lo .. nqs - 1
+  const int p_lo = 2 * kb, p_hi = (nqs - 1) / 2;
+  load_stage(p_lo);
+  store_stage(0);
+  __syncthreads();
+  for (int P = p_lo; P <= p_hi; ++P) {
+    const int buf = (P - p_lo) & 1;
+    if (P < p_hi) load_stage(P + 1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int qs = 2 * P + i;
+      if (qs < nqs && wave_live && 32 * qs + 31 >= kw0) {
+        const RhoBlock<D> &b = sb[buf][i];
+        const __bf16 *qrow = b.q + l32 * kKR;
+        f32x16 sc = zero16();
+#pragma unroll
+        for (int c = 0; c < kCh; ++c) sc = mfma32(lds_frag(qrow, c, h), kf[c], sc);
+        float lq[16], pq[16], wv[16];
+        col_rowvals(b.lse2, h, lq);
+        col_rowvals(b.rho, h, pq);
+        if (32 * qs == kw0) col_bids<true>(sc, lq, c2, l32, h, wv);
+        else col_bids<false>(sc, lq, c2, l32, h, wv);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) wv[r] *= pq[r];
+        const bf16x8 wf[2] = {pack8(wv), pack8(wv + 8)};
+#pragma unroll
+        for (int u = 0; u < kOB; ++u) {
+          const __bf16 *qtr = b.qt + (32 * u + l32) * kTRow;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) yt[u] = mfma32(lds_vfrag(qtr, j, h), wf[j], yt[u]);
+        }
+      }
+    }
+    if (P < p_hi) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+  if (!wave_live || key >= T) return;
+  // lane: key; element (u, r): dim 32u + acc_row(r, h)
+  __bf16 *dK = reinterpret_cast<__bf16 *>(a.dk) + head + (size_t)key * D;
+  const float *dKp = a.dkp + head + (size_t)key * D;
+#pragma unroll
+  for (int u = 0; u < kOB; ++u) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * u + 8 * g + 4 * h;
+      const f32x4 kp4 = *reinterpret_cast<const f32x4 *>(dKp + d0);
+      u32x2 kk;
+      kk[0] = pack_bf16x2((kp4[0] - yt[u][4 * g]) * cs, (kp4[1] - yt[u][4 * g + 1]) * cs);
+      kk[1] = pack_bf16x2((kp4[2] - yt[u][4 * g + 2]) * cs, (kp4[3] - yt[u][4 * g + 3]) * cs);
+      *reinterpret_cast<u32x2 *>(dK + d0) = kk;
     }
   }
 }
@@ -928,8 +950,9 @@ hipError_t launch_bwd_d(int mode, const BwdArgs &a, hipStream_t s) {
     // the forward's table, when the caller passes it, holds the same values
     if (!a.cin_given) e = launch_colsum_bf16(f, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_gsum_kernel<D, CLAMP>), dim3((unsigned)(nkb * a.BH)), dim3(256), 0, s,
-                       a, nqs);
+    // dV, dK' and the later blocks' g sums (read by the dQ pass)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<true, D, CLAMP>), dim3((unsigned)(nkb * a.BH)), dim3(256),
+                       0, s, a, nqs);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // PK = softmax-weighted keys: the tempered forward with the keys as values
@@ -952,8 +975,8 @@ hipError_t launch_bwd_d(int mode, const BwdArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e;
     e = launch_dtau(a, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<true, D, CLAMP>), dim3((unsigned)(nkb * a.BH)), dim3(256),
-                       0, s, a, nqs);
+    hipLaunchKernelGGL((bwd_dkrho_kernel<D>), dim3((unsigned)(nkb * a.BH)), dim3(256), 0, s, a,
+                       nqs);
   } else {
     hipLaunchKernelGGL((bwd_dq_kernel<false, D, false>), dim3((unsigned)(nqb * a.BH)), dim3(256),
                        0, s, a, nqb);
