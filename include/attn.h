@@ -128,8 +128,8 @@ int attn_fwd_noalloc(const void *q, const void *k, const void *v, void *out, int
 /* Bytes of device workspace attn_bwd and attn_bwd_ex need: five fp32 values
  * per query row (six for ATTN_F32 at d = 128), and for dilution the committed
  * demand and the later rows' gradient sums per (32-row query block, key):
- * B*H*16*n*(n+1) 32-bit values each, n = ceil(T/32), plus a [B,H,T,d] array
- * of `dtype` and, for ATTN_BF16, a [B,H,T,d] fp32 array.  0 for an
+ * B*H*16*n*(n+1) 32-bit values each, n = ceil(T/32), plus a [B,H,T,d] fp32
+ * array and, for ATTN_BF16, B*H*ceil(T/128)*T fp32 values.  0 for an
  * unsupported shape, mode, head dimension or dtype. */
 size_t attn_bwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype);
 

@@ -217,15 +217,17 @@ def test_bwd_workspace_sizes():
     n = 16384 // 32
     rows = 16 * 16384 * 4
     # five per-row arrays: lse2, 1/r, delta/r, rho and the rows' dL/dtau terms;
-    # bf16 dilution adds the softmax-weighted keys (bf16) and the fp32 partial
-    # key gradients
-    want = 5 * rows + 2 * 16 * 16 * n * (n + 1) * 4 + 16 * 16384 * 64 * (2 + 4)
+    # bf16 dilution adds the fp32 partial key gradients and each 128-key
+    # block's part of rho per row
+    rho_parts = 16 * (16384 // 128) * 16384 * 4
+    want = 5 * rows + 2 * 16 * 16 * n * (n + 1) * 4 + 16 * 16384 * 64 * 4 + rho_parts
     got = ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 1)
     assert want <= got <= want + 9 * 256
     assert 5 * rows <= ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 0, 1) <= 5 * rows + 5 * 256
-    # fp32 (d = 64): the softmax-weighted keys are fp32; no partial key gradients
+    # fp32 (d = 64): the fp32 softmax-weighted keys in place of the partial
+    # key gradients, and no parts of rho
     assert (ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 1)
-            - ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 0)) == 16 * 16384 * 64 * 2
+            - ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 0)) == rho_parts
     # fp32 at d = 128: dq runs in two 64-wide slices of d, so one more row
     # array (the second slice's dL/dtau terms), and fp32 keys twice as wide
     assert (ab.attn_bwd_workspace_bytes(1, 16, 16384, 128, 1, 0)
@@ -234,9 +236,9 @@ def test_bwd_workspace_sizes():
             - ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 0, 0)) == rows
     assert ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 2) == 0    # unknown dtype
     assert ab.attn_bwd_workspace_bytes(1, 16, 16384, 96, 1, 1) == 0
-    # d = 128: the softmax-weighted keys and partial key gradients are twice as wide
+    # d = 128: the partial key gradients are twice as wide
     assert (ab.attn_bwd_workspace_bytes(1, 16, 16384, 128, 1, 1)
-            - ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 1)) == 16 * 16384 * 64 * (2 + 4)
+            - ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 1)) == 16 * 16384 * 64 * 4
     assert (ab.attn_bwd_workspace_bytes(1, 16, 16384, 128, 0, 1)
             == ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 0, 1))
 

@@ -550,12 +550,13 @@ namespace {
 // delta/r, rho, then <q_i, dQ_i / c> in one partial sum per slice of d that
 // the dq kernel splits the head dimension into), then for dilution the
 // committed demand and the later blocks' gradient sums, per (32-row block,
-// key), the [B,H,T,d] array (storage type) of softmax-weighted keys and, for
-// bf16, the fp32 [B,H,T,d] partial key gradients sum_i p_ij dp_ij q_i.
+// key); for fp32 the [B,H,T,d] softmax-weighted keys; for bf16 the fp32
+// [B,H,T,d] partial key gradients sum_i p_ij dp_ij q_i and, per row, each
+// 128-key block's part of rho ([B*H][ceil(T/128)][T] fp32).
 constexpr size_t kBwdFixedRowArrays = 4;
 struct BwdWorkspace {
   int tslices;
-  size_t row_bytes, cin_bytes, gin_bytes, pk_bytes, dkp_bytes, total;
+  size_t row_bytes, cin_bytes, gin_bytes, pk_bytes, dkp_bytes, rhop_bytes, total;
 };
 
 // The bf16 dq kernel covers all of d in one workgroup; the fp32 one splits d
@@ -569,12 +570,13 @@ bool bwd_workspace(int B, int H, int T, int d, int mode, int dtype, BwdWorkspace
   ws->row_bytes = round_up(BH * (size_t)T * sizeof(float));
   ws->cin_bytes = mode == ATTN_DILUTION ? round_up(BH * attn::cin_floats_per_head(T, 0) * 4) : 0;
   ws->gin_bytes = mode == ATTN_DILUTION ? round_up(BH * attn::gin_floats_per_head(T) * 4) : 0;
-  const size_t esz = dtype == ATTN_BF16 ? 2 : 4;
-  ws->pk_bytes = mode == ATTN_DILUTION ? round_up(BH * (size_t)T * d * esz) : 0;
-  ws->dkp_bytes =
-      mode == ATTN_DILUTION && dtype == ATTN_BF16 ? round_up(BH * (size_t)T * d * sizeof(float)) : 0;
+  const bool dil = mode == ATTN_DILUTION, bf16 = dtype == ATTN_BF16;
+  const size_t nkb = ((size_t)T + 127) / 128;
+  ws->pk_bytes = dil && !bf16 ? round_up(BH * (size_t)T * d * sizeof(float)) : 0;
+  ws->dkp_bytes = dil && bf16 ? round_up(BH * (size_t)T * d * sizeof(float)) : 0;
+  ws->rhop_bytes = dil && bf16 ? round_up(BH * nkb * (size_t)T * sizeof(float)) : 0;
   ws->total = (kBwdFixedRowArrays + ws->tslices) * ws->row_bytes + ws->cin_bytes + ws->gin_bytes +
-              ws->pk_bytes + ws->dkp_bytes;
+              ws->pk_bytes + ws->dkp_bytes + ws->rhop_bytes;
   return true;
 }
 
@@ -681,8 +683,12 @@ int attn_bwd_ex(const void *q, const void *k, const void *v, const void *out, co
                     : reinterpret_cast<float *>(wtail);
     a.cin_given = fwd_cin ? 1 : 0;
     a.gin = reinterpret_cast<float *>(wtail + ws.cin_bytes);
-    a.pk = wtail + ws.cin_bytes + ws.gin_bytes;
-    if (ws.dkp_bytes) a.dkp = reinterpret_cast<float *>(wtail + ws.cin_bytes + ws.gin_bytes + ws.pk_bytes);
+    char *wt = wtail + ws.cin_bytes + ws.gin_bytes;
+    if (ws.pk_bytes) a.pk = wt;
+    wt += ws.pk_bytes;
+    if (ws.dkp_bytes) a.dkp = reinterpret_cast<float *>(wt);
+    wt += ws.dkp_bytes;
+    if (ws.rhop_bytes) a.rhop = reinterpret_cast<float *>(wt);
   }
   a.BH = B * H;
   a.T = T;

@@ -22,22 +22,22 @@
 // D = 128 the dQ and dK/dV kernels run one workgroup per CU, which doubles
 // the registers per lane for the doubled operands and accumulators.
 //
-// Passes (dilution; tempered runs 1, 5, 5b and 3 only, dK/dV top-down):
+// Passes (dilution; tempered runs 1, 4, 4b and 3 only, dK/dV top-down):
 //   1 bwd_prep_kernel   per row: log2-domain lse, 1/r, delta/r
 //   2 colsum_bf16_kernel (the forward's) committed demand per 32-row block
 //   3 bwd_dkdv_kernel   per 32 keys, walking 32-row blocks from the last one
 //                       up: the sum of g over every later block (G's block
-//                       part, carried in a register and stored for pass 5),
-//                       dV, and dK' = sum_i p_ij dp_ij q_i (fp32 workspace)
-//   4 rows_bf16_kernel  (the tempered forward with V := K) PK_i = sum_j p_ij k_j
-//   5 bwd_dq_kernel     per 32 query rows: X_i = sum_j p_ij dp_ij k_j and rho,
-//                       then dQ_i = c (X_i - rho_i PK_i) and <q_i, dQ_i / c>
-//   5b bwd_dtau_kernel  (when dL/dtau is asked for) per head: the rows' sum
-//   6 bwd_dkrho_kernel  per 32 keys: dK_j = c (dK'_j - sum_i p_ij rho_i q_i)
+//                       part, carried in a register and stored for pass 4),
+//                       dV, dK' = sum_i p_ij dp_ij q_i (fp32 workspace), and
+//                       per row its 128 keys' part of rho_i = sum_j p_ij dp_ij
+//   4 bwd_dq_kernel     per 32 query rows: rho_i from those parts, then
+//                       dQ_i = c sum_j p_ij (dp_ij - rho_i) k_j and <q_i, dQ_i / c>
+//   4b bwd_dtau_kernel  (when dL/dtau is asked for) per head: the rows' sum
+//   5 bwd_dkrho_kernel  per 32 keys: dK_j = c (dK'_j - sum_i p_ij rho_i q_i)
 // Splitting dK_j = c sum_i p_ij (dp_ij - rho_i) q_i at rho lets the dK/dV
 // pass run before rho is known (rho needs every key of a row, and dp needs
 // G, the column sums that pass carries), so one column pass over all pairs
-// does both G and dK/dV.
+// does G, dK/dV and the parts of rho.
 // Both in-block scans (the column prefix inside D and the column suffix
 // inside G) are matrix-core products against constant triangular operands,
 // as in the forward shares pass.
@@ -128,21 +128,26 @@ struct ScanConsts {
   bf16x8 le[2];    // inclusive prefix: 1 where the slot's query <= m
   bf16x8 ge[2];    // inclusive suffix: 1 where the slot's query >= m
   bf16x8 ones;     // slots (0, 0) and (0, 1): adds a per-key bf16 (hi, lo) pair
+  bf16x8 ident[2]; // B operand: 1 where the slot's query == n; with packed
+                   // S-layout values as the A operand (m = key, slots = queries)
+                   // it moves them to lane = query
 };
 
 __device__ __forceinline__ ScanConsts scan_consts(int l32, int h) {
   ScanConsts c;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    float le[8], ge[8];
+    float le[8], ge[8], id[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int qs = acc_row(8 * j + e, h);
       le[e] = qs <= l32 ? 1.0f : 0.0f;
       ge[e] = qs >= l32 ? 1.0f : 0.0f;
+      id[e] = qs == l32 ? 1.0f : 0.0f;
     }
     c.le[j] = pack8(le);
     c.ge[j] = pack8(ge);
+    c.ident[j] = pack8(id);
   }
   const float one = h == 0 ? 1.0f : 0.0f;
   c.ones = to_bf16x8(one, one, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f);
@@ -201,9 +206,11 @@ __device__ __forceinline__ void col_scores(const ColBlock<D> &b, const bf16x8 *k
 // Pass 3: dK and dV for this wave's keys.  The transposed Q and dO blocks
 // (dim-major) are the A operands of dK^T += Q^T dS and dV^T += dO^T a; the
 // packed dS and a (S layout) are their B operands.  Dilution takes p dp in
-// place of dS (rho enters in pass 6) and, walking bottom-up, carries in
+// place of dS (rho enters in pass 5) and, walking bottom-up, carries in
 // `running` each half-lane's sum of g over the blocks below; `gin_word`
-// returns that sum over both halves (bf16 pair) for the dQ pass.
+// returns that sum over both halves (bf16 pair) for the dQ pass, and
+// `rho_part` the block's rows' sums of the packed p dp over this wave's 32
+// keys (lane l32: row l32 of the block).
 template <int D>
 struct ColBlockT {
   __bf16 qt[D * kTRow];
@@ -214,8 +221,8 @@ template <bool DIL, bool DIAG, bool CLAMP, int D>
 __device__ __forceinline__ void dkdv_block(const ColBlock<D> &b, const ColBlockT<D> &bt,
                                            const bf16x8 *kf, const bf16x8 *vf,
                                            const ScanConsts &sc, uint32_t cin_word,
-                                           float &running, uint32_t &gin_word, float c2, int l32,
-                                           int h, f32x16 *dkt, f32x16 *dvt) {
+                                           float &running, uint32_t &gin_word, float &rho_part,
+                                           float c2, int l32, int h, f32x16 *dkt, f32x16 *dvt) {
   f32x16 s, da;
   col_scores(b, kf, vf, l32, h, s, da);
   float ds[16], aw[16];
@@ -268,6 +275,15 @@ __device__ __forceinline__ void dkdv_block(const ColBlock<D> &b, const ColBlockT
   }
   const bf16x8 sf[2] = {pack8(ds), pack8(ds + 8)};
   const bf16x8 af[2] = {pack8(aw), pack8(aw + 8)};
+  if constexpr (DIL) {
+    // the packed p dp moved to lane = row (keys in the elements), summed
+    f32x16 rt = mfma32(sf[0], sc.ident[0], zero16());
+    rt = mfma32(sf[1], sc.ident[1], rt);
+    float part = rt[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) part += rt[r];
+    rho_part = both_halves_sum(part);
+  }
 #pragma unroll
   for (int u = 0; u < Geom<D>::kOBlocks; ++u) {
     const __bf16 *qtr = bt.qt + (32 * u + l32) * kTRow;
@@ -299,6 +315,9 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
   // in LDS and are read per block, which keeps the kernel within two waves'
   // registers per SIMD without spills; the tempered form keeps them in registers
   __shared__ __attribute__((aligned(16))) __bf16 sKV[DIL ? 2 : 1][DIL ? kColKeys * kKR : 8];
+  // dilution: per block, each wave's sums of p dp over its keys (row l32),
+  // added over the four waves one iteration later (double buffered)
+  __shared__ float sRho[DIL ? 2 : 1][4][32];
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int bh = blockIdx.x % a.BH;
@@ -401,6 +420,16 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
   const int nblk = nqs - qs_lo;
   auto block_at = [&](int n) { return DIL ? nqs - 1 - n : qs_lo + n; };
   float running = 0.0f;   // dilution: sum of g over this half-lane's rows below
+  // dilution: this workgroup's part of rho for the rows of block qs, written
+  // as [bh][kb][row]
+  float *rhop = DIL ? a.rhop + ((size_t)bh * ((T + kColKeys - 1) / kColKeys) + kb) * T : nullptr;
+  auto flush_rho = [&](int qs, int buf) {
+    if (DIL && w == 0 && h == 0) {
+      const int row = 32 * qs + l32;
+      if (row < T) rhop[row] = ((sRho[buf][0][l32] + sRho[buf][1][l32]) + sRho[buf][2][l32]) +
+                               sRho[buf][3][l32];
+    }
+  };
   load_block(block_at(0));
   store_block(0);
   __syncthreads();
@@ -408,6 +437,8 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
     const int qs = block_at(n);
     const int buf = n & 1;
     if (n + 1 < nblk) load_block(block_at(n + 1));
+    if (n > 0) flush_rho(block_at(n - 1), buf ^ 1);
+    float rho_part = 0.0f;   // waves whose keys block qs does not see add 0
     if (wave_live && 32 * qs + 31 >= kw0) {
       uint32_t cw = 0u, gw = 0u;
       if constexpr (DIL) {
@@ -419,17 +450,19 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
         }
       }
       if (32 * qs == kw0)
-        dkdv_block<DIL, true, CLAMP>(sb[buf], st[buf], kf, vf, sc, cw, running, gw, c2, l32, h,
-                                     dkt, dvt);
+        dkdv_block<DIL, true, CLAMP>(sb[buf], st[buf], kf, vf, sc, cw, running, gw, rho_part, c2,
+                                     l32, h, dkt, dvt);
       else
-        dkdv_block<DIL, false, CLAMP>(sb[buf], st[buf], kf, vf, sc, cw, running, gw, c2, l32, h,
-                                      dkt, dvt);
+        dkdv_block<DIL, false, CLAMP>(sb[buf], st[buf], kf, vf, sc, cw, running, gw, rho_part, c2,
+                                      l32, h, dkt, dvt);
       // the wave's keys are all below 32 (qs + 1): block qs keeps an entry for each
       if (DIL && h == 0 && key < T) gin[(size_t)16 * qs * (qs + 1) + key] = gw;
     }
+    if (DIL && h == 0) sRho[buf][w][l32] = rho_part;
     if (n + 1 < nblk) store_block(buf ^ 1);
     __syncthreads();
   }
+  if (nblk > 0) flush_rho(block_at(nblk - 1), (nblk - 1) & 1);
   if (!wave_live || key >= T) return;
   // lane: key; element (u, r): dim 32u + acc_row(r, h)
   __bf16 *dK = reinterpret_cast<__bf16 *>(a.dk) + head + (size_t)key * D;
@@ -636,18 +669,17 @@ __device__ __forceinline__ DqConsts dq_consts(int l32, int h) {
 
 template <int D>
 struct DqState {
-  f32x16 x[Geom<D>::kOBlocks];   // X^T[d][query] = sum_j p_ij dp_ij k_j (tempered:
-                                 // sum_j dS_ij k_j); x[u] holds d in [32u, 32u + 32)
-  f32x4 rho;       // sum_j p_ij dp_ij, every element equal (dilution)
+  f32x16 x[Geom<D>::kOBlocks];   // X^T[d][query] = sum_j dS_ij k_j; x[u] holds d in
+                                 // [32u, 32u + 32)
 };
 
 template <bool DIL, bool DIAG, bool CLAMP, int D>
 __device__ __forceinline__ void dq_subtile(DqState<D> &st, const bf16x8 *qf, const bf16x8 *gf,
-                                           const DqConsts &dc, const bf16x8 &sel,
+                                           const DqConsts &dc,
                                            const __bf16 *kt_lds, const __bf16 *vt_lds,
                                            const __bf16 *ktt_lds, int t, uint32_t cin_word,
                                            uint32_t gin_word, float lse2, float invr, float dri,
-                                           int qrel, int l32, int h, float c2) {
+                                           float rho, int qrel, int l32, int h, float c2) {
   // S^T and dA^T for keys 32t.. of the tile (lane = query)
   const __bf16 *krow = kt_lds + (32 * t + l32) * Geom<D>::kKRow;
   const __bf16 *vrow = vt_lds + (32 * t + l32) * Geom<D>::kKRow;
@@ -695,11 +727,8 @@ __device__ __forceinline__ void dq_subtile(DqState<D> &st, const bf16x8 *qf, con
     G = mfma32(word_operand(gin_word), dc.bone, G);
     float e[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) e[r] = p[r] * __builtin_fmaf(dsg[r], invd[r], -G[r]);
-    const bf16x8 ef0 = pack8(e), ef1 = pack8(e + 8);
-    pv_update_d<D>(st.x, ktt_lds, t, l32, h, ef0, ef1);
-    st.rho = mfma16(sel, ef0, st.rho);
-    st.rho = mfma16(sel, ef1, st.rho);
+    for (int r = 0; r < 16; ++r) e[r] = p[r] * (__builtin_fmaf(dsg[r], invd[r], -G[r]) - rho);
+    pv_update_d<D>(st.x, ktt_lds, t, l32, h, pack8(e), pack8(e + 8));
   } else {
     float ds[16];
 #pragma unroll
@@ -751,7 +780,6 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dq_kernel(B
   const float invr = row_ok ? a.invr[ridx] : 0.0f;
   const float dri = row_ok ? a.dri[ridx] : 0.0f;
   const DqConsts dc = dq_consts(l32, h);
-  const bf16x8 sel = rowsum_selector(lane);
   const uint32_t eps_word = split2_bf16(fmaxf(a.eps, FLT_MIN));
   const uint32_t *cin_blk = nullptr, *gin_blk = nullptr;
   const int qsb = qw0 >> 5;   // this wave's 32-row block
@@ -818,7 +846,19 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dq_kernel(B
   DqState<D> st;
 #pragma unroll
   for (int u = 0; u < kOB; ++u) st.x[u] = zero16();
-  st.rho = zero4();
+  // dilution: rho_i = sum_j p_ij dp_ij from the dK/dV pass's parts (one per
+  // 128-key workgroup up to the row's own, added in a fixed order: even parts
+  // on the lower half-wave, odd ones on the upper), kept for the dK pass
+  float rho = 0.0f;
+  if constexpr (DIL) {
+    if (row_ok) {
+      const int nkb = (T + kColKeys - 1) / kColKeys;
+      const float *rp = a.rhop + (size_t)bh * nkb * T + row;
+      for (int kb = h; kb <= row / kColKeys; kb += 2) rho += rp[(size_t)kb * T];
+    }
+    rho = both_halves_sum(rho);
+    if (row_ok && h == 0) a.rho[ridx] = rho;
+  }
   __builtin_amdgcn_s_waitcnt(0);
 
   load_tile(0);
@@ -840,11 +880,11 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dq_kernel(B
 #pragma unroll 1
       for (int t = 0; t < 2; ++t) {
         if (kt < kd)
-          dq_subtile<DIL, false, CLAMP, D>(st, qf, gf, dc, sel, kl, vl, tl, t, cw[t], gw[t], lse2,
-                                           invr, dri, qrel, l32, h, c2);
+          dq_subtile<DIL, false, CLAMP, D>(st, qf, gf, dc, kl, vl, tl, t, cw[t], gw[t], lse2,
+                                           invr, dri, rho, qrel, l32, h, c2);
         else
-          dq_subtile<DIL, true, CLAMP, D>(st, qf, gf, dc, sel, kl, vl, tl, t, cw[t], gw[t], lse2,
-                                          invr, dri, qrel, l32, h, c2);
+          dq_subtile<DIL, true, CLAMP, D>(st, qf, gf, dc, kl, vl, tl, t, cw[t], gw[t], lse2,
+                                          invr, dri, rho, qrel, l32, h, c2);
       }
     }
     if (kt + 1 < nkt) store_tile(buf ^ 1);
@@ -852,13 +892,6 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dq_kernel(B
   }
   if (!wave_live || !row_ok) return;
   __bf16 *dQ = reinterpret_cast<__bf16 *>(a.dq) + head + (size_t)row * D;
-  float rho = 0.0f;
-  const __bf16 *PK = nullptr;
-  if constexpr (DIL) {
-    rho = st.rho[0];
-    if (h == 0) a.rho[ridx] = rho;
-    PK = reinterpret_cast<const __bf16 *>(a.pk) + head + (size_t)row * D;
-  }
   // lane: query; element (block u, r): dim 32u + acc_row(r, h).  With u_i =
   // dQ_i / c, <q_i, u_i> = sum_j dS_ij <q_i, k_j>: this row's share of dL/dtau.
   const __bf16 *Qr = Q + (size_t)row * D;
@@ -869,15 +902,8 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dq_kernel(B
     for (int g = 0; g < 4; ++g) {
       const int d0 = 32 * u + 8 * g + 4 * h;
       float x[4];
-      if constexpr (DIL) {
-        const u32x2 pw = *reinterpret_cast<const u32x2 *>(PK + d0);
-        const float pk[4] = {bf16_lo(pw[0]), bf16_hi(pw[0]), bf16_lo(pw[1]), bf16_hi(pw[1])};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = __builtin_fmaf(-rho, pk[i], st.x[u][4 * g + i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = st.x[u][4 * g + i];
-      }
+      for (int i = 0; i < 4; ++i) x[i] = st.x[u][4 * g + i];
       if (a.dtau) {
         const u32x2 qw = *reinterpret_cast<const u32x2 *>(Qr + d0);
         tq = __builtin_fmaf(bf16_lo(qw[0]), x[0], tq);
@@ -950,24 +976,10 @@ hipError_t launch_bwd_d(int mode, const BwdArgs &a, hipStream_t s) {
     // the forward's table, when the caller passes it, holds the same values
     if (!a.cin_given) e = launch_colsum_bf16(f, s);
     if (e != hipSuccess) return e;
-    // dV, dK' and the later blocks' g sums (read by the dQ pass)
+    // dV, dK', the parts of rho and the later blocks' g sums (read by the dQ pass)
     hipLaunchKernelGGL((bwd_dkdv_kernel<true, D, CLAMP>), dim3((unsigned)(nkb * a.BH)), dim3(256),
                        0, s, a, nqs);
     e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // PK = softmax-weighted keys: the tempered forward with the keys as values
-    FwdArgs t{};
-    t.q = a.q;
-    t.k = a.k;
-    t.v = a.k;
-    t.out = a.pk;
-    t.BH = a.BH;
-    t.T = t.Tq = t.kstride = a.T;
-    t.D = D;
-    t.ksplit = 1;
-    t.tau_bh = a.tau_bh;
-    t.c2 = a.c2;
-    e = launch_rows_bf16(kRowTempered, t, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dq_kernel<true, D, CLAMP>), dim3((unsigned)(nqb * a.BH)), dim3(256), 0,
                        s, a, nqb);

@@ -106,8 +106,10 @@ struct BwdArgs {
                           // committed + eps as bf16 pairs, fp32 path fp32
   float *gin;             // later blocks' share-gradient sums per (block, key): bf16
                           // pairs (bf16 path) or fp32
-  void *pk;               // [BH*T*D] workspace in the storage type: sum_j p_ij k_j (dilution)
+  void *pk;               // [BH*T*D] workspace, fp32 path: sum_j p_ij k_j (dilution)
   float *dkp;             // [BH*T*D] workspace, fp32 (bf16 dilution): sum_i p_ij dp_ij q_i
+  float *rhop;            // [BH][ceil(T/128)][T] workspace (bf16 dilution): per row, each
+                          // 128-key block's part of rho
   const float *tau_bh;    // [BH] per-head multipliers, or NULL (then c2, c carry tau)
   float *dtau;            // [BH] output: dL/dtau per head, or NULL
   float *trow;            // [tslices][BH*T] workspace: <q_i, dQ_i / c> per row (for
