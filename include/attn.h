@@ -126,7 +126,7 @@ int attn_fwd_noalloc(const void *q, const void *k, const void *v, void *out, int
                      int d, float tau, int mode, float eps, int dtype, void *hip_stream);
 
 /* Bytes of device workspace attn_bwd and attn_bwd_ex need: five fp32 values
- * per query row (six for ATTN_F32 at d = 128), and for dilution the committed
+ * per query row, and for dilution the committed
  * demand and the later rows' gradient sums per (32-row query block, key):
  * B*H*16*n*(n+1) 32-bit values each, n = ceil(T/32), plus a [B,H,T,d] fp32
  * array and, for ATTN_BF16, B*H*ceil(T/128)*T fp32 values.  0 for an

@@ -228,12 +228,11 @@ def test_bwd_workspace_sizes():
     # key gradients, and no parts of rho
     assert (ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 1)
             - ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 0)) == rho_parts
-    # fp32 at d = 128: dq runs in two 64-wide slices of d, so one more row
-    # array (the second slice's dL/dtau terms), and fp32 keys twice as wide
+    # fp32 at d = 128: the softmax-weighted keys are twice as wide
     assert (ab.attn_bwd_workspace_bytes(1, 16, 16384, 128, 1, 0)
-            - ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 0)) == rows + 16 * 16384 * 64 * 4
+            - ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 0)) == 16 * 16384 * 64 * 4
     assert (ab.attn_bwd_workspace_bytes(1, 16, 16384, 128, 0, 0)
-            - ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 0, 0)) == rows
+            == ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 0, 0))
     assert ab.attn_bwd_workspace_bytes(1, 16, 16384, 64, 1, 2) == 0    # unknown dtype
     assert ab.attn_bwd_workspace_bytes(1, 16, 16384, 96, 1, 1) == 0
     # d = 128: the partial key gradients are twice as wide

@@ -559,9 +559,9 @@ struct BwdWorkspace {
   size_t row_bytes, cin_bytes, gin_bytes, pk_bytes, dkp_bytes, rhop_bytes, total;
 };
 
-// The bf16 dq kernel covers all of d in one workgroup; the fp32 one splits d
-// into 64-wide slices.
-int bwd_tslices(int d, int dtype) { return dtype == ATTN_BF16 ? 1 : d / 64; }
+// Per-row partial sums of the rows' dL/dtau terms: every dq kernel covers all
+// of d in one workgroup, so one.
+int bwd_tslices(int, int) { return 1; }
 
 bool bwd_workspace(int B, int H, int T, int d, int mode, int dtype, BwdWorkspace *ws) {
   const size_t BH = (size_t)B * H;

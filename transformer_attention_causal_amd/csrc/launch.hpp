@@ -114,7 +114,7 @@ struct BwdArgs {
   float *dtau;            // [BH] output: dL/dtau per head, or NULL
   float *trow;            // [tslices][BH*T] workspace: <q_i, dQ_i / c> per row (for
                           // dtau), in tslices partial sums over slices of d
-  int tslices;            // 1, or the fp32 kernels' number of 64-wide slices of d
+  int tslices;            // partial sums per row (1: every dq kernel covers all of d)
   int cin_given;          // 1: cin is the forward's committed-demand table (read as is)
   int BH, T, D;           // D: head dimension, 64 or 128
   float c2;               // tau / sqrt(d) * log2(e)  (with tau_bh: log2(e) / sqrt(d))
