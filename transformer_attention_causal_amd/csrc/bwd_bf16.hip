@@ -385,7 +385,10 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
       const int u = tid + 256 * i, tdc = (u >> 4) % kRowChunks;
       qreg[i] = buf_load16(rq, 16u * u);
       greg[i] = buf_load16(rg, 16u * u);
-      const auto rt = (u >> 4) < kRowChunks ? rq : rg;
+      // Q or dO: the same for every lane of a wave (items split at a wave
+      // boundary), made a scalar so the buffer descriptor stays in SGPRs
+      const bool tq = __builtin_amdgcn_readfirstlane((u >> 4) < kRowChunks ? 1 : 0) != 0;
+      const auto rt = tq ? rq : rg;
       tr0[i] = buf_load16(rt, 4u * D * kp + 16u * tdc);
       tr1[i] = buf_load16(rt, 4u * D * kp + 2u * D + 16u * tdc);
     }
