@@ -19,11 +19,13 @@
 // A workgroup is four such waves, and the other operand's rows stream
 // through LDS in 64-row tiles that the four waves share, read as broadcasts.
 // With the own rows in registers the LDS holds only the shared tiles, so a
-// CU runs a wave on each of its SIMDs at d = 128 too.  The denominators match the fp32 forward's exactly: D =
-// max(committed + eps, FLT_MIN) + the inclusive prefix of the bids inside the
-// 32-row query block, with committed read from the fp32 forward's table.  The
-// scans inside a block run over lanes in the dQ kernel (shuffles across the 32
-// lanes of the block) and over the rows a lane walks in the column kernels.
+// CU runs a wave on each of its SIMDs at d = 128 too.
+//
+// The denominators match the fp32 forward's exactly: D = max(committed + eps,
+// FLT_MIN) + the inclusive prefix of the bids inside the 32-row query block,
+// with committed read from the fp32 forward's table.  The scans inside a
+// block run over lanes in the dQ kernel (shuffles across the 32 lanes of the
+// block) and over the rows a lane walks in the column kernels.
 #include "attn_common.hpp"
 #include "launch.hpp"
 
@@ -51,6 +53,7 @@ __device__ __forceinline__ float row_dot(float part) {
   if constexpr (D > kDS) return both_halves_sum(part);
   return part;
 }
+
 constexpr float kInvDMaxF32 = 18446744073709551616.0f;   // 2^64: 1/D clamp (eps = 0 only)
 constexpr float kNoRowBwdF32 = 1e30f;                    // lse2 of a position past T
 
