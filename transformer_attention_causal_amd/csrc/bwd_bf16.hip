@@ -225,6 +225,24 @@ __device__ __forceinline__ void dkdv_block(const ColBlock<D> &b, const ColBlockT
                                            float c2, int l32, int h, f32x16 *dkt, f32x16 *dvt) {
   f32x16 s, da;
   col_scores(b, kf, vf, l32, h, s, da);
+  // The transposed Q and dO fragments of the closing dK/dV products are read
+  // into registers ahead of them where registers allow (d = 128, one wave per
+  // SIMD; the tempered form), so that their LDS latency passes behind the
+  // vector work instead of before each product.  The dilution form reads them
+  // once the in-block prefix is formed, the tempered form right away.
+  constexpr bool kAhead = D > 64 || !DIL;
+  bf16x8 qtf[Geom<D>::kOBlocks][2], gtf[Geom<D>::kOBlocks][2];
+  auto read_ahead = [&]() {
+#pragma unroll
+    for (int u = 0; u < Geom<D>::kOBlocks; ++u)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        qtf[u][j] = lds_vfrag(bt.qt + (32 * u + l32) * kTRow, j, h);
+        gtf[u][j] = lds_vfrag(bt.gt + (32 * u + l32) * kTRow, j, h);
+      }
+    __builtin_amdgcn_sched_barrier(0);   // keep the reads where they are issued
+  };
+  if constexpr (kAhead && !DIL) read_ahead();
   float ds[16], aw[16];
   if constexpr (DIL) {
     // written out stage by stage so each per-row array and temporary dies
@@ -236,6 +254,7 @@ __device__ __forceinline__ void dkdv_block(const ColBlock<D> &b, const ColBlockT
     f32x16 d = mfma32(sc.le[0], pack8(p), zero16());
     d = mfma32(sc.le[1], pack8(p + 8), d);
     d = mfma32(sc.ones, word_operand(cin_word), d);
+    if constexpr (kAhead) read_ahead();
     float invd[16], sg[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -290,8 +309,13 @@ __device__ __forceinline__ void dkdv_block(const ColBlock<D> &b, const ColBlockT
     const __bf16 *gtr = bt.gt + (32 * u + l32) * kTRow;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      dkt[u] = mfma32(lds_vfrag(qtr, j, h), sf[j], dkt[u]);
-      dvt[u] = mfma32(lds_vfrag(gtr, j, h), af[j], dvt[u]);
+      if constexpr (kAhead) {
+        dkt[u] = mfma32(qtf[u][j], sf[j], dkt[u]);
+        dvt[u] = mfma32(gtf[u][j], af[j], dvt[u]);
+      } else {
+        dkt[u] = mfma32(lds_vfrag(qtr, j, h), sf[j], dkt[u]);
+        dvt[u] = mfma32(lds_vfrag(gtr, j, h), af[j], dvt[u]);
+      }
     }
   }
 }
@@ -692,6 +716,29 @@ __device__ __forceinline__ void dq_subtile(DqState<D> &st, const bf16x8 *qf, con
     s = mfma32(lds_frag(krow, c, h), qf[c], s);
     da = mfma32(lds_frag(vrow, c, h), gf[c], da);
   }
+  // The K^T fragments of the closing dQ products, read ahead as in the dK/dV
+  // pass (dilution: once the in-block prefix is formed; tempered: right away).
+  constexpr bool kAhead = D > 64 || !DIL;
+  bf16x8 kta[Geom<D>::kOBlocks][2];
+  auto read_ahead = [&]() {
+#pragma unroll
+    for (int i = 0; i < Geom<D>::kOBlocks; ++i)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) kta[i][c] = lds_vfrag(ktt_lds + (32 * i + l32) * kVRow + 32 * t, c, h);
+    __builtin_amdgcn_sched_barrier(0);   // keep the reads where they are issued
+  };
+  // dQ^T += K^T dS^T for the sub-tile's keys (e0, e1: the packed dS^T)
+  auto update = [&](const bf16x8 &e0, const bf16x8 &e1) {
+    if constexpr (kAhead) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int i = 0; i < Geom<D>::kOBlocks; ++i) st.x[i] = mfma32(kta[i][c], c == 0 ? e0 : e1, st.x[i]);
+    } else {
+      pv_update_d<D>(st.x, ktt_lds, t, l32, h, e0, e1);
+    }
+  };
+  if constexpr (kAhead && !DIL) read_ahead();
   float p[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -711,6 +758,7 @@ __device__ __forceinline__ void dq_subtile(DqState<D> &st, const bf16x8 *qf, con
     f32x16 d = mfma32(pa0, dc.upre[0], zero16());
     d = mfma32(pa1, dc.upre[1], d);
     d = mfma32(word_operand(cin_word), dc.bone, d);
+    if constexpr (kAhead) read_ahead();
     float invd[16], dsg[16], g[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -731,12 +779,12 @@ __device__ __forceinline__ void dq_subtile(DqState<D> &st, const bf16x8 *qf, con
     float e[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) e[r] = p[r] * (__builtin_fmaf(dsg[r], invd[r], -G[r]) - rho);
-    pv_update_d<D>(st.x, ktt_lds, t, l32, h, pack8(e), pack8(e + 8));
+    update(pack8(e), pack8(e + 8));
   } else {
     float ds[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) ds[r] = p[r] * (da[r] - dri);
-    pv_update_d<D>(st.x, ktt_lds, t, l32, h, pack8(ds), pack8(ds + 8));
+    update(pack8(ds), pack8(ds + 8));
   }
 }
 
