@@ -225,12 +225,11 @@ __device__ __forceinline__ void dkdv_block(const ColBlock<D> &b, const ColBlockT
                                            float c2, int l32, int h, f32x16 *dkt, f32x16 *dvt) {
   f32x16 s, da;
   col_scores(b, kf, vf, l32, h, s, da);
-  // The transposed Q and dO fragments of the closing dK/dV products are read
-  // into registers ahead of them where registers allow (d = 128, one wave per
-  // SIMD; the tempered form), so that their LDS latency passes behind the
-  // vector work instead of before each product.  The dilution form reads them
-  // once the in-block prefix is formed, the tempered form right away.
-  constexpr bool kAhead = D > 64 || !DIL;
+  // The tempered form reads the transposed Q and dO fragments of the closing
+  // dK/dV products into registers right after the score products, so that
+  // their LDS latency passes behind the vector work instead of before each
+  // product; the dilution form at d = 64 has no registers to spare for them.
+  constexpr bool kAhead = !DIL;
   bf16x8 qtf[Geom<D>::kOBlocks][2], gtf[Geom<D>::kOBlocks][2];
   auto read_ahead = [&]() {
 #pragma unroll
@@ -242,7 +241,7 @@ __device__ __forceinline__ void dkdv_block(const ColBlock<D> &b, const ColBlockT
       }
     __builtin_amdgcn_sched_barrier(0);   // keep the reads where they are issued
   };
-  if constexpr (kAhead && !DIL) read_ahead();
+  if constexpr (kAhead) read_ahead();
   float ds[16], aw[16];
   if constexpr (DIL) {
     // written out stage by stage so each per-row array and temporary dies
@@ -254,7 +253,6 @@ __device__ __forceinline__ void dkdv_block(const ColBlock<D> &b, const ColBlockT
     f32x16 d = mfma32(sc.le[0], pack8(p), zero16());
     d = mfma32(sc.le[1], pack8(p + 8), d);
     d = mfma32(sc.ones, word_operand(cin_word), d);
-    if constexpr (kAhead) read_ahead();
     float invd[16], sg[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -318,6 +316,104 @@ __device__ __forceinline__ void dkdv_block(const ColBlock<D> &b, const ColBlockT
       }
     }
   }
+}
+
+// The dilution form of pass 3 at d = 128, software-pipelined across blocks.
+// At one wave per SIMD a wave's matrix-core and vector work overlap only
+// where its own instruction stream interleaves them, and a block's closing
+// dK/dV products depend on the whole vector chain before them.  So block n's
+// closing products (operands qtf / gtf and the packed sf / af, carried in
+// registers) are issued during block n + 1, one beside each element step of
+// that block's vector chain, and block n + 1's fragments are read after them.
+// Each accumulator still receives its products block by block in the same
+// order, so the sums are the same bits.  The caller issues the last block's
+// products after the loop (dkdv_tail); before the first block the carried
+// operands are zero, and the products add +0.
+template <int D>
+struct DkdvCarry {
+  bf16x8 qtf[Geom<D>::kOBlocks][2], gtf[Geom<D>::kOBlocks][2];   // transposed Q / dO fragments
+  bf16x8 sf[2], af[2];   // packed dS (dilution: p dp) and a of the block
+};
+
+// Product i (0 .. 4 kOBlocks - 1) of the carried block's closing products.
+template <int D>
+__device__ __forceinline__ void dkdv_tail_step(const DkdvCarry<D> &cr, int i, f32x16 *dkt,
+                                               f32x16 *dvt) {
+  const int u = i >> 2, j = (i >> 1) & 1;
+  if (i & 1) dvt[u] = mfma32(cr.gtf[u][j], cr.af[j], dvt[u]);
+  else dkt[u] = mfma32(cr.qtf[u][j], cr.sf[j], dkt[u]);
+}
+
+template <int D>
+__device__ __forceinline__ void dkdv_tail(const DkdvCarry<D> &cr, f32x16 *dkt, f32x16 *dvt) {
+#pragma unroll
+  for (int i = 0; i < 4 * Geom<D>::kOBlocks; ++i) dkdv_tail_step<D>(cr, i, dkt, dvt);
+}
+
+template <bool DIAG, bool CLAMP, int D>
+__device__ __forceinline__ void dkdv_block_pipelined(const ColBlock<D> &b, const ColBlockT<D> &bt,
+                                                     const bf16x8 *kf, const bf16x8 *vf,
+                                                     const ScanConsts &sc, uint32_t cin_word,
+                                                     float &running, uint32_t &gin_word,
+                                                     float &rho_part, float c2, int l32, int h,
+                                                     DkdvCarry<D> &cr, f32x16 *dkt, f32x16 *dvt) {
+  static_assert(4 * Geom<D>::kOBlocks == 16, "one carried product per element step");
+  f32x16 s, da;
+  col_scores(b, kf, vf, l32, h, s, da);
+  float lq[16];
+  col_rowvals(b.lse2, h, lq);
+  float p[16];
+  col_bids<DIAG>(s, lq, c2, l32, h, p);
+  float iq[16], rq[16];
+  col_rowvals(b.invr, h, iq);
+  col_rowvals(b.dri, h, rq);
+  f32x16 d = mfma32(sc.le[0], pack8(p), zero16());
+  d = mfma32(sc.le[1], pack8(p + 8), d);
+  d = mfma32(sc.ones, word_operand(cin_word), d);
+  // the carried block's closing products, one beside each element step
+  float invd[16], dsg[16], g[16], aw[16];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    dkdv_tail_step<D>(cr, r, dkt, dvt);
+    invd[r] = inv_denominator<CLAMP>(d[r]);
+    const float sg = p[r] * invd[r];
+    aw[r] = sg * iq[r];
+    dsg[r] = __builtin_fmaf(da[r], iq[r], -rq[r]);
+    g[r] = dsg[r] * sg * invd[r];
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // this block's fragments, into the registers the carried products have read
+#pragma unroll
+  for (int u = 0; u < Geom<D>::kOBlocks; ++u)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      cr.qtf[u][j] = lds_vfrag(bt.qt + (32 * u + l32) * kTRow, j, h);
+      cr.gtf[u][j] = lds_vfrag(bt.gt + (32 * u + l32) * kTRow, j, h);
+    }
+  // G = gradient terms of the later blocks + inclusive suffix in this one
+  gin_word = split2_bf16(both_halves_sum(running));
+  f32x16 G = mfma32(sc.ge[0], pack8(g), zero16());
+  G = mfma32(sc.ge[1], pack8(g + 8), G);
+  G = mfma32(sc.ones, word_operand(gin_word), G);
+  float part = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) part += g[r];
+  running += part;
+  float ds[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ds[r] = p[r] * __builtin_fmaf(dsg[r], invd[r], -G[r]);
+  cr.sf[0] = pack8(ds);
+  cr.sf[1] = pack8(ds + 8);
+  cr.af[0] = pack8(aw);
+  cr.af[1] = pack8(aw + 8);
+  // the packed p dp moved to lane = row (keys in the elements), summed
+  f32x16 rt = mfma32(cr.sf[0], sc.ident[0], zero16());
+  rt = mfma32(cr.sf[1], sc.ident[1], rt);
+  float rsum = rt[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) rsum += rt[r];
+  rho_part = both_halves_sum(rsum);
 }
 
 // Waves per SIMD the dQ and dK/dV kernels are built for: two at d = 64; one
@@ -389,6 +485,17 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
   f32x16 dkt[kOB], dvt[kOB];
 #pragma unroll
   for (int u = 0; u < kOB; ++u) dkt[u] = dvt[u] = zero16();
+  // dilution at d = 128: each block's closing products are issued during the next one
+  constexpr bool kPipe = DIL && D > 64;
+  DkdvCarry<D> carry;
+  if constexpr (kPipe) {
+    const bf16x8 z = to_bf16x8(0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int u = 0; u < kOB; ++u)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) carry.qtf[u][j] = carry.gtf[u][j] = z;
+    carry.sf[0] = carry.sf[1] = carry.af[0] = carry.af[1] = z;
+  }
   __builtin_amdgcn_s_waitcnt(0);
 
   const int qs_lo = (kb * kColKeys) / 32;
@@ -476,12 +583,21 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
           vf[c] = lds_frag(vrow, c, h);
         }
       }
-      if (32 * qs == kw0)
-        dkdv_block<DIL, true, CLAMP>(sb[buf], st[buf], kf, vf, sc, cw, running, gw, rho_part, c2,
-                                     l32, h, dkt, dvt);
-      else
-        dkdv_block<DIL, false, CLAMP>(sb[buf], st[buf], kf, vf, sc, cw, running, gw, rho_part, c2,
-                                      l32, h, dkt, dvt);
+      if constexpr (kPipe) {
+        if (32 * qs == kw0)
+          dkdv_block_pipelined<true, CLAMP>(sb[buf], st[buf], kf, vf, sc, cw, running, gw,
+                                            rho_part, c2, l32, h, carry, dkt, dvt);
+        else
+          dkdv_block_pipelined<false, CLAMP>(sb[buf], st[buf], kf, vf, sc, cw, running, gw,
+                                             rho_part, c2, l32, h, carry, dkt, dvt);
+      } else {
+        if (32 * qs == kw0)
+          dkdv_block<DIL, true, CLAMP>(sb[buf], st[buf], kf, vf, sc, cw, running, gw, rho_part, c2,
+                                       l32, h, dkt, dvt);
+        else
+          dkdv_block<DIL, false, CLAMP>(sb[buf], st[buf], kf, vf, sc, cw, running, gw, rho_part,
+                                        c2, l32, h, dkt, dvt);
+      }
       // the wave's keys are all below 32 (qs + 1): block qs keeps an entry for each
       if (DIL && h == 0 && key < T) gin[(size_t)16 * qs * (qs + 1) + key] = gw;
     }
@@ -490,6 +606,7 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
     __syncthreads();
   }
   if (nblk > 0) flush_rho(block_at(nblk - 1), (nblk - 1) & 1);
+  if constexpr (kPipe) dkdv_tail<D>(carry, dkt, dvt);   // the last block's closing products
   if (!wave_live || key >= T) return;
   // lane: key; element (u, r): dim 32u + acc_row(r, h)
   __bf16 *dK = reinterpret_cast<__bf16 *>(a.dk) + head + (size_t)key * D;
