@@ -20,7 +20,11 @@
 //
 // Head dimension D = 64 or 128 (a template parameter of every kernel); at
 // D = 128 the dQ and dK/dV kernels run one workgroup per CU, which doubles
-// the registers per lane for the doubled operands and accumulators.
+// the registers per lane for the doubled operands and accumulators.  With
+// one wave per SIMD only a wave's own instruction order can overlap its
+// matrix-core and vector work, so at D = 128 the operands of the closing
+// products are read into registers ahead of them, and the dilution dK/dV
+// pass issues each block's closing products during the next block.
 //
 // Passes (dilution; tempered runs 1, 4, 4b and 3 only, dK/dV top-down):
 //   1 bwd_prep_kernel   per row: log2-domain lse, 1/r, delta/r
