@@ -650,6 +650,11 @@ struct RhoBlock {
   __bf16 q[32 * Geom<D>::kKRow];   // Q rows (A operand of S)
   __bf16 qt[D * kTRow];            // Q^T, dim-major (A operand of Y^T)
   float lse2[32], rho[32];
+  // The two blocks of a stage then sit 64 bytes off a multiple of 128 apart,
+  // so that the transposed stores of row pairs kp and kp + 16 (one into each
+  // block) fall in different LDS banks (without it: 2-way conflicts, 4e7
+  // conflict cycles per launch at d = 128).
+  float pad[16];
 };
 
 template <int D>
