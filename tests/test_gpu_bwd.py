@@ -294,6 +294,25 @@ def test_bwd_d128_per_head_tau_and_dtau(mode):
     check_dtau(got[3], ref[0], inp, g, taus, ref[4], f"d128 per-head mode={mode}")
 
 
+@pytest.mark.parametrize("mode", [0, 1], ids=["tempered", "dilution"])
+def test_bwd_d128_long_walk_t2049(mode):
+    """d = 128 at T = 2049 (65 blocks of 32 rows, the last one ragged) on the
+    focal heavy-key recipe with learned per-head multipliers, element by
+    element against the oracle.  A key wave walks up to 65 blocks here, so the
+    dK/dV products each block carries into the next (dilution), and the
+    closing products' operands read ahead in both passes, run over a long
+    walk and across every block boundary."""
+    w = PREFILL["focal_d128_t16k"]
+    inp = prefill_inputs(w, T=2049, H=1)
+    g = draw_grad(1, 1, 2049, 128, seed=w.seed + 1)
+    taus = learned_tau(1, 1, 128, seed=w.seed + 1)
+    got = run_bwd_heads(inp, g, mode, tau_bh=taus, eps=w.eps)
+    ref = oracle.attn_bwd(oracle.Bf16(inp.q), oracle.Bf16(inp.k), oracle.Bf16(inp.v),
+                          oracle.Bf16(g), 1.0, w.eps, mode, tau_bh=taus, want_dtau=True)
+    check_grads(got[:3], ref[:3], f"d128 T=2049 mode={mode}")
+    check_dtau(got[3], ref[0], inp, g, taus, ref[4], f"d128 T=2049 mode={mode}")
+
+
 def test_bwd_d128_value_totals_focal_t16k():
     """At the focal workload's full length (T = 16384, d = 128, learned
     per-head multipliers; 4 of its 20 heads): the sum invariants in either
