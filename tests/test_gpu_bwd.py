@@ -313,6 +313,25 @@ def test_bwd_d128_long_walk_t2049(mode):
     check_dtau(got[3], ref[0], inp, g, taus, ref[4], f"d128 T=2049 mode={mode}")
 
 
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["dilution_t16k", "focal_d128_t16k"])
+def test_bwd_t16k_one_head_against_oracle(name):
+    """The dilution backward at the workloads' full length, T = 16384, on one
+    head: every element of dq, dk and dv (and dL/dtau, with the focal
+    recipe's learned multiplier) against the oracle itself.  The other
+    full-length checks compare with the fp32 kernels and check invariants."""
+    w = PREFILL[name]
+    inp = prefill_inputs(w, H=1)
+    g = draw_grad(1, 1, w.T, w.d, seed=w.seed + 3)
+    taus = learned_tau(1, 1, w.d, seed=w.seed + 3) if w.d == 128 else None
+    got = run_bwd_heads(inp, g, 1, tau_bh=taus, eps=w.eps)
+    ref = oracle.attn_bwd(oracle.Bf16(inp.q), oracle.Bf16(inp.k), oracle.Bf16(inp.v),
+                          oracle.Bf16(g), 1.0, w.eps, 1, tau_bh=taus, want_dtau=taus is not None)
+    check_grads(got[:3], ref[:3], f"{name} one head vs oracle")
+    if taus is not None:
+        check_dtau(got[3], ref[0], inp, g, taus, ref[4], f"{name} one head vs oracle")
+
+
 def test_bwd_d128_value_totals_focal_t16k():
     """At the focal workload's full length (T = 16384, d = 128, learned
     per-head multipliers; 4 of its 20 heads): the sum invariants in either
