@@ -314,22 +314,24 @@ def test_bwd_d128_long_walk_t2049(mode):
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("mode", [0, 1], ids=["tempered", "dilution"])
 @pytest.mark.parametrize("name", ["dilution_t16k", "focal_d128_t16k"])
-def test_bwd_t16k_one_head_against_oracle(name):
-    """The dilution backward at the workloads' full length, T = 16384, on one
-    head: every element of dq, dk and dv (and dL/dtau, with the focal
+def test_bwd_t16k_one_head_against_oracle(name, mode):
+    """Either operator's backward at the workloads' full length, T = 16384,
+    on one head: every element of dq, dk and dv (and dL/dtau, with the focal
     recipe's learned multiplier) against the oracle itself.  The other
     full-length checks compare with the fp32 kernels and check invariants."""
     w = PREFILL[name]
     inp = prefill_inputs(w, H=1)
     g = draw_grad(1, 1, w.T, w.d, seed=w.seed + 3)
     taus = learned_tau(1, 1, w.d, seed=w.seed + 3) if w.d == 128 else None
-    got = run_bwd_heads(inp, g, 1, tau_bh=taus, eps=w.eps)
+    got = run_bwd_heads(inp, g, mode, tau_bh=taus, eps=w.eps)
     ref = oracle.attn_bwd(oracle.Bf16(inp.q), oracle.Bf16(inp.k), oracle.Bf16(inp.v),
-                          oracle.Bf16(g), 1.0, w.eps, 1, tau_bh=taus, want_dtau=taus is not None)
-    check_grads(got[:3], ref[:3], f"{name} one head vs oracle")
+                          oracle.Bf16(g), 1.0, w.eps, mode, tau_bh=taus,
+                          want_dtau=taus is not None)
+    check_grads(got[:3], ref[:3], f"{name} mode={mode} one head vs oracle")
     if taus is not None:
-        check_dtau(got[3], ref[0], inp, g, taus, ref[4], f"{name} one head vs oracle")
+        check_dtau(got[3], ref[0], inp, g, taus, ref[4], f"{name} mode={mode} one head vs oracle")
 
 
 def test_bwd_d128_value_totals_focal_t16k():
