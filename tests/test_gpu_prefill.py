@@ -259,3 +259,23 @@ def test_chunk_row_sums_match_whole_prefill():
     rel = float(np.max(np.abs(got / ref - 1.0)))
     print(f"chunk row sums vs whole: max rel {rel:.3e}")
     assert np.all(ref > 0) and rel <= 5e-3
+
+
+@pytest.mark.timeout(600)
+def test_bench_chunking_t16k_against_oracle():
+    """The measured chunked-prefill configuration at full length: T = 16384
+    (the dilution workload's recipe, heavy keys) as 8 chunks of 2048 rows over
+    the cache, demand carried in place, 2 heads; every row and the final
+    demand per key against the oracle's whole prefill."""
+    from transformer_attention_causal_amd.workloads import PREFILL, prefill_inputs
+
+    w = PREFILL["dilution_t16k"]
+    inp = prefill_inputs(w, H=2)
+    bounds = tuple(range(0, w.T + 1, 2048))
+    out, lse, dem = run_chunks(inp, bounds, w.T + 64, 1.0, ab.ATTN_DILUTION, w.eps)
+    ref, rlse, rdem = oracle.dilution_fwd(*oracle_qkv(inp), 1.0, w.eps)
+    assert_close(out, ref, "bf16", "8 x 2048 chunks at T=16384")
+    lse_err = float(np.max(np.abs(lse - rlse)))
+    print(f"8 x 2048 chunks lse: max-abs {lse_err:.3e}")
+    assert lse_err <= 2e-3
+    check_demand(dem, rdem, w.T, "bf16", "8 x 2048 chunks")

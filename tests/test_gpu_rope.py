@@ -167,3 +167,19 @@ def test_rope_chunks_carry_demand(dtype, d):
     dem = D.cpu().numpy()[:, :, :T]
     tol = 2e-2 if dtype == "bf16" else 1e-5
     assert np.max(np.abs(dem - rdem)) <= tol * max(1.0, float(rdem.max()))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("mode", [ab.ATTN_DILUTION, ab.ATTN_TEMPERED])
+def test_rope_focal_t16k_one_head(mode):
+    """The rotation at the focal workload's full length (T = 16384, d = 128,
+    heavy keys, a learned per-head multiplier), one head, against the oracle
+    on every row."""
+    from transformer_attention_causal_amd.workloads import PREFILL, prefill_inputs
+
+    w = PREFILL["focal_d128_t16k"]
+    inp = prefill_inputs(w, H=1)
+    freq = rope_freqs(128)
+    taus = learned_tau(1, 1, 128, seed=w.seed + 5)
+    out = device_rope(inp, freq, 0, 1.0, mode, tau_bh=taus)
+    check_rope(out, inp, freq, 0, 1.0, mode, f"rope focal t16k mode={mode}", tau_bh=taus)
