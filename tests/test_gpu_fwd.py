@@ -188,6 +188,45 @@ def test_dilution_with_huge_eps_is_tempered(d):
     assert ma <= 2e-2 * max(1.0, float(np.max(np.abs(tmp)))) and rr <= 1e-2
 
 
+@pytest.mark.parametrize("T", [2048, 2049])
+def test_fp32_tempered_either_side_of_tiling(T):
+    """The d = 64 fp32 tempered kernel accumulates each row's output in one
+    register set up to 2048 keys and per 64-key tile beyond: both forms, one
+    key apart, against the oracle at the fp32 bar."""
+    w = PREFILL["dilution_t16k"]
+    inp = prefill_inputs(w, T=T, H=1)
+    wide = {n: (getattr(inp, n).astype(np.uint32) << 16).view(np.float32) for n in ("q", "k", "v")}
+    f32 = type(inp)(**{**inp.__dict__, **wide, "dtype": "f32"})
+    out, lse = run_fwd(f32, TAU4, ab.ATTN_TEMPERED, want_lse=True)
+    ref, rlse = oracle.tempered_fwd(*oracle_qkv(f32), TAU4)
+    assert_close(out, ref, "f32", f"fp32 tempered T={T}")
+    assert float(np.max(np.abs(lse - rlse))) <= 1e-5
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["dilution_t16k", "focal_d128_t16k"])
+def test_fp32_t16k_one_head_against_oracle(name):
+    """The fp32 kernels at the full length, T = 16384, on one head of each
+    workload's recipe (values widened exactly from bf16), both operators:
+    every row, the LSE and the final demand per key against the oracle at the
+    fp32 bar, the bar the bf16-against-fp32 comparisons lean on."""
+    w = PREFILL[name]
+    inp = prefill_inputs(w, H=1)
+    wide = {n: (getattr(inp, n).astype(np.uint32) << 16).view(np.float32) for n in ("q", "k", "v")}
+    f32 = type(inp)(**{**inp.__dict__, **wide, "dtype": "f32"})
+    out, lse, dem = run_fwd(f32, 1.0, ab.ATTN_DILUTION, w.eps, want_lse=True, want_demand=True)
+    ref, rlse, rdem = oracle.dilution_fwd(*oracle_qkv(f32), 1.0, w.eps)
+    assert_close(out, ref, "f32", f"{name} fp32 dilution t16k")
+    lse_err = float(np.max(np.abs(lse - rlse)))
+    dem_err = float(np.max(np.abs(dem - rdem) / np.maximum(1.0, np.abs(rdem))))
+    print(f"{name} fp32 dilution t16k: lse {lse_err:.3e} demand {dem_err:.3e}")
+    assert lse_err <= 1e-5 and dem_err <= 1e-5
+    out, lse = run_fwd(f32, TAU4, ab.ATTN_TEMPERED, want_lse=True)
+    ref, rlse = oracle.tempered_fwd(*oracle_qkv(f32), TAU4)
+    assert_close(out, ref, "f32", f"{name} fp32 tempered t16k")
+    assert float(np.max(np.abs(lse - rlse))) <= 1e-5
+
+
 @pytest.mark.timeout(600)
 def test_t16k_bf16_against_fp32_kernels_all_rows():
     """The full T = 16384 workload, every row of all 16 heads (the oracle

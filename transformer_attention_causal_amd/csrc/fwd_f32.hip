@@ -22,7 +22,12 @@ constexpr int kFW = 4;            // waves per workgroup: they share each LDS ti
 constexpr int kFB = kFR * kFW;    // rows (row kernels) or keys (column sums) per workgroup
 constexpr float kNoRowF32 = 1e30f;  // log-sum-exp of a position that holds no row
 
-template <int MODE, int D>
+// Rows of up to this many keys keep the d = 64 tempered kernel's single
+// output accumulator (two waves per SIMD); longer rows take the tiled form
+// below, which holds full single precision at one wave per SIMD.
+constexpr int kUntiledMaxT = 2048;
+
+template <int MODE, int D, bool TILED>
 __global__ void __launch_bounds__(kFB) rows_f32_kernel(FwdArgs a, int nqb) {
   __shared__ __attribute__((aligned(16))) float sK[kFR * D];
   __shared__ __attribute__((aligned(16))) float sV[MODE == kRowLse ? 4 : kFR * D];
@@ -44,13 +49,29 @@ __global__ void __launch_bounds__(kFB) rows_f32_kernel(FwdArgs a, int nqb) {
   const float *K = reinterpret_cast<const float *>(a.k) + khead;
   const float *V = reinterpret_cast<const float *>(a.v) + khead;
 
-  float q[D], acc[D];
+  // Long rows keep full single precision: the row sum l is a compensated
+  // (Kahan) sum, and the output accumulates per 64-key tile (acct, from zero)
+  // before the tile is added to the running acc, so rounding grows with
+  // 64 + T/64 terms rather than T.  Against the running max m both hold
+  // scaled values; a_tile is the product of this tile's rescale factors.
+  // Untiled (TILED = false, the d = 64 tempered kernel on rows of up to
+  // kUntiledMaxT keys) the key loop accumulates straight into acc.
+  constexpr bool kTiled = TILED && MODE != kRowLse;
+  float q[D], acc[D], acct[kTiled ? D : 1];
+  float *ta = kTiled ? acct : acc;   // what the key loop accumulates into
 #pragma unroll
   for (int e = 0; e < D; ++e) {
     q[e] = live ? Q[(size_t)li * D + e] : 0.0f;
     acc[e] = 0.0f;
   }
-  float m = -INFINITY, l = 0.0f, lse2 = 0.0f;
+  float m = -INFINITY, l = 0.0f, lc = 0.0f, lse2 = 0.0f;
+  // l += x, compensated (lc carries the rounding of the additions so far)
+  auto add_l = [&](float x) {
+    const float y = x - lc;
+    const float t2 = l + y;
+    lc = (t2 - l) - y;
+    l = t2;
+  };
   const int qs = i >> 5;
   const float *cin_blk = nullptr;
   if constexpr (MODE == kRowShare) {
@@ -72,6 +93,11 @@ __global__ void __launch_bounds__(kFB) rows_f32_kernel(FwdArgs a, int nqb) {
     }
     __syncthreads();
     const int jn = min(kFR, kend - j0);   // <= 0 once the wave's keys are done
+    if constexpr (kTiled) {
+#pragma unroll
+      for (int e = 0; e < D; ++e) acct[e] = 0.0f;
+    }
+    float a_tile = 1.0f;
     for (int jj = 0; jj < jn; ++jj) {
       const int j = j0 + jj;
       float s = 0.0f;
@@ -84,10 +110,13 @@ __global__ void __launch_bounds__(kFB) rows_f32_kernel(FwdArgs a, int nqb) {
           const float m_new = fmaxf(m, x);
           const float alpha = exp2f(m - m_new);
           const float p = exp2f(x - m_new);
-          l = l * alpha + p;
+          l *= alpha;
+          lc *= alpha;
+          add_l(p);
           if constexpr (MODE == kRowTempered) {
+            a_tile *= alpha;
 #pragma unroll
-            for (int e = 0; e < D; ++e) acc[e] = __builtin_fmaf(p, sV[jj * D + e], acc[e] * alpha);
+            for (int e = 0; e < D; ++e) ta[e] = __builtin_fmaf(p, sV[jj * D + e], ta[e] * alpha);
           }
           m = m_new;
         }
@@ -105,10 +134,15 @@ __global__ void __launch_bounds__(kFB) rows_f32_kernel(FwdArgs a, int nqb) {
         float base = (live && j < 32 * (qs + 1)) ? cin_blk[j] : 0.0f;
         base = fmaxf(base + a.eps, eps_floor);
         const float share = p / (base + incl);
-        l += share;
+        add_l(share);
 #pragma unroll
-        for (int e = 0; e < D; ++e) acc[e] = __builtin_fmaf(share, sV[jj * D + e], acc[e]);
+        for (int e = 0; e < D; ++e) ta[e] = __builtin_fmaf(share, sV[jj * D + e], ta[e]);
       }
+    }
+    if constexpr (kTiled) {
+      // the tile's sum into the running one (a_tile = 1 in the share pass)
+#pragma unroll
+      for (int e = 0; e < D; ++e) acc[e] = __builtin_fmaf(acc[e], a_tile, acct[e]);
     }
   }
   if (!live) return;
@@ -190,10 +224,20 @@ static hipError_t launch_rows_f32_d(int mode, const FwdArgs &a, hipStream_t s) {
   dim3 grid((unsigned)(nqb * a.BH)), block(kFB);
   switch (mode) {
     case kRowTempered:
-      hipLaunchKernelGGL((rows_f32_kernel<kRowTempered, D>), grid, block, 0, s, a, nqb);
+      if constexpr (D == 64) {
+        if (a.T <= kUntiledMaxT) {
+          hipLaunchKernelGGL((rows_f32_kernel<kRowTempered, D, false>), grid, block, 0, s, a, nqb);
+          break;
+        }
+      }
+      hipLaunchKernelGGL((rows_f32_kernel<kRowTempered, D, true>), grid, block, 0, s, a, nqb);
       break;
-    case kRowLse: hipLaunchKernelGGL((rows_f32_kernel<kRowLse, D>), grid, block, 0, s, a, nqb); break;
-    default: hipLaunchKernelGGL((rows_f32_kernel<kRowShare, D>), grid, block, 0, s, a, nqb); break;
+    case kRowLse:
+      hipLaunchKernelGGL((rows_f32_kernel<kRowLse, D, true>), grid, block, 0, s, a, nqb);
+      break;
+    default:
+      hipLaunchKernelGGL((rows_f32_kernel<kRowShare, D, true>), grid, block, 0, s, a, nqb);
+      break;
   }
   return hipGetLastError();
 }
