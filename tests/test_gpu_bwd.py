@@ -487,6 +487,25 @@ def test_bwd_fp32_ragged_lengths(mode, T, d):
     check_dtau_f32(got[3], ref[0], inp, g, TAU4, ref[4], f"fp32 d={d} mode={mode} T={T}")
 
 
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("mode", [0, 1], ids=["tempered", "dilution"])
+@pytest.mark.parametrize("name", ["dilution_t16k", "focal_d128_t16k"])
+def test_bwd_fp32_t16k_one_head_against_oracle(name, mode):
+    """The fp32 backward at the workloads' full length, T = 16384, on one
+    head (values widened exactly from the bf16 recipe): every element of dq,
+    dk, dv and dL/dtau against the oracle at the fp32 bar."""
+    w = PREFILL[name]
+    inp = prefill_inputs(w, H=1)
+    wide = {n: (getattr(inp, n).astype(np.uint32) << 16).view(np.float32) for n in ("q", "k", "v")}
+    f32 = type(inp)(**{**inp.__dict__, **wide, "dtype": "f32"})
+    g = grad_f32(1, 1, w.T, w.d, seed=w.seed + 4)
+    taus = learned_tau(1, 1, w.d, seed=w.seed + 4)
+    got = run_bwd_f32(f32, g, mode, eps=w.eps, tau_bh=taus)
+    ref = oracle.attn_bwd(f32.q, f32.k, f32.v, g, 1.0, w.eps, mode, tau_bh=taus, want_dtau=True)
+    check_grads_f32(got[:3], ref[:3], f"fp32 {name} mode={mode} t16k")
+    check_dtau_f32(got[3], ref[0], f32, g, taus, ref[4], f"fp32 {name} mode={mode} t16k")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("eps", [0.0, 0.3])
 def test_bwd_fp32_dilution_eps_and_per_head_tau(eps, d):
