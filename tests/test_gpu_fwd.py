@@ -174,6 +174,28 @@ def test_stage_calls_are_the_forward(dtype, d, eps):
     assert_close(o2.float().cpu().numpy(), ref, dtype, f"stage calls {dtype} d={d} eps={eps}")
 
 
+def test_stage_calls_keep_their_workspace():
+    """The stage callables own the workspace they allocate: tensors allocated
+    after the callables are made (which may reuse any memory the allocator
+    holds free) are never written by the stages, and the output is still the
+    forward's."""
+    import torch
+
+    B, H, T, d = 1, 2, 1024, 64
+    inp = draw_qkv(B, H, T, d, "bf16", seed=4150, heavy_frac=0.05)
+    q, k, v = device_qkv(inp)
+    ref = ab.fwd(q, k, v, tau=TAU4, mode=ab.ATTN_DILUTION, eps=1e-6)
+    nbytes = ab.attn_fwd_workspace_bytes(B, H, T, d, ab.ATTN_DILUTION, ab.ATTN_BF16)
+    assert nbytes > 0
+    stages, out = ab.dilution_stages(q, k, v, tau=TAU4, eps=1e-6)
+    fill = [torch.full((nbytes,), 0x5A, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    for stage in stages:
+        stage()
+    torch.cuda.synchronize()
+    assert all(bool((f == 0x5A).all()) for f in fill)
+    assert torch.equal(out, ref)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_dilution_with_huge_eps_is_tempered(d):
     """With eps far above every demand the shares are p / eps, whose row

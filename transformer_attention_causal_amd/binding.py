@@ -360,7 +360,7 @@ def bwd(q, k, v, out, dout, lse, rowsum=None, tau: float = 1.0, mode: int = ATTN
                      fwd_workspace.data_ptr() if fwd_workspace is not None else None,
                      (fwd_workspace.numel() * fwd_workspace.element_size()
                       if fwd_workspace is not None else 0),
-                     workspace.data_ptr(), ws_bytes, _stream_handle(q.device))
+                     ptr(workspace), ws_bytes, _stream_handle(q.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd_ex")
     return dq, dk, dv
@@ -445,7 +445,9 @@ def dilution_stages(q, k, v, tau: float = 1.0, eps: float = 1e-6, out=None, work
                     lse_out=None, demand_out=None):
     """Run the three dilution stages as separate calls; returns a list of
     three zero-argument callables (lse, committed, shares) that enqueue one
-    stage each on the current stream, and the output tensor they fill."""
+    stage each on the current stream, and the output tensor they fill.  The
+    callables hold the workspace (allocated here when none is given), so it
+    stays allocated for as long as they do."""
     import torch
 
     if q.dim() != 4:
@@ -462,28 +464,33 @@ def dilution_stages(q, k, v, tau: float = 1.0, eps: float = 1e-6, out=None, work
         workspace, ws_bytes = fwd_workspace(B, H, T, ATTN_DILUTION, code, q.device, d)
     else:
         ws_bytes = workspace.numel() * workspace.element_size()
-    wp = workspace.data_ptr()
-    lp = lse_out.data_ptr() if lse_out is not None else None
-    dp = demand_out.data_ptr() if demand_out is not None else None
+    # The closures read every pointer from the tensors themselves, so each
+    # tensor (the workspace included) lives as long as the closures: a raw
+    # pointer alone would let the allocator hand its memory to a later tensor
+    # before a stage writes there.
 
     def check(st, where):
         if st != ATTN_OK:
             raise AttnError(st, where)
 
+    def ptr(t):
+        return t.data_ptr() if t is not None else None
+
     def lse():
-        check(attn_dilution_lse(q.data_ptr(), k.data_ptr(), B, H, T, d, float(tau), code, wp,
-                                ws_bytes, lp, _stream_handle(q.device)), "attn_dilution_lse")
+        check(attn_dilution_lse(q.data_ptr(), k.data_ptr(), B, H, T, d, float(tau), code,
+                                ptr(workspace), ws_bytes, ptr(lse_out),
+                                _stream_handle(q.device)), "attn_dilution_lse")
 
     def committed():
         check(attn_dilution_committed(q.data_ptr(), k.data_ptr(), B, H, T, d, float(tau),
-                                      float(eps), code, wp, ws_bytes, dp,
-                                      _stream_handle(q.device)),
+                                      float(eps), code, ptr(workspace), ws_bytes,
+                                      ptr(demand_out), _stream_handle(q.device)),
               "attn_dilution_committed")
 
     def shares():
         check(attn_dilution_shares(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B,
-                                   H, T, d, float(tau), float(eps), code, wp, ws_bytes,
-                                   _stream_handle(q.device)), "attn_dilution_shares")
+                                   H, T, d, float(tau), float(eps), code, ptr(workspace),
+                                   ws_bytes, _stream_handle(q.device)), "attn_dilution_shares")
 
     return [lse, committed, shares], out
 
@@ -524,7 +531,7 @@ def decode(q, kcache, vcache, demand, tau: float = 1.0, eps: float = 1e-6, kv_le
                         out.data_ptr(), S, H, Lcap,
                         kv_len.data_ptr() if kv_len is not None else None, d, float(tau),
                         tau_sh.data_ptr() if tau_sh is not None else None, float(eps),
-                        _dtype_code(q), workspace.data_ptr(), ws_bytes, _stream_handle(q.device))
+                        _dtype_code(q), ptr(workspace), ws_bytes, _stream_handle(q.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode_ex")
     return out
