@@ -500,3 +500,31 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(ab, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         ab.load()
+
+
+def _host_calls():
+    import torch
+
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    rows = torch.zeros(1, 2, 8, dtype=torch.float32)
+    dq = torch.zeros(2, 2, 64, dtype=torch.bfloat16)
+    cache = torch.zeros(2, 2, 16, 64, dtype=torch.bfloat16)
+    dem = torch.zeros(2, 2, 16, dtype=torch.float32)
+    return {
+        "fwd": lambda: ab.fwd(q, q, q),
+        "fwd_noalloc": lambda: ab.fwd_noalloc(q, q, q, q.clone()),
+        "bwd": lambda: ab.bwd(q, q, q, q, q, rows, rows, mode=ab.ATTN_DILUTION),
+        "prefill": lambda: ab.prefill(q, q, q, 8),
+        "dilution_stages": lambda: ab.dilution_stages(q, q, q),
+        "decode": lambda: ab.decode(dq, cache, cache, dem),
+    }
+
+
+@pytest.mark.parametrize("name", ["fwd", "fwd_noalloc", "bwd", "prefill", "dilution_stages",
+                                  "decode"])
+def test_wrappers_refuse_host_tensors(name):
+    """The kernels dereference every pointer they are given, so the torch
+    wrappers refuse tensors in host memory before anything reaches the
+    library."""
+    with pytest.raises(ValueError, match="GPU"):
+        _host_calls()[name]()

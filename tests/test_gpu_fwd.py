@@ -196,6 +196,42 @@ def test_stage_calls_keep_their_workspace():
     assert torch.equal(out, ref)
 
 
+def test_wrappers_refuse_misplaced_buffers():
+    """Workspaces, per-head arrays, lengths and outputs in host memory, of the
+    wrong shape or dtype, or caches of another dtype are refused before any
+    launch."""
+    import torch
+
+    B, H, T, d = 1, 2, 64, 64
+    g = dict(device="cuda")
+    q = torch.zeros(B, H, T, d, dtype=torch.bfloat16, **g)
+    rows = torch.zeros(B, H, T, dtype=torch.float32, **g)
+    host_ws = torch.zeros(1 << 20, dtype=torch.uint8)
+    host_bh = torch.ones(B, H, dtype=torch.float32)
+    cache = torch.zeros(2, H, 128, d, dtype=torch.bfloat16, **g)
+    dem = torch.zeros(2, H, 128, dtype=torch.float32, **g)
+    qd = torch.zeros(2, H, d, dtype=torch.bfloat16, **g)
+    bad = [
+        lambda: ab.fwd(q, q, q, mode=ab.ATTN_DILUTION, workspace=host_ws),
+        lambda: ab.dilution_stages(q, q, q, workspace=host_ws),
+        lambda: ab.bwd(q, q, q, q, q, rows, rows, mode=ab.ATTN_DILUTION, workspace=host_ws),
+        lambda: ab.bwd(q, q, q, q, q, rows, rows, mode=ab.ATTN_DILUTION, fwd_workspace=host_ws),
+        lambda: ab.bwd(q, q, q, q, q, rows, rows, mode=ab.ATTN_DILUTION, tau_bh=host_bh),
+        lambda: ab.prefill(q, q, q, T, tau_bh=host_bh),
+        lambda: ab.prefill(q, q, q, T, demand_in=torch.zeros(B, H, T)),
+        lambda: ab.prefill(q, q, q, T, workspace=host_ws),
+        lambda: ab.decode(qd, cache, cache, dem, kv_len=torch.full((2,), 5, dtype=torch.int32)),
+        lambda: ab.decode(qd, cache, cache, dem, tau_sh=torch.ones(2, H)),
+        lambda: ab.decode(qd, cache, cache, dem, out=torch.zeros(2, H, d, **g)),
+        lambda: ab.decode(qd, cache.float(), cache.float(), dem),
+        lambda: ab.decode(qd, cache, cache, dem, workspace=host_ws),
+    ]
+    for i, call in enumerate(bad):
+        with pytest.raises(ValueError):
+            call()
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_dilution_with_huge_eps_is_tempered(d):
     """With eps far above every demand the shares are p / eps, whose row

@@ -220,6 +220,11 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _ptr(t):
+    """The device address of an optional tensor (None passes through)."""
+    return t.data_ptr() if t is not None else None
+
+
 def _stream_handle(device):
     import torch
 
@@ -234,6 +239,31 @@ def _check_like(t, ref, name):
             or t.device != ref.device:
         raise ValueError(f"{name} must be a contiguous {ref.dtype} tensor of shape "
                          f"{tuple(ref.shape)} on {ref.device}")
+
+
+def _check_gpu(t, name):
+    """``t`` must be a tensor in GPU memory: the kernels dereference its pointer."""
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a tensor on a GPU device")
+
+
+def _check_buf(t, device, name):
+    """``t`` (optional: a workspace or another byte buffer) must be a contiguous
+    tensor on ``device``."""
+    if t is None:
+        return
+    if t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor on {device}")
+
+
+def _check_small(t, shape, dtype, device, name):
+    """``t`` (optional) must be a contiguous ``dtype`` tensor of ``shape`` on ``device``."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() \
+            or t.device != device:
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
+                         f"on {device}")
 
 
 def _check_rows(t, shape, device, name):
@@ -265,10 +295,12 @@ def fwd(q, k, v, tau: float = 1.0, mode: int = ATTN_TEMPERED, eps: float = 1e-6,
     if q.dim() != 4:
         raise ValueError("q, k, v must share one [B,H,T,d] shape")
     code = _dtype_code(q)
+    _check_gpu(q, "q")
     _check_like(q, q, "q")
     _check_like(k, q, "k")
     _check_like(v, q, "v")
     _check_like(out, q, "out")
+    _check_buf(workspace, q.device, "workspace")
     B, H, T, d = q.shape
     for name, t in (("lse_out", lse_out), ("demand_out", demand_out), ("rowsum_out", rowsum_out)):
         _check_rows(t, (B, H, T), q.device, name)
@@ -298,6 +330,7 @@ def fwd_noalloc(q, k, v, out, tau: float = 1.0, mode: int = ATTN_TEMPERED, eps: 
     if q.dim() != 4 or out is None:
         raise ValueError("q, k, v, out must share one [B,H,T,d] shape")
     code = _dtype_code(q)
+    _check_gpu(q, "q")
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
         _check_like(t, q, name)
     B, H, T, d = q.shape
@@ -331,9 +364,12 @@ def bwd(q, k, v, out, dout, lse, rowsum=None, tau: float = 1.0, mode: int = ATTN
     if q.dim() != 4:
         raise ValueError("q, k, v, out, dout must share one [B,H,T,d] shape")
     code = _dtype_code(q)
+    _check_gpu(q, "q")
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq),
                     ("dk", dk), ("dv", dv)):
         _check_like(t, q, name)
+    _check_buf(workspace, q.device, "workspace")
+    _check_buf(fwd_workspace, q.device, "fwd_workspace")
     B, H, T, d = q.shape
     if lse is None:
         raise ValueError("lse (the forward's lse_out) is required")
@@ -349,9 +385,7 @@ def bwd(q, k, v, out, dout, lse, rowsum=None, tau: float = 1.0, mode: int = ATTN
     else:
         ws_bytes = workspace.numel() * workspace.element_size()
     for name, t in (("tau_bh", tau_bh), ("dtau_out", dtau_out)):
-        if t is not None and (t.shape != (B, H) or t.dtype != torch.float32
-                              or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous float32 [B,H] tensor")
+        _check_small(t, (B, H), torch.float32, q.device, name)
     st = attn_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
                      lse.data_ptr(), rowsum.data_ptr() if rowsum is not None else None,
                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, T, d, float(tau),
@@ -360,7 +394,7 @@ def bwd(q, k, v, out, dout, lse, rowsum=None, tau: float = 1.0, mode: int = ATTN
                      fwd_workspace.data_ptr() if fwd_workspace is not None else None,
                      (fwd_workspace.numel() * fwd_workspace.element_size()
                       if fwd_workspace is not None else 0),
-                     ptr(workspace), ws_bytes, _stream_handle(q.device))
+                     _ptr(workspace), ws_bytes, _stream_handle(q.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd_ex")
     return dq, dk, dv
@@ -385,16 +419,15 @@ def prefill(q, kcache, vcache, Tk: int, tau: float = 1.0, mode: int = ATTN_DILUT
     Lcap = kcache.shape[2]
     if kcache.shape[:2] != (B, H) or kcache.shape[3] != d:
         raise ValueError("q and the caches disagree on B, H or d")
+    _check_gpu(q, "q")
     for t in (q, kcache, vcache):
-        if not t.is_contiguous() or t.dtype != q.dtype:
-            raise ValueError("q and the caches must be contiguous and share one dtype")
-    for t in (demand_in, demand_out):
-        if t is not None and (t.shape != (B, H, Lcap) or t.dtype != torch.float32
-                              or not t.is_contiguous()):
-            raise ValueError("demand arrays must be contiguous float32 [B,H,Lcap]")
-    if tau_bh is not None and (tau_bh.shape != (B, H) or tau_bh.dtype != torch.float32
-                               or not tau_bh.is_contiguous()):
-        raise ValueError("tau_bh must be a contiguous float32 [B,H] tensor")
+        if not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q and the caches must be contiguous, on one device and share "
+                             "one dtype")
+    for name, t in (("demand_in", demand_in), ("demand_out", demand_out)):
+        _check_small(t, (B, H, Lcap), torch.float32, q.device, name)
+    _check_small(tau_bh, (B, H), torch.float32, q.device, "tau_bh")
+    _check_buf(workspace, q.device, "workspace")
     code = _dtype_code(q)
     _check_like(out, q, "out")
     for name, t in (("lse_out", lse_out), ("rowsum_out", rowsum_out)):
@@ -453,8 +486,10 @@ def dilution_stages(q, k, v, tau: float = 1.0, eps: float = 1e-6, out=None, work
     if q.dim() != 4:
         raise ValueError("q, k, v must share one [B,H,T,d] shape")
     code = _dtype_code(q)
+    _check_gpu(q, "q")
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
         _check_like(t, q, name)
+    _check_buf(workspace, q.device, "workspace")
     B, H, T, d = q.shape
     for name, t in (("lse_out", lse_out), ("demand_out", demand_out)):
         _check_rows(t, (B, H, T), q.device, name)
@@ -473,23 +508,20 @@ def dilution_stages(q, k, v, tau: float = 1.0, eps: float = 1e-6, out=None, work
         if st != ATTN_OK:
             raise AttnError(st, where)
 
-    def ptr(t):
-        return t.data_ptr() if t is not None else None
-
     def lse():
         check(attn_dilution_lse(q.data_ptr(), k.data_ptr(), B, H, T, d, float(tau), code,
-                                ptr(workspace), ws_bytes, ptr(lse_out),
+                                _ptr(workspace), ws_bytes, _ptr(lse_out),
                                 _stream_handle(q.device)), "attn_dilution_lse")
 
     def committed():
         check(attn_dilution_committed(q.data_ptr(), k.data_ptr(), B, H, T, d, float(tau),
-                                      float(eps), code, ptr(workspace), ws_bytes,
-                                      ptr(demand_out), _stream_handle(q.device)),
+                                      float(eps), code, _ptr(workspace), ws_bytes,
+                                      _ptr(demand_out), _stream_handle(q.device)),
               "attn_dilution_committed")
 
     def shares():
         check(attn_dilution_shares(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B,
-                                   H, T, d, float(tau), float(eps), code, ptr(workspace),
+                                   H, T, d, float(tau), float(eps), code, _ptr(workspace),
                                    ws_bytes, _stream_handle(q.device)), "attn_dilution_shares")
 
     return [lse, committed, shares], out
@@ -508,30 +540,34 @@ def decode(q, kcache, vcache, demand, tau: float = 1.0, eps: float = 1e-6, kv_le
     optional [S,H] fp32 tensor of per-(sequence, head) multipliers.  Returns ``out``."""
     import torch
 
+    if kcache.dim() != 4:
+        raise ValueError("decode shapes must be q [S,H,d], caches [S,H,L,d], demand [S,H,L]")
     S, H, Lcap, d = kcache.shape
     if vcache.shape != kcache.shape or q.shape != (S, H, d) or demand.shape != (S, H, Lcap):
         raise ValueError("decode shapes must be q [S,H,d], caches [S,H,L,d], demand [S,H,L]")
     if demand.dtype != torch.float32:
         raise TypeError("demand must be float32")
+    _check_gpu(q, "q")
     for t in (q, kcache, vcache, demand):
-        if not t.is_contiguous():
-            raise ValueError("decode tensors must be contiguous")
+        if not t.is_contiguous() or t.device != q.device:
+            raise ValueError("decode tensors must be contiguous and on one device")
+    if kcache.dtype != q.dtype or vcache.dtype != q.dtype:
+        raise ValueError("q and the caches must share one dtype")
+    _check_like(out, q, "out")
+    _check_buf(workspace, q.device, "workspace")
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
         workspace, ws_bytes = decode_workspace(S, H, Lcap, q.device, d)
     else:
         ws_bytes = workspace.numel() * workspace.element_size()
-    if kv_len is not None and (kv_len.dtype != torch.int32 or kv_len.numel() != S):
-        raise ValueError("kv_len must be an int32 device tensor of length S")
-    if tau_sh is not None and (tau_sh.shape != (S, H) or tau_sh.dtype != torch.float32
-                               or not tau_sh.is_contiguous()):
-        raise ValueError("tau_sh must be a contiguous float32 [S,H] tensor")
+    _check_small(kv_len, (S,), torch.int32, q.device, "kv_len")
+    _check_small(tau_sh, (S, H), torch.float32, q.device, "tau_sh")
     st = attn_decode_ex(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), demand.data_ptr(),
                         out.data_ptr(), S, H, Lcap,
                         kv_len.data_ptr() if kv_len is not None else None, d, float(tau),
                         tau_sh.data_ptr() if tau_sh is not None else None, float(eps),
-                        _dtype_code(q), ptr(workspace), ws_bytes, _stream_handle(q.device))
+                        _dtype_code(q), _ptr(workspace), ws_bytes, _stream_handle(q.device))
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode_ex")
     return out
