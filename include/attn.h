@@ -87,7 +87,9 @@ size_t attn_fwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype)
  *   eps        share-denominator constant (dilution), finite and >= 0
  *   dtype      ATTN_F32 or ATTN_BF16
  *   workspace  device scratch of >= attn_fwd_workspace_bytes(...) bytes (may
- *              be NULL when that is 0); contents on entry are ignored
+ *              be NULL when that is 0); contents on entry are ignored.  It is
+ *              written, so it may not overlap q, k, v, out or any optional
+ *              output (else ATTN_EINVAL)
  *   hip_stream hipStream_t to enqueue on (NULL: default stream) */
 int attn_fwd(const void *q, const void *k, const void *v, void *out, int B, int H, int T, int d,
              float tau, int mode, float eps, int dtype, void *workspace, size_t workspace_bytes,
@@ -195,8 +197,9 @@ int attn_bwd_ex(const void *q, const void *k, const void *v, const void *out, co
 /* The dilution forward pass, one stage per call (attn_fwd with ATTN_DILUTION
  * runs exactly these three in order on one stream).  All three take the same
  * shape, tau, dtype and workspace (>= attn_fwd_workspace_bytes(...,
- * ATTN_DILUTION, dtype)); a stage reads what the previous stage left in the
- * workspace, so they must be enqueued in order on one stream.
+ * ATTN_DILUTION, dtype), overlapping no argument, as for attn_fwd); a stage
+ * reads what the previous stage left in the workspace, so they must be
+ * enqueued in order on one stream.
  *
  * attn_dilution_lse        stage 1: log-sum-exp of each query row's logits,
  *                          the normaliser of the causal softmax bids ("The
@@ -323,6 +326,8 @@ size_t attn_decode_workspace_bytes(int S, int H, int Lcap, int d);
  *            A kv_len outside [1, Lcap] is clamped to that range on device.
  *   d        64 or 128
  *   tau, eps as for attn_fwd; dtype must be ATTN_BF16 (else ATTN_ENOTSUP).
+ *   workspace >= attn_decode_workspace_bytes(S,H,Lcap,d) bytes; it is written,
+ *            so it may not overlap any other argument (else ATTN_EINVAL).
  * Consecutive steps must be ordered on one stream (each reads the demand the
  * previous one wrote). */
 int attn_decode(const void *q, const void *kcache, const void *vcache, float *demand, void *out,

@@ -160,6 +160,14 @@ def fwd(**kw):
     (dict(dtype=0, T=1 << 23), ab.ATTN_EINVAL),      # fp32 rows of 256 B: T < 2^23
     (dict(mode=1), ab.ATTN_EWORKSPACE),              # dilution without workspace
     (dict(mode=1, workspace=FAKE + 0x5000000, workspace_bytes=16), ab.ATTN_EWORKSPACE),
+    # the workspace is written: on a tensor argument or an output it is refused
+    (dict(mode=1, workspace=FAKE + 0x2000000 - 256, workspace_bytes=1 << 20),
+     ab.ATTN_EINVAL),                                                  # runs into v
+    (dict(mode=1, workspace=FAKE + 0x3000000, workspace_bytes=1 << 20), ab.ATTN_EINVAL),  # on out
+    (dict(mode=1, lse_out=FAKE + 0x4000000, workspace=FAKE + 0x4000000 - 256,
+          workspace_bytes=1 << 20), ab.ATTN_EINVAL),                   # runs into lse_out
+    (dict(mode=1, workspace=FAKE + 0x5000000, workspace_bytes=1 << 20),
+     ab.ATTN_EHIP),        # valid: validation passes and only the missing device is reported
 ])
 def test_fwd_rejects_bad_arguments(kw, status):
     assert fwd(**kw) == status
@@ -455,6 +463,10 @@ def dec(**kw):
     (dict(tau_sh=FAKE + 0x70000000), ab.ATTN_EWORKSPACE),
     (dict(out=FAKE + 0x1000000), ab.ATTN_EINVAL),     # out inside the K cache
     (dict(), ab.ATTN_EWORKSPACE),
+    (dict(workspace=FAKE + 0x40000000, workspace_bytes=1 << 20), ab.ATTN_EINVAL),  # on the demand
+    (dict(workspace=FAKE + 0x20000000 - 256, workspace_bytes=1 << 20),
+     ab.ATTN_EINVAL),                                                  # runs into the V cache
+    (dict(workspace=FAKE + 0x70000000, workspace_bytes=1 << 20), ab.ATTN_EHIP),  # valid
 ])
 def test_decode_rejects_bad_arguments(kw, status):
     assert dec(**kw) == status
@@ -483,6 +495,9 @@ def stage(name, **kw):
     (dict(d=96), ab.ATTN_ENOTSUP),
     (dict(), ab.ATTN_EWORKSPACE),                     # every stage reads or writes the workspace
     (dict(workspace=FAKE + 0x5000000, workspace_bytes=64), ab.ATTN_EWORKSPACE),
+    (dict(workspace=FAKE + 0x1000000 - 256, workspace_bytes=1 << 20),
+     ab.ATTN_EINVAL),                                 # the written workspace runs into k
+    (dict(workspace=FAKE + 0x5000000, workspace_bytes=1 << 20), ab.ATTN_EHIP),  # valid
 ])
 def test_stage_calls_reject_bad_arguments(name, kw, status):
     assert stage(name, **kw) == status

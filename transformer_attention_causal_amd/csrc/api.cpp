@@ -199,10 +199,24 @@ int validate_fwd(const void *q, const void *k, const void *v, const void *out, i
 
 namespace {
 
-int check_workspace(int B, int H, int T, int d, int dtype, void *workspace,
-                    size_t workspace_bytes, FwdWorkspace *ws) {
+// The workspace is written (the row log-sum-exps and the committed-demand
+// table), so it may not overlap any tensor argument or optional output; `v`,
+// `out` and the row outputs may be NULL.
+int check_workspace(const void *q, const void *k, const void *v, const void *out, int B, int H,
+                    int T, int d, int dtype, void *workspace, size_t workspace_bytes,
+                    const float *lse_out, const float *demand_out, const float *rowsum_out,
+                    FwdWorkspace *ws) {
   if (!fwd_workspace_layout(B, H, T, d, dtype, ws)) return ATTN_EINVAL;
   if (!workspace || workspace_bytes < ws->total || !aligned16(workspace)) return ATTN_EWORKSPACE;
+  const size_t esz = dtype == ATTN_BF16 ? 2 : 4;
+  const size_t nbytes = (size_t)B * H * (size_t)T * d * esz;
+  const size_t rbytes = (size_t)B * H * (size_t)T * sizeof(float);
+  const size_t n = ws->total;
+  if (overlaps(workspace, n, q, nbytes) || overlaps(workspace, n, k, nbytes) ||
+      overlaps(workspace, n, v, nbytes) || overlaps(workspace, n, out, nbytes) ||
+      overlaps(workspace, n, lse_out, rbytes) || overlaps(workspace, n, demand_out, rbytes) ||
+      overlaps(workspace, n, rowsum_out, rbytes))
+    return ATTN_EINVAL;
   return ATTN_OK;
 }
 
@@ -246,7 +260,9 @@ int attn_dilution_lse(const void *q, const void *k, int B, int H, int T, int d, 
                       void *hip_stream) {
   int st = check_fwd(q, k, nullptr, nullptr, B, H, T, d, tau, 0.0f, dtype, lse_out, nullptr);
   FwdWorkspace ws{};
-  if (st == ATTN_OK) st = check_workspace(B, H, T, d, dtype, workspace, workspace_bytes, &ws);
+  if (st == ATTN_OK)
+    st = check_workspace(q, k, nullptr, nullptr, B, H, T, d, dtype, workspace, workspace_bytes,
+                         lse_out, nullptr, nullptr, &ws);
   if (st == ATTN_OK) st = check_device();
   if (st != ATTN_OK) return st;
   attn::FwdArgs a = make_args(q, k, nullptr, nullptr, B, H, T, d, tau, 0.0f, workspace, ws);
@@ -261,7 +277,9 @@ int attn_dilution_committed(const void *q, const void *k, int B, int H, int T, i
                             float *demand_out, void *hip_stream) {
   int st = check_fwd(q, k, nullptr, nullptr, B, H, T, d, tau, eps, dtype, nullptr, demand_out);
   FwdWorkspace ws{};
-  if (st == ATTN_OK) st = check_workspace(B, H, T, d, dtype, workspace, workspace_bytes, &ws);
+  if (st == ATTN_OK)
+    st = check_workspace(q, k, nullptr, nullptr, B, H, T, d, dtype, workspace, workspace_bytes,
+                         nullptr, demand_out, nullptr, &ws);
   if (st == ATTN_OK) st = check_device();
   if (st != ATTN_OK) return st;
   // the table holds committed + eps: stage 3 adds no eps for these keys
@@ -277,7 +295,9 @@ int attn_dilution_shares(const void *q, const void *k, const void *v, void *out,
   if (!v || !out) return ATTN_EINVAL;
   int st = check_fwd(q, k, v, out, B, H, T, d, tau, eps, dtype, nullptr, nullptr);
   FwdWorkspace ws{};
-  if (st == ATTN_OK) st = check_workspace(B, H, T, d, dtype, workspace, workspace_bytes, &ws);
+  if (st == ATTN_OK)
+    st = check_workspace(q, k, v, out, B, H, T, d, dtype, workspace, workspace_bytes, nullptr,
+                         nullptr, nullptr, &ws);
   if (st == ATTN_OK) st = check_device();
   if (st != ATTN_OK) return st;
   attn::FwdArgs a = make_args(q, k, v, out, B, H, T, d, tau, eps, workspace, ws);
@@ -297,7 +317,8 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, int B, i
   if (st != ATTN_OK) return st;
   FwdWorkspace ws{};
   if (mode == ATTN_DILUTION) {
-    st = check_workspace(B, H, T, d, dtype, workspace, workspace_bytes, &ws);
+    st = check_workspace(q, k, v, out, B, H, T, d, dtype, workspace, workspace_bytes, lse_out,
+                         demand_out, rowsum_out, &ws);
     if (st != ATTN_OK) return st;
   }
   st = check_device();
@@ -750,6 +771,14 @@ int attn_decode_ex(const void *q, const void *kcache, const void *vcache, float 
   if (tau_sh && (overlaps(tau_sh, tau_bytes, out, out_bytes) || overlaps(tau_sh, tau_bytes, demand, dem_bytes)))
     return ATTN_EINVAL;
   if (!workspace || workspace_bytes < ws.total || !aligned16(workspace)) return ATTN_EWORKSPACE;
+  // the workspace is written (scores and per-chunk partials): it may not
+  // overlap any argument
+  if (overlaps(workspace, ws.total, q, out_bytes) || overlaps(workspace, ws.total, kcache, cache_bytes) ||
+      overlaps(workspace, ws.total, vcache, cache_bytes) ||
+      overlaps(workspace, ws.total, demand, dem_bytes) || overlaps(workspace, ws.total, out, out_bytes) ||
+      overlaps(workspace, ws.total, tau_sh, tau_bytes) ||
+      overlaps(workspace, ws.total, kv_len, (size_t)S * sizeof(int32_t)))
+    return ATTN_EINVAL;
   const int dev_status = check_device();
   if (dev_status != ATTN_OK) return dev_status;
 

@@ -3,7 +3,8 @@
 # AddressSanitizer and UndefinedBehaviorSanitizer: builds libattn_san.so with
 # the sanitizers on the host pass only, then runs the CPU-side ABI tests
 # against it with the ASan runtime loaded first.  No GPU is involved: every
-# call in those tests is rejected on the host before any device call.
+# call in those tests is rejected on the host before any launch (the few with
+# valid arguments stop at the device query, which finds no GPU).
 #   usage: transformer_attention_causal_amd/sanitize.sh [extra pytest arguments]
 set -euo pipefail
 cd "$(dirname "$0")/.."
