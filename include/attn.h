@@ -150,7 +150,9 @@ size_t attn_bwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype)
  *                       (vector-ALU kernels in full single precision), each
  *                       at d = 64 or 128; else ATTN_ENOTSUP
  *   workspace           device scratch of >= attn_bwd_workspace_bytes(...)
- *                       bytes; contents on entry are ignored
+ *                       bytes; contents on entry are ignored.  It is
+ *                       written, so it may not overlap any other argument
+ *                       (else ATTN_EINVAL)
  * Deterministic: fixed reduction orders, no atomics.  attn_bwd is
  * attn_bwd_ex with tau_bh = dtau_out = fwd_workspace = NULL. */
 int attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout,

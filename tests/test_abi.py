@@ -431,6 +431,12 @@ def bwd(**kw):
      ab.ATTN_EINVAL),                                    # inside the backward's workspace
     (dict(fwd_workspace=FAKE + 0xd000000, fwd_workspace_bytes=1 << 20,
           dtau_out=FAKE + 0xd000100, **BWD_WS), ab.ATTN_EINVAL),
+    # the backward's own workspace is written: on an argument it is refused
+    (dict(workspace=FAKE + 0x7000000, workspace_bytes=1 << 24), ab.ATTN_EINVAL),   # on dq
+    (dict(workspace=FAKE + 0x5000000 - 256, workspace_bytes=1 << 24),
+     ab.ATTN_EINVAL),                                                    # runs into lse
+    (dict(dtau_out=FAKE + 0xc000100, **BWD_WS), ab.ATTN_EINVAL),        # dtau_out inside it
+    (dict(**BWD_WS), ab.ATTN_EHIP),       # valid: only the missing device is reported
 ])
 def test_bwd_rejects_bad_arguments(kw, status):
     assert bwd(**kw) == status

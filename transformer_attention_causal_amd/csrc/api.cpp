@@ -661,6 +661,16 @@ int attn_bwd_ex(const void *q, const void *k, const void *v, const void *out, co
   BwdWorkspace ws;
   if (!bwd_workspace(B, H, T, d, mode, dtype, &ws)) return ATTN_EINVAL;
   if (!workspace || workspace_bytes < ws.total || !aligned16(workspace)) return ATTN_EWORKSPACE;
+  // the workspace is written: it may not overlap any argument
+  {
+    const void *tensors[8] = {q, k, v, out, dout, dq, dk, dv};
+    for (const void *t : tensors)
+      if (overlaps(workspace, ws.total, t, nbytes)) return ATTN_EINVAL;
+    if (overlaps(workspace, ws.total, lse, rbytes) || overlaps(workspace, ws.total, rowsum, rbytes) ||
+        overlaps(workspace, ws.total, tau_bh, tbytes) ||
+        overlaps(workspace, ws.total, dtau_out, tbytes))
+      return ATTN_EINVAL;
+  }
   // the dilution forward's workspace (read only): its committed-demand table
   // replaces the backward's own; ignored for ATTN_TEMPERED
   const char *fwd_cin = nullptr;
