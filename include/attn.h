@@ -79,8 +79,8 @@ size_t attn_fwd_workspace_bytes(int B, int H, int T, int d, int mode, int dtype)
  *   B, H, T    batch, heads, sequence length (each >= 1; T < 16777216 and
  *              T * d * element size < 2^31: the kernels address one head's
  *              rows with 32-bit byte offsets -- for bf16 T < 2^24 at d = 64
- *              and T < 2^23 at d = 128, for fp32 half of that; else
- *              ATTN_EINVAL)
+ *              and T < 2^23 at d = 128, for fp32 half of that; B * H * T
+ *              <= 2^32 rows in all; else ATTN_EINVAL)
  *   d          head dimension: 64 or 128 (else ATTN_ENOTSUP)
  *   tau        logit multiplier, finite and >= 0 (tau = 0 gives uniform bids)
  *   mode       ATTN_TEMPERED or ATTN_DILUTION

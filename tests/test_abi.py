@@ -158,6 +158,9 @@ def fwd(**kw):
     (dict(mode=1, d=128, T=(1 << 23) - 1, k=FAKE + (1 << 32), v=FAKE + (2 << 32),
           out=FAKE + (3 << 32)), ab.ATTN_EWORKSPACE),   # largest T at d = 128
     (dict(dtype=0, T=1 << 23), ab.ATTN_EINVAL),      # fp32 rows of 256 B: T < 2^23
+    (dict(H=4097, T=1 << 20), ab.ATTN_EINVAL),       # more than 2^32 rows in all
+    (dict(mode=1, H=4096, T=1 << 20, k=FAKE + (1 << 40), v=FAKE + (2 << 40),
+          out=FAKE + (3 << 40)), ab.ATTN_EWORKSPACE),   # exactly 2^32 rows passes
     (dict(mode=1), ab.ATTN_EWORKSPACE),              # dilution without workspace
     (dict(mode=1, workspace=FAKE + 0x5000000, workspace_bytes=16), ab.ATTN_EWORKSPACE),
     # the workspace is written: on a tensor argument or an output it is refused

@@ -123,6 +123,10 @@ bool shape_ok(int B, int H, int T) {
   // element counts must fit the kernels' 64-bit offsets and 32-bit grids
   const size_t BH = (size_t)B * H;
   if (BH > (size_t)INT32_MAX / 1024) return false;
+  // at most 2^32 rows in all (q alone would then exceed 512 GiB, more than a
+  // device holds): every launch's block count, such as B*H*ceil(T/128) or
+  // B*H*T*d/256 for the per-element passes, then stays below 2^31
+  if (BH * (size_t)T > ((size_t)1 << 32)) return false;
   return true;
 }
 
