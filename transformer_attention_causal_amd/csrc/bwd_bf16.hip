@@ -45,6 +45,11 @@
 // Both in-block scans (the column prefix inside D and the column suffix
 // inside G) are matrix-core products against constant triangular operands,
 // as in the forward shares pass.
+// The closing products (dK^T += Q^T dS, dV^T += dO^T a, dQ^T += K^T dS^T and
+// the rho pass's Q^T (p rho)) need Q, dO and K dim-major.  They read them
+// straight from the row-major LDS blocks with the transposing LDS load
+// (ds_read_b64_tr_b16), so each block is read from memory once, with
+// coalesced 16-byte loads, and stored to LDS once.
 #include "attn_common.hpp"
 #include "launch.hpp"
 #include "tiles.hpp"
@@ -54,7 +59,6 @@
 namespace attn {
 
 constexpr int kColKeys = 128;   // keys per workgroup in the column kernels (4 waves x 32)
-constexpr int kTRow = 36;       // LDS row stride of the transposed 32-row blocks (32 + 4 pad)
 constexpr float kInvDMax = 18446744073709551616.0f;   // 2^64: clamp on 1/D (eps = 0 only)
 constexpr float kNoClampEps = 1.0842021724855044e-19f;   // 2^-63
 
@@ -215,14 +219,9 @@ __device__ __forceinline__ void col_scores(const ColBlock<D> &b, const bf16x8 *k
 // returns that sum over both halves (bf16 pair) for the dQ pass, and
 // `rho_part` the block's rows' sums of the packed p dp over this wave's 32
 // keys (lane l32: row l32 of the block).
-template <int D>
-struct ColBlockT {
-  __bf16 qt[D * kTRow];
-  __bf16 gt[D * kTRow];
-};
 
 template <bool DIL, bool DIAG, bool CLAMP, int D>
-__device__ __forceinline__ void dkdv_block(const ColBlock<D> &b, const ColBlockT<D> &bt,
+__device__ __forceinline__ void dkdv_block(const ColBlock<D> &b,
                                            const bf16x8 *kf, const bf16x8 *vf,
                                            const ScanConsts &sc, uint32_t cin_word,
                                            float &running, uint32_t &gin_word, float &rho_part,
@@ -240,8 +239,8 @@ __device__ __forceinline__ void dkdv_block(const ColBlock<D> &b, const ColBlockT
     for (int u = 0; u < Geom<D>::kOBlocks; ++u)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        qtf[u][j] = lds_vfrag(bt.qt + (32 * u + l32) * kTRow, j, h);
-        gtf[u][j] = lds_vfrag(bt.gt + (32 * u + l32) * kTRow, j, h);
+        qtf[u][j] = lds_tr_frag(b.q, Geom<D>::kKRow, 16 * j, 32 * u);
+        gtf[u][j] = lds_tr_frag(b.g, Geom<D>::kKRow, 16 * j, 32 * u);
       }
     __builtin_amdgcn_sched_barrier(0);   // keep the reads where they are issued
   };
@@ -307,16 +306,14 @@ __device__ __forceinline__ void dkdv_block(const ColBlock<D> &b, const ColBlockT
   }
 #pragma unroll
   for (int u = 0; u < Geom<D>::kOBlocks; ++u) {
-    const __bf16 *qtr = bt.qt + (32 * u + l32) * kTRow;
-    const __bf16 *gtr = bt.gt + (32 * u + l32) * kTRow;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       if constexpr (kAhead) {
         dkt[u] = mfma32(qtf[u][j], sf[j], dkt[u]);
         dvt[u] = mfma32(gtf[u][j], af[j], dvt[u]);
       } else {
-        dkt[u] = mfma32(lds_vfrag(qtr, j, h), sf[j], dkt[u]);
-        dvt[u] = mfma32(lds_vfrag(gtr, j, h), af[j], dvt[u]);
+        dkt[u] = mfma32(lds_tr_frag(b.q, Geom<D>::kKRow, 16 * j, 32 * u), sf[j], dkt[u]);
+        dvt[u] = mfma32(lds_tr_frag(b.g, Geom<D>::kKRow, 16 * j, 32 * u), af[j], dvt[u]);
       }
     }
   }
@@ -355,7 +352,7 @@ __device__ __forceinline__ void dkdv_tail(const DkdvCarry<D> &cr, f32x16 *dkt, f
 }
 
 template <bool DIAG, bool CLAMP, int D>
-__device__ __forceinline__ void dkdv_block_pipelined(const ColBlock<D> &b, const ColBlockT<D> &bt,
+__device__ __forceinline__ void dkdv_block_pipelined(const ColBlock<D> &b,
                                                      const bf16x8 *kf, const bf16x8 *vf,
                                                      const ScanConsts &sc, uint32_t cin_word,
                                                      float &running, uint32_t &gin_word,
@@ -392,8 +389,8 @@ __device__ __forceinline__ void dkdv_block_pipelined(const ColBlock<D> &b, const
   for (int u = 0; u < Geom<D>::kOBlocks; ++u)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      cr.qtf[u][j] = lds_vfrag(bt.qt + (32 * u + l32) * kTRow, j, h);
-      cr.gtf[u][j] = lds_vfrag(bt.gt + (32 * u + l32) * kTRow, j, h);
+      cr.qtf[u][j] = lds_tr_frag(b.q, Geom<D>::kKRow, 16 * j, 32 * u);
+      cr.gtf[u][j] = lds_tr_frag(b.g, Geom<D>::kKRow, 16 * j, 32 * u);
     }
   // G = gradient terms of the later blocks + inclusive suffix in this one
   gin_word = split2_bf16(both_halves_sum(running));
@@ -434,7 +431,6 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
   constexpr int kRowChunks = D / 8;   // 16-byte chunks per row
   constexpr int kBlkLoads = 32 * kRowChunks / 256;   // per thread, per tensor
   __shared__ __attribute__((aligned(16))) ColBlock<D> sb[2];
-  __shared__ __attribute__((aligned(16))) ColBlockT<D> st[2];
   // dilution: this workgroup's K and V rows (the B operands of S and dA) sit
   // in LDS and are read per block, which keeps the kernel within two waves'
   // registers per SIMD without spills; the tempered form keeps them in registers
@@ -504,12 +500,10 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
 
   const int qs_lo = (kb * kColKeys) / 32;
   // loaders: chunk u = tid + 256 i of the Q and dO blocks is row
-  // u / kRowChunks, chunk u % kRowChunks; for the transposed copies, item
-  // u = tid + 256 i covers rows 2 kp, 2 kp + 1 (kp = u & 15) and chunk
-  // (u >> 4) % kRowChunks of Q (when (u >> 4) < kRowChunks) or dO.
-  u32x4 qreg[kBlkLoads], greg[kBlkLoads], tr0[kBlkLoads], tr1[kBlkLoads];
+  // u / kRowChunks, chunk u % kRowChunks.  The closing products read the
+  // blocks transposed straight from these row-major copies.
+  u32x4 qreg[kBlkLoads], greg[kBlkLoads];
   float lreg = 0.0f, ireg = 0.0f, rreg = 0.0f;
-  const int kp = tid & 15;
   auto load_block = [&](int qs) {
     const int row0 = 32 * qs;
     const int bytes = (T - row0) * (D * 2);
@@ -517,15 +511,9 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
     const auto rg = make_rsrc(G + (size_t)row0 * D, bytes);
 #pragma unroll
     for (int i = 0; i < kBlkLoads; ++i) {
-      const int u = tid + 256 * i, tdc = (u >> 4) % kRowChunks;
+      const int u = tid + 256 * i;
       qreg[i] = buf_load16(rq, 16u * u);
       greg[i] = buf_load16(rg, 16u * u);
-      // Q or dO: the same for every lane of a wave (items split at a wave
-      // boundary), made a scalar so the buffer descriptor stays in SGPRs
-      const bool tq = __builtin_amdgcn_readfirstlane((u >> 4) < kRowChunks ? 1 : 0) != 0;
-      const auto rt = tq ? rq : rg;
-      tr0[i] = buf_load16(rt, 4u * D * kp + 16u * tdc);
-      tr1[i] = buf_load16(rt, 4u * D * kp + 2u * D + 16u * tdc);
     }
     if (tid < 32) {
       const int row = row0 + tid;
@@ -539,12 +527,10 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
   auto store_block = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < kBlkLoads; ++i) {
-      const int u = tid + 256 * i, tdc = (u >> 4) % kRowChunks;
+      const int u = tid + 256 * i;
       const int off = (u / kRowChunks) * kKR + (u % kRowChunks) * 8;
       *reinterpret_cast<u32x4 *>(&sb[buf].q[off]) = qreg[i];
       *reinterpret_cast<u32x4 *>(&sb[buf].g[off]) = greg[i];
-      store_rows_transposed((u >> 4) < kRowChunks ? st[buf].qt : st[buf].gt, kTRow, kp, tdc,
-                            tr0[i], tr1[i]);
     }
     if (tid < 32) {
       sb[buf].lse2[tid] = lreg;
@@ -589,17 +575,17 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
       }
       if constexpr (kPipe) {
         if (32 * qs == kw0)
-          dkdv_block_pipelined<true, CLAMP>(sb[buf], st[buf], kf, vf, sc, cw, running, gw,
+          dkdv_block_pipelined<true, CLAMP>(sb[buf], kf, vf, sc, cw, running, gw,
                                             rho_part, c2, l32, h, carry, dkt, dvt);
         else
-          dkdv_block_pipelined<false, CLAMP>(sb[buf], st[buf], kf, vf, sc, cw, running, gw,
+          dkdv_block_pipelined<false, CLAMP>(sb[buf], kf, vf, sc, cw, running, gw,
                                              rho_part, c2, l32, h, carry, dkt, dvt);
       } else {
         if (32 * qs == kw0)
-          dkdv_block<DIL, true, CLAMP>(sb[buf], st[buf], kf, vf, sc, cw, running, gw, rho_part, c2,
+          dkdv_block<DIL, true, CLAMP>(sb[buf], kf, vf, sc, cw, running, gw, rho_part, c2,
                                        l32, h, dkt, dvt);
         else
-          dkdv_block<DIL, false, CLAMP>(sb[buf], st[buf], kf, vf, sc, cw, running, gw, rho_part,
+          dkdv_block<DIL, false, CLAMP>(sb[buf], kf, vf, sc, cw, running, gw, rho_part,
                                         c2, l32, h, dkt, dvt);
       }
       // the wave's keys are all below 32 (qs + 1): block qs keeps an entry for each
@@ -643,18 +629,12 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
 // keys (wave w 32 of them, the key row in registers as the B operand of
 // S = Q K^T) and walks the 32-row blocks that see them, two per barrier; per
 // block the bids are recomputed (S layout), scaled by their rows' rho,
-// packed and accumulated as Y^T += Q^T (p rho) against the block's
-// transposed Q rows.
+// packed and accumulated as Y^T += Q^T (p rho), with Q^T read transposed
+// from the block's row-major Q rows.
 template <int D>
 struct RhoBlock {
-  __bf16 q[32 * Geom<D>::kKRow];   // Q rows (A operand of S)
-  __bf16 qt[D * kTRow];            // Q^T, dim-major (A operand of Y^T)
+  __bf16 q[32 * Geom<D>::kKRow];   // Q rows (A operand of S; read transposed for Y^T)
   float lse2[32], rho[32];
-  // The two blocks of a stage then sit 64 bytes off a multiple of 128 apart,
-  // so that the transposed stores of row pairs kp and kp + 16 (one into each
-  // block) fall in different LDS banks (without it: 2-way conflicts, 4e7
-  // conflict cycles per launch at d = 128).
-  float pad[16];
 };
 
 template <int D>
@@ -662,7 +642,6 @@ __global__ void __launch_bounds__(256, 2) bwd_dkrho_kernel(BwdArgs a, int nqs) {
   constexpr int kKR = Geom<D>::kKRow, kCh = Geom<D>::kChunks, kOB = Geom<D>::kOBlocks;
   constexpr int kRowChunks = D / 8;                  // 16-byte chunks per row
   constexpr int kRowLoads = 64 * kRowChunks / 256;   // row-major chunks per thread and stage
-  constexpr int kTrLoads = 32 * kRowChunks / 256;    // (row pair, chunk) items per thread
   __shared__ __attribute__((aligned(16))) RhoBlock<D> sb[2][2];
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
@@ -688,21 +667,14 @@ __global__ void __launch_bounds__(256, 2) bwd_dkrho_kernel(BwdArgs a, int nqs) {
   __builtin_amdgcn_s_waitcnt(0);
 
   // a stage is the 64 rows of blocks (2P, 2P + 1).  Loaders: chunk
-  // u = tid + 256 i is row u / kRowChunks, chunk u % kRowChunks; transposed
-  // item u = tid + 256 i covers rows 2 kp, 2 kp + 1 (kp = u & 31) and chunk u >> 5
-  u32x4 qreg[kRowLoads], tr0[kTrLoads], tr1[kTrLoads];
+  // u = tid + 256 i is row u / kRowChunks, chunk u % kRowChunks
+  u32x4 qreg[kRowLoads];
   float lreg = 0.0f, hreg = 0.0f;
   auto load_stage = [&](int P) {              // 64 P < T for every stage loaded
     const int row0 = 64 * P;
     const auto rq = make_rsrc(Q + (size_t)row0 * D, (T - row0) * (D * 2));
 #pragma unroll
     for (int i = 0; i < kRowLoads; ++i) qreg[i] = buf_load16(rq, 16u * (tid + 256 * i));
-#pragma unroll
-    for (int i = 0; i < kTrLoads; ++i) {
-      const int u = tid + 256 * i, kp = u & 31, tdc = u >> 5;
-      tr0[i] = buf_load16(rq, 4u * D * kp + 16u * tdc);
-      tr1[i] = buf_load16(rq, 4u * D * kp + 2u * D + 16u * tdc);
-    }
     if (tid < 64) {
       const int row = row0 + tid;
       const bool ok = row < T;
@@ -717,11 +689,6 @@ __global__ void __launch_bounds__(256, 2) bwd_dkrho_kernel(BwdArgs a, int nqs) {
       const int u = tid + 256 * i, row = u / kRowChunks;
       *reinterpret_cast<u32x4 *>(&sb[buf][row >> 5].q[(row & 31) * kKR + (u % kRowChunks) * 8]) =
           qreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < kTrLoads; ++i) {
-      const int u = tid + 256 * i, kp = u & 31, tdc = u >> 5;
-      store_rows_transposed(sb[buf][kp >> 4].qt, kTRow, kp & 15, tdc, tr0[i], tr1[i]);
     }
     if (tid < 64) {
       sb[buf][tid >> 5].lse2[tid & 31] = lreg;
@@ -755,11 +722,10 @@ __global__ void __launch_bounds__(256, 2) bwd_dkrho_kernel(BwdArgs a, int nqs) {
         for (int r = 0; r < 16; ++r) wv[r] *= pq[r];
         const bf16x8 wf[2] = {pack8(wv), pack8(wv + 8)};
 #pragma unroll
-        for (int u = 0; u < kOB; ++u) {
-          const __bf16 *qtr = b.qt + (32 * u + l32) * kTRow;
+        for (int u = 0; u < kOB; ++u)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) yt[u] = mfma32(lds_vfrag(qtr, j, h), wf[j], yt[u]);
-        }
+          for (int j = 0; j < 2; ++j)
+            yt[u] = mfma32(lds_tr_frag(b.q, kKR, 16 * j, 32 * u), wf[j], yt[u]);
       }
     }
     if (P < p_hi) store_stage(buf ^ 1);
@@ -786,8 +752,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dkrho_kernel(BwdArgs a, int nqs) {
 // --------------------------------------------------------------- dQ rows
 //
 // A workgroup owns 128 query rows (wave w the 32 rows [qw0, qw0 + 32)) and
-// streams 64-key tiles of K (row-major, and transposed: the A operand of
-// dQ^T += K^T dS^T) and V (row-major) through LDS.  Scores are taken as S^T
+// streams 64-key tiles of K and V (row-major) through LDS; K also serves,
+// read transposed, as the A operand of dQ^T += K^T dS^T.  Scores are taken as S^T
 // (lane = query, element r = key acc_row(r, h)), so the per-row scalars are
 // per lane; the column scans need the bids and g with queries in the
 // operand slots, so those are moved to the S layout by identity products.
@@ -830,7 +796,7 @@ template <bool DIL, bool DIAG, bool CLAMP, int D>
 __device__ __forceinline__ void dq_subtile(DqState<D> &st, const bf16x8 *qf, const bf16x8 *gf,
                                            const DqConsts &dc,
                                            const __bf16 *kt_lds, const __bf16 *vt_lds,
-                                           const __bf16 *ktt_lds, int t, uint32_t cin_word,
+                                           int t, uint32_t cin_word,
                                            uint32_t gin_word, float lse2, float invr, float dri,
                                            float rho, int qrel, int l32, int h, float c2) {
   // S^T and dA^T for keys 32t.. of the tile (lane = query)
@@ -842,27 +808,30 @@ __device__ __forceinline__ void dq_subtile(DqState<D> &st, const bf16x8 *qf, con
     s = mfma32(lds_frag(krow, c, h), qf[c], s);
     da = mfma32(lds_frag(vrow, c, h), gf[c], da);
   }
-  // The K^T fragments of the closing dQ products, read ahead as in the dK/dV
-  // pass (dilution: once the in-block prefix is formed; tempered: right away).
+  // The K^T fragments of the closing dQ products, read transposed from the
+  // row-major K tile and ahead of the products as in the dK/dV pass
+  // (dilution: once the in-block prefix is formed; tempered: right away).
   constexpr bool kAhead = D > 64 || !DIL;
   bf16x8 kta[Geom<D>::kOBlocks][2];
+  auto kt_frag = [&](int i, int c) {
+    return lds_tr_frag(kt_lds, Geom<D>::kKRow, 32 * t + 16 * c, 32 * i);
+  };
   auto read_ahead = [&]() {
 #pragma unroll
     for (int i = 0; i < Geom<D>::kOBlocks; ++i)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) kta[i][c] = lds_vfrag(ktt_lds + (32 * i + l32) * kVRow + 32 * t, c, h);
+      for (int c = 0; c < 2; ++c) kta[i][c] = kt_frag(i, c);
     __builtin_amdgcn_sched_barrier(0);   // keep the reads where they are issued
   };
   // dQ^T += K^T dS^T for the sub-tile's keys (e0, e1: the packed dS^T)
   auto update = [&](const bf16x8 &e0, const bf16x8 &e1) {
-    if constexpr (kAhead) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int i = 0; i < Geom<D>::kOBlocks; ++i) st.x[i] = mfma32(kta[i][c], c == 0 ? e0 : e1, st.x[i]);
-    } else {
-      pv_update_d<D>(st.x, ktt_lds, t, l32, h, e0, e1);
-    }
+      for (int i = 0; i < Geom<D>::kOBlocks; ++i) {
+        if constexpr (kAhead) st.x[i] = mfma32(kta[i][c], c == 0 ? e0 : e1, st.x[i]);
+        else st.x[i] = mfma32(kt_frag(i, c), c == 0 ? e0 : e1, st.x[i]);
+      }
   };
   if constexpr (kAhead && !DIL) read_ahead();
   float p[16];
@@ -917,14 +886,12 @@ __device__ __forceinline__ void dq_subtile(DqState<D> &st, const bf16x8 *qf, con
 template <bool DIL, int D, bool CLAMP>
 __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dq_kernel(BwdArgs a,
                                                                                int nqb) {
-  constexpr int kKR = Geom<D>::kKRow, kKT = Geom<D>::kKTile, kVT = Geom<D>::kVTile;
+  constexpr int kKR = Geom<D>::kKRow, kKT = Geom<D>::kKTile;
   constexpr int kCh = Geom<D>::kChunks, kOB = Geom<D>::kOBlocks;
   constexpr int kRowChunks = D / 8;                     // 16-byte chunks per row
   constexpr int kTileLoads = kBN * kRowChunks / 256;    // per thread, per tensor
-  constexpr int kTrLoads = (kBN / 2) * kRowChunks / 256;   // transposed row pairs
   __shared__ __attribute__((aligned(16))) __bf16 sK[2 * kKT];
   __shared__ __attribute__((aligned(16))) __bf16 sV[2 * kKT];
-  __shared__ __attribute__((aligned(16))) __bf16 sKt[2 * kVT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
@@ -968,9 +935,9 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dq_kernel(B
   }
 
   // loaders: chunk u = tid + 256 i of the K and V tiles is key u / kRowChunks,
-  // chunk u % kRowChunks; transposed item u covers keys 2 (u & 31) and
-  // 2 (u & 31) + 1, chunk u >> 5.
-  u32x4 kreg[kTileLoads], vreg[kTileLoads], treg[kTrLoads][2];
+  // chunk u % kRowChunks.  The closing products read K transposed straight
+  // from its row-major tile.
+  u32x4 kreg[kTileLoads], vreg[kTileLoads];
   auto load_tile = [&](int kt) {   // kt < nkt, so its first key is < T
     const int key0 = kt * kBN;
     const int bytes = (T - key0) * (D * 2);
@@ -980,13 +947,6 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dq_kernel(B
     for (int i = 0; i < kTileLoads; ++i) {
       kreg[i] = buf_load16(rk, 16u * (tid + 256 * i));
       vreg[i] = buf_load16(rv, 16u * (tid + 256 * i));
-    }
-#pragma unroll
-    for (int i = 0; i < kTrLoads; ++i) {
-      const int u = tid + 256 * i;
-      const uint32_t off = 4u * D * (u & 31) + 16u * (u >> 5);
-      treg[i][0] = buf_load16(rk, off);
-      treg[i][1] = buf_load16(rk, off + 2u * D);
     }
   };
   auto store_tile = [&](int buf) {
@@ -998,11 +958,6 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dq_kernel(B
       const int off = (u / kRowChunks) * kKR + (u % kRowChunks) * 8;
       *reinterpret_cast<u32x4 *>(k + off) = kreg[i];
       *reinterpret_cast<u32x4 *>(v + off) = vreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < kTrLoads; ++i) {
-      const int u = tid + 256 * i;
-      store_rows_transposed(sKt + buf * kVT, kVRow, u & 31, u >> 5, treg[i][0], treg[i][1]);
     }
   };
   // committed demand (+eps) and later blocks' g sums of this wave's block on
@@ -1050,17 +1005,17 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dq_kernel(B
       load_words(kt + 1);
     }
     if (wave_live && kt <= kd) {
-      const __bf16 *kl = sK + buf * kKT, *vl = sV + buf * kKT, *tl = sKt + buf * kVT;
+      const __bf16 *kl = sK + buf * kKT, *vl = sV + buf * kKT;
       const int qrel = qw0 + l32 - kt * kBN;
       // one sub-tile at a time: the per-sub-tile temporaries would not fit
       // twice beside the accumulators
 #pragma unroll 1
       for (int t = 0; t < 2; ++t) {
         if (kt < kd)
-          dq_subtile<DIL, false, CLAMP, D>(st, qf, gf, dc, kl, vl, tl, t, cw[t], gw[t], lse2,
+          dq_subtile<DIL, false, CLAMP, D>(st, qf, gf, dc, kl, vl, t, cw[t], gw[t], lse2,
                                            invr, dri, rho, qrel, l32, h, c2);
         else
-          dq_subtile<DIL, true, CLAMP, D>(st, qf, gf, dc, kl, vl, tl, t, cw[t], gw[t], lse2,
+          dq_subtile<DIL, true, CLAMP, D>(st, qf, gf, dc, kl, vl, t, cw[t], gw[t], lse2,
                                           invr, dri, rho, qrel, l32, h, c2);
       }
     }

@@ -49,6 +49,30 @@ __device__ __forceinline__ bf16x8 lds_vfrag(const __bf16 *vrow, int c, int h) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// The same operand for a block held row-major in LDS (`blk`, rows of
+// `stride` bf16), read with the transposing LDS load: lane (i = lane % 32,
+// h = lane / 32) gets column c0 + i of rows r0 + 4h + {0..3} and
+// r0 + 8 + 4h + {0..3}, i.e. element r of the other operand's accumulator
+// order.  Each ds_read_b64_tr_b16 works on groups of 16 lanes: group lane
+// 4k + m addresses row k of the four rows, columns 4m .. 4m + 3 of the
+// group's 16, and lane n of the group receives column n of all four rows.
+// Addresses are 8-byte aligned when c0 is a multiple of 4 and the stride a
+// multiple of 4 elements.
+__device__ __forceinline__ bf16x8 lds_tr_frag(const __bf16 *blk, int stride, int r0, int c0) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  typedef __attribute__((address_space(3))) const __bf16 lds_bf16;
+  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+  const int row = r0 + 4 * (g >> 1) + (n >> 2);
+  const int col = c0 + 16 * (g & 1) + 4 * (n & 3);
+  lds_bf16 *p = (lds_bf16 *)(blk + row * stride + col);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 8 * stride));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  const u32x4 u = {a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(bf16x8, u);
+}
+
 __device__ __forceinline__ bf16x8 pack8(const float *v) {
   return to_bf16x8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
 }
