@@ -113,7 +113,7 @@ __device__ __forceinline__ void st_weights(const f32x16 *s, float m_run, int qre
 // normaliser accumulates anyway.
 template <int MODE, bool FP32SUM, bool DIAG, int D>
 __device__ __forceinline__ void st_tile(RowState<D> &st, const bf16x8 *qf, const bf16x8 &sel,
-                                        const __bf16 *kt_lds, const __bf16 *vt_lds, int kb,
+                                        const __bf16 *kt_lds, const __bf16 *v_lds, int kb,
                                         int qw0, int l32, int h, float c2) {
   f32x16 s[2] = {zero16(), zero16()};
   const __bf16 *krow0 = kt_lds + l32 * Geom<D>::kKRow;
@@ -147,7 +147,7 @@ __device__ __forceinline__ void st_tile(RowState<D> &st, const bf16x8 *qf, const
         const bf16x8 pf0 = pack8(p + 16 * t), pf1 = pack8(p + 16 * t + 8);
         st.lsum = mfma16(sel, pf0, st.lsum);
         st.lsum = mfma16(sel, pf1, st.lsum);
-        pv_update_d<D>(st.o, vt_lds, t, l32, h, pf0, pf1);
+        pv_update_d<D>(st.o, v_lds, t, pf0, pf1);
       }
     }
   } else {
@@ -180,7 +180,7 @@ __device__ __forceinline__ void st_tile(RowState<D> &st, const bf16x8 *qf, const
     st.lsum += tsum;
     if constexpr (MODE == kRowTempered) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) pv_update_d<D>(st.o, vt_lds, t, l32, h, pf[2 * t], pf[2 * t + 1]);
+      for (int t = 0; t < 2; ++t) pv_update_d<D>(st.o, v_lds, t, pf[2 * t], pf[2 * t + 1]);
     }
   }
 }
@@ -264,7 +264,7 @@ template <bool DIAG, int D>
 __device__ __forceinline__ void share_tile(RowState<D> &st, const bf16x8 *qf, const float *lseq,
                                            const ShareConsts &sc_, const bf16x8 &sel,
                                            const uint32_t *base,
-                                           const __bf16 *kt_lds, const __bf16 *vt_lds, int kb,
+                                           const __bf16 *kt_lds, const __bf16 *v_lds, int kb,
                                            int qw0, int l32, int h, float c2) {
   // The two 32-key sub-tiles are independent until share@V; their stages are
   // written staggered so that each sub-tile's matrix-core work overlaps the
@@ -292,7 +292,7 @@ __device__ __forceinline__ void share_tile(RowState<D> &st, const bf16x8 *qf, co
       share_values(dd, pt, sf0, sf1);
       st.lsum = mfma16(sel, sf0, st.lsum);
       st.lsum = mfma16(sel, sf1, st.lsum);
-      pv_update_d<D>(st.o, vt_lds, t, l32, h, sf0, sf1);
+      pv_update_d<D>(st.o, v_lds, t, sf0, sf1);
     }
     return;
   }
@@ -313,11 +313,11 @@ __device__ __forceinline__ void share_tile(RowState<D> &st, const bf16x8 *qf, co
   share_values(d0, pt0, sf00, sf01);
   st.lsum = mfma16(sel, sf00, st.lsum);
   st.lsum = mfma16(sel, sf01, st.lsum);
-  pv_update_d<D>(st.o, vt_lds, 0, l32, h, sf00, sf01);
+  pv_update_d<D>(st.o, v_lds, 0, sf00, sf01);
   share_values(d1, pt1, sf10, sf11);
   st.lsum = mfma16(sel, sf10, st.lsum);
   st.lsum = mfma16(sel, sf11, st.lsum);
-  pv_update_d<D>(st.o, vt_lds, 1, l32, h, sf10, sf11);
+  pv_update_d<D>(st.o, v_lds, 1, sf10, sf11);
 }
 
 // Waves per SIMD each mode is compiled for (register budget 512/n per lane).
@@ -335,7 +335,7 @@ __global__ void __launch_bounds__(256, (RowOccupancy<MODE, D>::value))
   using G = Geom<D>;
   constexpr bool kNeedV = (MODE != kRowLse);
   __shared__ __attribute__((aligned(16))) __bf16 sK[2 * G::kKTile];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[kNeedV ? 2 * G::kVTile : 8];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[kNeedV ? 2 * G::kKTile : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
@@ -377,13 +377,13 @@ __global__ void __launch_bounds__(256, (RowOccupancy<MODE, D>::value))
   for (int c = 0; c < G::kChunks; ++c)
     qf[c] = __builtin_bit_cast(bf16x8, load_row_chunk<D>(Q, qw0 + l32 - P, Tq, 2 * c + h));
 
-  // tile loaders: K as [key][d] rows; V transposed to [d][key] on the way in.
-  // Buffer loads with per-lane byte offsets fixed for the whole loop; keys
-  // past the end of the sequence read as zeros.  Each thread moves D/32
-  // 16-byte chunks of K and D/64 (row pair, d-chunk) items of V per tile.
+  // tile loaders: K and V as [key][d] rows (P@V reads V transposed from its
+  // row-major tile).  Buffer loads with per-lane byte offsets fixed for the
+  // whole loop; keys past the end of the sequence read as zeros.  Each
+  // thread moves D/32 16-byte chunks of K and of V per tile.
   constexpr int kRowBytes = 2 * D, kRowChunks = D / 8;
-  constexpr int kKL = D / 32, kVI = D / 64;
-  u32x4 kreg[kKL], vreg[2 * kVI];
+  constexpr int kKL = D / 32;
+  u32x4 kreg[kKL], vreg[kKL];
   auto load_tile = [&](int kt) {
     const int key0 = kt * kBN;                          // < T for every tile loaded
     const int bytes = (T - key0) * kRowBytes;
@@ -393,28 +393,18 @@ __global__ void __launch_bounds__(256, (RowOccupancy<MODE, D>::value))
     if constexpr (kNeedV) {
       const auto rv = make_rsrc(V + (size_t)key0 * D, bytes);
 #pragma unroll
-      for (int i = 0; i < kVI; ++i) {
-        const int u = tid + 256 * i, kp = u & 31, dc = u >> 5;
-        const uint32_t off = 2u * kRowBytes * kp + 16u * dc;
-        vreg[2 * i] = buf_load16(rv, off);
-        vreg[2 * i + 1] = buf_load16(rv, off + kRowBytes);
-      }
+      for (int i = 0; i < kKL; ++i) vreg[i] = buf_load16(rv, 16u * (tid + 256 * i));
     }
   };
   auto store_tile = [&](int buf) {
     __bf16 *k = sK + buf * G::kKTile;
+    __bf16 *vv = sV + buf * G::kKTile;
 #pragma unroll
     for (int i = 0; i < kKL; ++i) {
       const int u = tid + 256 * i;
-      *reinterpret_cast<u32x4 *>(k + (u / kRowChunks) * G::kKRow + (u % kRowChunks) * 8) = kreg[i];
-    }
-    if constexpr (kNeedV) {
-      __bf16 *vt = sV + buf * G::kVTile;
-#pragma unroll
-      for (int i = 0; i < kVI; ++i) {
-        const int u = tid + 256 * i;
-        store_rows_transposed(vt, kVRow, u & 31, u >> 5, vreg[2 * i], vreg[2 * i + 1]);
-      }
+      const int off = (u / kRowChunks) * G::kKRow + (u % kRowChunks) * 8;
+      *reinterpret_cast<u32x4 *>(k + off) = kreg[i];
+      if constexpr (kNeedV) *reinterpret_cast<u32x4 *>(vv + off) = vreg[i];
     }
   };
 
@@ -488,16 +478,16 @@ __global__ void __launch_bounds__(256, (RowOccupancy<MODE, D>::value))
       if constexpr (MODE == kRowShare) load_cin(kt + 1);
     }
     const __bf16 *kt_lds = sK + buf * G::kKTile;
-    const __bf16 *vt_lds = sV + (kNeedV ? buf * G::kVTile : 0);
+    const __bf16 *v_lds = sV + (kNeedV ? buf * G::kKTile : 0);
     const int kb = kt * kBN;
     if (wave_live && kt <= kd) {
       if constexpr (MODE == kRowShare) {
         const float *lsrc = kLdsLse ? sLse + 32 * w : lseq;
-        if (kt < kd) share_tile<false, D>(st, qf, lsrc, sc, sel, base, kt_lds, vt_lds, kb, qw0, l32, h, c2);
-        else share_tile<true, D>(st, qf, lsrc, sc, sel, base, kt_lds, vt_lds, kb, qw0, l32, h, c2);
+        if (kt < kd) share_tile<false, D>(st, qf, lsrc, sc, sel, base, kt_lds, v_lds, kb, qw0, l32, h, c2);
+        else share_tile<true, D>(st, qf, lsrc, sc, sel, base, kt_lds, v_lds, kb, qw0, l32, h, c2);
       } else {
-        if (kt < kd) st_tile<MODE, FP32SUM, false, D>(st, qf, sel, kt_lds, vt_lds, kb, qw0, l32, h, c2);
-        else st_tile<MODE, FP32SUM, true, D>(st, qf, sel, kt_lds, vt_lds, kb, qw0, l32, h, c2);
+        if (kt < kd) st_tile<MODE, FP32SUM, false, D>(st, qf, sel, kt_lds, v_lds, kb, qw0, l32, h, c2);
+        else st_tile<MODE, FP32SUM, true, D>(st, qf, sel, kt_lds, v_lds, kb, qw0, l32, h, c2);
       }
     }
     if (kt + 1 < nkt) store_tile(buf ^ 1);

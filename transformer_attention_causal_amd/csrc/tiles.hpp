@@ -8,7 +8,6 @@
 namespace attn {
 
 constexpr int kBN = 64;         // keys per LDS tile (row kernels)
-constexpr int kVRow = 68;       // LDS row stride of V^T tiles, bf16 (64 keys + 4 pad)
 constexpr float kNoRow = 1e30f;            // log-sum-exp given to positions with no row
 
 // LDS tile geometry for head dimension D (64 or 128).
@@ -16,13 +15,11 @@ template <int D>
 struct Geom {
   static constexpr int kKRow = D + 8;          // K / Q rows in LDS: D bf16 + 8 pad
   static constexpr int kKTile = kBN * kKRow;   // bf16 elements per K buffer
-  static constexpr int kVTile = D * kVRow;     // bf16 elements per V^T buffer
   static constexpr int kChunks = D / 16;       // 32x32x16 MFMA steps over d
   static constexpr int kOBlocks = D / 32;      // 32-row blocks of O^T
 };
 constexpr int kKRow = Geom<64>::kKRow;
 constexpr int kKTile = Geom<64>::kKTile;
-constexpr int kVTile = Geom<64>::kVTile;
 
 // Query index (within a wave's 32 rows) of accumulator element r in lane half h.
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
@@ -41,16 +38,8 @@ __device__ __forceinline__ bf16x8 lds_frag(const __bf16 *row, int c, int h) {
   return *reinterpret_cast<const bf16x8 *>(row + 16 * c + 8 * h);
 }
 
-// V^T operand for keys [16c+4h, +4) and [16c+8+4h, +4) of a 32-key sub-tile.
-__device__ __forceinline__ bf16x8 lds_vfrag(const __bf16 *vrow, int c, int h) {
-  u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + 16 * c + 4 * h);
-  u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 16 * c + 8 + 4 * h);
-  u32x4 u = {lo[0], lo[1], hi[0], hi[1]};
-  return __builtin_bit_cast(bf16x8, u);
-}
-
-// The same operand for a block held row-major in LDS (`blk`, rows of
-// `stride` bf16), read with the transposing LDS load: lane (i = lane % 32,
+// The dim-major (transposed) operand of a block held row-major in LDS
+// (`blk`, rows of `stride` bf16), read with the transposing LDS load: lane (i = lane % 32,
 // h = lane / 32) gets column c0 + i of rows r0 + 4h + {0..3} and
 // r0 + 8 + 4h + {0..3}, i.e. element r of the other operand's accumulator
 // order.  Each ds_read_b64_tr_b16 works on groups of 16 lanes: group lane
@@ -78,45 +67,18 @@ __device__ __forceinline__ bf16x8 pack8(const float *v) {
 }
 
 // O^T[d][query] += V^T[d][keys of sub-tile t] * P^T[keys][query] for every
-// 32-row block o[i] of d.  pf0/pf1 hold keys 0..15 / 16..31 of the sub-tile
-// in the accumulator-layout order.
+// 32-row block o[i] of d, with V^T read transposed from the row-major V
+// tile (`v_lds`, rows of Geom<D>::kKRow).  pf0/pf1 hold keys 0..15 / 16..31
+// of the sub-tile in the accumulator-layout order.
 template <int D>
-__device__ __forceinline__ void pv_update_d(f32x16 *o, const __bf16 *vt_lds, int t, int l32, int h,
-                                            const bf16x8 &pf0, const bf16x8 &pf1) {
+__device__ __forceinline__ void pv_update_d(f32x16 *o, const __bf16 *v_lds, int t, const bf16x8 &pf0,
+                                            const bf16x8 &pf1) {
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
 #pragma unroll
-    for (int i = 0; i < Geom<D>::kOBlocks; ++i) {
-      const __bf16 *vr = vt_lds + (32 * i + l32) * kVRow + 32 * t;
-      o[i] = mfma32(lds_vfrag(vr, c, h), c == 0 ? pf0 : pf1, o[i]);
-    }
-  }
-}
-
-// The d = 64 form with the two blocks of O^T held separately.
-__device__ __forceinline__ void pv_update(f32x16 &o0, f32x16 &o1, const __bf16 *vt_lds, int t,
-                                          int l32, int h, const bf16x8 &pf0, const bf16x8 &pf1) {
-  const __bf16 *v0 = vt_lds + l32 * kVRow + 32 * t;
-  const __bf16 *v1 = vt_lds + (32 + l32) * kVRow + 32 * t;
-  o0 = mfma32(lds_vfrag(v0, 0, h), pf0, o0);
-  o1 = mfma32(lds_vfrag(v1, 0, h), pf0, o1);
-  o0 = mfma32(lds_vfrag(v0, 1, h), pf1, o0);
-  o1 = mfma32(lds_vfrag(v1, 1, h), pf1, o1);
-}
-
-// Rows 2kp and 2kp+1 (d-chunk dc, 8 elements each) of a [rows][64] bf16 tile,
-// written transposed into a dim-major LDS tile of row stride `stride`:
-// element (row, dim) lands at dst[dim * stride + row].  Pairs of rows are
-// merged with byte permutes so every LDS store is 32 bits wide.
-__device__ __forceinline__ void store_rows_transposed(__bf16 *dst, int stride, int kp, int dc,
-                                                      const u32x4 &r0, const u32x4 &r1) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t a0 = r0[i], a1 = r1[i];
-    const uint32_t even = __builtin_amdgcn_perm(a1, a0, 0x05040100u);  // dim 8dc + 2i
-    const uint32_t odd = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // dim 8dc + 2i + 1
-    *reinterpret_cast<uint32_t *>(dst + (8 * dc + 2 * i) * stride + 2 * kp) = even;
-    *reinterpret_cast<uint32_t *>(dst + (8 * dc + 2 * i + 1) * stride + 2 * kp) = odd;
+    for (int i = 0; i < Geom<D>::kOBlocks; ++i)
+      o[i] = mfma32(lds_tr_frag(v_lds, Geom<D>::kKRow, 32 * t + 16 * c, 32 * i), c == 0 ? pf0 : pf1,
+                    o[i]);
   }
 }
 
