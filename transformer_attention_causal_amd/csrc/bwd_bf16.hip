@@ -162,13 +162,13 @@ __device__ __forceinline__ ScanConsts scan_consts(int l32, int h) {
   return c;
 }
 
-// Per-block LDS staging shared by the column kernels: Q and dO rows of one
-// 32-row block (row-major, the A operands of S = Q K^T and dA = dO V^T), and
-// the per-row scalars.
+// Per-block LDS staging of the dK/dV kernel: Q and dO rows of one 32-row
+// block (DualRows layout: the A operands of S = Q K^T and dA = dO V^T, read
+// transposed for the closing products), and the per-row scalars.
 template <int D>
 struct ColBlock {
-  __bf16 q[32 * Geom<D>::kKRow];
-  __bf16 g[32 * Geom<D>::kKRow];
+  __bf16 q[32 * DualRows<D>::kRow];
+  __bf16 g[32 * DualRows<D>::kRow];
   float lse2[32], invr[32], dri[32];
 };
 
@@ -200,14 +200,12 @@ template <int D>
 __device__ __forceinline__ void col_scores(const ColBlock<D> &b, const bf16x8 *kf,
                                            const bf16x8 *vf, int l32, int h, f32x16 &s,
                                            f32x16 &da) {
-  const __bf16 *qrow = b.q + l32 * Geom<D>::kKRow;
-  const __bf16 *grow = b.g + l32 * Geom<D>::kKRow;
   s = zero16();
   da = zero16();
 #pragma unroll
   for (int c = 0; c < Geom<D>::kChunks; ++c) {
-    s = mfma32(lds_frag(qrow, c, h), kf[c], s);
-    da = mfma32(lds_frag(grow, c, h), vf[c], da);
+    s = mfma32(lds_frag_swz<D>(b.q, l32, c, h), kf[c], s);
+    da = mfma32(lds_frag_swz<D>(b.g, l32, c, h), vf[c], da);
   }
 }
 
@@ -239,8 +237,8 @@ __device__ __forceinline__ void dkdv_block(const ColBlock<D> &b,
     for (int u = 0; u < Geom<D>::kOBlocks; ++u)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        qtf[u][j] = lds_tr_frag(b.q, Geom<D>::kKRow, 16 * j, 32 * u);
-        gtf[u][j] = lds_tr_frag(b.g, Geom<D>::kKRow, 16 * j, 32 * u);
+        qtf[u][j] = lds_tr_frag_swz<D>(b.q, 16 * j, 32 * u);
+        gtf[u][j] = lds_tr_frag_swz<D>(b.g, 16 * j, 32 * u);
       }
     __builtin_amdgcn_sched_barrier(0);   // keep the reads where they are issued
   };
@@ -312,8 +310,8 @@ __device__ __forceinline__ void dkdv_block(const ColBlock<D> &b,
         dkt[u] = mfma32(qtf[u][j], sf[j], dkt[u]);
         dvt[u] = mfma32(gtf[u][j], af[j], dvt[u]);
       } else {
-        dkt[u] = mfma32(lds_tr_frag(b.q, Geom<D>::kKRow, 16 * j, 32 * u), sf[j], dkt[u]);
-        dvt[u] = mfma32(lds_tr_frag(b.g, Geom<D>::kKRow, 16 * j, 32 * u), af[j], dvt[u]);
+        dkt[u] = mfma32(lds_tr_frag_swz<D>(b.q, 16 * j, 32 * u), sf[j], dkt[u]);
+        dvt[u] = mfma32(lds_tr_frag_swz<D>(b.g, 16 * j, 32 * u), af[j], dvt[u]);
       }
     }
   }
@@ -389,8 +387,8 @@ __device__ __forceinline__ void dkdv_block_pipelined(const ColBlock<D> &b,
   for (int u = 0; u < Geom<D>::kOBlocks; ++u)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      cr.qtf[u][j] = lds_tr_frag(b.q, Geom<D>::kKRow, 16 * j, 32 * u);
-      cr.gtf[u][j] = lds_tr_frag(b.g, Geom<D>::kKRow, 16 * j, 32 * u);
+      cr.qtf[u][j] = lds_tr_frag_swz<D>(b.q, 16 * j, 32 * u);
+      cr.gtf[u][j] = lds_tr_frag_swz<D>(b.g, 16 * j, 32 * u);
     }
   // G = gradient terms of the later blocks + inclusive suffix in this one
   gin_word = split2_bf16(both_halves_sum(running));
@@ -528,7 +526,7 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
 #pragma unroll
     for (int i = 0; i < kBlkLoads; ++i) {
       const int u = tid + 256 * i;
-      const int off = (u / kRowChunks) * kKR + (u % kRowChunks) * 8;
+      const int off = swz_off<D>(u / kRowChunks, (u % kRowChunks) * 8);
       *reinterpret_cast<u32x4 *>(&sb[buf].q[off]) = qreg[i];
       *reinterpret_cast<u32x4 *>(&sb[buf].g[off]) = greg[i];
     }
@@ -633,7 +631,7 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
 // from the block's row-major Q rows.
 template <int D>
 struct RhoBlock {
-  __bf16 q[32 * Geom<D>::kKRow];   // Q rows (A operand of S; read transposed for Y^T)
+  __bf16 q[32 * DualRows<D>::kRow];   // Q rows (A operand of S; read transposed for Y^T)
   float lse2[32], rho[32];
 };
 
@@ -687,7 +685,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkrho_kernel(BwdArgs a, int nqs) {
 #pragma unroll
     for (int i = 0; i < kRowLoads; ++i) {
       const int u = tid + 256 * i, row = u / kRowChunks;
-      *reinterpret_cast<u32x4 *>(&sb[buf][row >> 5].q[(row & 31) * kKR + (u % kRowChunks) * 8]) =
+      *reinterpret_cast<u32x4 *>(&sb[buf][row >> 5].q[swz_off<D>(row & 31, (u % kRowChunks) * 8)]) =
           qreg[i];
     }
     if (tid < 64) {
@@ -709,10 +707,9 @@ __global__ void __launch_bounds__(256, 2) bwd_dkrho_kernel(BwdArgs a, int nqs) {
       const int qs = 2 * P + i;
       if (qs < nqs && wave_live && 32 * qs + 31 >= kw0) {
         const RhoBlock<D> &b = sb[buf][i];
-        const __bf16 *qrow = b.q + l32 * kKR;
         f32x16 sc = zero16();
 #pragma unroll
-        for (int c = 0; c < kCh; ++c) sc = mfma32(lds_frag(qrow, c, h), kf[c], sc);
+        for (int c = 0; c < kCh; ++c) sc = mfma32(lds_frag_swz<D>(b.q, l32, c, h), kf[c], sc);
         float lq[16], pq[16], wv[16];
         col_rowvals(b.lse2, h, lq);
         col_rowvals(b.rho, h, pq);
@@ -725,7 +722,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkrho_kernel(BwdArgs a, int nqs) {
         for (int u = 0; u < kOB; ++u)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
-            yt[u] = mfma32(lds_tr_frag(b.q, kKR, 16 * j, 32 * u), wf[j], yt[u]);
+            yt[u] = mfma32(lds_tr_frag_swz<D>(b.q, 16 * j, 32 * u), wf[j], yt[u]);
       }
     }
     if (P < p_hi) store_stage(buf ^ 1);
@@ -800,12 +797,11 @@ __device__ __forceinline__ void dq_subtile(DqState<D> &st, const bf16x8 *qf, con
                                            uint32_t gin_word, float lse2, float invr, float dri,
                                            float rho, int qrel, int l32, int h, float c2) {
   // S^T and dA^T for keys 32t.. of the tile (lane = query)
-  const __bf16 *krow = kt_lds + (32 * t + l32) * Geom<D>::kKRow;
   const __bf16 *vrow = vt_lds + (32 * t + l32) * Geom<D>::kKRow;
   f32x16 s = zero16(), da = zero16();
 #pragma unroll
   for (int c = 0; c < Geom<D>::kChunks; ++c) {
-    s = mfma32(lds_frag(krow, c, h), qf[c], s);
+    s = mfma32(lds_frag_swz<D>(kt_lds, 32 * t + l32, c, h), qf[c], s);
     da = mfma32(lds_frag(vrow, c, h), gf[c], da);
   }
   // The K^T fragments of the closing dQ products, read transposed from the
@@ -814,7 +810,7 @@ __device__ __forceinline__ void dq_subtile(DqState<D> &st, const bf16x8 *qf, con
   constexpr bool kAhead = D > 64 || !DIL;
   bf16x8 kta[Geom<D>::kOBlocks][2];
   auto kt_frag = [&](int i, int c) {
-    return lds_tr_frag(kt_lds, Geom<D>::kKRow, 32 * t + 16 * c, 32 * i);
+    return lds_tr_frag_swz<D>(kt_lds, 32 * t + 16 * c, 32 * i);
   };
   auto read_ahead = [&]() {
 #pragma unroll
@@ -890,7 +886,8 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dq_kernel(B
   constexpr int kCh = Geom<D>::kChunks, kOB = Geom<D>::kOBlocks;
   constexpr int kRowChunks = D / 8;                     // 16-byte chunks per row
   constexpr int kTileLoads = kBN * kRowChunks / 256;    // per thread, per tensor
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2 * kKT];
+  constexpr int kKTs = kBN * DualRows<D>::kRow;   // the K tile, read both ways
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2 * kKTs];
   __shared__ __attribute__((aligned(16))) __bf16 sV[2 * kKT];
 
   const int tid = threadIdx.x;
@@ -950,14 +947,14 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dq_kernel(B
     }
   };
   auto store_tile = [&](int buf) {
-    __bf16 *k = sK + buf * kKT;
+    __bf16 *k = sK + buf * kKTs;
     __bf16 *v = sV + buf * kKT;
 #pragma unroll
     for (int i = 0; i < kTileLoads; ++i) {
       const int u = tid + 256 * i;
-      const int off = (u / kRowChunks) * kKR + (u % kRowChunks) * 8;
-      *reinterpret_cast<u32x4 *>(k + off) = kreg[i];
-      *reinterpret_cast<u32x4 *>(v + off) = vreg[i];
+      const int row = u / kRowChunks, e = (u % kRowChunks) * 8;
+      *reinterpret_cast<u32x4 *>(k + swz_off<D>(row, e)) = kreg[i];
+      *reinterpret_cast<u32x4 *>(v + row * kKR + e) = vreg[i];
     }
   };
   // committed demand (+eps) and later blocks' g sums of this wave's block on
@@ -1005,7 +1002,7 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dq_kernel(B
       load_words(kt + 1);
     }
     if (wave_live && kt <= kd) {
-      const __bf16 *kl = sK + buf * kKT, *vl = sV + buf * kKT;
+      const __bf16 *kl = sK + buf * kKTs, *vl = sV + buf * kKT;
       const int qrel = qw0 + l32 - kt * kBN;
       // one sub-tile at a time: the per-sub-tile temporaries would not fit
       // twice beside the accumulators

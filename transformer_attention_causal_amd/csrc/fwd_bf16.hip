@@ -111,7 +111,7 @@ __device__ __forceinline__ void st_weights(const f32x16 *s, float m_run, int qre
 // m_run = -inf, shows up there as inf or NaN.  The tile sum is the fp32 one
 // (FP32SUM) or the matrix-core row sum of the bf16 weights, which the output
 // normaliser accumulates anyway.
-template <int MODE, bool FP32SUM, bool DIAG, int D>
+template <int MODE, bool FP32SUM, bool DIAG, int D, int VR>
 __device__ __forceinline__ void st_tile(RowState<D> &st, const bf16x8 *qf, const bf16x8 &sel,
                                         const __bf16 *kt_lds, const __bf16 *v_lds, int kb,
                                         int qw0, int l32, int h, float c2) {
@@ -147,7 +147,7 @@ __device__ __forceinline__ void st_tile(RowState<D> &st, const bf16x8 *qf, const
         const bf16x8 pf0 = pack8(p + 16 * t), pf1 = pack8(p + 16 * t + 8);
         st.lsum = mfma16(sel, pf0, st.lsum);
         st.lsum = mfma16(sel, pf1, st.lsum);
-        pv_update_d<D>(st.o, v_lds, t, pf0, pf1);
+        pv_update_d<D, VR>(st.o, v_lds, t, pf0, pf1);
       }
     }
   } else {
@@ -180,7 +180,7 @@ __device__ __forceinline__ void st_tile(RowState<D> &st, const bf16x8 *qf, const
     st.lsum += tsum;
     if constexpr (MODE == kRowTempered) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) pv_update_d<D>(st.o, v_lds, t, pf[2 * t], pf[2 * t + 1]);
+      for (int t = 0; t < 2; ++t) pv_update_d<D, VR>(st.o, v_lds, t, pf[2 * t], pf[2 * t + 1]);
     }
   }
 }
@@ -260,7 +260,7 @@ __device__ __forceinline__ void share_values(const f32x16 &d, const f32x16 &pt, 
   sf1 = pack8(sh + 8);
 }
 
-template <bool DIAG, int D>
+template <bool DIAG, int D, int VR>
 __device__ __forceinline__ void share_tile(RowState<D> &st, const bf16x8 *qf, const float *lseq,
                                            const ShareConsts &sc_, const bf16x8 &sel,
                                            const uint32_t *base,
@@ -292,7 +292,7 @@ __device__ __forceinline__ void share_tile(RowState<D> &st, const bf16x8 *qf, co
       share_values(dd, pt, sf0, sf1);
       st.lsum = mfma16(sel, sf0, st.lsum);
       st.lsum = mfma16(sel, sf1, st.lsum);
-      pv_update_d<D>(st.o, v_lds, t, sf0, sf1);
+      pv_update_d<D, VR>(st.o, v_lds, t, sf0, sf1);
     }
     return;
   }
@@ -313,11 +313,11 @@ __device__ __forceinline__ void share_tile(RowState<D> &st, const bf16x8 *qf, co
   share_values(d0, pt0, sf00, sf01);
   st.lsum = mfma16(sel, sf00, st.lsum);
   st.lsum = mfma16(sel, sf01, st.lsum);
-  pv_update_d<D>(st.o, v_lds, 0, sf00, sf01);
+  pv_update_d<D, VR>(st.o, v_lds, 0, sf00, sf01);
   share_values(d1, pt1, sf10, sf11);
   st.lsum = mfma16(sel, sf10, st.lsum);
   st.lsum = mfma16(sel, sf11, st.lsum);
-  pv_update_d<D>(st.o, v_lds, 1, sf10, sf11);
+  pv_update_d<D, VR>(st.o, v_lds, 1, sf10, sf11);
 }
 
 // Waves per SIMD each mode is compiled for (register budget 512/n per lane).
@@ -335,7 +335,15 @@ __global__ void __launch_bounds__(256, (RowOccupancy<MODE, D>::value))
   using G = Geom<D>;
   constexpr bool kNeedV = (MODE != kRowLse);
   __shared__ __attribute__((aligned(16))) __bf16 sK[2 * G::kKTile];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[kNeedV ? 2 * G::kKTile : 8];
+  // V tile row stride: P@V reads V only transposed, half a wave four rows
+  // of 64 bytes per load, which is free of bank conflicts when the stride is
+  // 64 or 192 bytes off a multiple of 256 (d + 32 elements).  That padding
+  // is used where the registers allow it (the tempered kernel at d = 128,
+  // where the conflicts cost most); elsewhere V has K's d + 8 and meets 2-way
+  // conflicts.
+  constexpr int kVR = (MODE == kRowTempered && D == 128) ? D + 32 : G::kKRow;
+  constexpr int kVT = kBN * kVR;
+  __shared__ __attribute__((aligned(16))) __bf16 sV[kNeedV ? 2 * kVT : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
@@ -398,13 +406,14 @@ __global__ void __launch_bounds__(256, (RowOccupancy<MODE, D>::value))
   };
   auto store_tile = [&](int buf) {
     __bf16 *k = sK + buf * G::kKTile;
-    __bf16 *vv = sV + buf * G::kKTile;
+    __bf16 *vv = sV + buf * kVT;
 #pragma unroll
     for (int i = 0; i < kKL; ++i) {
       const int u = tid + 256 * i;
-      const int off = (u / kRowChunks) * G::kKRow + (u % kRowChunks) * 8;
+      const int row = u / kRowChunks, e = (u % kRowChunks) * 8, off = row * G::kKRow + e;
       *reinterpret_cast<u32x4 *>(k + off) = kreg[i];
-      if constexpr (kNeedV) *reinterpret_cast<u32x4 *>(vv + off) = vreg[i];
+      if constexpr (kNeedV)
+        *reinterpret_cast<u32x4 *>(vv + (kVR == G::kKRow ? off : row * kVR + e)) = vreg[i];
     }
   };
 
@@ -478,16 +487,16 @@ __global__ void __launch_bounds__(256, (RowOccupancy<MODE, D>::value))
       if constexpr (MODE == kRowShare) load_cin(kt + 1);
     }
     const __bf16 *kt_lds = sK + buf * G::kKTile;
-    const __bf16 *v_lds = sV + (kNeedV ? buf * G::kKTile : 0);
+    const __bf16 *v_lds = sV + (kNeedV ? buf * kVT : 0);
     const int kb = kt * kBN;
     if (wave_live && kt <= kd) {
       if constexpr (MODE == kRowShare) {
         const float *lsrc = kLdsLse ? sLse + 32 * w : lseq;
-        if (kt < kd) share_tile<false, D>(st, qf, lsrc, sc, sel, base, kt_lds, v_lds, kb, qw0, l32, h, c2);
-        else share_tile<true, D>(st, qf, lsrc, sc, sel, base, kt_lds, v_lds, kb, qw0, l32, h, c2);
+        if (kt < kd) share_tile<false, D, kVR>(st, qf, lsrc, sc, sel, base, kt_lds, v_lds, kb, qw0, l32, h, c2);
+        else share_tile<true, D, kVR>(st, qf, lsrc, sc, sel, base, kt_lds, v_lds, kb, qw0, l32, h, c2);
       } else {
-        if (kt < kd) st_tile<MODE, FP32SUM, false, D>(st, qf, sel, kt_lds, v_lds, kb, qw0, l32, h, c2);
-        else st_tile<MODE, FP32SUM, true, D>(st, qf, sel, kt_lds, v_lds, kb, qw0, l32, h, c2);
+        if (kt < kd) st_tile<MODE, FP32SUM, false, D, kVR>(st, qf, sel, kt_lds, v_lds, kb, qw0, l32, h, c2);
+        else st_tile<MODE, FP32SUM, true, D, kVR>(st, qf, sel, kt_lds, v_lds, kb, qw0, l32, h, c2);
       }
     }
     if (kt + 1 < nkt) store_tile(buf ^ 1);
