@@ -552,19 +552,31 @@ __global__ void __launch_bounds__(256, (BwdOccupancy<D>::value)) bwd_dkdv_kernel
                                sRho[buf][3][l32];
     }
   };
+  // dilution: the committed demand (+ eps) of block qs on this lane's key,
+  // loaded with the block's rows one iteration ahead: a load issued inside
+  // the iteration would make its wait drain the next block's loads as well
+  uint32_t cw_next = 0u;
+  auto load_cin = [&](int qs) {
+    if constexpr (DIL)
+      cw_next = (wave_live && key < 32 * qs) ? cin[cin_block_offset(qs, 0) + key] : eps_word;
+  };
   load_block(block_at(0));
+  load_cin(block_at(0));
   store_block(0);
   __syncthreads();
   for (int n = 0; n < nblk; ++n) {
     const int qs = block_at(n);
     const int buf = n & 1;
-    if (n + 1 < nblk) load_block(block_at(n + 1));
+    const uint32_t cw_cur = cw_next;
+    if (n + 1 < nblk) {
+      load_block(block_at(n + 1));
+      load_cin(block_at(n + 1));
+    }
     if (n > 0) flush_rho(block_at(n - 1), buf ^ 1);
     float rho_part = 0.0f;   // waves whose keys block qs does not see add 0
     if (wave_live && 32 * qs + 31 >= kw0) {
-      uint32_t cw = 0u, gw = 0u;
+      uint32_t cw = cw_cur, gw = 0u;
       if constexpr (DIL) {
-        cw = key < 32 * qs ? cin[cin_block_offset(qs, 0) + key] : eps_word;
 #pragma unroll
         for (int c = 0; c < kCh; ++c) {
           kf[c] = lds_frag(krow, c, h);
