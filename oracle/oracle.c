@@ -85,6 +85,8 @@ static int nthreads(void) {
 #define MAX_PARTS 256
 /* rows shorter than this are summed by one thread (fork/join costs more) */
 #define PAR_MIN_ROW 256
+/* query rows the dilution passes take together (inner parallelism) */
+#define ROW_BATCH 64
 
 /*
  * Causal softmax bids of one query row ([FOCAL] eq. 1 applied to the logits
@@ -201,59 +203,54 @@ int oracle_tempered_fwd(const void *q, const void *k, const void *v, int dtype, 
  * whose output is formed (all rows still add their bids to D).  D (length T)
  * enters as the demand already committed before row P -- zero for a plain
  * prefill, the earlier chunks' column totals otherwise -- and leaves as the
- * final column totals.
+ * final column totals.  pbuf and sbuf hold the bids and shares of
+ * ROW_BATCH rows (of one row without inner parallelism), T values each.
  */
 static void dilution_head(const double *Qh, const double *Kh, const double *Vh, int P, int T,
                           int d, double c, double eps, const unsigned char *want, double *Oh,
-                          double *lse_h, double *D, double *p, int inner_parallel) {
-  for (int i = P; i < T; ++i) {
-    const int par = inner_parallel && i + 1 >= PAR_MIN_ROW;
-    const int li = i - P;
-    const double l = causal_bids(Qh + (size_t)li * d, Kh, i, d, c, p, inner_parallel);
-    if (lse_h) lse_h[li] = l;
-    if (!want || want[li]) {
+                          double *lse_h, double *D, double *pbuf, double *sbuf, int inner_parallel) {
+  /* ROW_BATCH rows at a time (one without inner parallelism): first the
+     batch's bids, row by row; then the shares, key by key with the rows in
+     order, each row's share of key j formed against the demand the rows
+     before it committed, after which its own bid joins D_j; last each row's
+     sums over its keys in increasing j.  Every value is the expression of
+     the definition above for one (row, key) pair; the batch only lets the
+     rows share each pass over K and V. */
+  const int R = inner_parallel ? ROW_BATCH : 1;
+  for (int i0 = P; i0 < T; i0 += R) {
+    const int i1 = i0 + R < T ? i0 + R : T;
+#pragma omp parallel for if (inner_parallel) schedule(dynamic, 1)
+    for (int i = i0; i < i1; ++i) {
+      const int li = i - P;
+      double *p = pbuf + (size_t)(i - i0) * T;
+      const double l = causal_bids(Qh + (size_t)li * d, Kh, i, d, c, p, 0);
+      if (lse_h) lse_h[li] = l;
+    }
+#pragma omp parallel for if (inner_parallel) schedule(static)
+    for (int j = 0; j < i1; ++j) {
+      for (int i = j > i0 ? j : i0; i < i1; ++i) {
+        const double *p = pbuf + (size_t)(i - i0) * T;
+        sbuf[(size_t)(i - i0) * T + j] = p[j] > 0.0 ? p[j] / (D[j] + p[j] + eps) : 0.0;
+        D[j] += p[j];
+      }
+    }
+#pragma omp parallel for if (inner_parallel) schedule(dynamic, 1)
+    for (int i = i0; i < i1; ++i) {
+      const int li = i - P;
+      if (want && !want[li]) continue;
+      const double *sh = sbuf + (size_t)(i - i0) * T;
       double r = 0.0;
       double acc[512];
       for (int e = 0; e < d; ++e) acc[e] = 0.0;
-      if (par) {
-        /* same sums, split across threads; partial accumulators are added in
-           a fixed order afterwards */
-        int nt = nthreads();
-        double *part = calloc((size_t)nt * (d + 1), sizeof(double));
-#pragma omp parallel
-        {
-          int t = 0;
-#ifdef _OPENMP
-          t = omp_get_thread_num();
-#endif
-          double *pa = part + (size_t)t * (d + 1);
-#pragma omp for schedule(static)
-          for (int j = 0; j <= i; ++j) {
-            if (p[j] > 0.0) {
-              const double share = p[j] / (D[j] + p[j] + eps);
-              pa[d] += share;
-              for (int e = 0; e < d; ++e) pa[e] += share * Vh[(size_t)j * d + e];
-            }
-          }
-        }
-        for (int t = 0; t < nt; ++t) {
-          for (int e = 0; e < d; ++e) acc[e] += part[(size_t)t * (d + 1) + e];
-          r += part[(size_t)t * (d + 1) + d];
-        }
-        free(part);
-      } else {
-        for (int j = 0; j <= i; ++j) {
-          if (p[j] > 0.0) {
-            const double share = p[j] / (D[j] + p[j] + eps);
-            r += share;
-            for (int e = 0; e < d; ++e) acc[e] += share * Vh[(size_t)j * d + e];
-          }
+      for (int j = 0; j <= i; ++j) {
+        const double share = sh[j];
+        if (share > 0.0) {
+          r += share;
+          for (int e = 0; e < d; ++e) acc[e] += share * Vh[(size_t)j * d + e];
         }
       }
       for (int e = 0; e < d; ++e) Oh[(size_t)li * d + e] = acc[e] / r;
     }
-#pragma omp parallel for if (par) schedule(static)
-    for (int j = 0; j <= i; ++j) D[j] += p[j];
   }
 }
 
@@ -267,19 +264,21 @@ static int dilution_one_head(const void *q, const void *k, const void *v, int dt
   double *Kh = malloc(sizeof(double) * (size_t)T * d);
   double *Vh = malloc(sizeof(double) * (size_t)T * d);
   double *D = calloc((size_t)T, sizeof(double));
-  double *p = malloc(sizeof(double) * (size_t)T);
+  const size_t rows = inner_parallel ? ROW_BATCH : 1;
+  double *p = malloc(sizeof(double) * rows * (size_t)T);
+  double *sh = malloc(sizeof(double) * rows * (size_t)T);
   int rc = 0;
-  if (!Qh || !Kh || !Vh || !D || !p) {
+  if (!Qh || !Kh || !Vh || !D || !p || !sh) {
     rc = -2;
   } else {
     widen_block(Qh, q, dtype, base, (size_t)T * d);
     widen_block(Kh, k, dtype, base, (size_t)T * d);
     widen_block(Vh, v, dtype, base, (size_t)T * d);
     dilution_head(Qh, Kh, Vh, 0, T, d, c, eps, want, out + base,
-                  lse ? lse + (size_t)bh * T : NULL, D, p, inner_parallel);
+                  lse ? lse + (size_t)bh * T : NULL, D, p, sh, inner_parallel);
     if (demand) memcpy(demand + (size_t)bh * T, D, sizeof(double) * (size_t)T);
   }
-  free(Qh); free(Kh); free(Vh); free(D); free(p);
+  free(Qh); free(Kh); free(Vh); free(D); free(p); free(sh);
   return rc;
 }
 
@@ -360,8 +359,10 @@ int oracle_prefill(const void *q, const void *kc, const void *vc, int dtype, dou
     double *Kh = malloc(sizeof(double) * (size_t)Tk * d);
     double *Vh = malloc(sizeof(double) * (size_t)Tk * d);
     double *D = calloc((size_t)Tk, sizeof(double));
-    double *p = malloc(sizeof(double) * (size_t)Tk);
-    if (!Qh || !Kh || !Vh || !D || !p) {
+    const size_t rows = (mode == 1 && inner) ? ROW_BATCH : 1;
+    double *p = malloc(sizeof(double) * rows * (size_t)Tk);
+    double *sh = mode == 1 ? malloc(sizeof(double) * rows * (size_t)Tk) : NULL;
+    if (!Qh || !Kh || !Vh || !D || !p || (mode == 1 && !sh)) {
 #pragma omp atomic write
       failed = 1;
     } else {
@@ -371,7 +372,7 @@ int oracle_prefill(const void *q, const void *kc, const void *vc, int dtype, dou
       double *lse_h = lse ? lse + (size_t)bh * Tq : NULL;
       if (mode == 1) {
         if (demand) memcpy(D, demand + (size_t)bh * Lcap, sizeof(double) * (size_t)Tk);
-        dilution_head(Qh, Kh, Vh, P, Tk, d, c, eps, NULL, out + qbase, lse_h, D, p, inner);
+        dilution_head(Qh, Kh, Vh, P, Tk, d, c, eps, NULL, out + qbase, lse_h, D, p, sh, inner);
         if (demand) memcpy(demand + (size_t)bh * Lcap, D, sizeof(double) * (size_t)Tk);
       } else {
         for (int i = P; i < Tk; ++i) {
@@ -384,7 +385,7 @@ int oracle_prefill(const void *q, const void *kc, const void *vc, int dtype, dou
         }
       }
     }
-    free(Qh); free(Kh); free(Vh); free(D); free(p);
+    free(Qh); free(Kh); free(Vh); free(D); free(p); free(sh);
   }
   return failed ? -2 : 0;
 }

@@ -11,6 +11,9 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
     config.addinivalue_line("markers", "slow: long CPU work")
+    import gpu_util
+
+    gpu_util.PYTEST_CONFIG = config
 
 
 @pytest.fixture(scope="session")

@@ -15,6 +15,25 @@ BF16_REL_RMS = 1e-2
 F32_MAX_ABS = 1e-5    # fp32 path
 DEMAND_TOTAL_REL = 1e-4
 
+# pytest's config, set by conftest: lets say() write past output capture
+PYTEST_CONFIG = None
+
+
+def say(*args, **_kw):
+    """Print a figure or a progress line straight to the terminal, past
+    pytest's output capture, so that a long comparison shows each finished
+    step as it happens rather than only when its test ends."""
+    import sys
+
+    msg = " ".join(str(a) for a in args)
+    capman = PYTEST_CONFIG.pluginmanager.getplugin("capturemanager") if PYTEST_CONFIG else None
+    if capman is None:
+        say(msg, flush=True)
+        return
+    with capman.global_and_fixture_disabled():
+        sys.stderr.write(msg + "\n")
+        sys.stderr.flush()
+
 
 def to_device(x: np.ndarray, dtype: str):
     import torch
@@ -50,7 +69,7 @@ def errors(got: np.ndarray, ref: np.ndarray):
 
 def assert_close(got, ref, dtype: str, what: str = ""):
     max_abs, rel_rms = errors(got, ref)
-    print(f"{what}: max-abs {max_abs:.3e} rel-RMS {rel_rms:.3e}")
+    say(f"{what}: max-abs {max_abs:.3e} rel-RMS {rel_rms:.3e}")
     if dtype == "bf16":
         assert max_abs <= BF16_MAX_ABS and rel_rms <= BF16_REL_RMS, \
             f"{what}: max-abs {max_abs:.3e} rel-RMS {rel_rms:.3e}"
@@ -82,7 +101,7 @@ def assert_workload(got, ref, what: str):
     figures and the worst element are printed and recorded."""
     max_abs, rel_rms = errors(got, ref)
     where, r, g = worst_element(got, ref)
-    print(f"{what}: max-abs {max_abs:.3e} rel-RMS {rel_rms:.3e} "
+    say(f"{what}: max-abs {max_abs:.3e} rel-RMS {rel_rms:.3e} "
           f"(worst at {where}: ref {r:.5f}, got {g:.5f})", flush=True)
     record(what, max_abs=max_abs, rel_rms=rel_rms, worst_at=list(where), worst_ref=r,
            worst_got=g, elements=int(np.asarray(ref).size))

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import errors, to_device
+from gpu_util import errors, to_device, say
 from transformer_attention_causal_amd import binding as ab
 from transformer_attention_causal_amd.workloads import (PREFILL, draw_grad, draw_qkv, learned_tau,
                                                         prefill_inputs)
@@ -45,7 +45,7 @@ def check_grads(got, ref, what):
     for name, g, r in zip(("dq", "dk", "dv"), got, ref):
         max_abs, rel_rms = errors(g, r)
         scale = float(np.max(np.abs(r)))
-        print(f"{what} {name}: max-abs {max_abs:.3e} (scale {scale:.3e}) rel-RMS {rel_rms:.3e}")
+        say(f"{what} {name}: max-abs {max_abs:.3e} (scale {scale:.3e}) rel-RMS {rel_rms:.3e}")
         if scale == 0.0:
             # vanishes identically (dQ and dK at T = 1: one key, so dS = 0):
             # fp32 rounding of terms the size of the other gradients
@@ -115,7 +115,7 @@ def check_sum_invariants(got, g, mode, what):
     err = np.max(np.abs(dv_sum - do_sum)) / np.max(np.abs(do_sum))
     dk = got[1].astype(np.float64)
     dk_rel = np.max(np.abs(dk.sum(axis=2)) / np.abs(dk).sum(axis=2))
-    print(f"{what}: dV total rel err {err:.3e}, |sum dK| / sum |dK| {dk_rel:.3e}")
+    say(f"{what}: dV total rel err {err:.3e}, |sum dK| / sum |dK| {dk_rel:.3e}")
     assert err <= 5e-3, what
     assert dk_rel <= DK_SUM_REL[mode], what
     assert np.all(np.isfinite(got[0])) and np.all(np.isfinite(got[1])), what
@@ -204,7 +204,7 @@ def check_dtau(got, ref_dq, inp, g, taus, dtau_ref, what):
     un = np.maximum(un, 1e-5 * terms)
     bound = np.sum(qn * un, axis=-1) / math.sqrt(d)
     err = np.abs(got.astype(np.float64) - dtau_ref)
-    print(f"{what} dtau: max err/bound {np.max(err / bound):.3e}, "
+    say(f"{what} dtau: max err/bound {np.max(err / bound):.3e}, "
           f"max err/|ref| {np.max(err / np.maximum(np.abs(dtau_ref), 1e-30)):.3e}")
     assert np.all(np.isfinite(got))
     assert np.all(err <= DTAU_REL * bound), what
@@ -243,7 +243,7 @@ def test_bwd_dtau_scalar_and_zero_tau(mode):
             # the bound needs u = dQ / c, which the oracle's dQ no longer
             # carries at c = 0: the relative bar on the value itself instead
             err = np.abs(got[3] - ref[4]) / np.abs(ref[4])
-            print(f"tau=0 mode={mode} dtau rel err {np.max(err):.3e}")
+            say(f"tau=0 mode={mode} dtau rel err {np.max(err):.3e}")
             assert np.all(err <= 2e-2)
         else:
             check_grads(got[:3], ref[:3], f"scalar tau mode={mode}")
@@ -437,7 +437,7 @@ def check_grads_f32(got, ref, what):
     for name, gg, r in zip(("dq", "dk", "dv"), got, ref):
         max_abs, rel_rms = errors(gg, r)
         scale = float(np.max(np.abs(r)))
-        print(f"{what} {name}: max-abs {max_abs:.3e} (scale {scale:.3e}) rel-RMS {rel_rms:.3e}")
+        say(f"{what} {name}: max-abs {max_abs:.3e} (scale {scale:.3e}) rel-RMS {rel_rms:.3e}")
         if scale == 0.0:
             assert max_abs <= 1e-6 * big, (what, name)
             continue
@@ -464,7 +464,7 @@ def check_dtau_f32(got, ref_dq, inp, g, taus, dtau_ref, what):
              * np.max(np.linalg.norm(k, axis=-1), axis=-1, keepdims=True))
     cond = np.sum(np.maximum(row, 1e-5 * terms), axis=-1) / math.sqrt(d)
     err = np.abs(got.astype(np.float64) - dtau_ref)
-    print(f"{what} dtau: max err/cond {np.max(err / cond):.3e}")
+    say(f"{what} dtau: max err/cond {np.max(err / cond):.3e}")
     assert np.all(np.isfinite(got))
     assert np.all(err <= F32_DTAU_REL * cond), what
 
@@ -616,7 +616,7 @@ def test_bwd_reads_the_forwards_committed_table(dtype, d, per_head):
     bar = 1e-6 if dtype == "f32" else 1e-3
     for name, a, b in zip(("dq", "dk", "dv", "dtau"), res[0], res[1]):
         ma, rr = errors(b, a)
-        print(f"{dtype} d={d} reuse vs recompute {name}: max-abs {ma:.3e} rel-RMS {rr:.3e}")
+        say(f"{dtype} d={d} reuse vs recompute {name}: max-abs {ma:.3e} rel-RMS {rr:.3e}")
         assert rr <= bar, name
     ov = (lambda x: x) if dtype == "f32" else oracle.Bf16
     ref = oracle.attn_bwd(ov(inp.q), ov(inp.k), ov(inp.v), ov(g), tau, 1e-6, 1, tau_bh=taus,
@@ -658,6 +658,6 @@ def test_bwd_t16k_reading_the_forwards_table():
         torch.cuda.empty_cache()
     for name, a, b in zip(("dq", "dk", "dv"), res[0], res[1]):
         ma, rr = errors(b, a)
-        print(f"t16k reuse vs recompute {name}: max-abs {ma:.3e} rel-RMS {rr:.3e}")
+        say(f"t16k reuse vs recompute {name}: max-abs {ma:.3e} rel-RMS {rr:.3e}")
         assert rr <= 1e-3, name
     check_sum_invariants(res[1], g, 1, "t16k reading the forward's table")

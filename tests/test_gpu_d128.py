@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 from gpu_util import (DEMAND_TOTAL_REL, assert_close, assert_workload, oracle_qkv,
-                      oracle_view, to_device)
+                      oracle_view, to_device, say)
 from transformer_attention_causal_amd import binding as ab
 from transformer_attention_causal_amd.workloads import (PREFILL, decode_initial_demand,
                                                         decode_queries, draw_qkv, learned_tau,
@@ -180,7 +180,7 @@ def test_focal_d128_t16k_bf16_against_fp32_kernels_all_rows():
         assert np.max(np.abs(lse - rlse)) <= LSE_TOL["bf16"]
         if dil:
             tot = np.max(np.abs(dem.astype(np.float64).sum(-1) / rdem.astype(np.float64).sum(-1) - 1.0))
-            print(f"focal d128 demand totals bf16 vs fp32 kernels: {tot:.3e}")
+            say(f"focal d128 demand totals bf16 vs fp32 kernels: {tot:.3e}")
             assert tot <= DEMAND_TOTAL_REL
             assert np.max(np.abs(dem - rdem)) <= DEMAND_TOL["bf16"] * max(1.0, float(rdem.max()))
 

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import DEMAND_TOTAL_REL, assert_close, to_device
+from gpu_util import DEMAND_TOTAL_REL, assert_close, to_device, say
 from transformer_attention_causal_amd import binding as ab
 from transformer_attention_causal_amd.workloads import (decode_cache_host, decode_initial_demand,
                                                         decode_queries, draw_qkv)
@@ -103,7 +103,7 @@ def test_fused_and_chunked_decode_agree(d):
     torch.cuda.synchronize()
     a, b = o_fused.float().cpu().numpy(), o_chunk.float().cpu().numpy()
     err = float(np.max(np.abs(a - b)))
-    print(f"d={d}: fused vs chunked max-abs {err:.3e}")
+    say(f"d={d}: fused vs chunked max-abs {err:.3e}")
     assert err <= 2e-2 * max(1.0, float(np.max(np.abs(a))))
     dd = np.abs(Ds.cpu().numpy() - Db[:, :, :L].cpu().numpy())
     assert float(dd.max()) <= 1e-5 * max(1.0, float(D0.max()) + 1.0)

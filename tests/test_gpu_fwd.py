@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import DEMAND_TOTAL_REL, assert_close, device_qkv, errors, oracle_qkv
+from gpu_util import DEMAND_TOTAL_REL, assert_close, device_qkv, errors, oracle_qkv, say
 from transformer_attention_causal_amd import binding as ab
 from transformer_attention_causal_amd.workloads import PREFILL, draw_qkv, prefill_inputs
 
@@ -114,7 +114,7 @@ def test_softmax_t2048_workload():
     inp = prefill_inputs(w)
     out = run_fwd(inp, TAU4, ab.ATTN_TEMPERED)
     ref, _ = oracle.tempered_fwd(*oracle_qkv(inp), TAU4)
-    print("softmax_t2048 max-abs %.3e rel-RMS %.3e" % errors(out, ref))
+    say("softmax_t2048 max-abs %.3e rel-RMS %.3e" % errors(out, ref))
     assert_close(out, ref, "bf16", "softmax_t2048")
 
 
@@ -241,7 +241,7 @@ def test_dilution_with_huge_eps_is_tempered(d):
     dil = run_fwd(inp, TAU4, ab.ATTN_DILUTION, eps=1e9)
     tmp = run_fwd(inp, TAU4, ab.ATTN_TEMPERED)
     ma, rr = errors(dil, tmp)
-    print(f"d={d}: dilution(eps=1e9) vs tempered max-abs {ma:.3e} rel-RMS {rr:.3e}")
+    say(f"d={d}: dilution(eps=1e9) vs tempered max-abs {ma:.3e} rel-RMS {rr:.3e}")
     # two bf16 outputs of one value differ by at most a rounding step or two
     assert ma <= 2e-2 * max(1.0, float(np.max(np.abs(tmp)))) and rr <= 1e-2
 
@@ -277,7 +277,7 @@ def test_fp32_t16k_one_head_against_oracle(name):
     assert_close(out, ref, "f32", f"{name} fp32 dilution t16k")
     lse_err = float(np.max(np.abs(lse - rlse)))
     dem_err = float(np.max(np.abs(dem - rdem) / np.maximum(1.0, np.abs(rdem))))
-    print(f"{name} fp32 dilution t16k: lse {lse_err:.3e} demand {dem_err:.3e}")
+    say(f"{name} fp32 dilution t16k: lse {lse_err:.3e} demand {dem_err:.3e}")
     assert lse_err <= 1e-5 and dem_err <= 1e-5
     out, lse = run_fwd(f32, TAU4, ab.ATTN_TEMPERED, want_lse=True)
     ref, rlse = oracle.tempered_fwd(*oracle_qkv(f32), TAU4)
@@ -303,7 +303,7 @@ def test_t16k_bf16_against_fp32_kernels_all_rows():
             torch.cuda.empty_cache()
             ref, rdem = run_fwd(f32, tau, mode, w.eps, want_demand=True)
             tot = np.max(np.abs(dem.sum(-1) / rdem.sum(-1) - 1.0))
-            print(f"t16k demand totals bf16 vs fp32 kernels: {tot:.3e}")
+            say(f"t16k demand totals bf16 vs fp32 kernels: {tot:.3e}")
             assert tot <= DEMAND_TOTAL_REL
             assert np.max(np.abs(dem - rdem)) <= 2e-2 * max(1.0, float(rdem.max()))
         else:
@@ -330,7 +330,7 @@ def test_t128k_bf16_against_fp32_kernels_all_rows():
     ref, rdem = run_fwd(f32, 1.0, ab.ATTN_DILUTION, w.eps, want_demand=True)
     torch.cuda.empty_cache()
     exact = [float(np.max(np.abs(x.astype(np.float64).sum(-1) / w.T - 1.0))) for x in (dem, rdem)]
-    print(f"t128k demand totals vs T: bf16 {exact[0]:.3e}, fp32 kernels {exact[1]:.3e}")
+    say(f"t128k demand totals vs T: bf16 {exact[0]:.3e}, fp32 kernels {exact[1]:.3e}")
     assert max(exact) <= DEMAND_TOTAL_REL
     assert np.max(np.abs(dem.sum(-1) / rdem.sum(-1) - 1.0)) <= DEMAND_TOTAL_REL
     assert np.max(np.abs(dem - rdem)) <= 2e-2 * max(1.0, float(rdem.max()))

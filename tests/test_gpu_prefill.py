@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import DEMAND_TOTAL_REL, assert_close, oracle_qkv, oracle_view, to_device
+from gpu_util import DEMAND_TOTAL_REL, assert_close, oracle_qkv, oracle_view, to_device, say
 from transformer_attention_causal_amd import binding as ab
 from transformer_attention_causal_amd.workloads import draw_qkv
 
@@ -59,12 +59,12 @@ def check_demand(dem, rdem, T, dtype, what):
     dem = dem[..., :T]
     if dtype == "f32":
         err = float(np.max(np.abs(dem - rdem) / np.maximum(1.0, np.abs(rdem))))
-        print(f"{what} demand: max rel {err:.3e}")
+        say(f"{what} demand: max rel {err:.3e}")
         assert err <= 1e-5
     else:
         tot = float(np.max(np.abs(dem.sum(axis=-1) / rdem.sum(axis=-1) - 1.0)))
         err = float(np.max(np.abs(dem - rdem)) / max(1.0, float(np.max(rdem))))
-        print(f"{what} demand: totals rel {tot:.3e} per-key {err:.3e}")
+        say(f"{what} demand: totals rel {tot:.3e} per-key {err:.3e}")
         assert tot <= DEMAND_TOTAL_REL and err <= 2e-2
 
 
@@ -139,7 +139,7 @@ def test_chunk_from_carried_demand(dtype, Tk, Tq):
     assert np.all(got[..., Tk:] == 7.0)
     tol = 1e-5 if dtype == "f32" else 2e-2
     err = np.max(np.abs(got[..., :Tk] - Dref[..., :Tk]) / np.maximum(1.0, Dref[..., :Tk]))
-    print(f"carried demand Tk={Tk} Tq={Tq}: demand max rel {err:.3e}")
+    say(f"carried demand Tk={Tk} Tq={Tq}: demand max rel {err:.3e}")
     assert err <= tol
     # the chunk adds one unit of demand per row
     added = got[..., :Tk].astype(np.float64).sum(-1) - D0[..., :Tk].astype(np.float64).sum(-1)
@@ -257,7 +257,7 @@ def test_chunk_row_sums_match_whole_prefill():
     got = torch.cat(parts, dim=2).cpu().numpy().astype(np.float64)
     ref = rs_whole.cpu().numpy().astype(np.float64)
     rel = float(np.max(np.abs(got / ref - 1.0)))
-    print(f"chunk row sums vs whole: max rel {rel:.3e}")
+    say(f"chunk row sums vs whole: max rel {rel:.3e}")
     assert np.all(ref > 0) and rel <= 5e-3
 
 
@@ -276,6 +276,6 @@ def test_bench_chunking_t16k_against_oracle():
     ref, rlse, rdem = oracle.dilution_fwd(*oracle_qkv(inp), 1.0, w.eps)
     assert_close(out, ref, "bf16", "8 x 2048 chunks at T=16384")
     lse_err = float(np.max(np.abs(lse - rlse)))
-    print(f"8 x 2048 chunks lse: max-abs {lse_err:.3e}")
+    say(f"8 x 2048 chunks lse: max-abs {lse_err:.3e}")
     assert lse_err <= 2e-3
     check_demand(dem, rdem, w.T, "bf16", "8 x 2048 chunks")

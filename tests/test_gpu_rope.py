@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import assert_close, errors, oracle_view, to_device
+from gpu_util import assert_close, errors, oracle_view, to_device, say
 from transformer_attention_causal_amd import binding as ab
 from transformer_attention_causal_amd.workloads import draw_qkv, learned_tau
 
@@ -68,7 +68,7 @@ def check_rope(out, inp, freq, pos0, tau, mode, what, tau_bh=None):
     rounded = oracle_rope_forward(inp, freq, pos0, tau, mode, tau_bh=tau_bh, rounded=True)
     assert_close(got, rounded, "bf16", what + " (rotated rows in bf16)")
     ma, rr = errors(got, exact)
-    print(f"{what} against the exact rotation: max-abs {ma:.3e} rel-RMS {rr:.3e}")
+    say(f"{what} against the exact rotation: max-abs {ma:.3e} rel-RMS {rr:.3e}")
     assert rr <= 1e-2, what
 
 

@@ -25,15 +25,13 @@ MUTANTS = [
      "const long lo = (long)(i) * t / n, hi = (long)(i) * (t + 1) / n;"),
     ("bids_not_normalised", "p[j] = exp(p[j] - l);", "p[j] = exp(p[j] - M);"),
     ("lse_wrong_sign", "const double l = M + log(Z);", "const double l = M - log(Z);"),
-    ("diagonal_bid_not_committed", "for (int j = 0; j <= i; ++j) D[j] += p[j];",
-     "for (int j = 0; j < i; ++j) D[j] += p[j];"),
+    ("diagonal_bid_not_committed", "        D[j] += p[j];", "        if (i > j) D[j] += p[j];"),
+    ("demand_never_committed", "        D[j] += p[j];\n", "\n"),
     ("shares_not_renormalised", "Oh[(size_t)li * d + e] = acc[e] / r;",
      "Oh[(size_t)li * d + e] = acc[e];"),
-    ("value_rows_reversed", "pa[e] += share * Vh[(size_t)j * d + e];",
-     "pa[e] += share * Vh[(size_t)(i - j) * d + e];"),
-    ("value_rows_reversed_serial",
-     "            for (int e = 0; e < d; ++e) acc[e] += share * Vh[(size_t)j * d + e];",
-     "            for (int e = 0; e < d; ++e) acc[e] += share * Vh[(size_t)(i - j) * d + e];"),
+    ("value_rows_reversed",
+     "          for (int e = 0; e < d; ++e) acc[e] += share * Vh[(size_t)j * d + e];",
+     "          for (int e = 0; e < d; ++e) acc[e] += share * Vh[(size_t)(i - j) * d + e];"),
     ("tempered_value_row_off_by_one", "acc[e] += p[j] * Vh[(size_t)j * d + e];",
      "acc[e] += p[j] * Vh[(size_t)(j > 0 ? j - 1 : 0) * d + e];"),
     ("decode_committed_inclusive", "(Dh[j] + p[j] + eps)", "(Dh[j] + 2.0 * p[j] + eps)"),
@@ -46,8 +44,8 @@ MUTANTS = [
     ("prefill_demand_in_ignored",
      "if (demand) memcpy(D, demand + (size_t)bh * Lcap, sizeof(double) * (size_t)Tk);", ""),
     ("prefill_keys_from_chunk_start",
-     "causal_bids(Qh + (size_t)li * d, Kh, i, d, c, p, inner_parallel)",
-     "causal_bids(Qh + (size_t)li * d, Kh, li, d, c, p, inner_parallel)"),
+     "causal_bids(Qh + (size_t)li * d, Kh, i, d, c, p, 0)",
+     "causal_bids(Qh + (size_t)li * d, Kh, li, d, c, p, 0)"),
     ("prefill_cache_stride", "kbase = (size_t)bh * Lcap * d", "kbase = (size_t)bh * Tk * d"),
     ("prefill_tempered_keys_from_chunk_start",
      "causal_bids(Qh + (size_t)(i - P) * d, Kh, i, d, c, p, inner)",
