@@ -264,6 +264,9 @@ def main():
             seg[n].append(e[j].elapsed_time(e[j + 1]))
     ms = {n: float(np.median(seg[n])) for n in names}
     ms_min = {n: float(np.min(seg[n])) for n in names}
+    # the three dilution launches as one call: first launch's start to the
+    # last one's end, the gaps between launches included
+    dil_call_ms = float(np.median([e[0].elapsed_time(e[3]) for e in evs]))
     log("bench: per-launch ms " + json.dumps({n: round(ms[n], 4) for n in names}))
 
     # ------------------------------------------------------------- backward
@@ -503,6 +506,8 @@ def main():
             "dilution_fwd": {"ms": round(dil_ms, 4), "tflops": round(dil_tflops, 3),
                              "frac_of_bf16_peak": round(dil_tflops / PEAK_BF16_TFLOPS, 4),
                              "stages": stages_out,
+                             "whole_call_ms": round(dil_call_ms, 4),
+                             "whole_call_tflops": round(flops / (dil_call_ms * 1e-3) / 1e12, 3),
                              "executed_mfma_busy_rocprof": measured_busy("dilution_fwd", FWD_SOURCES)},
             "tempered_fwd": {"ms": round(ms["tempered"], 4), "tflops": round(tmp_tflops, 3),
                              "frac_of_bf16_peak": round(tmp_tflops / PEAK_BF16_TFLOPS, 4),
