@@ -6,8 +6,10 @@
  * shares no code, header, table or helper with it.
  *
  * Every quantity is computed straight from its definition, one query row at a
- * time, in double precision.  Inputs arrive as fp64, fp32 or raw bf16 bits and
- * are widened exactly to double before any arithmetic.
+ * time (the dilution passes hold up to 64 rows' bids at once, each share and
+ * sum still formed for one row), in double precision.  Inputs arrive as
+ * fp64, fp32 or raw bf16 bits and are widened exactly to double before any
+ * arithmetic.
  *
  * Sources (cited by page title and section):
  *   [FOCAL]  "Learning to Focus: Focal Attention for Selective and Scalable
